@@ -1,0 +1,137 @@
+"""Plain CPU oracle for the DSA decode step (indexer scores, exact top-k, attention).
+
+TEST INFRASTRUCTURE ONLY: the test-suite, the smoke check and the CPU-baseline leg
+of the benchmark may import this package; the product path never does. It shares
+no code with the HIP library. The arithmetic lives in ``dsa_oracle.cpp`` (plain
+C++, int64 scores, std::stable_sort, fp64 softmax); this module compiles it with
+g++ and calls it through ctypes on numpy arrays.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "dsa_oracle.cpp")
+_LIB = os.path.join(_HERE, "liboracle_dsa.so")
+_lib = None
+
+F32, BF16 = 0, 1
+
+
+def build(force=True):
+    """Compile dsa_oracle.cpp into liboracle_dsa.so next to it (plain g++, -O2)."""
+    if not force and os.path.exists(_LIB):
+        return _LIB
+    tmp = _LIB + ".tmp%d" % os.getpid()
+    subprocess.check_call(["g++", "-O2", "-std=c++17", "-shared", "-fPIC", "-o", tmp, _SRC])
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        p, i32, i64, dbl = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
+        lib.dsa_ref_index_scores.argtypes = [p, p, p, p, i32, i32, i32, i64, p]
+        lib.dsa_ref_topk_select.argtypes = [p, p, i32, i64, i32, p]
+        lib.dsa_ref_sparse_attn.argtypes = [p, p, p, i32, i32, i32, i32, i64, i32, dbl, i32, p]
+        lib.dsa_ref_decode_step.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32, i32,
+                                            i64, i32, dbl, i32, p, p, p]
+        for f in (lib.dsa_ref_index_scores, lib.dsa_ref_topk_select, lib.dsa_ref_sparse_attn,
+                  lib.dsa_ref_decode_step):
+            f.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError("%s failed: oracle code %d (1 = bad argument, 2 = score overflows int32)"
+                         % (what, rc))
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a)
+    if a.dtype != dtype:
+        raise TypeError("expected %s, got %s" % (np.dtype(dtype), a.dtype))
+    return a
+
+
+def _kv_dtype(a):
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:  # bf16 bit patterns
+        return BF16
+    raise TypeError("attention inputs must be float32 or bf16 bit patterns (uint16)")
+
+
+def index_scores(iq, iw, ik, ctx_len):
+    """iq [B,Hi,Di] int8, iw [B,Hi] int8, ik [N,Di] int8, ctx_len [B] int32 -> scores [B,N] int32.
+
+    Entries at or past ctx_len[b] are left at 0 (the oracle never writes them).
+    """
+    iq, iw, ik = _c(iq, np.int8), _c(iw, np.int8), _c(ik, np.int8)
+    ctx_len = _c(ctx_len, np.int32)
+    B, Hi, Di = iq.shape
+    N = ik.shape[0]
+    assert ik.shape[1] == Di and iw.shape == (B, Hi) and ctx_len.shape == (B,)
+    scores = np.zeros((B, N), np.int32)
+    _check(_load().dsa_ref_index_scores(_ptr(iq), _ptr(iw), _ptr(ik), _ptr(ctx_len), B, Hi, Di, N,
+                                        _ptr(scores)), "index_scores")
+    return scores
+
+
+def topk_select(scores, ctx_len, k):
+    """scores [B,N] int32, ctx_len [B] int32 -> idx [B,k] int32 ((score desc, pos asc), -1 pad)."""
+    scores, ctx_len = _c(scores, np.int32), _c(ctx_len, np.int32)
+    B, N = scores.shape
+    idx = np.empty((B, k), np.int32)
+    _check(_load().dsa_ref_topk_select(_ptr(scores), _ptr(ctx_len), B, N, k, _ptr(idx)),
+           "topk_select")
+    return idx
+
+
+def sparse_attn(q, kv, idx, Dv, scale):
+    """q [B,Hq,Dk], kv [N,Dk] (float32 or bf16 bits as uint16), idx [B,k] -> out [B,Hq,Dv] float64."""
+    dt = _kv_dtype(q)
+    if _kv_dtype(kv) != dt:
+        raise TypeError("q and kv must share a dtype")
+    q, kv, idx = np.ascontiguousarray(q), np.ascontiguousarray(kv), _c(idx, np.int32)
+    B, Hq, Dk = q.shape
+    N = kv.shape[0]
+    k = idx.shape[1]
+    assert kv.shape[1] == Dk and idx.shape[0] == B
+    out = np.empty((B, Hq, Dv), np.float64)
+    _check(_load().dsa_ref_sparse_attn(_ptr(q), _ptr(kv), _ptr(idx), B, Hq, Dk, Dv, N, k,
+                                       float(scale), dt, _ptr(out)), "sparse_attn")
+    return out
+
+
+def decode_step(iq, iw, ik, q, kv, ctx_len, k, Dv, scale):
+    """All three stages; returns (scores [B,N] int32, idx [B,k] int32, out [B,Hq,Dv] float64)."""
+    iq, iw, ik = _c(iq, np.int8), _c(iw, np.int8), _c(ik, np.int8)
+    ctx_len = _c(ctx_len, np.int32)
+    dt = _kv_dtype(q)
+    if _kv_dtype(kv) != dt:
+        raise TypeError("q and kv must share a dtype")
+    q, kv = np.ascontiguousarray(q), np.ascontiguousarray(kv)
+    B, Hi, Di = iq.shape
+    _, Hq, Dk = q.shape
+    N = ik.shape[0]
+    assert kv.shape == (N, Dk)
+    scores = np.zeros((B, N), np.int32)
+    idx = np.empty((B, k), np.int32)
+    out = np.empty((B, Hq, Dv), np.float64)
+    _check(_load().dsa_ref_decode_step(_ptr(iq), _ptr(iw), _ptr(ik), _ptr(q), _ptr(kv), _ptr(ctx_len),
+                                       B, Hi, Di, Hq, Dk, Dv, N, k, float(scale), dt,
+                                       _ptr(scores), _ptr(idx), _ptr(out)), "decode_step")
+    return scores, idx, out

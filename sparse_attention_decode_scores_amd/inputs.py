@@ -1,0 +1,134 @@
+"""Seeded synthetic inputs for the DSA decode step (shared by the tests, the oracle
+checks and the benchmark). This module draws numbers and nothing else: none of the
+method's arithmetic lives here.
+
+Workloads (no real GLM-5.3-Flash weights or caches are available, so every array
+is synthetic with the shapes of the model's DSA layers):
+
+  cfg0   B=1, context 4,096, k=256; indexer 4 heads x 64, query and keys int8
+         uniform on [-8, 8], head weights uniform on [1, 4]; attention 8 heads x 64,
+         one shared fp32 N(0,1) row per position used as key and value; scale 1/8.
+  cfg1   B=1, context 16,384, k=2,048; indexer 64 heads x 128 with one shared
+         128-dim key per position, int8 uniform on [-16, 16], head weights uniform
+         on [1, 8]; attention 16 heads over a shared latent row of 512 latent + 64
+         rope values per position, bf16 N(0,1)*0.5; output 512 values per head;
+         scale 1/sqrt(576) = 1/24.
+  cfg2   cfg1 shapes at context 62,464, eleven independent layers (own seeds).
+  cfg3   cfg1 shapes at context 300,000 with indexer keys on the coarse grid
+         {-2..2}.
+  cfg4   width-8 verify block: B=8 over a shared 131,072-position cache; row r
+         sees ctx_len = 131,065 + r.
+  cfg3T  cfg3 with every key row drawn from a pool of 512 rows, so that many
+         positions share a score exactly (ties at the selection threshold).
+  cfgZ   cfg1 with an all-zero indexer query: every score is 0.
+
+Integer ranges are inclusive. Seeds: numpy PCG64 ``default_rng(1000 + c)`` for
+cfg c, ``2000 + l`` for layer l of cfg2, 1030 for cfg3T, 1090 for cfgZ. Arrays are
+drawn in the order iq, iw, ik, q, kv.
+
+bf16 values are carried as uint16 bit patterns (round to nearest even from the
+fp32 draw).
+"""
+import numpy as np
+
+CONFIGS = {
+    "cfg0": dict(B=1, N=4096, k=256, Hi=4, Di=64, Hq=8, Dk=64, Dv=64, dtype="f32",
+                 scale=1.0 / 8.0, qk_range=8, w_range=(1, 4), key_range=8, layers=1, seed=1000),
+    "cfg1": dict(B=1, N=16384, k=2048, Hi=64, Di=128, Hq=16, Dk=576, Dv=512, dtype="bf16",
+                 scale=1.0 / 24.0, qk_range=16, w_range=(1, 8), key_range=16, layers=1, seed=1001),
+    "cfg2": dict(B=1, N=62464, k=2048, Hi=64, Di=128, Hq=16, Dk=576, Dv=512, dtype="bf16",
+                 scale=1.0 / 24.0, qk_range=16, w_range=(1, 8), key_range=16, layers=11, seed=2000),
+    "cfg3": dict(B=1, N=300000, k=2048, Hi=64, Di=128, Hq=16, Dk=576, Dv=512, dtype="bf16",
+                 scale=1.0 / 24.0, qk_range=16, w_range=(1, 8), key_range=2, layers=1, seed=1003),
+    "cfg4": dict(B=8, N=131072, k=2048, Hi=64, Di=128, Hq=16, Dk=576, Dv=512, dtype="bf16",
+                 scale=1.0 / 24.0, qk_range=16, w_range=(1, 8), key_range=16, layers=1, seed=1004),
+    "cfg3T": dict(B=1, N=300000, k=2048, Hi=64, Di=128, Hq=16, Dk=576, Dv=512, dtype="bf16",
+                  scale=1.0 / 24.0, qk_range=16, w_range=(1, 8), key_range=2, layers=1, seed=1030,
+                  key_pool=512),
+    "cfgZ": dict(B=1, N=16384, k=2048, Hi=64, Di=128, Hq=16, Dk=576, Dv=512, dtype="bf16",
+                 scale=1.0 / 24.0, qk_range=16, w_range=(1, 8), key_range=16, layers=1, seed=1090,
+                 zero_query=True),
+}
+
+
+def f32_to_bf16_bits(x):
+    """Round float32 values to bf16 (nearest, ties to even) and return the uint16 bits."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    try:  # torch's multi-threaded conversion, same rounding; plain numpy otherwise
+        import torch
+        return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    except ImportError:
+        pass
+    flat = x.reshape(-1).view(np.uint32)
+    out = np.empty(flat.shape, np.uint16)
+    step = 1 << 22
+    for s in range(0, flat.size, step):  # chunked: keeps temporaries in cache
+        u = flat[s:s + step]
+        t = u >> np.uint32(16)
+        t &= np.uint32(1)
+        t += np.uint32(0x7FFF)
+        t += u
+        t >>= np.uint32(16)
+        out[s:s + step] = t
+    return out.reshape(x.shape)
+
+
+def bf16_bits_to_f32(b):
+    """Widen uint16 bf16 bit patterns to float32 (exact)."""
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def ctx_lengths(name):
+    c = CONFIGS[name]
+    if name == "cfg4":
+        return np.array([c["N"] - 7 + r for r in range(c["B"])], np.int32)
+    return np.full(c["B"], c["N"], np.int32)
+
+
+def _normal(rng, shape, dtype, mul):
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    if mul != 1.0:
+        x *= np.float32(mul)
+    return x if dtype == "f32" else f32_to_bf16_bits(x)
+
+
+def make(name, layer=0):
+    """Inputs of one layer of workload ``name`` as a dict of numpy arrays plus its shapes."""
+    c = dict(CONFIGS[name])
+    if not 0 <= layer < c["layers"]:
+        raise ValueError("layer out of range")
+    rng = np.random.default_rng(c["seed"] + layer)
+    B, N, Hi, Di, Hq, Dk = c["B"], c["N"], c["Hi"], c["Di"], c["Hq"], c["Dk"]
+    qr, kr = c["qk_range"], c["key_range"]
+    iq = rng.integers(-qr, qr + 1, size=(B, Hi, Di), dtype=np.int8)
+    iw = rng.integers(c["w_range"][0], c["w_range"][1] + 1, size=(B, Hi), dtype=np.int8)
+    if c.get("key_pool"):
+        pool = rng.integers(-kr, kr + 1, size=(c["key_pool"], Di), dtype=np.int8)
+        ik = pool[rng.integers(0, c["key_pool"], size=N)]
+    else:
+        ik = rng.integers(-kr, kr + 1, size=(N, Di), dtype=np.int8)
+    if c.get("zero_query"):
+        iq[...] = 0
+    mul = 1.0 if c["dtype"] == "f32" else 0.5
+    q = _normal(rng, (B, Hq, Dk), c["dtype"], mul)
+    kv = _normal(rng, (N, Dk), c["dtype"], mul)
+    c.update(iq=iq, iw=iw, ik=np.ascontiguousarray(ik), q=q, kv=kv, ctx_len=ctx_lengths(name),
+             name=name, layer=layer)
+    return c
+
+
+def random_case(seed, B, N, k, Hi, Di, Hq, Dk, Dv, dtype="bf16", ctx_len=None, qk_range=16,
+                key_range=16, w_range=(1, 8), scale=None):
+    """A seeded case of arbitrary shape with the same value recipe as the workloads."""
+    rng = np.random.default_rng(seed)
+    iq = rng.integers(-qk_range, qk_range + 1, size=(B, Hi, Di), dtype=np.int8)
+    iw = rng.integers(w_range[0], w_range[1] + 1, size=(B, Hi), dtype=np.int8)
+    ik = rng.integers(-key_range, key_range + 1, size=(N, Di), dtype=np.int8)
+    mul = 1.0 if dtype == "f32" else 0.5
+    q = _normal(rng, (B, Hq, Dk), dtype, mul)
+    kv = _normal(rng, (N, Dk), dtype, mul)
+    if ctx_len is None:
+        ctx_len = np.full(B, N, np.int32)
+    return dict(B=B, N=N, k=k, Hi=Hi, Di=Di, Hq=Hq, Dk=Dk, Dv=Dv, dtype=dtype,
+                scale=(1.0 / np.sqrt(Dk)) if scale is None else scale, iq=iq, iw=iw, ik=ik, q=q,
+                kv=kv, ctx_len=np.asarray(ctx_len, np.int32), layers=1, name="random", layer=0)
