@@ -8,7 +8,7 @@ import importlib
 
 __all__ = ["dsa_index_scores", "dsa_topk_select", "dsa_sparse_attn", "dsa_decode_step",
            "dsa_workspace_size", "dsa_status_string", "dsa_read_stats", "DSAError",
-           "FLAG_FORCE_FALLBACK", "library_path", "build"]
+           "FLAG_FORCE_FALLBACK", "library_path", "build", "new_workspace", "load_library"]
 
 
 def __getattr__(name):

@@ -1,0 +1,345 @@
+// C entry points of libdsa: host-side validation, workspace layout and launch
+// planning. Every check runs before anything is enqueued; nothing here allocates
+// device memory or synchronises (except dsa_read_stats, documented as such).
+#include <math.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "../../include/dsa.h"
+#include "kernels.h"
+
+namespace dsa {
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
+
+int splits_for(int k) {
+  int s = (k + 63) / 64;
+  return s < 1 ? 1 : (s > kMaxSplits ? kMaxSplits : s);
+}
+int rankers_for(int k) {
+  int r = (k + 15) / 16;
+  return r < 1 ? 1 : (r > kMaxRankBlocks ? kMaxRankBlocks : r);
+}
+
+// Byte offsets of the workspace regions.
+struct Layout {
+  size_t stats, cand, xc, ml, o, bad, sort, total;
+};
+Layout layout(int B, int64_t N, int k, int Hq, int Dv) {
+  const int S = splits_for(k);
+  Layout L;
+  L.stats = 0;
+  L.cand = up(sizeof(RowStats) * kMaxBatch);
+  L.xc = L.cand + up((size_t)B * kCandCap * 8);
+  L.ml = L.xc + up((size_t)B * kMaxChunks * 8);
+  L.o = L.ml + up((size_t)B * S * Hq * 8);
+  L.bad = L.o + up((size_t)B * S * Hq * Dv * 4);
+  L.sort = L.bad + up((size_t)B * S * 4);
+  L.total = L.sort + up((size_t)B * 2 * (size_t)N * 8);
+  return L;
+}
+
+// LDS bytes a workgroup may use on the current device (gfx950: 160 KiB; that value
+// is also assumed when no device can be queried, so host-only validation behaves
+// as on the GPU).
+int lds_limit() {
+  constexpr int kGfx950Lds = 160 * 1024;
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kGfx950Lds;
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+        v <= 0)
+      v = kGfx950Lds;
+    cached[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+dsa_status check_rows(const int32_t* ctx_len, int B, int64_t N, RowLens* lens, int* nmax) {
+  if (ctx_len == nullptr || B < 1 || B > DSA_MAX_BATCH || N < 1 || N > INT32_MAX)
+    return DSA_ERR_INVALID_ARG;
+  memset(lens, 0, sizeof(*lens));
+  int mx = 0;
+  for (int b = 0; b < B; ++b) {
+    if (ctx_len[b] < 1 || (int64_t)ctx_len[b] > N) return DSA_ERR_INVALID_ARG;
+    lens->n[b] = ctx_len[b];
+    mx = ctx_len[b] > mx ? ctx_len[b] : mx;
+  }
+  *nmax = mx;
+  return DSA_OK;
+}
+
+dsa_status check_index(const int8_t* iq, const int8_t* iw, const int8_t* ik, int Hi, int Di) {
+  if (!iq || !iw || !ik) return DSA_ERR_INVALID_ARG;
+  if (Hi < 1 || Hi > DSA_MAX_INDEX_HEADS || Di < 32 || Di > DSA_MAX_INDEX_DIM || Di % 32 != 0)
+    return DSA_ERR_INVALID_ARG;
+  if (!aligned(iq, 16) || !aligned(ik, 16)) return DSA_ERR_INVALID_ARG;
+  return DSA_OK;
+}
+
+dsa_status check_attn(const void* q, const void* kv, int Hq, int Dk, int Dv, float scale,
+                      dsa_dtype dt, AttnChoice* ch) {
+  if (!q || !kv) return DSA_ERR_INVALID_ARG;
+  if (Hq < 1 || Hq > DSA_MAX_ATTN_HEADS || Dk < 1 || Dk > DSA_MAX_ATTN_DIM || Dv < 1 || Dv > Dk)
+    return DSA_ERR_INVALID_ARG;
+  if (dt != DSA_F32 && dt != DSA_BF16) return DSA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return DSA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(kv, 16)) return DSA_ERR_INVALID_ARG;
+  *ch = choose_attn(dt == DSA_BF16, Hq, Dk, Dv);
+  if (ch->kind == ATTN_NONE) return DSA_ERR_UNSUPPORTED;
+  if (select_lds_bytes(*ch, Hq, Dk, DSA_MAX_K) > (size_t)lds_limit()) return DSA_ERR_UNSUPPORTED;
+  return DSA_OK;
+}
+
+dsa_status check_ws(void* ws, size_t ws_bytes, const Layout& L) {
+  if (ws == nullptr || !aligned(ws, 256)) return DSA_ERR_WORKSPACE;
+  if (ws_bytes < L.total) return DSA_ERR_WORKSPACE;
+  return DSA_OK;
+}
+
+// Chunking of the candidate pass for rows of at most nmax positions.
+struct ChunkPlan {
+  int P, G, m;
+};
+ChunkPlan chunk_plan(int nmax, int k) {
+  ChunkPlan c;
+  if (nmax <= kCandCap) {  // short rows: every position is a candidate
+    c.P = 64;
+    c.m = 64;
+    c.G = (nmax + 63) / 64;
+    return c;
+  }
+  c.m = k <= 2048 ? 32 : 64;
+  const int gmax = kCandCap / c.m;
+  const int64_t per = ((int64_t)nmax + gmax - 1) / gmax;
+  c.P = (int)((per + 63) / 64 * 64);
+  c.G = (int)(((int64_t)nmax + c.P - 1) / c.P);
+  return c;
+}
+
+int rows_per_score_launch(int Hi, int Di, int B) {
+  const int hp = (Hi + 31) / 32 * 32;
+  int bg = 65536 / (hp * Di);
+  bg = bg < 1 ? 1 : bg;
+  return bg < B ? bg : B;
+}
+
+dsa_status hip_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
+
+dsa_status run_scores(const int8_t* iq, const int8_t* iw, const int8_t* ik, const RowLens& lens,
+                      int B, int Hi, int Di, int64_t N, int nmax, int32_t* scores, bool cand,
+                      const ChunkPlan& cp, uint64_t* cbuf, uint64_t* xbuf, hipStream_t s) {
+  ScoreArgs a;
+  a.iq = iq;
+  a.iw = iw;
+  a.ik = ik;
+  a.scores = scores;
+  a.cand = cbuf;
+  a.xc = xbuf;
+  a.lens = lens;
+  a.N = N;
+  a.nmax = nmax;
+  a.Hi = Hi;
+  a.Di = Di;
+  a.m = cp.m;
+  if (cand) {
+    a.P = cp.P;
+    a.G = cp.G;
+  } else {
+    a.P = (int)((((int64_t)nmax + 64 * 2048 - 1) / (64 * 2048)) * 64);
+    a.G = (int)(((int64_t)nmax + a.P - 1) / a.P);
+  }
+  const int MT = (Hi + 31) / 32, KT = Di / 32;
+  const int bg = rows_per_score_launch(Hi, Di, B);
+  for (int b0 = 0; b0 < B; b0 += bg) {
+    a.b0 = b0;
+    a.Bg = B - b0 < bg ? B - b0 : bg;
+    hipError_t e = launch_score(a, MT, KT, cand, a.G, s);
+    if (e != hipSuccess) return DSA_ERR_HIP;
+  }
+  return DSA_OK;
+}
+
+bool cand_fits(int Hi, int Di, int B, const ChunkPlan& cp, bool fused) {
+  size_t need;
+  if (fused) {
+    const int bg = rows_per_score_launch(Hi, Di, B);
+    need = score_lds_bytes((Hi + 31) / 32, Di / 32, bg, cp.P, true);
+  } else {
+    need = 4096 + (size_t)cp.P * 4;
+  }
+  return need <= (size_t)lds_limit();
+}
+
+AttnArgs attn_args(const void* q, const void* kv, int64_t N, int Hq, int Dk, int Dv, float scale,
+                   int k, uint8_t* w, const Layout& L) {
+  AttnArgs at;
+  at.q = q;
+  at.kv = kv;
+  at.N = N;
+  at.Hq = Hq;
+  at.Dk = Dk;
+  at.Dv = Dv;
+  at.scale = scale;
+  at.part_ml = reinterpret_cast<float2*>(w + L.ml);
+  at.part_o = reinterpret_cast<float*>(w + L.o);
+  at.S = splits_for(k);
+  return at;
+}
+
+SelArgs sel_args(const int32_t* scores, const RowLens& lens, int64_t N, int k, int32_t* idx,
+                 uint8_t* w, const Layout& L, const ChunkPlan& cp, bool have_cand, unsigned flags) {
+  SelArgs a;
+  a.scores = scores;
+  a.cand = reinterpret_cast<const uint64_t*>(w + L.cand);
+  a.xc = reinterpret_cast<const uint64_t*>(w + L.xc);
+  a.idx = idx;
+  a.stats = reinterpret_cast<RowStats*>(w + L.stats);
+  a.sortbuf = reinterpret_cast<uint64_t*>(w + L.sort);
+  a.lens = lens;
+  a.N = N;
+  a.k = k;
+  a.G = cp.G;
+  a.m = cp.m;
+  a.have_cand = have_cand ? 1 : 0;
+  a.force = (flags & DSA_FLAG_FORCE_FALLBACK) ? 1 : 0;
+  a.R = rankers_for(k);
+  return a;
+}
+
+}  // namespace
+}  // namespace dsa
+
+using namespace dsa;
+
+extern "C" {
+
+const char* dsa_status_string(dsa_status status) {
+  switch (status) {
+    case DSA_OK: return "DSA_OK";
+    case DSA_ERR_INVALID_ARG: return "DSA_ERR_INVALID_ARG: an argument is out of range";
+    case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED: shape outside the built kernels";
+    case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE: workspace missing, misaligned or too small";
+    case DSA_ERR_HIP: return "DSA_ERR_HIP: the HIP runtime refused a launch";
+  }
+  return "unknown dsa_status";
+}
+
+size_t dsa_workspace_size(int B, int64_t N, int k, int Hq, int Dv) {
+  if (B < 1 || B > DSA_MAX_BATCH || N < 1 || N > INT32_MAX || k < 1 || k > DSA_MAX_K || Hq < 1 ||
+      Hq > DSA_MAX_ATTN_HEADS || Dv < 1 || Dv > DSA_MAX_ATTN_DIM)
+    return 0;
+  return layout(B, N, k, Hq, Dv).total;
+}
+
+dsa_status dsa_index_scores(const int8_t* iq, const int8_t* iw, const int8_t* ik,
+                            const int32_t* ctx_len, int B, int Hi, int Di, int64_t N,
+                            int32_t* scores, hipStream_t stream) {
+  RowLens lens;
+  int nmax = 0;
+  dsa_status st = check_rows(ctx_len, B, N, &lens, &nmax);
+  if (st != DSA_OK) return st;
+  if ((st = check_index(iq, iw, ik, Hi, Di)) != DSA_OK) return st;
+  if (!scores || !aligned(scores, 4)) return DSA_ERR_INVALID_ARG;
+  ChunkPlan cp{64, 1, 32};
+  return run_scores(iq, iw, ik, lens, B, Hi, Di, N, nmax, scores, false, cp, nullptr, nullptr,
+                    stream);
+}
+
+dsa_status dsa_topk_select(const int32_t* scores, const int32_t* ctx_len, int B, int64_t N, int k,
+                           int32_t* idx, void* ws, size_t ws_bytes, unsigned flags,
+                           hipStream_t stream) {
+  RowLens lens;
+  int nmax = 0;
+  dsa_status st = check_rows(ctx_len, B, N, &lens, &nmax);
+  if (st != DSA_OK) return st;
+  if (!scores || !idx || k < 1 || k > DSA_MAX_K || (flags & ~DSA_FLAG_FORCE_FALLBACK))
+    return DSA_ERR_INVALID_ARG;
+  const Layout L = layout(B, N, k, 1, 1);
+  if ((st = check_ws(ws, ws_bytes, L)) != DSA_OK) return st;
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  const ChunkPlan cp = chunk_plan(nmax, k);
+  const bool have = cand_fits(0, 32, B, cp, false) && !(flags & DSA_FLAG_FORCE_FALLBACK);
+  if (have) {
+    CandArgs ca;
+    ca.scores = scores;
+    ca.cand = reinterpret_cast<uint64_t*>(w + L.cand);
+    ca.xc = reinterpret_cast<uint64_t*>(w + L.xc);
+    ca.lens = lens;
+    ca.N = N;
+    ca.P = cp.P;
+    ca.G = cp.G;
+    ca.m = cp.m;
+    if (launch_chunk_candidates(ca, B, stream) != hipSuccess) return DSA_ERR_HIP;
+  }
+  const SelArgs sa = sel_args(scores, lens, N, k, idx, w, L, cp, have, flags);
+  AttnArgs at{};
+  at.S = 0;
+  return hip_status(launch_select(sa, at, AttnChoice{ATTN_NONE, 0, 0}, B, stream));
+}
+
+dsa_status dsa_sparse_attn(const void* q, const void* kv, const int32_t* idx, int B, int Hq, int Dk,
+                           int Dv, int64_t N, int k, float scale, dsa_dtype dt, float* out,
+                           void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (B < 1 || B > DSA_MAX_BATCH || N < 1 || N > INT32_MAX || k < 1 || k > DSA_MAX_K || !idx || !out)
+    return DSA_ERR_INVALID_ARG;
+  AttnChoice ch;
+  dsa_status st = check_attn(q, kv, Hq, Dk, Dv, scale, dt, &ch);
+  if (st != DSA_OK) return st;
+  const Layout L = layout(B, N, k, Hq, Dv);
+  if ((st = check_ws(ws, ws_bytes, L)) != DSA_OK) return st;
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  const AttnArgs at = attn_args(q, kv, N, Hq, Dk, Dv, scale, k, w, L);
+  int32_t* bad = reinterpret_cast<int32_t*>(w + L.bad);
+  if (launch_attend_idx(idx, k, bad, at, ch, B, stream) != hipSuccess) return DSA_ERR_HIP;
+  return hip_status(
+      launch_combine(at, bad, reinterpret_cast<RowStats*>(w + L.stats), out, B, stream));
+}
+
+dsa_status dsa_decode_step(const int8_t* iq, const int8_t* iw, const int8_t* ik, const void* q,
+                           const void* kv, const int32_t* ctx_len, int B, int Hi, int Di, int Hq,
+                           int Dk, int Dv, int64_t N, int k, float scale, dsa_dtype dt,
+                           int32_t* scores, int32_t* idx, float* out, void* ws, size_t ws_bytes,
+                           unsigned flags, hipStream_t stream) {
+  RowLens lens;
+  int nmax = 0;
+  dsa_status st = check_rows(ctx_len, B, N, &lens, &nmax);
+  if (st != DSA_OK) return st;
+  if ((st = check_index(iq, iw, ik, Hi, Di)) != DSA_OK) return st;
+  if (!scores || !idx || !out || k < 1 || k > DSA_MAX_K || (flags & ~DSA_FLAG_FORCE_FALLBACK))
+    return DSA_ERR_INVALID_ARG;
+  AttnChoice ch;
+  if ((st = check_attn(q, kv, Hq, Dk, Dv, scale, dt, &ch)) != DSA_OK) return st;
+  const Layout L = layout(B, N, k, Hq, Dv);
+  if ((st = check_ws(ws, ws_bytes, L)) != DSA_OK) return st;
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  const ChunkPlan cp = chunk_plan(nmax, k);
+  const bool have = cand_fits(Hi, Di, B, cp, true) && !(flags & DSA_FLAG_FORCE_FALLBACK);
+  st = run_scores(iq, iw, ik, lens, B, Hi, Di, N, nmax, scores, have, cp,
+                  reinterpret_cast<uint64_t*>(w + L.cand), reinterpret_cast<uint64_t*>(w + L.xc),
+                  stream);
+  if (st != DSA_OK) return st;
+  const SelArgs sa = sel_args(scores, lens, N, k, idx, w, L, cp, have, flags);
+  const AttnArgs at = attn_args(q, kv, N, Hq, Dk, Dv, scale, k, w, L);
+  if (launch_select(sa, at, ch, B, stream) != hipSuccess) return DSA_ERR_HIP;
+  return hip_status(launch_combine(at, nullptr, nullptr, out, B, stream));
+}
+
+dsa_status dsa_read_stats(const void* ws, size_t ws_bytes, int B, dsa_row_stats* stats,
+                          hipStream_t stream) {
+  if (!ws || !stats || B < 1 || B > DSA_MAX_BATCH) return DSA_ERR_INVALID_ARG;
+  if (ws_bytes < sizeof(RowStats) * (size_t)B) return DSA_ERR_WORKSPACE;
+  static_assert(sizeof(RowStats) == sizeof(dsa_row_stats), "stats layout");
+  if (hipMemcpyAsync(stats, ws, sizeof(RowStats) * B, hipMemcpyDeviceToHost, stream) != hipSuccess)
+    return DSA_ERR_HIP;
+  return hip_status(hipStreamSynchronize(stream));
+}
+
+}  // extern "C"

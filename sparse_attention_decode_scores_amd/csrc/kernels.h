@@ -1,0 +1,91 @@
+// Internal launch interface between the C API (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace dsa {
+
+__host__ __device__ constexpr size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
+
+struct ScoreArgs {
+  const int8_t* iq;
+  const int8_t* iw;
+  const int8_t* ik;
+  int32_t* scores;
+  uint64_t* cand;  // [B][G][m] best keys per chunk (candidate pass only)
+  uint64_t* xc;    // [B][G] best key left out of each chunk
+  RowLens lens;
+  int64_t N;       // row stride of scores
+  int nmax;        // largest ctx_len: positions at or past it are never scored
+  int b0, Bg;      // this launch scores rows b0 .. b0+Bg-1
+  int Hi, Di;
+  int P;           // positions per chunk (multiple of 64)
+  int G;           // chunks per row
+  int m;           // candidates kept per chunk
+};
+
+hipError_t launch_score(const ScoreArgs& a, int MT, int KT, bool cand, int grid, hipStream_t s);
+size_t score_lds_bytes(int MT, int KT, int Bg, int P, bool cand);
+
+// Stand-alone candidate pass over scores already in memory.
+struct CandArgs {
+  const int32_t* scores;
+  uint64_t* cand;
+  uint64_t* xc;
+  RowLens lens;
+  int64_t N;
+  int P, G, m;
+};
+hipError_t launch_chunk_candidates(const CandArgs& a, int B, hipStream_t s);
+
+// Attention operands.
+struct AttnArgs {
+  const void* q;   // [B][Hq][Dk]
+  const void* kv;  // [N][Dk]
+  int64_t N;
+  int Hq, Dk, Dv;
+  float scale;
+  float2* part_ml;  // [B][S][Hq] running max and sum of each split
+  float* part_o;    // [B][S][Hq][Dv] unnormalised output of each split
+  int S;            // splits per row
+};
+
+enum AttnKind { ATTN_NONE = 0, ATTN_MFMA_BF16 = 1, ATTN_GENERIC_F32 = 2, ATTN_GENERIC_BF16 = 3 };
+
+// Selection stage (+ attention when kind != ATTN_NONE), one launch.
+struct SelArgs {
+  const int32_t* scores;
+  const uint64_t* cand;
+  const uint64_t* xc;
+  int32_t* idx;        // [B][k]
+  RowStats* stats;     // [B]
+  uint64_t* sortbuf;   // [B][2][N] scratch of the exhaustive path
+  RowLens lens;
+  int64_t N;
+  int k;
+  int G, m;            // candidate layout
+  int have_cand;       // 0: the candidate pass did not run (chunks too long)
+  int force;           // DSA_FLAG_FORCE_FALLBACK
+  int R;               // ranking workgroups per row
+};
+
+struct AttnChoice {
+  AttnKind kind;
+  int hqt;   // 16-head tiles (MFMA path)
+  int sb;    // rows staged per sub-block
+};
+
+AttnChoice choose_attn(int dt_bf16, int Hq, int Dk, int Dv);
+// LDS bytes of one workgroup of the selection kernel (largest of the two roles).
+size_t select_lds_bytes(AttnChoice ch, int Hq, int Dk, int k);
+hipError_t launch_select(const SelArgs& a, const AttnArgs& at, AttnChoice ch, int B, hipStream_t s);
+hipError_t launch_attend_idx(const int32_t* idx, int k, int32_t* part_bad, const AttnArgs& at,
+                             AttnChoice ch, int B, hipStream_t s);
+hipError_t launch_combine(const AttnArgs& at, const int32_t* part_bad, RowStats* stats, float* out,
+                          int B, hipStream_t s);
+
+}  // namespace dsa

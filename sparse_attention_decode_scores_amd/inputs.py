@@ -23,8 +23,10 @@ is synthetic with the shapes of the model's DSA layers):
   cfgZ   cfg1 with an all-zero indexer query: every score is 0.
 
 Integer ranges are inclusive. Seeds: numpy PCG64 ``default_rng(1000 + c)`` for
-cfg c, ``2000 + l`` for layer l of cfg2, 1030 for cfg3T, 1090 for cfgZ. Arrays are
-drawn in the order iq, iw, ik, q, kv.
+cfg c, ``2000 + l`` for layer l of cfg2, 1030 for cfg3T, 1090 for cfgZ; the integer
+arrays are drawn from it in the order iq, iw, ik. The normal arrays are drawn in
+blocks of 16,384 rows, block j of q from ``default_rng([seed, 1, j])`` and of kv
+from ``default_rng([seed, 2, j])`` (so they can be drawn on several threads).
 
 bf16 values are carried as uint16 bit patterns (round to nearest even from the
 fp32 draw).
@@ -85,10 +87,28 @@ def ctx_lengths(name):
     return np.full(c["B"], c["N"], np.int32)
 
 
-def _normal(rng, shape, dtype, mul):
-    x = rng.standard_normal(size=shape, dtype=np.float32)
-    if mul != 1.0:
-        x *= np.float32(mul)
+_BLOCK_ROWS = 16384
+
+
+def _normal(seed, tag, shape, dtype, mul):
+    """N(0,1)*mul of the given shape (rows along axis 0), drawn block by block."""
+    shape = tuple(shape)
+    x = np.empty(shape, np.float32)
+    nblk = (shape[0] + _BLOCK_ROWS - 1) // _BLOCK_ROWS
+
+    def fill(j):
+        a, b = j * _BLOCK_ROWS, min(shape[0], (j + 1) * _BLOCK_ROWS)
+        r = np.random.default_rng([seed, tag, j])
+        x[a:b] = r.standard_normal(size=(b - a,) + shape[1:], dtype=np.float32)
+        if mul != 1.0:
+            x[a:b] *= np.float32(mul)
+
+    if nblk > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(min(8, nblk)) as ex:
+            list(ex.map(fill, range(nblk)))
+    else:
+        fill(0)
     return x if dtype == "f32" else f32_to_bf16_bits(x)
 
 
@@ -110,8 +130,9 @@ def make(name, layer=0):
     if c.get("zero_query"):
         iq[...] = 0
     mul = 1.0 if c["dtype"] == "f32" else 0.5
-    q = _normal(rng, (B, Hq, Dk), c["dtype"], mul)
-    kv = _normal(rng, (N, Dk), c["dtype"], mul)
+    seed = c["seed"] + layer
+    q = _normal(seed, 1, (B, Hq, Dk), c["dtype"], mul)
+    kv = _normal(seed, 2, (N, Dk), c["dtype"], mul)
     c.update(iq=iq, iw=iw, ik=np.ascontiguousarray(ik), q=q, kv=kv, ctx_len=ctx_lengths(name),
              name=name, layer=layer)
     return c
@@ -125,8 +146,8 @@ def random_case(seed, B, N, k, Hi, Di, Hq, Dk, Dv, dtype="bf16", ctx_len=None, q
     iw = rng.integers(w_range[0], w_range[1] + 1, size=(B, Hi), dtype=np.int8)
     ik = rng.integers(-key_range, key_range + 1, size=(N, Di), dtype=np.int8)
     mul = 1.0 if dtype == "f32" else 0.5
-    q = _normal(rng, (B, Hq, Dk), dtype, mul)
-    kv = _normal(rng, (N, Dk), dtype, mul)
+    q = _normal(seed, 1, (B, Hq, Dk), dtype, mul)
+    kv = _normal(seed, 2, (N, Dk), dtype, mul)
     if ctx_len is None:
         ctx_len = np.full(B, N, np.int32)
     return dict(B=B, N=N, k=k, Hi=Hi, Di=Di, Hq=Hq, Dk=Dk, Dv=Dv, dtype=dtype,

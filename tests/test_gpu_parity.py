@@ -1,0 +1,265 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Scores and indices must match bit for bit; attention must satisfy
+max|gpu - ref| <= 1e-2 and ||gpu - ref||_2 / ||ref||_2 <= 2e-3 (over every output of
+the case). Full workload sizes are compared element by element: the oracle
+finishes each of them in seconds."""
+import sys
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+from sparse_attention_decode_scores_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS, REL_L2 = 1e-2, 2e-3
+_cache = {}
+
+
+def note(*a):
+    print("[gpu-parity]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch():
+    t = pytest.importorskip("torch")
+    if not t.cuda.is_available():
+        pytest.skip("no GPU")
+    return t
+
+
+@pytest.fixture(scope="module")
+def dsa(torch):
+    from sparse_attention_decode_scores_amd import binding
+    binding.load_library()
+    return binding
+
+
+def dev_inputs(torch, c):
+    d = {}
+    for key in ("iq", "iw", "ik"):
+        d[key] = torch.from_numpy(np.ascontiguousarray(c[key])).cuda()
+    for key in ("q", "kv"):
+        a = np.ascontiguousarray(c[key])
+        if a.dtype == np.uint16:
+            d[key] = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        else:
+            d[key] = torch.from_numpy(a).cuda()
+    return d
+
+
+def case(name, layer=0):
+    key = (name, layer)
+    if key not in _cache:
+        c = inputs.make(name, layer)
+        ref = oracle.decode_step(c["iq"], c["iw"], c["ik"], c["q"], c["kv"], c["ctx_len"], c["k"],
+                                 c["Dv"], c["scale"])
+        if len(_cache) > 3:
+            _cache.clear()
+        _cache[key] = (c, ref)
+    return _cache[key]
+
+
+def check_attention(out, ref, what):
+    out = np.asarray(out, np.float64)
+    err = np.abs(out - ref)
+    rel = np.linalg.norm(out - ref) / max(np.linalg.norm(ref), 1e-300)
+    note("%s: max-abs %.3e rel-l2 %.3e" % (what, err.max(), rel))
+    assert err.max() <= MAX_ABS, what
+    assert rel <= REL_L2, what
+
+
+def check_scores(gpu, ref, ctx_len, what):
+    for b, n in enumerate(ctx_len):
+        assert np.array_equal(gpu[b, :n], ref[b, :n]), "%s row %d scores differ" % (what, b)
+
+
+def run_step(torch, dsa, c, d, flags=0):
+    ws = dsa.new_workspace(c["B"], c["N"], c["k"], c["Hq"], c["Dv"])
+    scores, idx, out = dsa.dsa_decode_step(d["iq"], d["iw"], d["ik"], d["q"], d["kv"], c["ctx_len"],
+                                           c["k"], c["Dv"], c["scale"], workspace=ws, flags=flags)
+    torch.cuda.synchronize()
+    stats = dsa.dsa_read_stats(ws, c["B"])
+    return scores.cpu().numpy(), idx.cpu().numpy(), out.cpu().numpy(), stats
+
+
+def expected_ties(ref_scores, ref_idx, ctx_len, k):
+    t = []
+    for b, n in enumerate(ctx_len):
+        m = min(k, n)
+        sel = ref_scores[b, ref_idx[b, :m]]
+        t.append(int((sel == sel[-1]).sum()))
+    return t
+
+
+@pytest.mark.parametrize("name", ["cfg0", "cfg1", "cfg3", "cfg4", "cfg3T", "cfgZ"])
+def test_decode_step_matches_oracle(torch, dsa, name):
+    note("decode_step", name)
+    c, (rs, ri, ro) = case(name)
+    d = dev_inputs(torch, c)
+    note("running", name, "B=%d N=%d k=%d" % (c["B"], c["N"], c["k"]))
+    s, i, o, stats = run_step(torch, dsa, c, d)
+    check_scores(s, rs, c["ctx_len"], name)
+    assert np.array_equal(i, ri), name + " indices differ"
+    check_attention(o, ro, name)
+    ties = expected_ties(rs, ri, c["ctx_len"], c["k"])
+    for b, st in enumerate(stats):
+        note(name, "row", b, st)
+        assert st["selected"] == min(c["k"], int(c["ctx_len"][b]))
+        assert st["kth_score"] == int(rs[b, ri[b, st["selected"] - 1]])
+        assert st["tied_at_kth"] == ties[b]
+        assert st["path"] == (1 if name == "cfgZ" else 0)
+        if name == "cfgZ":
+            assert st["reason"] == 2
+
+
+def test_cfg2_eleven_layers(torch, dsa):
+    c0 = inputs.make("cfg2", 0)
+    outs, refs = [], []
+    for layer in range(c0["layers"]):
+        note("cfg2 layer", layer)
+        c, (rs, ri, ro) = case("cfg2", layer)
+        d = dev_inputs(torch, c)
+        s, i, o, _ = run_step(torch, dsa, c, d)
+        check_scores(s, rs, c["ctx_len"], "cfg2 layer %d" % layer)
+        assert np.array_equal(i, ri), "cfg2 layer %d indices differ" % layer
+        outs.append(o)
+        refs.append(ro)
+    check_attention(np.stack(outs), np.stack(refs), "cfg2 all layers")
+
+
+@pytest.mark.parametrize("name", ["cfg1", "cfg3T"])
+def test_forced_fallback_is_bit_identical(torch, dsa, name):
+    note("forced fallback", name)
+    c, (rs, ri, ro) = case(name)
+    d = dev_inputs(torch, c)
+    s1, i1, o1, st1 = run_step(torch, dsa, c, d)
+    s2, i2, o2, st2 = run_step(torch, dsa, c, d, flags=dsa.FLAG_FORCE_FALLBACK)
+    assert np.array_equal(i2, ri)
+    assert np.array_equal(i1, i2)
+    assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32)), "attention differs between paths"
+    assert all(st["path"] == 1 and st["reason"] == 1 for st in st2)
+    assert all(st["path"] == 0 for st in st1)
+
+
+def test_runs_are_bit_identical(torch, dsa):
+    c, _ = case("cfg1")
+    d = dev_inputs(torch, c)
+    first = run_step(torch, dsa, c, d)
+    for _ in range(3):
+        again = run_step(torch, dsa, c, d)
+        for a, b in zip(first[:3], again[:3]):
+            assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+# ---------------------------------------------------------------- stand-alone stages
+
+def test_index_scores_standalone(torch, dsa):
+    for name in ("cfg1", "cfg4"):
+        c, (rs, _, _) = case(name)
+        d = dev_inputs(torch, c)
+        note("index_scores", name)
+        s = dsa.dsa_index_scores(d["iq"], d["iw"], d["ik"], c["ctx_len"])
+        torch.cuda.synchronize()
+        check_scores(s.cpu().numpy(), rs, c["ctx_len"], name)
+
+
+def test_scores_past_ctx_len_untouched(torch, dsa):
+    c = inputs.random_case(5, B=2, N=700, k=64, Hi=8, Di=64, Hq=1, Dk=64, Dv=64,
+                           ctx_len=[700, 333])
+    d = dev_inputs(torch, c)
+    s = torch.full((2, 700), -12345, dtype=torch.int32, device="cuda")
+    dsa.dsa_index_scores(d["iq"], d["iw"], d["ik"], c["ctx_len"], scores=s)
+    torch.cuda.synchronize()
+    s = s.cpu().numpy()
+    ref = oracle.index_scores(c["iq"], c["iw"], c["ik"], c["ctx_len"])
+    assert np.array_equal(s[0], ref[0]) and np.array_equal(s[1, :333], ref[1, :333])
+    assert (s[1, 333:] == -12345).all()
+
+
+@pytest.mark.parametrize("name", ["cfg1", "cfg3T", "cfgZ"])
+@pytest.mark.parametrize("flags", [0, 1])
+def test_topk_standalone(torch, dsa, name, flags):
+    c, (rs, ri, _) = case(name)
+    note("topk_select", name, "flags", flags)
+    idx = dsa.dsa_topk_select(torch.from_numpy(rs).cuda(), c["ctx_len"], c["k"], flags=flags)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), ri)
+
+
+def test_topk_heavy_ties_and_short_rows(torch, dsa):
+    rng = np.random.default_rng(77)
+    for N, k, span, ctx in [(20000, 2048, 3, [20000, 15000, 2000, 1]), (9000, 4096, 50, [9000, 9000]),
+                            (300, 256, 1 << 30, [300, 10]), (70000, 1, 5, [70000]),
+                            (150000, 4096, 1 << 20, [150000, 149999])]:
+        B = len(ctx)
+        s = rng.integers(-span, span, size=(B, N)).astype(np.int32)
+        ctx = np.array(ctx, np.int32)
+        ref = oracle.topk_select(s, ctx, k)
+        note("topk random N=%d k=%d span=%d" % (N, k, span))
+        for flags in (0, 1):
+            idx = dsa.dsa_topk_select(torch.from_numpy(s).cuda(), ctx, k, flags=flags)
+            torch.cuda.synchronize()
+            assert np.array_equal(idx.cpu().numpy(), ref), (N, k, span, flags)
+
+
+def test_sparse_attn_standalone_with_skipped_entries(torch, dsa):
+    c, (rs, ri, ro) = case("cfg1")
+    d = dev_inputs(torch, c)
+    note("sparse_attn cfg1")
+    out = dsa.dsa_sparse_attn(d["q"], d["kv"], torch.from_numpy(ri).cuda(), c["Dv"], c["scale"])
+    torch.cuda.synchronize()
+    check_attention(out.cpu().numpy(), ro, "sparse_attn cfg1")
+    # -1 entries are skipped; out-of-range entries are skipped and counted
+    idx = ri.copy()
+    idx[0, 100:300] = -1
+    idx[0, 5] = c["N"] + 3
+    idx[0, 7] = -9
+    ws = dsa.new_workspace(1, c["N"], c["k"], c["Hq"], c["Dv"])
+    out = dsa.dsa_sparse_attn(d["q"], d["kv"], torch.from_numpy(idx).cuda(), c["Dv"], c["scale"],
+                              workspace=ws)
+    torch.cuda.synchronize()
+    valid = idx.copy()
+    valid[0, 5] = -1
+    valid[0, 7] = -1
+    ref = oracle.sparse_attn(c["q"], c["kv"], valid, c["Dv"], c["scale"])
+    check_attention(out.cpu().numpy(), ref, "sparse_attn with skips")
+    assert dsa.dsa_read_stats(ws, 1)[0]["bad_indices"] == 2
+
+
+# ---------------------------------------------------------------- shapes and edge cases
+
+EDGE = [
+    # (label, kwargs for random_case)
+    ("tiny-N1-k1", dict(B=1, N=1, k=1, Hi=4, Di=32, Hq=2, Dk=64, Dv=64)),
+    ("n-below-k", dict(B=1, N=100, k=256, Hi=64, Di=128, Hq=16, Dk=576, Dv=512)),
+    ("ragged-rows", dict(B=3, N=9000, k=2048, Hi=64, Di=128, Hq=16, Dk=576, Dv=512,
+                         ctx_len=[9000, 4500, 7])),
+    ("odd-heads-dims", dict(B=2, N=12345, k=512, Hi=40, Di=96, Hq=20, Dk=192, Dv=128)),
+    ("di-256-k4096", dict(B=1, N=50000, k=4096, Hi=64, Di=256, Hq=64, Dk=576, Dv=512)),
+    ("hq1-small-dk", dict(B=2, N=5000, k=300, Hi=4, Di=32, Hq=1, Dk=64, Dv=64)),
+    ("dk1024-sb32", dict(B=1, N=20000, k=1000, Hi=32, Di=64, Hq=16, Dk=1024, Dv=512)),
+    ("generic-bf16", dict(B=2, N=3000, k=200, Hi=16, Di=64, Hq=6, Dk=80, Dv=40)),
+    ("generic-f32", dict(B=2, N=70000, k=2048, Hi=8, Di=64, Hq=8, Dk=64, Dv=64, dtype="f32")),
+    ("verify-rows", dict(B=8, N=40000, k=2048, Hi=64, Di=128, Hq=16, Dk=576, Dv=512,
+                         ctx_len=[39993 + r for r in range(8)])),
+    ("many-rows", dict(B=16, N=20000, k=2048, Hi=64, Di=128, Hq=16, Dk=576, Dv=512)),
+]
+
+
+@pytest.mark.parametrize("label,kw", EDGE, ids=[e[0] for e in EDGE])
+def test_edge_cases(torch, dsa, label, kw):
+    c = inputs.random_case(zlib.crc32(label.encode()) % 100000, **kw)
+    note("edge", label)
+    rs, ri, ro = oracle.decode_step(c["iq"], c["iw"], c["ik"], c["q"], c["kv"], c["ctx_len"], c["k"],
+                                    c["Dv"], c["scale"])
+    d = dev_inputs(torch, c)
+    for flags in (0, 1):
+        s, i, o, stats = run_step(torch, dsa, c, d, flags)
+        check_scores(s, rs, c["ctx_len"], label)
+        assert np.array_equal(i, ri), "%s indices differ (flags %d)" % (label, flags)
+        check_attention(o, ro, "%s flags %d" % (label, flags))
