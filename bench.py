@@ -1,0 +1,309 @@
+#!/usr/bin/env python3
+"""Benchmark of the DSA decode step (indexer scores -> exact top-k -> sparse attention)
+on one MI355X, through the libdsa C ABI.
+
+One "step" is one decode token through the workload's DSA layers: every stage of
+the path (dsa_decode_step) over one batch of synthetic inputs already resident in
+HBM. Default workload: 300,000 cached positions, k = 2,048, one query row.
+
+Cold cache by construction: the step cycles through --sets independent input sets
+(keys, latent cache, queries), so by the time a set comes back the other sets have
+streamed far more than the 256 MB Infinity Cache holds. The timed steps are HIP
+graph replays (one graph holds one step per set), bracketed by synchronisations.
+A second, eager pass over the same steps records HIP events between the stages
+(dsa_decode_step_timed) to time the dominant kernel, the indexer pass, live.
+
+Prints one JSON line (see the design doc for every field).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "DSA decode step µs & indexer+gather HBM GB/s, top-2048 at 62k/300k ctx"
+HBM_PEAK_GBPS = 8000.0
+SCORE_SOURCES = ["sparse_attention_decode_scores_amd/csrc/score.hip",
+                 "sparse_attention_decode_scores_amd/csrc/common.h",
+                 "sparse_attention_decode_scores_amd/csrc/chunk_select.h"]
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "score_kernel_hbm_counters.json")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def score_kernel_sha():
+    h = hashlib.sha256()
+    for p in SCORE_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def device_set(torch, c, s, name):
+    """Inputs of rotation set s: set 0 from the shared generator, later sets drawn on the
+    GPU with the same distributions (torch generator seeded 9000 + s)."""
+    from sparse_attention_decode_scores_amd import inputs
+    dev = torch.device("cuda")
+    if s == 0:
+        d = {}
+        for key in ("iq", "iw", "ik"):
+            d[key] = torch.from_numpy(np.ascontiguousarray(c[key])).to(dev)
+        for key in ("q", "kv"):
+            a = np.ascontiguousarray(c[key])
+            d[key] = (torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if a.dtype == np.uint16
+                      else torch.from_numpy(a)).to(dev)
+        return d
+    g = torch.Generator(device=dev)
+    g.manual_seed(9000 + 100 * s + c.get("layer", 0))
+    qr, kr = c["qk_range"], c["key_range"]
+    w0, w1 = c["w_range"]
+    d = {
+        "iq": torch.randint(-qr, qr + 1, (c["B"], c["Hi"], c["Di"]), dtype=torch.int8, device=dev, generator=g),
+        "iw": torch.randint(w0, w1 + 1, (c["B"], c["Hi"]), dtype=torch.int8, device=dev, generator=g),
+        "ik": torch.randint(-kr, kr + 1, (c["N"], c["Di"]), dtype=torch.int8, device=dev, generator=g),
+    }
+    mul = 1.0 if c["dtype"] == "f32" else 0.5
+    for key, shape in (("q", (c["B"], c["Hq"], c["Dk"])), ("kv", (c["N"], c["Dk"]))):
+        x = torch.randn(shape, dtype=torch.float32, device=dev, generator=g) * mul
+        d[key] = x if c["dtype"] == "f32" else x.to(torch.bfloat16)
+    return d
+
+
+def essential_bytes(c):
+    """Algorithmic HBM bytes of one layer: every indexer key once, the scores written,
+    the k gathered latent rows, queries, weights and the output."""
+    B, N, Di, Dk, Dv, Hq, Hi, k = (c[x] for x in ("B", "N", "Di", "Dk", "Dv", "Hq", "Hi", "k"))
+    esz = 4 if c["dtype"] == "f32" else 2
+    keys = N * Di
+    scores = B * N * 4
+    gather = sum(min(k, int(n)) for n in c["ctx_len"]) * Dk * esz
+    small = B * Hi * Di + B * Hi + B * Hq * Dk * esz + B * Hq * Dv * 4 + B * k * 4
+    return keys, scores, gather, small
+
+
+def score_kernel_bytes(c):
+    """Algorithmic bytes of one launch of the indexer pass: keys read once, queries and
+    weights, scores written (the per-position figure is Di + 4*B bytes)."""
+    return c["N"] * c["Di"] + c["B"] * c["N"] * 4 + c["B"] * c["Hi"] * (c["Di"] + 1)
+
+
+def cpu_baseline(cfg_name, layers, budget_s):
+    import oracle
+    from sparse_attention_decode_scores_amd import inputs
+    runs, spent, per_layer = 0, 0.0, []
+    layer = 0
+    while True:
+        c = inputs.make(cfg_name, layer % layers)
+        t = time.perf_counter()
+        oracle.decode_step(c["iq"], c["iw"], c["ik"], c["q"], c["kv"], c["ctx_len"], c["k"], c["Dv"],
+                           c["scale"])
+        dt = time.perf_counter() - t
+        per_layer.append(dt)
+        spent += dt
+        runs += 1
+        layer += 1
+        if spent >= budget_s or runs >= 50:
+            break
+    us_step = float(np.mean(per_layer)) * layers * 1e6
+    sample = ("%d oracle decode-step call(s) on layer input(s) of %s (%d positions, k=%d), "
+              "%.1f s of CPU work; step = %d layer(s) x mean per-layer time"
+              % (runs, cfg_name, c["N"], c["k"], spent, layers))
+    return {"value": us_step, "unit": "us", "cores": 1, "kind": "oracle", "sample": sample}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=240)
+    ap.add_argument("--warmup", type=int, default=24)
+    ap.add_argument("--config", default="cfg3", choices=["cfg1", "cfg2", "cfg3", "cfg4"])
+    ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = default per workload)")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy (scale reference for HBM counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the design for "
+              "position-sharding over RCCL is described in DESIGN.md). Run with --gpus 1.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    from sparse_attention_decode_scores_amd import binding, inputs
+
+    binding.load_library()
+    torch.cuda.set_device(0)
+    cfg = inputs.CONFIGS[args.config]
+    layers = cfg["layers"]
+    R = args.sets or (1 if layers > 1 else 12)
+    log("workload", args.config, "layers", layers, "sets", R)
+
+    # inputs: [set][layer]
+    host = [inputs.make(args.config, l) for l in range(layers)]
+    sets = []
+    for s in range(R):
+        sets.append([device_set(torch, host[l], s, args.config) for l in range(layers)])
+    c = host[0]
+    B, N, k, Hq, Dv = c["B"], c["N"], c["k"], c["Hq"], c["Dv"]
+    ws = binding.new_workspace(B, N, k, Hq, Dv)
+    scores = torch.zeros((B, N), dtype=torch.int32, device="cuda")
+    idx = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    out = torch.empty((B, Hq, Dv), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    log("inputs resident: %.2f GB" % (torch.cuda.memory_allocated() / 1e9))
+
+    def step(s, stage_events=None):
+        for l in range(layers):
+            d = sets[s][l]
+            ev = None if stage_events is None else stage_events[l]
+            binding.dsa_decode_step(d["iq"], d["iw"], d["ik"], d["q"], d["kv"], host[l]["ctx_len"], k,
+                                    Dv, c["scale"], scores=scores, idx=idx, out=out, workspace=ws,
+                                    stage_events=ev)
+
+    for i in range(args.warmup):
+        step(i % R)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    graphs = []
+    if not args.no_graph:
+        stream = torch.cuda.Stream()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            full = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(full, stream=stream):
+                for s in range(R):
+                    step(s)
+            tail = None
+            if K % R:
+                tail = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(tail, stream=stream):
+                    for s in range(K % R):
+                        step(s)
+        torch.cuda.synchronize()
+        full.replay()
+        if tail is not None:
+            tail.replay()
+        torch.cuda.synchronize()
+        graphs = [full] * (K // R) + ([tail] if tail is not None else [])
+
+    # ---- timed region: K steps
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    if graphs:
+        for g in graphs:
+            g.replay()
+    else:
+        for i in range(K):
+            step(i % R)
+    e1.record()
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t0
+    gpu_ms = e0.elapsed_time(e1)
+    us_step = wall_s * 1e6 / K
+    log("timed %d steps: wall %.3f ms, events %.3f ms -> %.2f us/step" % (K, wall_s * 1e3, gpu_ms, us_step))
+
+    # ---- stage timing pass (eager, events between the stages)
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(layers)]
+           for _ in range(K)]
+    for per_step in evs:  # torch creates the HIP event on first record
+        for per_layer in per_step:
+            for e in per_layer:
+                e.record()
+    torch.cuda.synchronize()
+    for i in range(K):
+        step(i % R, evs[i])
+    torch.cuda.synchronize()
+    st = np.array([[[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
+                    for e in per_step] for per_step in evs]) * 1e3  # us [K][layers][3]
+    score_us = float(st[:, :, 0].mean())
+    select_us = float(st[:, :, 1].mean())
+    combine_us = float(st[:, :, 2].mean())
+    log("stage events (eager): score %.2f us, select+attend %.2f us, combine %.2f us"
+        % (score_us, select_us, combine_us))
+    stats = binding.dsa_read_stats(ws, B)
+
+    if args.copy_calibration:
+        src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 5 x 256 MiB device copies")
+
+    kb = score_kernel_bytes(c)
+    achieved = kb / (score_us * 1e-6) / 1e9
+    traffic = None
+    if os.path.exists(PMC_SUMMARY):
+        with open(PMC_SUMMARY) as f:
+            pmc = json.load(f)
+        if pmc.get("kernel_source_sha") == score_kernel_sha() and pmc.get("config") == args.config:
+            traffic = pmc.get("hbm_bytes_per_launch")
+    keys, sc_bytes, gather, small = essential_bytes(c)
+    step_bytes = layers * (keys + sc_bytes + gather + small)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline: timing the oracle for about %.0f s" % args.cpu_seconds)
+        cpu = cpu_baseline(args.config, layers, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(us_step, 3),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(us_step / 1e3, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8 indexer (int32 accumulate) + bf16 attention (fp32 accumulate)",
+        "data": "synthetic (seeded; no model weights or caches)",
+        "config": {
+            "workload": "%s: %d cached positions, k=%d, %d query row(s), %d layer(s)/step; indexer "
+                        "%d heads x %d int8, one shared key per position; attention %d heads over a "
+                        "%d-value bf16 latent row (%d output values)"
+                        % (args.config, N, k, B, layers, c["Hi"], c["Di"], Hq, c["Dk"], Dv),
+            "cache": "cold: %d rotating input sets of %.0f MB each" % (R, layers * (keys + N * c["Dk"] * 2) / 1e6)
+                     if R > 1 else "cold: %d layers x %.0f MB streamed per step" % (layers, (keys + N * c["Dk"] * 2) / 1e6),
+            "launch": "HIP graph replay of %d step(s) per graph" % R if graphs else "eager launches",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "indexer score pass (k_score, int8 MFMA + per-chunk candidates)",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": kb,
+            "launch_us": round(score_us, 3),
+        },
+        "cpu_baseline": cpu,
+        "stages_us_eager_events": {"score": round(score_us, 3), "select_attend": round(select_us, 3),
+                                   "combine": round(combine_us, 3)},
+        "step_essential_bytes": step_bytes,
+        "step_essential_GBps": round(step_bytes / (us_step * 1e-6) / 1e9, 1),
+        "selection_paths": [s["path"] for s in stats],
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -164,6 +164,21 @@ dsa_status dsa_decode_step(const int8_t* iq, const int8_t* iw, const int8_t* ik,
                            size_t ws_bytes, unsigned flags, hipStream_t stream);
 
 /*
+ * dsa_decode_step with stage timing: when stage_events is not NULL it must point
+ * to 4 events created on the current device; they are recorded on `stream`
+ * before stage 1, after stage 1, after stage 2 (selection and the attention
+ * splits share one launch) and after the final combine. Everything else is as
+ * for dsa_decode_step, which is this call with stage_events = NULL. For
+ * profilers and benchmarks; the events add a few queue packets per step.
+ */
+dsa_status dsa_decode_step_timed(const int8_t* iq, const int8_t* iw, const int8_t* ik,
+                                 const void* q, const void* kv, const int32_t* ctx_len, int B,
+                                 int Hi, int Di, int Hq, int Dk, int Dv, int64_t N, int k,
+                                 float scale, dsa_dtype dt, int32_t* scores, int32_t* idx,
+                                 float* out, void* ws, size_t ws_bytes, unsigned flags,
+                                 hipStream_t stream, hipEvent_t* stage_events);
+
+/*
  * Copies the per-row stats of the last call that used `ws` into stats[0..B).
  * Synchronises `stream` (call it outside timed regions).
  */

@@ -20,7 +20,7 @@ DSA_F32, DSA_BF16 = 0, 1
 STATUS_NAMES = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED",
                 3: "DSA_ERR_WORKSPACE", 4: "DSA_ERR_HIP"}
 EXPORTED = ("dsa_status_string", "dsa_workspace_size", "dsa_index_scores", "dsa_topk_select",
-            "dsa_sparse_attn", "dsa_decode_step", "dsa_read_stats")
+            "dsa_sparse_attn", "dsa_decode_step", "dsa_decode_step_timed", "dsa_read_stats")
 
 
 class DSAError(RuntimeError):
@@ -63,6 +63,7 @@ def load_library():
         lib.dsa_sparse_attn.argtypes = [p, p, p, i32, i32, i32, i32, i64, i32, f32, i32, p, p, sz, p]
         lib.dsa_decode_step.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i64, i32,
                                         f32, i32, p, p, p, p, sz, u32, p]
+        lib.dsa_decode_step_timed.argtypes = lib.dsa_decode_step.argtypes + [p]
         lib.dsa_read_stats.argtypes = [p, sz, i32, p, p]
         for name in EXPORTED[2:]:
             getattr(lib, name).restype = i32
@@ -189,8 +190,12 @@ def dsa_sparse_attn(q, kv, idx, Dv, scale, out=None, workspace=None, stream=None
 
 
 def dsa_decode_step(iq, iw, ik, q, kv, ctx_len, k, Dv, scale, scores=None, idx=None, out=None,
-                    workspace=None, flags=0, stream=None):
-    """The three stages through one layer; returns (scores, idx, out)."""
+                    workspace=None, flags=0, stream=None, stage_events=None):
+    """The three stages through one layer; returns (scores, idx, out).
+
+    stage_events: optional sequence of 4 torch.cuda.Event(enable_timing=True), recorded
+    on the stream before stage 1, after stage 1, after stage 2 and at the end
+    (dsa_decode_step_timed)."""
     torch = _torch()
     lib = load_library()
     B, Hi, Di = iq.shape
@@ -209,13 +214,19 @@ def dsa_decode_step(iq, iw, ik, q, kv, ctx_len, k, Dv, scale, scores=None, idx=N
         out = torch.empty((B, Hq, Dv), dtype=torch.float32, device=dev)
     if workspace is None:
         workspace = new_workspace(B, N, k, Hq, Dv, dev)
-    rc = lib.dsa_decode_step(_dev(iq, "iq", torch.int8), _dev(iw, "iw", torch.int8),
-                             _dev(ik, "ik", torch.int8), _dev(q, "q"), _dev(kv, "kv"),
-                             lens.ctypes.data_as(ctypes.c_void_p), B, Hi, Di, Hq, Dk, Dv, N, k,
-                             float(scale), dt, _dev(scores, "scores", torch.int32),
-                             _dev(idx, "idx", torch.int32), _dev(out, "out", torch.float32),
-                             _dev(workspace, "workspace"),
-                             workspace.numel() * workspace.element_size(), flags, _stream(stream))
+    args = [_dev(iq, "iq", torch.int8), _dev(iw, "iw", torch.int8), _dev(ik, "ik", torch.int8),
+            _dev(q, "q"), _dev(kv, "kv"), lens.ctypes.data_as(ctypes.c_void_p), B, Hi, Di, Hq, Dk,
+            Dv, N, k, float(scale), dt, _dev(scores, "scores", torch.int32),
+            _dev(idx, "idx", torch.int32), _dev(out, "out", torch.float32),
+            _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), flags,
+            _stream(stream)]
+    if stage_events is None:
+        rc = lib.dsa_decode_step(*args)
+    else:
+        if len(stage_events) != 4:
+            raise ValueError("stage_events must hold 4 events")
+        evs = (ctypes.c_void_p * 4)(*[e.cuda_event for e in stage_events])
+        rc = lib.dsa_decode_step_timed(*args, ctypes.cast(evs, ctypes.c_void_p))
     _check(rc, "dsa_decode_step")
     return scores, idx, out
 

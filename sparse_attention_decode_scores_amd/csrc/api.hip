@@ -36,7 +36,7 @@ Layout layout(int B, int64_t N, int k, int Hq, int Dv) {
   L.xc = L.cand + up((size_t)B * kCandCap * 8);
   L.ml = L.xc + up((size_t)B * kMaxChunks * 8);
   L.o = L.ml + up((size_t)B * S * Hq * 8);
-  L.bad = L.o + up((size_t)B * S * Hq * Dv * 4);
+  L.bad = L.o + up((size_t)B * S * ((Hq + 15) / 16 * 16) * Dv * 4);
   L.sort = L.bad + up((size_t)B * S * 4);
   L.total = L.sort + up((size_t)B * 2 * (size_t)N * 8);
   return L;
@@ -170,10 +170,12 @@ dsa_status run_scores(const int8_t* iq, const int8_t* iw, const int8_t* ik, cons
 bool cand_fits(int Hi, int Di, int B, const ChunkPlan& cp, bool fused) {
   size_t need;
   if (fused) {
+    if (cp.P > score_max_chunk()) return false;
     const int bg = rows_per_score_launch(Hi, Di, B);
     need = score_lds_bytes((Hi + 31) / 32, Di / 32, bg, cp.P, true);
   } else {
-    need = 4096 + (size_t)cp.P * 4;
+    if (cp.P > chunk_cand_max_chunk()) return false;
+    need = 8192 + (size_t)cp.P * 4;
   }
   return need <= (size_t)lds_limit();
 }
@@ -191,6 +193,7 @@ AttnArgs attn_args(const void* q, const void* kv, int64_t N, int Hq, int Dk, int
   at.part_ml = reinterpret_cast<float2*>(w + L.ml);
   at.part_o = reinterpret_cast<float*>(w + L.o);
   at.S = splits_for(k);
+  at.frag = 0;
   return at;
 }
 
@@ -296,18 +299,20 @@ dsa_status dsa_sparse_attn(const void* q, const void* kv, const int32_t* idx, in
   const Layout L = layout(B, N, k, Hq, Dv);
   if ((st = check_ws(ws, ws_bytes, L)) != DSA_OK) return st;
   uint8_t* w = static_cast<uint8_t*>(ws);
-  const AttnArgs at = attn_args(q, kv, N, Hq, Dk, Dv, scale, k, w, L);
+  AttnArgs at = attn_args(q, kv, N, Hq, Dk, Dv, scale, k, w, L);
+  at.frag = ch.kind == ATTN_MFMA_BF16;
   int32_t* bad = reinterpret_cast<int32_t*>(w + L.bad);
   if (launch_attend_idx(idx, k, bad, at, ch, B, stream) != hipSuccess) return DSA_ERR_HIP;
   return hip_status(
       launch_combine(at, bad, reinterpret_cast<RowStats*>(w + L.stats), out, B, stream));
 }
 
-dsa_status dsa_decode_step(const int8_t* iq, const int8_t* iw, const int8_t* ik, const void* q,
-                           const void* kv, const int32_t* ctx_len, int B, int Hi, int Di, int Hq,
-                           int Dk, int Dv, int64_t N, int k, float scale, dsa_dtype dt,
-                           int32_t* scores, int32_t* idx, float* out, void* ws, size_t ws_bytes,
-                           unsigned flags, hipStream_t stream) {
+dsa_status dsa_decode_step_timed(const int8_t* iq, const int8_t* iw, const int8_t* ik,
+                                 const void* q, const void* kv, const int32_t* ctx_len, int B,
+                                 int Hi, int Di, int Hq, int Dk, int Dv, int64_t N, int k,
+                                 float scale, dsa_dtype dt, int32_t* scores, int32_t* idx,
+                                 float* out, void* ws, size_t ws_bytes, unsigned flags,
+                                 hipStream_t stream, hipEvent_t* stage_events) {
   RowLens lens;
   int nmax = 0;
   dsa_status st = check_rows(ctx_len, B, N, &lens, &nmax);
@@ -319,17 +324,37 @@ dsa_status dsa_decode_step(const int8_t* iq, const int8_t* iw, const int8_t* ik,
   if ((st = check_attn(q, kv, Hq, Dk, Dv, scale, dt, &ch)) != DSA_OK) return st;
   const Layout L = layout(B, N, k, Hq, Dv);
   if ((st = check_ws(ws, ws_bytes, L)) != DSA_OK) return st;
+  if (stage_events != nullptr)
+    for (int i = 0; i < 4; ++i)
+      if (stage_events[i] == nullptr) return DSA_ERR_INVALID_ARG;
+  auto mark = [&](int i) {
+    return stage_events == nullptr || hipEventRecord(stage_events[i], stream) == hipSuccess;
+  };
   uint8_t* w = static_cast<uint8_t*>(ws);
   const ChunkPlan cp = chunk_plan(nmax, k);
   const bool have = cand_fits(Hi, Di, B, cp, true) && !(flags & DSA_FLAG_FORCE_FALLBACK);
+  if (!mark(0)) return DSA_ERR_HIP;
   st = run_scores(iq, iw, ik, lens, B, Hi, Di, N, nmax, scores, have, cp,
                   reinterpret_cast<uint64_t*>(w + L.cand), reinterpret_cast<uint64_t*>(w + L.xc),
                   stream);
   if (st != DSA_OK) return st;
+  if (!mark(1)) return DSA_ERR_HIP;
   const SelArgs sa = sel_args(scores, lens, N, k, idx, w, L, cp, have, flags);
-  const AttnArgs at = attn_args(q, kv, N, Hq, Dk, Dv, scale, k, w, L);
+  AttnArgs at = attn_args(q, kv, N, Hq, Dk, Dv, scale, k, w, L);
+  at.frag = ch.kind == ATTN_MFMA_BF16;
   if (launch_select(sa, at, ch, B, stream) != hipSuccess) return DSA_ERR_HIP;
-  return hip_status(launch_combine(at, nullptr, nullptr, out, B, stream));
+  if (!mark(2)) return DSA_ERR_HIP;
+  if (launch_combine(at, nullptr, nullptr, out, B, stream) != hipSuccess) return DSA_ERR_HIP;
+  return mark(3) ? DSA_OK : DSA_ERR_HIP;
+}
+
+dsa_status dsa_decode_step(const int8_t* iq, const int8_t* iw, const int8_t* ik, const void* q,
+                           const void* kv, const int32_t* ctx_len, int B, int Hi, int Di, int Hq,
+                           int Dk, int Dv, int64_t N, int k, float scale, dsa_dtype dt,
+                           int32_t* scores, int32_t* idx, float* out, void* ws, size_t ws_bytes,
+                           unsigned flags, hipStream_t stream) {
+  return dsa_decode_step_timed(iq, iw, ik, q, kv, ctx_len, B, Hi, Di, Hq, Dk, Dv, N, k, scale, dt,
+                               scores, idx, out, ws, ws_bytes, flags, stream, nullptr);
 }
 
 dsa_status dsa_read_stats(const void* ws, size_t ws_bytes, int B, dsa_row_stats* stats,

@@ -16,30 +16,22 @@
 
 namespace dsa {
 
-__device__ __forceinline__ float wave_max_f(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
-__device__ __forceinline__ float wave_sum_f(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
+constexpr int kAttnBlock = 512;
+constexpr int kAttnWaves = kAttnBlock / 64;
 
-// Online-softmax bookkeeping of one sub-block: wave w updates heads w, w+4, ...;
+// Online-softmax bookkeeping of one sub-block: wave w updates heads w, w+8, ...;
 // lane r is row r of the sub-block (sb <= 64). lg[h][r] holds scaled logits
 // (-inf for absent rows) and is overwritten with exp(logit - new max).
 __device__ __forceinline__ void softmax_update(float* lg, int sb, int nheads, float* mrun,
                                                float* lrun, float* alpha) {
   const int lane = lane_id();
-  for (int h = wave_id(); h < nheads; h += kWaves) {
+  for (int h = wave_id(); h < nheads; h += kAttnWaves) {
     const float v = lane < sb ? lg[h * sb + lane] : -INFINITY;
     const float mo = mrun[h];
-    const float mn = fmaxf(mo, wave_max_f(v));
+    const float mn = fmaxf(mo, wave_reduce_max_f(v));
     const float p = v == -INFINITY ? 0.f : __expf(v - mn);
     if (lane < sb) lg[h * sb + lane] = p;
-    const float sum = wave_sum_f(p);
+    const float sum = wave_reduce_sum_f(p);
     if (lane == 0) {
       const float a = mo == -INFINITY ? 0.f : __expf(mo - mn);
       lrun[h] = lrun[h] * a + sum;
@@ -53,15 +45,34 @@ __device__ __forceinline__ void softmax_update(float* lg, int sb, int nheads, fl
 // 16 heads per tile as the A operand and 16 staged rows per tile as the B
 // operand; output = P V with P split into two bf16 terms (high part exact,
 // remainder rounded) so the probabilities keep ~16 bits. Needs Dk % 32 == 0,
-// Dv % 64 == 0, Dv <= 512, Hq <= 16 * HQT.
+// Dv % 16 == 0, Dv <= 512, Hq <= 16 * HQT, (Dk / 8) * SB <= 16 * block size.
 template <int HQT, int SB>
 struct AttnMfma {
   static constexpr int HP = 16 * HQT;
-  static constexpr int kMaxTilesPerWave = 8;  // Dv <= 512
+  static constexpr int kMaxTilesPerWave = 32 / kAttnWaves;  // Dv <= 512
+  static constexpr int kMaxLoads = 16;                      // 16-byte loads per thread per sub-block
+  static constexpr bool kQInLds = HQT == 1;                 // query heads staged in LDS
   __host__ __device__ static int row_bytes(int Dk) { return Dk * 2 + 16; }
+  __host__ __device__ static size_t q_bytes(int Dk) {
+    return kQInLds ? align16((size_t)HP * row_bytes(Dk)) : 0;
+  }
   __host__ __device__ static size_t lds_bytes(int Hq, int Dk) {
     (void)Hq;
-    return align16((size_t)SB * row_bytes(Dk)) + (size_t)HP * SB * 4 + 3 * HP * 4;
+    return q_bytes(Dk) + align16((size_t)SB * row_bytes(Dk)) + (size_t)HP * SB * 4 + 3 * HP * 4;
+  }
+
+  // Starts copying the row's query heads into LDS (zero rows for padded heads);
+  // call before other work so the loads overlap it. Visible after the next barrier.
+  __device__ static void prefetch(const AttnArgs& p, int b, uint8_t* work) {
+    if (!kQInLds) return;
+    const int Dk = p.Dk, rb = row_bytes(Dk), cpr = Dk >> 3;
+    const uint8_t* q = reinterpret_cast<const uint8_t*>(p.q) + (int64_t)b * p.Hq * Dk * 2;
+    for (int i = threadIdx.x; i < HP * cpr; i += kAttnBlock) {
+      const int h = i / cpr, c = i - h * cpr;
+      v4i v = {0, 0, 0, 0};
+      if (h < p.Hq) v = *(const v4i*)(q + ((int64_t)h * Dk + 8 * c) * 2);
+      *(v4i*)(work + h * rb + 16 * c) = v;
+    }
   }
 
   template <typename PosAt>
@@ -69,9 +80,10 @@ struct AttnMfma {
                              uint8_t* work) {
     const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
     const int Dk = p.Dk, Dv = p.Dv, KS = Dk >> 5, rb = row_bytes(Dk);
-    const int ntw = Dv >> 6;  // 16-wide output tiles per wave
-    uint8_t* rows = work;
-    float* lg = reinterpret_cast<float*>(work + align16((size_t)SB * rb));
+    const int nt_all = Dv >> 4;  // 16-wide output tiles
+    const uint8_t* qs = work;
+    uint8_t* rows = work + q_bytes(Dk);
+    float* lg = reinterpret_cast<float*>(rows + align16((size_t)SB * rb));
     float* mrun = lg + HP * SB;
     float* lrun = mrun + HP;
     float* alpha = lrun + HP;
@@ -83,40 +95,66 @@ struct AttnMfma {
     for (int mt = 0; mt < HQT; ++mt)
 #pragma unroll
       for (int j = 0; j < kMaxTilesPerWave; ++j) o[mt][j] = v4f{0.f, 0.f, 0.f, 0.f};
-    for (int h = tid; h < HP; h += kBlock) {
+    for (int h = tid; h < HP; h += kAttnBlock) {
       mrun[h] = -INFINITY;
       lrun[h] = 0.f;
     }
 
     for (int s0 = 0; s0 < cnt; s0 += SB) {
       const int nr = cnt - s0 < SB ? cnt - s0 : SB;
-      // gather the sub-block's rows with 16-byte loads
+      // gather the sub-block's rows with 16-byte loads, all issued before any store
       const int cpr = Dk >> 3;
-      for (int i = tid; i < SB * cpr; i += kBlock) {
+      v4i buf[kMaxLoads];
+#pragma unroll
+      for (int j = 0; j < kMaxLoads; ++j) {
+        const int i = tid + kAttnBlock * j;
         const int r = i / cpr, c = i - r * cpr;
-        v4i v = {0, 0, 0, 0};
-        if (r < nr) {
+        buf[j] = v4i{0, 0, 0, 0};
+        if (i < SB * cpr && r < nr) {
           const int64_t pos = pos_at(s0 + r);
-          v = *(const v4i*)(kv + (pos * Dk + 8 * c) * 2);
+          buf[j] = *(const v4i*)(kv + (pos * Dk + 8 * c) * 2);
         }
-        *(v4i*)(rows + r * rb + 16 * c) = v;
       }
-      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < kMaxLoads; ++j) {
+        const int i = tid + kAttnBlock * j;
+        const int r = i / cpr, c = i - r * cpr;
+        if (i < SB * cpr) *(v4i*)(rows + r * rb + 16 * c) = buf[j];
+      }
+      lds_barrier();
+      DSA_MARK(1, 6);
       // logits: D[head][row], head = 16*mt + 4*(l/16) + r, row = 16*nt + l%16
-      for (int nt = wave; nt < SB / 16; nt += kWaves) {
+      for (int nt = wave; nt < SB / 16; nt += kAttnWaves) {
         v4f acc[HQT];
 #pragma unroll
         for (int mt = 0; mt < HQT; ++mt) acc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
         const uint8_t* rrow = rows + (16 * nt + (lane & 15)) * rb + 16 * (lane >> 4);
-        for (int kk = 0; kk < KS; ++kk) {
-          const v8bf bfr = *(const v8bf*)(rrow + 64 * kk);
+        const int h_a = lane & 15;
+        auto afrag = [&](int mt, int kk) {
+          v8bf afr = {};
+          if (kQInLds)
+            afr = *(const v8bf*)(qs + (16 * mt + h_a) * rb + 64 * kk + 16 * (lane >> 4));
+          else if (16 * mt + h_a < p.Hq)
+            afr = *(const v8bf*)(q + (int64_t)(16 * mt + h_a) * Dk + 32 * kk + 8 * (lane >> 4));
+          return afr;
+        };
+        // fragments of k-step kk+1 are loaded while k-step kk runs on the matrix cores
+        v8bf bcur = *(const v8bf*)(rrow);
+        v8bf acur[HQT];
 #pragma unroll
-          for (int mt = 0; mt < HQT; ++mt) {
-            const int h = 16 * mt + (lane & 15);
-            v8bf afr = {};
-            if (h < p.Hq) afr = *(const v8bf*)(q + (int64_t)h * Dk + 32 * kk + 8 * (lane >> 4));
-            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr, acc[mt], 0, 0, 0);
-          }
+        for (int mt = 0; mt < HQT; ++mt) acur[mt] = afrag(mt, 0);
+        for (int kk = 0; kk < KS; ++kk) {
+          const int kn = kk + 1 < KS ? kk + 1 : kk;
+          const v8bf bnext = *(const v8bf*)(rrow + 64 * kn);
+          v8bf anext[HQT];
+#pragma unroll
+          for (int mt = 0; mt < HQT; ++mt) anext[mt] = afrag(mt, kn);
+#pragma unroll
+          for (int mt = 0; mt < HQT; ++mt)
+            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(acur[mt], bcur, acc[mt], 0, 0, 0);
+          bcur = bnext;
+#pragma unroll
+          for (int mt = 0; mt < HQT; ++mt) acur[mt] = anext[mt];
         }
         const int row = 16 * nt + (lane & 15);
 #pragma unroll
@@ -126,9 +164,11 @@ struct AttnMfma {
             lg[(16 * mt + 4 * (lane >> 4) + r) * SB + row] =
                 row < nr ? acc[mt][r] * p.scale : -INFINITY;
       }
-      __syncthreads();
+      lds_barrier();
+      DSA_MARK(1, 7);
       softmax_update(lg, SB, HP, mrun, lrun, alpha);
-      __syncthreads();
+      lds_barrier();
+      DSA_MARK(1, 8);
       // output: D[head][dv] += P[head][row] V[row][dv]
 #pragma unroll
       for (int mt = 0; mt < HQT; ++mt)
@@ -137,29 +177,39 @@ struct AttnMfma {
           const float a = alpha[16 * mt + 4 * (lane >> 4) + r];
 #pragma unroll
           for (int j = 0; j < kMaxTilesPerWave; ++j)
-            if (j < ntw) o[mt][j][r] *= a;
+            if (wave + kAttnWaves * j < nt_all) o[mt][j][r] *= a;
         }
       for (int kk = 0; kk < SB / 32; ++kk) {
         v8bf ahi[HQT], alo[HQT];
 #pragma unroll
         for (int mt = 0; mt < HQT; ++mt) {
           const float* pp = lg + (16 * mt + (lane & 15)) * SB + 32 * kk + 8 * (lane >> 4);
+          const v4f p0 = *(const v4f*)pp, p1 = *(const v4f*)(pp + 4);
 #pragma unroll
           for (int t = 0; t < 8; ++t) {
-            const float pv = pp[t];
+            const float pv = t < 4 ? p0[t] : p1[t - 4];
             const float hi = __uint_as_float(__float_as_uint(pv) & 0xFFFF0000u);
             ahi[mt][t] = (__bf16)hi;
             alo[mt][t] = (__bf16)(pv - hi);
           }
         }
+        // B fragment: V[rows 32*kk + 8*(l/16) + t][dv 16*nt + l%16], t < 8, read with two
+        // transposing LDS loads: lane j of each 16-lane group names the 4-value chunk
+        // (row base + j/4, columns 4*(j%4)..+3) and receives column j of the 4 rows.
+        const int tr_row = 32 * kk + 8 * (lane >> 4) + ((lane & 15) >> 2);
+        const int tr_col = 4 * (lane & 3);
 #pragma unroll
         for (int j = 0; j < kMaxTilesPerWave; ++j) {
-          if (j >= ntw) break;
-          const int nt = wave + kWaves * j;
-          const uint8_t* vb = rows + (32 * kk + 8 * (lane >> 4)) * rb + (16 * nt + (lane & 15)) * 2;
-          v8bf bfr;
-#pragma unroll
-          for (int t = 0; t < 8; ++t) bfr[t] = *(const __bf16*)(vb + t * rb);
+          const int nt = wave + kAttnWaves * j;
+          if (nt >= nt_all) break;
+          const uint8_t* va = rows + tr_row * rb + (16 * nt + tr_col) * 2;
+          typedef short v4s __attribute__((ext_vector_type(4)));
+          typedef __attribute__((address_space(3))) v4s lds_v4s;
+          const v4s r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(va));
+          const v4s r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(va + 4 * rb));
+          typedef short v8s __attribute__((ext_vector_type(8)));
+          const v8s both = __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7);
+          const v8bf bfr = __builtin_bit_cast(v8bf, both);
 #pragma unroll
           for (int mt = 0; mt < HQT; ++mt) {
             o[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[mt], bfr, o[mt][j], 0, 0, 0);
@@ -167,22 +217,22 @@ struct AttnMfma {
           }
         }
       }
-      __syncthreads();
+      lds_barrier();
+      DSA_MARK(1, 9);
     }
 
+    // partial output in accumulator order: element ((mt * tiles + nt) * 64 + lane) * 4 + r
+    // is head 16*mt + 4*(lane/16) + r, value 16*nt + lane%16 (one 16-byte store per tile)
     const int64_t pb = (int64_t)b * p.S + split;
-    for (int h = tid; h < p.Hq; h += kBlock) p.part_ml[pb * p.Hq + h] = make_float2(mrun[h], lrun[h]);
+    for (int h = tid; h < p.Hq; h += kAttnBlock) p.part_ml[pb * p.Hq + h] = make_float2(mrun[h], lrun[h]);
+    float* po = p.part_o + pb * HP * Dv;
 #pragma unroll
     for (int mt = 0; mt < HQT; ++mt)
 #pragma unroll
       for (int j = 0; j < kMaxTilesPerWave; ++j) {
-        if (j >= ntw) break;
-        const int dv = 16 * (wave + kWaves * j) + (lane & 15);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int h = 16 * mt + 4 * (lane >> 4) + r;
-          if (h < p.Hq) p.part_o[(pb * p.Hq + h) * Dv + dv] = o[mt][j][r];
-        }
+        const int nt = wave + kAttnWaves * j;
+        if (nt >= nt_all) break;
+        *(v4f*)(po + ((int64_t)(mt * nt_all + nt) * 64 + lane) * 4) = o[mt][j];
       }
   }
 };
@@ -192,7 +242,7 @@ struct AttnMfma {
 template <typename T>
 struct AttnGeneric {
   static constexpr int SB = 32;
-  static constexpr int kMaxPerThread = 16;
+  static constexpr int kMaxPerThread = 4096 / kAttnBlock;
   __host__ __device__ static size_t lds_bytes(int Hq, int Dk) {
     return (size_t)SB * Dk * 4 + (size_t)Hq * Dk * 4 + (size_t)Hq * SB * 4 + 3 * (size_t)Hq * 4;
   }
@@ -200,6 +250,8 @@ struct AttnGeneric {
     if constexpr (sizeof(T) == 4) return reinterpret_cast<const float*>(base)[i];
     else return bf16_to_f32(reinterpret_cast<const uint16_t*>(base)[i]);
   }
+
+  __device__ static void prefetch(const AttnArgs&, int, uint8_t*) {}
 
   template <typename PosAt>
   __device__ static void run(const AttnArgs& p, int b, int split, PosAt pos_at, int cnt,
@@ -212,8 +264,8 @@ struct AttnGeneric {
     float* mrun = lg + Hq * SB;
     float* lrun = mrun + Hq;
     float* alpha = lrun + Hq;
-    for (int i = tid; i < Hq * Dk; i += kBlock) qs[i] = ld(p.q, (int64_t)b * Hq * Dk + i);
-    for (int h = tid; h < Hq; h += kBlock) {
+    for (int i = tid; i < Hq * Dk; i += kAttnBlock) qs[i] = ld(p.q, (int64_t)b * Hq * Dk + i);
+    for (int h = tid; h < Hq; h += kAttnBlock) {
       mrun[h] = -INFINITY;
       lrun[h] = 0.f;
     }
@@ -223,24 +275,24 @@ struct AttnGeneric {
 
     for (int s0 = 0; s0 < cnt; s0 += SB) {
       const int nr = cnt - s0 < SB ? cnt - s0 : SB;
-      for (int i = tid; i < SB * Dk; i += kBlock) {
+      for (int i = tid; i < SB * Dk; i += kAttnBlock) {
         const int r = i / Dk, d = i - r * Dk;
         rows[i] = r < nr ? ld(p.kv, pos_at(s0 + r) * Dk + d) : 0.f;
       }
-      __syncthreads();
-      for (int pr = tid; pr < Hq * SB; pr += kBlock) {
+      lds_barrier();
+      for (int pr = tid; pr < Hq * SB; pr += kAttnBlock) {
         const int h = pr / SB, r = pr - h * SB;
         float dot = 0.f;
         if (r < nr)
           for (int d = 0; d < Dk; ++d) dot = fmaf(qs[h * Dk + d], rows[r * Dk + d], dot);
         lg[pr] = r < nr ? dot * p.scale : -INFINITY;
       }
-      __syncthreads();
+      lds_barrier();
       softmax_update(lg, SB, Hq, mrun, lrun, alpha);
-      __syncthreads();
+      lds_barrier();
 #pragma unroll
       for (int j = 0; j < kMaxPerThread; ++j) {
-        const int pr = tid + kBlock * j;
+        const int pr = tid + kAttnBlock * j;
         if (pr < Hq * Dv) {
           const int h = pr / Dv, dv = pr - h * Dv;
           float acc = o[j] * alpha[h];
@@ -248,13 +300,13 @@ struct AttnGeneric {
           o[j] = acc;
         }
       }
-      __syncthreads();
+      lds_barrier();
     }
     const int64_t pb = (int64_t)b * p.S + split;
-    for (int h = tid; h < Hq; h += kBlock) p.part_ml[pb * Hq + h] = make_float2(mrun[h], lrun[h]);
+    for (int h = tid; h < Hq; h += kAttnBlock) p.part_ml[pb * Hq + h] = make_float2(mrun[h], lrun[h]);
 #pragma unroll
     for (int j = 0; j < kMaxPerThread; ++j) {
-      const int pr = tid + kBlock * j;
+      const int pr = tid + kAttnBlock * j;
       if (pr < Hq * Dv) p.part_o[pb * Hq * Dv + pr] = o[j];
     }
   }
@@ -263,6 +315,7 @@ struct AttnGeneric {
 // Selection only (no attention role).
 struct AttnNone {
   __host__ __device__ static size_t lds_bytes(int, int) { return 0; }
+  __device__ static void prefetch(const AttnArgs&, int, uint8_t*) {}
   template <typename PosAt>
   __device__ static void run(const AttnArgs&, int, int, PosAt, int, uint8_t*) {}
 };

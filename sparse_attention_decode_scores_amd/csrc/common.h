@@ -7,8 +7,6 @@
 namespace dsa {
 
 constexpr int kMaxBatch = 16;
-constexpr int kBlock = 256;            // threads per workgroup for every kernel
-constexpr int kWaves = kBlock / 64;
 constexpr int kCandCap = 8192;         // candidate keys per row kept by the chunk pass
 constexpr int kMaxChunks = 256;
 constexpr int kMaxSplits = 32;         // attention splits per row
@@ -29,168 +27,226 @@ struct RowStats {
   int32_t path, reason, selected, kth_score, candidates, tied_at_kth, bad_indices, reserved;
 };
 
-// A position's ordering key: score first (order-preserving map of int32 onto
-// uint32), then the complement of the position so that, for equal scores, the
-// lower position has the larger key. Larger key = earlier in the output. Keys of
-// distinct positions are distinct, and every real key is >= 2^31, so 0 can stand
-// for "no position".
+// Order-preserving map of an int32 score onto uint32.
+__device__ __forceinline__ uint32_t score_bits(int32_t s) { return (uint32_t)s ^ 0x80000000u; }
+
+// A position's ordering key: score first, then the complement of the position so
+// that, for equal scores, the lower position has the larger key. Larger key =
+// earlier in the output. Keys of distinct positions are distinct, and every real
+// key is >= 2^31, so 0 stands for "no position".
 __device__ __forceinline__ uint64_t make_key(int32_t score, uint32_t pos) {
-  return ((uint64_t)((uint32_t)score ^ 0x80000000u) << 32) | (uint64_t)(0xFFFFFFFFu - pos);
+  return ((uint64_t)score_bits(score) << 32) | (uint64_t)(0xFFFFFFFFu - pos);
 }
 __device__ __forceinline__ uint32_t key_pos(uint64_t key) { return 0xFFFFFFFFu - (uint32_t)key; }
+__device__ __forceinline__ uint32_t key_ubits(uint64_t key) { return (uint32_t)(key >> 32); }
 __device__ __forceinline__ int32_t key_score(uint64_t key) {
-  return (int32_t)((uint32_t)(key >> 32) ^ 0x80000000u);
+  return (int32_t)(key_ubits(key) ^ 0x80000000u);
 }
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Workgroup barrier for LDS communication only: waits for this wave's LDS
+// operations, not for its outstanding global loads and stores (a full
+// __syncthreads() also drains those, a memory round trip when stores are in
+// flight). Use __syncthreads() where waves exchange data through global memory.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 __device__ __forceinline__ uint64_t lanemask_lt() { return (1ull << lane_id()) - 1ull; }
 
-__device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+// Phase timestamps for performance analysis builds (-DDSA_TRACE): thread 0 of a
+// workgroup stores the 100 MHz real-time counter into a per-kernel table. In
+// normal builds the marks compile to nothing.
+#ifdef DSA_TRACE
+constexpr int kTraceKernels = 4, kTraceBlocks = 512, kTracePhases = 16;
+extern __device__ uint64_t dsa_trace[kTraceKernels][kTraceBlocks][kTracePhases];
+#define DSA_MARK(kernel, phase)                                                              \
+  do {                                                                                       \
+    const int blk_ = blockIdx.x + gridDim.x * blockIdx.y;                                    \
+    if (threadIdx.x == 0 && blk_ < kTraceBlocks)                                             \
+      dsa_trace[kernel][blk_][phase] = __builtin_amdgcn_s_memrealtime();                     \
+  } while (0)
+#else
+#define DSA_MARK(kernel, phase) \
+  do {                          \
+  } while (0)
+#endif
+
+// ---- wave primitives on the DPP datapath (VALU-speed lane exchange; the ds_
+// shuffle path costs an LDS round trip per step).
+namespace dpp {
+constexpr int kQuadXor1 = 0xB1;      // quad_perm 1,0,3,2
+constexpr int kQuadXor2 = 0x4E;      // quad_perm 2,3,0,1
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowMirror = 0x140, kRowHalfMirror = 0x141;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+}  // namespace dpp
+
+// Reduction of a 32-bit value over the wave; every lane gets the result.
+// Within each 16-lane row by DPP, then across the four rows through readlane.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, Op op) {
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, dpp::kQuadXor1, 0xF, 0xF, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, dpp::kQuadXor2, 0xF, 0xF, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, dpp::kRowHalfMirror, 0xF, 0xF, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, dpp::kRowMirror, 0xF, 0xF, false));
+  const uint32_t r0 = __builtin_amdgcn_readlane((int)v, 0), r1 = __builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane((int)v, 32), r3 = __builtin_amdgcn_readlane((int)v, 48);
+  return op(op(r0, r1), op(r2, r3));
+}
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+  return wave_reduce_u32(v, [](uint32_t a, uint32_t b) { return a + b; });
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  return wave_reduce_u32(v, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+}
+__device__ __forceinline__ uint32_t wave_maxr_u32(uint32_t v) {
+  return wave_reduce_u32(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+}
+__device__ __forceinline__ uint64_t wave_maxr_u64(uint64_t v) {
+  // the high word decides; the low word only among lanes holding the top high word
+  const uint32_t hi = wave_maxr_u32((uint32_t)(v >> 32));
+  const uint32_t lo = wave_maxr_u32((uint32_t)(v >> 32) == hi ? (uint32_t)v : 0u);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ float wave_reduce_max_f(float v) {
+  return __uint_as_float(wave_reduce_u32(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+  }));
+}
+__device__ __forceinline__ float wave_reduce_sum_f(float v) {
+  return __uint_as_float(wave_reduce_u32(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+  }));
+}
+
+// Inclusive prefix sum over the wave (lane order).
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, dpp::kRowShr1, 0xF, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, dpp::kRowShr2, 0xF, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, dpp::kRowShr4, 0xF, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, dpp::kRowShr8, 0xF, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, dpp::kRowBcast15, 0xA, 0xF, false);
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, dpp::kRowBcast31, 0xC, 0xF, false);
   return v;
 }
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+
+// Exclusive prefix sum over the block (thread order); *total gets the block sum.
+// `part` is LDS scratch of BLOCK/64 words. Two barriers.
+template <int BLOCK>
+__device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t* part, uint32_t* total) {
+  const uint32_t incl = wave_incl_scan_u32(v);
+  const uint32_t wtot = __builtin_amdgcn_readlane((int)incl, 63);
+  lds_barrier();  // previous users of `part` are done
+  if (lane_id() == 0) part[wave_id()] = wtot;
+  lds_barrier();
+  uint32_t before = 0, all = 0;
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    uint64_t w = __shfl_xor(v, o);
-    v = w > v ? w : v;
+  for (int w = 0; w < BLOCK / 64; ++w) {
+    const uint32_t s = part[w];
+    before += w < wave_id() ? s : 0u;
+    all += s;
   }
-  return v;
+  *total = all;
+  return before + incl - v;
 }
 
-// Block-wide reductions through a small LDS scratch (>= kWaves slots).
-__device__ __forceinline__ int block_sum(int v, int* scratch) {
-  v = wave_sum(v);
-  __syncthreads();
-  if (lane_id() == 0) scratch[wave_id()] = v;
-  __syncthreads();
-  int t = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) t += scratch[w];
-  return t;
-}
-__device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t* scratch) {
-  v = wave_max_u64(v);
-  __syncthreads();
-  if (lane_id() == 0) scratch[wave_id()] = v;
-  __syncthreads();
-  uint64_t t = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) t = scratch[w] > t ? scratch[w] : t;
-  return t;
-}
-
-// LDS state used by block_kth_largest.
-struct SelectSmem {
-  uint32_t hist[256];
-  uint64_t red[kWaves];
-  uint32_t digit, above, found;
-  uint64_t result;
+// LDS state of the radix selection below.
+constexpr int kRadixBits = 11;
+constexpr int kRadixBins = 1 << kRadixBits;
+struct RadixSmem {
+  uint32_t hist[2][kRadixBins];  // alternate passes; each pass leaves its buffer zeroed
+  uint32_t part[16];
+  uint32_t digit, above;
 };
 
-// Exact value of the rank-th largest of `count` distinct keys produced by
-// key_at(i) (rank is 1-based, 1 <= rank <= count), by most-significant-digit
-// radix selection: each pass histograms one byte of the keys that match the
-// bytes fixed so far and fixes the byte holding the rank-th key. Leading bytes
-// shared by the smallest and largest key are fixed without a pass; a pass
-// that leaves a single matching key ends the search. Every thread of the
-// block must call it; every thread gets the result.
-template <typename KeyAt>
-__device__ uint64_t block_kth_largest(int count, int rank, KeyAt key_at, SelectSmem& sm) {
-  const int tid = threadIdx.x;
-  // min and max key decide which leading bytes need no pass
-  uint64_t lo = ~0ull, hi = 0;
-  for (int i = tid; i < count; i += kBlock) {
-    uint64_t k = key_at(i);
-    lo = k < lo ? k : lo;
-    hi = k > hi ? k : hi;
-  }
-  hi = block_max_u64(hi, sm.red);
-  lo = ~block_max_u64(~lo, sm.red);
-  if (rank == 1) return hi;
-  if (rank == count) return lo;
-  uint64_t diff = lo ^ hi;
-  int byte = 7;
-  while (byte > 0 && ((diff >> (8 * byte)) & 0xFF) == 0) --byte;
-  uint64_t prefix = hi & (byte == 7 ? 0ull : (~0ull << (8 * (byte + 1))));
-  int need = rank;
-  for (;; --byte) {
-    const uint64_t hmask = byte == 7 ? 0ull : (~0ull << (8 * (byte + 1)));
-    for (int i = tid; i < 256; i += kBlock) sm.hist[i] = 0;
-    __syncthreads();
-    for (int i = tid; i < count; i += kBlock) {
-      uint64_t k = key_at(i);
-      if (((k ^ prefix) & hmask) == 0) atomicAdd(&sm.hist[(k >> (8 * byte)) & 0xFF], 1u);
-    }
-    __syncthreads();
-    if (tid < 64) {
-      // lane L owns digits 4L..4L+3; find d with above(d) < need <= above(d) + hist[d]
-      const int L = tid;
-      uint32_t h0 = sm.hist[4 * L], h1 = sm.hist[4 * L + 1], h2 = sm.hist[4 * L + 2],
-               h3 = sm.hist[4 * L + 3];
-      uint32_t own = h0 + h1 + h2 + h3;
-      // inclusive scan from the top lane down: s = sum over lanes >= L
-      uint32_t s = own;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        uint32_t t = __shfl_down(s, o);
-        if (L + o < 64) s += t;
-      }
-      uint32_t above = s - own;  // keys in digits above 4L+3
-      uint32_t hs[4] = {h0, h1, h2, h3};
-#pragma unroll
-      for (int j = 3; j >= 0; --j) {
-        if (above < (uint32_t)need && (uint32_t)need <= above + hs[j]) {
-          sm.digit = 4 * L + j;
-          sm.above = above;
-          sm.found = hs[j];
-        }
-        above += hs[j];
-      }
-    }
-    __syncthreads();
-    const uint32_t d = sm.digit, ab = sm.above, cnt = sm.found;
-    __syncthreads();
-    need -= (int)ab;
-    prefix |= (uint64_t)d << (8 * byte);
-    if (byte == 0) return prefix;
-    if (cnt == 1) {
-      // the only key that matches the fixed bytes is the answer
-      const uint64_t m2 = ~0ull << (8 * byte);
-      for (int i = tid; i < count; i += kBlock) {
-        uint64_t k = key_at(i);
-        if (((k ^ prefix) & m2) == 0) sm.result = k;
-      }
-      __syncthreads();
-      uint64_t r = sm.result;
-      __syncthreads();
-      return r;
-    }
-  }
+// Zeroes both histogram buffers; call once before the first block_select_range
+// (early, so it overlaps other work), followed by any barrier.
+template <int BLOCK>
+__device__ __forceinline__ void radix_clear(RadixSmem& sm) {
+  for (int i = threadIdx.x; i < 2 * kRadixBins; i += BLOCK) (&sm.hist[0][0])[i] = 0;
 }
 
-// Ordered stream compaction of a block: call with the same `round` sequence
-// on every thread; returns the output slot of this thread's element when
-// `keep` is true. `base` (LDS) carries the running count across rounds and must
-// start at 0; counts[kWaves] is LDS scratch.
-__device__ __forceinline__ int block_compact_slot(bool keep, int* counts, int* base) {
-  const uint64_t bal = __ballot(keep);
-  const int in_wave = __popcll(bal & lanemask_lt());
-  __syncthreads();
-  if (lane_id() == 0) counts[wave_id()] = __popcll(bal);
-  __syncthreads();
-  int before = *base;
-  int total = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    if (w < wave_id()) before += counts[w];
-    total += counts[w];
+// Score-level radix selection. `each(f)` calls f(v) for every value this thread
+// contributes; lo and hi are the smallest and largest of all contributed values.
+// Finds T, the rank-th largest value (1 <= rank <= number of values), and the
+// number of values above T. The digits are 11-bit slices of v - lo, most
+// significant first, over the bit length of hi - lo: each pass spreads the values
+// over up to 2048 bins (values crowding a narrow band still spread out; LDS
+// atomics on one bin serialise), and a range of 2^21 takes two passes. Three
+// barriers per pass. Every thread of the block calls it and gets the same T.
+template <int BLOCK, class Each>
+__device__ __forceinline__ uint32_t block_select_range(Each each, uint32_t lo, uint32_t hi, int rank,
+                                       uint32_t* above_out, RadixSmem& sm) {
+  static_assert(kRadixBins % BLOCK == 0, "bins per thread");
+  constexpr int BPT = kRadixBins / BLOCK;
+  const int tid = threadIdx.x;
+  const uint32_t range = hi - lo;
+  if (range == 0) {  // every value is equal
+    *above_out = 0;
+    return hi;
   }
-  __syncthreads();
-  if (threadIdx.x == 0) *base += total;
-  return before + in_wave;
+  int shift = 32 - __clz(range);  // low bits of v - lo still undecided
+  uint32_t prefix = 0;            // decided high bits of v - lo
+  uint32_t above = 0;
+  uint32_t need = (uint32_t)rank;
+  int buf = 0;
+  while (shift > 0) {
+    const int nshift = shift > kRadixBits ? shift - kRadixBits : 0;
+    uint32_t* hist = sm.hist[buf];
+    each([&](uint32_t v) {
+      const uint32_t off = v - lo;
+      if (((uint64_t)off >> shift) == (uint64_t)prefix)
+        atomicAdd(&hist[(off >> nshift) & (kRadixBins - 1)], 1u);
+    });
+    lds_barrier();
+    DSA_MARK(3, 2 + 2 * (shift > kRadixBits ? 0 : 1));
+    uint32_t h[BPT], own = 0;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      h[j] = hist[tid * BPT + j];
+      hist[tid * BPT + j] = 0;  // only this thread reads these bins
+      own += h[j];
+    }
+    uint32_t total;
+    const uint32_t before = block_excl_scan_u32<BLOCK>(own, sm.part, &total);
+    uint32_t ab = total - before - own;  // values in bins above this thread's bins
+#pragma unroll
+    for (int j = BPT - 1; j >= 0; --j) {
+      if (ab < need && need <= ab + h[j]) {
+        sm.digit = tid * BPT + j;
+        sm.above = ab;
+      }
+      ab += h[j];
+    }
+    lds_barrier();
+    DSA_MARK(3, 3 + 2 * (shift > kRadixBits ? 0 : 1));
+    const uint32_t d = sm.digit, ab2 = sm.above;
+    need -= ab2;
+    above += ab2;
+    prefix = (prefix << (shift - nshift)) | d;
+    shift = nshift;
+    buf ^= 1;
+  }
+  *above_out = above;
+  return lo + prefix;
+}
+
+// Block exchange of per-wave partial results: lane 0 of each wave stores its
+// wave's values, then every thread reads all of them. Two barriers.
+template <int BLOCK, int NV>
+__device__ __forceinline__ void block_exchange(const uint32_t (&mine)[NV], uint32_t (*slots)[NV],
+                                               uint32_t (&all)[BLOCK / 64][NV]) {
+  lds_barrier();
+  if (lane_id() == 0)
+#pragma unroll
+    for (int i = 0; i < NV; ++i) slots[wave_id()][i] = mine[i];
+  lds_barrier();
+#pragma unroll
+  for (int w = 0; w < BLOCK / 64; ++w)
+#pragma unroll
+    for (int i = 0; i < NV; ++i) all[w][i] = slots[w][i];
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }

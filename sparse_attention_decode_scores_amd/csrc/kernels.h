@@ -29,6 +29,8 @@ struct ScoreArgs {
 };
 
 hipError_t launch_score(const ScoreArgs& a, int MT, int KT, bool cand, int grid, hipStream_t s);
+int score_max_chunk();        // longest chunk the score kernel's candidate pass takes
+int chunk_cand_max_chunk();   // the same for the stand-alone candidate kernel
 size_t score_lds_bytes(int MT, int KT, int Bg, int P, bool cand);
 
 // Stand-alone candidate pass over scores already in memory.
@@ -50,8 +52,9 @@ struct AttnArgs {
   int Hq, Dk, Dv;
   float scale;
   float2* part_ml;  // [B][S][Hq] running max and sum of each split
-  float* part_o;    // [B][S][Hq][Dv] unnormalised output of each split
+  float* part_o;    // [B][S][Hp*Dv] unnormalised output of each split (layout per `frag`)
   int S;            // splits per row
+  int frag;         // 1: part_o in matrix-core accumulator order with Hp = Hq rounded to 16
 };
 
 enum AttnKind { ATTN_NONE = 0, ATTN_MFMA_BF16 = 1, ATTN_GENERIC_F32 = 2, ATTN_GENERIC_BF16 = 3 };

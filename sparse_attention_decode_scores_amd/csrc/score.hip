@@ -19,6 +19,9 @@
 
 namespace dsa {
 
+constexpr int kScoreBlock = 512;
+constexpr int kScoreWaves = kScoreBlock / 64;
+
 namespace {
 
 // Key fragment of the B operand: lane l holds 16 consecutive dims of key
@@ -40,19 +43,22 @@ __device__ __forceinline__ void load_keys(v4i (&kf)[2][KT], const int8_t* __rest
 }  // namespace
 
 template <int MT, int KT, bool CAND, bool ONE>
-__global__ __launch_bounds__(kBlock) void k_score(ScoreArgs a) {
+__global__ __launch_bounds__(kScoreBlock) void k_score(ScoreArgs a) {
   constexpr int HP = 32 * MT;  // heads padded to whole tiles (padding has q = 0, w = 0)
   constexpr int DI = 32 * KT;
   extern __shared__ __align__(16) uint8_t smem[];
-  ChunkSmem& csm = *reinterpret_cast<ChunkSmem*>(smem);
-  int8_t* qs = reinterpret_cast<int8_t*>(smem + align16(sizeof(ChunkSmem)));  // [Bg][HP][DI]
+  using Smem = ChunkSmem<kScoreBlock>;
+  Smem& csm = *reinterpret_cast<Smem*>(smem);
+  int8_t* qs = reinterpret_cast<int8_t*>(smem + align16(sizeof(Smem)));       // [Bg][HP][DI]
   int8_t* wsm = qs + a.Bg * HP * DI;                                           // [Bg][HP]
   int32_t* sc = reinterpret_cast<int32_t*>(wsm + a.Bg * HP);                   // [Bg][P]
 
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   const int c = blockIdx.x;
+  DSA_MARK(0, 0);
+  if (CAND) radix_clear<kScoreBlock>(csm.radix);
 
-  for (int i = tid; i < a.Bg * HP * (DI / 16); i += kBlock) {
+  for (int i = tid; i < a.Bg * HP * (DI / 16); i += kScoreBlock) {
     const int bb = i / (HP * (DI / 16));
     const int rem = i - bb * (HP * (DI / 16));
     const int h = rem / (DI / 16), part = rem - h * (DI / 16);
@@ -60,11 +66,11 @@ __global__ __launch_bounds__(kBlock) void k_score(ScoreArgs a) {
     if (h < a.Hi) v = *(const v4i*)(a.iq + ((int64_t)(a.b0 + bb) * a.Hi + h) * DI + 16 * part);
     *(v4i*)(qs + (bb * HP + h) * DI + 16 * part) = v;
   }
-  for (int i = tid; i < a.Bg * HP; i += kBlock) {
+  for (int i = tid; i < a.Bg * HP; i += kScoreBlock) {
     const int bb = i / HP, h = i - bb * HP;
     wsm[i] = h < a.Hi ? a.iw[(int64_t)(a.b0 + bb) * a.Hi + h] : (int8_t)0;
   }
-  __syncthreads();
+  lds_barrier();
 
   // A fragments and weights of a single row stay in registers for the whole chunk.
   v4i qreg[ONE ? MT : 1][ONE ? KT : 1];
@@ -85,6 +91,7 @@ __global__ __launch_bounds__(kBlock) void k_score(ScoreArgs a) {
     }
   }
 
+  DSA_MARK(0, 1);
   const int64_t cbeg = (int64_t)c * a.P;
   const int64_t last = (int64_t)a.nmax - 1;
   const int64_t clen64 = (int64_t)a.nmax - cbeg;
@@ -93,9 +100,9 @@ __global__ __launch_bounds__(kBlock) void k_score(ScoreArgs a) {
 
   v4i kcur[2][KT], knext[2][KT];
   if (wave < npairs) load_keys<KT>(kcur, a.ik, cbeg + 64 * wave, last);
-  for (int tp = wave; tp < npairs; tp += kWaves) {
+  for (int tp = wave; tp < npairs; tp += kScoreWaves) {
     const int64_t p0 = cbeg + 64 * tp;
-    if (tp + kWaves < npairs) load_keys<KT>(knext, a.ik, p0 + 64 * kWaves, last);
+    if (tp + kScoreWaves < npairs) load_keys<KT>(knext, a.ik, p0 + 64 * kScoreWaves, last);
     for (int bb = 0; bb < a.Bg; ++bb) {
       const int8_t* qb = qs + bb * HP * DI;
       int half[2];
@@ -144,21 +151,27 @@ __global__ __launch_bounds__(kBlock) void k_score(ScoreArgs a) {
       for (int kt = 0; kt < KT; ++kt) kcur[t][kt] = knext[t][kt];
   }
 
+  DSA_MARK(0, 2);
   if (CAND) {
-    __syncthreads();
+    lds_barrier();
+    DSA_MARK(0, 3);
     for (int bb = 0; bb < a.Bg; ++bb) {
       const int b = a.b0 + bb;
       const int64_t n64 = (int64_t)a.lens.n[b] - cbeg;
       const int count = n64 > clen ? clen : (int)(n64 > 0 ? n64 : 0);
-      chunk_candidates(sc + bb * a.P, count, (uint32_t)cbeg, a.m,
-                       a.cand + ((int64_t)b * a.G + c) * a.m, a.xc + (int64_t)b * a.G + c, csm);
-      __syncthreads();
+      chunk_candidates<kScoreBlock>(sc + bb * a.P, count, (uint32_t)cbeg, a.m,
+                                    a.cand + ((int64_t)b * a.G + c) * a.m,
+                                    a.xc + (int64_t)b * a.G + c, csm);
+      lds_barrier();
     }
+    DSA_MARK(0, 4);
   }
 }
 
+int score_max_chunk() { return kChunkPerThread * kScoreBlock; }
+
 size_t score_lds_bytes(int MT, int KT, int Bg, int P, bool cand) {
-  return align16(sizeof(ChunkSmem)) + (size_t)Bg * 32 * MT * 32 * KT + (size_t)Bg * 32 * MT +
+  return align16(sizeof(ChunkSmem<kScoreBlock>)) + (size_t)Bg * 32 * MT * 32 * KT + (size_t)Bg * 32 * MT +
          (cand ? (size_t)Bg * P * 4 : 0) + 16;
 }
 
@@ -168,7 +181,7 @@ static hipError_t launch_score_t(const ScoreArgs& a, int grid, size_t lds, hipSt
   hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fn, dim3(grid), dim3(kBlock), lds, s, a);
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(kScoreBlock), lds, s, a);
   return hipGetLastError();
 }
 

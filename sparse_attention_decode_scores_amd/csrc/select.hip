@@ -32,36 +32,44 @@ namespace dsa {
 
 // ------------------------------------------------------------------ candidates over stored scores
 
-__global__ __launch_bounds__(kBlock) void k_chunk_cand(CandArgs a) {
+constexpr int kSelBlock = kAttnBlock;  // selection, ranking and attention share the launch
+constexpr int kSelWaves = kSelBlock / 64;
+constexpr int kUPerThread = kCandCap / kSelBlock;  // candidate keys held per thread
+
+__global__ __launch_bounds__(kSelBlock) void k_chunk_cand(CandArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
-  ChunkSmem& csm = *reinterpret_cast<ChunkSmem*>(smem);
-  int32_t* sc = reinterpret_cast<int32_t*>(smem + align16(sizeof(ChunkSmem)));
+  using Smem = ChunkSmem<kSelBlock>;
+  Smem& csm = *reinterpret_cast<Smem*>(smem);
+  int32_t* sc = reinterpret_cast<int32_t*>(smem + align16(sizeof(Smem)));
   const int c = blockIdx.x, b = blockIdx.y;
   const int64_t cbeg = (int64_t)c * a.P;
   const int64_t n64 = (int64_t)a.lens.n[b] - cbeg;
   const int count = n64 > a.P ? a.P : (int)(n64 > 0 ? n64 : 0);
   const int32_t* row = a.scores + (int64_t)b * a.N + cbeg;
-  for (int i = threadIdx.x; i < count; i += kBlock) sc[i] = row[i];
-  __syncthreads();
-  chunk_candidates(sc, count, (uint32_t)cbeg, a.m, a.cand + ((int64_t)b * a.G + c) * a.m,
-                   a.xc + (int64_t)b * a.G + c, csm);
+  radix_clear<kSelBlock>(csm.radix);
+  for (int i = threadIdx.x; i < count; i += kSelBlock) sc[i] = row[i];
+  lds_barrier();
+  chunk_candidates<kSelBlock>(sc, count, (uint32_t)cbeg, a.m, a.cand + ((int64_t)b * a.G + c) * a.m,
+                              a.xc + (int64_t)b * a.G + c, csm);
 }
 
 hipError_t launch_chunk_candidates(const CandArgs& a, int B, hipStream_t s) {
-  const size_t lds = align16(sizeof(ChunkSmem)) + (size_t)a.P * 4;
+  const size_t lds = align16(sizeof(ChunkSmem<kSelBlock>)) + (size_t)a.P * 4;
   hipError_t e = hipFuncSetAttribute((const void*)k_chunk_cand,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_chunk_cand, dim3(a.G, B), dim3(kBlock), lds, s, a);
+  hipLaunchKernelGGL(k_chunk_cand, dim3(a.G, B), dim3(kSelBlock), lds, s, a);
   return hipGetLastError();
 }
+
+int chunk_cand_max_chunk() { return kChunkPerThread * kSelBlock; }
 
 // ------------------------------------------------------------------ exhaustive ordered sort
 
 struct SortSmem {
   uint32_t hist[256];
   uint32_t base[256];
-  uint32_t wc[kWaves][256];
+  uint32_t wc[kSelWaves][256];
   int skip;
 };
 
@@ -69,12 +77,12 @@ struct SortSmem {
 // byte-wide counting passes from the least significant byte. The input is built
 // in position order, so equal scores keep ascending positions. Returns the
 // buffer that holds the result (bufA or bufB). One workgroup.
-__device__ const uint64_t* block_sort_row(const int32_t* __restrict__ scores, int n,
+__device__ __forceinline__ const uint64_t* block_sort_row(const int32_t* __restrict__ scores, int n,
                                           uint64_t* bufA, uint64_t* bufB, SortSmem& ss) {
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
-  for (int i = tid; i < n; i += kBlock)
-    bufA[i] = ((uint64_t)((uint32_t)scores[i] ^ 0x80000000u) << 32) | (uint32_t)i;
-  for (int i = tid; i < kWaves * 256; i += kBlock) (&ss.wc[0][0])[i] = 0;
+  for (int i = tid; i < n; i += kSelBlock)
+    bufA[i] = ((uint64_t)score_bits(scores[i]) << 32) | (uint32_t)i;
+  for (int i = tid; i < kSelWaves * 256; i += kSelBlock) (&ss.wc[0][0])[i] = 0;
   __threadfence_block();
   __syncthreads();
   uint64_t* src = bufA;
@@ -82,9 +90,9 @@ __device__ const uint64_t* block_sort_row(const int32_t* __restrict__ scores, in
   for (int pass = 0; pass < 4; ++pass) {
     const int sh = 32 + 8 * pass;
     auto digit = [sh](uint64_t e) { return 255u - (uint32_t)((e >> sh) & 0xFF); };
-    ss.hist[tid] = 0;
+    if (tid < 256) ss.hist[tid] = 0;
     __syncthreads();
-    for (int i = tid; i < n; i += kBlock) atomicAdd(&ss.hist[digit(src[i])], 1u);
+    for (int i = tid; i < n; i += kSelBlock) atomicAdd(&ss.hist[digit(src[i])], 1u);
     __syncthreads();
     if (tid < 64) {
       const uint32_t h0 = ss.hist[4 * tid], h1 = ss.hist[4 * tid + 1], h2 = ss.hist[4 * tid + 2],
@@ -96,7 +104,7 @@ __device__ const uint64_t* block_sort_row(const int32_t* __restrict__ scores, in
         const uint32_t t = __shfl_up(s, o);
         if (tid >= o) s += t;
       }
-      uint32_t ex = s - own;
+      const uint32_t ex = s - own;
       ss.base[4 * tid] = ex;
       ss.base[4 * tid + 1] = ex + h0;
       ss.base[4 * tid + 2] = ex + h0 + h1;
@@ -110,7 +118,7 @@ __device__ const uint64_t* block_sort_row(const int32_t* __restrict__ scores, in
       __syncthreads();
       continue;  // every element has the same digit: the order is unchanged
     }
-    for (int t0 = 0; t0 < n; t0 += kBlock) {
+    for (int t0 = 0; t0 < n; t0 += kSelBlock) {
       const int i = t0 + tid;
       const bool valid = i < n;
       const uint64_t e = valid ? src[i] : 0;
@@ -133,10 +141,10 @@ __device__ const uint64_t* block_sort_row(const int32_t* __restrict__ scores, in
         dst[off] = e;
       }
       __syncthreads();
-      {
+      if (tid < 256) {
         uint32_t t = 0;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
+        for (int w = 0; w < kSelWaves; ++w) {
           t += ss.wc[w][tid];
           ss.wc[w][tid] = 0;
         }
@@ -156,18 +164,122 @@ __device__ const uint64_t* block_sort_row(const int32_t* __restrict__ scores, in
 // ------------------------------------------------------------------ selection (+ attention)
 
 struct SelSmem {
-  SelectSmem sel;
-  SortSmem sort;
-  int counts[kWaves];
-  int base;
-  int ired[kWaves];
-  uint64_t ured[kWaves];
+  RadixSmem radix;
+  uint32_t xch[kSelWaves][5];
+  uint64_t kstar;
 };
 
-// LDS: SelSmem | selected keys [k] | region shared by the candidate union and
-// the attention working set.
+// Exchanges (sum, min, max, max64) over the block in one round.
+struct Stats4 {
+  uint32_t sum, lo, hi;
+  uint64_t mx;
+};
+__device__ __forceinline__ Stats4 block_stats(uint32_t sum, uint32_t lo, uint32_t hi, uint64_t mx,
+                                              SelSmem& sm) {
+  const uint64_t wmx = wave_maxr_u64(mx);
+  const uint32_t mine[5] = {wave_sum_u32(sum), ~wave_min_u32(lo), wave_maxr_u32(hi),
+                            (uint32_t)(wmx >> 32), (uint32_t)wmx};
+  uint32_t all[kSelWaves][5];
+  block_exchange<kSelBlock, 5>(mine, sm.xch, all);
+  Stats4 r{0, 0, 0, 0};
+  uint32_t nlo = 0;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) {
+    r.sum += all[w][0];
+    nlo = all[w][1] > nlo ? all[w][1] : nlo;
+    r.hi = all[w][2] > r.hi ? all[w][2] : r.hi;
+    const uint64_t m = ((uint64_t)all[w][3] << 32) | all[w][4];
+    r.mx = m > r.mx ? m : r.mx;
+  }
+  r.lo = ~nlo;
+  return r;
+}
+
+// Writes the selected keys held E per thread (contiguous, position order) to sel:
+// those scoring above T, then the first need_eq scoring exactly T in position
+// order. Returns (in sm.kstar, valid after the call) the last key taken at T.
+template <int E, class ValidAt>
+__device__ __forceinline__ void write_selected(const uint64_t (&key)[E], ValidAt valid_at, uint32_t T,
+                                               uint32_t need_eq, uint32_t run_sel, uint32_t run_eq,
+                                               uint64_t* sel, SelSmem& sm, uint32_t* tot_sel,
+                                               uint32_t* tot_eq) {
+  uint32_t gt = 0, eq = 0;
+#pragma unroll
+  for (int j = 0; j < E; ++j)
+    if (valid_at(j)) {
+      const uint32_t u = key_ubits(key[j]);
+      gt += u > T;
+      eq += u == T;
+    }
+  uint32_t total;
+  const uint32_t before = block_excl_scan_u32<kSelBlock>(gt | (eq << 16), sm.radix.part, &total);
+  const uint32_t eq_before = run_eq + (before >> 16);
+  uint32_t slot = run_sel + (before & 0xFFFF) + (eq_before < need_eq ? eq_before - run_eq
+                                                                      : (need_eq > run_eq ? need_eq - run_eq : 0));
+  uint32_t eqr = eq_before;
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    if (!valid_at(j)) continue;
+    const uint32_t u = key_ubits(key[j]);
+    if (u > T) {
+      sel[slot++] = key[j];
+    } else if (u == T) {
+      if (eqr < need_eq) {
+        sel[slot++] = key[j];
+        if (eqr == need_eq - 1) sm.kstar = key[j];
+      }
+      ++eqr;
+    }
+  }
+  const uint32_t teq = total >> 16;
+  const uint32_t taken = run_eq >= need_eq ? 0 : (run_eq + teq <= need_eq ? teq : need_eq - run_eq);
+  *tot_sel = (total & 0xFFFF) + taken;
+  *tot_eq = teq;
+}
+
+// Exhaustive selection: the kk best keys of the row's n positions, written to sel
+// in position order; returns the kk-th best key. Streams the scores from memory
+// (a pass for the range, one radix pass per 11 bits of it, then one ordered
+// compaction pass).
+__device__ __forceinline__ uint64_t select_row_exhaustive(const int32_t* __restrict__ row, int n, int kk,
+                                          uint64_t* sel, uint32_t* tied, SelSmem& sm) {
+  const int tid = threadIdx.x;
+  uint32_t lo = 0xFFFFFFFFu, hi = 0;
+  for (int i = tid; i < n; i += kSelBlock) {
+    const uint32_t u = score_bits(row[i]);
+    lo = u < lo ? u : lo;
+    hi = u > hi ? u : hi;
+  }
+  const Stats4 st = block_stats(0, lo, hi, 0, sm);
+  auto each = [&](auto f) {
+    for (int i = tid; i < n; i += kSelBlock) f(score_bits(row[i]));
+  };
+  uint32_t above;
+  const uint32_t T = block_select_range<kSelBlock>(each, st.lo, st.hi, kk, &above, sm.radix);
+  const uint32_t need_eq = (uint32_t)kk - above;
+  *tied = need_eq;
+  uint32_t run_sel = 0, run_eq = 0;
+  constexpr int E = 16;
+  for (int base = 0; base < n; base += kSelBlock * E) {
+    const int i0 = base + tid * E;
+    uint64_t key[E];
+#pragma unroll
+    for (int j = 0; j < E; ++j)
+      key[j] = i0 + j < n ? make_key(row[i0 + j], (uint32_t)(i0 + j)) : 0ull;
+    uint32_t ts, te;
+    write_selected<E>(key, [&](int j) { return i0 + j < n; }, T, need_eq, run_sel, run_eq, sel, sm,
+                      &ts, &te);
+    run_sel += ts;
+    run_eq += te;
+  }
+  lds_barrier();
+  return sm.kstar;
+}
+
+// LDS: SelSmem | selected keys [k] | region: the attention working set, or the
+// sort state of the exhaustive path (the two roles never need both).
 template <class Attn>
-__global__ __launch_bounds__(kBlock) void k_select(SelArgs a, AttnArgs at) {
+__global__ __launch_bounds__(kSelBlock) void k_select(SelArgs a, AttnArgs at) {
   extern __shared__ __align__(16) uint8_t smem[];
   SelSmem& sm = *reinterpret_cast<SelSmem*>(smem);
   uint64_t* sel = reinterpret_cast<uint64_t*>(smem + align16(sizeof(SelSmem)));
@@ -178,144 +290,165 @@ __global__ __launch_bounds__(kBlock) void k_select(SelArgs a, AttnArgs at) {
   const bool attn_role = (int)blockIdx.x < S;
   const int n = a.lens.n[b];
   const int32_t* row = a.scores + (int64_t)b * a.N;
+  DSA_MARK(1, 0);
 
   int reason = a.force ? 1 : (a.have_cand ? 0 : 3);
-  int nvalid = 0, nsel = 0;
+  uint32_t nvalid = 0, nsel = 0, tied = 0;
   uint64_t kstar = 0;
+  uint64_t key[kUPerThread];
+  uint64_t mx = 0;
   if (reason == 0) {
+    // the candidate union U: thread t holds keys [16t, 16t + 16) (position order)
     const int C = a.G * a.m;
-    uint64_t* U = reinterpret_cast<uint64_t*>(region);
-    const uint64_t* cu = a.cand + (int64_t)b * C;
-    int nz = 0;
-    for (int i = tid; i < C; i += kBlock) {
-      const uint64_t v = cu[i];
-      U[i] = v;
-      nz += v != 0;
+    typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
+    const u64x2* src = reinterpret_cast<const u64x2*>(a.cand + (int64_t)b * C + tid * kUPerThread);
+    const bool have = tid * kUPerThread < C;
+#pragma unroll
+    for (int j = 0; j < kUPerThread / 2; ++j) {
+      const u64x2 v = have ? src[j] : u64x2{0ull, 0ull};
+      key[2 * j] = v.x;
+      key[2 * j + 1] = v.y;
     }
-    uint64_t mx = 0;
-    for (int i = tid; i < a.G; i += kBlock) {
-      const uint64_t v = a.xc[(int64_t)b * a.G + i];
-      mx = v > mx ? v : mx;
-    }
-    nvalid = block_sum(nz, sm.ired);
-    mx = block_max_u64(mx, sm.ured);
-    const int kk = a.k < nvalid ? a.k : nvalid;
-    kstar = block_kth_largest(C, kk, [&](int i) { return U[i]; }, sm.sel);
-    const bool ok = mx < kstar && (nvalid >= a.k || mx == 0);
-    if (ok) {
-      if (tid == 0) sm.base = 0;
-      __syncthreads();
-      for (int r0 = 0; r0 < C; r0 += kBlock) {
-        const int i = r0 + tid;
-        const uint64_t v = i < C ? U[i] : 0;
-        const bool keep = i < C && v >= kstar;
-        const int slot = block_compact_slot(keep, sm.counts, &sm.base);
-        if (keep) sel[slot] = v;
+    mx = tid < a.G ? a.xc[(int64_t)b * a.G + tid] : 0ull;
+  }
+  radix_clear<kSelBlock>(sm.radix);
+  if (attn_role) Attn::prefetch(at, b, region);
+  if (reason == 0) {
+    uint32_t nz = 0, lo = 0xFFFFFFFFu, hi = 0;
+#pragma unroll
+    for (int j = 0; j < kUPerThread; ++j)
+      if (key[j] != 0) {
+        const uint32_t u = key_ubits(key[j]);
+        ++nz;
+        lo = u < lo ? u : lo;
+        hi = u > hi ? u : hi;
       }
+    DSA_MARK(1, 11);
+    const Stats4 st = block_stats(nz, lo, hi, mx, sm);
+    nvalid = st.sum;
+    mx = st.mx;
+    DSA_MARK(1, 1);
+    const uint32_t kk = (uint32_t)a.k < nvalid ? (uint32_t)a.k : nvalid;
+    auto each = [&](auto f) {
+#pragma unroll
+      for (int j = 0; j < kUPerThread; ++j)
+        if (key[j] != 0) f(key_ubits(key[j]));
+    };
+    uint32_t above;
+    const uint32_t T = block_select_range<kSelBlock>(each, st.lo, st.hi, (int)kk, &above, sm.radix);
+    const uint32_t need_eq = kk - above;
+    DSA_MARK(1, 2);
+    uint32_t ts, te;
+    write_selected<kUPerThread>(key, [&](int j) { return key[j] != 0; }, T, need_eq, 0, 0, sel, sm,
+                                &ts, &te);
+    lds_barrier();
+    DSA_MARK(1, 3);
+    kstar = sm.kstar;
+    // every dropped key is below the k-th candidate: the candidates hold the top k
+    const bool ok = mx < kstar && (nvalid >= (uint32_t)a.k || mx == 0);
+    if (ok) {
       nsel = kk;
+      tied = need_eq;
     } else {
       reason = 2;
     }
-    __syncthreads();
   }
 
   if (reason != 0) {
     if (!attn_role) {
       if ((int)blockIdx.x != S) return;  // one ranking workgroup sorts the whole row
       uint64_t* ba = a.sortbuf + (int64_t)b * 2 * a.N;
-      const uint64_t* sorted = block_sort_row(row, n, ba, ba + a.N, sm.sort);
+      const uint64_t* sorted =
+          block_sort_row(row, n, ba, ba + a.N, *reinterpret_cast<SortSmem*>(region));
       const int kk = a.k < n ? a.k : n;
       int32_t* out = a.idx + (int64_t)b * a.k;
       const uint32_t ulast = (uint32_t)(sorted[kk - 1] >> 32);
-      int tied = 0;
-      for (int j = tid; j < a.k; j += kBlock) {
+      uint32_t t = 0;
+      for (int j = tid; j < a.k; j += kSelBlock) {
         if (j < kk) {
           const uint64_t e = sorted[j];
           out[j] = (int32_t)(uint32_t)e;
-          tied += (uint32_t)(e >> 32) == ulast;
+          t += (uint32_t)(e >> 32) == ulast;
         } else {
           out[j] = -1;
         }
       }
-      tied = block_sum(tied, sm.ired);
+      t = block_stats(t, 0, 0, 0, sm).sum;
       if (tid == 0) {
         RowStats st;
         st.path = 1;
         st.reason = reason;
         st.selected = kk;
         st.kth_score = (int32_t)(ulast ^ 0x80000000u);
-        st.candidates = nvalid;
-        st.tied_at_kth = tied;
+        st.candidates = (int32_t)nvalid;
+        st.tied_at_kth = (int32_t)t;
         st.bad_indices = 0;
         st.reserved = 0;
         a.stats[b] = st;
       }
       return;
     }
-    // attention workgroups select the same set over every position
+    // attention workgroups select the same set from every position
     const int kk = a.k < n ? a.k : n;
-    auto key_at = [&](int i) { return make_key(row[i], (uint32_t)i); };
-    kstar = block_kth_largest(n, kk, key_at, sm.sel);
-    if (tid == 0) sm.base = 0;
-    __syncthreads();
-    for (int r0 = 0; r0 < n; r0 += kBlock) {
-      const int i = r0 + tid;
-      uint64_t v = 0;
-      bool keep = false;
-      if (i < n) {
-        v = key_at(i);
-        keep = v >= kstar;
-      }
-      const int slot = block_compact_slot(keep, sm.counts, &sm.base);
-      if (keep) sel[slot] = v;
-    }
-    nsel = kk;
+    kstar = select_row_exhaustive(row, n, kk, sel, &tied, sm);
+    nsel = (uint32_t)kk;
   }
-  __syncthreads();
+  lds_barrier();
+  DSA_MARK(1, 4);
 
   if (attn_role) {
-    const int per = (nsel + S - 1) / S;
+    const int per = ((int)nsel + S - 1) / S;
     const int e0 = (int)blockIdx.x * per;
-    int cnt = nsel - e0;
+    int cnt = (int)nsel - e0;
     cnt = cnt < 0 ? 0 : (cnt > per ? per : cnt);
     Attn::run(at, b, blockIdx.x, [&](int i) { return (int64_t)key_pos(sel[e0 + i]); }, cnt,
               region);
+    DSA_MARK(1, 10);
     return;
   }
 
-  // ranking: slot of a key = number of selected keys larger than it
+  // ranking: the slot of a key is the number of selected keys larger than it
+  constexpr int TPE = 32;  // threads per ranked key
   const int r = (int)blockIdx.x - S;
-  const int per = (nsel + a.R - 1) / a.R;
+  const int per = ((int)nsel + a.R - 1) / a.R;
   const int e0 = r * per;
-  const int e1 = e0 + per < nsel ? e0 + per : nsel;
+  const int e1 = e0 + per < (int)nsel ? e0 + per : (int)nsel;
   int32_t* out = a.idx + (int64_t)b * a.k;
-  for (int base = e0; base < e1; base += kBlock / 16) {
-    const int e = base + (tid >> 4);
-    const int part = tid & 15;
+  for (int base = e0; base < e1; base += kSelBlock / TPE) {
+    const int e = base + tid / TPE;
+    const int part = tid % TPE;
     const uint64_t me = e < e1 ? sel[e] : ~0ull;
-    int cnt = 0;
-    if (e < e1)
-      for (int x = part; x < nsel; x += 16) cnt += sel[x] > me;
-    cnt += __shfl_xor(cnt, 8);
-    cnt += __shfl_xor(cnt, 4);
-    cnt += __shfl_xor(cnt, 2);
-    cnt += __shfl_xor(cnt, 1);
+    uint32_t cnt = 0;
+    // keys part, part + TPE, ...: eight loads in flight per step, masked past nsel
+    for (int x0 = part; x0 < (int)nsel; x0 += 8 * TPE) {
+      uint64_t v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int x = x0 + i * TPE;
+        v[i] = sel[x < (int)nsel ? x : (int)nsel - 1];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) cnt += (x0 + i * TPE < (int)nsel) && v[i] > me;
+    }
+    // sum over the 32 lanes of this key (half a wave)
+    cnt += (uint32_t)__builtin_amdgcn_mov_dpp((int)cnt, dpp::kQuadXor1, 0xF, 0xF, false);
+    cnt += (uint32_t)__builtin_amdgcn_mov_dpp((int)cnt, dpp::kQuadXor2, 0xF, 0xF, false);
+    cnt += (uint32_t)__builtin_amdgcn_mov_dpp((int)cnt, dpp::kRowHalfMirror, 0xF, 0xF, false);
+    cnt += (uint32_t)__builtin_amdgcn_mov_dpp((int)cnt, dpp::kRowMirror, 0xF, 0xF, false);
+    cnt += (uint32_t)__shfl_xor((int)cnt, 16);
     if (e < e1 && part == 0) out[cnt] = (int32_t)key_pos(me);
   }
+  DSA_MARK(1, 5);
   if (r == 0) {
-    for (int j = nsel + tid; j < a.k; j += kBlock) out[j] = -1;
-    const uint32_t ulast = (uint32_t)(kstar >> 32);
-    int tied = 0;
-    for (int i = tid; i < nsel; i += kBlock) tied += (uint32_t)(sel[i] >> 32) == ulast;
-    tied = block_sum(tied, sm.ired);
+    for (int j = (int)nsel + tid; j < a.k; j += kSelBlock) out[j] = -1;
     if (tid == 0) {
       RowStats st;
       st.path = 0;
       st.reason = 0;
-      st.selected = nsel;
+      st.selected = (int32_t)nsel;
       st.kth_score = key_score(kstar);
-      st.candidates = nvalid;
-      st.tied_at_kth = tied;
+      st.candidates = (int32_t)nvalid;
+      st.tied_at_kth = (int32_t)tied;
       st.bad_indices = 0;
       st.reserved = 0;
       a.stats[b] = st;
@@ -325,10 +458,9 @@ __global__ __launch_bounds__(kBlock) void k_select(SelArgs a, AttnArgs at) {
 
 template <class Attn>
 static size_t select_lds_t(int Hq, int Dk, int k) {
-  const size_t region_c = (size_t)kCandCap * 8;
-  const size_t region_a = Attn::lds_bytes(Hq, Dk);
+  const size_t ra = Attn::lds_bytes(Hq, Dk);
   return align16(sizeof(SelSmem)) + align16((size_t)k * 8) +
-         (region_c > region_a ? region_c : region_a);
+         (ra > sizeof(SortSmem) ? ra : sizeof(SortSmem));
 }
 
 template <class Attn>
@@ -338,15 +470,15 @@ static hipError_t launch_select_t(const SelArgs& a, const AttnArgs& at, int B, h
   hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fn, dim3(at.S + a.R, B), dim3(kBlock), lds, s, a, at);
+  hipLaunchKernelGGL(fn, dim3(at.S + a.R, B), dim3(kSelBlock), lds, s, a, at);
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ attention over given indices
 
 template <class Attn>
-__global__ __launch_bounds__(kBlock) void k_attend_idx(const int32_t* __restrict__ idx, int k,
-                                                       int32_t* __restrict__ part_bad, AttnArgs at) {
+__global__ __launch_bounds__(kSelBlock) void k_attend_idx(const int32_t* __restrict__ idx, int k,
+                                                          int32_t* __restrict__ part_bad, AttnArgs at) {
   extern __shared__ __align__(16) uint8_t smem[];
   SelSmem& sm = *reinterpret_cast<SelSmem*>(smem);
   const int per = (k + at.S - 1) / at.S;
@@ -357,22 +489,21 @@ __global__ __launch_bounds__(kBlock) void k_attend_idx(const int32_t* __restrict
   const int e0 = j * per;
   const int e1 = e0 + per < k ? e0 + per : k;
   const int32_t* row = idx + (int64_t)b * k;
-  if (tid == 0) sm.base = 0;
-  __syncthreads();
-  int bad = 0;
-  for (int r0 = e0; r0 < e1; r0 += kBlock) {
+  Attn::prefetch(at, b, region);
+  uint32_t bad = 0, run = 0;
+  for (int r0 = e0; r0 < e1; r0 += kSelBlock) {
     const int i = r0 + tid;
     const int32_t v = i < e1 ? row[i] : -1;
     const bool keep = v >= 0 && (int64_t)v < at.N;
     bad += (v != -1 && !keep);
-    const int slot = block_compact_slot(keep, sm.counts, &sm.base);
+    uint32_t total;
+    const uint32_t slot = run + block_excl_scan_u32<kSelBlock>(keep ? 1u : 0u, sm.radix.part, &total);
     if (keep) posl[slot] = v;
+    run += total;
   }
-  bad = block_sum(bad, sm.ired);
-  const int cnt = sm.base;
-  __syncthreads();
-  if (tid == 0) part_bad[(int64_t)b * at.S + j] = bad;
-  Attn::run(at, b, j, [&](int i) { return (int64_t)posl[i]; }, cnt, region);
+  bad = block_stats(bad, 0, 0, 0, sm).sum;
+  if (tid == 0) part_bad[(int64_t)b * at.S + j] = (int32_t)bad;
+  Attn::run(at, b, j, [&](int i) { return (int64_t)posl[i]; }, (int)run, region);
 }
 
 template <class Attn>
@@ -384,7 +515,7 @@ static hipError_t launch_attend_t(const int32_t* idx, int k, int32_t* part_bad, 
   hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fn, dim3(at.S, B), dim3(kBlock), lds, s, idx, k, part_bad, at);
+  hipLaunchKernelGGL(fn, dim3(at.S, B), dim3(kSelBlock), lds, s, idx, k, part_bad, at);
   return hipGetLastError();
 }
 
@@ -392,7 +523,7 @@ static hipError_t launch_attend_t(const int32_t* idx, int k, int32_t* part_bad, 
 
 AttnChoice choose_attn(int dt_bf16, int Hq, int Dk, int Dv) {
   AttnChoice c{ATTN_NONE, 0, 0};
-  if (dt_bf16 && Hq >= 1 && Hq <= 64 && Dk % 32 == 0 && Dk <= 1024 && Dv % 64 == 0 && Dv <= 512 &&
+  if (dt_bf16 && Hq >= 1 && Hq <= 64 && Dk % 32 == 0 && Dk <= 1024 && Dv % 16 == 0 && Dv <= 512 &&
       Dv <= Dk) {
     c.kind = ATTN_MFMA_BF16;
     c.hqt = (Hq + 15) / 16;
@@ -479,39 +610,115 @@ hipError_t launch_attend_idx(const int32_t* idx, int k, int32_t* part_bad, const
 
 // ------------------------------------------------------------------ combine
 
-// out[b][h][v] = sum_s e^(m_s - M) o_s[h][v] / sum_s e^(m_s - M) l_s, splits in order.
-__global__ __launch_bounds__(kBlock) void k_combine(AttnArgs at, const int32_t* __restrict__ part_bad,
-                                                    RowStats* __restrict__ stats, float* __restrict__ out) {
-  const int b = blockIdx.y;
-  const int i = blockIdx.x * kBlock + threadIdx.x;
-  if (part_bad != nullptr && blockIdx.x == 0 && threadIdx.x == 0) {
-    int t = 0;
-    for (int s = 0; s < at.S; ++s) t += part_bad[(int64_t)b * at.S + s];
-    stats[b].bad_indices = t;
-  }
-  if (i >= at.Hq * at.Dv) return;
-  const int h = i / at.Dv;
-  const float2* ml = at.part_ml + (int64_t)b * at.S * at.Hq + h;
-  float M = -INFINITY;
-  for (int s = 0; s < at.S; ++s) M = fmaxf(M, ml[(int64_t)s * at.Hq].x);
-  float num = 0.f, den = 0.f;
-  if (M != -INFINITY) {
-    const float* po = at.part_o + (int64_t)b * at.S * at.Hq * at.Dv + i;
-    for (int s = 0; s < at.S; ++s) {
-      const float2 v = ml[(int64_t)s * at.Hq];
-      if (v.x == -INFINITY) continue;
-      const float w = __expf(v.x - M);
-      num = fmaf(w, po[(int64_t)s * at.Hq * at.Dv], num);
-      den = fmaf(w, v.y, den);
+constexpr int kCombBlock = 64;
+
+// out[b][h][v] = sum_s w_s o_s[h][v] with w_s = e^(m_s - M) / sum_s e^(m_s - M) l_s,
+// M = max_s m_s, splits summed in index order. FRAG: partials in the matrix-core
+// accumulator order (4 heads per 16-byte element, see AttnMfma); otherwise
+// row-major [head][value]. Each workgroup (one wave) first forms the split
+// weights of every head, then combines 64 elements.
+template <bool FRAG>
+__global__ __launch_bounds__(kCombBlock) void k_combine(AttnArgs at, const int32_t* __restrict__ part_bad,
+                                                       RowStats* __restrict__ stats, float* __restrict__ out) {
+  __shared__ __align__(16) float wsh[64][kMaxSplits];  // split weights per head (0 past S)
+  const int b = blockIdx.y, lane = threadIdx.x;
+  const int S = at.S, Hq = at.Hq, Dv = at.Dv;
+  const int HP = FRAG ? (Hq + 15) / 16 * 16 : Hq;
+  DSA_MARK(2, 0);
+  {
+    // lane h forms the weights of head h over the splits (no cross-lane work)
+    const int h = lane < Hq ? lane : Hq - 1;
+    float2 ml[kMaxSplits];
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s) {
+      const int sc = s < S ? s : S - 1;
+      ml[s] = at.part_ml[((int64_t)b * S + sc) * Hq + h];
     }
+    float M = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s) M = fmaxf(M, s < S ? ml[s].x : -INFINITY);
+    float e[kMaxSplits], den = 0.f;
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s) {
+      e[s] = (s < S && ml[s].x != -INFINITY) ? __expf(ml[s].x - M) : 0.f;
+      den = fmaf(e[s], ml[s].y, den);
+    }
+    const float inv = (lane < Hq && den > 0.f) ? 1.f / den : 0.f;
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; s += 4)
+      *(v4f*)&wsh[lane][s] = v4f{e[s] * inv, e[s + 1] * inv, e[s + 2] * inv, e[s + 3] * inv};
   }
-  out[(int64_t)b * at.Hq * at.Dv + i] = den > 0.f ? num / den : 0.f;
+  if (part_bad != nullptr && blockIdx.x == 0) {
+    const uint32_t nb = wave_sum_u32(lane < S ? (uint32_t)part_bad[(int64_t)b * S + lane] : 0u);
+    if (lane == 0) stats[b].bad_indices = (int32_t)nb;
+  }
+  lds_barrier();
+  DSA_MARK(2, 2);
+  const int64_t split_stride = (int64_t)HP * Dv;
+  const float* po = at.part_o + (int64_t)b * S * split_stride;
+  if (FRAG) {
+    const int e4 = blockIdx.x * kCombBlock + lane;  // 16-byte element index
+    if (e4 * 4 >= HP * Dv) return;
+    const int tiles = Dv / 16;
+    const int tile = e4 >> 6, l = e4 & 63;
+    const int h0 = 16 * (tile / tiles) + 4 * (l >> 4), v = 16 * (tile % tiles) + (l & 15);
+    v4f part[kMaxSplits];
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s) {
+      const int sc = s < S ? s : S - 1;  // weight 0 past S
+      part[s] = *(const v4f*)(po + sc * split_stride + (int64_t)e4 * 4);
+    }
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const v4f* wrow = reinterpret_cast<const v4f*>(wsh[h0 + r]);
+#pragma unroll
+      for (int s4 = 0; s4 < kMaxSplits / 4; ++s4) {
+        const v4f w = wrow[s4];
+        acc[r] = fmaf(w[0], part[4 * s4][r], acc[r]);
+        acc[r] = fmaf(w[1], part[4 * s4 + 1][r], acc[r]);
+        acc[r] = fmaf(w[2], part[4 * s4 + 2][r], acc[r]);
+        acc[r] = fmaf(w[3], part[4 * s4 + 3][r], acc[r]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (h0 + r < Hq) out[((int64_t)b * Hq + h0 + r) * Dv + v] = acc[r];
+  } else {
+    const int e = blockIdx.x * kCombBlock + lane;
+    if (e >= Hq * Dv) return;
+    const int h = e / Dv;
+    float part[kMaxSplits];
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s) {
+      const int sc = s < S ? s : S - 1;
+      part[s] = po[sc * split_stride + e];
+    }
+    const v4f* wrow = reinterpret_cast<const v4f*>(wsh[h]);
+    float acc = 0.f;
+#pragma unroll
+    for (int s4 = 0; s4 < kMaxSplits / 4; ++s4) {
+      const v4f w = wrow[s4];
+      acc = fmaf(w[0], part[4 * s4], acc);
+      acc = fmaf(w[1], part[4 * s4 + 1], acc);
+      acc = fmaf(w[2], part[4 * s4 + 2], acc);
+      acc = fmaf(w[3], part[4 * s4 + 3], acc);
+    }
+    out[(int64_t)b * Hq * Dv + e] = acc;
+  }
+  DSA_MARK(2, 1);
 }
 
 hipError_t launch_combine(const AttnArgs& at, const int32_t* part_bad, RowStats* stats, float* out,
                           int B, hipStream_t s) {
-  const int grid = (at.Hq * at.Dv + kBlock - 1) / kBlock;
-  hipLaunchKernelGGL(k_combine, dim3(grid, B), dim3(kBlock), 0, s, at, part_bad, stats, out);
+  if (at.frag) {
+    const int hp = (at.Hq + 15) / 16 * 16;
+    const int grid = (hp * at.Dv / 4 + kCombBlock - 1) / kCombBlock;
+    hipLaunchKernelGGL(k_combine<true>, dim3(grid, B), dim3(kCombBlock), 0, s, at, part_bad, stats, out);
+  } else {
+    const int grid = (at.Hq * at.Dv + kCombBlock - 1) / kCombBlock;
+    hipLaunchKernelGGL(k_combine<false>, dim3(grid, B), dim3(kCombBlock), 0, s, at, part_bad, stats, out);
+  }
   return hipGetLastError();
 }
 
