@@ -10,13 +10,13 @@ Cold cache by construction: the step cycles through --sets independent input set
 (keys, latent cache, queries), so by the time a set comes back the other sets have
 streamed far more than the 256 MB Infinity Cache holds. The timed steps are HIP
 graph replays (one graph holds one step per set), bracketed by synchronisations.
-A second, eager pass over the same steps records HIP events between the stages
-(dsa_decode_step_timed) to time the dominant kernel, the indexer pass, live.
+A second, eager pass over the same steps has the runtime stamp HIP events with the
+start and end of each stage's kernel (dsa_decode_step_timed), which times the
+indexer pass and the selection + attention pass live, kernel by kernel.
 
 Prints one JSON line (see the design doc for every field).
 """
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -29,22 +29,11 @@ sys.path.insert(0, ROOT)
 
 METRIC = "DSA decode step µs & indexer+gather HBM GB/s, top-2048 at 62k/300k ctx"
 HBM_PEAK_GBPS = 8000.0
-SCORE_SOURCES = ["sparse_attention_decode_scores_amd/csrc/score.hip",
-                 "sparse_attention_decode_scores_amd/csrc/common.h",
-                 "sparse_attention_decode_scores_amd/csrc/chunk_select.h"]
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "score_kernel_hbm_counters.json")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "decode_step_ctx300k_hbm_counters.json")
 
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
-
-
-def score_kernel_sha():
-    h = hashlib.sha256()
-    for p in SCORE_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
 
 
 def device_set(torch, c, s, name):
@@ -95,13 +84,35 @@ def score_kernel_bytes(c):
     return c["N"] * c["Di"] + c["B"] * c["N"] * 4 + c["B"] * c["Hi"] * (c["Di"] + 1)
 
 
-def cpu_baseline(cfg_name, layers, budget_s):
+def gather_pass_bytes(c):
+    """Algorithmic bytes of one launch of the selection + attention pass: the k selected
+    latent rows of every query row (Dk values each) and the attention queries. Candidate
+    keys and split partials are working data of this design, not counted."""
+    esz = 4 if c["dtype"] == "f32" else 2
+    rows = sum(min(c["k"], int(n)) for n in c["ctx_len"])
+    return rows * c["Dk"] * esz + c["B"] * c["Hq"] * c["Dk"] * esz
+
+
+def measured_traffic(config):
+    """HBM bytes per launch of each libdsa kernel from the committed counter summary, or
+    None for a kernel whose sources changed since the counters were taken."""
+    from sparse_attention_decode_scores_amd.profsum import library_source_sha
+    if not os.path.exists(PMC_SUMMARY):
+        return {}
+    with open(PMC_SUMMARY) as f:
+        pmc = json.load(f)
+    if pmc.get("kernel_source_sha") != library_source_sha() or pmc.get("config") != config:
+        return {}
+    return {k: v.get("hbm_bytes_per_launch") for k, v in pmc.get("kernels", {}).items()}
+
+
+def cpu_baseline(name, layers, budget_s):
     import oracle
     from sparse_attention_decode_scores_amd import inputs
     runs, spent, per_layer = 0, 0.0, []
     layer = 0
     while True:
-        c = inputs.make(cfg_name, layer % layers)
+        c = inputs.make(name, layer % layers)
         t = time.perf_counter()
         oracle.decode_step(c["iq"], c["iw"], c["ik"], c["q"], c["kv"], c["ctx_len"], c["k"], c["Dv"],
                            c["scale"])
@@ -115,7 +126,7 @@ def cpu_baseline(cfg_name, layers, budget_s):
     us_step = float(np.mean(per_layer)) * layers * 1e6
     sample = ("%d oracle decode-step call(s) on layer input(s) of %s (%d positions, k=%d), "
               "%.1f s of CPU work; step = %d layer(s) x mean per-layer time"
-              % (runs, cfg_name, c["N"], c["k"], spent, layers))
+              % (runs, name, c["N"], c["k"], spent, layers))
     return {"value": us_step, "unit": "us", "cores": 1, "kind": "oracle", "sample": sample}
 
 
@@ -124,13 +135,13 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=240)
     ap.add_argument("--warmup", type=int, default=24)
-    ap.add_argument("--config", default="cfg3", choices=["cfg1", "cfg2", "cfg3", "cfg4"])
+    ap.add_argument("--config", default="ctx300k", choices=["ctx16k", "ctx62k_11layers", "ctx300k", "verify8_ctx131k"])
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = default per workload)")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run a plain 256 MiB device copy (scale reference for HBM counters)")
+                    help="also run a plain copy kernel of 256 MiB (scale reference for HBM counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -164,13 +175,13 @@ def main():
     torch.cuda.synchronize()
     log("inputs resident: %.2f GB" % (torch.cuda.memory_allocated() / 1e9))
 
-    def step(s, stage_events=None):
+    def step(s, kernel_events=None):
         for l in range(layers):
             d = sets[s][l]
-            ev = None if stage_events is None else stage_events[l]
+            ev = None if kernel_events is None else kernel_events[l]
             binding.dsa_decode_step(d["iq"], d["iw"], d["ik"], d["q"], d["kv"], host[l]["ctx_len"], k,
                                     Dv, c["scale"], scores=scores, idx=idx, out=out, workspace=ws,
-                                    stage_events=ev)
+                                    kernel_events=ev)
 
     for i in range(args.warmup):
         step(i % R)
@@ -217,8 +228,8 @@ def main():
     us_step = wall_s * 1e6 / K
     log("timed %d steps: wall %.3f ms, events %.3f ms -> %.2f us/step" % (K, wall_s * 1e3, gpu_ms, us_step))
 
-    # ---- stage timing pass (eager, events between the stages)
-    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(layers)]
+    # ---- kernel timing pass (eager; events carry each stage kernel's own start and end)
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(layers)]
            for _ in range(K)]
     for per_step in evs:  # torch creates the HIP event on first record
         for per_layer in per_step:
@@ -228,12 +239,12 @@ def main():
     for i in range(K):
         step(i % R, evs[i])
     torch.cuda.synchronize()
-    st = np.array([[[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
+    st = np.array([[[e[0].elapsed_time(e[1]), e[2].elapsed_time(e[3]), e[4].elapsed_time(e[5])]
                     for e in per_step] for per_step in evs]) * 1e3  # us [K][layers][3]
     score_us = float(st[:, :, 0].mean())
     select_us = float(st[:, :, 1].mean())
     combine_us = float(st[:, :, 2].mean())
-    log("stage events (eager): score %.2f us, select+attend %.2f us, combine %.2f us"
+    log("kernel durations (eager, HIP events): score %.2f us, select+attend %.2f us, combine %.2f us"
         % (score_us, select_us, combine_us))
     stats = binding.dsa_read_stats(ws, B)
 
@@ -241,18 +252,15 @@ def main():
         src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(5):
-            dst.copy_(src)
+            torch.neg(src, out=dst)
         torch.cuda.synchronize()
-        log("copy calibration: 5 x 256 MiB device copies")
+        log("copy calibration: 5 x torch.neg over 256 MiB")
 
     kb = score_kernel_bytes(c)
     achieved = kb / (score_us * 1e-6) / 1e9
-    traffic = None
-    if os.path.exists(PMC_SUMMARY):
-        with open(PMC_SUMMARY) as f:
-            pmc = json.load(f)
-        if pmc.get("kernel_source_sha") == score_kernel_sha() and pmc.get("config") == args.config:
-            traffic = pmc.get("hbm_bytes_per_launch")
+    traffic = measured_traffic(args.config)
+    gb = gather_pass_bytes(c)
+    g_achieved = gb / (select_us * 1e-6) / 1e9
     keys, sc_bytes, gather, small = essential_bytes(c)
     step_bytes = layers * (keys + sc_bytes + gather + small)
 
@@ -290,12 +298,23 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": traffic,
+            "traffic": traffic.get("k_score"),
             "algorithmic_bytes_per_launch": kb,
             "launch_us": round(score_us, 3),
         },
+        "roofline_gather": {
+            "bound": "hbm",
+            "kernel": "selection + sparse attention pass (k_select: exact top-k, row gather, split-K attention)",
+            "achieved": round(g_achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(g_achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic.get("k_select"),
+            "algorithmic_bytes_per_launch": gb,
+            "launch_us": round(select_us, 3),
+        },
         "cpu_baseline": cpu,
-        "stages_us_eager_events": {"score": round(score_us, 3), "select_attend": round(select_us, 3),
+        "kernel_us_events": {"score": round(score_us, 3), "select_attend": round(select_us, 3),
                                    "combine": round(combine_us, 3)},
         "step_essential_bytes": step_bytes,
         "step_essential_GBps": round(step_bytes / (us_step * 1e-6) / 1e9, 1),

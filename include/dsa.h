@@ -164,19 +164,22 @@ dsa_status dsa_decode_step(const int8_t* iq, const int8_t* iw, const int8_t* ik,
                            size_t ws_bytes, unsigned flags, hipStream_t stream);
 
 /*
- * dsa_decode_step with stage timing: when stage_events is not NULL it must point
- * to 4 events created on the current device; they are recorded on `stream`
- * before stage 1, after stage 1, after stage 2 (selection and the attention
- * splits share one launch) and after the final combine. Everything else is as
- * for dsa_decode_step, which is this call with stage_events = NULL. For
- * profilers and benchmarks; the events add a few queue packets per step.
+ * dsa_decode_step with per-kernel timing: when kernel_events is not NULL it must
+ * point to 6 events created on the current device. Events 2i and 2i+1 receive
+ * the start and end timestamps of stage i's kernel dispatch (i = 0: indexer
+ * scores with per-chunk candidates; 1: selection and attention splits, one
+ * launch; 2: combine of the splits), so hipEventElapsedTime(e[2i], e[2i+1]) is
+ * that kernel's own duration without queueing or launch gaps. When the indexer
+ * stage needs several launches (many query rows), the pair spans all of them.
+ * Everything else is as for dsa_decode_step, which is this call with
+ * kernel_events = NULL. Returns DSA_ERR_INVALID_ARG if any of the 6 is NULL.
  */
 dsa_status dsa_decode_step_timed(const int8_t* iq, const int8_t* iw, const int8_t* ik,
                                  const void* q, const void* kv, const int32_t* ctx_len, int B,
                                  int Hi, int Di, int Hq, int Dk, int Dv, int64_t N, int k,
                                  float scale, dsa_dtype dt, int32_t* scores, int32_t* idx,
                                  float* out, void* ws, size_t ws_bytes, unsigned flags,
-                                 hipStream_t stream, hipEvent_t* stage_events);
+                                 hipStream_t stream, hipEvent_t* kernel_events);
 
 /*
  * Copies the per-row stats of the last call that used `ws` into stats[0..B).

@@ -190,12 +190,12 @@ def dsa_sparse_attn(q, kv, idx, Dv, scale, out=None, workspace=None, stream=None
 
 
 def dsa_decode_step(iq, iw, ik, q, kv, ctx_len, k, Dv, scale, scores=None, idx=None, out=None,
-                    workspace=None, flags=0, stream=None, stage_events=None):
+                    workspace=None, flags=0, stream=None, kernel_events=None):
     """The three stages through one layer; returns (scores, idx, out).
 
-    stage_events: optional sequence of 4 torch.cuda.Event(enable_timing=True), recorded
-    on the stream before stage 1, after stage 1, after stage 2 and at the end
-    (dsa_decode_step_timed)."""
+    kernel_events: optional sequence of 6 torch.cuda.Event(enable_timing=True), each
+    already recorded once (torch creates the HIP event lazily). Events 2i, 2i+1 take
+    the start and end of stage i's kernel (dsa_decode_step_timed)."""
     torch = _torch()
     lib = load_library()
     B, Hi, Di = iq.shape
@@ -220,12 +220,12 @@ def dsa_decode_step(iq, iw, ik, q, kv, ctx_len, k, Dv, scale, scores=None, idx=N
             _dev(idx, "idx", torch.int32), _dev(out, "out", torch.float32),
             _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), flags,
             _stream(stream)]
-    if stage_events is None:
+    if kernel_events is None:
         rc = lib.dsa_decode_step(*args)
     else:
-        if len(stage_events) != 4:
-            raise ValueError("stage_events must hold 4 events")
-        evs = (ctypes.c_void_p * 4)(*[e.cuda_event for e in stage_events])
+        if len(kernel_events) != 6:
+            raise ValueError("kernel_events must hold 6 events")
+        evs = (ctypes.c_void_p * 6)(*[e.cuda_event for e in kernel_events])
         rc = lib.dsa_decode_step_timed(*args, ctypes.cast(evs, ctypes.c_void_p))
     _check(rc, "dsa_decode_step")
     return scores, idx, out

@@ -135,7 +135,8 @@ dsa_status hip_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_
 
 dsa_status run_scores(const int8_t* iq, const int8_t* iw, const int8_t* ik, const RowLens& lens,
                       int B, int Hi, int Di, int64_t N, int nmax, int32_t* scores, bool cand,
-                      const ChunkPlan& cp, uint64_t* cbuf, uint64_t* xbuf, hipStream_t s) {
+                      const ChunkPlan& cp, uint64_t* cbuf, uint64_t* xbuf, hipStream_t s,
+                      KTimer t = {}) {
   ScoreArgs a;
   a.iq = iq;
   a.iw = iw;
@@ -161,7 +162,10 @@ dsa_status run_scores(const int8_t* iq, const int8_t* iw, const int8_t* ik, cons
   for (int b0 = 0; b0 < B; b0 += bg) {
     a.b0 = b0;
     a.Bg = B - b0 < bg ? B - b0 : bg;
-    hipError_t e = launch_score(a, MT, KT, cand, a.G, s);
+    KTimer tl;  // the first launch starts the stage's time, the last one ends it
+    if (b0 == 0) tl.start = t.start;
+    if (b0 + bg >= B) tl.stop = t.stop;
+    hipError_t e = launch_score(a, MT, KT, cand, a.G, s, tl);
     if (e != hipSuccess) return DSA_ERR_HIP;
   }
   return DSA_OK;
@@ -312,7 +316,7 @@ dsa_status dsa_decode_step_timed(const int8_t* iq, const int8_t* iw, const int8_
                                  int Hi, int Di, int Hq, int Dk, int Dv, int64_t N, int k,
                                  float scale, dsa_dtype dt, int32_t* scores, int32_t* idx,
                                  float* out, void* ws, size_t ws_bytes, unsigned flags,
-                                 hipStream_t stream, hipEvent_t* stage_events) {
+                                 hipStream_t stream, hipEvent_t* kernel_events) {
   RowLens lens;
   int nmax = 0;
   dsa_status st = check_rows(ctx_len, B, N, &lens, &nmax);
@@ -324,28 +328,24 @@ dsa_status dsa_decode_step_timed(const int8_t* iq, const int8_t* iw, const int8_
   if ((st = check_attn(q, kv, Hq, Dk, Dv, scale, dt, &ch)) != DSA_OK) return st;
   const Layout L = layout(B, N, k, Hq, Dv);
   if ((st = check_ws(ws, ws_bytes, L)) != DSA_OK) return st;
-  if (stage_events != nullptr)
-    for (int i = 0; i < 4; ++i)
-      if (stage_events[i] == nullptr) return DSA_ERR_INVALID_ARG;
-  auto mark = [&](int i) {
-    return stage_events == nullptr || hipEventRecord(stage_events[i], stream) == hipSuccess;
-  };
+  KTimer tm[3];
+  if (kernel_events != nullptr) {
+    for (int i = 0; i < 6; ++i)
+      if (kernel_events[i] == nullptr) return DSA_ERR_INVALID_ARG;
+    for (int i = 0; i < 3; ++i) tm[i] = KTimer{kernel_events[2 * i], kernel_events[2 * i + 1]};
+  }
   uint8_t* w = static_cast<uint8_t*>(ws);
   const ChunkPlan cp = chunk_plan(nmax, k);
   const bool have = cand_fits(Hi, Di, B, cp, true) && !(flags & DSA_FLAG_FORCE_FALLBACK);
-  if (!mark(0)) return DSA_ERR_HIP;
   st = run_scores(iq, iw, ik, lens, B, Hi, Di, N, nmax, scores, have, cp,
                   reinterpret_cast<uint64_t*>(w + L.cand), reinterpret_cast<uint64_t*>(w + L.xc),
-                  stream);
+                  stream, tm[0]);
   if (st != DSA_OK) return st;
-  if (!mark(1)) return DSA_ERR_HIP;
   const SelArgs sa = sel_args(scores, lens, N, k, idx, w, L, cp, have, flags);
   AttnArgs at = attn_args(q, kv, N, Hq, Dk, Dv, scale, k, w, L);
   at.frag = ch.kind == ATTN_MFMA_BF16;
-  if (launch_select(sa, at, ch, B, stream) != hipSuccess) return DSA_ERR_HIP;
-  if (!mark(2)) return DSA_ERR_HIP;
-  if (launch_combine(at, nullptr, nullptr, out, B, stream) != hipSuccess) return DSA_ERR_HIP;
-  return mark(3) ? DSA_OK : DSA_ERR_HIP;
+  if (launch_select(sa, at, ch, B, stream, tm[1]) != hipSuccess) return DSA_ERR_HIP;
+  return hip_status(launch_combine(at, nullptr, nullptr, out, B, stream, tm[2]));
 }
 
 dsa_status dsa_decode_step(const int8_t* iq, const int8_t* iw, const int8_t* ik, const void* q,

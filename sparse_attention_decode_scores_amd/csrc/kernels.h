@@ -1,6 +1,7 @@
 // Internal launch interface between the C API (api.cpp) and the kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -10,6 +11,22 @@
 namespace dsa {
 
 __host__ __device__ constexpr size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
+
+// Optional timing of one launch: the runtime stamps `start` with the dispatch's
+// begin time and `stop` with its end time (the timestamps a kernel trace shows).
+struct KTimer {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
+template <class F, class... A>
+inline hipError_t launch_timed(F fn, dim3 grid, dim3 block, size_t lds, hipStream_t s, KTimer t,
+                               A... args) {
+  if (t.start != nullptr || t.stop != nullptr)
+    hipExtLaunchKernelGGL(fn, grid, block, (uint32_t)lds, s, t.start, t.stop, 0u, args...);
+  else
+    hipLaunchKernelGGL(fn, grid, block, lds, s, args...);
+  return hipGetLastError();
+}
 
 struct ScoreArgs {
   const int8_t* iq;
@@ -28,7 +45,8 @@ struct ScoreArgs {
   int m;           // candidates kept per chunk
 };
 
-hipError_t launch_score(const ScoreArgs& a, int MT, int KT, bool cand, int grid, hipStream_t s);
+hipError_t launch_score(const ScoreArgs& a, int MT, int KT, bool cand, int grid, hipStream_t s,
+                        KTimer t = {});
 int score_max_chunk();        // longest chunk the score kernel's candidate pass takes
 int chunk_cand_max_chunk();   // the same for the stand-alone candidate kernel
 size_t score_lds_bytes(int MT, int KT, int Bg, int P, bool cand);
@@ -85,10 +103,11 @@ struct AttnChoice {
 AttnChoice choose_attn(int dt_bf16, int Hq, int Dk, int Dv);
 // LDS bytes of one workgroup of the selection kernel (largest of the two roles).
 size_t select_lds_bytes(AttnChoice ch, int Hq, int Dk, int k);
-hipError_t launch_select(const SelArgs& a, const AttnArgs& at, AttnChoice ch, int B, hipStream_t s);
+hipError_t launch_select(const SelArgs& a, const AttnArgs& at, AttnChoice ch, int B, hipStream_t s,
+                         KTimer t = {});
 hipError_t launch_attend_idx(const int32_t* idx, int k, int32_t* part_bad, const AttnArgs& at,
                              AttnChoice ch, int B, hipStream_t s);
 hipError_t launch_combine(const AttnArgs& at, const int32_t* part_bad, RowStats* stats, float* out,
-                          int B, hipStream_t s);
+                          int B, hipStream_t s, KTimer t = {});
 
 }  // namespace dsa

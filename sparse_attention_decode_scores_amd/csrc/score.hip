@@ -176,28 +176,28 @@ size_t score_lds_bytes(int MT, int KT, int Bg, int P, bool cand) {
 }
 
 template <int MT, int KT, bool CAND, bool ONE>
-static hipError_t launch_score_t(const ScoreArgs& a, int grid, size_t lds, hipStream_t s) {
+static hipError_t launch_score_t(const ScoreArgs& a, int grid, size_t lds, hipStream_t s, KTimer t) {
   auto fn = k_score<MT, KT, CAND, ONE>;
   hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fn, dim3(grid), dim3(kScoreBlock), lds, s, a);
-  return hipGetLastError();
+  return launch_timed(fn, dim3(grid), dim3(kScoreBlock), lds, s, t, a);
 }
 
 template <int MT, int KT>
-static hipError_t launch_score_mk(const ScoreArgs& a, bool cand, int grid, size_t lds, hipStream_t s) {
+static hipError_t launch_score_mk(const ScoreArgs& a, bool cand, int grid, size_t lds, hipStream_t s,
+                                  KTimer t) {
   const bool one = a.Bg == 1;
-  if (cand) return one ? launch_score_t<MT, KT, true, true>(a, grid, lds, s)
-                       : launch_score_t<MT, KT, true, false>(a, grid, lds, s);
-  return one ? launch_score_t<MT, KT, false, true>(a, grid, lds, s)
-             : launch_score_t<MT, KT, false, false>(a, grid, lds, s);
+  if (cand) return one ? launch_score_t<MT, KT, true, true>(a, grid, lds, s, t)
+                       : launch_score_t<MT, KT, true, false>(a, grid, lds, s, t);
+  return one ? launch_score_t<MT, KT, false, true>(a, grid, lds, s, t)
+             : launch_score_t<MT, KT, false, false>(a, grid, lds, s, t);
 }
 
-hipError_t launch_score(const ScoreArgs& a, int MT, int KT, bool cand, int grid, hipStream_t s) {
+hipError_t launch_score(const ScoreArgs& a, int MT, int KT, bool cand, int grid, hipStream_t s, KTimer t) {
   const size_t lds = score_lds_bytes(MT, KT, a.Bg, a.P, cand);
 #define DSA_SCORE_CASE(M, K) \
-  if (MT == M && KT == K) return launch_score_mk<M, K>(a, cand, grid, lds, s);
+  if (MT == M && KT == K) return launch_score_mk<M, K>(a, cand, grid, lds, s, t);
   DSA_SCORE_CASE(1, 1) DSA_SCORE_CASE(1, 2) DSA_SCORE_CASE(1, 3) DSA_SCORE_CASE(1, 4)
   DSA_SCORE_CASE(1, 5) DSA_SCORE_CASE(1, 6) DSA_SCORE_CASE(1, 7) DSA_SCORE_CASE(1, 8)
   DSA_SCORE_CASE(2, 1) DSA_SCORE_CASE(2, 2) DSA_SCORE_CASE(2, 3) DSA_SCORE_CASE(2, 4)

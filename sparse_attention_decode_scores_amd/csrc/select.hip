@@ -464,14 +464,13 @@ static size_t select_lds_t(int Hq, int Dk, int k) {
 }
 
 template <class Attn>
-static hipError_t launch_select_t(const SelArgs& a, const AttnArgs& at, int B, hipStream_t s) {
+static hipError_t launch_select_t(const SelArgs& a, const AttnArgs& at, int B, hipStream_t s, KTimer t) {
   const size_t lds = select_lds_t<Attn>(at.Hq, at.Dk, a.k);
   auto fn = k_select<Attn>;
   hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fn, dim3(at.S + a.R, B), dim3(kSelBlock), lds, s, a, at);
-  return hipGetLastError();
+  return launch_timed(fn, dim3(at.S + a.R, B), dim3(kSelBlock), lds, s, t, a, at);
 }
 
 // ------------------------------------------------------------------ attention over given indices
@@ -598,8 +597,9 @@ size_t select_lds_bytes(AttnChoice ch, int Hq, int Dk, int k) {
   return select_lds_dispatch(ch, Hq, Dk, k);
 }
 
-hipError_t launch_select(const SelArgs& a, const AttnArgs& at, AttnChoice ch, int B, hipStream_t s) {
-  DSA_ATTN_DISPATCH(launch_select_t, a, at, B, s)
+hipError_t launch_select(const SelArgs& a, const AttnArgs& at, AttnChoice ch, int B, hipStream_t s,
+                         KTimer t) {
+  DSA_ATTN_DISPATCH(launch_select_t, a, at, B, s, t)
 }
 
 hipError_t launch_attend_idx(const int32_t* idx, int k, int32_t* part_bad, const AttnArgs& at,
@@ -710,16 +710,14 @@ __global__ __launch_bounds__(kCombBlock) void k_combine(AttnArgs at, const int32
 }
 
 hipError_t launch_combine(const AttnArgs& at, const int32_t* part_bad, RowStats* stats, float* out,
-                          int B, hipStream_t s) {
+                          int B, hipStream_t s, KTimer t) {
   if (at.frag) {
     const int hp = (at.Hq + 15) / 16 * 16;
     const int grid = (hp * at.Dv / 4 + kCombBlock - 1) / kCombBlock;
-    hipLaunchKernelGGL(k_combine<true>, dim3(grid, B), dim3(kCombBlock), 0, s, at, part_bad, stats, out);
-  } else {
-    const int grid = (at.Hq * at.Dv + kCombBlock - 1) / kCombBlock;
-    hipLaunchKernelGGL(k_combine<false>, dim3(grid, B), dim3(kCombBlock), 0, s, at, part_bad, stats, out);
+    return launch_timed(k_combine<true>, dim3(grid, B), dim3(kCombBlock), 0, s, t, at, part_bad, stats, out);
   }
-  return hipGetLastError();
+  const int grid = (at.Hq * at.Dv + kCombBlock - 1) / kCombBlock;
+  return launch_timed(k_combine<false>, dim3(grid, B), dim3(kCombBlock), 0, s, t, at, part_bad, stats, out);
 }
 
 }  // namespace dsa

@@ -5,25 +5,28 @@ method's arithmetic lives here.
 Workloads (no real GLM-5.3-Flash weights or caches are available, so every array
 is synthetic with the shapes of the model's DSA layers):
 
-  cfg0   B=1, context 4,096, k=256; indexer 4 heads x 64, query and keys int8
-         uniform on [-8, 8], head weights uniform on [1, 4]; attention 8 heads x 64,
-         one shared fp32 N(0,1) row per position used as key and value; scale 1/8.
-  cfg1   B=1, context 16,384, k=2,048; indexer 64 heads x 128 with one shared
-         128-dim key per position, int8 uniform on [-16, 16], head weights uniform
-         on [1, 8]; attention 16 heads over a shared latent row of 512 latent + 64
-         rope values per position, bf16 N(0,1)*0.5; output 512 values per head;
-         scale 1/sqrt(576) = 1/24.
-  cfg2   cfg1 shapes at context 62,464, eleven independent layers (own seeds).
-  cfg3   cfg1 shapes at context 300,000 with indexer keys on the coarse grid
-         {-2..2}.
-  cfg4   width-8 verify block: B=8 over a shared 131,072-position cache; row r
-         sees ctx_len = 131,065 + r.
-  cfg3T  cfg3 with every key row drawn from a pool of 512 rows, so that many
-         positions share a score exactly (ties at the selection threshold).
-  cfgZ   cfg1 with an all-zero indexer query: every score is 0.
+  tiny_4k           B=1, context 4,096, k=256; indexer 4 heads x 64, query and keys
+                    int8 uniform on [-8, 8], head weights uniform on [1, 4]; attention
+                    8 heads x 64, one shared fp32 N(0,1) row per position used as key
+                    and value; scale 1/8.
+  ctx16k            B=1, context 16,384, k=2,048; indexer 64 heads x 128 with one
+                    shared 128-dim key per position, int8 uniform on [-16, 16], head
+                    weights uniform on [1, 8]; attention 16 heads over a shared latent
+                    row of 512 latent + 64 rope values per position, bf16 N(0,1)*0.5;
+                    output 512 values per head; scale 1/sqrt(576) = 1/24.
+  ctx62k_11layers   ctx16k shapes at context 62,464, eleven independent layers (own
+                    seeds) per step.
+  ctx300k           ctx16k shapes at context 300,000 with indexer keys on the coarse
+                    grid {-2..2}.
+  verify8_ctx131k   width-8 verify block: B=8 over a shared 131,072-position cache;
+                    row r sees ctx_len = 131,065 + r.
+  ctx300k_tiepool   ctx300k with every key row drawn from a pool of 512 rows, so that
+                    many positions share a score exactly (ties at the threshold).
+  ctx16k_zeroquery  ctx16k with an all-zero indexer query: every score is 0.
 
-Integer ranges are inclusive. Seeds: numpy PCG64 ``default_rng(1000 + c)`` for
-cfg c, ``2000 + l`` for layer l of cfg2, 1030 for cfg3T, 1090 for cfgZ; the integer
+Integer ranges are inclusive. Seeds (numpy PCG64 ``default_rng(seed)``): tiny_4k
+1000, ctx16k 1001, ctx300k 1003, verify8_ctx131k 1004, ctx300k_tiepool 1030,
+ctx16k_zeroquery 1090, and 2000 + l for layer l of ctx62k_11layers; the integer
 arrays are drawn from it in the order iq, iw, ik. The normal arrays are drawn in
 blocks of 16,384 rows, block j of q from ``default_rng([seed, 1, j])`` and of kv
 from ``default_rng([seed, 2, j])`` (so they can be drawn on several threads).
@@ -33,23 +36,18 @@ fp32 draw).
 """
 import numpy as np
 
+_LAYER = dict(Hi=64, Di=128, Hq=16, Dk=576, Dv=512, dtype="bf16", scale=1.0 / 24.0, qk_range=16,
+              w_range=(1, 8), key_range=16, layers=1)
+
 CONFIGS = {
-    "cfg0": dict(B=1, N=4096, k=256, Hi=4, Di=64, Hq=8, Dk=64, Dv=64, dtype="f32",
-                 scale=1.0 / 8.0, qk_range=8, w_range=(1, 4), key_range=8, layers=1, seed=1000),
-    "cfg1": dict(B=1, N=16384, k=2048, Hi=64, Di=128, Hq=16, Dk=576, Dv=512, dtype="bf16",
-                 scale=1.0 / 24.0, qk_range=16, w_range=(1, 8), key_range=16, layers=1, seed=1001),
-    "cfg2": dict(B=1, N=62464, k=2048, Hi=64, Di=128, Hq=16, Dk=576, Dv=512, dtype="bf16",
-                 scale=1.0 / 24.0, qk_range=16, w_range=(1, 8), key_range=16, layers=11, seed=2000),
-    "cfg3": dict(B=1, N=300000, k=2048, Hi=64, Di=128, Hq=16, Dk=576, Dv=512, dtype="bf16",
-                 scale=1.0 / 24.0, qk_range=16, w_range=(1, 8), key_range=2, layers=1, seed=1003),
-    "cfg4": dict(B=8, N=131072, k=2048, Hi=64, Di=128, Hq=16, Dk=576, Dv=512, dtype="bf16",
-                 scale=1.0 / 24.0, qk_range=16, w_range=(1, 8), key_range=16, layers=1, seed=1004),
-    "cfg3T": dict(B=1, N=300000, k=2048, Hi=64, Di=128, Hq=16, Dk=576, Dv=512, dtype="bf16",
-                  scale=1.0 / 24.0, qk_range=16, w_range=(1, 8), key_range=2, layers=1, seed=1030,
-                  key_pool=512),
-    "cfgZ": dict(B=1, N=16384, k=2048, Hi=64, Di=128, Hq=16, Dk=576, Dv=512, dtype="bf16",
-                 scale=1.0 / 24.0, qk_range=16, w_range=(1, 8), key_range=16, layers=1, seed=1090,
-                 zero_query=True),
+    "tiny_4k": dict(B=1, N=4096, k=256, Hi=4, Di=64, Hq=8, Dk=64, Dv=64, dtype="f32", scale=1.0 / 8.0,
+                    qk_range=8, w_range=(1, 4), key_range=8, layers=1, seed=1000),
+    "ctx16k": dict(_LAYER, B=1, N=16384, k=2048, seed=1001),
+    "ctx62k_11layers": dict(_LAYER, B=1, N=62464, k=2048, layers=11, seed=2000),
+    "ctx300k": dict(_LAYER, B=1, N=300000, k=2048, key_range=2, seed=1003),
+    "verify8_ctx131k": dict(_LAYER, B=8, N=131072, k=2048, seed=1004, verify_offsets=True),
+    "ctx300k_tiepool": dict(_LAYER, B=1, N=300000, k=2048, key_range=2, seed=1030, key_pool=512),
+    "ctx16k_zeroquery": dict(_LAYER, B=1, N=16384, k=2048, seed=1090, zero_query=True),
 }
 
 
@@ -82,7 +80,7 @@ def bf16_bits_to_f32(b):
 
 def ctx_lengths(name):
     c = CONFIGS[name]
-    if name == "cfg4":
+    if c.get("verify_offsets"):
         return np.array([c["N"] - 7 + r for r in range(c["B"])], np.int32)
     return np.full(c["B"], c["N"], np.int32)
 

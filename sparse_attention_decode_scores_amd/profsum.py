@@ -1,0 +1,177 @@
+"""Summaries of rocprofv3 results for the libdsa kernels (host-side, no GPU needed).
+
+Reads the rocpd SQLite databases that `rocprofv3 -d DIR -o NAME` writes
+(DIR/NAME_results.db) and writes short text summaries:
+
+  stats     per-kernel dispatch count and duration of a --kernel-trace --stats run
+  counters  HBM bytes per dispatch of each libdsa kernel from two --pmc runs (FETCH_SIZE,
+            then WRITE_SIZE), each scaled by what the same counter reads for a plain
+            copy kernel of known size run in the same process (torch.neg over 64 Mi fp32
+            values: 256 MiB read, 256 MiB written)
+
+The counter summary records a hash of the kernel sources it was taken from; a
+reader treats it as stale once the sources change.
+"""
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sqlite3
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+KERNEL_SOURCES = sorted(
+    [os.path.relpath(p, ROOT) for p in glob.glob(os.path.join(ROOT, "sparse_attention_decode_scores_amd", "csrc", "*"))
+     if p.endswith((".hip", ".h"))] + ["include/dsa.h"])
+LIB_KERNELS = ("k_score", "k_select", "k_combine", "k_chunk_cand", "k_attend_idx")
+COPY_MATCH = "neg_kernel"
+COPY_BYTES = 64 * 1024 * 1024 * 4  # read and written by one calibration dispatch
+
+
+def library_source_sha():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(p.encode())
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _db(path):
+    if os.path.isdir(path):
+        found = sorted(glob.glob(os.path.join(path, "**", "*_results.db"), recursive=True))
+        if not found:
+            raise SystemExit("no *_results.db under %s" % path)
+        path = found[-1]
+    return sqlite3.connect("file:%s?mode=ro" % path, uri=True)
+
+
+def short_name(name):
+    for k in LIB_KERNELS:
+        if "dsa::" + k in name:
+            return k
+    return None
+
+
+def kernel_stats(db):
+    con = _db(db)
+    rows = con.execute("SELECT name, COUNT(*), AVG(end - start), MIN(end - start), MAX(end - start), "
+                       "SUM(end - start) FROM kernels GROUP BY name ORDER BY SUM(end - start) DESC").fetchall()
+    total = sum(r[5] for r in rows) or 1
+    return [{"name": r[0], "calls": r[1], "avg_us": r[2] / 1e3, "min_us": r[3] / 1e3, "max_us": r[4] / 1e3,
+             "pct": 100.0 * r[5] / total} for r in rows]
+
+
+def counter_per_kernel(db, counter):
+    """{kernel name: (dispatches, mean value per dispatch)} for one counter (KiB for *_SIZE)."""
+    con = _db(db)
+    rows = con.execute("SELECT kernel_name, dispatch_id, SUM(value) FROM counters_collection "
+                       "WHERE counter_name = ? GROUP BY kernel_name, dispatch_id", (counter,)).fetchall()
+    acc = {}
+    for name, _, v in rows:
+        n, s = acc.get(name, (0, 0.0))
+        acc[name] = (n + 1, s + float(v))
+    return {k: (n, s / n) for k, (n, s) in acc.items()}
+
+
+def _copy_value(per_kernel, counter):
+    cands = [(n, v) for k, (n, v) in per_kernel.items() if COPY_MATCH in k]
+    if not cands:
+        raise SystemExit("no %s dispatch (%s) in the %s run; kernels seen: %s"
+                         % (COPY_MATCH, "calibration copy", counter, sorted(per_kernel)[:20]))
+    n = sum(c[0] for c in cands)
+    return n, sum(c[0] * c[1] for c in cands) / n
+
+
+def cmd_stats(args):
+    rows = kernel_stats(args.db)
+    lines = ["# Kernel durations: %s" % args.title, "",
+             "Command (from the repository root on the GPU host):", "", "```", args.command, "```", "",
+             "| kernel | calls | avg us | min us | max us | % of kernel time |",
+             "|---|---:|---:|---:|---:|---:|"]
+    for r in rows[:args.top]:
+        nm = r["name"] if len(r["name"]) <= 90 else r["name"][:87] + "..."
+        lines.append("| `%s` | %d | %.2f | %.2f | %.2f | %.1f |"
+                     % (nm.replace("|", "\\|"), r["calls"], r["avg_us"], r["min_us"], r["max_us"], r["pct"]))
+    lines.append("")
+    if args.note:
+        lines += [args.note, ""]
+    with open(args.out, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
+def cmd_counters(args):
+    fetch = counter_per_kernel(args.fetch_db, "FETCH_SIZE")
+    write = counter_per_kernel(args.write_db, "WRITE_SIZE")
+    nf, cf = _copy_value(fetch, "FETCH_SIZE")
+    nw, cw = _copy_value(write, "WRITE_SIZE")
+    f_scale = COPY_BYTES / (cf * 1024.0)
+    w_scale = COPY_BYTES / (cw * 1024.0)
+    kernels = {}
+    for name in sorted(set(fetch) | set(write)):
+        k = short_name(name)
+        if k is None:
+            continue
+        fn, fv = fetch.get(name, (0, 0.0))
+        wn, wv = write.get(name, (0, 0.0))
+        ent = kernels.setdefault(k, {"names": [], "fetch_dispatches": 0, "write_dispatches": 0,
+                                     "_f": 0.0, "_w": 0.0})
+        ent["names"].append(name)
+        ent["fetch_dispatches"] += fn
+        ent["write_dispatches"] += wn
+        ent["_f"] += fn * fv
+        ent["_w"] += wn * wv
+    for k, ent in kernels.items():
+        fkib = ent.pop("_f") / max(ent["fetch_dispatches"], 1)
+        wkib = ent.pop("_w") / max(ent["write_dispatches"], 1)
+        ent["fetch_kib_per_dispatch"] = round(fkib, 1)
+        ent["write_kib_per_dispatch"] = round(wkib, 1)
+        ent["hbm_read_bytes_per_launch"] = int(fkib * 1024 * f_scale)
+        ent["hbm_write_bytes_per_launch"] = int(wkib * 1024 * w_scale)
+        ent["hbm_bytes_per_launch"] = ent["hbm_read_bytes_per_launch"] + ent["hbm_write_bytes_per_launch"]
+    out = {
+        "config": args.config,
+        "kernel_source_sha": library_source_sha(),
+        "command_fetch": args.command_fetch,
+        "command_write": args.command_write,
+        "summary_command": " ".join(sys.argv),
+        "copy_calibration": {
+            "kernel": "torch.neg over 64 Mi fp32 values (%d bytes read, %d written per dispatch)"
+                      % (COPY_BYTES, COPY_BYTES),
+            "fetch_kib_per_dispatch": round(cf, 1), "fetch_dispatches": nf,
+            "write_kib_per_dispatch": round(cw, 1), "write_dispatches": nw,
+            "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+        },
+        "kernels": kernels,
+    }
+    with open(args.out, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("--db", required=True)
+    s.add_argument("--command", required=True)
+    s.add_argument("--title", required=True)
+    s.add_argument("--out", required=True)
+    s.add_argument("--note", default="")
+    s.add_argument("--top", type=int, default=14)
+    c = sub.add_parser("counters")
+    c.add_argument("--fetch-db", required=True)
+    c.add_argument("--write-db", required=True)
+    c.add_argument("--config", required=True)
+    c.add_argument("--command-fetch", required=True)
+    c.add_argument("--command-write", required=True)
+    c.add_argument("--out", required=True)
+    args = ap.parse_args(argv)
+    (cmd_stats if args.cmd == "stats" else cmd_counters)(args)
+
+
+if __name__ == "__main__":
+    main()

@@ -96,7 +96,7 @@ def expected_ties(ref_scores, ref_idx, ctx_len, k):
     return t
 
 
-@pytest.mark.parametrize("name", ["cfg0", "cfg1", "cfg3", "cfg4", "cfg3T", "cfgZ"])
+@pytest.mark.parametrize("name", ["tiny_4k", "ctx16k", "ctx300k", "verify8_ctx131k", "ctx300k_tiepool", "ctx16k_zeroquery"])
 def test_decode_step_matches_oracle(torch, dsa, name):
     note("decode_step", name)
     c, (rs, ri, ro) = case(name)
@@ -112,27 +112,27 @@ def test_decode_step_matches_oracle(torch, dsa, name):
         assert st["selected"] == min(c["k"], int(c["ctx_len"][b]))
         assert st["kth_score"] == int(rs[b, ri[b, st["selected"] - 1]])
         assert st["tied_at_kth"] == ties[b]
-        assert st["path"] == (1 if name == "cfgZ" else 0)
-        if name == "cfgZ":
+        assert st["path"] == (1 if name == "ctx16k_zeroquery" else 0)
+        if name == "ctx16k_zeroquery":
             assert st["reason"] == 2
 
 
-def test_cfg2_eleven_layers(torch, dsa):
-    c0 = inputs.make("cfg2", 0)
+def test_ctx62k_eleven_layers(torch, dsa):
+    c0 = inputs.make("ctx62k_11layers", 0)
     outs, refs = [], []
     for layer in range(c0["layers"]):
-        note("cfg2 layer", layer)
-        c, (rs, ri, ro) = case("cfg2", layer)
+        note("ctx62k_11layers layer", layer)
+        c, (rs, ri, ro) = case("ctx62k_11layers", layer)
         d = dev_inputs(torch, c)
         s, i, o, _ = run_step(torch, dsa, c, d)
-        check_scores(s, rs, c["ctx_len"], "cfg2 layer %d" % layer)
-        assert np.array_equal(i, ri), "cfg2 layer %d indices differ" % layer
+        check_scores(s, rs, c["ctx_len"], "ctx62k_11layers layer %d" % layer)
+        assert np.array_equal(i, ri), "ctx62k_11layers layer %d indices differ" % layer
         outs.append(o)
         refs.append(ro)
-    check_attention(np.stack(outs), np.stack(refs), "cfg2 all layers")
+    check_attention(np.stack(outs), np.stack(refs), "ctx62k_11layers all layers")
 
 
-@pytest.mark.parametrize("name", ["cfg1", "cfg3T"])
+@pytest.mark.parametrize("name", ["ctx16k", "ctx300k_tiepool"])
 def test_forced_fallback_is_bit_identical(torch, dsa, name):
     note("forced fallback", name)
     c, (rs, ri, ro) = case(name)
@@ -147,7 +147,7 @@ def test_forced_fallback_is_bit_identical(torch, dsa, name):
 
 
 def test_runs_are_bit_identical(torch, dsa):
-    c, _ = case("cfg1")
+    c, _ = case("ctx16k")
     d = dev_inputs(torch, c)
     first = run_step(torch, dsa, c, d)
     for _ in range(3):
@@ -156,10 +156,36 @@ def test_runs_are_bit_identical(torch, dsa):
             assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
 
 
+@pytest.mark.parametrize("name", ["ctx16k", "verify8_ctx131k"])
+def test_timed_step_matches_untimed(torch, dsa, name):
+    """dsa_decode_step_timed gives the same bytes as dsa_decode_step, and its events hold
+    positive kernel durations (ctx16k: one query row; verify8_ctx131k: eight)."""
+    c, _ = case(name)
+    d = dev_inputs(torch, c)
+    plain = run_step(torch, dsa, c, d)
+    ws = dsa.new_workspace(c["B"], c["N"], c["k"], c["Hq"], c["Dv"])
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    for e in evs:
+        e.record()
+    torch.cuda.synchronize()
+    scores, idx, out = dsa.dsa_decode_step(d["iq"], d["iw"], d["ik"], d["q"], d["kv"], c["ctx_len"],
+                                           c["k"], c["Dv"], c["scale"], workspace=ws,
+                                           kernel_events=evs)
+    torch.cuda.synchronize()
+    for a, b in zip(plain[:3], (scores.cpu().numpy(), idx.cpu().numpy(), out.cpu().numpy())):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+    ms = [evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(3)]
+    note("%s kernel ms: %s" % (name, ms))
+    assert all(0.0 < t < 50.0 for t in ms)
+    with pytest.raises(ValueError):
+        dsa.dsa_decode_step(d["iq"], d["iw"], d["ik"], d["q"], d["kv"], c["ctx_len"], c["k"], c["Dv"],
+                            c["scale"], workspace=ws, kernel_events=evs[:4])
+
+
 # ---------------------------------------------------------------- stand-alone stages
 
 def test_index_scores_standalone(torch, dsa):
-    for name in ("cfg1", "cfg4"):
+    for name in ("ctx16k", "verify8_ctx131k"):
         c, (rs, _, _) = case(name)
         d = dev_inputs(torch, c)
         note("index_scores", name)
@@ -181,7 +207,7 @@ def test_scores_past_ctx_len_untouched(torch, dsa):
     assert (s[1, 333:] == -12345).all()
 
 
-@pytest.mark.parametrize("name", ["cfg1", "cfg3T", "cfgZ"])
+@pytest.mark.parametrize("name", ["ctx16k", "ctx300k_tiepool", "ctx16k_zeroquery"])
 @pytest.mark.parametrize("flags", [0, 1])
 def test_topk_standalone(torch, dsa, name, flags):
     c, (rs, ri, _) = case(name)
@@ -208,12 +234,12 @@ def test_topk_heavy_ties_and_short_rows(torch, dsa):
 
 
 def test_sparse_attn_standalone_with_skipped_entries(torch, dsa):
-    c, (rs, ri, ro) = case("cfg1")
+    c, (rs, ri, ro) = case("ctx16k")
     d = dev_inputs(torch, c)
-    note("sparse_attn cfg1")
+    note("sparse_attn ctx16k")
     out = dsa.dsa_sparse_attn(d["q"], d["kv"], torch.from_numpy(ri).cuda(), c["Dv"], c["scale"])
     torch.cuda.synchronize()
-    check_attention(out.cpu().numpy(), ro, "sparse_attn cfg1")
+    check_attention(out.cpu().numpy(), ro, "sparse_attn ctx16k")
     # -1 entries are skipped; out-of-range entries are skipped and counted
     idx = ri.copy()
     idx[0, 100:300] = -1

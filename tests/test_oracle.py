@@ -162,7 +162,7 @@ def test_length_at_most_k_returns_every_position():
 
 
 def test_selection_order_properties_on_workload():
-    c = inputs.make("cfg0")
+    c = inputs.make("tiny_4k")
     s = oracle.index_scores(c["iq"], c["iw"], c["ik"], c["ctx_len"])
     idx = oracle.topk_select(s, c["ctx_len"], c["k"])[0]
     sel = s[0, idx]
@@ -224,7 +224,7 @@ def test_attention_matches_torch_sdpa_over_whole_context(dtype):
 
 
 def test_attention_permutation_invariance_and_minus_one_skipping():
-    c = inputs.make("cfg0")
+    c = inputs.make("tiny_4k")
     rng = np.random.default_rng(4)
     idx = rng.choice(c["N"], size=(1, 256), replace=False).astype(np.int32)
     out = oracle.sparse_attn(c["q"], c["kv"], idx, c["Dv"], c["scale"])
@@ -262,7 +262,7 @@ def test_decode_step_on_hand8_example():
 
 
 def test_workload_generator_is_deterministic():
-    a, b = inputs.make("cfg0"), inputs.make("cfg0")
+    a, b = inputs.make("tiny_4k"), inputs.make("tiny_4k")
     for key in ("iq", "iw", "ik", "q", "kv", "ctx_len"):
         assert (a[key] == b[key]).all()
-    assert inputs.ctx_lengths("cfg4").tolist() == [131065 + r for r in range(8)]
+    assert inputs.ctx_lengths("verify8_ctx131k").tolist() == [131065 + r for r in range(8)]
