@@ -125,9 +125,10 @@ ChunkPlan chunk_plan(int nmax, int k) {
 }
 
 int rows_per_score_launch(int Hi, int Di, int B) {
-  const int hp = (Hi + 31) / 32 * 32;
-  int bg = 65536 / (hp * Di);
+  const int hp = (Hi + 31) / 32 * 32;  // Hi <= 64 and Di <= 256 give at least 4 rows
+  int bg = kScoreQBytes / (hp * Di);
   bg = bg < 1 ? 1 : bg;
+  bg = bg * hp > 512 ? 512 / hp : bg;  // one head weight per thread of the block
   return bg < B ? bg : B;
 }
 

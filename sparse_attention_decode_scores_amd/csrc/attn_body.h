@@ -45,12 +45,13 @@ __device__ __forceinline__ void softmax_update(float* lg, int sb, int nheads, fl
 // 16 heads per tile as the A operand and 16 staged rows per tile as the B
 // operand; output = P V with P split into two bf16 terms (high part exact,
 // remainder rounded) so the probabilities keep ~16 bits. Needs Dk % 32 == 0,
-// Dv % 16 == 0, Dv <= 512, Hq <= 16 * HQT, (Dk / 8) * SB <= 16 * block size.
+// Dv % 16 == 0, Dv <= 512, Hq <= 16 * HQT, (Dk / 8) * SB <= kMaxLoads * block size.
 template <int HQT, int SB>
 struct AttnMfma {
   static constexpr int HP = 16 * HQT;
   static constexpr int kMaxTilesPerWave = 32 / kAttnWaves;  // Dv <= 512
-  static constexpr int kMaxLoads = 16;                      // 16-byte loads per thread per sub-block
+  static constexpr int kMaxLoads = 9;                       // 16-byte loads per thread per sub-block
+  static constexpr int kLogitBatch = HQT == 1 ? 6 : (HQT == 2 ? 4 : 2);  // k-steps loaded together
   static constexpr bool kQInLds = HQT == 1;                 // query heads staged in LDS
   __host__ __device__ static int row_bytes(int Dk) { return Dk * 2 + 16; }
   __host__ __device__ static size_t q_bytes(int Dk) {
@@ -61,17 +62,36 @@ struct AttnMfma {
     return q_bytes(Dk) + align16((size_t)SB * row_bytes(Dk)) + (size_t)HP * SB * 4 + 3 * HP * 4;
   }
 
-  // Starts copying the row's query heads into LDS (zero rows for padded heads);
-  // call before other work so the loads overlap it. Visible after the next barrier.
-  __device__ static void prefetch(const AttnArgs& p, int b, uint8_t* work) {
+  // The row's query heads travel in two steps: load_q requests them into registers
+  // (call it first, so the loads overlap other work) and store_q writes them to
+  // LDS (zero rows for padded heads) before run; run's first barrier publishes them.
+  static constexpr int kQPer = 4;  // 16 heads x at most 1,024 values, 16 bytes per slot
+  struct QFrag {
+    v4i v[kQInLds ? kQPer : 1];
+  };
+  __device__ static QFrag load_q(const AttnArgs& p, int b) {
+    QFrag f;
+    if (!kQInLds) return f;
+    const int Dk = p.Dk, cpr = Dk >> 3;
+    const uint8_t* q = reinterpret_cast<const uint8_t*>(p.q) + (int64_t)b * p.Hq * Dk * 2;
+#pragma unroll
+    for (int j = 0; j < kQPer; ++j) {  // every slot loads a present value (clamped)
+      int i = threadIdx.x + kAttnBlock * j;
+      i = i < HP * cpr ? i : HP * cpr - 1;
+      const int h = i / cpr, c = i - h * cpr;
+      const int hc = h < p.Hq ? h : p.Hq - 1;
+      f.v[kQInLds ? j : 0] = *(const v4i*)(q + ((int64_t)hc * Dk + 8 * c) * 2);
+    }
+    return f;
+  }
+  __device__ static void store_q(const QFrag& f, const AttnArgs& p, uint8_t* work) {
     if (!kQInLds) return;
     const int Dk = p.Dk, rb = row_bytes(Dk), cpr = Dk >> 3;
-    const uint8_t* q = reinterpret_cast<const uint8_t*>(p.q) + (int64_t)b * p.Hq * Dk * 2;
-    for (int i = threadIdx.x; i < HP * cpr; i += kAttnBlock) {
+#pragma unroll
+    for (int j = 0; j < kQPer; ++j) {
+      const int i = threadIdx.x + kAttnBlock * j;
       const int h = i / cpr, c = i - h * cpr;
-      v4i v = {0, 0, 0, 0};
-      if (h < p.Hq) v = *(const v4i*)(q + ((int64_t)h * Dk + 8 * c) * 2);
-      *(v4i*)(work + h * rb + 16 * c) = v;
+      if (i < HP * cpr) *(v4i*)(work + h * rb + 16 * c) = h < p.Hq ? f.v[kQInLds ? j : 0] : v4i{0, 0, 0, 0};
     }
   }
 
@@ -102,24 +122,30 @@ struct AttnMfma {
 
     for (int s0 = 0; s0 < cnt; s0 += SB) {
       const int nr = cnt - s0 < SB ? cnt - s0 : SB;
-      // gather the sub-block's rows with 16-byte loads, all issued before any store
+      // gather the sub-block's rows with 16-byte loads: every position is read from
+      // LDS first, then every row load is issued, then the stores. Reads and loads
+      // are unconditional (a branch would make the compiler wait on each one):
+      // slots past the sub-block's chunks or rows re-read its last row, and only
+      // present rows' data is stored (absent rows store zeros).
       const int cpr = Dk >> 3;
+      const int nch = SB * cpr;  // <= kMaxLoads * block size (checked when the path is chosen)
+      int32_t rp[kMaxLoads];
+#pragma unroll
+      for (int j = 0; j < kMaxLoads; ++j) {
+        const int r = (tid + kAttnBlock * j) / cpr;
+        rp[j] = (int32_t)pos_at(s0 + (r < nr ? r : nr - 1));
+      }
       v4i buf[kMaxLoads];
 #pragma unroll
       for (int j = 0; j < kMaxLoads; ++j) {
-        const int i = tid + kAttnBlock * j;
-        const int r = i / cpr, c = i - r * cpr;
-        buf[j] = v4i{0, 0, 0, 0};
-        if (i < SB * cpr && r < nr) {
-          const int64_t pos = pos_at(s0 + r);
-          buf[j] = *(const v4i*)(kv + (pos * Dk + 8 * c) * 2);
-        }
+        const int c = (tid + kAttnBlock * j) % cpr;
+        buf[j] = *(const v4i*)(kv + ((int64_t)rp[j] * Dk + 8 * c) * 2);
       }
 #pragma unroll
       for (int j = 0; j < kMaxLoads; ++j) {
         const int i = tid + kAttnBlock * j;
         const int r = i / cpr, c = i - r * cpr;
-        if (i < SB * cpr) *(v4i*)(rows + r * rb + 16 * c) = buf[j];
+        if (i < nch) *(v4i*)(rows + r * rb + 16 * c) = r < nr ? buf[j] : v4i{0, 0, 0, 0};
       }
       lds_barrier();
       DSA_MARK(1, 6);
@@ -131,30 +157,34 @@ struct AttnMfma {
         const uint8_t* rrow = rows + (16 * nt + (lane & 15)) * rb + 16 * (lane >> 4);
         const int h_a = lane & 15;
         auto afrag = [&](int mt, int kk) {
-          v8bf afr = {};
-          if (kQInLds)
-            afr = *(const v8bf*)(qs + (16 * mt + h_a) * rb + 64 * kk + 16 * (lane >> 4));
-          else if (16 * mt + h_a < p.Hq)
-            afr = *(const v8bf*)(q + (int64_t)(16 * mt + h_a) * Dk + 32 * kk + 8 * (lane >> 4));
-          return afr;
+          if (kQInLds) return *(const v8bf*)(qs + (16 * mt + h_a) * rb + 64 * kk + 16 * (lane >> 4));
+          // heads past Hq read a present head (always issued) and are zeroed at use
+          const int h = 16 * mt + h_a < p.Hq ? 16 * mt + h_a : p.Hq - 1;
+          return *(const v8bf*)(q + (int64_t)h * Dk + 32 * kk + 8 * (lane >> 4));
         };
-        // fragments of k-step kk+1 are loaded while k-step kk runs on the matrix cores
-        v8bf bcur = *(const v8bf*)(rrow);
-        v8bf acur[HQT];
+        // fragments of kLogitBatch k-steps are loaded before their matrix-core steps
+        for (int k0 = 0; k0 < KS; k0 += kLogitBatch) {
+          v8bf bfrag[kLogitBatch];
+          v8bf afr[HQT][kLogitBatch];
 #pragma unroll
-        for (int mt = 0; mt < HQT; ++mt) acur[mt] = afrag(mt, 0);
-        for (int kk = 0; kk < KS; ++kk) {
-          const int kn = kk + 1 < KS ? kk + 1 : kk;
-          const v8bf bnext = *(const v8bf*)(rrow + 64 * kn);
-          v8bf anext[HQT];
+          for (int t = 0; t < kLogitBatch; ++t) {
+            if (k0 + t < KS) {
+              bfrag[t] = *(const v8bf*)(rrow + 64 * (k0 + t));
 #pragma unroll
-          for (int mt = 0; mt < HQT; ++mt) anext[mt] = afrag(mt, kn);
+              for (int mt = 0; mt < HQT; ++mt) afr[mt][t] = afrag(mt, k0 + t);
+            }
+          }
 #pragma unroll
-          for (int mt = 0; mt < HQT; ++mt)
-            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(acur[mt], bcur, acc[mt], 0, 0, 0);
-          bcur = bnext;
+          for (int t = 0; t < kLogitBatch; ++t) {
+            if (k0 + t < KS) {
 #pragma unroll
-          for (int mt = 0; mt < HQT; ++mt) acur[mt] = anext[mt];
+              for (int mt = 0; mt < HQT; ++mt) {
+                v8bf a = afr[mt][t];
+                if (!kQInLds && 16 * mt + h_a >= p.Hq) a = v8bf{};
+                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bfrag[t], acc[mt], 0, 0, 0);
+              }
+            }
+          }
         }
         const int row = 16 * nt + (lane & 15);
 #pragma unroll
@@ -196,24 +226,33 @@ struct AttnMfma {
         // B fragment: V[rows 32*kk + 8*(l/16) + t][dv 16*nt + l%16], t < 8, read with two
         // transposing LDS loads: lane j of each 16-lane group names the 4-value chunk
         // (row base + j/4, columns 4*(j%4)..+3) and receives column j of the 4 rows.
+        // Every tile's fragment is read before the first matrix-core step.
         const int tr_row = 32 * kk + 8 * (lane >> 4) + ((lane & 15) >> 2);
         const int tr_col = 4 * (lane & 3);
+        typedef short v4s __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) v4s lds_v4s;
+        typedef short v8s __attribute__((ext_vector_type(8)));
+        v4s vr[kMaxTilesPerWave][2];
 #pragma unroll
         for (int j = 0; j < kMaxTilesPerWave; ++j) {
           const int nt = wave + kAttnWaves * j;
-          if (nt >= nt_all) break;
-          const uint8_t* va = rows + tr_row * rb + (16 * nt + tr_col) * 2;
-          typedef short v4s __attribute__((ext_vector_type(4)));
-          typedef __attribute__((address_space(3))) v4s lds_v4s;
-          const v4s r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(va));
-          const v4s r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(va + 4 * rb));
-          typedef short v8s __attribute__((ext_vector_type(8)));
-          const v8s both = __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7);
-          const v8bf bfr = __builtin_bit_cast(v8bf, both);
+          if (nt < nt_all) {
+            const uint8_t* va = rows + tr_row * rb + (16 * nt + tr_col) * 2;
+            vr[j][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(va));
+            vr[j][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(va + 4 * rb));
+          }
+        }
 #pragma unroll
-          for (int mt = 0; mt < HQT; ++mt) {
-            o[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[mt], bfr, o[mt][j], 0, 0, 0);
-            o[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[mt], bfr, o[mt][j], 0, 0, 0);
+        for (int j = 0; j < kMaxTilesPerWave; ++j) {
+          const int nt = wave + kAttnWaves * j;
+          if (nt < nt_all) {
+            const v8s both = __builtin_shufflevector(vr[j][0], vr[j][1], 0, 1, 2, 3, 4, 5, 6, 7);
+            const v8bf bfr = __builtin_bit_cast(v8bf, both);
+#pragma unroll
+            for (int mt = 0; mt < HQT; ++mt) {
+              o[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[mt], bfr, o[mt][j], 0, 0, 0);
+              o[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[mt], bfr, o[mt][j], 0, 0, 0);
+            }
           }
         }
       }
@@ -251,7 +290,9 @@ struct AttnGeneric {
     else return bf16_to_f32(reinterpret_cast<const uint16_t*>(base)[i]);
   }
 
-  __device__ static void prefetch(const AttnArgs&, int, uint8_t*) {}
+  struct QFrag {};
+  __device__ static QFrag load_q(const AttnArgs&, int) { return QFrag{}; }
+  __device__ static void store_q(const QFrag&, const AttnArgs&, uint8_t*) {}
 
   template <typename PosAt>
   __device__ static void run(const AttnArgs& p, int b, int split, PosAt pos_at, int cnt,
@@ -315,7 +356,9 @@ struct AttnGeneric {
 // Selection only (no attention role).
 struct AttnNone {
   __host__ __device__ static size_t lds_bytes(int, int) { return 0; }
-  __device__ static void prefetch(const AttnArgs&, int, uint8_t*) {}
+  struct QFrag {};
+  __device__ static QFrag load_q(const AttnArgs&, int) { return QFrag{}; }
+  __device__ static void store_q(const QFrag&, const AttnArgs&, uint8_t*) {}
   template <typename PosAt>
   __device__ static void run(const AttnArgs&, int, int, PosAt, int, uint8_t*) {}
 };

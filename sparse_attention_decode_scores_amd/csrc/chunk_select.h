@@ -15,6 +15,39 @@ struct ChunkSmem {
   uint32_t xch[BLOCK / 64][2];
 };
 
+// Histogram of a chunk's scores over monotone log-spaced bins: sign, exponent and
+// 4 mantissa bits of the magnitude, so a bin spans at most 1/16 of its values
+// (scores of magnitude below 16 get a bin each). 896 of the 1024 bins are used.
+constexpr int kHistBins = 1024;
+__device__ __forceinline__ uint32_t score_bin(int32_t s) {
+  const uint32_t x = s >= 0 ? (uint32_t)s : ~(uint32_t)s;  // ~s = -s - 1 >= 0
+  uint32_t code = x;
+  if (x >= 16) {
+    const uint32_t e = 31u - (uint32_t)__builtin_clz(x);  // 4 .. 30
+    code = 16u * (e - 3u) + ((x >> (e - 4u)) & 15u);     // 16 .. 447
+  }
+  return s >= 0 ? 448u + code : 447u - code;
+}
+
+// Lowest score that score_bin maps to bin b (b < 896).
+__device__ __forceinline__ int32_t bin_floor(uint32_t b) {
+  if (b >= 448u) {
+    const uint32_t code = b - 448u;
+    if (code < 16u) return (int32_t)code;
+    const uint32_t e = code / 16u + 3u;
+    return (int32_t)((16u + code % 16u) << (e - 4u));
+  }
+  const uint32_t code = 447u - b;  // magnitudes x of this bin end at xh; the score is ~x
+  uint32_t xh = code;
+  if (code >= 16u) {
+    const uint32_t e = code / 16u + 3u;
+    xh = ((16u + code % 16u + 1u) << (e - 4u)) - 1u;
+  }
+  return (int32_t)~xh;
+}
+
+constexpr int kWaveStage = 136;  // staging slots per wave for wave_chunk_candidates (m <= 64, + 8 read slack)
+
 // scores: LDS copy of the chunk's scores (entry i is position pos0 + i); count:
 // valid entries (<= 0 means none; at most 16 * BLOCK). Writes out[0..m) (the m
 // best keys, in position order, 0-padded) and *x_out = the best key not kept
@@ -99,6 +132,230 @@ __device__ __forceinline__ void chunk_candidates(const int32_t* scores, int coun
     }
   }
   DSA_MARK(3, 10);
+}
+
+// Lowest score of the bin that holds the (m+1)-th best of `count` keys (m < count),
+// from their histogram over score_bin, computed by one wave: lane l sums bins
+// 1008-16l .. 1023-16l (best first) and one wave scan finds the bin. Returns
+// false when the histogram does not count `count` keys.
+__device__ __forceinline__ bool threshold_floor(const uint32_t* hist, int count, int m, int32_t* tlo) {
+  const int l = lane_id();
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const int bin0 = kHistBins - 16 - 16 * l;
+  uint32_t h[16];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(hist + bin0 + 4 * q);
+    h[4 * q] = v.x;
+    h[4 * q + 1] = v.y;
+    h[4 * q + 2] = v.z;
+    h[4 * q + 3] = v.w;
+  }
+  uint32_t sum = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) sum += h[j];
+  const uint32_t incl = wave_incl_scan_u32(sum);
+  if ((uint32_t)__builtin_amdgcn_readlane((int)incl, 63) != (uint32_t)count) return false;
+  const uint32_t want = (uint32_t)m + 1;
+  int tb = -1;
+  uint32_t acc = incl - sum;  // keys in better bins than this lane's
+#pragma unroll
+  for (int j = 15; j >= 0; --j) {
+    tb = (tb < 0 && acc < want && want <= acc + h[j]) ? bin0 + j : tb;
+    acc += h[j];
+  }
+  const uint64_t has = __ballot(tb >= 0);  // exactly one lane
+  *tlo = bin_floor((uint32_t)__builtin_amdgcn_readlane(tb, __builtin_ctzll(has)));
+  return true;
+}
+
+// The same result as chunk_candidates, computed by one wave without block
+// barriers, from a histogram of the chunk's scores over score_bin that the caller
+// filled while producing them (hist counts the `count` valid positions):
+//  1. threshold_floor finds the bin holding the (m+1)-th best key;
+//  2. every key scoring at least that bin's lowest score is staged in LDS in
+//     position order (ballot compaction): the keys of higher bins (fewer than m+1)
+//     plus that bin's keys;
+//  3. each staged key is ranked against the others; the m best, in staging order,
+//     are the output and the one of rank m is x, the best key left out.
+// Returns false, having written nothing, when more than m + 64 keys are staged
+// (heavy ties) or the histogram does not count `count` keys: the caller then runs
+// chunk_candidates. `stage` is this wave's LDS area of kWaveStage keys.
+__device__ __forceinline__ bool wave_chunk_candidates(const int32_t* scores, int count, uint32_t pos0,
+                                                      int m, const uint32_t* hist,
+                                                      uint64_t* __restrict__ out,
+                                                      uint64_t* __restrict__ x_out, uint64_t* stage) {
+  const int l = lane_id();
+  DSA_MARK(3, 0);
+  if (count <= m) {
+    for (int i = l; i < m; i += 64) out[i] = i < count ? make_key(scores[i], pos0 + (uint32_t)i) : 0ull;
+    if (l == 0) *x_out = 0;
+    return true;
+  }
+  int32_t tlo;
+  if (!threshold_floor(hist, count, m, &tlo)) return false;
+
+  const uint64_t lt = lanemask_lt();
+  const uint32_t cap = (uint32_t)m + 64;
+  uint32_t ns = 0;
+  // rows of 64 positions, eight rows' loads in flight at a time
+  for (int r0 = 0; r0 < count; r0 += 8 * 64) {
+    int32_t v[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int i = r0 + 64 * t + l;
+      v[t] = scores[i < count ? i : count - 1];
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int i = r0 + 64 * t + l;
+      const bool in = i < count && v[t] >= tlo;
+      const uint64_t b = __ballot(in);
+      const uint32_t slot = ns + (uint32_t)__popcll(b & lt);
+      if (in && slot < cap) stage[slot] = make_key(v[t], pos0 + (uint32_t)i);
+      ns += (uint32_t)__popcll(b);
+    }
+  }
+  if (ns > cap) return false;
+  DSA_MARK(3, 8);
+
+  const bool two = ns > 64;
+  const uint64_t k0 = l < (int)ns ? stage[l] : 0ull;
+  const uint64_t k1 = l + 64 < (int)ns ? stage[l + 64] : 0ull;
+  uint32_t r0 = 0, r1 = 0;
+  // every lane compares its keys with all staged keys: 8 keys per step, read as
+  // four 16-byte broadcasts (the staging area has kWaveStage >= cap + 8 slots)
+  typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
+  for (int j0 = 0; j0 < (int)ns; j0 += 8) {
+    u64x2 e[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) e[t] = *reinterpret_cast<const u64x2*>(stage + j0 + 2 * t);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const uint64_t x = (t & 1) ? e[t >> 1].y : e[t >> 1].x;
+      const bool live = j0 + t < (int)ns;
+      r0 += (live && x > k0) ? 1u : 0u;
+      if (two) r1 += (live && x > k1) ? 1u : 0u;
+    }
+  }
+  DSA_MARK(3, 9);
+  // staged keys are distinct, so the ranks are a permutation of 0 .. ns-1
+  const bool s0 = l < (int)ns && r0 < (uint32_t)m;
+  const bool s1 = l + 64 < (int)ns && r1 < (uint32_t)m;
+  const uint64_t b0 = __ballot(s0), b1 = __ballot(s1);
+  if (s0) out[__popcll(b0 & lt)] = k0;
+  if (s1) out[__popcll(b0) + __popcll(b1 & lt)] = k1;
+  const uint64_t xb0 = __ballot(l < (int)ns && r0 == (uint32_t)m);
+  const uint64_t xb1 = __ballot(l + 64 < (int)ns && r1 == (uint32_t)m);
+  const int xl = xb0 ? __builtin_ctzll(xb0) : __builtin_ctzll(xb1);
+  const uint64_t xk = xb0 ? k0 : k1;
+  const uint32_t xlo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)xk, xl);
+  const uint32_t xhi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(xk >> 32), xl);
+  if (l == 0) *x_out = ((uint64_t)xhi << 32) | xlo;
+  DSA_MARK(3, 10);
+  return true;
+}
+
+// LDS of block_chunk_candidates.
+template <int BLOCK>
+struct BlockCandSmem {
+  uint64_t wstage[BLOCK / 64][kWaveStage];  // each wave's staged keys
+  uint64_t all[kWaveStage];                 // all staged keys, position order
+  uint32_t rank[kWaveStage];
+  uint32_t wcount[BLOCK / 64];
+};
+
+// The same result as chunk_candidates for one chunk, by the whole block with
+// three barriers (the caller's barrier after filling `scores` and `hist` comes
+// first): every wave finds the threshold bin's lowest score (threshold_floor);
+// wave w stages the keys at or above it from its own run of 64-position rows
+// (ballot compaction, position order); the runs are concatenated; eight (or
+// four) threads per staged key count the staged keys above it, which is its
+// rank; wave 0 writes the m best in position order and x = the key of rank m.
+// Returns false (uniformly, nothing written) where wave_chunk_candidates does.
+template <int BLOCK>
+__device__ __forceinline__ bool block_chunk_candidates(const int32_t* scores, int count, uint32_t pos0,
+                                                       int m, const uint32_t* hist,
+                                                       uint64_t* __restrict__ out,
+                                                       uint64_t* __restrict__ x_out,
+                                                       BlockCandSmem<BLOCK>& sm) {
+  constexpr int W = BLOCK / 64;
+  const int tid = threadIdx.x, l = lane_id(), w = wave_id();
+  if (count <= m) {
+    for (int i = tid; i < m; i += BLOCK) out[i] = i < count ? make_key(scores[i], pos0 + (uint32_t)i) : 0ull;
+    if (tid == 0) *x_out = 0;
+    return true;
+  }
+  int32_t tlo;
+  if (!threshold_floor(hist, count, m, &tlo)) return false;  // same outcome in every wave
+  DSA_MARK(3, 1);
+
+  const uint64_t lt = lanemask_lt();
+  const uint32_t cap = (uint32_t)m + 64;
+  const int nrows = (count + 63) >> 6;
+  const int per = (nrows + W - 1) / W;
+  const int rbeg = w * per, rend = rbeg + per < nrows ? rbeg + per : nrows;
+  uint32_t ns = 0;
+  for (int r0 = rbeg; r0 < rend; r0 += 4) {
+    int32_t v[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int i = 64 * (r0 + t) + l;
+      v[t] = scores[i < count ? i : count - 1];
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int i = 64 * (r0 + t) + l;
+      const bool in = r0 + t < rend && i < count && v[t] >= tlo;
+      const uint64_t b = __ballot(in);
+      const uint32_t slot = ns + (uint32_t)__popcll(b & lt);
+      if (in && slot < cap) sm.wstage[w][slot] = make_key(v[t], pos0 + (uint32_t)i);
+      ns += (uint32_t)__popcll(b);
+    }
+  }
+  if (l == 0) sm.wcount[w] = ns;
+  lds_barrier();
+  uint32_t total = 0, off = 0;
+#pragma unroll
+  for (int q = 0; q < W; ++q) {
+    const uint32_t c = sm.wcount[q];
+    off += q < w ? c : 0u;
+    total += c;
+  }
+  if (total > cap) return false;  // uniform
+  for (int j = l; j < (int)ns; j += 64) sm.all[off + j] = sm.wstage[w][j];
+  lds_barrier();
+  DSA_MARK(3, 8);
+
+  // rank of staged key i: TPE threads each compare it with every TPE-th key
+  const int tpe = total > (uint32_t)(BLOCK / 8) ? 4 : 8;  // BLOCK / tpe >= cap keys
+  const int i = tid / tpe, part = tid % tpe;
+  uint32_t r = 0;
+  if (i < (int)total) {
+    const uint64_t me = sm.all[i];
+    for (int j = part; j < (int)total; j += tpe) r += sm.all[j] > me ? 1u : 0u;
+  }
+  r += (uint32_t)__builtin_amdgcn_mov_dpp((int)r, dpp::kQuadXor1, 0xF, 0xF, false);
+  r += (uint32_t)__builtin_amdgcn_mov_dpp((int)r, dpp::kQuadXor2, 0xF, 0xF, false);
+  if (tpe == 8) r += (uint32_t)__builtin_amdgcn_mov_dpp((int)r, dpp::kRowHalfMirror, 0xF, 0xF, false);
+  if (part == 0 && i < (int)total) sm.rank[i] = r;
+  lds_barrier();
+  DSA_MARK(3, 9);
+
+  if (w == 0) {
+    uint32_t base = 0;
+    for (int q = 0; q < (int)total; q += 64) {
+      const int j = q + l;
+      const uint32_t rk = j < (int)total ? sm.rank[j] : ~0u;
+      const bool sel = rk < (uint32_t)m;
+      const uint64_t b = __ballot(sel);
+      if (sel) out[base + (uint32_t)__popcll(b & lt)] = sm.all[j];
+      if (rk == (uint32_t)m) *x_out = sm.all[j];
+      base += (uint32_t)__popcll(b);
+    }
+  }
+  DSA_MARK(3, 10);
+  return true;
 }
 
 }  // namespace dsa

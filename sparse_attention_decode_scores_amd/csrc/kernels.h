@@ -45,6 +45,10 @@ struct ScoreArgs {
   int m;           // candidates kept per chunk
 };
 
+// Query bytes (rows x padded heads x dims) one score launch stages; the launch
+// planner keeps Bg * HP * DI at or below it, and Bg * HP at or below the block size.
+constexpr int kScoreQBytes = 65536;
+
 hipError_t launch_score(const ScoreArgs& a, int MT, int KT, bool cand, int grid, hipStream_t s,
                         KTimer t = {});
 int score_max_chunk();        // longest chunk the score kernel's candidate pass takes

@@ -6,7 +6,7 @@
 // (heads x dim times dim x positions), so it runs on the int8 matrix cores:
 // v_mfma_i32_32x32x32_i8 with the query heads as the A operand (32 heads per
 // tile, held in registers or LDS) and 32 keys per tile streamed from HBM as the B
-// operand with 16-byte loads. The ReLU, the per-head weight and the sum over heads
+// operand with 16-byte loads, three tiles per wave in flight. The ReLU, the per-head weight and the sum over heads
 // are applied to the accumulators in registers; one cross-lane add finishes the
 // head sum. The key cache is read exactly once per launch.
 //
@@ -21,22 +21,24 @@ namespace dsa {
 
 constexpr int kScoreBlock = 512;
 constexpr int kScoreWaves = kScoreBlock / 64;
+static_assert(kScoreQBytes % (16 * kScoreBlock) == 0, "query staging slots");
 
 namespace {
 
 // Key fragment of the B operand: lane l holds 16 consecutive dims of key
-// (p0 + (l & 31)), starting at dim 32*kt + 16*(l >> 5).
+// (64*tile + 32*t + (l & 31)) of the chunk, starting at dim 32*kt + 16*(l >> 5).
+// Raw buffer loads against a resource that covers exactly the chunk's valid keys:
+// always issued (so the compiler's wait counts stay exact), zero past the end
+// without touching memory.
 template <int KT>
-__device__ __forceinline__ void load_keys(v4i (&kf)[2][KT], const int8_t* __restrict__ ik,
-                                          int64_t p0, int64_t last) {
+__device__ __forceinline__ void load_keys(v4i (&kf)[2][KT], __amdgpu_buffer_rsrc_t rs, int tile) {
   const int lane = lane_id();
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    int64_t pos = p0 + 32 * t + (lane & 31);
-    pos = pos > last ? last : pos;
-    const int8_t* row = ik + pos * (32 * KT) + 16 * (lane >> 5);
+    const int off = (64 * tile + 32 * t + (lane & 31)) * (32 * KT) + 16 * (lane >> 5);
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt) kf[t][kt] = *(const v4i*)(row + 32 * kt);
+    for (int kt = 0; kt < KT; ++kt)
+      kf[t][kt] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 32 * kt, 0, 0));
   }
 }
 
@@ -52,24 +54,62 @@ __global__ __launch_bounds__(kScoreBlock) void k_score(ScoreArgs a) {
   int8_t* qs = reinterpret_cast<int8_t*>(smem + align16(sizeof(Smem)));       // [Bg][HP][DI]
   int8_t* wsm = qs + a.Bg * HP * DI;                                           // [Bg][HP]
   int32_t* sc = reinterpret_cast<int32_t*>(wsm + a.Bg * HP);                   // [Bg][P]
+  uint32_t* hist = reinterpret_cast<uint32_t*>(sc + a.Bg * a.P);              // [Bg][kHistBins]
+  using CandSmem = BlockCandSmem<kScoreBlock>;
+  CandSmem& bsm = *reinterpret_cast<CandSmem*>(hist + a.Bg * kHistBins);
+  int* fallback = reinterpret_cast<int*>(&bsm + 1);                             // [Bg]
 
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   const int c = blockIdx.x;
   DSA_MARK(0, 0);
-  if (CAND) radix_clear<kScoreBlock>(csm.radix);
+  const int64_t cbeg = (int64_t)c * a.P;
+  const int64_t clen64 = (int64_t)a.nmax - cbeg;
+  const int clen = clen64 > a.P ? a.P : (int)(clen64 > 0 ? clen64 : 0);
+  const int npairs = (clen + 63) >> 6;
 
-  for (int i = tid; i < a.Bg * HP * (DI / 16); i += kScoreBlock) {
+  // Requests go out in this order: this launch's query heads and weights (into
+  // registers), then the first three key tiles of every wave (a whole chunk of up
+  // to 1,536 positions), whose latency then overlaps the query staging; each tile
+  // buffer is refilled as soon as it is consumed. Every load is unconditional
+  // (clamped addresses; padding is zeroed when stored), so no register copy has
+  // to wait for a load that is still in flight.
+  constexpr int kQPer = ONE ? (MT * KT + 7) / 8 : kScoreQBytes / 16 / kScoreBlock;
+  const int nq = a.Bg * HP * (DI / 16);
+  v4i qv[kQPer];
+#pragma unroll
+  for (int j = 0; j < kQPer; ++j) {
+    int i = tid + kScoreBlock * j;
+    i = i < nq ? i : nq - 1;
     const int bb = i / (HP * (DI / 16));
     const int rem = i - bb * (HP * (DI / 16));
-    const int h = rem / (DI / 16), part = rem - h * (DI / 16);
-    v4i v = {0, 0, 0, 0};
-    if (h < a.Hi) v = *(const v4i*)(a.iq + ((int64_t)(a.b0 + bb) * a.Hi + h) * DI + 16 * part);
-    *(v4i*)(qs + (bb * HP + h) * DI + 16 * part) = v;
+    int h = rem / (DI / 16);
+    const int part = rem - h * (DI / 16);
+    h = h < a.Hi ? h : a.Hi - 1;
+    qv[j] = *(const v4i*)(a.iq + ((int64_t)(a.b0 + bb) * a.Hi + h) * DI + 16 * part);
   }
-  for (int i = tid; i < a.Bg * HP; i += kScoreBlock) {
-    const int bb = i / HP, h = i - bb * HP;
-    wsm[i] = h < a.Hi ? a.iw[(int64_t)(a.b0 + bb) * a.Hi + h] : (int8_t)0;
+  const int wi = tid < a.Bg * HP ? tid : a.Bg * HP - 1;
+  const int wh = wi % HP < a.Hi ? wi % HP : a.Hi - 1;
+  const int8_t wv = a.iw[(int64_t)(a.b0 + wi / HP) * a.Hi + wh];
+
+  // buffer resource word 3 for gfx9 raw buffers: 32-bit data format, no swizzle
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(a.ik + cbeg * DI), (short)0, clen * DI, 0x00020000);
+  v4i kb0[2][KT], kb1[2][KT], kb2[2][KT];
+  load_keys<KT>(kb0, rs, wave);
+  load_keys<KT>(kb1, rs, wave + kScoreWaves);
+  load_keys<KT>(kb2, rs, wave + 2 * kScoreWaves);
+
+  if (CAND) {
+    radix_clear<kScoreBlock>(csm.radix);
+    for (int i = tid; i < a.Bg * kHistBins; i += kScoreBlock) hist[i] = 0;
   }
+#pragma unroll
+  for (int j = 0; j < kQPer; ++j) {
+    const int i = tid + kScoreBlock * j;
+    const int h = (i % (HP * (DI / 16))) / (DI / 16);
+    if (i < nq) *(v4i*)(qs + 16 * i) = h < a.Hi ? qv[j] : v4i{0, 0, 0, 0};
+  }
+  if (tid < a.Bg * HP) wsm[tid] = tid % HP < a.Hi ? wv : (int8_t)0;
   lds_barrier();
 
   // A fragments and weights of a single row stay in registers for the whole chunk.
@@ -91,19 +131,13 @@ __global__ __launch_bounds__(kScoreBlock) void k_score(ScoreArgs a) {
     }
   }
 
-  DSA_MARK(0, 1);
-  const int64_t cbeg = (int64_t)c * a.P;
-  const int64_t last = (int64_t)a.nmax - 1;
-  const int64_t clen64 = (int64_t)a.nmax - cbeg;
-  const int clen = clen64 > a.P ? a.P : (int)(clen64 > 0 ? clen64 : 0);
-  const int npairs = (clen + 63) >> 6;
-
-  v4i kcur[2][KT], knext[2][KT];
-  if (wave < npairs) load_keys<KT>(kcur, a.ik, cbeg + 64 * wave, last);
-  for (int tp = wave; tp < npairs; tp += kScoreWaves) {
+  // Scores of 64 positions (tile tp) from the key fragments `cur`, which are then
+  // refilled with tile tp + 24. With candidates, scores stay in LDS until the chunk
+  // is done (no global store in the loop: its completion would be waited for later).
+  auto tile = [&](v4i(&cur)[2][KT], int tp) {
     const int64_t p0 = cbeg + 64 * tp;
-    if (tp + kScoreWaves < npairs) load_keys<KT>(knext, a.ik, p0 + 64 * kScoreWaves, last);
-    for (int bb = 0; bb < a.Bg; ++bb) {
+    const int nb = ONE ? 1 : a.Bg;  // a compile-time trip count keeps the wait counts exact
+    for (int bb = 0; bb < nb; ++bb) {
       const int8_t* qb = qs + bb * HP * DI;
       int half[2];
 #pragma unroll
@@ -118,7 +152,7 @@ __global__ __launch_bounds__(kScoreBlock) void k_score(ScoreArgs a) {
             const v4i qf = ONE ? qreg[ONE ? mt : 0][ONE ? kt : 0]
                                : *(const v4i*)(qb + (32 * mt + (lane & 31)) * DI + 32 * kt +
                                                16 * (lane >> 5));
-            acc[mt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(qf, kcur[t][kt], acc[mt], 0, 0, 0);
+            acc[mt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(qf, cur[t][kt], acc[mt], 0, 0, 0);
           }
         }
         // accumulator r of lane l holds head 32*mt + 8*(r/4) + 4*(l/32) + r%4 of key l%32
@@ -142,26 +176,68 @@ __global__ __launch_bounds__(kScoreBlock) void k_score(ScoreArgs a) {
       }
       const int val = lane < 32 ? half[0] : half[1];
       const int64_t pos = p0 + lane;
-      if (pos < a.lens.n[a.b0 + bb]) a.scores[(int64_t)(a.b0 + bb) * a.N + pos] = val;
-      if (CAND) sc[bb * a.P + (int)(pos - cbeg)] = val;
+      if (CAND) {
+        sc[bb * a.P + (int)(pos - cbeg)] = val;
+        if (pos < a.lens.n[a.b0 + bb]) atomicAdd(&hist[bb * kHistBins + score_bin(val)], 1u);
+      } else if (pos < a.lens.n[a.b0 + bb]) {
+        a.scores[(int64_t)(a.b0 + bb) * a.N + pos] = val;
+      }
     }
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) kcur[t][kt] = knext[t][kt];
+    load_keys<KT>(cur, rs, tp + 3 * kScoreWaves);
+  };
+
+  DSA_MARK(0, 1);
+  // three key buffers rotate by name (a register copy would wait for its load)
+  for (int tp = wave; tp < npairs; tp += 3 * kScoreWaves) {
+    tile(kb0, tp);
+    if (tp + kScoreWaves >= npairs) break;
+    tile(kb1, tp + kScoreWaves);
+    if (tp + 2 * kScoreWaves >= npairs) break;
+    tile(kb2, tp + 2 * kScoreWaves);
   }
 
   DSA_MARK(0, 2);
   if (CAND) {
     lds_barrier();
     DSA_MARK(0, 3);
+    if (ONE) {
+      // one row: the whole block selects the chunk's candidates
+      const int b = a.b0;
+      const int64_t n64 = (int64_t)a.lens.n[b] - cbeg;
+      const int count = n64 > clen ? clen : (int)(n64 > 0 ? n64 : 0);
+      const bool ok = block_chunk_candidates<kScoreBlock>(sc, count, (uint32_t)cbeg, a.m, hist,
+                                                          a.cand + ((int64_t)b * a.G + c) * a.m,
+                                                          a.xc + (int64_t)b * a.G + c, bsm);
+      if (tid == 0) fallback[0] = ok ? 0 : 1;
+    } else {
+      // several rows: wave w selects the candidates of rows w, w + 8, ...
+      for (int bb = wave; bb < a.Bg; bb += kScoreWaves) {
+        const int b = a.b0 + bb;
+        const int64_t n64 = (int64_t)a.lens.n[b] - cbeg;
+        const int count = n64 > clen ? clen : (int)(n64 > 0 ? n64 : 0);
+        const bool ok = wave_chunk_candidates(sc + bb * a.P, count, (uint32_t)cbeg, a.m, hist + bb * kHistBins,
+                                              a.cand + ((int64_t)b * a.G + c) * a.m,
+                                              a.xc + (int64_t)b * a.G + c, bsm.wstage[wave]);
+        if (lane == 0) fallback[bb] = ok ? 0 : 1;
+      }
+    }
+    DSA_MARK(0, 5);
     for (int bb = 0; bb < a.Bg; ++bb) {
       const int b = a.b0 + bb;
       const int64_t n64 = (int64_t)a.lens.n[b] - cbeg;
       const int count = n64 > clen ? clen : (int)(n64 > 0 ? n64 : 0);
+      int32_t* dst = a.scores + (int64_t)b * a.N + cbeg;
+      for (int i = tid; i < count; i += kScoreBlock) dst[i] = sc[bb * a.P + i];
+    }
+    lds_barrier();
+    for (int bb = 0; bb < a.Bg; ++bb) {  // rows whose threshold bin held too many keys
+      if (!fallback[bb]) continue;
+      const int b = a.b0 + bb;
+      const int64_t n64 = (int64_t)a.lens.n[b] - cbeg;
+      const int count = n64 > clen ? clen : (int)(n64 > 0 ? n64 : 0);
       chunk_candidates<kScoreBlock>(sc + bb * a.P, count, (uint32_t)cbeg, a.m,
-                                    a.cand + ((int64_t)b * a.G + c) * a.m,
-                                    a.xc + (int64_t)b * a.G + c, csm);
+                                    a.cand + ((int64_t)b * a.G + c) * a.m, a.xc + (int64_t)b * a.G + c,
+                                    csm);
       lds_barrier();
     }
     DSA_MARK(0, 4);
@@ -172,7 +248,10 @@ int score_max_chunk() { return kChunkPerThread * kScoreBlock; }
 
 size_t score_lds_bytes(int MT, int KT, int Bg, int P, bool cand) {
   return align16(sizeof(ChunkSmem<kScoreBlock>)) + (size_t)Bg * 32 * MT * 32 * KT + (size_t)Bg * 32 * MT +
-         (cand ? (size_t)Bg * P * 4 : 0) + 16;
+         (cand ? (size_t)Bg * P * 4 + (size_t)Bg * kHistBins * 4 + sizeof(BlockCandSmem<kScoreBlock>) +
+                     (size_t)Bg * 4
+               : 0) +
+         16;
 }
 
 template <int MT, int KT, bool CAND, bool ONE>

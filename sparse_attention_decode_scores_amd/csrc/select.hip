@@ -311,8 +311,8 @@ __global__ __launch_bounds__(kSelBlock) void k_select(SelArgs a, AttnArgs at) {
     }
     mx = tid < a.G ? a.xc[(int64_t)b * a.G + tid] : 0ull;
   }
+  const typename Attn::QFrag qf = Attn::load_q(at, b);  // every workgroup: exact wait counts
   radix_clear<kSelBlock>(sm.radix);
-  if (attn_role) Attn::prefetch(at, b, region);
   if (reason == 0) {
     uint32_t nz = 0, lo = 0xFFFFFFFFu, hi = 0;
 #pragma unroll
@@ -401,6 +401,7 @@ __global__ __launch_bounds__(kSelBlock) void k_select(SelArgs a, AttnArgs at) {
     const int e0 = (int)blockIdx.x * per;
     int cnt = (int)nsel - e0;
     cnt = cnt < 0 ? 0 : (cnt > per ? per : cnt);
+    Attn::store_q(qf, at, region);
     Attn::run(at, b, blockIdx.x, [&](int i) { return (int64_t)key_pos(sel[e0 + i]); }, cnt,
               region);
     DSA_MARK(1, 10);
@@ -488,7 +489,7 @@ __global__ __launch_bounds__(kSelBlock) void k_attend_idx(const int32_t* __restr
   const int e0 = j * per;
   const int e1 = e0 + per < k ? e0 + per : k;
   const int32_t* row = idx + (int64_t)b * k;
-  Attn::prefetch(at, b, region);
+  const typename Attn::QFrag qf = Attn::load_q(at, b);
   uint32_t bad = 0, run = 0;
   for (int r0 = e0; r0 < e1; r0 += kSelBlock) {
     const int i = r0 + tid;
@@ -502,6 +503,7 @@ __global__ __launch_bounds__(kSelBlock) void k_attend_idx(const int32_t* __restr
   }
   bad = block_stats(bad, 0, 0, 0, sm).sum;
   if (tid == 0) part_bad[(int64_t)b * at.S + j] = (int32_t)bad;
+  Attn::store_q(qf, at, region);
   Attn::run(at, b, j, [&](int i) { return (int64_t)posl[i]; }, (int)run, region);
 }
 
@@ -527,7 +529,8 @@ AttnChoice choose_attn(int dt_bf16, int Hq, int Dk, int Dv) {
     c.kind = ATTN_MFMA_BF16;
     c.hqt = (Hq + 15) / 16;
     c.sb = Dk <= 576 ? 64 : 32;
-    return c;
+    if ((Dk / 8) * c.sb <= AttnMfma<1, 64>::kMaxLoads * kAttnBlock) return c;  // one gather pass
+    c = AttnChoice{ATTN_NONE, 0, 0};
   }
   if (Hq >= 1 && Hq * Dv <= 4096 && Dk <= 512 && Dv <= Dk) {
     c.kind = dt_bf16 ? ATTN_GENERIC_BF16 : ATTN_GENERIC_F32;
@@ -625,15 +628,32 @@ __global__ __launch_bounds__(kCombBlock) void k_combine(AttnArgs at, const int32
   const int S = at.S, Hq = at.Hq, Dv = at.Dv;
   const int HP = FRAG ? (Hq + 15) / 16 * 16 : Hq;
   DSA_MARK(2, 0);
+  // Every load is issued before any arithmetic: first the (max, sum) pairs this lane
+  // turns into weights, then the partial outputs this lane combines (they do not
+  // depend on the weights), so the whole pass waits for one memory round trip.
+  const int64_t split_stride = (int64_t)HP * Dv;
+  const float* po = at.part_o + (int64_t)b * S * split_stride;
+  const int h = lane < Hq ? lane : Hq - 1;
+  float2 ml[kMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) {
+    const int sc = s < S ? s : S - 1;
+    ml[s] = at.part_ml[((int64_t)b * S + sc) * Hq + h];
+  }
+  const int nel = FRAG ? HP * Dv / 4 : Hq * Dv;           // 16-byte (FRAG) or 4-byte elements
+  const int el = blockIdx.x * kCombBlock + lane;
+  const int elc = el < nel ? el : nel - 1;
+  v4f part[FRAG ? kMaxSplits : 1];
+  float partf[FRAG ? 1 : kMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) {
+    const int sc = s < S ? s : S - 1;  // weight 0 past S
+    if (FRAG) part[FRAG ? s : 0] = *(const v4f*)(po + sc * split_stride + (int64_t)elc * 4);
+    else partf[FRAG ? 0 : s] = po[sc * split_stride + elc];
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the arithmetic below
   {
     // lane h forms the weights of head h over the splits (no cross-lane work)
-    const int h = lane < Hq ? lane : Hq - 1;
-    float2 ml[kMaxSplits];
-#pragma unroll
-    for (int s = 0; s < kMaxSplits; ++s) {
-      const int sc = s < S ? s : S - 1;
-      ml[s] = at.part_ml[((int64_t)b * S + sc) * Hq + h];
-    }
     float M = -INFINITY;
 #pragma unroll
     for (int s = 0; s < kMaxSplits; ++s) M = fmaxf(M, s < S ? ml[s].x : -INFINITY);
@@ -648,26 +668,15 @@ __global__ __launch_bounds__(kCombBlock) void k_combine(AttnArgs at, const int32
     for (int s = 0; s < kMaxSplits; s += 4)
       *(v4f*)&wsh[lane][s] = v4f{e[s] * inv, e[s + 1] * inv, e[s + 2] * inv, e[s + 3] * inv};
   }
-  if (part_bad != nullptr && blockIdx.x == 0) {
-    const uint32_t nb = wave_sum_u32(lane < S ? (uint32_t)part_bad[(int64_t)b * S + lane] : 0u);
-    if (lane == 0) stats[b].bad_indices = (int32_t)nb;
-  }
   lds_barrier();
   DSA_MARK(2, 2);
-  const int64_t split_stride = (int64_t)HP * Dv;
-  const float* po = at.part_o + (int64_t)b * S * split_stride;
-  if (FRAG) {
-    const int e4 = blockIdx.x * kCombBlock + lane;  // 16-byte element index
-    if (e4 * 4 >= HP * Dv) return;
+  // the count of invalid indices (stand-alone attention) is read last, so its wait
+  // does not hold up the combine
+  const bool count_bad = part_bad != nullptr && blockIdx.x == 0;
+  if (el < nel && FRAG) {
     const int tiles = Dv / 16;
-    const int tile = e4 >> 6, l = e4 & 63;
+    const int tile = el >> 6, l = el & 63;
     const int h0 = 16 * (tile / tiles) + 4 * (l >> 4), v = 16 * (tile % tiles) + (l & 15);
-    v4f part[kMaxSplits];
-#pragma unroll
-    for (int s = 0; s < kMaxSplits; ++s) {
-      const int sc = s < S ? s : S - 1;  // weight 0 past S
-      part[s] = *(const v4f*)(po + sc * split_stride + (int64_t)e4 * 4);
-    }
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -675,36 +684,32 @@ __global__ __launch_bounds__(kCombBlock) void k_combine(AttnArgs at, const int32
 #pragma unroll
       for (int s4 = 0; s4 < kMaxSplits / 4; ++s4) {
         const v4f w = wrow[s4];
-        acc[r] = fmaf(w[0], part[4 * s4][r], acc[r]);
-        acc[r] = fmaf(w[1], part[4 * s4 + 1][r], acc[r]);
-        acc[r] = fmaf(w[2], part[4 * s4 + 2][r], acc[r]);
-        acc[r] = fmaf(w[3], part[4 * s4 + 3][r], acc[r]);
+        acc[r] = fmaf(w[0], part[FRAG ? 4 * s4 : 0][r], acc[r]);
+        acc[r] = fmaf(w[1], part[FRAG ? 4 * s4 + 1 : 0][r], acc[r]);
+        acc[r] = fmaf(w[2], part[FRAG ? 4 * s4 + 2 : 0][r], acc[r]);
+        acc[r] = fmaf(w[3], part[FRAG ? 4 * s4 + 3 : 0][r], acc[r]);
       }
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       if (h0 + r < Hq) out[((int64_t)b * Hq + h0 + r) * Dv + v] = acc[r];
-  } else {
-    const int e = blockIdx.x * kCombBlock + lane;
-    if (e >= Hq * Dv) return;
-    const int h = e / Dv;
-    float part[kMaxSplits];
-#pragma unroll
-    for (int s = 0; s < kMaxSplits; ++s) {
-      const int sc = s < S ? s : S - 1;
-      part[s] = po[sc * split_stride + e];
-    }
-    const v4f* wrow = reinterpret_cast<const v4f*>(wsh[h]);
+  } else if (el < nel) {
+    const int hh = el / Dv;
+    const v4f* wrow = reinterpret_cast<const v4f*>(wsh[hh]);
     float acc = 0.f;
 #pragma unroll
     for (int s4 = 0; s4 < kMaxSplits / 4; ++s4) {
       const v4f w = wrow[s4];
-      acc = fmaf(w[0], part[4 * s4], acc);
-      acc = fmaf(w[1], part[4 * s4 + 1], acc);
-      acc = fmaf(w[2], part[4 * s4 + 2], acc);
-      acc = fmaf(w[3], part[4 * s4 + 3], acc);
+      acc = fmaf(w[0], partf[FRAG ? 0 : 4 * s4], acc);
+      acc = fmaf(w[1], partf[FRAG ? 0 : 4 * s4 + 1], acc);
+      acc = fmaf(w[2], partf[FRAG ? 0 : 4 * s4 + 2], acc);
+      acc = fmaf(w[3], partf[FRAG ? 0 : 4 * s4 + 3], acc);
     }
-    out[(int64_t)b * Hq * Dv + e] = acc;
+    out[(int64_t)b * Hq * Dv + el] = acc;
+  }
+  if (count_bad) {
+    const uint32_t nb = wave_sum_u32(lane < S ? (uint32_t)part_bad[(int64_t)b * S + lane] : 0u);
+    if (lane == 0) stats[b].bad_indices = (int32_t)nb;
   }
   DSA_MARK(2, 1);
 }
