@@ -248,6 +248,19 @@ def main():
         % (score_us, select_us, combine_us))
     stats = binding.dsa_read_stats(ws, B)
 
+    # reference read rate: a vendor streaming reduction over the same key caches, in the
+    # same cold rotation (context for the roofline fraction, not part of the metric)
+    rd = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(4 * R)]
+    acc = torch.zeros((), dtype=torch.int64, device="cuda")
+    for i, (r0, r1) in enumerate(rd):
+        ik32 = sets[i % R][0]["ik"].view(torch.int32)
+        r0.record()
+        torch.sum(ik32, dtype=torch.int64, out=acc)
+        r1.record()
+    torch.cuda.synchronize()
+    read_us = float(np.mean([r0.elapsed_time(r1) for r0, r1 in rd[R:]])) * 1e3
+    read_bytes = c["N"] * c["Di"]
+
     if args.copy_calibration:
         src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
@@ -314,6 +327,14 @@ def main():
             "launch_us": round(select_us, 3),
         },
         "cpu_baseline": cpu,
+        "read_reference": {
+            "what": "torch.sum over one layer's key cache (int8 viewed as int32), same cold rotation, "
+                    "eager; HIP events around each launch, so dispatch latency is included (the "
+                    "kernel trace gives the kernel's own time); a streaming-read rate for this buffer",
+            "bytes": read_bytes,
+            "us": round(read_us, 3),
+            "GBps": round(read_bytes / (read_us * 1e-6) / 1e9, 1),
+        },
         "kernel_us_events": {"score": round(score_us, 3), "select_attend": round(select_us, 3),
                                    "combine": round(combine_us, 3)},
         "step_essential_bytes": step_bytes,

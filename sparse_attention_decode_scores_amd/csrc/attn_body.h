@@ -74,24 +74,36 @@ struct AttnMfma {
     if (!kQInLds) return f;
     const int Dk = p.Dk, cpr = Dk >> 3;
     const uint8_t* q = reinterpret_cast<const uint8_t*>(p.q) + (int64_t)b * p.Hq * Dk * 2;
+    const int step_h = kAttnBlock / cpr, step_c = kAttnBlock - step_h * cpr;
+    int h = (int)threadIdx.x / cpr, c = (int)threadIdx.x - h * cpr;  // one divide, then steps
 #pragma unroll
-    for (int j = 0; j < kQPer; ++j) {  // every slot loads a present value (clamped)
-      int i = threadIdx.x + kAttnBlock * j;
-      i = i < HP * cpr ? i : HP * cpr - 1;
-      const int h = i / cpr, c = i - h * cpr;
+    for (int j = 0; j < kQPer; ++j) {  // every slot loads a present value (clamped head)
       const int hc = h < p.Hq ? h : p.Hq - 1;
       f.v[kQInLds ? j : 0] = *(const v4i*)(q + ((int64_t)hc * Dk + 8 * c) * 2);
+      c += step_c;
+      h += step_h;
+      if (c >= cpr) {
+        c -= cpr;
+        ++h;
+      }
     }
     return f;
   }
   __device__ static void store_q(const QFrag& f, const AttnArgs& p, uint8_t* work) {
     if (!kQInLds) return;
     const int Dk = p.Dk, rb = row_bytes(Dk), cpr = Dk >> 3;
+    const int step_h = kAttnBlock / cpr, step_c = kAttnBlock - step_h * cpr;
+    int h = (int)threadIdx.x / cpr, c = (int)threadIdx.x - h * cpr;  // one divide, then steps
 #pragma unroll
     for (int j = 0; j < kQPer; ++j) {
-      const int i = threadIdx.x + kAttnBlock * j;
-      const int h = i / cpr, c = i - h * cpr;
-      if (i < HP * cpr) *(v4i*)(work + h * rb + 16 * c) = h < p.Hq ? f.v[kQInLds ? j : 0] : v4i{0, 0, 0, 0};
+      if ((int)threadIdx.x + kAttnBlock * j < HP * cpr)
+        *(v4i*)(work + h * rb + 16 * c) = h < p.Hq ? f.v[kQInLds ? j : 0] : v4i{0, 0, 0, 0};
+      c += step_c;
+      h += step_h;
+      if (c >= cpr) {
+        c -= cpr;
+        ++h;
+      }
     }
   }
 
@@ -120,6 +132,27 @@ struct AttnMfma {
       lrun[h] = 0.f;
     }
 
+    // gather slot j of this thread is chunk i = tid + 512 j of a sub-block: row
+    // i / cpr, 16-byte column i % cpr, stepped without dividing (a divide by a
+    // runtime value costs dozens of instructions)
+    int rr[kMaxLoads], cc[kMaxLoads];
+    {
+      const int cpr = Dk >> 3;
+      const int step_r = kAttnBlock / cpr, step_c = kAttnBlock - step_r * cpr;
+      int r = tid / cpr, c = tid - r * cpr;
+#pragma unroll
+      for (int j = 0; j < kMaxLoads; ++j) {
+        rr[j] = r;
+        cc[j] = c;
+        c += step_c;
+        r += step_r;
+        if (c >= cpr) {
+          c -= cpr;
+          ++r;
+        }
+      }
+    }
+
     for (int s0 = 0; s0 < cnt; s0 += SB) {
       const int nr = cnt - s0 < SB ? cnt - s0 : SB;
       // gather the sub-block's rows with 16-byte loads: every position is read from
@@ -129,24 +162,20 @@ struct AttnMfma {
       // present rows' data is stored (absent rows store zeros).
       const int cpr = Dk >> 3;
       const int nch = SB * cpr;  // <= kMaxLoads * block size (checked when the path is chosen)
+      DSA_MARK(1, 12);
       int32_t rp[kMaxLoads];
 #pragma unroll
-      for (int j = 0; j < kMaxLoads; ++j) {
-        const int r = (tid + kAttnBlock * j) / cpr;
-        rp[j] = (int32_t)pos_at(s0 + (r < nr ? r : nr - 1));
-      }
+      for (int j = 0; j < kMaxLoads; ++j) rp[j] = (int32_t)pos_at(s0 + (rr[j] < nr ? rr[j] : nr - 1));
       v4i buf[kMaxLoads];
 #pragma unroll
-      for (int j = 0; j < kMaxLoads; ++j) {
-        const int c = (tid + kAttnBlock * j) % cpr;
-        buf[j] = *(const v4i*)(kv + ((int64_t)rp[j] * Dk + 8 * c) * 2);
-      }
+      for (int j = 0; j < kMaxLoads; ++j) buf[j] = *(const v4i*)(kv + ((int64_t)rp[j] * Dk + 8 * cc[j]) * 2);
+      DSA_MARK(1, 13);
 #pragma unroll
       for (int j = 0; j < kMaxLoads; ++j) {
-        const int i = tid + kAttnBlock * j;
-        const int r = i / cpr, c = i - r * cpr;
-        if (i < nch) *(v4i*)(rows + r * rb + 16 * c) = r < nr ? buf[j] : v4i{0, 0, 0, 0};
+        if (tid + kAttnBlock * j < nch)
+          *(v4i*)(rows + rr[j] * rb + 16 * cc[j]) = rr[j] < nr ? buf[j] : v4i{0, 0, 0, 0};
       }
+      DSA_MARK(1, 14);
       lds_barrier();
       DSA_MARK(1, 6);
       // logits: D[head][row], head = 16*mt + 4*(l/16) + r, row = 16*nt + l%16

@@ -263,57 +263,76 @@ struct BlockCandSmem {
   uint64_t all[kWaveStage];                 // all staged keys, position order
   uint32_t rank[kWaveStage];
   uint32_t wcount[BLOCK / 64];
+  int32_t tlo;
+  uint32_t ok;
 };
 
-// The same result as chunk_candidates for one chunk, by the whole block with
-// three barriers (the caller's barrier after filling `scores` and `hist` comes
-// first): every wave finds the threshold bin's lowest score (threshold_floor);
-// wave w stages the keys at or above it from its own run of 64-position rows
-// (ballot compaction, position order); the runs are concatenated; eight (or
-// four) threads per staged key count the staged keys above it, which is its
-// rank; wave 0 writes the m best in position order and x = the key of rank m.
-// Returns false (uniformly, nothing written) where wave_chunk_candidates does.
+// The same result as chunk_candidates for one chunk, by the first four waves of
+// the block (one per SIMD, so none shares its issue slots); the other waves only
+// pass the barriers. Four barriers (the caller's barrier after filling `scores`
+// and `hist` comes first): wave 0 finds the threshold bin's lowest score
+// (threshold_floor); active wave w stages the keys at or above it from its own
+// run of 64-position rows (ballot compaction, position order); the runs are
+// concatenated; two or four threads per staged key count the staged keys above
+// it, which is its rank; wave 0 writes the m best in position order and x = the
+// key of rank m. Returns false (uniformly, nothing written) where
+// wave_chunk_candidates does.
 template <int BLOCK>
 __device__ __forceinline__ bool block_chunk_candidates(const int32_t* scores, int count, uint32_t pos0,
                                                        int m, const uint32_t* hist,
                                                        uint64_t* __restrict__ out,
                                                        uint64_t* __restrict__ x_out,
                                                        BlockCandSmem<BLOCK>& sm) {
-  constexpr int W = BLOCK / 64;
+  constexpr int W = 4;            // active waves
+  constexpr int AT = 64 * W;      // active threads
+  static_assert(BLOCK >= AT, "four waves");
   const int tid = threadIdx.x, l = lane_id(), w = wave_id();
+  const bool active = w < W;
   if (count <= m) {
     for (int i = tid; i < m; i += BLOCK) out[i] = i < count ? make_key(scores[i], pos0 + (uint32_t)i) : 0ull;
     if (tid == 0) *x_out = 0;
     return true;
   }
-  int32_t tlo;
-  if (!threshold_floor(hist, count, m, &tlo)) return false;  // same outcome in every wave
+  // wave 0 finds the threshold; the others wait at the barrier that publishes it
+  if (w == 0) {
+    int32_t t;
+    const bool ok = threshold_floor(hist, count, m, &t);
+    if (l == 0) {
+      sm.tlo = t;
+      sm.ok = ok ? 1u : 0u;
+    }
+  }
+  lds_barrier();
+  if (!sm.ok) return false;  // uniform
+  const int32_t tlo = sm.tlo;
   DSA_MARK(3, 1);
 
   const uint64_t lt = lanemask_lt();
   const uint32_t cap = (uint32_t)m + 64;
-  const int nrows = (count + 63) >> 6;
-  const int per = (nrows + W - 1) / W;
-  const int rbeg = w * per, rend = rbeg + per < nrows ? rbeg + per : nrows;
   uint32_t ns = 0;
-  for (int r0 = rbeg; r0 < rend; r0 += 4) {
-    int32_t v[4];
+  if (active) {
+    const int nrows = (count + 63) >> 6;
+    const int per = (nrows + W - 1) / W;
+    const int rbeg = w * per, rend = rbeg + per < nrows ? rbeg + per : nrows;
+    for (int r0 = rbeg; r0 < rend; r0 += 4) {
+      int32_t v[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int i = 64 * (r0 + t) + l;
-      v[t] = scores[i < count ? i : count - 1];
-    }
+      for (int t = 0; t < 4; ++t) {
+        const int i = 64 * (r0 + t) + l;
+        v[t] = scores[i < count ? i : count - 1];
+      }
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int i = 64 * (r0 + t) + l;
-      const bool in = r0 + t < rend && i < count && v[t] >= tlo;
-      const uint64_t b = __ballot(in);
-      const uint32_t slot = ns + (uint32_t)__popcll(b & lt);
-      if (in && slot < cap) sm.wstage[w][slot] = make_key(v[t], pos0 + (uint32_t)i);
-      ns += (uint32_t)__popcll(b);
+      for (int t = 0; t < 4; ++t) {
+        const int i = 64 * (r0 + t) + l;
+        const bool in = r0 + t < rend && i < count && v[t] >= tlo;
+        const uint64_t b = __ballot(in);
+        const uint32_t slot = ns + (uint32_t)__popcll(b & lt);
+        if (in && slot < cap) sm.wstage[w][slot] = make_key(v[t], pos0 + (uint32_t)i);
+        ns += (uint32_t)__popcll(b);
+      }
     }
+    if (l == 0) sm.wcount[w] = ns;
   }
-  if (l == 0) sm.wcount[w] = ns;
   lds_barrier();
   uint32_t total = 0, off = 0;
 #pragma unroll
@@ -323,22 +342,22 @@ __device__ __forceinline__ bool block_chunk_candidates(const int32_t* scores, in
     total += c;
   }
   if (total > cap) return false;  // uniform
-  for (int j = l; j < (int)ns; j += 64) sm.all[off + j] = sm.wstage[w][j];
+  if (active)
+    for (int j = l; j < (int)ns; j += 64) sm.all[off + j] = sm.wstage[w][j];
   lds_barrier();
   DSA_MARK(3, 8);
 
-  // rank of staged key i: TPE threads each compare it with every TPE-th key
-  const int tpe = total > (uint32_t)(BLOCK / 8) ? 4 : 8;  // BLOCK / tpe >= cap keys
+  // rank of staged key i: tpe active threads each compare it with every tpe-th key
+  const int tpe = total > (uint32_t)(AT / 4) ? 2 : 4;  // AT / tpe >= cap keys
   const int i = tid / tpe, part = tid % tpe;
   uint32_t r = 0;
-  if (i < (int)total) {
+  if (active && i < (int)total) {
     const uint64_t me = sm.all[i];
     for (int j = part; j < (int)total; j += tpe) r += sm.all[j] > me ? 1u : 0u;
   }
   r += (uint32_t)__builtin_amdgcn_mov_dpp((int)r, dpp::kQuadXor1, 0xF, 0xF, false);
-  r += (uint32_t)__builtin_amdgcn_mov_dpp((int)r, dpp::kQuadXor2, 0xF, 0xF, false);
-  if (tpe == 8) r += (uint32_t)__builtin_amdgcn_mov_dpp((int)r, dpp::kRowHalfMirror, 0xF, 0xF, false);
-  if (part == 0 && i < (int)total) sm.rank[i] = r;
+  if (tpe == 4) r += (uint32_t)__builtin_amdgcn_mov_dpp((int)r, dpp::kQuadXor2, 0xF, 0xF, false);
+  if (active && part == 0 && i < (int)total) sm.rank[i] = r;
   lds_barrier();
   DSA_MARK(3, 9);
 

@@ -56,20 +56,44 @@ __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 __device__ __forceinline__ uint64_t lanemask_lt() { return (1ull << lane_id()) - 1ull; }
 
 // Phase timestamps for performance analysis builds (-DDSA_TRACE): thread 0 of a
-// workgroup stores the 100 MHz real-time counter into a per-kernel table. In
-// normal builds the marks compile to nothing.
+// workgroup keeps the 100 MHz real-time counter per phase in LDS (a global store
+// here would hold up the wave's next wait for memory) and copies the table out at
+// the kernel's exits. In normal builds the marks compile to nothing.
 #ifdef DSA_TRACE
 constexpr int kTraceKernels = 4, kTraceBlocks = 512, kTracePhases = 16;
 extern __device__ uint64_t dsa_trace[kTraceKernels][kTraceBlocks][kTracePhases];
+__device__ __forceinline__ uint64_t* dsa_trace_lds() {
+  __shared__ uint64_t t[kTraceKernels * kTracePhases];
+  return t;
+}
+#define DSA_TRACE_BEGIN()                                                                    \
+  do {                                                                                       \
+    if (threadIdx.x == 0)                                                                    \
+      for (int i_ = 0; i_ < kTraceKernels * kTracePhases; ++i_) dsa_trace_lds()[i_] = 0;     \
+  } while (0)
 #define DSA_MARK(kernel, phase)                                                              \
+  do {                                                                                       \
+    if (threadIdx.x == 0)                                                                    \
+      dsa_trace_lds()[(kernel) * kTracePhases + (phase)] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
+#define DSA_TRACE_FLUSH()                                                                    \
   do {                                                                                       \
     const int blk_ = blockIdx.x + gridDim.x * blockIdx.y;                                    \
     if (threadIdx.x == 0 && blk_ < kTraceBlocks)                                             \
-      dsa_trace[kernel][blk_][phase] = __builtin_amdgcn_s_memrealtime();                     \
+      for (int i_ = 0; i_ < kTraceKernels * kTracePhases; ++i_) {                            \
+        const uint64_t v_ = dsa_trace_lds()[i_];                                             \
+        if (v_) dsa_trace[i_ / kTracePhases][blk_][i_ % kTracePhases] = v_;                  \
+      }                                                                                      \
   } while (0)
 #else
+#define DSA_TRACE_BEGIN() \
+  do {                    \
+  } while (0)
 #define DSA_MARK(kernel, phase) \
   do {                          \
+  } while (0)
+#define DSA_TRACE_FLUSH() \
+  do {                    \
   } while (0)
 #endif
 
@@ -192,14 +216,19 @@ __device__ __forceinline__ uint32_t block_select_range(Each each, uint32_t lo, u
   uint32_t above = 0;
   uint32_t need = (uint32_t)rank;
   int buf = 0;
+  bool first = true;
   while (shift > 0) {
     const int nshift = shift > kRadixBits ? shift - kRadixBits : 0;
     uint32_t* hist = sm.hist[buf];
-    each([&](uint32_t v) {
-      const uint32_t off = v - lo;
-      if (((uint64_t)off >> shift) == (uint64_t)prefix)
-        atomicAdd(&hist[(off >> nshift) & (kRadixBins - 1)], 1u);
-    });
+    if (first) {  // every value is in range: no prefix to match (and shift may be 32)
+      each([&](uint32_t v) { atomicAdd(&hist[((v - lo) >> nshift) & (kRadixBins - 1)], 1u); });
+    } else {  // shift < 32 from the second pass on
+      each([&](uint32_t v) {
+        const uint32_t off = v - lo;
+        if ((off >> shift) == prefix) atomicAdd(&hist[(off >> nshift) & (kRadixBins - 1)], 1u);
+      });
+    }
+    first = false;
     lds_barrier();
     DSA_MARK(3, 2 + 2 * (shift > kRadixBits ? 0 : 1));
     uint32_t h[BPT], own = 0;

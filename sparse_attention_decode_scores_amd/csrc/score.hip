@@ -61,6 +61,7 @@ __global__ __launch_bounds__(kScoreBlock) void k_score(ScoreArgs a) {
 
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   const int c = blockIdx.x;
+  DSA_TRACE_BEGIN();
   DSA_MARK(0, 0);
   const int64_t cbeg = (int64_t)c * a.P;
   const int64_t clen64 = (int64_t)a.nmax - cbeg;
@@ -200,6 +201,18 @@ __global__ __launch_bounds__(kScoreBlock) void k_score(ScoreArgs a) {
   if (CAND) {
     lds_barrier();
     DSA_MARK(0, 3);
+    // the scores leave LDS first: the selection below waits for no memory
+    // operation, so these stores complete underneath it. The key requests past
+    // the chunk's end (buffer reads that return zeros) are drained before them,
+    // so no later wait for those registers covers the stores.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // gfx9 encoding: vmcnt(0), expcnt and lgkmcnt untouched
+    for (int bb = 0; bb < a.Bg; ++bb) {
+      const int b = a.b0 + bb;
+      const int64_t n64 = (int64_t)a.lens.n[b] - cbeg;
+      const int count = n64 > clen ? clen : (int)(n64 > 0 ? n64 : 0);
+      int32_t* dst = a.scores + (int64_t)b * a.N + cbeg;
+      for (int i = tid; i < count; i += kScoreBlock) dst[i] = sc[bb * a.P + i];
+    }
     if (ONE) {
       // one row: the whole block selects the chunk's candidates
       const int b = a.b0;
@@ -222,13 +235,6 @@ __global__ __launch_bounds__(kScoreBlock) void k_score(ScoreArgs a) {
       }
     }
     DSA_MARK(0, 5);
-    for (int bb = 0; bb < a.Bg; ++bb) {
-      const int b = a.b0 + bb;
-      const int64_t n64 = (int64_t)a.lens.n[b] - cbeg;
-      const int count = n64 > clen ? clen : (int)(n64 > 0 ? n64 : 0);
-      int32_t* dst = a.scores + (int64_t)b * a.N + cbeg;
-      for (int i = tid; i < count; i += kScoreBlock) dst[i] = sc[bb * a.P + i];
-    }
     lds_barrier();
     for (int bb = 0; bb < a.Bg; ++bb) {  // rows whose threshold bin held too many keys
       if (!fallback[bb]) continue;
@@ -242,6 +248,7 @@ __global__ __launch_bounds__(kScoreBlock) void k_score(ScoreArgs a) {
     }
     DSA_MARK(0, 4);
   }
+  DSA_TRACE_FLUSH();
 }
 
 int score_max_chunk() { return kChunkPerThread * kScoreBlock; }

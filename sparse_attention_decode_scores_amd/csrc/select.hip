@@ -276,6 +276,40 @@ __device__ __forceinline__ uint64_t select_row_exhaustive(const int32_t* __restr
   return sm.kstar;
 }
 
+// write_selected for one batch of E keys per thread with their score bits sv and
+// presence mask already extracted (32-bit tests, writes predicated rather than
+// branched per key).
+template <int E>
+__device__ __forceinline__ void write_selected_u(const uint64_t (&key)[E], const uint32_t (&sv)[E],
+                                                 uint32_t vmask, uint32_t T, uint32_t need_eq,
+                                                 uint64_t* sel, SelSmem& sm, uint32_t* tot_sel,
+                                                 uint32_t* tot_eq) {
+  uint32_t gt = 0, eq = 0;
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    const bool v = (vmask >> j) & 1u;
+    gt += v && sv[j] > T ? 1u : 0u;
+    eq += v && sv[j] == T ? 1u : 0u;
+  }
+  uint32_t total;
+  const uint32_t before = block_excl_scan_u32<kSelBlock>(gt | (eq << 16), sm.radix.part, &total);
+  uint32_t eqr = before >> 16;  // keys at T in earlier threads
+  uint32_t slot = (before & 0xFFFF) + (eqr < need_eq ? eqr : need_eq);
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    const bool v = (vmask >> j) & 1u;
+    const bool at_t = v && sv[j] == T;
+    const bool take = (v && sv[j] > T) || (at_t && eqr < need_eq);
+    if (take) sel[slot] = key[j];
+    if (at_t && eqr == need_eq - 1) sm.kstar = key[j];
+    slot += take ? 1u : 0u;
+    eqr += at_t ? 1u : 0u;
+  }
+  const uint32_t teq = total >> 16;
+  *tot_sel = (total & 0xFFFF) + (teq < need_eq ? teq : need_eq);
+  *tot_eq = teq;
+}
+
 // LDS: SelSmem | selected keys [k] | region: the attention working set, or the
 // sort state of the exhaustive path (the two roles never need both).
 template <class Attn>
@@ -290,6 +324,7 @@ __global__ __launch_bounds__(kSelBlock) void k_select(SelArgs a, AttnArgs at) {
   const bool attn_role = (int)blockIdx.x < S;
   const int n = a.lens.n[b];
   const int32_t* row = a.scores + (int64_t)b * a.N;
+  DSA_TRACE_BEGIN();
   DSA_MARK(1, 0);
 
   int reason = a.force ? 1 : (a.have_cand ? 0 : 3);
@@ -314,17 +349,23 @@ __global__ __launch_bounds__(kSelBlock) void k_select(SelArgs a, AttnArgs at) {
   const typename Attn::QFrag qf = Attn::load_q(at, b);  // every workgroup: exact wait counts
   radix_clear<kSelBlock>(sm.radix);
   if (reason == 0) {
-    uint32_t nz = 0, lo = 0xFFFFFFFFu, hi = 0;
+    // 32-bit views of the candidate keys: score bits and presence (a present key's
+    // low word, 0xFFFFFFFF - position, is never 0)
+    uint32_t sv[kUPerThread], vmask = 0;
 #pragma unroll
-    for (int j = 0; j < kUPerThread; ++j)
-      if (key[j] != 0) {
-        const uint32_t u = key_ubits(key[j]);
-        ++nz;
-        lo = u < lo ? u : lo;
-        hi = u > hi ? u : hi;
-      }
+    for (int j = 0; j < kUPerThread; ++j) {
+      sv[j] = key_ubits(key[j]);
+      vmask |= (uint32_t)key[j] != 0u ? 1u << j : 0u;
+    }
+    uint32_t lo = 0xFFFFFFFFu, hi = 0;
+#pragma unroll
+    for (int j = 0; j < kUPerThread; ++j) {
+      const bool v = (vmask >> j) & 1u;
+      lo = v && sv[j] < lo ? sv[j] : lo;
+      hi = v && sv[j] > hi ? sv[j] : hi;
+    }
     DSA_MARK(1, 11);
-    const Stats4 st = block_stats(nz, lo, hi, mx, sm);
+    const Stats4 st = block_stats((uint32_t)__popc(vmask), lo, hi, mx, sm);
     nvalid = st.sum;
     mx = st.mx;
     DSA_MARK(1, 1);
@@ -332,15 +373,14 @@ __global__ __launch_bounds__(kSelBlock) void k_select(SelArgs a, AttnArgs at) {
     auto each = [&](auto f) {
 #pragma unroll
       for (int j = 0; j < kUPerThread; ++j)
-        if (key[j] != 0) f(key_ubits(key[j]));
+        if ((vmask >> j) & 1u) f(sv[j]);
     };
     uint32_t above;
     const uint32_t T = block_select_range<kSelBlock>(each, st.lo, st.hi, (int)kk, &above, sm.radix);
     const uint32_t need_eq = kk - above;
     DSA_MARK(1, 2);
     uint32_t ts, te;
-    write_selected<kUPerThread>(key, [&](int j) { return key[j] != 0; }, T, need_eq, 0, 0, sel, sm,
-                                &ts, &te);
+    write_selected_u<kUPerThread>(key, sv, vmask, T, need_eq, sel, sm, &ts, &te);
     lds_barrier();
     DSA_MARK(1, 3);
     kstar = sm.kstar;
@@ -356,7 +396,10 @@ __global__ __launch_bounds__(kSelBlock) void k_select(SelArgs a, AttnArgs at) {
 
   if (reason != 0) {
     if (!attn_role) {
-      if ((int)blockIdx.x != S) return;  // one ranking workgroup sorts the whole row
+      if ((int)blockIdx.x != S) {  // one ranking workgroup sorts the whole row
+        DSA_TRACE_FLUSH();
+        return;
+      }
       uint64_t* ba = a.sortbuf + (int64_t)b * 2 * a.N;
       const uint64_t* sorted =
           block_sort_row(row, n, ba, ba + a.N, *reinterpret_cast<SortSmem*>(region));
@@ -386,6 +429,7 @@ __global__ __launch_bounds__(kSelBlock) void k_select(SelArgs a, AttnArgs at) {
         st.reserved = 0;
         a.stats[b] = st;
       }
+      DSA_TRACE_FLUSH();
       return;
     }
     // attention workgroups select the same set from every position
@@ -405,6 +449,7 @@ __global__ __launch_bounds__(kSelBlock) void k_select(SelArgs a, AttnArgs at) {
     Attn::run(at, b, blockIdx.x, [&](int i) { return (int64_t)key_pos(sel[e0 + i]); }, cnt,
               region);
     DSA_MARK(1, 10);
+    DSA_TRACE_FLUSH();
     return;
   }
 
@@ -455,6 +500,7 @@ __global__ __launch_bounds__(kSelBlock) void k_select(SelArgs a, AttnArgs at) {
       a.stats[b] = st;
     }
   }
+  DSA_TRACE_FLUSH();
 }
 
 template <class Attn>
@@ -627,6 +673,7 @@ __global__ __launch_bounds__(kCombBlock) void k_combine(AttnArgs at, const int32
   const int b = blockIdx.y, lane = threadIdx.x;
   const int S = at.S, Hq = at.Hq, Dv = at.Dv;
   const int HP = FRAG ? (Hq + 15) / 16 * 16 : Hq;
+  DSA_TRACE_BEGIN();
   DSA_MARK(2, 0);
   // Every load is issued before any arithmetic: first the (max, sum) pairs this lane
   // turns into weights, then the partial outputs this lane combines (they do not
@@ -712,6 +759,7 @@ __global__ __launch_bounds__(kCombBlock) void k_combine(AttnArgs at, const int32
     if (lane == 0) stats[b].bad_indices = (int32_t)nb;
   }
   DSA_MARK(2, 1);
+  DSA_TRACE_FLUSH();
 }
 
 hipError_t launch_combine(const AttnArgs& at, const int32_t* part_bad, RowStats* stats, float* out,
