@@ -55,12 +55,16 @@ def short_name(name):
 
 
 def kernel_stats(db):
+    """Per (kernel, grid) rows: one kernel launched with different grids (different
+    workloads in one run) is listed once per grid."""
     con = _db(db)
-    rows = con.execute("SELECT name, COUNT(*), AVG(end - start), MIN(end - start), MAX(end - start), "
-                       "SUM(end - start) FROM kernels GROUP BY name ORDER BY SUM(end - start) DESC").fetchall()
-    total = sum(r[5] for r in rows) or 1
-    return [{"name": r[0], "calls": r[1], "avg_us": r[2] / 1e3, "min_us": r[3] / 1e3, "max_us": r[4] / 1e3,
-             "pct": 100.0 * r[5] / total} for r in rows]
+    rows = con.execute("SELECT name, grid_x * grid_y * grid_z, workgroup_x * workgroup_y * workgroup_z, "
+                       "COUNT(*), AVG(end - start), MIN(end - start), MAX(end - start), SUM(end - start) "
+                       "FROM kernels GROUP BY name, grid_x, grid_y, grid_z "
+                       "ORDER BY SUM(end - start) DESC").fetchall()
+    total = sum(r[7] for r in rows) or 1
+    return [{"name": r[0], "grid": r[1], "block": r[2], "calls": r[3], "avg_us": r[4] / 1e3,
+             "min_us": r[5] / 1e3, "max_us": r[6] / 1e3, "pct": 100.0 * r[7] / total} for r in rows]
 
 
 def counter_per_kernel(db, counter):
@@ -88,12 +92,13 @@ def cmd_stats(args):
     rows = kernel_stats(args.db)
     lines = ["# Kernel durations: %s" % args.title, "",
              "Command (from the repository root on the GPU host):", "", "```", args.command, "```", "",
-             "| kernel | calls | avg us | min us | max us | % of kernel time |",
-             "|---|---:|---:|---:|---:|---:|"]
+             "| kernel | grid threads | calls | avg us | min us | max us | % of kernel time |",
+             "|---|---:|---:|---:|---:|---:|---:|"]
     for r in rows[:args.top]:
         nm = r["name"] if len(r["name"]) <= 90 else r["name"][:87] + "..."
-        lines.append("| `%s` | %d | %.2f | %.2f | %.2f | %.1f |"
-                     % (nm.replace("|", "\\|"), r["calls"], r["avg_us"], r["min_us"], r["max_us"], r["pct"]))
+        lines.append("| `%s` | %d | %d | %.2f | %.2f | %.2f | %.1f |"
+                     % (nm.replace("|", "\\|"), r["grid"], r["calls"], r["avg_us"], r["min_us"], r["max_us"],
+                        r["pct"]))
     lines.append("")
     if args.note:
         lines += [args.note, ""]
