@@ -108,7 +108,23 @@ dsa_status check_ws(void* ws, size_t ws_bytes, const Layout& L) {
 struct ChunkPlan {
   int P, G, m;
 };
-ChunkPlan chunk_plan(int nmax, int k) {
+// One-row plan (score kernel k_score_row): chunks of whole 32-key units, as many
+// chunks as candidate slots allow (at most one per compute unit), so every wave of
+// a chunk has at most one unit more than another.
+ChunkPlan chunk_plan_row(int nmax, int k) {
+  ChunkPlan c;
+  c.m = k <= 2048 ? 32 : 64;
+  const int gmax = kCandCap / c.m < kMaxChunks ? kCandCap / c.m : kMaxChunks;
+  const int64_t units = ((int64_t)nmax + 31) / 32;
+  int64_t per = (units + gmax - 1) / gmax;
+  if (per > 8) per = (per + 7) / 8 * 8;  // the same number of units for every wave
+  c.P = (int)(per * 32);
+  c.G = (int)(((int64_t)nmax + c.P - 1) / c.P);
+  return c;
+}
+
+ChunkPlan chunk_plan(int nmax, int k, bool row) {
+  if (row) return chunk_plan_row(nmax, k);
   ChunkPlan c;
   if (nmax <= kCandCap) {  // short rows: every position is a candidate
     c.P = 64;
@@ -133,6 +149,7 @@ int rows_per_score_launch(int Hi, int Di, int B) {
 }
 
 dsa_status hip_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
+
 
 dsa_status run_scores(const int8_t* iq, const int8_t* iw, const int8_t* ik, const RowLens& lens,
                       int B, int Hi, int Di, int64_t N, int nmax, int32_t* scores, bool cand,
@@ -159,6 +176,11 @@ dsa_status run_scores(const int8_t* iq, const int8_t* iw, const int8_t* ik, cons
     a.G = (int)(((int64_t)nmax + a.P - 1) / a.P);
   }
   const int MT = (Hi + 31) / 32, KT = Di / 32;
+  if (cand && B == 1) {  // the decode hot path: one row, candidates on
+    a.b0 = 0;
+    a.Bg = 1;
+    return hip_status(launch_score_row(a, MT, KT, kScoreRowDepth, a.G, s, t));
+  }
   const int bg = rows_per_score_launch(Hi, Di, B);
   for (int b0 = 0; b0 < B; b0 += bg) {
     a.b0 = b0;
@@ -174,7 +196,10 @@ dsa_status run_scores(const int8_t* iq, const int8_t* iw, const int8_t* ik, cons
 
 bool cand_fits(int Hi, int Di, int B, const ChunkPlan& cp, bool fused) {
   size_t need;
-  if (fused) {
+  if (fused && B == 1) {
+    if (cp.P > score_row_max_chunk()) return false;
+    need = score_row_lds_bytes(cp.P);
+  } else if (fused) {
     if (cp.P > score_max_chunk()) return false;
     const int bg = rows_per_score_launch(Hi, Di, B);
     need = score_lds_bytes((Hi + 31) / 32, Di / 32, bg, cp.P, true);
@@ -273,7 +298,7 @@ dsa_status dsa_topk_select(const int32_t* scores, const int32_t* ctx_len, int B,
   const Layout L = layout(B, N, k, 1, 1);
   if ((st = check_ws(ws, ws_bytes, L)) != DSA_OK) return st;
   uint8_t* w = static_cast<uint8_t*>(ws);
-  const ChunkPlan cp = chunk_plan(nmax, k);
+  const ChunkPlan cp = chunk_plan(nmax, k, false);
   const bool have = cand_fits(0, 32, B, cp, false) && !(flags & DSA_FLAG_FORCE_FALLBACK);
   if (have) {
     CandArgs ca;
@@ -336,7 +361,7 @@ dsa_status dsa_decode_step_timed(const int8_t* iq, const int8_t* iw, const int8_
     for (int i = 0; i < 3; ++i) tm[i] = KTimer{kernel_events[2 * i], kernel_events[2 * i + 1]};
   }
   uint8_t* w = static_cast<uint8_t*>(ws);
-  const ChunkPlan cp = chunk_plan(nmax, k);
+  const ChunkPlan cp = chunk_plan(nmax, k, B == 1);
   const bool have = cand_fits(Hi, Di, B, cp, true) && !(flags & DSA_FLAG_FORCE_FALLBACK);
   st = run_scores(iq, iw, ik, lens, B, Hi, Di, N, nmax, scores, have, cp,
                   reinterpret_cast<uint64_t*>(w + L.cand), reinterpret_cast<uint64_t*>(w + L.xc),

@@ -169,6 +169,37 @@ __device__ __forceinline__ bool threshold_floor(const uint32_t* hist, int count,
   return true;
 }
 
+// Lowest score of the bin that holds the want-th best of `count` keys, from their
+// histogram over score_bin, by one wave in two levels: lane l sums bins
+// 1008-16l .. 1023-16l (best first) and a wave scan finds the lane whose group of
+// 16 bins holds it; then 16 lanes re-read that group's bins and a row scan finds
+// the bin. Returns false when the histogram does not count `count` keys.
+__device__ __forceinline__ bool hist_threshold(const uint32_t* hist, int count, uint32_t want, int32_t* tlo) {
+  const int l = lane_id();
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4* g = reinterpret_cast<const u32x4*>(hist + kHistBins - 16 - 16 * l);
+  const u32x4 a0 = g[0], a1 = g[1], a2 = g[2], a3 = g[3];
+  const u32x4 t = a0 + a1 + a2 + a3;
+  const uint32_t sum = t.x + t.y + t.z + t.w;
+  const uint32_t incl = wave_incl_scan_u32(sum);
+  if ((uint32_t)__builtin_amdgcn_readlane((int)incl, 63) != (uint32_t)count) return false;
+  const uint32_t excl = incl - sum;  // keys in better groups than this lane's
+  const uint64_t hit = __ballot(excl < want && want <= incl);  // exactly one lane
+  const int L = (int)__builtin_ctzll(hit);
+  const uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)excl, L);
+  // lane j < 16 (and its copies in the other rows) takes bin 1023 - 16L - j
+  const int bj = kHistBins - 1 - 16 * L - (l & 15);
+  uint32_t c = hist[bj];
+  c += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)c, dpp::kRowShr1, 0xF, 0xF, false);
+  c += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)c, dpp::kRowShr2, 0xF, 0xF, false);
+  c += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)c, dpp::kRowShr4, 0xF, 0xF, false);
+  c += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)c, dpp::kRowShr8, 0xF, 0xF, false);
+  const uint64_t hit2 = __ballot(base + c >= want) & 0xFFFFull;  // first row
+  const int jstar = (int)__builtin_ctzll(hit2);
+  *tlo = bin_floor((uint32_t)(kHistBins - 1 - 16 * L - jstar));
+  return true;
+}
+
 // The same result as chunk_candidates, computed by one wave without block
 // barriers, from a histogram of the chunk's scores over score_bin that the caller
 // filled while producing them (hist counts the `count` valid positions):
@@ -301,6 +332,7 @@ __device__ __forceinline__ bool block_chunk_candidates(const int32_t* scores, in
       sm.tlo = t;
       sm.ok = ok ? 1u : 0u;
     }
+    DSA_MARK(3, 2);
   }
   lds_barrier();
   if (!sm.ok) return false;  // uniform
@@ -332,8 +364,10 @@ __device__ __forceinline__ bool block_chunk_candidates(const int32_t* scores, in
       }
     }
     if (l == 0) sm.wcount[w] = ns;
+    DSA_MARK(3, 3);
   }
   lds_barrier();
+  DSA_MARK(3, 4);
   uint32_t total = 0, off = 0;
 #pragma unroll
   for (int q = 0; q < W; ++q) {
@@ -344,6 +378,7 @@ __device__ __forceinline__ bool block_chunk_candidates(const int32_t* scores, in
   if (total > cap) return false;  // uniform
   if (active)
     for (int j = l; j < (int)ns; j += 64) sm.all[off + j] = sm.wstage[w][j];
+  DSA_MARK(3, 5);
   lds_barrier();
   DSA_MARK(3, 8);
 

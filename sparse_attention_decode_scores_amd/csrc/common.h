@@ -52,7 +52,9 @@ __device__ __forceinline__ int lane_id() { return __lane_id(); }
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
-__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+// The wave's index in the workgroup, as a scalar (uniform) value, so loops and
+// branches on it stay uniform control flow.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 __device__ __forceinline__ uint64_t lanemask_lt() { return (1ull << lane_id()) - 1ull; }
 
 // Phase timestamps for performance analysis builds (-DDSA_TRACE): thread 0 of a
@@ -71,11 +73,22 @@ __device__ __forceinline__ uint64_t* dsa_trace_lds() {
     if (threadIdx.x == 0)                                                                    \
       for (int i_ = 0; i_ < kTraceKernels * kTracePhases; ++i_) dsa_trace_lds()[i_] = 0;     \
   } while (0)
+#ifdef DSA_TRACE_CLOCK
+// also the shader clock counter of kernel-0 marks, in the kernel-2 table
+#define DSA_MARK(kernel, phase)                                                              \
+  do {                                                                                       \
+    if (threadIdx.x == 0) {                                                                  \
+      dsa_trace_lds()[(kernel) * kTracePhases + (phase)] = __builtin_amdgcn_s_memrealtime(); \
+      if ((kernel) == 0) dsa_trace_lds()[2 * kTracePhases + (phase)] = __builtin_amdgcn_s_memtime(); \
+    }                                                                                        \
+  } while (0)
+#else
 #define DSA_MARK(kernel, phase)                                                              \
   do {                                                                                       \
     if (threadIdx.x == 0)                                                                    \
       dsa_trace_lds()[(kernel) * kTracePhases + (phase)] = __builtin_amdgcn_s_memrealtime(); \
   } while (0)
+#endif
 #define DSA_TRACE_FLUSH()                                                                    \
   do {                                                                                       \
     const int blk_ = blockIdx.x + gridDim.x * blockIdx.y;                                    \

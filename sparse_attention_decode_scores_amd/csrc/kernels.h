@@ -40,7 +40,7 @@ struct ScoreArgs {
   int nmax;        // largest ctx_len: positions at or past it are never scored
   int b0, Bg;      // this launch scores rows b0 .. b0+Bg-1
   int Hi, Di;
-  int P;           // positions per chunk (multiple of 64)
+  int P;           // positions per chunk (multiple of 64; of 32 for the one-row kernel)
   int G;           // chunks per row
   int m;           // candidates kept per chunk
 };
@@ -51,6 +51,14 @@ constexpr int kScoreQBytes = 65536;
 
 hipError_t launch_score(const ScoreArgs& a, int MT, int KT, bool cand, int grid, hipStream_t s,
                         KTimer t = {});
+// One query row with candidates (the decode hot path): chunks of P = 32u positions,
+// D units of 32 keys in flight per wave (2 or 3; two measured faster: three keep
+// more requests queued without raising the key stream's rate).
+hipError_t launch_score_row(const ScoreArgs& a, int MT, int KT, int D, int grid, hipStream_t s,
+                            KTimer t = {});
+constexpr int kScoreRowDepth = 2;
+size_t score_row_lds_bytes(int P);
+int score_row_max_chunk();
 int score_max_chunk();        // longest chunk the score kernel's candidate pass takes
 int chunk_cand_max_chunk();   // the same for the stand-alone candidate kernel
 size_t score_lds_bytes(int MT, int KT, int Bg, int P, bool cand);

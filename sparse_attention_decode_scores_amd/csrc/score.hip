@@ -99,6 +99,7 @@ __global__ __launch_bounds__(kScoreBlock) void k_score(ScoreArgs a) {
   load_keys<KT>(kb0, rs, wave);
   load_keys<KT>(kb1, rs, wave + kScoreWaves);
   load_keys<KT>(kb2, rs, wave + 2 * kScoreWaves);
+  DSA_MARK(0, 9);
 
   if (CAND) {
     radix_clear<kScoreBlock>(csm.radix);
@@ -111,7 +112,9 @@ __global__ __launch_bounds__(kScoreBlock) void k_score(ScoreArgs a) {
     if (i < nq) *(v4i*)(qs + 16 * i) = h < a.Hi ? qv[j] : v4i{0, 0, 0, 0};
   }
   if (tid < a.Bg * HP) wsm[tid] = tid % HP < a.Hi ? wv : (int8_t)0;
+  DSA_MARK(0, 10);
   lds_barrier();
+  DSA_MARK(0, 11);
 
   // A fragments and weights of a single row stay in registers for the whole chunk.
   v4i qreg[ONE ? MT : 1][ONE ? KT : 1];
@@ -206,6 +209,7 @@ __global__ __launch_bounds__(kScoreBlock) void k_score(ScoreArgs a) {
     // the chunk's end (buffer reads that return zeros) are drained before them,
     // so no later wait for those registers covers the stores.
     __builtin_amdgcn_s_waitcnt(0x0F70);  // gfx9 encoding: vmcnt(0), expcnt and lgkmcnt untouched
+    DSA_MARK(0, 6);
     for (int bb = 0; bb < a.Bg; ++bb) {
       const int b = a.b0 + bb;
       const int64_t n64 = (int64_t)a.lens.n[b] - cbeg;
@@ -213,6 +217,7 @@ __global__ __launch_bounds__(kScoreBlock) void k_score(ScoreArgs a) {
       int32_t* dst = a.scores + (int64_t)b * a.N + cbeg;
       for (int i = tid; i < count; i += kScoreBlock) dst[i] = sc[bb * a.P + i];
     }
+    DSA_MARK(0, 7);
     if (ONE) {
       // one row: the whole block selects the chunk's candidates
       const int b = a.b0;
@@ -249,6 +254,271 @@ __global__ __launch_bounds__(kScoreBlock) void k_score(ScoreArgs a) {
     DSA_MARK(0, 4);
   }
   DSA_TRACE_FLUSH();
+}
+
+// ------------------------------------------------------------------ one query row
+//
+// The decode hot path (one query row per launch, candidates on). Every wave is
+// independent until the chunk's scores are complete: it loads its own query
+// fragments straight into registers and keeps D units of 32 keys in flight, so
+// no wave waits on another while the key cache streams in (a block barrier after
+// the loads are issued would hold every wave until the slowest one has had its
+// whole share of the chunk accepted by the memory pipeline).
+
+constexpr int kUnit = 32;                                    // keys per matrix-core tile
+constexpr int kMaxUnits = kChunkPerThread * kScoreBlock / kUnit;
+constexpr int kRowStage = 144;  // >= cap (m + 64 <= 128) + 16 read slack
+
+struct RowCandSmem {
+  uint64_t all[kRowStage];  // staged keys, in order of arrival
+  uint32_t nstaged;
+};
+
+namespace {
+
+// B fragments of unit j (keys 32j .. 32j + 31 of the chunk): lane l holds dims
+// 32kt + 16(l >> 5) .. +15 of key 32j + (l & 31). Raw buffer loads against a
+// resource that covers exactly the chunk's valid keys (zeros past the end).
+template <int KT>
+__device__ __forceinline__ void load_unit(v4i (&kf)[KT], __amdgpu_buffer_rsrc_t rs, int j) {
+  const int lane = lane_id();
+  const int off = (kUnit * j + (lane & 31)) * (32 * KT) + 16 * (lane >> 5);
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt)
+    kf[kt] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 32 * kt, 0, 0));
+}
+
+}  // namespace
+
+template <int MT, int KT, int D>
+__global__ __launch_bounds__(kScoreBlock) void k_score_row(ScoreArgs a) {
+  static_assert(D == 2 || D == 3, "units in flight per wave");
+  constexpr int DI = 32 * KT;
+  extern __shared__ __align__(16) uint8_t smem[];
+  using Smem = ChunkSmem<kScoreBlock>;
+  Smem& csm = *reinterpret_cast<Smem*>(smem);
+  int32_t* sc = reinterpret_cast<int32_t*>(smem + align16(sizeof(Smem)));                     // [P]
+  uint32_t* hist = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(sc) + align16((size_t)a.P * 4));
+  RowCandSmem& rsm = *reinterpret_cast<RowCandSmem*>(hist + kHistBins);
+
+  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+  const int c = blockIdx.x, b = a.b0;
+  DSA_TRACE_BEGIN();
+  DSA_MARK(0, 0);
+  const int64_t cbeg = (int64_t)c * a.P;
+  const int64_t n64 = (int64_t)a.lens.n[b] - cbeg;
+  const int count = n64 > a.P ? a.P : (int)(n64 > 0 ? n64 : 0);  // valid positions of the chunk
+  const int units = (count + kUnit - 1) / kUnit;
+  const int nu = units > wave ? (units - wave + kScoreWaves - 1) / kScoreWaves : 0;  // this wave's units
+
+  // A operand: lane l holds head 32mt + (l & 31), dims 32kt + 16(l >> 5) .. +15; lane
+  // l also holds the weight of head l (Hi <= 64). Requested before any key.
+  const int8_t* qrow = a.iq + (int64_t)b * a.Hi * DI;
+  v4i qreg[MT][KT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int h = 32 * mt + (lane & 31) < a.Hi ? 32 * mt + (lane & 31) : a.Hi - 1;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) qreg[mt][kt] = *(const v4i*)(qrow + h * DI + 32 * kt + 16 * (lane >> 5));
+  }
+  const int wl = (int)a.iw[(int64_t)b * a.Hi + (lane < a.Hi ? lane : a.Hi - 1)];
+
+  // the histogram is shared by the waves: cleared before any of them adds to it
+  for (int i = tid; i < kHistBins; i += kScoreBlock) hist[i] = 0;
+  if (tid == 0) rsm.nstaged = 0;
+  lds_barrier();
+
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(a.ik + cbeg * DI), (short)0, count * DI, 0x00020000);
+  v4i kb0[KT], kb1[KT], kb2[KT];
+  load_unit<KT>(kb0, rs, wave);
+  load_unit<KT>(kb1, rs, wave + kScoreWaves);
+  if constexpr (D == 3) load_unit<KT>(kb2, rs, wave + 2 * kScoreWaves);
+
+  // weights in accumulator order: value r of tile mt at lane l is head
+  // 32mt + 8(r / 4) + 4(l >> 5) + r % 4; padding heads (q = 0) get weight 0
+  int wreg[MT][16];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int h = 32 * mt + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      const int w = __shfl(wl, h & 63);
+      wreg[mt][r] = h < a.Hi ? w : 0;
+    }
+    if (32 * mt + (lane & 31) >= a.Hi)
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) qreg[mt][kt] = v4i{0, 0, 0, 0};
+  }
+
+  // unit i of this wave (chunk keys 32j .. 32j + 31, j = wave + 8i): scores into LDS
+  // and the histogram; its key registers are then refilled with unit i + D.
+  auto unit = [&](v4i(&kf)[KT], int i) {
+    const int j = wave + kScoreWaves * i;
+    v16i acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = v16i{};
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        acc[mt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(qreg[mt][kt], kf[kt], acc[mt], 0, 0, 0);
+    load_unit<KT>(kf, rs, j + kScoreWaves * D);
+    int part = 0;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int v = acc[mt][r];
+        part += __mul24(wreg[mt][r], v > 0 ? v : 0);
+      }
+    part += __shfl_xor(part, 32);
+    const int p = kUnit * j + (lane & 31);
+    if (lane < 32) {
+      sc[p] = part;
+      if (p < count) atomicAdd(&hist[score_bin(part)], 1u);
+    }
+  };
+
+  DSA_MARK(0, 1);
+  // whole rounds of D units (the buffers rotate by name: a register copy would
+  // wait for its load), then the last nu % D units; every iteration issues the same
+  // loads in the same order, which keeps the compiler's wait counts exact
+  int i = 0;
+  for (; i + D <= nu; i += D) {
+    unit(kb0, i);
+    unit(kb1, i + 1);
+    if constexpr (D == 3) unit(kb2, i + 2);
+  }
+  if (i < nu) {
+    unit(kb0, i);
+    if constexpr (D == 3)
+      if (i + 1 < nu) unit(kb1, i + 1);
+  }
+  DSA_MARK(0, 2);
+  lds_barrier();  // every score and histogram count of the chunk is in LDS
+  DSA_MARK(0, 3);
+
+  const int m = a.m;
+  uint64_t* out = a.cand + ((int64_t)b * a.G + c) * m;
+  uint64_t* xout = a.xc + (int64_t)b * a.G + c;
+  // the scores leave for HBM as they are read below (raw buffer stores against a
+  // resource that covers exactly the chunk's valid positions: the padding is
+  // dropped without a branch); nothing waits for these stores
+  const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
+      a.scores + (int64_t)b * a.N + cbeg, (short)0, count * 4, 0x00020000);
+  const uint64_t lt = lanemask_lt();
+  if (count <= m) {  // every valid position is a candidate
+    for (int i = tid; i < m; i += kScoreBlock) {
+      const int32_t v = sc[i < units * kUnit ? i : 0];
+      if (i < units * kUnit) __builtin_amdgcn_raw_buffer_store_b32(v, rsc, 4 * i, 0, 0);
+      out[i] = i < count ? make_key(v, (uint32_t)(cbeg + i)) : 0ull;
+    }
+    if (tid == 0) *xout = 0;
+    DSA_TRACE_FLUSH();
+    return;
+  }
+
+  // 1. every wave finds the bin that holds the (m+1)-th best key (same result in each)
+  int32_t tlo = 0;
+  const bool hok = hist_threshold(hist, count, (uint32_t)m + 1, &tlo);
+  DSA_MARK(0, 6);
+  // 2. every key scoring at least that bin's floor is staged, in order of arrival
+  //    (the ranks below fix the output order): four positions per thread per pass
+  for (int i0 = 0; i0 < units * kUnit; i0 += 4 * kScoreBlock) {
+    int32_t v[4];
+    uint64_t bal[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {  // every read before any use
+      const int i = i0 + tid + kScoreBlock * q;
+      v[q] = sc[i < units * kUnit ? i : 0];
+    }
+    uint32_t nb = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = i0 + tid + kScoreBlock * q;
+      __builtin_amdgcn_raw_buffer_store_b32(v[q], rsc, 4 * i, 0, 0);
+      bal[q] = __ballot(i < count && v[q] >= tlo);
+      nb += (uint32_t)__popcll(bal[q]);
+    }
+    if (nb == 0) continue;
+    uint32_t slot = 0;
+    if (lane == 0) slot = atomicAdd(&rsm.nstaged, nb);
+    slot = (uint32_t)__builtin_amdgcn_readfirstlane((int)slot);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = i0 + tid + kScoreBlock * q;
+      const uint32_t at = slot + (uint32_t)__popcll(bal[q] & lt);
+      if (((bal[q] >> lane) & 1ull) && at < (uint32_t)kRowStage) rsm.all[at] = make_key(v[q], (uint32_t)(cbeg + i));
+      slot += (uint32_t)__popcll(bal[q]);
+    }
+  }
+  lds_barrier();
+  DSA_MARK(0, 7);
+  const uint32_t total = rsm.nstaged;
+  const bool fast = hok && total <= (uint32_t)m + 64;  // uniform over the block
+  if (fast) {
+    // 3. rank of staged key t = number of staged keys above it (four threads per
+    //    key). Staged keys are distinct and include the m + 1 best, so ranks 0 .. m
+    //    are the chunk's m + 1 best keys in order: rank r < m goes to slot r of
+    //    the output (best first; keys of equal score stay in position order), and
+    //    rank m is x, the best key left out.
+    const int t = tid >> 2, part = tid & 3;
+    uint32_t r = 0;
+    uint64_t me = 0;
+    if (t < (int)total) {
+      me = rsm.all[t];
+      for (int s0 = 0; s0 < (int)total; s0 += 16) {
+        uint64_t v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = rsm.all[s0 + part + 4 * u];  // < kRowStage
+#pragma unroll
+        for (int u = 0; u < 4; ++u) r += (s0 + part + 4 * u < (int)total && v[u] > me) ? 1u : 0u;
+      }
+    }
+    r += (uint32_t)__builtin_amdgcn_mov_dpp((int)r, dpp::kQuadXor1, 0xF, 0xF, false);
+    r += (uint32_t)__builtin_amdgcn_mov_dpp((int)r, dpp::kQuadXor2, 0xF, 0xF, false);
+    if (part == 0 && t < (int)total) {
+      if (r < (uint32_t)m) out[r] = me;
+      else if (r == (uint32_t)m) *xout = me;
+    }
+  } else {
+    // heavy ties at the threshold: exact radix selection over the chunk's scores
+    radix_clear<kScoreBlock>(csm.radix);
+    lds_barrier();
+    chunk_candidates<kScoreBlock>(sc, count, (uint32_t)cbeg, m, out, xout, csm);
+  }
+  DSA_MARK(0, 4);
+  DSA_TRACE_FLUSH();
+}
+
+size_t score_row_lds_bytes(int P) {
+  return align16(sizeof(ChunkSmem<kScoreBlock>)) + align16((size_t)P * 4) + (size_t)kHistBins * 4 +
+         sizeof(RowCandSmem) + 16;
+}
+
+int score_row_max_chunk() { return kMaxUnits * kUnit; }
+
+template <int MT, int KT>
+static hipError_t launch_score_row_t(const ScoreArgs& a, int D, int grid, hipStream_t s, KTimer t) {
+  auto fn = D == 3 ? k_score_row<MT, KT, 3> : k_score_row<MT, KT, 2>;
+  const size_t lds = score_row_lds_bytes(a.P);
+  hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)lds);
+  if (e != hipSuccess) return e;
+  return launch_timed(fn, dim3(grid), dim3(kScoreBlock), lds, s, t, a);
+}
+
+hipError_t launch_score_row(const ScoreArgs& a, int MT, int KT, int D, int grid, hipStream_t s,
+                            KTimer t) {
+#define DSA_SCORE_ROW_CASE(M, K) \
+  if (MT == M && KT == K) return launch_score_row_t<M, K>(a, D, grid, s, t);
+  DSA_SCORE_ROW_CASE(1, 1) DSA_SCORE_ROW_CASE(1, 2) DSA_SCORE_ROW_CASE(1, 3) DSA_SCORE_ROW_CASE(1, 4)
+  DSA_SCORE_ROW_CASE(1, 5) DSA_SCORE_ROW_CASE(1, 6) DSA_SCORE_ROW_CASE(1, 7) DSA_SCORE_ROW_CASE(1, 8)
+  DSA_SCORE_ROW_CASE(2, 1) DSA_SCORE_ROW_CASE(2, 2) DSA_SCORE_ROW_CASE(2, 3) DSA_SCORE_ROW_CASE(2, 4)
+  DSA_SCORE_ROW_CASE(2, 5) DSA_SCORE_ROW_CASE(2, 6) DSA_SCORE_ROW_CASE(2, 7) DSA_SCORE_ROW_CASE(2, 8)
+#undef DSA_SCORE_ROW_CASE
+  return hipErrorInvalidValue;
 }
 
 int score_max_chunk() { return kChunkPerThread * kScoreBlock; }
