@@ -242,6 +242,16 @@ SelArgs sel_args(const int32_t* scores, const RowLens& lens, int64_t N, int k, i
   a.G = cp.G;
   a.m = cp.m;
   a.have_cand = have_cand ? 1 : 0;
+  memset(&a.cand_valid, 0, sizeof(a.cand_valid));
+  for (int b = 0; b < kMaxBatch; ++b) {  // each chunk keeps min(m, its valid positions)
+    int64_t v = 0;
+    for (int c = 0; c < cp.G && have_cand; ++c) {
+      int64_t cnt = (int64_t)lens.n[b] - (int64_t)c * cp.P;
+      cnt = cnt < 0 ? 0 : (cnt > cp.P ? cp.P : cnt);
+      v += cnt < cp.m ? cnt : cp.m;
+    }
+    a.cand_valid.n[b] = (int32_t)v;
+  }
   a.force = (flags & DSA_FLAG_FORCE_FALLBACK) ? 1 : 0;
   a.R = rankers_for(k);
   return a;

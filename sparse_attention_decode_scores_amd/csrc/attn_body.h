@@ -68,9 +68,30 @@ struct AttnMfma {
   static constexpr int kQPer = 4;  // 16 heads x at most 1,024 values, 16 bytes per slot
   struct QFrag {
     v4i v[kQInLds ? kQPer : 1];
+    int rr[kMaxLoads], cc[kMaxLoads];  // gather slot j of this thread: row, 16-byte column
   };
   __device__ static QFrag load_q(const AttnArgs& p, int b) {
     QFrag f;
+    {
+      // gather slot j of this thread is chunk i = tid + 512 j of a sub-block: row
+      // i / cpr, 16-byte column i % cpr, stepped without dividing (a divide by a
+      // runtime value costs dozens of instructions); worked out here, before the
+      // positions are known
+      const int cpr = p.Dk >> 3;
+      const int step_r = kAttnBlock / cpr, step_c = kAttnBlock - step_r * cpr;
+      int r = (int)threadIdx.x / cpr, c = (int)threadIdx.x - r * cpr;
+#pragma unroll
+      for (int j = 0; j < kMaxLoads; ++j) {
+        f.rr[j] = r;
+        f.cc[j] = c;
+        c += step_c;
+        r += step_r;
+        if (c >= cpr) {
+          c -= cpr;
+          ++r;
+        }
+      }
+    }
     if (!kQInLds) return f;
     const int Dk = p.Dk, cpr = Dk >> 3;
     const uint8_t* q = reinterpret_cast<const uint8_t*>(p.q) + (int64_t)b * p.Hq * Dk * 2;
@@ -107,9 +128,11 @@ struct AttnMfma {
     }
   }
 
+  // qf: the query fragments from load_q; they are written to LDS once the first
+  // sub-block's row loads are in flight.
   template <typename PosAt>
   __device__ static void run(const AttnArgs& p, int b, int split, PosAt pos_at, int cnt,
-                             uint8_t* work) {
+                             uint8_t* work, const QFrag& qf) {
     const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
     const int Dk = p.Dk, Dv = p.Dv, KS = Dk >> 5, rb = row_bytes(Dk);
     const int nt_all = Dv >> 4;  // 16-wide output tiles
@@ -132,26 +155,8 @@ struct AttnMfma {
       lrun[h] = 0.f;
     }
 
-    // gather slot j of this thread is chunk i = tid + 512 j of a sub-block: row
-    // i / cpr, 16-byte column i % cpr, stepped without dividing (a divide by a
-    // runtime value costs dozens of instructions)
-    int rr[kMaxLoads], cc[kMaxLoads];
-    {
-      const int cpr = Dk >> 3;
-      const int step_r = kAttnBlock / cpr, step_c = kAttnBlock - step_r * cpr;
-      int r = tid / cpr, c = tid - r * cpr;
-#pragma unroll
-      for (int j = 0; j < kMaxLoads; ++j) {
-        rr[j] = r;
-        cc[j] = c;
-        c += step_c;
-        r += step_r;
-        if (c >= cpr) {
-          c -= cpr;
-          ++r;
-        }
-      }
-    }
+    const int* rr = qf.rr;
+    const int* cc = qf.cc;
 
     for (int s0 = 0; s0 < cnt; s0 += SB) {
       const int nr = cnt - s0 < SB ? cnt - s0 : SB;
@@ -169,6 +174,7 @@ struct AttnMfma {
       v4i buf[kMaxLoads];
 #pragma unroll
       for (int j = 0; j < kMaxLoads; ++j) buf[j] = *(const v4i*)(kv + ((int64_t)rp[j] * Dk + 8 * cc[j]) * 2);
+      if (s0 == 0) store_q(qf, p, work);  // published by the barrier below
       DSA_MARK(1, 13);
 #pragma unroll
       for (int j = 0; j < kMaxLoads; ++j) {
@@ -325,7 +331,7 @@ struct AttnGeneric {
 
   template <typename PosAt>
   __device__ static void run(const AttnArgs& p, int b, int split, PosAt pos_at, int cnt,
-                             uint8_t* work) {
+                             uint8_t* work, const QFrag&) {
     const int tid = threadIdx.x;
     const int Hq = p.Hq, Dk = p.Dk, Dv = p.Dv;
     float* rows = reinterpret_cast<float*>(work);
@@ -389,7 +395,7 @@ struct AttnNone {
   __device__ static QFrag load_q(const AttnArgs&, int) { return QFrag{}; }
   __device__ static void store_q(const QFrag&, const AttnArgs&, uint8_t*) {}
   template <typename PosAt>
-  __device__ static void run(const AttnArgs&, int, int, PosAt, int, uint8_t*) {}
+  __device__ static void run(const AttnArgs&, int, int, PosAt, int, uint8_t*, const QFrag&) {}
 };
 
 }  // namespace dsa

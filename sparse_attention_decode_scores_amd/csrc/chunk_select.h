@@ -49,8 +49,8 @@ __device__ __forceinline__ int32_t bin_floor(uint32_t b) {
 constexpr int kWaveStage = 136;  // staging slots per wave for wave_chunk_candidates (m <= 64, + 8 read slack)
 
 // scores: LDS copy of the chunk's scores (entry i is position pos0 + i); count:
-// valid entries (<= 0 means none; at most 16 * BLOCK). Writes out[0..m) (the m
-// best keys, in position order, 0-padded) and *x_out = the best key not kept
+// valid entries (<= 0 means none; at most 16 * BLOCK). Writes entries 0..m-1 of
+// `out` (the m best keys, in position order, 0-padded) and *x_out = the best key not kept
 // (0 if every valid position is kept).
 //
 // The (m+1)-th best score T comes from a radix selection over the scores; the
@@ -58,12 +58,12 @@ constexpr int kWaveStage = 136;  // staging slots per wave for wave_chunk_candid
 // scoring exactly T, which is the key order (score, then lower position).
 template <int BLOCK>
 __device__ __forceinline__ void chunk_candidates(const int32_t* scores, int count, uint32_t pos0, int m,
-                                 uint64_t* __restrict__ out, uint64_t* __restrict__ x_out,
+                                 CandOut out, uint64_t* __restrict__ x_out,
                                  ChunkSmem<BLOCK>& sm) {
   const int tid = threadIdx.x;
   if (count <= m) {
     for (int i = tid; i < m; i += BLOCK)
-      out[i] = i < count ? make_key(scores[i], pos0 + (uint32_t)i) : 0ull;
+      out.put(i, i < count ? make_key(scores[i], pos0 + (uint32_t)i) : 0ull);
     if (tid == 0) *x_out = 0;
     return;
   }
@@ -123,9 +123,9 @@ __device__ __forceinline__ void chunk_candidates(const int32_t* scores, int coun
     if (j < per && i < count) {
       const uint64_t key = ((uint64_t)u[j] << 32) | (uint64_t)(0xFFFFFFFFu - (pos0 + (uint32_t)i));
       if (u[j] > T) {
-        out[slot++] = key;
+        out.put(slot++, key);
       } else if (u[j] == T) {
-        if (eqr < need_eq - 1) out[slot++] = key;
+        if (eqr < need_eq - 1) out.put(slot++, key);
         else if (eqr == need_eq - 1) *x_out = key;  // exactly one thread holds it
         ++eqr;
       }
@@ -214,12 +214,12 @@ __device__ __forceinline__ bool hist_threshold(const uint32_t* hist, int count, 
 // chunk_candidates. `stage` is this wave's LDS area of kWaveStage keys.
 __device__ __forceinline__ bool wave_chunk_candidates(const int32_t* scores, int count, uint32_t pos0,
                                                       int m, const uint32_t* hist,
-                                                      uint64_t* __restrict__ out,
+                                                      CandOut out,
                                                       uint64_t* __restrict__ x_out, uint64_t* stage) {
   const int l = lane_id();
   DSA_MARK(3, 0);
   if (count <= m) {
-    for (int i = l; i < m; i += 64) out[i] = i < count ? make_key(scores[i], pos0 + (uint32_t)i) : 0ull;
+    for (int i = l; i < m; i += 64) out.put(i, i < count ? make_key(scores[i], pos0 + (uint32_t)i) : 0ull);
     if (l == 0) *x_out = 0;
     return true;
   }
@@ -274,8 +274,8 @@ __device__ __forceinline__ bool wave_chunk_candidates(const int32_t* scores, int
   const bool s0 = l < (int)ns && r0 < (uint32_t)m;
   const bool s1 = l + 64 < (int)ns && r1 < (uint32_t)m;
   const uint64_t b0 = __ballot(s0), b1 = __ballot(s1);
-  if (s0) out[__popcll(b0 & lt)] = k0;
-  if (s1) out[__popcll(b0) + __popcll(b1 & lt)] = k1;
+  if (s0) out.put((int)__popcll(b0 & lt), k0);
+  if (s1) out.put((int)(__popcll(b0) + __popcll(b1 & lt)), k1);
   const uint64_t xb0 = __ballot(l < (int)ns && r0 == (uint32_t)m);
   const uint64_t xb1 = __ballot(l + 64 < (int)ns && r1 == (uint32_t)m);
   const int xl = xb0 ? __builtin_ctzll(xb0) : __builtin_ctzll(xb1);
@@ -311,7 +311,7 @@ struct BlockCandSmem {
 template <int BLOCK>
 __device__ __forceinline__ bool block_chunk_candidates(const int32_t* scores, int count, uint32_t pos0,
                                                        int m, const uint32_t* hist,
-                                                       uint64_t* __restrict__ out,
+                                                       CandOut out,
                                                        uint64_t* __restrict__ x_out,
                                                        BlockCandSmem<BLOCK>& sm) {
   constexpr int W = 4;            // active waves
@@ -320,7 +320,7 @@ __device__ __forceinline__ bool block_chunk_candidates(const int32_t* scores, in
   const int tid = threadIdx.x, l = lane_id(), w = wave_id();
   const bool active = w < W;
   if (count <= m) {
-    for (int i = tid; i < m; i += BLOCK) out[i] = i < count ? make_key(scores[i], pos0 + (uint32_t)i) : 0ull;
+    for (int i = tid; i < m; i += BLOCK) out.put(i, i < count ? make_key(scores[i], pos0 + (uint32_t)i) : 0ull);
     if (tid == 0) *x_out = 0;
     return true;
   }
@@ -403,7 +403,7 @@ __device__ __forceinline__ bool block_chunk_candidates(const int32_t* scores, in
       const uint32_t rk = j < (int)total ? sm.rank[j] : ~0u;
       const bool sel = rk < (uint32_t)m;
       const uint64_t b = __ballot(sel);
-      if (sel) out[base + (uint32_t)__popcll(b & lt)] = sm.all[j];
+      if (sel) out.put((int)(base + (uint32_t)__popcll(b & lt)), sm.all[j]);
       if (rk == (uint32_t)m) *x_out = sm.all[j];
       base += (uint32_t)__popcll(b);
     }

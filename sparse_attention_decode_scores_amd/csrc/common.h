@@ -17,6 +17,22 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
+// Storage slot of entry u of a row's candidate union (kCandCap entries per row).
+// The selection kernel's thread t (of 512) holds entries 16t .. 16t + 15 and reads
+// them as eight 16-byte pieces; piece j of every thread lies in one contiguous run,
+// so each of those loads is fully coalesced: entry 16t + 2j + e sits at slot
+// 1024j + 2t + e.
+__host__ __device__ __forceinline__ int cand_slot(int u) {
+  return ((u >> 1) & 7) * 1024 + (u >> 4) * 2 + (u & 1);
+}
+
+// One chunk's candidate list: entries u0 .. u0 + m - 1 of its row's union.
+struct CandOut {
+  uint64_t* row;  // the row's kCandCap slots
+  int u0;
+  __device__ __forceinline__ void put(int i, uint64_t key) const { row[cand_slot(u0 + i)] = key; }
+};
+
 // Per-row lengths passed by value (kernel arguments are captured by HIP graphs).
 struct RowLens {
   int32_t n[kMaxBatch];

@@ -33,7 +33,7 @@ struct ScoreArgs {
   const int8_t* iw;
   const int8_t* ik;
   int32_t* scores;
-  uint64_t* cand;  // [B][G][m] best keys per chunk (candidate pass only)
+  uint64_t* cand;  // [B][kCandCap] candidate union per row (entry c*m + i at cand_slot)
   uint64_t* xc;    // [B][G] best key left out of each chunk
   RowLens lens;
   int64_t N;       // row stride of scores
@@ -102,6 +102,7 @@ struct SelArgs {
   int k;
   int G, m;            // candidate layout
   int have_cand;       // 0: the candidate pass did not run (chunks too long)
+  RowLens cand_valid;  // per row: union entries that hold a candidate (the rest are 0)
   int force;           // DSA_FLAG_FORCE_FALLBACK
   int R;               // ranking workgroups per row
 };

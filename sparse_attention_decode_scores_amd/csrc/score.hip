@@ -224,7 +224,7 @@ __global__ __launch_bounds__(kScoreBlock) void k_score(ScoreArgs a) {
       const int64_t n64 = (int64_t)a.lens.n[b] - cbeg;
       const int count = n64 > clen ? clen : (int)(n64 > 0 ? n64 : 0);
       const bool ok = block_chunk_candidates<kScoreBlock>(sc, count, (uint32_t)cbeg, a.m, hist,
-                                                          a.cand + ((int64_t)b * a.G + c) * a.m,
+                                                          CandOut{a.cand + (int64_t)b * kCandCap, c * a.m},
                                                           a.xc + (int64_t)b * a.G + c, bsm);
       if (tid == 0) fallback[0] = ok ? 0 : 1;
     } else {
@@ -234,7 +234,7 @@ __global__ __launch_bounds__(kScoreBlock) void k_score(ScoreArgs a) {
         const int64_t n64 = (int64_t)a.lens.n[b] - cbeg;
         const int count = n64 > clen ? clen : (int)(n64 > 0 ? n64 : 0);
         const bool ok = wave_chunk_candidates(sc + bb * a.P, count, (uint32_t)cbeg, a.m, hist + bb * kHistBins,
-                                              a.cand + ((int64_t)b * a.G + c) * a.m,
+                                              CandOut{a.cand + (int64_t)b * kCandCap, c * a.m},
                                               a.xc + (int64_t)b * a.G + c, bsm.wstage[wave]);
         if (lane == 0) fallback[bb] = ok ? 0 : 1;
       }
@@ -247,7 +247,7 @@ __global__ __launch_bounds__(kScoreBlock) void k_score(ScoreArgs a) {
       const int64_t n64 = (int64_t)a.lens.n[b] - cbeg;
       const int count = n64 > clen ? clen : (int)(n64 > 0 ? n64 : 0);
       chunk_candidates<kScoreBlock>(sc + bb * a.P, count, (uint32_t)cbeg, a.m,
-                                    a.cand + ((int64_t)b * a.G + c) * a.m, a.xc + (int64_t)b * a.G + c,
+                                    CandOut{a.cand + (int64_t)b * kCandCap, c * a.m}, a.xc + (int64_t)b * a.G + c,
                                     csm);
       lds_barrier();
     }
@@ -400,7 +400,7 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(ScoreArgs a) {
   DSA_MARK(0, 3);
 
   const int m = a.m;
-  uint64_t* out = a.cand + ((int64_t)b * a.G + c) * m;
+  const CandOut out{a.cand + (int64_t)b * kCandCap, c * m};
   uint64_t* xout = a.xc + (int64_t)b * a.G + c;
   // the scores leave for HBM as they are read below (raw buffer stores against a
   // resource that covers exactly the chunk's valid positions: the padding is
@@ -412,7 +412,7 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(ScoreArgs a) {
     for (int i = tid; i < m; i += kScoreBlock) {
       const int32_t v = sc[i < units * kUnit ? i : 0];
       if (i < units * kUnit) __builtin_amdgcn_raw_buffer_store_b32(v, rsc, 4 * i, 0, 0);
-      out[i] = i < count ? make_key(v, (uint32_t)(cbeg + i)) : 0ull;
+      out.put(i, i < count ? make_key(v, (uint32_t)(cbeg + i)) : 0ull);
     }
     if (tid == 0) *xout = 0;
     DSA_TRACE_FLUSH();
@@ -479,7 +479,7 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(ScoreArgs a) {
     r += (uint32_t)__builtin_amdgcn_mov_dpp((int)r, dpp::kQuadXor1, 0xF, 0xF, false);
     r += (uint32_t)__builtin_amdgcn_mov_dpp((int)r, dpp::kQuadXor2, 0xF, 0xF, false);
     if (part == 0 && t < (int)total) {
-      if (r < (uint32_t)m) out[r] = me;
+      if (r < (uint32_t)m) out.put((int)r, me);
       else if (r == (uint32_t)m) *xout = me;
     }
   } else {

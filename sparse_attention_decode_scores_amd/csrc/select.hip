@@ -49,7 +49,7 @@ __global__ __launch_bounds__(kSelBlock) void k_chunk_cand(CandArgs a) {
   radix_clear<kSelBlock>(csm.radix);
   for (int i = threadIdx.x; i < count; i += kSelBlock) sc[i] = row[i];
   lds_barrier();
-  chunk_candidates<kSelBlock>(sc, count, (uint32_t)cbeg, a.m, a.cand + ((int64_t)b * a.G + c) * a.m,
+  chunk_candidates<kSelBlock>(sc, count, (uint32_t)cbeg, a.m, CandOut{a.cand + (int64_t)b * kCandCap, c * a.m},
                               a.xc + (int64_t)b * a.G + c, csm);
 }
 
@@ -166,8 +166,10 @@ __device__ __forceinline__ const uint64_t* block_sort_row(const int32_t* __restr
 struct SelSmem {
   RadixSmem radix;
   uint32_t xch[kSelWaves][5];
+  uint64_t mxw[kSelWaves];  // per wave: the best key a chunk left out
   uint64_t kstar;
 };
+static_assert(kUPerThread == 16 && kSelBlock == 512, "cand_slot layout: 512 threads x 16 entries");
 
 // Exchanges (sum, min, max, max64) over the block in one round.
 struct Stats4 {
@@ -333,16 +335,18 @@ __global__ __launch_bounds__(kSelBlock) void k_select(SelArgs a, AttnArgs at) {
   uint64_t key[kUPerThread];
   uint64_t mx = 0;
   if (reason == 0) {
-    // the candidate union U: thread t holds keys [16t, 16t + 16) (position order)
+    // the candidate union U: thread t holds entries [16t, 16t + 16), eight 16-byte
+    // pieces, piece j of all threads contiguous (cand_slot); entries past the
+    // union's end are absent (key 0)
     const int C = a.G * a.m;
     typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
-    const u64x2* src = reinterpret_cast<const u64x2*>(a.cand + (int64_t)b * C + tid * kUPerThread);
-    const bool have = tid * kUPerThread < C;
+    const u64x2* src = reinterpret_cast<const u64x2*>(a.cand + (int64_t)b * kCandCap) + tid;
 #pragma unroll
     for (int j = 0; j < kUPerThread / 2; ++j) {
-      const u64x2 v = have ? src[j] : u64x2{0ull, 0ull};
-      key[2 * j] = v.x;
-      key[2 * j + 1] = v.y;
+      const u64x2 v = src[(kCandCap / 16) * j];
+      const int u = kUPerThread * tid + 2 * j;
+      key[2 * j] = u < C ? v.x : 0ull;
+      key[2 * j + 1] = u + 1 < C ? v.y : 0ull;
     }
     mx = tid < a.G ? a.xc[(int64_t)b * a.G + tid] : 0ull;
   }
@@ -365,9 +369,24 @@ __global__ __launch_bounds__(kSelBlock) void k_select(SelArgs a, AttnArgs at) {
       hi = v && sv[j] > hi ? sv[j] : hi;
     }
     DSA_MARK(1, 11);
-    const Stats4 st = block_stats((uint32_t)__popc(vmask), lo, hi, mx, sm);
-    nvalid = st.sum;
-    mx = st.mx;
+    // the range of the candidates' scores (its exchange also publishes the cleared
+    // radix histograms); the best dropped key is only needed for the coverage
+    // check, so its load is not waited for here
+    uint32_t rng[2];
+    {
+      const uint32_t mine[2] = {~wave_min_u32(lo), wave_maxr_u32(hi)};
+      uint32_t all[kSelWaves][2];
+      block_exchange<kSelBlock, 2>(mine, reinterpret_cast<uint32_t(*)[2]>(&sm.xch[0][0]), all);
+      uint32_t nlo = 0, mhi = 0;
+#pragma unroll
+      for (int w = 0; w < kSelWaves; ++w) {
+        nlo = all[w][0] > nlo ? all[w][0] : nlo;
+        mhi = all[w][1] > mhi ? all[w][1] : mhi;
+      }
+      rng[0] = ~nlo;
+      rng[1] = mhi;
+    }
+    nvalid = (uint32_t)a.cand_valid.n[b];
     DSA_MARK(1, 1);
     const uint32_t kk = (uint32_t)a.k < nvalid ? (uint32_t)a.k : nvalid;
     auto each = [&](auto f) {
@@ -376,14 +395,19 @@ __global__ __launch_bounds__(kSelBlock) void k_select(SelArgs a, AttnArgs at) {
         if ((vmask >> j) & 1u) f(sv[j]);
     };
     uint32_t above;
-    const uint32_t T = block_select_range<kSelBlock>(each, st.lo, st.hi, (int)kk, &above, sm.radix);
+    const uint32_t T = block_select_range<kSelBlock>(each, rng[0], rng[1], (int)kk, &above, sm.radix);
     const uint32_t need_eq = kk - above;
     DSA_MARK(1, 2);
     uint32_t ts, te;
     write_selected_u<kUPerThread>(key, sv, vmask, T, need_eq, sel, sm, &ts, &te);
+    const uint64_t wmx = wave_maxr_u64(mx);
+    if (lane_id() == 0) sm.mxw[wave_id()] = wmx;
     lds_barrier();
     DSA_MARK(1, 3);
     kstar = sm.kstar;
+    mx = 0;
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w) mx = sm.mxw[w] > mx ? sm.mxw[w] : mx;
     // every dropped key is below the k-th candidate: the candidates hold the top k
     const bool ok = mx < kstar && (nvalid >= (uint32_t)a.k || mx == 0);
     if (ok) {
@@ -445,9 +469,8 @@ __global__ __launch_bounds__(kSelBlock) void k_select(SelArgs a, AttnArgs at) {
     const int e0 = (int)blockIdx.x * per;
     int cnt = (int)nsel - e0;
     cnt = cnt < 0 ? 0 : (cnt > per ? per : cnt);
-    Attn::store_q(qf, at, region);
     Attn::run(at, b, blockIdx.x, [&](int i) { return (int64_t)key_pos(sel[e0 + i]); }, cnt,
-              region);
+              region, qf);
     DSA_MARK(1, 10);
     DSA_TRACE_FLUSH();
     return;
@@ -549,8 +572,7 @@ __global__ __launch_bounds__(kSelBlock) void k_attend_idx(const int32_t* __restr
   }
   bad = block_stats(bad, 0, 0, 0, sm).sum;
   if (tid == 0) part_bad[(int64_t)b * at.S + j] = (int32_t)bad;
-  Attn::store_q(qf, at, region);
-  Attn::run(at, b, j, [&](int i) { return (int64_t)posl[i]; }, (int)run, region);
+  Attn::run(at, b, j, [&](int i) { return (int64_t)posl[i]; }, (int)run, region, qf);
 }
 
 template <class Attn>
