@@ -15,8 +15,14 @@ namespace {
 constexpr size_t kAlign = 256;
 inline size_t up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
 
-int splits_for(int k) {
-  int s = (k + 63) / 64;
+// Attention splits per row: 64 selected rows per split on the vector-ALU paths;
+// 32 on the matrix-core path (more workgroups, each with half the serial work).
+int splits_for(int k, bool mfma = false) {
+  if (mfma) {
+    const int s = (k + 31) / 32;
+    return s < 1 ? 1 : (s > kMaxWideSplits ? kMaxWideSplits : s);
+  }
+  const int s = (k + 63) / 64;
   return s < 1 ? 1 : (s > kMaxSplits ? kMaxSplits : s);
 }
 int rankers_for(int k) {
@@ -29,7 +35,7 @@ struct Layout {
   size_t stats, cand, xc, ml, o, bad, sort, total;
 };
 Layout layout(int B, int64_t N, int k, int Hq, int Dv) {
-  const int S = splits_for(k);
+  const int S = splits_for(k, true);  // the larger of the two split counts
   Layout L;
   L.stats = 0;
   L.cand = up(sizeof(RowStats) * kMaxBatch);
@@ -227,6 +233,18 @@ AttnArgs attn_args(const void* q, const void* kv, int64_t N, int Hq, int Dk, int
   return at;
 }
 
+// Split count and partial layout for the chosen attention path.
+void set_attn_path(AttnArgs* at, const AttnChoice& ch, int k) {
+  at->frag = ch.kind == ATTN_MFMA_BF16;
+  at->S = splits_for(k, at->frag != 0);
+}
+
+hipError_t combine(const AttnArgs& at, const int32_t* part_bad, RowStats* stats, float* out, int B,
+                   hipStream_t s, KTimer t = {}) {
+  if (at.S > kMaxSplits) return launch_combine_wide(at, part_bad, stats, out, B, s, t);
+  return launch_combine(at, part_bad, stats, out, B, s, t);
+}
+
 SelArgs sel_args(const int32_t* scores, const RowLens& lens, int64_t N, int k, int32_t* idx,
                  uint8_t* w, const Layout& L, const ChunkPlan& cp, bool have_cand, unsigned flags) {
   SelArgs a;
@@ -340,11 +358,10 @@ dsa_status dsa_sparse_attn(const void* q, const void* kv, const int32_t* idx, in
   if ((st = check_ws(ws, ws_bytes, L)) != DSA_OK) return st;
   uint8_t* w = static_cast<uint8_t*>(ws);
   AttnArgs at = attn_args(q, kv, N, Hq, Dk, Dv, scale, k, w, L);
-  at.frag = ch.kind == ATTN_MFMA_BF16;
+  set_attn_path(&at, ch, k);
   int32_t* bad = reinterpret_cast<int32_t*>(w + L.bad);
   if (launch_attend_idx(idx, k, bad, at, ch, B, stream) != hipSuccess) return DSA_ERR_HIP;
-  return hip_status(
-      launch_combine(at, bad, reinterpret_cast<RowStats*>(w + L.stats), out, B, stream));
+  return hip_status(combine(at, bad, reinterpret_cast<RowStats*>(w + L.stats), out, B, stream));
 }
 
 dsa_status dsa_decode_step_timed(const int8_t* iq, const int8_t* iw, const int8_t* ik,
@@ -379,9 +396,9 @@ dsa_status dsa_decode_step_timed(const int8_t* iq, const int8_t* iw, const int8_
   if (st != DSA_OK) return st;
   const SelArgs sa = sel_args(scores, lens, N, k, idx, w, L, cp, have, flags);
   AttnArgs at = attn_args(q, kv, N, Hq, Dk, Dv, scale, k, w, L);
-  at.frag = ch.kind == ATTN_MFMA_BF16;
+  set_attn_path(&at, ch, k);
   if (launch_select(sa, at, ch, B, stream, tm[1]) != hipSuccess) return DSA_ERR_HIP;
-  return hip_status(launch_combine(at, nullptr, nullptr, out, B, stream, tm[2]));
+  return hip_status(combine(at, nullptr, nullptr, out, B, stream, tm[2]));
 }
 
 dsa_status dsa_decode_step(const int8_t* iq, const int8_t* iw, const int8_t* ik, const void* q,

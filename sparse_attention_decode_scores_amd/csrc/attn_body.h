@@ -128,178 +128,194 @@ struct AttnMfma {
     }
   }
 
-  // qf: the query fragments from load_q; they are written to LDS once the first
-  // sub-block's row loads are in flight.
-  template <typename PosAt>
-  __device__ static void run(const AttnArgs& p, int b, int split, PosAt pos_at, int cnt,
-                             uint8_t* work, const QFrag& qf) {
-    const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
-    const int Dk = p.Dk, Dv = p.Dv, KS = Dk >> 5, rb = row_bytes(Dk);
-    const int nt_all = Dv >> 4;  // 16-wide output tiles
-    const uint8_t* qs = work;
-    uint8_t* rows = work + q_bytes(Dk);
-    float* lg = reinterpret_cast<float*>(rows + align16((size_t)SB * rb));
-    float* mrun = lg + HP * SB;
-    float* lrun = mrun + HP;
-    float* alpha = lrun + HP;
-    const __bf16* q = reinterpret_cast<const __bf16*>(p.q) + (int64_t)b * p.Hq * Dk;
-    const uint8_t* kv = reinterpret_cast<const uint8_t*>(p.kv);
+  // LDS working set: [query heads (kQInLds)] [SB staged rows] [logits HP x SB]
+  // [running max, sum, rescale per head].
+  struct Work {
+    const uint8_t* qs;
+    uint8_t* rows;
+    float *lg, *mrun, *lrun, *alpha;
+  };
+  __device__ static Work work_of(const AttnArgs& p, uint8_t* work) {
+    Work w;
+    w.qs = work;
+    w.rows = work + q_bytes(p.Dk);
+    w.lg = reinterpret_cast<float*>(w.rows + align16((size_t)SB * row_bytes(p.Dk)));
+    w.mrun = w.lg + HP * SB;
+    w.lrun = w.mrun + HP;
+    w.alpha = w.lrun + HP;
+    return w;
+  }
+  typedef v4f Acc[HQT][kMaxTilesPerWave];
 
-    v4f o[HQT][kMaxTilesPerWave];
+  // The rows of one sub-block in flight: gather slot j of this thread holds the
+  // 16-byte column qf.cc[j] of sub-block row qf.rr[j] (rows at or past nr re-read row
+  // nr - 1: every load is issued, so the compiler's wait counts stay exact).
+  struct Rows {
+    v4i v[kMaxLoads];
+  };
+  template <typename PosAt>
+  __device__ static Rows gather(const AttnArgs& p, const QFrag& qf, PosAt pos_at, int nr) {
+    const uint8_t* kv = reinterpret_cast<const uint8_t*>(p.kv);
+    int32_t rp[kMaxLoads];
+#pragma unroll
+    for (int j = 0; j < kMaxLoads; ++j) rp[j] = (int32_t)pos_at(qf.rr[j] < nr ? qf.rr[j] : nr - 1);
+    Rows r;
+#pragma unroll
+    for (int j = 0; j < kMaxLoads; ++j) r.v[j] = *(const v4i*)(kv + ((int64_t)rp[j] * p.Dk + 8 * qf.cc[j]) * 2);
+    return r;
+  }
+  // Stores gathered rows (absent rows as zeros) and, with `with_q`, the query heads;
+  // the next barrier publishes them.
+  __device__ static void put(const Rows& r, const QFrag& qf, const AttnArgs& p, int nr, bool with_q,
+                             uint8_t* work) {
+    const Work w = work_of(p, work);
+    const int rb = row_bytes(p.Dk), nch = SB * (p.Dk >> 3);  // nch <= kMaxLoads * block size
+    if (with_q) store_q(qf, p, work);
+#pragma unroll
+    for (int j = 0; j < kMaxLoads; ++j)
+      if ((int)threadIdx.x + kAttnBlock * j < nch)
+        *(v4i*)(w.rows + qf.rr[j] * rb + 16 * qf.cc[j]) = qf.rr[j] < nr ? r.v[j] : v4i{0, 0, 0, 0};
+  }
+  __device__ static void begin(const AttnArgs& p, uint8_t* work, Acc& o) {
+    const Work w = work_of(p, work);
 #pragma unroll
     for (int mt = 0; mt < HQT; ++mt)
 #pragma unroll
       for (int j = 0; j < kMaxTilesPerWave; ++j) o[mt][j] = v4f{0.f, 0.f, 0.f, 0.f};
-    for (int h = tid; h < HP; h += kAttnBlock) {
-      mrun[h] = -INFINITY;
-      lrun[h] = 0.f;
+    for (int h = threadIdx.x; h < HP; h += kAttnBlock) {
+      w.mrun[h] = -INFINITY;
+      w.lrun[h] = 0.f;
     }
+  }
 
-    const int* rr = qf.rr;
-    const int* cc = qf.cc;
-
-    for (int s0 = 0; s0 < cnt; s0 += SB) {
-      const int nr = cnt - s0 < SB ? cnt - s0 : SB;
-      // gather the sub-block's rows with 16-byte loads: every position is read from
-      // LDS first, then every row load is issued, then the stores. Reads and loads
-      // are unconditional (a branch would make the compiler wait on each one):
-      // slots past the sub-block's chunks or rows re-read its last row, and only
-      // present rows' data is stored (absent rows store zeros).
-      const int cpr = Dk >> 3;
-      const int nch = SB * cpr;  // <= kMaxLoads * block size (checked when the path is chosen)
-      DSA_MARK(1, 12);
-      int32_t rp[kMaxLoads];
+  // One staged sub-block: row r takes part iff bit r of `live` is set. Logits on
+  // the matrix cores, online-softmax update, then P V accumulated into o.
+  __device__ static void sub_block(const AttnArgs& p, int b, uint64_t live, uint8_t* work, Acc& o) {
+    const int lane = lane_id(), wave = wave_id();
+    const int Dk = p.Dk, KS = Dk >> 5, rb = row_bytes(Dk), nt_all = p.Dv >> 4;
+    const Work w = work_of(p, work);
+    const __bf16* q = reinterpret_cast<const __bf16*>(p.q) + (int64_t)b * p.Hq * Dk;
+    lds_barrier();
+    DSA_MARK(1, 6);
+    // logits: D[head][row], head = 16*mt + 4*(l/16) + r, row = 16*nt + l%16
+    for (int nt = wave; nt < SB / 16; nt += kAttnWaves) {
+      v4f acc[HQT];
 #pragma unroll
-      for (int j = 0; j < kMaxLoads; ++j) rp[j] = (int32_t)pos_at(s0 + (rr[j] < nr ? rr[j] : nr - 1));
-      v4i buf[kMaxLoads];
+      for (int mt = 0; mt < HQT; ++mt) acc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
+      const uint8_t* rrow = w.rows + (16 * nt + (lane & 15)) * rb + 16 * (lane >> 4);
+      const int h_a = lane & 15;
+      auto afrag = [&](int mt, int kk) {
+        if (kQInLds) return *(const v8bf*)(w.qs + (16 * mt + h_a) * rb + 64 * kk + 16 * (lane >> 4));
+        // heads past Hq read a present head (always issued) and are zeroed at use
+        const int h = 16 * mt + h_a < p.Hq ? 16 * mt + h_a : p.Hq - 1;
+        return *(const v8bf*)(q + (int64_t)h * Dk + 32 * kk + 8 * (lane >> 4));
+      };
+      // fragments of kLogitBatch k-steps are loaded before their matrix-core steps
+      for (int k0 = 0; k0 < KS; k0 += kLogitBatch) {
+        v8bf bfrag[kLogitBatch];
+        v8bf afr[HQT][kLogitBatch];
 #pragma unroll
-      for (int j = 0; j < kMaxLoads; ++j) buf[j] = *(const v4i*)(kv + ((int64_t)rp[j] * Dk + 8 * cc[j]) * 2);
-      if (s0 == 0) store_q(qf, p, work);  // published by the barrier below
-      DSA_MARK(1, 13);
+        for (int t = 0; t < kLogitBatch; ++t) {
+          if (k0 + t < KS) {
+            bfrag[t] = *(const v8bf*)(rrow + 64 * (k0 + t));
 #pragma unroll
-      for (int j = 0; j < kMaxLoads; ++j) {
-        if (tid + kAttnBlock * j < nch)
-          *(v4i*)(rows + rr[j] * rb + 16 * cc[j]) = rr[j] < nr ? buf[j] : v4i{0, 0, 0, 0};
-      }
-      DSA_MARK(1, 14);
-      lds_barrier();
-      DSA_MARK(1, 6);
-      // logits: D[head][row], head = 16*mt + 4*(l/16) + r, row = 16*nt + l%16
-      for (int nt = wave; nt < SB / 16; nt += kAttnWaves) {
-        v4f acc[HQT];
-#pragma unroll
-        for (int mt = 0; mt < HQT; ++mt) acc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
-        const uint8_t* rrow = rows + (16 * nt + (lane & 15)) * rb + 16 * (lane >> 4);
-        const int h_a = lane & 15;
-        auto afrag = [&](int mt, int kk) {
-          if (kQInLds) return *(const v8bf*)(qs + (16 * mt + h_a) * rb + 64 * kk + 16 * (lane >> 4));
-          // heads past Hq read a present head (always issued) and are zeroed at use
-          const int h = 16 * mt + h_a < p.Hq ? 16 * mt + h_a : p.Hq - 1;
-          return *(const v8bf*)(q + (int64_t)h * Dk + 32 * kk + 8 * (lane >> 4));
-        };
-        // fragments of kLogitBatch k-steps are loaded before their matrix-core steps
-        for (int k0 = 0; k0 < KS; k0 += kLogitBatch) {
-          v8bf bfrag[kLogitBatch];
-          v8bf afr[HQT][kLogitBatch];
-#pragma unroll
-          for (int t = 0; t < kLogitBatch; ++t) {
-            if (k0 + t < KS) {
-              bfrag[t] = *(const v8bf*)(rrow + 64 * (k0 + t));
-#pragma unroll
-              for (int mt = 0; mt < HQT; ++mt) afr[mt][t] = afrag(mt, k0 + t);
-            }
+            for (int mt = 0; mt < HQT; ++mt) afr[mt][t] = afrag(mt, k0 + t);
           }
+        }
 #pragma unroll
-          for (int t = 0; t < kLogitBatch; ++t) {
-            if (k0 + t < KS) {
+        for (int t = 0; t < kLogitBatch; ++t) {
+          if (k0 + t < KS) {
 #pragma unroll
-              for (int mt = 0; mt < HQT; ++mt) {
-                v8bf a = afr[mt][t];
-                if (!kQInLds && 16 * mt + h_a >= p.Hq) a = v8bf{};
-                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bfrag[t], acc[mt], 0, 0, 0);
-              }
+            for (int mt = 0; mt < HQT; ++mt) {
+              v8bf a = afr[mt][t];
+              if (!kQInLds && 16 * mt + h_a >= p.Hq) a = v8bf{};
+              acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bfrag[t], acc[mt], 0, 0, 0);
             }
           }
         }
-        const int row = 16 * nt + (lane & 15);
-#pragma unroll
-        for (int mt = 0; mt < HQT; ++mt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            lg[(16 * mt + 4 * (lane >> 4) + r) * SB + row] =
-                row < nr ? acc[mt][r] * p.scale : -INFINITY;
       }
-      lds_barrier();
-      DSA_MARK(1, 7);
-      softmax_update(lg, SB, HP, mrun, lrun, alpha);
-      lds_barrier();
-      DSA_MARK(1, 8);
-      // output: D[head][dv] += P[head][row] V[row][dv]
+      const int row = 16 * nt + (lane & 15);
+      const bool in = (live >> row) & 1ull;
 #pragma unroll
       for (int mt = 0; mt < HQT; ++mt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float a = alpha[16 * mt + 4 * (lane >> 4) + r];
+        for (int r = 0; r < 4; ++r) w.lg[(16 * mt + 4 * (lane >> 4) + r) * SB + row] = in ? acc[mt][r] * p.scale : -INFINITY;
+    }
+    lds_barrier();
+    DSA_MARK(1, 7);
+    softmax_update(w.lg, SB, HP, w.mrun, w.lrun, w.alpha);
+    lds_barrier();
+    DSA_MARK(1, 8);
+    // output: D[head][dv] += P[head][row] V[row][dv]
 #pragma unroll
-          for (int j = 0; j < kMaxTilesPerWave; ++j)
-            if (wave + kAttnWaves * j < nt_all) o[mt][j][r] *= a;
+    for (int mt = 0; mt < HQT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float a = w.alpha[16 * mt + 4 * (lane >> 4) + r];
+#pragma unroll
+        for (int j = 0; j < kMaxTilesPerWave; ++j)
+          if (wave + kAttnWaves * j < nt_all) o[mt][j][r] *= a;
+      }
+    for (int kk = 0; kk < SB / 32; ++kk) {
+      v8bf ahi[HQT], alo[HQT];
+#pragma unroll
+      for (int mt = 0; mt < HQT; ++mt) {
+        const float* pp = w.lg + (16 * mt + (lane & 15)) * SB + 32 * kk + 8 * (lane >> 4);
+        const v4f p0 = *(const v4f*)pp, p1 = *(const v4f*)(pp + 4);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const float pv = t < 4 ? p0[t] : p1[t - 4];
+          const float hi = __uint_as_float(__float_as_uint(pv) & 0xFFFF0000u);
+          ahi[mt][t] = (__bf16)hi;
+          alo[mt][t] = (__bf16)(pv - hi);
         }
-      for (int kk = 0; kk < SB / 32; ++kk) {
-        v8bf ahi[HQT], alo[HQT];
+      }
+      // B fragment: V[rows 32*kk + 8*(l/16) + t][dv 16*nt + l%16], t < 8, read with two
+      // transposing LDS loads: lane j of each 16-lane group names the 4-value chunk
+      // (row base + j/4, columns 4*(j%4)..+3) and receives column j of the 4 rows.
+      // Every tile's fragment is read before the first matrix-core step.
+      const int tr_row = 32 * kk + 8 * (lane >> 4) + ((lane & 15) >> 2);
+      const int tr_col = 4 * (lane & 3);
+      typedef short v4s __attribute__((ext_vector_type(4)));
+      typedef __attribute__((address_space(3))) v4s lds_v4s;
+      typedef short v8s __attribute__((ext_vector_type(8)));
+      v4s vr[kMaxTilesPerWave][2];
 #pragma unroll
-        for (int mt = 0; mt < HQT; ++mt) {
-          const float* pp = lg + (16 * mt + (lane & 15)) * SB + 32 * kk + 8 * (lane >> 4);
-          const v4f p0 = *(const v4f*)pp, p1 = *(const v4f*)(pp + 4);
-#pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            const float pv = t < 4 ? p0[t] : p1[t - 4];
-            const float hi = __uint_as_float(__float_as_uint(pv) & 0xFFFF0000u);
-            ahi[mt][t] = (__bf16)hi;
-            alo[mt][t] = (__bf16)(pv - hi);
-          }
+      for (int j = 0; j < kMaxTilesPerWave; ++j) {
+        const int nt = wave + kAttnWaves * j;
+        if (nt < nt_all) {
+          const uint8_t* va = w.rows + tr_row * rb + (16 * nt + tr_col) * 2;
+          vr[j][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(va));
+          vr[j][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(va + 4 * rb));
         }
-        // B fragment: V[rows 32*kk + 8*(l/16) + t][dv 16*nt + l%16], t < 8, read with two
-        // transposing LDS loads: lane j of each 16-lane group names the 4-value chunk
-        // (row base + j/4, columns 4*(j%4)..+3) and receives column j of the 4 rows.
-        // Every tile's fragment is read before the first matrix-core step.
-        const int tr_row = 32 * kk + 8 * (lane >> 4) + ((lane & 15) >> 2);
-        const int tr_col = 4 * (lane & 3);
-        typedef short v4s __attribute__((ext_vector_type(4)));
-        typedef __attribute__((address_space(3))) v4s lds_v4s;
-        typedef short v8s __attribute__((ext_vector_type(8)));
-        v4s vr[kMaxTilesPerWave][2];
+      }
 #pragma unroll
-        for (int j = 0; j < kMaxTilesPerWave; ++j) {
-          const int nt = wave + kAttnWaves * j;
-          if (nt < nt_all) {
-            const uint8_t* va = rows + tr_row * rb + (16 * nt + tr_col) * 2;
-            vr[j][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(va));
-            vr[j][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(va + 4 * rb));
-          }
-        }
+      for (int j = 0; j < kMaxTilesPerWave; ++j) {
+        const int nt = wave + kAttnWaves * j;
+        if (nt < nt_all) {
+          const v8s both = __builtin_shufflevector(vr[j][0], vr[j][1], 0, 1, 2, 3, 4, 5, 6, 7);
+          const v8bf bfr = __builtin_bit_cast(v8bf, both);
 #pragma unroll
-        for (int j = 0; j < kMaxTilesPerWave; ++j) {
-          const int nt = wave + kAttnWaves * j;
-          if (nt < nt_all) {
-            const v8s both = __builtin_shufflevector(vr[j][0], vr[j][1], 0, 1, 2, 3, 4, 5, 6, 7);
-            const v8bf bfr = __builtin_bit_cast(v8bf, both);
-#pragma unroll
-            for (int mt = 0; mt < HQT; ++mt) {
-              o[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[mt], bfr, o[mt][j], 0, 0, 0);
-              o[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[mt], bfr, o[mt][j], 0, 0, 0);
-            }
+          for (int mt = 0; mt < HQT; ++mt) {
+            o[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[mt], bfr, o[mt][j], 0, 0, 0);
+            o[mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[mt], bfr, o[mt][j], 0, 0, 0);
           }
         }
       }
-      lds_barrier();
-      DSA_MARK(1, 9);
     }
+    lds_barrier();
+    DSA_MARK(1, 9);
+  }
 
-    // partial output in accumulator order: element ((mt * tiles + nt) * 64 + lane) * 4 + r
-    // is head 16*mt + 4*(lane/16) + r, value 16*nt + lane%16 (one 16-byte store per tile)
+  // The split's partial result: (max, sum) per head and the unnormalised output in
+  // accumulator order: element ((mt * tiles + nt) * 64 + lane) * 4 + r is head
+  // 16*mt + 4*(lane/16) + r, value 16*nt + lane%16 (one 16-byte store per tile).
+  __device__ static void finish(const AttnArgs& p, int b, int split, uint8_t* work, const Acc& o) {
+    const int lane = lane_id(), wave = wave_id(), nt_all = p.Dv >> 4;
+    const Work w = work_of(p, work);
     const int64_t pb = (int64_t)b * p.S + split;
-    for (int h = tid; h < p.Hq; h += kAttnBlock) p.part_ml[pb * p.Hq + h] = make_float2(mrun[h], lrun[h]);
-    float* po = p.part_o + pb * HP * Dv;
+    for (int h = threadIdx.x; h < p.Hq; h += kAttnBlock) p.part_ml[pb * p.Hq + h] = make_float2(w.mrun[h], w.lrun[h]);
+    float* po = p.part_o + pb * HP * p.Dv;
 #pragma unroll
     for (int mt = 0; mt < HQT; ++mt)
 #pragma unroll
@@ -308,6 +324,26 @@ struct AttnMfma {
         if (nt >= nt_all) break;
         *(v4f*)(po + ((int64_t)(mt * nt_all + nt) * 64 + lane) * 4) = o[mt][j];
       }
+  }
+
+  // Attention over cnt listed positions (pos_at(i), i < cnt) as split `split`: the
+  // positions are staged SB at a time; the query fragments (load_q) are written to
+  // LDS once the first sub-block's row loads are in flight.
+  template <typename PosAt>
+  __device__ static void run(const AttnArgs& p, int b, int split, PosAt pos_at, int cnt,
+                             uint8_t* work, const QFrag& qf) {
+    Acc o;
+    begin(p, work, o);
+    for (int s0 = 0; s0 < cnt; s0 += SB) {
+      const int nr = cnt - s0 < SB ? cnt - s0 : SB;
+      DSA_MARK(1, 12);
+      const Rows r = gather(p, qf, [&](int i) { return pos_at(s0 + i); }, nr);
+      DSA_MARK(1, 13);
+      put(r, qf, p, nr, s0 == 0, work);
+      DSA_MARK(1, 14);
+      sub_block(p, b, nr >= 64 ? ~0ull : (1ull << nr) - 1ull, work, o);
+    }
+    finish(p, b, split, work, o);
   }
 };
 

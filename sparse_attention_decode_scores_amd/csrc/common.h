@@ -9,7 +9,8 @@ namespace dsa {
 constexpr int kMaxBatch = 16;
 constexpr int kCandCap = 8192;         // candidate keys per row kept by the chunk pass
 constexpr int kMaxChunks = 256;
-constexpr int kMaxSplits = 32;         // attention splits per row
+constexpr int kMaxSplits = 32;         // attention splits per row (vector-ALU attention)
+constexpr int kMaxWideSplits = 128;    // attention splits per row (matrix-core attention)
 constexpr int kMaxRankBlocks = 128;
 
 typedef int v4i __attribute__((ext_vector_type(4)));

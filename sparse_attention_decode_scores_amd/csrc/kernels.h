@@ -122,5 +122,8 @@ hipError_t launch_attend_idx(const int32_t* idx, int k, int32_t* part_bad, const
                              AttnChoice ch, int B, hipStream_t s);
 hipError_t launch_combine(const AttnArgs& at, const int32_t* part_bad, RowStats* stats, float* out,
                           int B, hipStream_t s, KTimer t = {});
+// The combine for more than kMaxSplits splits (matrix-core partial layout).
+hipError_t launch_combine_wide(const AttnArgs& at, const int32_t* part_bad, RowStats* stats, float* out,
+                               int B, hipStream_t s, KTimer t = {});
 
 }  // namespace dsa

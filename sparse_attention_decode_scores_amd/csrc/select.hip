@@ -328,6 +328,10 @@ __global__ __launch_bounds__(kSelBlock) void k_select(SelArgs a, AttnArgs at) {
   const int32_t* row = a.scores + (int64_t)b * a.N;
   DSA_TRACE_BEGIN();
   DSA_MARK(1, 0);
+  // The attention arguments are first needed after the selection; reading two of
+  // them here brings their part of the argument block into the scalar cache early
+  // (a first read at that point would wait for a memory round trip).
+  if (at.frag == -1 && at.part_o == nullptr) a.stats[0].reserved = at.Dk;
 
   int reason = a.force ? 1 : (a.have_cand ? 0 : 3);
   uint32_t nvalid = 0, nsel = 0, tied = 0;
@@ -596,7 +600,7 @@ AttnChoice choose_attn(int dt_bf16, int Hq, int Dk, int Dv) {
       Dv <= Dk) {
     c.kind = ATTN_MFMA_BF16;
     c.hqt = (Hq + 15) / 16;
-    c.sb = Dk <= 576 ? 64 : 32;
+    c.sb = 32;  // a split's 32 rows form one sub-block
     if ((Dk / 8) * c.sb <= AttnMfma<1, 64>::kMaxLoads * kAttnBlock) return c;  // one gather pass
     c = AttnChoice{ATTN_NONE, 0, 0};
   }
@@ -680,6 +684,114 @@ hipError_t launch_attend_idx(const int32_t* idx, int k, int32_t* part_bad, const
 }
 
 // ------------------------------------------------------------------ combine
+
+constexpr int kCombWideBlock = 256;
+
+// The combine for many splits (up to kMaxWideSplits; partials in accumulator
+// order): one workgroup per 16 output elements of that order (4 heads x 16
+// values). It forms the split weights of its 4 heads (64 thread groups,
+// fixed-order reductions), then 16 thread groups each sum every 16th split and the
+// groups are added in order, so the result does not depend on timing.
+__global__ __launch_bounds__(kCombWideBlock) void k_combine_wide(AttnArgs at, const int32_t* __restrict__ part_bad,
+                                                                 RowStats* __restrict__ stats, float* __restrict__ out) {
+  __shared__ float wt[4][kMaxWideSplits];
+  __shared__ float red[4][65];
+  __shared__ v4f part[16][16];
+  const int b = blockIdx.y, t = threadIdx.x;
+  const int S = at.S, Hq = at.Hq, Dv = at.Dv;
+  const int HP = (Hq + 15) / 16 * 16, tiles = Dv / 16;
+  const int quad = blockIdx.x, tile = quad >> 2, l0 = 16 * (quad & 3);
+  const int h0 = 16 * (tile / tiles) + 4 * (quad & 3);  // heads h0 .. h0 + 3
+  DSA_TRACE_BEGIN();
+  DSA_MARK(2, 0);
+  // every load first: this thread's (max, sum) pairs, then its partial outputs
+  const int h = t & 3, g = t >> 2;
+  const int hh = h0 + h < Hq ? h0 + h : Hq - 1;
+  float2 ml[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int sp = g + 64 * i;
+    ml[i] = at.part_ml[((int64_t)b * S + (sp < S ? sp : S - 1)) * Hq + hh];
+  }
+  const int e = t & 15, q = t >> 4;
+  const float* po = at.part_o + (int64_t)b * S * HP * Dv;
+  const int64_t el = (int64_t)tile * 64 + l0 + e;  // 16-byte element
+  constexpr int kPer = kMaxWideSplits / 16;
+  v4f v[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int sp = q + 16 * i;
+    v[i] = *(const v4f*)(po + (int64_t)(sp < S ? sp : S - 1) * HP * Dv + el * 4);
+  }
+  // split weights e^(m_s - M) / L of the four heads
+  red[h][g] = fmaxf(g < S ? ml[0].x : -INFINITY, g + 64 < S ? ml[1].x : -INFINITY);
+  lds_barrier();
+  if (t < 4) {
+    float M = -INFINITY;
+    for (int j = 0; j < 64; ++j) M = fmaxf(M, red[t][j]);
+    red[t][64] = M;
+  }
+  lds_barrier();
+  const float M = red[h][64];
+  float ew[2], sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int sp = g + 64 * i;
+    ew[i] = (sp < S && ml[i].x != -INFINITY) ? __expf(ml[i].x - M) : 0.f;
+    sum = fmaf(ew[i], ml[i].y, sum);
+  }
+  red[h][g] = sum;
+  lds_barrier();
+  if (t < 4) {
+    float L = 0.f;
+    for (int j = 0; j < 64; ++j) L += red[t][j];
+    red[t][64] = (h0 + t < Hq && L > 0.f) ? 1.f / L : 0.f;
+  }
+  lds_barrier();
+  const float inv = red[h][64];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int sp = g + 64 * i;
+    if (sp < S) wt[h][sp] = ew[i] * inv;
+  }
+  lds_barrier();
+  DSA_MARK(2, 2);
+  v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int sp = q + 16 * i;
+    if (sp < S)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] = fmaf(wt[r][sp], v[i][r], acc[r]);
+  }
+  part[q][e] = acc;
+  lds_barrier();
+  if (t < 16) {
+    v4f tot = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 16; ++j) tot += part[j][t];
+    const int vcol = 16 * (tile % tiles) + t;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (h0 + r < Hq) out[((int64_t)b * Hq + h0 + r) * Dv + vcol] = tot[r];
+  }
+  // the count of invalid indices (stand-alone attention), read last
+  if (part_bad != nullptr && quad == 0 && t < 64) {
+    uint32_t nb = 0;
+    for (int sp = t; sp < S; sp += 64) nb += (uint32_t)part_bad[(int64_t)b * S + sp];
+    nb = wave_sum_u32(nb);
+    if (t == 0) stats[b].bad_indices = (int32_t)nb;
+  }
+  DSA_TRACE_FLUSH();
+}
+
+hipError_t launch_combine_wide(const AttnArgs& at, const int32_t* part_bad, RowStats* stats, float* out,
+                               int B, hipStream_t s, KTimer t) {
+  if (!at.frag || at.S > kMaxWideSplits) return hipErrorInvalidValue;
+  const int quads = (at.Hq + 15) / 16 * (at.Dv / 16) * 4;
+  return launch_timed(k_combine_wide, dim3(quads, B), dim3(kCombWideBlock), 0, s, t, at, part_bad, stats,
+                      out);
+}
 
 constexpr int kCombBlock = 64;
 
