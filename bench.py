@@ -372,7 +372,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "indexer score pass (k_score, int8 MFMA + per-chunk candidates)",
+            "kernel": "indexer score pass (k_score_row: int8 MFMA, per-chunk top-m candidates)",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

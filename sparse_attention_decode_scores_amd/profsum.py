@@ -141,7 +141,8 @@ def cmd_counters(args):
         "kernel_source_sha": library_source_sha(),
         "command_fetch": args.command_fetch,
         "command_write": args.command_write,
-        "summary_command": " ".join(sys.argv),
+        "summary_command": "python3 -m sparse_attention_decode_scores_amd.profsum " + " ".join(
+            "'%s'" % x if " " in x else x for x in sys.argv[1:]),
         "copy_calibration": {
             "kernel": "torch.neg over 64 Mi fp32 values (%d bytes read, %d written per dispatch)"
                       % (COPY_BYTES, COPY_BYTES),
