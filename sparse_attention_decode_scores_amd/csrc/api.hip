@@ -113,13 +113,16 @@ dsa_status check_ws(void* ws, size_t ws_bytes, const Layout& L) {
 // Chunking of the candidate pass for rows of at most nmax positions.
 struct ChunkPlan {
   int P, G, m;
+  int ilv;  // one-row plan: interleaved chunks (row_chunk_units)
 };
 // One-row plan (score kernel k_score_row): chunks of whole 32-key units, as many
 // chunks as candidate slots allow (at most one per compute unit), so every wave of
 // a chunk has at most one unit more than another.
-ChunkPlan chunk_plan_row(int nmax, int k) {
+ChunkPlan chunk_plan_row(int nmax, int k, int Di) {
   ChunkPlan c;
   c.m = k <= 2048 ? 32 : 64;
+  // interleaved while every key offset of a row fits a buffer offset
+  c.ilv = (int64_t)nmax * Di <= ((int64_t)1 << 30) ? 1 : 0;
   const int gmax = kCandCap / c.m < kMaxChunks ? kCandCap / c.m : kMaxChunks;
   const int64_t units = ((int64_t)nmax + 31) / 32;
   int64_t per = (units + gmax - 1) / gmax;
@@ -129,9 +132,10 @@ ChunkPlan chunk_plan_row(int nmax, int k) {
   return c;
 }
 
-ChunkPlan chunk_plan(int nmax, int k, bool row) {
-  if (row) return chunk_plan_row(nmax, k);
+ChunkPlan chunk_plan(int nmax, int k, bool row, int Di) {
+  if (row) return chunk_plan_row(nmax, k, Di);
   ChunkPlan c;
+  c.ilv = 0;
   if (nmax <= kCandCap) {  // short rows: every position is a candidate
     c.P = 64;
     c.m = 64;
@@ -174,6 +178,7 @@ dsa_status run_scores(const int8_t* iq, const int8_t* iw, const int8_t* ik, cons
   a.Hi = Hi;
   a.Di = Di;
   a.m = cp.m;
+  a.ilv = 0;
   if (cand) {
     a.P = cp.P;
     a.G = cp.G;
@@ -185,6 +190,7 @@ dsa_status run_scores(const int8_t* iq, const int8_t* iw, const int8_t* ik, cons
   if (cand && B == 1) {  // the decode hot path: one row, candidates on
     a.b0 = 0;
     a.Bg = 1;
+    a.ilv = cp.ilv;
     return hip_status(launch_score_row(a, MT, KT, kScoreRowDepth, a.G, s, t));
   }
   const int bg = rows_per_score_launch(Hi, Di, B);
@@ -263,9 +269,9 @@ SelArgs sel_args(const int32_t* scores, const RowLens& lens, int64_t N, int k, i
   memset(&a.cand_valid, 0, sizeof(a.cand_valid));
   for (int b = 0; b < kMaxBatch; ++b) {  // each chunk keeps min(m, its valid positions)
     int64_t v = 0;
-    for (int c = 0; c < cp.G && have_cand; ++c) {
-      int64_t cnt = (int64_t)lens.n[b] - (int64_t)c * cp.P;
-      cnt = cnt < 0 ? 0 : (cnt > cp.P ? cp.P : cnt);
+    for (int c = 0; c < cp.G && have_cand && lens.n[b] > 0; ++c) {
+      int cnt;
+      row_chunk_units(lens.n[b], c, cp.G, cp.P, cp.ilv, &cnt);
       v += cnt < cp.m ? cnt : cp.m;
     }
     a.cand_valid.n[b] = (int32_t)v;
@@ -309,7 +315,7 @@ dsa_status dsa_index_scores(const int8_t* iq, const int8_t* iw, const int8_t* ik
   if (st != DSA_OK) return st;
   if ((st = check_index(iq, iw, ik, Hi, Di)) != DSA_OK) return st;
   if (!scores || !aligned(scores, 4)) return DSA_ERR_INVALID_ARG;
-  ChunkPlan cp{64, 1, 32};
+  ChunkPlan cp{64, 1, 32, 0};
   return run_scores(iq, iw, ik, lens, B, Hi, Di, N, nmax, scores, false, cp, nullptr, nullptr,
                     stream);
 }
@@ -326,7 +332,7 @@ dsa_status dsa_topk_select(const int32_t* scores, const int32_t* ctx_len, int B,
   const Layout L = layout(B, N, k, 1, 1);
   if ((st = check_ws(ws, ws_bytes, L)) != DSA_OK) return st;
   uint8_t* w = static_cast<uint8_t*>(ws);
-  const ChunkPlan cp = chunk_plan(nmax, k, false);
+  const ChunkPlan cp = chunk_plan(nmax, k, false, 0);
   const bool have = cand_fits(0, 32, B, cp, false) && !(flags & DSA_FLAG_FORCE_FALLBACK);
   if (have) {
     CandArgs ca;
@@ -388,7 +394,7 @@ dsa_status dsa_decode_step_timed(const int8_t* iq, const int8_t* iw, const int8_
     for (int i = 0; i < 3; ++i) tm[i] = KTimer{kernel_events[2 * i], kernel_events[2 * i + 1]};
   }
   uint8_t* w = static_cast<uint8_t*>(ws);
-  const ChunkPlan cp = chunk_plan(nmax, k, B == 1);
+  const ChunkPlan cp = chunk_plan(nmax, k, B == 1, Di);
   const bool have = cand_fits(Hi, Di, B, cp, true) && !(flags & DSA_FLAG_FORCE_FALLBACK);
   st = run_scores(iq, iw, ik, lens, B, Hi, Di, N, nmax, scores, have, cp,
                   reinterpret_cast<uint64_t*>(w + L.cand), reinterpret_cast<uint64_t*>(w + L.xc),

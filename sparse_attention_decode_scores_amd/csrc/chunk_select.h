@@ -20,13 +20,15 @@ struct ChunkSmem {
 // (scores of magnitude below 16 get a bin each). 896 of the 1024 bins are used.
 constexpr int kHistBins = 1024;
 __device__ __forceinline__ uint32_t score_bin(int32_t s) {
-  const uint32_t x = s >= 0 ? (uint32_t)s : ~(uint32_t)s;  // ~s = -s - 1 >= 0
-  uint32_t code = x;
-  if (x >= 16) {
-    const uint32_t e = 31u - (uint32_t)__builtin_clz(x);  // 4 .. 30
-    code = 16u * (e - 3u) + ((x >> (e - 4u)) & 15u);     // 16 .. 447
-  }
-  return s >= 0 ? 448u + code : 447u - code;
+  // x = |s| for s >= 0, ~s = -s - 1 for s < 0. For x >= 16 with top bit e (4 .. 30)
+  // the code is 16(e - 3) + the four bits below it, which is 16·sh + (x >> sh) with
+  // sh = e - 4; below 16, sh clamps to 0 and the code is x. Negative scores mirror.
+  const uint32_t neg = (uint32_t)(s >> 31);  // all ones for s < 0
+  const uint32_t x = (uint32_t)s ^ neg;
+  const uint32_t lz = (uint32_t)__builtin_clz(x | 1u);
+  const uint32_t sh = lz < 27u ? 27u - lz : 0u;
+  const uint32_t code = (sh << 4) + (x >> sh);  // 0 .. 447
+  return 448u + (code ^ neg);                   // s < 0: 447 - code
 }
 
 // Lowest score that score_bin maps to bin b (b < 896).
@@ -48,7 +50,8 @@ __device__ __forceinline__ int32_t bin_floor(uint32_t b) {
 
 constexpr int kWaveStage = 136;  // staging slots per wave for wave_chunk_candidates (m <= 64, + 8 read slack)
 
-// scores: LDS copy of the chunk's scores (entry i is position pos0 + i); count:
+// scores: LDS copy of the chunk's scores, entry i for position
+// pos0 + (i / 32)·ustride + i % 32 (ustride = 32: consecutive positions); count:
 // valid entries (<= 0 means none; at most 16 * BLOCK). Writes entries 0..m-1 of
 // `out` (the m best keys, in position order, 0-padded) and *x_out = the best key not kept
 // (0 if every valid position is kept).
@@ -59,11 +62,12 @@ constexpr int kWaveStage = 136;  // staging slots per wave for wave_chunk_candid
 template <int BLOCK>
 __device__ __forceinline__ void chunk_candidates(const int32_t* scores, int count, uint32_t pos0, int m,
                                  CandOut out, uint64_t* __restrict__ x_out,
-                                 ChunkSmem<BLOCK>& sm) {
+                                 ChunkSmem<BLOCK>& sm, uint32_t ustride = 32) {
   const int tid = threadIdx.x;
+  auto pos = [=](int i) { return pos0 + (uint32_t)(i >> 5) * ustride + (uint32_t)(i & 31); };
   if (count <= m) {
     for (int i = tid; i < m; i += BLOCK)
-      out.put(i, i < count ? make_key(scores[i], pos0 + (uint32_t)i) : 0ull);
+      out.put(i, i < count ? make_key(scores[i], pos(i)) : 0ull);
     if (tid == 0) *x_out = 0;
     return;
   }
@@ -121,7 +125,7 @@ __device__ __forceinline__ void chunk_candidates(const int32_t* scores, int coun
   for (int j = 0; j < kChunkPerThread; ++j) {
     const int i = i0 + j;
     if (j < per && i < count) {
-      const uint64_t key = ((uint64_t)u[j] << 32) | (uint64_t)(0xFFFFFFFFu - (pos0 + (uint32_t)i));
+      const uint64_t key = ((uint64_t)u[j] << 32) | (uint64_t)(0xFFFFFFFFu - pos(i));
       if (u[j] > T) {
         out.put(slot++, key);
       } else if (u[j] == T) {

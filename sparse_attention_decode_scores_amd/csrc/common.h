@@ -106,6 +106,13 @@ __device__ __forceinline__ uint64_t* dsa_trace_lds() {
       dsa_trace_lds()[(kernel) * kTracePhases + (phase)] = __builtin_amdgcn_s_memrealtime(); \
   } while (0)
 #endif
+// per-wave stamp: lane 0 of wave w writes phase (phase0 + w)
+#define DSA_MARK_WAVE(kernel, phase0)                                                        \
+  do {                                                                                       \
+    if ((threadIdx.x & 63) == 0)                                                             \
+      dsa_trace_lds()[(kernel) * kTracePhases + (phase0) + (threadIdx.x >> 6)] =               \
+          __builtin_amdgcn_s_memrealtime();                                                  \
+  } while (0)
 #define DSA_TRACE_FLUSH()                                                                    \
   do {                                                                                       \
     const int blk_ = blockIdx.x + gridDim.x * blockIdx.y;                                    \
@@ -121,6 +128,9 @@ __device__ __forceinline__ uint64_t* dsa_trace_lds() {
   } while (0)
 #define DSA_MARK(kernel, phase) \
   do {                          \
+  } while (0)
+#define DSA_MARK_WAVE(kernel, phase0) \
+  do {                                \
   } while (0)
 #define DSA_TRACE_FLUSH() \
   do {                    \
@@ -175,6 +185,13 @@ __device__ __forceinline__ float wave_reduce_sum_f(float v) {
   }));
 }
 
+// a * b + c on the low 24 bits of a and b (signed), one v_mad_i32_i24.
+__device__ __forceinline__ int mad_i24(int a, int b, int c) {
+  int d;
+  asm("v_mad_i32_i24 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
+
 // Inclusive prefix sum over the wave (lane order).
 __device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
   v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, dpp::kRowShr1, 0xF, 0xF, false);
@@ -212,7 +229,7 @@ constexpr int kRadixBins = 1 << kRadixBits;
 struct RadixSmem {
   uint32_t hist[2][kRadixBins];  // alternate passes; each pass leaves its buffer zeroed
   uint32_t part[16];
-  uint32_t digit, above;
+  uint32_t digit, above, inbin;
 };
 
 // Zeroes both histogram buffers; call once before the first block_select_range
@@ -222,32 +239,56 @@ __device__ __forceinline__ void radix_clear(RadixSmem& sm) {
   for (int i = threadIdx.x; i < 2 * kRadixBins; i += BLOCK) (&sm.hist[0][0])[i] = 0;
 }
 
-// Score-level radix selection. `each(f)` calls f(v) for every value this thread
-// contributes; lo and hi are the smallest and largest of all contributed values.
-// Finds T, the rank-th largest value (1 <= rank <= number of values), and the
-// number of values above T. The digits are 11-bit slices of v - lo, most
-// significant first, over the bit length of hi - lo: each pass spreads the values
-// over up to 2048 bins (values crowding a narrow band still spread out; LDS
-// atomics on one bin serialise), and a range of 2^21 takes two passes. Three
-// barriers per pass. Every thread of the block calls it and gets the same T.
+// block_excl_scan_u32 without its first barrier: for callers whose last
+// barrier already separates every earlier use of `part`. One barrier.
+template <int BLOCK>
+__device__ __forceinline__ uint32_t block_excl_scan_fresh_u32(uint32_t v, uint32_t* part, uint32_t* total) {
+  const uint32_t incl = wave_incl_scan_u32(v);
+  const uint32_t wtot = __builtin_amdgcn_readlane((int)incl, 63);
+  if (lane_id() == 0) part[wave_id()] = wtot;
+  lds_barrier();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < BLOCK / 64; ++w) {
+    const uint32_t s = part[w];
+    before += w < wave_id() ? s : 0u;
+    all += s;
+  }
+  *total = all;
+  return before + incl - v;
+}
+
+// Result of block_narrow: the rank-th largest value lies in [binlo, binhi], which
+// holds `inbin` values; `above` values are larger than binhi.
+struct RadixBin {
+  uint32_t binlo, binhi, above, inbin;
+};
+
+// Score-level radix narrowing. `each(f)` calls f(v) for every value this thread
+// contributes; lo and hi are the smallest and largest of all n contributed values.
+// The digits are 11-bit slices of v - lo, most significant first, over the bit
+// length of hi - lo: each pass spreads the values over up to 2048 bins (values
+// crowding a narrow band still spread out; LDS atomics on one bin serialise) and
+// keeps the bin that holds the rank-th largest value (1 <= rank <= n). Passes stop
+// once that bin holds at most `cap` values, or is a single value (a range of 2^21
+// takes two passes). Three barriers per pass. Every thread of the block calls it
+// and gets the same result; each pass leaves its histogram buffer zeroed.
 template <int BLOCK, class Each>
-__device__ __forceinline__ uint32_t block_select_range(Each each, uint32_t lo, uint32_t hi, int rank,
-                                       uint32_t* above_out, RadixSmem& sm) {
+__device__ __forceinline__ RadixBin block_narrow(Each each, uint32_t lo, uint32_t hi, uint32_t rank, uint32_t n,
+                                                 uint32_t cap, RadixSmem& sm) {
   static_assert(kRadixBins % BLOCK == 0, "bins per thread");
   constexpr int BPT = kRadixBins / BLOCK;
   const int tid = threadIdx.x;
   const uint32_t range = hi - lo;
-  if (range == 0) {  // every value is equal
-    *above_out = 0;
-    return hi;
-  }
+  if (range == 0) return RadixBin{hi, hi, 0u, n};  // every value is equal
+  if (n <= cap) return RadixBin{lo, hi, 0u, n};    // the whole range is one bin
   int shift = 32 - __clz(range);  // low bits of v - lo still undecided
   uint32_t prefix = 0;            // decided high bits of v - lo
-  uint32_t above = 0;
-  uint32_t need = (uint32_t)rank;
+  uint32_t above = 0, inbin = n;
+  uint32_t need = rank;
   int buf = 0;
   bool first = true;
-  while (shift > 0) {
+  while (shift > 0 && inbin > cap) {
     const int nshift = shift > kRadixBits ? shift - kRadixBits : 0;
     uint32_t* hist = sm.hist[buf];
     if (first) {  // every value is in range: no prefix to match (and shift may be 32)
@@ -269,27 +310,40 @@ __device__ __forceinline__ uint32_t block_select_range(Each each, uint32_t lo, u
       own += h[j];
     }
     uint32_t total;
-    const uint32_t before = block_excl_scan_u32<BLOCK>(own, sm.part, &total);
+    // the histogram barrier above separates every earlier reader of sm.part
+    const uint32_t before = block_excl_scan_fresh_u32<BLOCK>(own, sm.part, &total);
     uint32_t ab = total - before - own;  // values in bins above this thread's bins
 #pragma unroll
     for (int j = BPT - 1; j >= 0; --j) {
       if (ab < need && need <= ab + h[j]) {
         sm.digit = tid * BPT + j;
         sm.above = ab;
+        sm.inbin = h[j];
       }
       ab += h[j];
     }
     lds_barrier();
     DSA_MARK(3, 3 + 2 * (shift > kRadixBits ? 0 : 1));
     const uint32_t d = sm.digit, ab2 = sm.above;
+    inbin = sm.inbin;
     need -= ab2;
     above += ab2;
     prefix = (prefix << (shift - nshift)) | d;
     shift = nshift;
     buf ^= 1;
   }
-  *above_out = above;
-  return lo + prefix;
+  const uint32_t binlo = lo + (prefix << shift);  // shift <= 21 after a pass
+  return RadixBin{binlo, binlo + ((1u << shift) - 1u), above, inbin};
+}
+
+// Score-level radix selection: T, the rank-th largest value, and the number of
+// values above T (block_narrow down to a single value).
+template <int BLOCK, class Each>
+__device__ __forceinline__ uint32_t block_select_range(Each each, uint32_t lo, uint32_t hi, int rank,
+                                                       uint32_t* above_out, RadixSmem& sm) {
+  const RadixBin r = block_narrow<BLOCK>(each, lo, hi, (uint32_t)rank, 0xFFFFFFFFu, 0u, sm);
+  *above_out = r.above;
+  return r.binlo;
 }
 
 // Block exchange of per-wave partial results: lane 0 of each wave stores its

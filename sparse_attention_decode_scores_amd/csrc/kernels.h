@@ -43,7 +43,29 @@ struct ScoreArgs {
   int P;           // positions per chunk (multiple of 64; of 32 for the one-row kernel)
   int G;           // chunks per row
   int m;           // candidates kept per chunk
+  int ilv;         // one-row kernel: chunk c holds the row's 32-key units c, c + G, ...
+                   // (else P consecutive positions)
 };
+
+// Geometry of chunk c of a row of n positions in units of 32 positions: with ilv,
+// the chunk holds the row's units c, c + G, c + 2G, ...; otherwise the P / 32
+// consecutive units from c·P / 32 (P a multiple of 32). Returns the chunk's unit
+// count and sets *count to its valid positions (only its last unit can be cut
+// short by the row's end).
+__host__ __device__ inline int row_chunk_units(int n, int c, int G, int P, int ilv, int* count) {
+  const int U = (n + 31) / 32;
+  const int us = ilv ? 1 : P / 32, js = ilv ? G : 1;
+  int units;
+  if (ilv) units = c < U ? (U - c + G - 1) / G : 0;
+  else units = U - c * us < us ? (U - c * us > 0 ? U - c * us : 0) : us;
+  if (units == 0) {
+    *count = 0;
+    return 0;
+  }
+  const int64_t last = 32 * ((int64_t)c * us + (int64_t)(units - 1) * js);  // its last unit's first position
+  *count = 32 * (units - 1) + (n - last < 32 ? (int)(n - last) : 32);
+  return units;
+}
 
 // Query bytes (rows x padded heads x dims) one score launch stages; the launch
 // planner keeps Bg * HP * DI at or below it, and Bg * HP at or below the block size.

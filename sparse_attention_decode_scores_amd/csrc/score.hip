@@ -272,17 +272,19 @@ constexpr int kRowStage = 144;  // >= cap (m + 64 <= 128) + 16 read slack
 struct RowCandSmem {
   uint64_t all[kRowStage];  // staged keys, in order of arrival
   uint32_t nstaged;
+  uint32_t next;            // the chunk's next unclaimed unit
 };
 
 namespace {
 
-// B fragments of unit j (keys 32j .. 32j + 31 of the chunk): lane l holds dims
-// 32kt + 16(l >> 5) .. +15 of key 32j + (l & 31). Raw buffer loads against a
-// resource that covers exactly the chunk's valid keys (zeros past the end).
+// B fragments of the chunk's unit j (keys 32j·js .. 32j·js + 31 from the chunk's
+// first key): lane l holds dims 32kt + 16(l >> 5) .. +15 of the unit's key l & 31.
+// Raw buffer loads against a resource that ends with the chunk's last valid key
+// (zeros past it).
 template <int KT>
-__device__ __forceinline__ void load_unit(v4i (&kf)[KT], __amdgpu_buffer_rsrc_t rs, int j) {
+__device__ __forceinline__ void load_unit(v4i (&kf)[KT], __amdgpu_buffer_rsrc_t rs, int j, int js) {
   const int lane = lane_id();
-  const int off = (kUnit * j + (lane & 31)) * (32 * KT) + 16 * (lane >> 5);
+  const int off = (kUnit * j * js + (lane & 31)) * (32 * KT) + 16 * (lane >> 5);
 #pragma unroll
   for (int kt = 0; kt < KT; ++kt)
     kf[kt] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 32 * kt, 0, 0));
@@ -305,11 +307,18 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(ScoreArgs a) {
   const int c = blockIdx.x, b = a.b0;
   DSA_TRACE_BEGIN();
   DSA_MARK(0, 0);
-  const int64_t cbeg = (int64_t)c * a.P;
-  const int64_t n64 = (int64_t)a.lens.n[b] - cbeg;
-  const int count = n64 > a.P ? a.P : (int)(n64 > 0 ? n64 : 0);  // valid positions of the chunk
-  const int units = (count + kUnit - 1) / kUnit;
-  const int nu = units > wave ? (units - wave + kScoreWaves - 1) / kScoreWaves : 0;  // this wave's units
+  // Chunk c is a set of 32-key units of the row: interleaved (a.ilv), units c, c + G,
+  // c + 2G, ..., so that at any moment the launch streams one contiguous stretch of
+  // keys; otherwise P / 32 consecutive units. Local unit j is row unit c·us + j·js.
+  const int n = a.lens.n[b];
+  const int us = a.ilv ? 1 : a.P / kUnit, js = a.ilv ? a.G : 1;
+  int count;  // valid positions of the chunk
+  const int units = row_chunk_units(n, c, a.G, a.P, a.ilv, &count);
+  const int64_t cbeg = (int64_t)kUnit * c * us;     // the chunk's first position
+  const uint32_t ustride = (uint32_t)(kUnit * js);  // positions from one local unit to the next
+  // local entry i is position cbeg + (i / 32)·ustride + i % 32; span: row positions
+  // from the chunk's first to its last valid one
+  const int span = units > 0 ? (int)((int64_t)(units - 1) * ustride) + (count - kUnit * (units - 1)) : 0;
 
   // A operand: lane l holds head 32mt + (l & 31), dims 32kt + 16(l >> 5) .. +15; lane
   // l also holds the weight of head l (Hi <= 64). Requested before any key.
@@ -325,15 +334,18 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(ScoreArgs a) {
 
   // the histogram is shared by the waves: cleared before any of them adds to it
   for (int i = tid; i < kHistBins; i += kScoreBlock) hist[i] = 0;
-  if (tid == 0) rsm.nstaged = 0;
+  if (tid == 0) {
+    rsm.nstaged = 0;
+    rsm.next = kScoreWaves * D;  // units 0 .. 8D - 1 are requested below, D per wave
+  }
   lds_barrier();
 
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<int8_t*>(a.ik + cbeg * DI), (short)0, count * DI, 0x00020000);
+      const_cast<int8_t*>(a.ik + cbeg * DI), (short)0, span * DI, 0x00020000);
   v4i kb0[KT], kb1[KT], kb2[KT];
-  load_unit<KT>(kb0, rs, wave);
-  load_unit<KT>(kb1, rs, wave + kScoreWaves);
-  if constexpr (D == 3) load_unit<KT>(kb2, rs, wave + 2 * kScoreWaves);
+  load_unit<KT>(kb0, rs, wave, js);
+  load_unit<KT>(kb1, rs, wave + kScoreWaves, js);
+  if constexpr (D == 3) load_unit<KT>(kb2, rs, wave + 2 * kScoreWaves, js);
 
   // weights in accumulator order: value r of tile mt at lane l is head
   // 32mt + 8(r / 4) + 4(l >> 5) + r % 4; padding heads (q = 0) get weight 0
@@ -351,51 +363,69 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(ScoreArgs a) {
       for (int kt = 0; kt < KT; ++kt) qreg[mt][kt] = v4i{0, 0, 0, 0};
   }
 
-  // unit i of this wave (chunk keys 32j .. 32j + 31, j = wave + 8i): scores into LDS
-  // and the histogram; its key registers are then refilled with unit i + D.
-  auto unit = [&](v4i(&kf)[KT], int i) {
-    const int j = wave + kScoreWaves * i;
+  // Unit j of the chunk in buffer kf: scores into LDS and the histogram. The
+  // buffer is refilled with the next unclaimed unit (an LDS counter, so the waves
+  // whose keys come back first take more of the chunk; the requests of the later
+  // waves otherwise queue behind theirs every round) and j becomes that unit, which
+  // is past the chunk's end once every unit is taken (its loads then return zeros).
+  // A buffer whose unit is past the end is only refilled; the refill is issued
+  // on both paths between the products and the rest (an if/else around it would
+  // let the compiler hoist it into fresh registers and copy them back every
+  // iteration, which waits for every load).
+  auto unit = [&](v4i(&kf)[KT], int& j) {
+    uint32_t nxt = 0;
+    if (lane == 0) nxt = atomicAdd(&rsm.next, 1u);  // back during the matrix products
+    const bool live = j < units;                    // uniform over the wave
     v16i acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = v16i{};
+    if (live) {
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          acc[mt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(qreg[mt][kt], kf[kt], acc[mt], 0, 0, 0);
+    }
+    const int jn = __builtin_amdgcn_readfirstlane((int)nxt);
+    load_unit<KT>(kf, rs, jn, js);
+    if (live) {
+      // two independent multiply-add chains (left to itself the compiler pairs the
+      // products with three-input adds, 2.5 instructions per head instead of 2)
+      int p0 = 0, p1 = 0;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
-        acc[mt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(qreg[mt][kt], kf[kt], acc[mt], 0, 0, 0);
-    load_unit<KT>(kf, rs, j + kScoreWaves * D);
-    int part = 0;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int v = acc[mt][r];
-        part += __mul24(wreg[mt][r], v > 0 ? v : 0);
+        for (int r = 0; r < 16; r += 2) {
+          const int v0 = acc[mt][r], v1 = acc[mt][r + 1];
+          p0 = mad_i24(wreg[mt][r], v0 > 0 ? v0 : 0, p0);
+          p1 = mad_i24(wreg[mt][r + 1], v1 > 0 ? v1 : 0, p1);
+        }
+      // lanes l and l ^ 32 hold the same key's other heads: one lane-half swap
+      const int ph = p0 + p1;
+      const auto sw = __builtin_amdgcn_permlane32_swap(ph, ph, false, false);
+      const int part = sw[0] + sw[1];
+      const int p = kUnit * j + (lane & 31);
+      if (lane < 32) {
+        sc[p] = part;
+        if (p < count) atomicAdd(&hist[score_bin(part)], 1u);
       }
-    part += __shfl_xor(part, 32);
-    const int p = kUnit * j + (lane & 31);
-    if (lane < 32) {
-      sc[p] = part;
-      if (p < count) atomicAdd(&hist[score_bin(part)], 1u);
     }
+    j = jn;
   };
 
   DSA_MARK(0, 1);
-  // whole rounds of D units (the buffers rotate by name: a register copy would
-  // wait for its load), then the last nu % D units; every iteration issues the same
-  // loads in the same order, which keeps the compiler's wait counts exact
-  int i = 0;
-  for (; i + D <= nu; i += D) {
-    unit(kb0, i);
-    unit(kb1, i + 1);
-    if constexpr (D == 3) unit(kb2, i + 2);
-  }
-  if (i < nu) {
-    unit(kb0, i);
-    if constexpr (D == 3)
-      if (i + 1 < nu) unit(kb1, i + 1);
+  // The buffers rotate by name (a register copy would wait for its load) and are
+  // taken in the order their loads were issued, every iteration the same, and the
+  // loop only exits at its head. Claimed units increase, so j0 < j1 (< j2)
+  // throughout: once j0 is past the end, so are the others.
+  int j0 = wave, j1 = wave + kScoreWaves, j2 = wave + 2 * kScoreWaves;
+  while (j0 < units) {
+    unit(kb0, j0);
+    unit(kb1, j1);
+    if constexpr (D == 3) unit(kb2, j2);
   }
   DSA_MARK(0, 2);
+  DSA_MARK_WAVE(0, 8);
   lds_barrier();  // every score and histogram count of the chunk is in LDS
   DSA_MARK(0, 3);
 
@@ -406,13 +436,15 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(ScoreArgs a) {
   // resource that covers exactly the chunk's valid positions: the padding is
   // dropped without a branch); nothing waits for these stores
   const __amdgpu_buffer_rsrc_t rsc = __builtin_amdgcn_make_buffer_rsrc(
-      a.scores + (int64_t)b * a.N + cbeg, (short)0, count * 4, 0x00020000);
+      a.scores + (int64_t)b * a.N + cbeg, (short)0, span * 4, 0x00020000);
+  // row position of local entry i, and its offset from the chunk's first position
+  auto rel = [&](int i) { return (uint32_t)(i >> 5) * ustride + (uint32_t)(i & 31); };
   const uint64_t lt = lanemask_lt();
   if (count <= m) {  // every valid position is a candidate
     for (int i = tid; i < m; i += kScoreBlock) {
       const int32_t v = sc[i < units * kUnit ? i : 0];
-      if (i < units * kUnit) __builtin_amdgcn_raw_buffer_store_b32(v, rsc, 4 * i, 0, 0);
-      out.put(i, i < count ? make_key(v, (uint32_t)(cbeg + i)) : 0ull);
+      if (i < units * kUnit) __builtin_amdgcn_raw_buffer_store_b32(v, rsc, 4 * rel(i), 0, 0);
+      out.put(i, i < count ? make_key(v, (uint32_t)cbeg + rel(i)) : 0ull);
     }
     if (tid == 0) *xout = 0;
     DSA_TRACE_FLUSH();
@@ -437,7 +469,7 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(ScoreArgs a) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int i = i0 + tid + kScoreBlock * q;
-      __builtin_amdgcn_raw_buffer_store_b32(v[q], rsc, 4 * i, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(v[q], rsc, 4 * rel(i), 0, 0);
       bal[q] = __ballot(i < count && v[q] >= tlo);
       nb += (uint32_t)__popcll(bal[q]);
     }
@@ -449,7 +481,7 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(ScoreArgs a) {
     for (int q = 0; q < 4; ++q) {
       const int i = i0 + tid + kScoreBlock * q;
       const uint32_t at = slot + (uint32_t)__popcll(bal[q] & lt);
-      if (((bal[q] >> lane) & 1ull) && at < (uint32_t)kRowStage) rsm.all[at] = make_key(v[q], (uint32_t)(cbeg + i));
+      if (((bal[q] >> lane) & 1ull) && at < (uint32_t)kRowStage) rsm.all[at] = make_key(v[q], (uint32_t)cbeg + rel(i));
       slot += (uint32_t)__popcll(bal[q]);
     }
   }
@@ -486,7 +518,7 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(ScoreArgs a) {
     // heavy ties at the threshold: exact radix selection over the chunk's scores
     radix_clear<kScoreBlock>(csm.radix);
     lds_barrier();
-    chunk_candidates<kScoreBlock>(sc, count, (uint32_t)cbeg, m, out, xout, csm);
+    chunk_candidates<kScoreBlock>(sc, count, (uint32_t)cbeg, m, out, xout, csm, ustride);
   }
   DSA_MARK(0, 4);
   DSA_TRACE_FLUSH();

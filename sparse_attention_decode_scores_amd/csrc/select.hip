@@ -8,10 +8,14 @@
 // order either way.
 //  * Candidate path. The score pass left, for every chunk of positions, its m
 //    best keys and the best key it dropped (x_c). Every workgroup of this kernel
-//    loads that candidate union U (at most 8192 keys, LDS resident), finds the
-//    k-th largest key K* of U by radix selection, and checks that no chunk
-//    dropped a key >= K*. When that holds, the top k of the row are exactly the
-//    keys of U that are >= K*; they are compacted in position order.
+//    loads that candidate union U (at most 8192 keys, 16 per thread in
+//    registers), narrows by radix passes over the scores (and, when one score
+//    value holds many keys, over the positions of those keys) to a key range
+//    that holds the k-th largest key K* and at most 256 keys, ranks the keys of
+//    that range among themselves, and checks that no chunk dropped a key >= K*.
+//    When that holds, the top k of the row are exactly the keys of U that are
+//    >= K*: the keys above the range, in union order, then the best of the
+//    range, in key order.
 //  * Exhaustive path ("ambiguous" case: a chunk holds more than m keys at or
 //    above K*, which happens when many positions tie at the threshold; or the
 //    flag forces it): the top-k set comes from a radix selection over every
@@ -22,8 +26,10 @@
 //  * ranking workgroups order the selected keys: each takes a slice and counts,
 //    for each of its keys, how many selected keys are larger; that count is the
 //    output slot (keys are distinct, so the slots are a permutation);
-//  * attention workgroups each take a slice of the selected positions (in position
-//    order, identical on both paths) and write one split of the attention.
+//  * attention workgroups each take a slice of the selected positions, in the
+//    order the selection produced them (that order differs between the two paths,
+//    which changes only the rounding of the attention), and write one split of
+//    the attention.
 #include "attn_body.h"
 #include "chunk_select.h"
 #include "kernels.h"
@@ -168,8 +174,13 @@ struct SelSmem {
   uint32_t xch[kSelWaves][5];
   uint64_t mxw[kSelWaves];  // per wave: the best key a chunk left out
   uint64_t kstar;
+  uint32_t tied;
 };
 static_assert(kUPerThread == 16 && kSelBlock == 512, "cand_slot layout: 512 threads x 16 entries");
+
+// Once the radix bin that holds the k-th best candidate has at most this many
+// keys, they are ranked among themselves instead of narrowed further.
+constexpr uint32_t kMaxBinRank = 256;
 
 // Exchanges (sum, min, max, max64) over the block in one round.
 struct Stats4 {
@@ -278,42 +289,75 @@ __device__ __forceinline__ uint64_t select_row_exhaustive(const int32_t* __restr
   return sm.kstar;
 }
 
-// write_selected for one batch of E keys per thread with their score bits sv and
-// presence mask already extracted (32-bit tests, writes predicated rather than
-// branched per key).
+// Splits the candidates held E per thread around the key range [klo, khi]: keys
+// above it go to sel, keys in it to bin, both in union order. Every key is
+// written, the others to this thread's slot of sink (one computed address per key
+// and no branch: per-key branches cost more than the stores). One barrier.
 template <int E>
-__device__ __forceinline__ void write_selected_u(const uint64_t (&key)[E], const uint32_t (&sv)[E],
-                                                 uint32_t vmask, uint32_t T, uint32_t need_eq,
-                                                 uint64_t* sel, SelSmem& sm, uint32_t* tot_sel,
-                                                 uint32_t* tot_eq) {
-  uint32_t gt = 0, eq = 0;
+__device__ __forceinline__ void split_at_bin(const uint64_t (&key)[E], uint32_t vmask, uint64_t klo,
+                                             uint64_t khi, uint64_t* sel, uint64_t* bin, uint64_t* sink,
+                                             SelSmem& sm) {
+  uint32_t up = 0, in = 0;
 #pragma unroll
   for (int j = 0; j < E; ++j) {
     const bool v = (vmask >> j) & 1u;
-    gt += v && sv[j] > T ? 1u : 0u;
-    eq += v && sv[j] == T ? 1u : 0u;
+    up += v && key[j] > khi ? 1u : 0u;
+    in += v && key[j] >= klo && key[j] <= khi ? 1u : 0u;
   }
   uint32_t total;
-  const uint32_t before = block_excl_scan_u32<kSelBlock>(gt | (eq << 16), sm.radix.part, &total);
-  uint32_t eqr = before >> 16;  // keys at T in earlier threads
-  uint32_t slot = (before & 0xFFFF) + (eqr < need_eq ? eqr : need_eq);
+  // the caller's last barrier separates every earlier reader of the scan slots
+  const uint32_t before = block_excl_scan_fresh_u32<kSelBlock>(up | (in << 16), sm.radix.part, &total);
+  uint32_t su = before & 0xFFFF, si = before >> 16;
+  uint64_t* const mine = sink + threadIdx.x;
 #pragma unroll
   for (int j = 0; j < E; ++j) {
     const bool v = (vmask >> j) & 1u;
-    const bool at_t = v && sv[j] == T;
-    const bool take = (v && sv[j] > T) || (at_t && eqr < need_eq);
-    if (take) sel[slot] = key[j];
-    if (at_t && eqr == need_eq - 1) sm.kstar = key[j];
-    slot += take ? 1u : 0u;
-    eqr += at_t ? 1u : 0u;
+    const bool a = v && key[j] > khi;
+    const bool b = v && key[j] >= klo && !a;
+    *(a ? sel + su : (b ? bin + si : mine)) = key[j];
+    su += a ? 1u : 0u;
+    si += b ? 1u : 0u;
   }
-  const uint32_t teq = total >> 16;
-  *tot_sel = (total & 0xFFFF) + (teq < need_eq ? teq : need_eq);
-  *tot_eq = teq;
+}
+
+// Ranks the n keys of bin among themselves (rank = number of larger keys; keys
+// are distinct, so the ranks are a permutation) and writes the need best to
+// out[rank], best first; the one of rank need - 1 (the k-th best overall) goes to
+// sm.kstar and the number of taken keys with its score to sm.tied. Eight threads
+// per key.
+__device__ __forceinline__ void rank_bin(const uint64_t* bin, uint32_t n, uint32_t need, uint64_t* out,
+                                         SelSmem& sm) {
+  const int g = threadIdx.x >> 3, part = threadIdx.x & 7;
+  for (uint32_t base = 0; base < n; base += kSelBlock / 8) {
+    const uint32_t i = base + (uint32_t)g;
+    const uint64_t me = i < n ? bin[i] : ~0ull;
+    uint32_t r = 0, te = 0;
+    for (uint32_t j = (uint32_t)part; j < n; j += 8) {
+      const uint64_t v = bin[j];
+      const bool gtr = v > me;
+      r += gtr ? 1u : 0u;
+      te += gtr && (uint32_t)(v >> 32) == (uint32_t)(me >> 32) ? 1u : 0u;
+    }
+    // sums over the eight threads of this key
+    r += (uint32_t)__builtin_amdgcn_mov_dpp((int)r, dpp::kQuadXor1, 0xF, 0xF, false);
+    te += (uint32_t)__builtin_amdgcn_mov_dpp((int)te, dpp::kQuadXor1, 0xF, 0xF, false);
+    r += (uint32_t)__builtin_amdgcn_mov_dpp((int)r, dpp::kQuadXor2, 0xF, 0xF, false);
+    te += (uint32_t)__builtin_amdgcn_mov_dpp((int)te, dpp::kQuadXor2, 0xF, 0xF, false);
+    r += (uint32_t)__builtin_amdgcn_mov_dpp((int)r, dpp::kRowHalfMirror, 0xF, 0xF, false);
+    te += (uint32_t)__builtin_amdgcn_mov_dpp((int)te, dpp::kRowHalfMirror, 0xF, 0xF, false);
+    if (part == 0 && i < n && r < need) {
+      out[r] = me;
+      if (r == need - 1) {
+        sm.kstar = me;
+        sm.tied = te + 1;
+      }
+    }
+  }
 }
 
 // LDS: SelSmem | selected keys [k] | region: the attention working set, or the
-// sort state of the exhaustive path (the two roles never need both).
+// sort state of the exhaustive path (the two roles never need both); on the
+// candidate path it first holds the keys of the k-th key's radix bin.
 template <class Attn>
 __global__ __launch_bounds__(kSelBlock) void k_select(SelArgs a, AttnArgs at) {
   extern __shared__ __align__(16) uint8_t smem[];
@@ -398,15 +442,43 @@ __global__ __launch_bounds__(kSelBlock) void k_select(SelArgs a, AttnArgs at) {
       for (int j = 0; j < kUPerThread; ++j)
         if ((vmask >> j) & 1u) f(sv[j]);
     };
-    uint32_t above;
-    const uint32_t T = block_select_range<kSelBlock>(each, rng[0], rng[1], (int)kk, &above, sm.radix);
-    const uint32_t need_eq = kk - above;
+    // radix passes until the bin of the kk-th best key is small
+    const RadixBin rb = block_narrow<kSelBlock>(each, rng[0], rng[1], kk, nvalid, kMaxBinRank, sm.radix);
     DSA_MARK(1, 2);
-    uint32_t ts, te;
-    write_selected_u<kUPerThread>(key, sv, vmask, T, need_eq, sel, sm, &ts, &te);
     const uint64_t wmx = wave_maxr_u64(mx);
+    // the key range that holds the kk-th best key: the keys above it are taken
+    uint64_t klo = (uint64_t)rb.binlo << 32, khi = ((uint64_t)rb.binhi << 32) | 0xFFFFFFFFull;
+    uint32_t above = rb.above, inbin = rb.inbin, tie_above = 0;
+    if (rb.inbin > kMaxBinRank) {  // uniform: one score value T holds that many keys
+      // the same narrowing over the low key words of the keys at T (a larger low
+      // word is an earlier position)
+      const uint32_t T = rb.binlo;
+      auto each_tie = [&](auto f) {
+#pragma unroll
+        for (int j = 0; j < kUPerThread; ++j)
+          if (((vmask >> j) & 1u) && sv[j] == T) f((uint32_t)key[j]);
+      };
+      const RadixBin rt =
+          block_narrow<kSelBlock>(each_tie, 0u, 0xFFFFFFFFu, kk - rb.above, rb.inbin, kMaxBinRank, sm.radix);
+      klo = ((uint64_t)T << 32) | rt.binlo;
+      khi = ((uint64_t)T << 32) | rt.binhi;
+      above += rt.above;
+      inbin = rt.inbin;
+      tie_above = rt.above;
+    }
+    DSA_MARK(3, 11);
+    // the keys above the range are taken in union order, then the range's best in
+    // key order (equal scores: ascending positions)
+    uint64_t* bin = reinterpret_cast<uint64_t*>(region);
+    split_at_bin<kUPerThread>(key, vmask, klo, khi, sel, bin, bin + kMaxBinRank, sm);
+    DSA_MARK(3, 12);
     if (lane_id() == 0) sm.mxw[wave_id()] = wmx;
     lds_barrier();
+    DSA_MARK(3, 13);
+    rank_bin(bin, inbin, kk - above, sel + above, sm);
+    DSA_MARK(3, 14);
+    lds_barrier();
+    const uint32_t tie = tie_above + sm.tied;
     DSA_MARK(1, 3);
     kstar = sm.kstar;
     mx = 0;
@@ -416,7 +488,7 @@ __global__ __launch_bounds__(kSelBlock) void k_select(SelArgs a, AttnArgs at) {
     const bool ok = mx < kstar && (nvalid >= (uint32_t)a.k || mx == 0);
     if (ok) {
       nsel = kk;
-      tied = need_eq;
+      tied = tie;
     } else {
       reason = 2;
     }
@@ -529,6 +601,8 @@ __global__ __launch_bounds__(kSelBlock) void k_select(SelArgs a, AttnArgs at) {
   }
   DSA_TRACE_FLUSH();
 }
+
+static_assert(sizeof(SortSmem) >= (kMaxBinRank + kSelBlock) * 8, "bin keys and sink slots fit the LDS region");
 
 template <class Attn>
 static size_t select_lds_t(int Hq, int Dk, int k) {

@@ -23,10 +23,14 @@ is synthetic with the shapes of the model's DSA layers):
   ctx300k_tiepool   ctx300k with every key row drawn from a pool of 512 rows, so that
                     many positions share a score exactly (ties at the threshold).
   ctx16k_zeroquery  ctx16k with an all-zero indexer query: every score is 0.
+  ctx16k_hotstride  ctx16k with the key rows of every 256th block of 32 positions
+                    (positions 0-31 and 8,192-8,223) replaced by the indexer query of
+                    row 0, head 0: those 64 positions tie at one score that only about
+                    120 other positions exceed, so all 64 are in the top 2,048.
 
 Integer ranges are inclusive. Seeds (numpy PCG64 ``default_rng(seed)``): tiny_4k
 1000, ctx16k 1001, ctx300k 1003, verify8_ctx131k 1004, ctx300k_tiepool 1030,
-ctx16k_zeroquery 1090, and 2000 + l for layer l of ctx62k_11layers; the integer
+ctx16k_zeroquery 1090, ctx16k_hotstride 1091, and 2000 + l for layer l of ctx62k_11layers; the integer
 arrays are drawn from it in the order iq, iw, ik. The normal arrays are drawn in
 blocks of 16,384 rows, block j of q from ``default_rng([seed, 1, j])`` and of kv
 from ``default_rng([seed, 2, j])`` (so they can be drawn on several threads).
@@ -48,6 +52,7 @@ CONFIGS = {
     "verify8_ctx131k": dict(_LAYER, B=8, N=131072, k=2048, seed=1004, verify_offsets=True),
     "ctx300k_tiepool": dict(_LAYER, B=1, N=300000, k=2048, key_range=2, seed=1030, key_pool=512),
     "ctx16k_zeroquery": dict(_LAYER, B=1, N=16384, k=2048, seed=1090, zero_query=True),
+    "ctx16k_hotstride": dict(_LAYER, B=1, N=16384, k=2048, seed=1091, hot_stride=256),
 }
 
 
@@ -127,6 +132,10 @@ def make(name, layer=0):
         ik = rng.integers(-kr, kr + 1, size=(N, Di), dtype=np.int8)
     if c.get("zero_query"):
         iq[...] = 0
+    if c.get("hot_stride"):
+        blocks = np.arange(N) // 32
+        ik = ik.copy()
+        ik[blocks % c["hot_stride"] == 0] = iq[0, 0]
     mul = 1.0 if c["dtype"] == "f32" else 0.5
     seed = c["seed"] + layer
     q = _normal(seed, 1, (B, Hq, Dk), c["dtype"], mul)
