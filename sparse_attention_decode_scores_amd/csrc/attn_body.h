@@ -41,6 +41,36 @@ __device__ __forceinline__ void softmax_update(float* lg, int sb, int nheads, fl
   }
 }
 
+// The same update for 32-row sub-blocks from partial logits: the logit of head
+// h, row r is scale * sum over q < parts of lgp[(q * hp + h) * 32 + r] (summed in
+// that order), -inf for rows whose bit in `live` is clear; lg receives the
+// probabilities. Each wave takes two heads at once, one per 32-lane half.
+__device__ __forceinline__ void softmax_update_parts32(const float* lgp, int parts, int hp, uint64_t live,
+                                                       float scale, float* lg, int nheads, float* mrun,
+                                                       float* lrun, float* alpha) {
+  const int lane = lane_id(), r = lane & 31;
+  const bool in = (live >> r) & 1ull;
+  for (int h0 = wave_id(); h0 < nheads; h0 += 2 * kAttnWaves) {
+    const int h = h0 + kAttnWaves * (lane >> 5);
+    const bool hv = h < nheads;
+    const int hc = hv ? h : h0;  // a present head (its result is discarded)
+    const float mo = mrun[hc];
+    float t = 0.f;
+    for (int q = 0; q < parts; ++q) t += lgp[(q * hp + hc) * 32 + r];
+    const float v = in && hv ? t * scale : -INFINITY;
+    const float mn = fmaxf(mo, half_reduce_max_f(v));
+    const float p = v == -INFINITY ? 0.f : __expf(v - mn);
+    if (hv) lg[h * 32 + r] = p;
+    const float sum = half_reduce_sum_f(p);
+    if (r == 0 && hv) {
+      const float a = mo == -INFINITY ? 0.f : __expf(mo - mn);
+      lrun[h] = lrun[h] * a + sum;
+      mrun[h] = mn;
+      alpha[h] = a;
+    }
+  }
+}
+
 // bf16 inputs on the matrix cores (v_mfma_f32_16x16x32_bf16): logits = Q K^T with
 // 16 heads per tile as the A operand and 16 staged rows per tile as the B
 // operand; output = P V with P split into two bf16 terms (high part exact,
@@ -53,13 +83,17 @@ struct AttnMfma {
   static constexpr int kMaxLoads = 9;                       // 16-byte loads per thread per sub-block
   static constexpr int kLogitBatch = HQT == 1 ? 6 : (HQT == 2 ? 4 : 2);  // k-steps loaded together
   static constexpr bool kQInLds = HQT == 1;                 // query heads staged in LDS
+  static constexpr int kTiles = SB / 16;                    // 16-row tiles of a sub-block
+  static constexpr int kParts = kAttnWaves / kTiles;        // waves per tile, each a share of the k-steps
+  static_assert(SB == 32 && kAttnWaves % kTiles == 0, "32-row sub-blocks (the softmax takes one row per lane of a half-wave)");
   __host__ __device__ static int row_bytes(int Dk) { return Dk * 2 + 16; }
   __host__ __device__ static size_t q_bytes(int Dk) {
     return kQInLds ? align16((size_t)HP * row_bytes(Dk)) : 0;
   }
   __host__ __device__ static size_t lds_bytes(int Hq, int Dk) {
     (void)Hq;
-    return q_bytes(Dk) + align16((size_t)SB * row_bytes(Dk)) + (size_t)HP * SB * 4 + 3 * HP * 4;
+    return q_bytes(Dk) + align16((size_t)SB * row_bytes(Dk)) + (size_t)HP * SB * 4 + 3 * HP * 4 +
+           (size_t)kParts * HP * SB * 4;
   }
 
   // The row's query heads travel in two steps: load_q requests them into registers
@@ -128,12 +162,12 @@ struct AttnMfma {
     }
   }
 
-  // LDS working set: [query heads (kQInLds)] [SB staged rows] [logits HP x SB]
-  // [running max, sum, rescale per head].
+  // LDS working set: [query heads (kQInLds)] [SB staged rows] [probabilities HP x SB]
+  // [running max, sum, rescale per head] [partial logits kParts x HP x SB].
   struct Work {
     const uint8_t* qs;
     uint8_t* rows;
-    float *lg, *mrun, *lrun, *alpha;
+    float *lg, *mrun, *lrun, *alpha, *lgp;
   };
   __device__ static Work work_of(const AttnArgs& p, uint8_t* work) {
     Work w;
@@ -143,6 +177,7 @@ struct AttnMfma {
     w.mrun = w.lg + HP * SB;
     w.lrun = w.mrun + HP;
     w.alpha = w.lrun + HP;
+    w.lgp = w.alpha + HP;
     return w;
   }
   typedef v4f Acc[HQT][kMaxTilesPerWave];
@@ -197,8 +232,13 @@ struct AttnMfma {
     const __bf16* q = reinterpret_cast<const __bf16*>(p.q) + (int64_t)b * p.Hq * Dk;
     lds_barrier();
     DSA_MARK(1, 6);
-    // logits: D[head][row], head = 16*mt + 4*(l/16) + r, row = 16*nt + l%16
-    for (int nt = wave; nt < SB / 16; nt += kAttnWaves) {
+    // logits: D[head][row], head = 16*mt + 4*(l/16) + r, row = 16*nt + l%16. Wave w
+    // takes row tile w % kTiles and the w / kTiles-th share of the k-steps (every
+    // wave works; one wave per tile would chain all k-steps), and writes its
+    // partial sums; the softmax adds the shares in a fixed order.
+    {
+      const int nt = wave % kTiles, kq = wave / kTiles;
+      const int ks0 = KS * kq / kParts, ks1 = KS * (kq + 1) / kParts;
       v4f acc[HQT];
 #pragma unroll
       for (int mt = 0; mt < HQT; ++mt) acc[mt] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -211,12 +251,12 @@ struct AttnMfma {
         return *(const v8bf*)(q + (int64_t)h * Dk + 32 * kk + 8 * (lane >> 4));
       };
       // fragments of kLogitBatch k-steps are loaded before their matrix-core steps
-      for (int k0 = 0; k0 < KS; k0 += kLogitBatch) {
+      for (int k0 = ks0; k0 < ks1; k0 += kLogitBatch) {
         v8bf bfrag[kLogitBatch];
         v8bf afr[HQT][kLogitBatch];
 #pragma unroll
         for (int t = 0; t < kLogitBatch; ++t) {
-          if (k0 + t < KS) {
+          if (k0 + t < ks1) {
             bfrag[t] = *(const v8bf*)(rrow + 64 * (k0 + t));
 #pragma unroll
             for (int mt = 0; mt < HQT; ++mt) afr[mt][t] = afrag(mt, k0 + t);
@@ -224,7 +264,7 @@ struct AttnMfma {
         }
 #pragma unroll
         for (int t = 0; t < kLogitBatch; ++t) {
-          if (k0 + t < KS) {
+          if (k0 + t < ks1) {
 #pragma unroll
             for (int mt = 0; mt < HQT; ++mt) {
               v8bf a = afr[mt][t];
@@ -235,15 +275,14 @@ struct AttnMfma {
         }
       }
       const int row = 16 * nt + (lane & 15);
-      const bool in = (live >> row) & 1ull;
 #pragma unroll
       for (int mt = 0; mt < HQT; ++mt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) w.lg[(16 * mt + 4 * (lane >> 4) + r) * SB + row] = in ? acc[mt][r] * p.scale : -INFINITY;
+        for (int r = 0; r < 4; ++r) w.lgp[(kq * HP + 16 * mt + 4 * (lane >> 4) + r) * SB + row] = acc[mt][r];
     }
     lds_barrier();
     DSA_MARK(1, 7);
-    softmax_update(w.lg, SB, HP, w.mrun, w.lrun, w.alpha);
+    softmax_update_parts32(w.lgp, kParts, HP, live, p.scale, w.lg, HP, w.mrun, w.lrun, w.alpha);
     lds_barrier();
     DSA_MARK(1, 8);
     // output: D[head][dv] += P[head][row] V[row][dv]

@@ -159,6 +159,28 @@ __device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, Op op) {
   const uint32_t r2 = __builtin_amdgcn_readlane((int)v, 32), r3 = __builtin_amdgcn_readlane((int)v, 48);
   return op(op(r0, r1), op(r2, r3));
 }
+// The same over each 32-lane half of the wave: lanes 0..31 get the reduction of
+// lanes 0..31, lanes 32..63 that of lanes 32..63.
+template <class Op>
+__device__ __forceinline__ uint32_t half_reduce_u32(uint32_t v, Op op) {
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, dpp::kQuadXor1, 0xF, 0xF, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, dpp::kQuadXor2, 0xF, 0xF, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, dpp::kRowHalfMirror, 0xF, 0xF, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, dpp::kRowMirror, 0xF, 0xF, false));
+  const uint32_t r0 = __builtin_amdgcn_readlane((int)v, 0), r1 = __builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane((int)v, 32), r3 = __builtin_amdgcn_readlane((int)v, 48);
+  return lane_id() < 32 ? op(r0, r1) : op(r2, r3);
+}
+__device__ __forceinline__ float half_reduce_max_f(float v) {
+  return __uint_as_float(half_reduce_u32(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+  }));
+}
+__device__ __forceinline__ float half_reduce_sum_f(float v) {
+  return __uint_as_float(half_reduce_u32(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+  }));
+}
 __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
   return wave_reduce_u32(v, [](uint32_t a, uint32_t b) { return a + b; });
 }

@@ -675,7 +675,7 @@ AttnChoice choose_attn(int dt_bf16, int Hq, int Dk, int Dv) {
     c.kind = ATTN_MFMA_BF16;
     c.hqt = (Hq + 15) / 16;
     c.sb = 32;  // a split's 32 rows form one sub-block
-    if ((Dk / 8) * c.sb <= AttnMfma<1, 64>::kMaxLoads * kAttnBlock) return c;  // one gather pass
+    if ((Dk / 8) * c.sb <= AttnMfma<1, 32>::kMaxLoads * kAttnBlock) return c;  // one gather pass
     c = AttnChoice{ATTN_NONE, 0, 0};
   }
   if (Hq >= 1 && Hq * Dv <= 4096 && Dk <= 512 && Dv <= Dk) {
@@ -691,28 +691,15 @@ AttnChoice choose_attn(int dt_bf16, int Hq, int Dk, int Dv) {
     case ATTN_GENERIC_F32: return FN<AttnGeneric<float>>(__VA_ARGS__);                 \
     case ATTN_GENERIC_BF16: return FN<AttnGeneric<uint16_t>>(__VA_ARGS__);             \
     case ATTN_MFMA_BF16:                                                               \
-      if (ch.sb == 64) {                                                               \
-        switch (ch.hqt) {                                                              \
-          case 1: return FN<AttnMfma<1, 64>>(__VA_ARGS__);                             \
-          case 2: return FN<AttnMfma<2, 64>>(__VA_ARGS__);                             \
-          case 3: return FN<AttnMfma<3, 64>>(__VA_ARGS__);                             \
-          case 4: return FN<AttnMfma<4, 64>>(__VA_ARGS__);                             \
-        }                                                                              \
-      } else {                                                                         \
-        switch (ch.hqt) {                                                              \
-          case 1: return FN<AttnMfma<1, 32>>(__VA_ARGS__);                             \
-          case 2: return FN<AttnMfma<2, 32>>(__VA_ARGS__);                             \
-          case 3: return FN<AttnMfma<3, 32>>(__VA_ARGS__);                             \
-          case 4: return FN<AttnMfma<4, 32>>(__VA_ARGS__);                             \
-        }                                                                              \
+      switch (ch.hqt) {                                                                \
+        case 1: return FN<AttnMfma<1, 32>>(__VA_ARGS__);                               \
+        case 2: return FN<AttnMfma<2, 32>>(__VA_ARGS__);                               \
+        case 3: return FN<AttnMfma<3, 32>>(__VA_ARGS__);                               \
+        case 4: return FN<AttnMfma<4, 32>>(__VA_ARGS__);                               \
       }                                                                                \
   }                                                                                    \
   return hipErrorInvalidValue;
 
-using AttnM1x64 = AttnMfma<1, 64>;
-using AttnM2x64 = AttnMfma<2, 64>;
-using AttnM3x64 = AttnMfma<3, 64>;
-using AttnM4x64 = AttnMfma<4, 64>;
 using AttnM1x32 = AttnMfma<1, 32>;
 using AttnM2x32 = AttnMfma<2, 32>;
 using AttnM3x32 = AttnMfma<3, 32>;
@@ -724,14 +711,6 @@ static size_t select_lds_dispatch(AttnChoice ch, int Hq, int Dk, int k) {
     case ATTN_GENERIC_F32: return select_lds_t<AttnGeneric<float>>(Hq, Dk, k);
     case ATTN_GENERIC_BF16: return select_lds_t<AttnGeneric<uint16_t>>(Hq, Dk, k);
     case ATTN_MFMA_BF16:
-      if (ch.sb == 64) {
-        switch (ch.hqt) {
-          case 1: return select_lds_t<AttnM1x64>(Hq, Dk, k);
-          case 2: return select_lds_t<AttnM2x64>(Hq, Dk, k);
-          case 3: return select_lds_t<AttnM3x64>(Hq, Dk, k);
-          default: return select_lds_t<AttnM4x64>(Hq, Dk, k);
-        }
-      }
       switch (ch.hqt) {
         case 1: return select_lds_t<AttnM1x32>(Hq, Dk, k);
         case 2: return select_lds_t<AttnM2x32>(Hq, Dk, k);
