@@ -211,8 +211,9 @@ __device__ __forceinline__ bool hist_threshold(const uint32_t* hist, int count, 
 //  2. every key scoring at least that bin's lowest score is staged in LDS in
 //     position order (ballot compaction): the keys of higher bins (fewer than m+1)
 //     plus that bin's keys;
-//  3. each staged key is ranked against the others; the m best, in staging order,
-//     are the output and the one of rank m is x, the best key left out.
+//  3. each staged key is ranked against the others; the m best go to the output
+//     slot of their rank (best first) and the one of rank m is x, the best key
+//     left out.
 // Returns false, having written nothing, when more than m + 64 keys are staged
 // (heavy ties) or the histogram does not count `count` keys: the caller then runs
 // chunk_candidates. `stage` is this wave's LDS area of kWaveStage keys.
@@ -277,9 +278,8 @@ __device__ __forceinline__ bool wave_chunk_candidates(const int32_t* scores, int
   // staged keys are distinct, so the ranks are a permutation of 0 .. ns-1
   const bool s0 = l < (int)ns && r0 < (uint32_t)m;
   const bool s1 = l + 64 < (int)ns && r1 < (uint32_t)m;
-  const uint64_t b0 = __ballot(s0), b1 = __ballot(s1);
-  if (s0) out.put((int)__popcll(b0 & lt), k0);
-  if (s1) out.put((int)(__popcll(b0) + __popcll(b1 & lt)), k1);
+  if (s0) out.put((int)r0, k0);  // slot = rank: the list is best first
+  if (s1) out.put((int)r1, k1);
   const uint64_t xb0 = __ballot(l < (int)ns && r0 == (uint32_t)m);
   const uint64_t xb1 = __ballot(l + 64 < (int)ns && r1 == (uint32_t)m);
   const int xl = xb0 ? __builtin_ctzll(xb0) : __builtin_ctzll(xb1);
@@ -309,8 +309,8 @@ struct BlockCandSmem {
 // (threshold_floor); active wave w stages the keys at or above it from its own
 // run of 64-position rows (ballot compaction, position order); the runs are
 // concatenated; two or four threads per staged key count the staged keys above
-// it, which is its rank; wave 0 writes the m best in position order and x = the
-// key of rank m. Returns false (uniformly, nothing written) where
+// it, which is its rank; wave 0 writes the m best to the slot of their rank (best
+// first) and x = the key of rank m. Returns false (uniformly, nothing written) where
 // wave_chunk_candidates does.
 template <int BLOCK>
 __device__ __forceinline__ bool block_chunk_candidates(const int32_t* scores, int count, uint32_t pos0,
@@ -401,15 +401,11 @@ __device__ __forceinline__ bool block_chunk_candidates(const int32_t* scores, in
   DSA_MARK(3, 9);
 
   if (w == 0) {
-    uint32_t base = 0;
     for (int q = 0; q < (int)total; q += 64) {
       const int j = q + l;
       const uint32_t rk = j < (int)total ? sm.rank[j] : ~0u;
-      const bool sel = rk < (uint32_t)m;
-      const uint64_t b = __ballot(sel);
-      if (sel) out.put((int)(base + (uint32_t)__popcll(b & lt)), sm.all[j]);
+      if (rk < (uint32_t)m) out.put((int)rk, sm.all[j]);  // slot = rank: best first
       if (rk == (uint32_t)m) *x_out = sm.all[j];
-      base += (uint32_t)__popcll(b);
     }
   }
   DSA_MARK(3, 10);

@@ -181,6 +181,8 @@ static_assert(kUPerThread == 16 && kSelBlock == 512, "cand_slot layout: 512 thre
 // Once the radix bin that holds the k-th best candidate has at most this many
 // keys, they are ranked among themselves instead of narrowed further.
 constexpr uint32_t kMaxBinRank = 256;
+constexpr int kBinPad = 16;  // LDS slots before the bin's keys (split_sorted's base may point there)
+static_assert(kBinPad >= kUPerThread, "split_sorted: up <= keys per thread");
 
 // Exchanges (sum, min, max, max64) over the block in one round.
 struct Stats4 {
@@ -320,6 +322,32 @@ __device__ __forceinline__ void split_at_bin(const uint64_t (&key)[E], uint32_t 
   }
 }
 
+// split_at_bin for keys that run best first in every thread (absent keys, 0,
+// last): the keys above the range are a prefix of each thread's keys and the
+// range's keys follow, so key j goes to a base chosen by two counts, plus j (one
+// computed address per key, no per-key counters). bin must have kBinPad slots
+// before it, and sink kSelBlock + E.
+template <int E>
+__device__ __forceinline__ void split_sorted(const uint64_t (&key)[E], uint64_t klo, uint64_t khi,
+                                             uint64_t* sel, uint64_t* bin, uint64_t* sink, SelSmem& sm) {
+  const uint64_t klo1 = klo > 0 ? klo : 1;  // a present key is never 0
+  uint32_t up = 0, ge = 0;
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    up += key[j] > khi ? 1u : 0u;
+    ge += key[j] >= klo1 ? 1u : 0u;
+  }
+  uint32_t total;
+  // the caller's last barrier separates every earlier reader of the scan slots
+  const uint32_t before = block_excl_scan_fresh_u32<kSelBlock>(up | ((ge - up) << 16), sm.radix.part, &total);
+  const uint32_t su = before & 0xFFFF, si = before >> 16;
+  uint64_t* const a = sel + su;              // key j < up goes to a[j]
+  uint64_t* const b = bin + si - up;         // key up <= j < ge goes to b[j] (up <= E <= kBinPad)
+  uint64_t* const c = sink + threadIdx.x;    // the others to c[j]
+#pragma unroll
+  for (int j = 0; j < E; ++j) ((uint32_t)j < up ? a : ((uint32_t)j < ge ? b : c))[j] = key[j];
+}
+
 // Ranks the n keys of bin among themselves (rank = number of larger keys; keys
 // are distinct, so the ranks are a permutation) and writes the need best to
 // out[rank], best first; the one of rank need - 1 (the k-th best overall) goes to
@@ -416,23 +444,32 @@ __global__ __launch_bounds__(kSelBlock) void k_select(SelArgs a, AttnArgs at) {
       lo = v && sv[j] < lo ? sv[j] : lo;
       hi = v && sv[j] > hi ? sv[j] : hi;
     }
+    // whether this thread's keys run best first (the score pass's lists do, and
+    // absent keys, 0, come last; lists written in position order do not)
+    bool desc = true;
+#pragma unroll
+    for (int j = 0; j + 1 < kUPerThread; ++j) desc = desc && key[j] >= key[j + 1];
     DSA_MARK(1, 11);
-    // the range of the candidates' scores (its exchange also publishes the cleared
-    // radix histograms); the best dropped key is only needed for the coverage
-    // check, so its load is not waited for here
+    // the range of the candidates' scores and whether every thread's keys run best
+    // first (the exchange also publishes the cleared radix histograms); the best
+    // dropped key is only needed for the coverage check, so its load is not waited
+    // for here
     uint32_t rng[2];
+    bool sorted;
     {
-      const uint32_t mine[2] = {~wave_min_u32(lo), wave_maxr_u32(hi)};
-      uint32_t all[kSelWaves][2];
-      block_exchange<kSelBlock, 2>(mine, reinterpret_cast<uint32_t(*)[2]>(&sm.xch[0][0]), all);
-      uint32_t nlo = 0, mhi = 0;
+      const uint32_t mine[3] = {~wave_min_u32(lo), wave_maxr_u32(hi), __ballot(!desc) != 0 ? 1u : 0u};
+      uint32_t all[kSelWaves][3];
+      block_exchange<kSelBlock, 3>(mine, reinterpret_cast<uint32_t(*)[3]>(&sm.xch[0][0]), all);
+      uint32_t nlo = 0, mhi = 0, unsorted = 0;
 #pragma unroll
       for (int w = 0; w < kSelWaves; ++w) {
         nlo = all[w][0] > nlo ? all[w][0] : nlo;
         mhi = all[w][1] > mhi ? all[w][1] : mhi;
+        unsorted |= all[w][2];
       }
       rng[0] = ~nlo;
       rng[1] = mhi;
+      sorted = unsorted == 0;
     }
     nvalid = (uint32_t)a.cand_valid.n[b];
     DSA_MARK(1, 1);
@@ -469,8 +506,11 @@ __global__ __launch_bounds__(kSelBlock) void k_select(SelArgs a, AttnArgs at) {
     DSA_MARK(3, 11);
     // the keys above the range are taken in union order, then the range's best in
     // key order (equal scores: ascending positions)
-    uint64_t* bin = reinterpret_cast<uint64_t*>(region);
-    split_at_bin<kUPerThread>(key, vmask, klo, khi, sel, bin, bin + kMaxBinRank, sm);
+    uint64_t* bin = reinterpret_cast<uint64_t*>(region) + kBinPad;
+    if (sorted)  // uniform
+      split_sorted<kUPerThread>(key, klo, khi, sel, bin, bin + kMaxBinRank, sm);
+    else
+      split_at_bin<kUPerThread>(key, vmask, klo, khi, sel, bin, bin + kMaxBinRank, sm);
     DSA_MARK(3, 12);
     if (lane_id() == 0) sm.mxw[wave_id()] = wmx;
     lds_barrier();
@@ -537,7 +577,8 @@ __global__ __launch_bounds__(kSelBlock) void k_select(SelArgs a, AttnArgs at) {
     kstar = select_row_exhaustive(row, n, kk, sel, &tied, sm);
     nsel = (uint32_t)kk;
   }
-  lds_barrier();
+  // sel is complete and published on both paths (the last barrier of either
+  // selection follows its last write), and the LDS region is free again
   DSA_MARK(1, 4);
 
   if (attn_role) {
@@ -602,7 +643,8 @@ __global__ __launch_bounds__(kSelBlock) void k_select(SelArgs a, AttnArgs at) {
   DSA_TRACE_FLUSH();
 }
 
-static_assert(sizeof(SortSmem) >= (kMaxBinRank + kSelBlock) * 8, "bin keys and sink slots fit the LDS region");
+static_assert(sizeof(SortSmem) >= (kBinPad + kMaxBinRank + kSelBlock + kUPerThread) * 8,
+              "bin keys and sink slots fit the LDS region");
 
 template <class Attn>
 static size_t select_lds_t(int Hq, int Dk, int k) {
