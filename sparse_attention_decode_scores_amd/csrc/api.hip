@@ -32,7 +32,7 @@ int rankers_for(int k) {
 
 // Byte offsets of the workspace regions.
 struct Layout {
-  size_t stats, cand, xc, ml, o, bad, sort, total;
+  size_t stats, cand, xc, sums, ml, o, bad, sort, total;
 };
 Layout layout(int B, int64_t N, int k, int Hq, int Dv) {
   const int S = splits_for(k, true);  // the larger of the two split counts
@@ -40,7 +40,8 @@ Layout layout(int B, int64_t N, int k, int Hq, int Dv) {
   L.stats = 0;
   L.cand = up(sizeof(RowStats) * kMaxBatch);
   L.xc = L.cand + up((size_t)B * kCandCap * 8);
-  L.ml = L.xc + up((size_t)B * kMaxChunks * 8);
+  L.sums = L.xc + up((size_t)B * kMaxChunks * 8);
+  L.ml = L.sums + up((size_t)B * kMaxChunks * sizeof(ChunkSum));
   L.o = L.ml + up((size_t)B * S * Hq * 8);
   L.bad = L.o + up((size_t)B * S * ((Hq + 15) / 16 * 16) * Dv * 4);
   L.sort = L.bad + up((size_t)B * S * 4);
@@ -164,7 +165,7 @@ dsa_status hip_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_
 dsa_status run_scores(const int8_t* iq, const int8_t* iw, const int8_t* ik, const RowLens& lens,
                       int B, int Hi, int Di, int64_t N, int nmax, int32_t* scores, bool cand,
                       const ChunkPlan& cp, uint64_t* cbuf, uint64_t* xbuf, hipStream_t s,
-                      KTimer t = {}) {
+                      KTimer t = {}, ChunkSum* sums = nullptr) {
   ScoreArgs a;
   a.iq = iq;
   a.iw = iw;
@@ -172,6 +173,7 @@ dsa_status run_scores(const int8_t* iq, const int8_t* iw, const int8_t* ik, cons
   a.scores = scores;
   a.cand = cbuf;
   a.xc = xbuf;
+  a.sums = nullptr;
   a.lens = lens;
   a.N = N;
   a.nmax = nmax;
@@ -191,6 +193,7 @@ dsa_status run_scores(const int8_t* iq, const int8_t* iw, const int8_t* ik, cons
     a.b0 = 0;
     a.Bg = 1;
     a.ilv = cp.ilv;
+    a.sums = sums;
     return hip_status(launch_score_row(a, MT, KT, kScoreRowDepth, a.G, s, t));
   }
   const int bg = rows_per_score_launch(Hi, Di, B);
@@ -252,11 +255,13 @@ hipError_t combine(const AttnArgs& at, const int32_t* part_bad, RowStats* stats,
 }
 
 SelArgs sel_args(const int32_t* scores, const RowLens& lens, int64_t N, int k, int32_t* idx,
-                 uint8_t* w, const Layout& L, const ChunkPlan& cp, bool have_cand, unsigned flags) {
+                 uint8_t* w, const Layout& L, const ChunkPlan& cp, bool have_cand, unsigned flags,
+                 bool sums = false) {
   SelArgs a;
   a.scores = scores;
   a.cand = reinterpret_cast<const uint64_t*>(w + L.cand);
   a.xc = reinterpret_cast<const uint64_t*>(w + L.xc);
+  a.sums = sums && have_cand ? reinterpret_cast<const ChunkSum*>(w + L.sums) : nullptr;
   a.idx = idx;
   a.stats = reinterpret_cast<RowStats*>(w + L.stats);
   a.sortbuf = reinterpret_cast<uint64_t*>(w + L.sort);
@@ -396,11 +401,13 @@ dsa_status dsa_decode_step_timed(const int8_t* iq, const int8_t* iw, const int8_
   uint8_t* w = static_cast<uint8_t*>(ws);
   const ChunkPlan cp = chunk_plan(nmax, k, B == 1, Di);
   const bool have = cand_fits(Hi, Di, B, cp, true) && !(flags & DSA_FLAG_FORCE_FALLBACK);
+  // the one-row score pass also leaves per-chunk summaries for the selection
+  const bool sums = have && B == 1;
   st = run_scores(iq, iw, ik, lens, B, Hi, Di, N, nmax, scores, have, cp,
                   reinterpret_cast<uint64_t*>(w + L.cand), reinterpret_cast<uint64_t*>(w + L.xc),
-                  stream, tm[0]);
+                  stream, tm[0], sums ? reinterpret_cast<ChunkSum*>(w + L.sums) : nullptr);
   if (st != DSA_OK) return st;
-  const SelArgs sa = sel_args(scores, lens, N, k, idx, w, L, cp, have, flags);
+  const SelArgs sa = sel_args(scores, lens, N, k, idx, w, L, cp, have, flags, sums);
   AttnArgs at = attn_args(q, kv, N, Hq, Dk, Dv, scale, k, w, L);
   set_attn_path(&at, ch, k);
   if (launch_select(sa, at, ch, B, stream, tm[1]) != hipSuccess) return DSA_ERR_HIP;

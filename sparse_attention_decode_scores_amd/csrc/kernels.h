@@ -28,6 +28,14 @@ inline hipError_t launch_timed(F fn, dim3 grid, dim3 block, size_t lds, hipStrea
   return hipGetLastError();
 }
 
+// Per chunk of the one-row score pass: the lowest and highest score bits of its
+// kept candidates (an empty chunk has lo > hi) and whether its list runs best
+// first. The selection takes the union's range and order from these instead of
+// reducing them over its keys.
+struct ChunkSum {
+  uint32_t lo, hi, ordered, pad;
+};
+
 struct ScoreArgs {
   const int8_t* iq;
   const int8_t* iw;
@@ -35,6 +43,7 @@ struct ScoreArgs {
   int32_t* scores;
   uint64_t* cand;  // [B][kCandCap] candidate union per row (entry c*m + i at cand_slot)
   uint64_t* xc;    // [B][G] best key left out of each chunk
+  ChunkSum* sums;  // one-row kernel: [B][kMaxChunks] chunk summaries, or nullptr
   RowLens lens;
   int64_t N;       // row stride of scores
   int nmax;        // largest ctx_len: positions at or past it are never scored
@@ -116,6 +125,7 @@ struct SelArgs {
   const int32_t* scores;
   const uint64_t* cand;
   const uint64_t* xc;
+  const ChunkSum* sums;  // [B][kMaxChunks] from the one-row score pass, or nullptr
   int32_t* idx;        // [B][k]
   RowStats* stats;     // [B]
   uint64_t* sortbuf;   // [B][2][N] scratch of the exhaustive path

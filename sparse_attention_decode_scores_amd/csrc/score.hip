@@ -447,6 +447,13 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(ScoreArgs a) {
       out.put(i, i < count ? make_key(v, (uint32_t)cbeg + rel(i)) : 0ull);
     }
     if (tid == 0) *xout = 0;
+    if (a.sums != nullptr && wave == 0) {  // m <= 64: the first wave covers the list
+      const bool v = lane < count;
+      const uint32_t u = v ? score_bits(sc[lane]) : 0u;
+      const uint32_t lo = wave_min_u32(v ? u : 0xFFFFFFFFu), hi = wave_maxr_u32(u);
+      // position order: best first only when at most one key is present
+      if (lane == 0) a.sums[(int64_t)b * kMaxChunks + c] = ChunkSum{lo, hi, count <= 1 ? 1u : 0u, 0u};
+    }
     DSA_TRACE_FLUSH();
     return;
   }
@@ -513,12 +520,23 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(ScoreArgs a) {
     if (part == 0 && t < (int)total) {
       if (r < (uint32_t)m) out.put((int)r, me);
       else if (r == (uint32_t)m) *xout = me;
+      if (a.sums != nullptr) {  // the list runs best first: its ends give the range
+        ChunkSum* cs = a.sums + (int64_t)b * kMaxChunks + c;
+        if (r == 0) {
+          cs->hi = key_ubits(me);
+          cs->ordered = 1u;
+        }
+        if (r == (uint32_t)m - 1) cs->lo = key_ubits(me);
+      }
     }
   } else {
     // heavy ties at the threshold: exact radix selection over the chunk's scores
     radix_clear<kScoreBlock>(csm.radix);
     lds_barrier();
     chunk_candidates<kScoreBlock>(sc, count, (uint32_t)cbeg, m, out, xout, csm, ustride);
+    // a list in position order; the whole score range bounds it
+    if (a.sums != nullptr && tid == 0)
+      a.sums[(int64_t)b * kMaxChunks + c] = ChunkSum{0u, 0xFFFFFFFFu, 0u, 0u};
   }
   DSA_MARK(0, 4);
   DSA_TRACE_FLUSH();

@@ -426,6 +426,19 @@ __global__ __launch_bounds__(kSelBlock) void k_select(SelArgs a, AttnArgs at) {
     }
     mx = tid < a.G ? a.xc[(int64_t)b * a.G + tid] : 0ull;
   }
+  // every wave reads all chunk summaries (four per lane; clamped repeats change
+  // neither a minimum, a maximum nor an or)
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 csum[4];
+  const bool have_sums = a.sums != nullptr && reason == 0;  // uniform
+  if (have_sums) {
+    const u32x4* sp = reinterpret_cast<const u32x4*>(a.sums + (int64_t)b * kMaxChunks);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = lane_id() + 64 * i;
+      csum[i] = sp[c < a.G ? c : a.G - 1];
+    }
+  }
   const typename Attn::QFrag qf = Attn::load_q(at, b);  // every workgroup: exact wait counts
   radix_clear<kSelBlock>(sm.radix);
   if (reason == 0) {
@@ -437,6 +450,24 @@ __global__ __launch_bounds__(kSelBlock) void k_select(SelArgs a, AttnArgs at) {
       sv[j] = key_ubits(key[j]);
       vmask |= (uint32_t)key[j] != 0u ? 1u << j : 0u;
     }
+    uint32_t rng[2];
+    bool sorted;
+    if (have_sums) {
+      // the range and order of the union from the chunk summaries, in every wave
+      // (no exchange; one barrier publishes the cleared radix histograms)
+      uint32_t lo = 0xFFFFFFFFu, hi = 0, unordered = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lo = csum[i].x < lo ? csum[i].x : lo;
+        hi = csum[i].y > hi ? csum[i].y : hi;
+        unordered |= csum[i].z == 0u ? 1u : 0u;
+      }
+      rng[0] = wave_min_u32(lo);
+      rng[1] = wave_maxr_u32(hi);
+      sorted = __ballot(unordered != 0u) == 0;
+      lds_barrier();
+      DSA_MARK(1, 11);
+    } else {
     uint32_t lo = 0xFFFFFFFFu, hi = 0;
 #pragma unroll
     for (int j = 0; j < kUPerThread; ++j) {
@@ -454,8 +485,6 @@ __global__ __launch_bounds__(kSelBlock) void k_select(SelArgs a, AttnArgs at) {
     // first (the exchange also publishes the cleared radix histograms); the best
     // dropped key is only needed for the coverage check, so its load is not waited
     // for here
-    uint32_t rng[2];
-    bool sorted;
     {
       const uint32_t mine[3] = {~wave_min_u32(lo), wave_maxr_u32(hi), __ballot(!desc) != 0 ? 1u : 0u};
       uint32_t all[kSelWaves][3];
@@ -470,6 +499,7 @@ __global__ __launch_bounds__(kSelBlock) void k_select(SelArgs a, AttnArgs at) {
       rng[0] = ~nlo;
       rng[1] = mhi;
       sorted = unsorted == 0;
+    }
     }
     nvalid = (uint32_t)a.cand_valid.n[b];
     DSA_MARK(1, 1);
