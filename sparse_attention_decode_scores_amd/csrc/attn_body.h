@@ -103,6 +103,7 @@ struct AttnMfma {
   struct QFrag {
     v4i v[kQInLds ? kQPer : 1];
     int rr[kMaxLoads], cc[kMaxLoads];  // gather slot j of this thread: row, 16-byte column
+    int lo[kMaxLoads];                 // its LDS byte offset among the staged rows
   };
   __device__ static QFrag load_q(const AttnArgs& p, int b) {
     QFrag f;
@@ -118,6 +119,7 @@ struct AttnMfma {
       for (int j = 0; j < kMaxLoads; ++j) {
         f.rr[j] = r;
         f.cc[j] = c;
+        f.lo[j] = r * row_bytes(p.Dk) + 16 * c;
         c += step_c;
         r += step_r;
         if (c >= cpr) {
@@ -125,6 +127,10 @@ struct AttnMfma {
           ++r;
         }
       }
+      // computed here, while the kernel waits for its first loads: the empty asm
+      // keeps the compiler from recomputing them where they are used
+#pragma unroll
+      for (int j = 0; j < kMaxLoads; ++j) asm volatile("" : "+v"(f.rr[j]), "+v"(f.cc[j]), "+v"(f.lo[j]));
     }
     if (!kQInLds) return f;
     const int Dk = p.Dk, cpr = Dk >> 3;
@@ -209,7 +215,7 @@ struct AttnMfma {
 #pragma unroll
     for (int j = 0; j < kMaxLoads; ++j)
       if ((int)threadIdx.x + kAttnBlock * j < nch)
-        *(v4i*)(w.rows + qf.rr[j] * rb + 16 * qf.cc[j]) = qf.rr[j] < nr ? r.v[j] : v4i{0, 0, 0, 0};
+        *(v4i*)(w.rows + qf.lo[j]) = qf.rr[j] < nr ? r.v[j] : v4i{0, 0, 0, 0};
   }
   __device__ static void begin(const AttnArgs& p, uint8_t* work, Acc& o) {
     const Work w = work_of(p, work);
@@ -224,8 +230,11 @@ struct AttnMfma {
   }
 
   // One staged sub-block: row r takes part iff bit r of `live` is set. Logits on
-  // the matrix cores, online-softmax update, then P V accumulated into o.
-  __device__ static void sub_block(const AttnArgs& p, int b, uint64_t live, uint8_t* work, Acc& o) {
+  // the matrix cores, online-softmax update, then P V accumulated into o. With
+  // `last`, no barrier follows (nothing overwrites the staged rows afterwards, and
+  // finish reads only what the softmax barrier published).
+  __device__ static void sub_block(const AttnArgs& p, int b, uint64_t live, uint8_t* work, Acc& o,
+                                   bool last) {
     const int lane = lane_id(), wave = wave_id();
     const int Dk = p.Dk, KS = Dk >> 5, rb = row_bytes(Dk), nt_all = p.Dv >> 4;
     const Work w = work_of(p, work);
@@ -342,7 +351,7 @@ struct AttnMfma {
         }
       }
     }
-    lds_barrier();
+    if (!last) lds_barrier();  // uniform
     DSA_MARK(1, 9);
   }
 
@@ -380,7 +389,7 @@ struct AttnMfma {
       DSA_MARK(1, 13);
       put(r, qf, p, nr, s0 == 0, work);
       DSA_MARK(1, 14);
-      sub_block(p, b, nr >= 64 ? ~0ull : (1ull << nr) - 1ull, work, o);
+      sub_block(p, b, nr >= 64 ? ~0ull : (1ull << nr) - 1ull, work, o, s0 + SB >= cnt);
     }
     finish(p, b, split, work, o);
   }
