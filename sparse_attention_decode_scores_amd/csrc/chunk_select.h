@@ -19,6 +19,8 @@ struct ChunkSmem {
 // 4 mantissa bits of the magnitude, so a bin spans at most 1/16 of its values
 // (scores of magnitude below 16 get a bin each). 896 of the 1024 bins are used.
 constexpr int kHistBins = 1024;
+constexpr int kHistGroups = kHistBins / 16;  // one per lane of a wave
+static_assert(kHistGroups == 64, "hist_threshold: one group per lane");
 __device__ __forceinline__ uint32_t score_bin(int32_t s) {
   // x = |s| for s >= 0, ~s = -s - 1 for s < 0. For x >= 16 with top bit e (4 .. 30)
   // the code is 16(e - 3) + the four bits below it, which is 16·sh + (x >> sh) with
@@ -174,17 +176,16 @@ __device__ __forceinline__ bool threshold_floor(const uint32_t* hist, int count,
 }
 
 // Lowest score of the bin that holds the want-th best of `count` keys, from their
-// histogram over score_bin, by one wave in two levels: lane l sums bins
-// 1008-16l .. 1023-16l (best first) and a wave scan finds the lane whose group of
-// 16 bins holds it; then 16 lanes re-read that group's bins and a row scan finds
-// the bin. Returns false when the histogram does not count `count` keys.
-__device__ __forceinline__ bool hist_threshold(const uint32_t* hist, int count, uint32_t want, int32_t* tlo) {
+// histogram over score_bin and its sums over groups of 16 bins (groups[g] = bins
+// 16g .. 16g + 15, kept alongside so that this reads one word per lane without bank
+// conflicts), by one wave in two levels: lane l takes group 63 - l (best first) and
+// a wave scan finds the lane whose group holds it; then 16 lanes read that group's
+// bins and a row scan finds the bin. Returns false when the histogram does not
+// count `count` keys.
+__device__ __forceinline__ bool hist_threshold(const uint32_t* hist, const uint32_t* groups, int count,
+                                               uint32_t want, int32_t* tlo) {
   const int l = lane_id();
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4* g = reinterpret_cast<const u32x4*>(hist + kHistBins - 16 - 16 * l);
-  const u32x4 a0 = g[0], a1 = g[1], a2 = g[2], a3 = g[3];
-  const u32x4 t = a0 + a1 + a2 + a3;
-  const uint32_t sum = t.x + t.y + t.z + t.w;
+  const uint32_t sum = groups[kHistGroups - 1 - l];  // bins 1008 - 16l .. 1023 - 16l
   const uint32_t incl = wave_incl_scan_u32(sum);
   if ((uint32_t)__builtin_amdgcn_readlane((int)incl, 63) != (uint32_t)count) return false;
   const uint32_t excl = incl - sum;  // keys in better groups than this lane's

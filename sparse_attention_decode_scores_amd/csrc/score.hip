@@ -301,7 +301,8 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(ScoreArgs a) {
   Smem& csm = *reinterpret_cast<Smem*>(smem);
   int32_t* sc = reinterpret_cast<int32_t*>(smem + align16(sizeof(Smem)));                     // [P]
   uint32_t* hist = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(sc) + align16((size_t)a.P * 4));
-  RowCandSmem& rsm = *reinterpret_cast<RowCandSmem*>(hist + kHistBins);
+  uint32_t* hgroup = hist + kHistBins;  // [kHistGroups]: sums of 16 bins
+  RowCandSmem& rsm = *reinterpret_cast<RowCandSmem*>(hgroup + kHistGroups);
 
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   const int c = blockIdx.x, b = a.b0;
@@ -333,7 +334,7 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(ScoreArgs a) {
   const int wl = (int)a.iw[(int64_t)b * a.Hi + (lane < a.Hi ? lane : a.Hi - 1)];
 
   // the histogram is shared by the waves: cleared before any of them adds to it
-  for (int i = tid; i < kHistBins; i += kScoreBlock) hist[i] = 0;
+  for (int i = tid; i < kHistBins + kHistGroups; i += kScoreBlock) hist[i] = 0;  // and hgroup
   if (tid == 0) {
     rsm.nstaged = 0;
     rsm.next = kScoreWaves * D;  // units 0 .. 8D - 1 are requested below, D per wave
@@ -407,7 +408,11 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(ScoreArgs a) {
       const int p = kUnit * j + (lane & 31);
       if (lane < 32) {
         sc[p] = part;
-        if (p < count) atomicAdd(&hist[score_bin(part)], 1u);
+        if (p < count) {
+          const uint32_t bn = score_bin(part);
+          atomicAdd(&hist[bn], 1u);
+          atomicAdd(&hgroup[bn >> 4], 1u);
+        }
       }
     }
     j = jn;
@@ -460,7 +465,7 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(ScoreArgs a) {
 
   // 1. every wave finds the bin that holds the (m+1)-th best key (same result in each)
   int32_t tlo = 0;
-  const bool hok = hist_threshold(hist, count, (uint32_t)m + 1, &tlo);
+  const bool hok = hist_threshold(hist, hgroup, count, (uint32_t)m + 1, &tlo);
   DSA_MARK(0, 6);
   // 2. every key scoring at least that bin's floor is staged, in order of arrival
   //    (the ranks below fix the output order): four positions per thread per pass
@@ -543,7 +548,7 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(ScoreArgs a) {
 }
 
 size_t score_row_lds_bytes(int P) {
-  return align16(sizeof(ChunkSmem<kScoreBlock>)) + align16((size_t)P * 4) + (size_t)kHistBins * 4 +
+  return align16(sizeof(ChunkSmem<kScoreBlock>)) + align16((size_t)P * 4) + (size_t)(kHistBins + kHistGroups) * 4 +
          sizeof(RowCandSmem) + 16;
 }
 
