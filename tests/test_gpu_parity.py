@@ -267,6 +267,28 @@ def test_sparse_attn_standalone_with_skipped_entries(torch, dsa):
     assert dsa.dsa_read_stats(ws, 1)[0]["bad_indices"] == 2
 
 
+def test_constant_row_takes_chunk_fallback(torch, dsa):
+    # Every score of a 40,000-position row is 0. Each chunk of the one-row score pass
+    # (five interleaved 32-position units, 160 positions) then stages all of its
+    # positions, more than m + 64, and takes the radix fallback, whose positions step
+    # by G units; its chunk summary gives the whole score range, and the selection
+    # narrows one 8,000-way tie by position. Chunk c keeps the row's unit c, so the
+    # candidates still cover the top k (positions 0 .. k-1) and the fast path holds.
+    c = inputs.random_case(4242, B=1, N=40000, k=2048, Hi=64, Di=128, Hq=16, Dk=576, Dv=512)
+    c["iq"][...] = 0
+    note("constant row: N=40000 k=2048, zero indexer query")
+    rs, ri, ro = oracle.decode_step(c["iq"], c["iw"], c["ik"], c["q"], c["kv"], c["ctx_len"], c["k"],
+                                    c["Dv"], c["scale"])
+    assert np.array_equal(ri[0], np.arange(2048))
+    d = dev_inputs(torch, c)
+    s, i, o, stats = run_step(torch, dsa, c, d)
+    check_scores(s, rs, c["ctx_len"], "constant row")
+    assert np.array_equal(i, ri)
+    check_attention(o, ro, "constant row")
+    st = stats[0]
+    assert st["path"] == 0 and st["selected"] == 2048 and st["tied_at_kth"] == 2048 and st["kth_score"] == 0
+
+
 # ---------------------------------------------------------------- shapes and edge cases
 
 EDGE = [
