@@ -39,6 +39,7 @@ namespace dsa {
 // ------------------------------------------------------------------ candidates over stored scores
 
 constexpr int kSelBlock = kAttnBlock;  // selection, ranking and attention share the launch
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kSelWaves = kSelBlock / 64;
 constexpr int kUPerThread = kCandCap / kSelBlock;  // candidate keys held per thread
 
@@ -383,6 +384,53 @@ __device__ __forceinline__ void rank_bin(const uint64_t* bin, uint32_t n, uint32
   }
 }
 
+// The union's score range [rng[0], rng[1]] and whether every thread's keys run best
+// first, from the chunk summaries (four per lane, all chunks in every wave: no
+// exchange between waves).
+__device__ __forceinline__ void union_range_from_sums(const u32x4 (&csum)[4], uint32_t* rng, bool* sorted) {
+  uint32_t lo = 0xFFFFFFFFu, hi = 0, unordered = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    lo = csum[i].x < lo ? csum[i].x : lo;
+    hi = csum[i].y > hi ? csum[i].y : hi;
+    unordered |= csum[i].z == 0u ? 1u : 0u;
+  }
+  rng[0] = wave_min_u32(lo);
+  rng[1] = wave_maxr_u32(hi);
+  *sorted = __ballot(unordered != 0u) == 0;
+}
+
+// The same from the keys themselves (when no summaries exist), by one block
+// exchange, which also publishes the cleared radix histograms. A thread's keys run
+// best first when each is at least the next (absent keys, 0, come last).
+template <int E>
+__device__ __forceinline__ void union_range_exchange(const uint64_t (&key)[E], const uint32_t (&sv)[E],
+                                                     uint32_t vmask, SelSmem& sm, uint32_t* rng, bool* sorted) {
+  uint32_t lo = 0xFFFFFFFFu, hi = 0;
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    const bool v = (vmask >> j) & 1u;
+    lo = v && sv[j] < lo ? sv[j] : lo;
+    hi = v && sv[j] > hi ? sv[j] : hi;
+  }
+  bool desc = true;
+#pragma unroll
+  for (int j = 0; j + 1 < E; ++j) desc = desc && key[j] >= key[j + 1];
+  const uint32_t mine[3] = {~wave_min_u32(lo), wave_maxr_u32(hi), __ballot(!desc) != 0 ? 1u : 0u};
+  uint32_t all[kSelWaves][3];
+  block_exchange<kSelBlock, 3>(mine, reinterpret_cast<uint32_t(*)[3]>(&sm.xch[0][0]), all);
+  uint32_t nlo = 0, mhi = 0, unsorted = 0;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) {
+    nlo = all[w][0] > nlo ? all[w][0] : nlo;
+    mhi = all[w][1] > mhi ? all[w][1] : mhi;
+    unsorted |= all[w][2];
+  }
+  rng[0] = ~nlo;
+  rng[1] = mhi;
+  *sorted = unsorted == 0;
+}
+
 // LDS: SelSmem | selected keys [k] | region: the attention working set, or the
 // sort state of the exhaustive path (the two roles never need both); on the
 // candidate path it first holds the keys of the k-th key's radix bin.
@@ -427,8 +475,8 @@ __global__ __launch_bounds__(kSelBlock) void k_select(SelArgs a, AttnArgs at) {
     mx = tid < a.G ? a.xc[(int64_t)b * a.G + tid] : 0ull;
   }
   // every wave reads all chunk summaries (four per lane; clamped repeats change
-  // neither a minimum, a maximum nor an or)
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  // neither a minimum, a maximum nor an or); the best dropped key is only needed
+  // for the coverage check, so its load is not waited for before that
   u32x4 csum[4];
   const bool have_sums = a.sums != nullptr && reason == 0;  // uniform
   if (have_sums) {
@@ -453,54 +501,12 @@ __global__ __launch_bounds__(kSelBlock) void k_select(SelArgs a, AttnArgs at) {
     uint32_t rng[2];
     bool sorted;
     if (have_sums) {
-      // the range and order of the union from the chunk summaries, in every wave
-      // (no exchange; one barrier publishes the cleared radix histograms)
-      uint32_t lo = 0xFFFFFFFFu, hi = 0, unordered = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        lo = csum[i].x < lo ? csum[i].x : lo;
-        hi = csum[i].y > hi ? csum[i].y : hi;
-        unordered |= csum[i].z == 0u ? 1u : 0u;
-      }
-      rng[0] = wave_min_u32(lo);
-      rng[1] = wave_maxr_u32(hi);
-      sorted = __ballot(unordered != 0u) == 0;
-      lds_barrier();
-      DSA_MARK(1, 11);
+      union_range_from_sums(csum, rng, &sorted);
+      lds_barrier();  // publishes the cleared radix histograms
     } else {
-    uint32_t lo = 0xFFFFFFFFu, hi = 0;
-#pragma unroll
-    for (int j = 0; j < kUPerThread; ++j) {
-      const bool v = (vmask >> j) & 1u;
-      lo = v && sv[j] < lo ? sv[j] : lo;
-      hi = v && sv[j] > hi ? sv[j] : hi;
+      union_range_exchange<kUPerThread>(key, sv, vmask, sm, rng, &sorted);
     }
-    // whether this thread's keys run best first (the score pass's lists do, and
-    // absent keys, 0, come last; lists written in position order do not)
-    bool desc = true;
-#pragma unroll
-    for (int j = 0; j + 1 < kUPerThread; ++j) desc = desc && key[j] >= key[j + 1];
     DSA_MARK(1, 11);
-    // the range of the candidates' scores and whether every thread's keys run best
-    // first (the exchange also publishes the cleared radix histograms); the best
-    // dropped key is only needed for the coverage check, so its load is not waited
-    // for here
-    {
-      const uint32_t mine[3] = {~wave_min_u32(lo), wave_maxr_u32(hi), __ballot(!desc) != 0 ? 1u : 0u};
-      uint32_t all[kSelWaves][3];
-      block_exchange<kSelBlock, 3>(mine, reinterpret_cast<uint32_t(*)[3]>(&sm.xch[0][0]), all);
-      uint32_t nlo = 0, mhi = 0, unsorted = 0;
-#pragma unroll
-      for (int w = 0; w < kSelWaves; ++w) {
-        nlo = all[w][0] > nlo ? all[w][0] : nlo;
-        mhi = all[w][1] > mhi ? all[w][1] : mhi;
-        unsorted |= all[w][2];
-      }
-      rng[0] = ~nlo;
-      rng[1] = mhi;
-      sorted = unsorted == 0;
-    }
-    }
     nvalid = (uint32_t)a.cand_valid.n[b];
     DSA_MARK(1, 1);
     const uint32_t kk = (uint32_t)a.k < nvalid ? (uint32_t)a.k : nvalid;
