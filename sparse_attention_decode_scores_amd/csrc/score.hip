@@ -305,7 +305,10 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(ScoreArgs a) {
   RowCandSmem& rsm = *reinterpret_cast<RowCandSmem*>(hgroup + kHistGroups);
 
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
-  const int c = blockIdx.x, b = a.b0;
+  // a batch of one: the row is row 0, a constant, so that every argument address is
+  // known at entry and their reads go out together (an index read from the argument
+  // block would put a second round trip before the first key request)
+  const int c = blockIdx.x, b = 0;
   DSA_TRACE_BEGIN();
   DSA_MARK(0, 0);
   // Chunk c is a set of 32-key units of the row: interleaved (a.ilv), units c, c + G,

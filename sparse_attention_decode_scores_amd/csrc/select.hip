@@ -448,10 +448,16 @@ __global__ __launch_bounds__(kSelBlock) void k_select(SelArgs a, AttnArgs at) {
   const int32_t* row = a.scores + (int64_t)b * a.N;
   DSA_TRACE_BEGIN();
   DSA_MARK(1, 0);
-  // The attention arguments are first needed after the selection; reading two of
-  // them here brings their part of the argument block into the scalar cache early
-  // (a first read at that point would wait for a memory round trip).
-  if (at.frag == -1 && at.part_o == nullptr) a.stats[0].reserved = at.Dk;
+  // One field from each 64-byte line of the argument block, read here and waited for
+  // together: every later argument read hits the scalar cache. (Read where first
+  // used, behind the branches before them, the fields took three memory round trips
+  // in a row before the first candidate load; the attention arguments, first used
+  // after the selection, would take another there.)
+  {
+    const uint64_t* l0 = a.cand;
+    const int l1 = a.lens.n[b], l2 = a.have_cand, l3 = a.force, l4 = at.S;
+    asm volatile("" ::"s"(l0), "s"(l1), "s"(l2), "s"(l3), "s"(l4));
+  }
 
   int reason = a.force ? 1 : (a.have_cand ? 0 : 3);
   uint32_t nvalid = 0, nsel = 0, tied = 0;
