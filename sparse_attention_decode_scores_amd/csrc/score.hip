@@ -6,11 +6,14 @@
 // (heads x dim times dim x positions), so it runs on the int8 matrix cores:
 // v_mfma_i32_32x32x32_i8 with the query heads as the A operand (32 heads per
 // tile, held in registers or LDS) and 32 keys per tile streamed from HBM as the B
-// operand with 16-byte loads, three tiles per wave in flight. The ReLU, the per-head weight and the sum over heads
-// are applied to the accumulators in registers; one cross-lane add finishes the
-// head sum. The key cache is read exactly once per launch.
+// operand with 16-byte loads (k_score_row, one query row: two 32-key units per
+// wave in flight; k_score, several rows: three 64-key tiles). The ReLU, the
+// per-head weight and the sum over heads are applied to the accumulators in
+// registers; one cross-lane add finishes the head sum. The key cache is read
+// exactly once per launch.
 //
-// With candidates enabled, each workgroup owns one contiguous chunk of positions
+// With candidates enabled, each workgroup owns one chunk of positions (for one
+// row: every G-th 32-key unit of the row; for several rows: a contiguous stretch)
 // and, after scoring it, keeps the chunk's m best keys (and the best key it
 // drops) for the selection stage: the "scans that narrow the candidates" of the
 // ds4 glm53-m3ultra branch post (2026-09-09 "rising" page, long-context paragraph).
@@ -505,26 +508,29 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(ScoreArgs a) {
   const uint32_t total = rsm.nstaged;
   const bool fast = hok && total <= (uint32_t)m + 64;  // uniform over the block
   if (fast) {
-    // 3. rank of staged key t = number of staged keys above it (four threads per
-    //    key). Staged keys are distinct and include the m + 1 best, so ranks 0 .. m
-    //    are the chunk's m + 1 best keys in order: rank r < m goes to slot r of
-    //    the output (best first; keys of equal score stay in position order), and
-    //    rank m is x, the best key left out.
-    const int t = tid >> 2, part = tid & 3;
+    // 3. rank of staged key t = number of staged keys above it (eight threads per
+    //    key when at most 64 keys are staged, the usual case, else four). Staged
+    //    keys are distinct and include the m + 1 best, so ranks 0 .. m are the
+    //    chunk's m + 1 best keys in order: rank r < m goes to slot r of the output
+    //    (best first; keys of equal score stay in position order), and rank m is
+    //    x, the best key left out.
+    const bool wide = total <= 64u;  // uniform
+    const int tpk = wide ? 8 : 4, t = tid / tpk, part = tid % tpk;
     uint32_t r = 0;
     uint64_t me = 0;
     if (t < (int)total) {
       me = rsm.all[t];
-      for (int s0 = 0; s0 < (int)total; s0 += 16) {
+      for (int s0 = 0; s0 < (int)total; s0 += 4 * tpk) {
         uint64_t v[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = rsm.all[s0 + part + 4 * u];  // < kRowStage
+        for (int u = 0; u < 4; ++u) v[u] = rsm.all[s0 + part + tpk * u];  // < kRowStage
 #pragma unroll
-        for (int u = 0; u < 4; ++u) r += (s0 + part + 4 * u < (int)total && v[u] > me) ? 1u : 0u;
+        for (int u = 0; u < 4; ++u) r += (s0 + part + tpk * u < (int)total && v[u] > me) ? 1u : 0u;
       }
     }
     r += (uint32_t)__builtin_amdgcn_mov_dpp((int)r, dpp::kQuadXor1, 0xF, 0xF, false);
     r += (uint32_t)__builtin_amdgcn_mov_dpp((int)r, dpp::kQuadXor2, 0xF, 0xF, false);
+    if (wide) r += (uint32_t)__builtin_amdgcn_mov_dpp((int)r, dpp::kRowHalfMirror, 0xF, 0xF, false);
     if (part == 0 && t < (int)total) {
       if (r < (uint32_t)m) out.put((int)r, me);
       else if (r == (uint32_t)m) *xout = me;
