@@ -13,6 +13,9 @@ ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
          # keep the compiler from forming packed fp32 instructions
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # leading scalar and pointer kernel arguments (up to eight, stopping at the
+         # first structure) arrive in scalar registers at wave launch
+         "-mllvm", "-amdgpu-kernarg-preload-count=8",
          "-I", os.path.join(ROOT, "include")]
 
 

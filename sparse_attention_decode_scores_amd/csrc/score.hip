@@ -295,15 +295,22 @@ __device__ __forceinline__ void load_unit(v4i (&kf)[KT], __amdgpu_buffer_rsrc_t 
 
 }  // namespace
 
+// The arguments that the first requests need come first, as separate scalars: the
+// leading arguments can be preloaded into scalar registers at wave launch, so the
+// query and key requests need not wait for a read of the argument block (a.iq,
+// a.iw, a.ik, a.lens.n[0], a.G, a.P, a.ilv and a.Hi, passed again).
 template <int MT, int KT, int D>
-__global__ __launch_bounds__(kScoreBlock) void k_score_row(ScoreArgs a) {
+__global__ __launch_bounds__(kScoreBlock) void k_score_row(const int8_t* __restrict__ iq,
+                                                           const int8_t* __restrict__ iw,
+                                                           const int8_t* __restrict__ ik, int n, int G, int P,
+                                                           int ilv, int Hi, ScoreArgs a) {
   static_assert(D == 2 || D == 3, "units in flight per wave");
   constexpr int DI = 32 * KT;
   extern __shared__ __align__(16) uint8_t smem[];
   using Smem = ChunkSmem<kScoreBlock>;
   Smem& csm = *reinterpret_cast<Smem*>(smem);
   int32_t* sc = reinterpret_cast<int32_t*>(smem + align16(sizeof(Smem)));                     // [P]
-  uint32_t* hist = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(sc) + align16((size_t)a.P * 4));
+  uint32_t* hist = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(sc) + align16((size_t)P * 4));
   uint32_t* hgroup = hist + kHistBins;  // [kHistGroups]: sums of 16 bins
   RowCandSmem& rsm = *reinterpret_cast<RowCandSmem*>(hgroup + kHistGroups);
 
@@ -314,13 +321,12 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(ScoreArgs a) {
   const int c = blockIdx.x, b = 0;
   DSA_TRACE_BEGIN();
   DSA_MARK(0, 0);
-  // Chunk c is a set of 32-key units of the row: interleaved (a.ilv), units c, c + G,
+  // Chunk c is a set of 32-key units of the row: interleaved (ilv), units c, c + G,
   // c + 2G, ..., so that at any moment the launch streams one contiguous stretch of
   // keys; otherwise P / 32 consecutive units. Local unit j is row unit c·us + j·js.
-  const int n = a.lens.n[b];
-  const int us = a.ilv ? 1 : a.P / kUnit, js = a.ilv ? a.G : 1;
+  const int us = ilv ? 1 : P / kUnit, js = ilv ? G : 1;
   int count;  // valid positions of the chunk
-  const int units = row_chunk_units(n, c, a.G, a.P, a.ilv, &count);
+  const int units = row_chunk_units(n, c, G, P, ilv, &count);
   const int64_t cbeg = (int64_t)kUnit * c * us;     // the chunk's first position
   const uint32_t ustride = (uint32_t)(kUnit * js);  // positions from one local unit to the next
   // local entry i is position cbeg + (i / 32)·ustride + i % 32; span: row positions
@@ -329,15 +335,15 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(ScoreArgs a) {
 
   // A operand: lane l holds head 32mt + (l & 31), dims 32kt + 16(l >> 5) .. +15; lane
   // l also holds the weight of head l (Hi <= 64). Requested before any key.
-  const int8_t* qrow = a.iq + (int64_t)b * a.Hi * DI;
+  const int8_t* qrow = iq + (int64_t)b * Hi * DI;
   v4i qreg[MT][KT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    const int h = 32 * mt + (lane & 31) < a.Hi ? 32 * mt + (lane & 31) : a.Hi - 1;
+    const int h = 32 * mt + (lane & 31) < Hi ? 32 * mt + (lane & 31) : Hi - 1;
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) qreg[mt][kt] = *(const v4i*)(qrow + h * DI + 32 * kt + 16 * (lane >> 5));
   }
-  const int wl = (int)a.iw[(int64_t)b * a.Hi + (lane < a.Hi ? lane : a.Hi - 1)];
+  const int wl = (int)iw[(int64_t)b * Hi + (lane < Hi ? lane : Hi - 1)];
 
   // the histogram is shared by the waves: cleared before any of them adds to it
   for (int i = tid; i < kHistBins + kHistGroups; i += kScoreBlock) hist[i] = 0;  // and hgroup
@@ -348,7 +354,7 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(ScoreArgs a) {
   lds_barrier();
 
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<int8_t*>(a.ik + cbeg * DI), (short)0, span * DI, 0x00020000);
+      const_cast<int8_t*>(ik + cbeg * DI), (short)0, span * DI, 0x00020000);
   v4i kb0[KT], kb1[KT], kb2[KT];
   load_unit<KT>(kb0, rs, wave, js);
   load_unit<KT>(kb1, rs, wave + kScoreWaves, js);
@@ -363,9 +369,9 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(ScoreArgs a) {
     for (int r = 0; r < 16; ++r) {
       const int h = 32 * mt + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
       const int w = __shfl(wl, h & 63);
-      wreg[mt][r] = h < a.Hi ? w : 0;
+      wreg[mt][r] = h < Hi ? w : 0;
     }
-    if (32 * mt + (lane & 31) >= a.Hi)
+    if (32 * mt + (lane & 31) >= Hi)
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) qreg[mt][kt] = v4i{0, 0, 0, 0};
   }
@@ -442,7 +448,7 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(ScoreArgs a) {
 
   const int m = a.m;
   const CandOut out{a.cand + (int64_t)b * kCandCap, c * m};
-  uint64_t* xout = a.xc + (int64_t)b * a.G + c;
+  uint64_t* xout = a.xc + (int64_t)b * G + c;
   // the scores leave for HBM as they are read below (raw buffer stores against a
   // resource that covers exactly the chunk's valid positions: the padding is
   // dropped without a branch); nothing waits for these stores
@@ -570,7 +576,8 @@ static hipError_t launch_score_row_t(const ScoreArgs& a, int D, int grid, hipStr
   hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
-  return launch_timed(fn, dim3(grid), dim3(kScoreBlock), lds, s, t, a);
+  return launch_timed(fn, dim3(grid), dim3(kScoreBlock), lds, s, t, a.iq, a.iw, a.ik, a.lens.n[0], a.G, a.P, a.ilv,
+                      a.Hi, a);
 }
 
 hipError_t launch_score_row(const ScoreArgs& a, int MT, int KT, int D, int grid, hipStream_t s,

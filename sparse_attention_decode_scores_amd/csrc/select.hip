@@ -39,7 +39,7 @@ namespace dsa {
 // ------------------------------------------------------------------ candidates over stored scores
 
 constexpr int kSelBlock = kAttnBlock;  // selection, ranking and attention share the launch
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x3 __attribute__((ext_vector_type(3)));  // a chunk summary without its padding
 constexpr int kSelWaves = kSelBlock / 64;
 constexpr int kUPerThread = kCandCap / kSelBlock;  // candidate keys held per thread
 
@@ -387,7 +387,7 @@ __device__ __forceinline__ void rank_bin(const uint64_t* bin, uint32_t n, uint32
 // The union's score range [rng[0], rng[1]] and whether every thread's keys run best
 // first, from the chunk summaries (four per lane, all chunks in every wave: no
 // exchange between waves).
-__device__ __forceinline__ void union_range_from_sums(const u32x4 (&csum)[4], uint32_t* rng, bool* sorted) {
+__device__ __forceinline__ void union_range_from_sums(const u32x3 (&csum)[4], uint32_t* rng, bool* sorted) {
   uint32_t lo = 0xFFFFFFFFu, hi = 0, unordered = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -434,66 +434,88 @@ __device__ __forceinline__ void union_range_exchange(const uint64_t (&key)[E], c
 // LDS: SelSmem | selected keys [k] | region: the attention working set, or the
 // sort state of the exhaustive path (the two roles never need both); on the
 // candidate path it first holds the keys of the k-th key's radix bin.
+// The arguments that the first requests need come first, as separate scalars: the
+// leading arguments can be preloaded into scalar registers at wave launch, so the
+// candidate, summary and query requests need not wait for a read of the argument
+// block (a.cand, a.sums, a.G, at.q, at.Hq, at.Dk and at.S, passed again).
 template <class Attn>
-__global__ __launch_bounds__(kSelBlock) void k_select(SelArgs a, AttnArgs at) {
+__global__ __launch_bounds__(kSelBlock) void k_select(const uint64_t* __restrict__ cand,
+                                                      const ChunkSum* __restrict__ sums, const void* __restrict__ q,
+                                                      int G, int Hq, int Dk, int S, SelArgs a, AttnArgs at) {
   extern __shared__ __align__(16) uint8_t smem[];
   SelSmem& sm = *reinterpret_cast<SelSmem*>(smem);
   uint64_t* sel = reinterpret_cast<uint64_t*>(smem + align16(sizeof(SelSmem)));
   uint8_t* region = smem + align16(sizeof(SelSmem)) + align16((size_t)a.k * 8);
   const int tid = threadIdx.x;
   const int b = blockIdx.y;
-  const int S = at.S;
   const bool attn_role = (int)blockIdx.x < S;
   const int n = a.lens.n[b];
   const int32_t* row = a.scores + (int64_t)b * a.N;
   DSA_TRACE_BEGIN();
   DSA_MARK(1, 0);
-  // One field from each 64-byte line of the argument block, read here and waited for
-  // together: every later argument read hits the scalar cache. (Read where first
-  // used, behind the branches before them, the fields took three memory round trips
-  // in a row before the first candidate load; the attention arguments, first used
-  // after the selection, would take another there.)
+  // Requests first, all from preloaded arguments. The candidate union U: thread t
+  // holds entries [16t, 16t + 16), eight 16-byte pieces, piece j of all threads
+  // contiguous (cand_slot); its workspace region always exists, and the entries are
+  // used on the candidate path only.
+  typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
+  uint64_t key[kUPerThread];
   {
-    const uint64_t* l0 = a.cand;
-    const int l1 = a.lens.n[b], l2 = a.have_cand, l3 = a.force, l4 = at.S;
-    asm volatile("" ::"s"(l0), "s"(l1), "s"(l2), "s"(l3), "s"(l4));
+    const u64x2* src = reinterpret_cast<const u64x2*>(cand + (int64_t)b * kCandCap) + tid;
+#pragma unroll
+    for (int j = 0; j < kUPerThread / 2; ++j) {
+      const u64x2 v = src[(kCandCap / 16) * j];
+      key[2 * j] = v.x;
+      key[2 * j + 1] = v.y;
+    }
+  }
+  // every wave reads all chunk summaries (four per lane; clamped repeats change
+  // neither a minimum, a maximum nor an or). The loads are issued in any case (a
+  // branch around them leaves their registers possibly in flight where the paths
+  // join, and the compiler then waits for every load before reusing one): without
+  // summaries they read the candidate region instead, and the values go unused.
+  const bool sums_on = sums != nullptr && G > 0;  // uniform
+  u32x3 csum[4];  // lo, hi, ordered (the padding word is not read)
+  {
+    const uint8_t* sp = sums_on ? reinterpret_cast<const uint8_t*>(sums + (int64_t)b * kMaxChunks)
+                                : reinterpret_cast<const uint8_t*>(cand + (int64_t)b * kCandCap);
+    const int last = G > 0 ? G - 1 : 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = lane_id() + 64 * i;
+      csum[i] = *reinterpret_cast<const u32x3*>(sp + sizeof(ChunkSum) * (c < last ? c : last));
+    }
+  }
+  // the requests above go out before anything else (left to itself the scheduler
+  // put the attention's address arithmetic first)
+  __builtin_amdgcn_sched_barrier(0);
+  AttnArgs atq = at;  // the query's address and shape from the preloaded arguments
+  atq.q = q;
+  atq.Hq = Hq;
+  atq.Dk = Dk;
+  const typename Attn::QFrag qf = Attn::load_q(atq, b);  // every workgroup: exact wait counts
+  // Then fields from every 64-byte line of the argument block, read here and waited
+  // for together, so every later argument read hits the scalar cache (read where
+  // first used, behind the branches before them, they took several memory round
+  // trips in a row).
+  {
+    const int32_t* l0 = a.idx;
+    const int l1 = a.lens.n[b], l2 = a.have_cand, l3 = a.cand_valid.n[b], l4 = a.force, l5 = at.S;
+    asm volatile("" ::"s"(l0), "s"(l1), "s"(l2), "s"(l3), "s"(l4), "s"(l5));
   }
 
   int reason = a.force ? 1 : (a.have_cand ? 0 : 3);
   uint32_t nvalid = 0, nsel = 0, tied = 0;
   uint64_t kstar = 0;
-  uint64_t key[kUPerThread];
   uint64_t mx = 0;
   if (reason == 0) {
-    // the candidate union U: thread t holds entries [16t, 16t + 16), eight 16-byte
-    // pieces, piece j of all threads contiguous (cand_slot); entries past the
-    // union's end are absent (key 0)
-    const int C = a.G * a.m;
-    typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
-    const u64x2* src = reinterpret_cast<const u64x2*>(a.cand + (int64_t)b * kCandCap) + tid;
+    // entries past the union's end are absent (key 0); the best dropped key is only
+    // needed for the coverage check, so its load is not waited for before that
+    const int C = G * a.m;
 #pragma unroll
-    for (int j = 0; j < kUPerThread / 2; ++j) {
-      const u64x2 v = src[(kCandCap / 16) * j];
-      const int u = kUPerThread * tid + 2 * j;
-      key[2 * j] = u < C ? v.x : 0ull;
-      key[2 * j + 1] = u + 1 < C ? v.y : 0ull;
-    }
-    mx = tid < a.G ? a.xc[(int64_t)b * a.G + tid] : 0ull;
+    for (int j = 0; j < kUPerThread; ++j) key[j] = kUPerThread * tid + j < C ? key[j] : 0ull;
+    mx = tid < G ? a.xc[(int64_t)b * G + tid] : 0ull;
   }
-  // every wave reads all chunk summaries (four per lane; clamped repeats change
-  // neither a minimum, a maximum nor an or); the best dropped key is only needed
-  // for the coverage check, so its load is not waited for before that
-  u32x4 csum[4];
-  const bool have_sums = a.sums != nullptr && reason == 0;  // uniform
-  if (have_sums) {
-    const u32x4* sp = reinterpret_cast<const u32x4*>(a.sums + (int64_t)b * kMaxChunks);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = lane_id() + 64 * i;
-      csum[i] = sp[c < a.G ? c : a.G - 1];
-    }
-  }
-  const typename Attn::QFrag qf = Attn::load_q(at, b);  // every workgroup: exact wait counts
+  const bool have_sums = sums_on && reason == 0;  // uniform
   radix_clear<kSelBlock>(sm.radix);
   if (reason == 0) {
     // 32-bit views of the candidate keys: score bits and presence (a present key's
@@ -702,7 +724,8 @@ static hipError_t launch_select_t(const SelArgs& a, const AttnArgs& at, int B, h
   hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
-  return launch_timed(fn, dim3(at.S + a.R, B), dim3(kSelBlock), lds, s, t, a, at);
+  return launch_timed(fn, dim3(at.S + a.R, B), dim3(kSelBlock), lds, s, t, a.cand, a.sums, at.q, a.G, at.Hq, at.Dk,
+                      at.S, a, at);
 }
 
 // ------------------------------------------------------------------ attention over given indices
@@ -829,13 +852,16 @@ constexpr int kCombWideBlock = 256;
 // values). It forms the split weights of its 4 heads (64 thread groups,
 // fixed-order reductions), then 16 thread groups each sum every 16th split and the
 // groups are added in order, so the result does not depend on timing.
-__global__ __launch_bounds__(kCombWideBlock) void k_combine_wide(AttnArgs at, const int32_t* __restrict__ part_bad,
+// (the partials' addresses and shape come first, preloaded at wave launch: at.part_ml,
+// at.part_o, at.S, at.Hq and at.Dv, passed again)
+__global__ __launch_bounds__(kCombWideBlock) void k_combine_wide(const float2* __restrict__ part_ml,
+                                                                 const float* __restrict__ part_o, int S, int Hq,
+                                                                 int Dv, AttnArgs at, const int32_t* __restrict__ part_bad,
                                                                  RowStats* __restrict__ stats, float* __restrict__ out) {
   __shared__ float wt[4][kMaxWideSplits];
   __shared__ float red[4][65];
   __shared__ v4f part[16][16];
   const int b = blockIdx.y, t = threadIdx.x;
-  const int S = at.S, Hq = at.Hq, Dv = at.Dv;
   const int HP = (Hq + 15) / 16 * 16, tiles = Dv / 16;
   const int quad = blockIdx.x, tile = quad >> 2, l0 = 16 * (quad & 3);
   const int h0 = 16 * (tile / tiles) + 4 * (quad & 3);  // heads h0 .. h0 + 3
@@ -848,10 +874,10 @@ __global__ __launch_bounds__(kCombWideBlock) void k_combine_wide(AttnArgs at, co
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int sp = g + 64 * i;
-    ml[i] = at.part_ml[((int64_t)b * S + (sp < S ? sp : S - 1)) * Hq + hh];
+    ml[i] = part_ml[((int64_t)b * S + (sp < S ? sp : S - 1)) * Hq + hh];
   }
   const int e = t & 15, q = t >> 4;
-  const float* po = at.part_o + (int64_t)b * S * HP * Dv;
+  const float* po = part_o + (int64_t)b * S * HP * Dv;
   const int64_t el = (int64_t)tile * 64 + l0 + e;  // 16-byte element
   constexpr int kPer = kMaxWideSplits / 16;
   v4f v[kPer];
@@ -926,8 +952,8 @@ hipError_t launch_combine_wide(const AttnArgs& at, const int32_t* part_bad, RowS
                                int B, hipStream_t s, KTimer t) {
   if (!at.frag || at.S > kMaxWideSplits) return hipErrorInvalidValue;
   const int quads = (at.Hq + 15) / 16 * (at.Dv / 16) * 4;
-  return launch_timed(k_combine_wide, dim3(quads, B), dim3(kCombWideBlock), 0, s, t, at, part_bad, stats,
-                      out);
+  return launch_timed(k_combine_wide, dim3(quads, B), dim3(kCombWideBlock), 0, s, t, at.part_ml, at.part_o, at.S,
+                      at.Hq, at.Dv, at, part_bad, stats, out);
 }
 
 constexpr int kCombBlock = 64;
