@@ -114,16 +114,17 @@ dsa_status check_ws(void* ws, size_t ws_bytes, const Layout& L) {
 // Chunking of the candidate pass for rows of at most nmax positions.
 struct ChunkPlan {
   int P, G, m;
-  int ilv;  // one-row plan: interleaved chunks (row_chunk_units)
+  int ilv;  // 1: chunk c holds the row's 32-key units c, c + G, ... (one-row plan; row_chunk_units)
 };
-// One-row plan (score kernel k_score_row): chunks of whole 32-key units, as many
-// chunks as candidate slots allow (at most one per compute unit), so every wave of
-// a chunk has at most one unit more than another.
+// One-row plan (score kernel k_score_row): chunks of whole 32-key units,
+// interleaved over the row, as many chunks as candidate slots allow (at most one
+// per compute unit), so every wave of a chunk has at most one unit more than
+// another. (cand_fits takes the plan only when a chunk fits the kernel, which
+// bounds a row to 2^21 positions, so every key offset fits a buffer offset.)
 ChunkPlan chunk_plan_row(int nmax, int k, int Di) {
   ChunkPlan c;
   c.m = k <= 2048 ? 32 : 64;
-  // interleaved while every key offset of a row fits a buffer offset
-  c.ilv = (int64_t)nmax * Di <= ((int64_t)1 << 30) ? 1 : 0;
+  c.ilv = 1;
   const int gmax = kCandCap / c.m < kMaxChunks ? kCandCap / c.m : kMaxChunks;
   const int64_t units = ((int64_t)nmax + 31) / 32;
   int64_t per = (units + gmax - 1) / gmax;
@@ -180,7 +181,6 @@ dsa_status run_scores(const int8_t* iq, const int8_t* iw, const int8_t* ik, cons
   a.Hi = Hi;
   a.Di = Di;
   a.m = cp.m;
-  a.ilv = 0;
   if (cand) {
     a.P = cp.P;
     a.G = cp.G;
@@ -192,7 +192,6 @@ dsa_status run_scores(const int8_t* iq, const int8_t* iw, const int8_t* ik, cons
   if (cand && B == 1) {  // the decode hot path: one row, candidates on
     a.b0 = 0;
     a.Bg = 1;
-    a.ilv = cp.ilv;
     a.sums = sums;
     return hip_status(launch_score_row(a, MT, KT, kScoreRowDepth, a.G, s, t));
   }
@@ -213,6 +212,8 @@ bool cand_fits(int Hi, int Di, int B, const ChunkPlan& cp, bool fused) {
   size_t need;
   if (fused && B == 1) {
     if (cp.P > score_row_max_chunk()) return false;
+    // the kernel addresses a chunk's keys, interleaved over the row, by 32-bit offsets
+    if ((int64_t)cp.G * cp.P * Di >= ((int64_t)1 << 31)) return false;
     need = score_row_lds_bytes(cp.P);
   } else if (fused) {
     if (cp.P > score_max_chunk()) return false;

@@ -52,8 +52,6 @@ struct ScoreArgs {
   int P;           // positions per chunk (multiple of 64; of 32 for the one-row kernel)
   int G;           // chunks per row
   int m;           // candidates kept per chunk
-  int ilv;         // one-row kernel: chunk c holds the row's 32-key units c, c + G, ...
-                   // (else P consecutive positions)
 };
 
 // Geometry of chunk c of a row of n positions in units of 32 positions: with ilv,

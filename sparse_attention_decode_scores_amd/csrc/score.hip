@@ -298,12 +298,12 @@ __device__ __forceinline__ void load_unit(v4i (&kf)[KT], __amdgpu_buffer_rsrc_t 
 // The arguments that the first requests need come first, as separate scalars: the
 // leading arguments can be preloaded into scalar registers at wave launch, so the
 // query and key requests need not wait for a read of the argument block (a.iq,
-// a.iw, a.ik, a.lens.n[0], a.G, a.P, a.ilv and a.Hi, passed again).
+// a.iw, a.ik, a.lens.n[0], a.G, a.P and a.Hi, passed again).
 template <int MT, int KT, int D>
 __global__ __launch_bounds__(kScoreBlock) void k_score_row(const int8_t* __restrict__ iq,
                                                            const int8_t* __restrict__ iw,
                                                            const int8_t* __restrict__ ik, int n, int G, int P,
-                                                           int ilv, int Hi, ScoreArgs a) {
+                                                           int Hi, ScoreArgs a) {
   static_assert(D == 2 || D == 3, "units in flight per wave");
   constexpr int DI = 32 * KT;
   extern __shared__ __align__(16) uint8_t smem[];
@@ -321,13 +321,13 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(const int8_t* __restr
   const int c = blockIdx.x, b = 0;
   DSA_TRACE_BEGIN();
   DSA_MARK(0, 0);
-  // Chunk c is a set of 32-key units of the row: interleaved (ilv), units c, c + G,
-  // c + 2G, ..., so that at any moment the launch streams one contiguous stretch of
-  // keys; otherwise P / 32 consecutive units. Local unit j is row unit c·us + j·js.
-  const int us = ilv ? 1 : P / kUnit, js = ilv ? G : 1;
+  // Chunk c is the row's 32-key units c, c + G, c + 2G, ... (interleaved, so that at
+  // any moment the launch streams one contiguous stretch of keys): local unit j is
+  // row unit c + j·G.
+  const int js = G;
   int count;  // valid positions of the chunk
-  const int units = row_chunk_units(n, c, G, P, ilv, &count);
-  const int64_t cbeg = (int64_t)kUnit * c * us;     // the chunk's first position
+  const int units = row_chunk_units(n, c, G, P, 1, &count);
+  const int64_t cbeg = (int64_t)kUnit * c;          // the chunk's first position
   const uint32_t ustride = (uint32_t)(kUnit * js);  // positions from one local unit to the next
   // local entry i is position cbeg + (i / 32)·ustride + i % 32; span: row positions
   // from the chunk's first to its last valid one
@@ -576,8 +576,8 @@ static hipError_t launch_score_row_t(const ScoreArgs& a, int D, int grid, hipStr
   hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
-  return launch_timed(fn, dim3(grid), dim3(kScoreBlock), lds, s, t, a.iq, a.iw, a.ik, a.lens.n[0], a.G, a.P, a.ilv,
-                      a.Hi, a);
+  return launch_timed(fn, dim3(grid), dim3(kScoreBlock), lds, s, t, a.iq, a.iw, a.ik, a.lens.n[0], a.G, a.P, a.Hi,
+                      a);
 }
 
 hipError_t launch_score_row(const ScoreArgs& a, int MT, int KT, int D, int grid, hipStream_t s,
