@@ -355,7 +355,7 @@ dsa_status dsa_topk_select(const int32_t* scores, const int32_t* ctx_len, int B,
   const SelArgs sa = sel_args(scores, lens, N, k, idx, w, L, cp, have, flags);
   AttnArgs at{};
   at.S = 0;
-  return hip_status(launch_select(sa, at, AttnChoice{ATTN_NONE, 0, 0}, B, stream));
+  return hip_status(launch_select(sa, at, AttnChoice{ATTN_NONE, 0, 0, 0}, B, stream));
 }
 
 dsa_status dsa_sparse_attn(const void* q, const void* kv, const int32_t* idx, int B, int Hq, int Dk,

@@ -75,12 +75,15 @@ __device__ __forceinline__ void softmax_update_parts32(const float* lgp, int par
 // 16 heads per tile as the A operand and 16 staged rows per tile as the B
 // operand; output = P V with P split into two bf16 terms (high part exact,
 // remainder rounded) so the probabilities keep ~16 bits. Needs Dk % 32 == 0,
-// Dv % 16 == 0, Dv <= 512, Hq <= 16 * HQT, (Dk / 8) * SB <= kMaxLoads * block size.
-template <int HQT, int SB>
+// Dv % 16 == 0, Dv <= 512, Hq <= 16 * HQT, (Dk / 8) * SB <= NL * block size. NL, the
+// 16-byte row loads per thread per sub-block, is fitted to Dk by the caller: slots
+// past the sub-block re-read a present row, so spare slots are spare address work
+// on the latency-critical gather.
+template <int HQT, int SB, int NL = 9>
 struct AttnMfma {
   static constexpr int HP = 16 * HQT;
   static constexpr int kMaxTilesPerWave = 32 / kAttnWaves;  // Dv <= 512
-  static constexpr int kMaxLoads = 9;                       // 16-byte loads per thread per sub-block
+  static constexpr int kMaxLoads = NL;                      // 16-byte loads per thread per sub-block
   static constexpr int kLogitBatch = HQT == 1 ? 6 : (HQT == 2 ? 4 : 2);  // k-steps loaded together
   static constexpr bool kQInLds = HQT == 1;                 // query heads staged in LDS
   static constexpr int kTiles = SB / 16;                    // 16-row tiles of a sub-block

@@ -141,6 +141,7 @@ struct AttnChoice {
   AttnKind kind;
   int hqt;   // 16-head tiles (MFMA path)
   int sb;    // rows staged per sub-block
+  int nl;    // MFMA path: 16-byte row loads per thread per sub-block (5 or 9)
 };
 
 AttnChoice choose_attn(int dt_bf16, int Hq, int Dk, int Dv);

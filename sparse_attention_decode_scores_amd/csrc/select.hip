@@ -776,14 +776,16 @@ static hipError_t launch_attend_t(const int32_t* idx, int k, int32_t* part_bad, 
 // ------------------------------------------------------------------ dispatch
 
 AttnChoice choose_attn(int dt_bf16, int Hq, int Dk, int Dv) {
-  AttnChoice c{ATTN_NONE, 0, 0};
+  AttnChoice c{ATTN_NONE, 0, 0, 0};
   if (dt_bf16 && Hq >= 1 && Hq <= 64 && Dk % 32 == 0 && Dk <= 1024 && Dv % 16 == 0 && Dv <= 512 &&
       Dv <= Dk) {
     c.kind = ATTN_MFMA_BF16;
     c.hqt = (Hq + 15) / 16;
     c.sb = 32;  // a split's 32 rows form one sub-block
-    if ((Dk / 8) * c.sb <= AttnMfma<1, 32>::kMaxLoads * kAttnBlock) return c;  // one gather pass
-    c = AttnChoice{ATTN_NONE, 0, 0};
+    // one gather pass; five loads per thread cover Dk <= 640 (the 576-value latent row)
+    c.nl = c.hqt == 1 && (Dk / 8) * c.sb <= AttnMfma<1, 32, 5>::kMaxLoads * kAttnBlock ? 5 : 9;
+    if ((Dk / 8) * c.sb <= AttnMfma<1, 32>::kMaxLoads * kAttnBlock) return c;
+    c = AttnChoice{ATTN_NONE, 0, 0, 0};
   }
   if (Hq >= 1 && Hq * Dv <= 4096 && Dk <= 512 && Dv <= Dk) {
     c.kind = dt_bf16 ? ATTN_GENERIC_BF16 : ATTN_GENERIC_F32;
@@ -799,7 +801,9 @@ AttnChoice choose_attn(int dt_bf16, int Hq, int Dk, int Dv) {
     case ATTN_GENERIC_BF16: return FN<AttnGeneric<uint16_t>>(__VA_ARGS__);             \
     case ATTN_MFMA_BF16:                                                               \
       switch (ch.hqt) {                                                                \
-        case 1: return FN<AttnMfma<1, 32>>(__VA_ARGS__);                               \
+        case 1:                                                                        \
+          if (ch.nl == 5) return FN<AttnMfma<1, 32, 5>>(__VA_ARGS__);                  \
+          return FN<AttnMfma<1, 32>>(__VA_ARGS__);                                     \
         case 2: return FN<AttnMfma<2, 32>>(__VA_ARGS__);                               \
         case 3: return FN<AttnMfma<3, 32>>(__VA_ARGS__);                               \
         case 4: return FN<AttnMfma<4, 32>>(__VA_ARGS__);                               \
