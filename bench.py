@@ -12,7 +12,9 @@ streamed far more than the 256 MB Infinity Cache holds. The timed steps are HIP
 graph replays (one graph holds one step per set), bracketed by synchronisations.
 A second, eager pass over the same steps has the runtime stamp HIP events with the
 start and end of each stage's kernel (dsa_decode_step_timed), which times the
-indexer pass and the selection + attention pass live, kernel by kernel.
+indexer pass and the selection + attention pass live, kernel by kernel; its steps
+are queued in chunks behind a short sleep kernel, so they run back to back as in
+the graph rather than each starting on an idle GPU.
 
 Prints one JSON line (see the design doc for every field).
 """
@@ -297,8 +299,16 @@ def main():
             for e in per_layer:
                 e.record()
     torch.cuda.synchronize()
-    for i in range(K):
-        step(i % R, evs[i])
+    # The host takes longer to issue an eager step than the GPU takes to run it, so
+    # steps issued one after another would each start on an idle GPU. Each chunk of
+    # steps is therefore queued behind a sleep kernel (longer than the host needs to
+    # issue the chunk) and then runs back to back. Every step counts, so these means
+    # are the eager pass's means in the kernel trace of the same command.
+    chunk = 30
+    for i0 in range(0, K, chunk):
+        torch.cuda._sleep(16_000_000)  # several ms at the shader clock
+        for i in range(i0, min(K, i0 + chunk)):
+            step(i % R, evs[i])
     torch.cuda.synchronize()
     st = np.array([[[e[0].elapsed_time(e[1]), e[2].elapsed_time(e[3]), e[4].elapsed_time(e[5])]
                     for e in per_step] for per_step in evs]) * 1e3  # us [K][layers][3]

@@ -67,6 +67,28 @@ def kernel_stats(db):
              "min_us": r[5] / 1e3, "max_us": r[6] / 1e3, "pct": 100.0 * r[7] / total} for r in rows]
 
 
+def kernel_passes(db, split):
+    """Per library kernel (and grid), the mean duration of consecutive groups of its
+    calls in start order: split is [(label, count), ...], the passes of the command
+    in the order they ran."""
+    con = _db(db)
+    calls = {}
+    for name, grid, dur in con.execute("SELECT name, grid_x * grid_y * grid_z, end - start FROM kernels "
+                                       "ORDER BY start"):
+        if short_name(name) is not None:
+            calls.setdefault((name, grid), []).append(dur)
+    out = []
+    for (name, grid), durs in calls.items():
+        i = 0
+        for label, n in split:
+            part = durs[i:i + n]
+            i += n
+            if part:
+                out.append({"name": name, "grid": grid, "pass": label, "calls": len(part),
+                            "avg_us": sum(part) / len(part) / 1e3})
+    return out
+
+
 def counter_per_kernel(db, counter):
     """{kernel name: (dispatches, mean value per dispatch)} for one counter (KiB for *_SIZE)."""
     con = _db(db)
@@ -100,6 +122,19 @@ def cmd_stats(args):
                      % (nm.replace("|", "\\|"), r["grid"], r["calls"], r["avg_us"], r["min_us"], r["max_us"],
                         r["pct"]))
     lines.append("")
+    if args.split:
+        split = []
+        for item in args.split.split(","):
+            label, n = item.rsplit(":", 1)
+            split.append((label, int(n)))
+        lines += ["Library kernels by pass (each kernel's calls in start order: %s):"
+                  % ", ".join("%s %d" % s_ for s_ in split), "",
+                  "| kernel | grid threads | pass | calls | avg us |", "|---|---:|---|---:|---:|"]
+        for r in kernel_passes(args.db, split):
+            nm = r["name"] if len(r["name"]) <= 90 else r["name"][:87] + "..."
+            lines.append("| `%s` | %d | %s | %d | %.2f |"
+                         % (nm.replace("|", "\\|"), r["grid"], r["pass"], r["calls"], r["avg_us"]))
+        lines.append("")
     if args.note:
         lines += [args.note, ""]
     with open(args.out, "w") as f:
@@ -168,6 +203,7 @@ def main(argv=None):
     s.add_argument("--out", required=True)
     s.add_argument("--note", default="")
     s.add_argument("--top", type=int, default=14)
+    s.add_argument("--split", default="", help="label:count,... the passes of the command, in order")
     c = sub.add_parser("counters")
     c.add_argument("--fetch-db", required=True)
     c.add_argument("--write-db", required=True)
