@@ -118,17 +118,16 @@ struct ChunkPlan {
 };
 // One-row plan (score kernel k_score_row): chunks of whole 32-key units,
 // interleaved over the row, as many chunks as candidate slots allow (at most one
-// per compute unit), so every wave of a chunk has at most one unit more than
-// another. (cand_fits takes the plan only when a chunk fits the kernel, which
-// bounds a row to 2^21 positions, so every key offset fits a buffer offset.)
+// per compute unit; the chunk's waves claim its units as they go, so any count of
+// units balances). (cand_fits takes the plan only when a chunk fits the kernel,
+// which bounds a row to 2^21 positions, so every key offset fits a buffer offset.)
 ChunkPlan chunk_plan_row(int nmax, int k, int Di) {
   ChunkPlan c;
   c.m = k <= 2048 ? 32 : 64;
   c.ilv = 1;
   const int gmax = kCandCap / c.m < kMaxChunks ? kCandCap / c.m : kMaxChunks;
   const int64_t units = ((int64_t)nmax + 31) / 32;
-  int64_t per = (units + gmax - 1) / gmax;
-  if (per > 8) per = (per + 7) / 8 * 8;  // the same number of units for every wave
+  const int64_t per = (units + gmax - 1) / gmax;
   c.P = (int)(per * 32);
   c.G = (int)(((int64_t)nmax + c.P - 1) / c.P);
   return c;
