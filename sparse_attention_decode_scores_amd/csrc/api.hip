@@ -32,7 +32,7 @@ int rankers_for(int k) {
 
 // Byte offsets of the workspace regions.
 struct Layout {
-  size_t stats, cand, xc, sums, ml, o, bad, sort, total;
+  size_t stats, cand, xc, sums, ml, o, bad, total;
 };
 Layout layout(int B, int64_t N, int k, int Hq, int Dv) {
   const int S = splits_for(k, true);  // the larger of the two split counts
@@ -44,8 +44,7 @@ Layout layout(int B, int64_t N, int k, int Hq, int Dv) {
   L.ml = L.sums + up((size_t)B * kMaxChunks * sizeof(ChunkSum));
   L.o = L.ml + up((size_t)B * S * Hq * 8);
   L.bad = L.o + up((size_t)B * S * ((Hq + 15) / 16 * 16) * Dv * 4);
-  L.sort = L.bad + up((size_t)B * S * 4);
-  L.total = L.sort + up((size_t)B * 2 * (size_t)N * 8);
+  L.total = L.bad + up((size_t)B * S * 4);
   return L;
 }
 
@@ -83,22 +82,25 @@ dsa_status check_rows(const int32_t* ctx_len, int B, int64_t N, RowLens* lens, i
   return DSA_OK;
 }
 
+// Indexer shapes: Hi >= 1 and Di a positive multiple of 16 are valid; the kernels
+// are built for Hi <= 64 and Di <= 256 (DSA_ERR_UNSUPPORTED beyond).
 dsa_status check_index(const int8_t* iq, const int8_t* iw, const int8_t* ik, int Hi, int Di) {
   if (!iq || !iw || !ik) return DSA_ERR_INVALID_ARG;
-  if (Hi < 1 || Hi > DSA_MAX_INDEX_HEADS || Di < 32 || Di > DSA_MAX_INDEX_DIM || Di % 32 != 0)
-    return DSA_ERR_INVALID_ARG;
+  if (Hi < 1 || Di < 16 || Di % 16 != 0) return DSA_ERR_INVALID_ARG;
   if (!aligned(iq, 16) || !aligned(ik, 16)) return DSA_ERR_INVALID_ARG;
+  if (Hi > DSA_MAX_INDEX_HEADS || Di > DSA_MAX_INDEX_DIM) return DSA_ERR_UNSUPPORTED;
   return DSA_OK;
 }
 
 dsa_status check_attn(const void* q, const void* kv, int Hq, int Dk, int Dv, float scale,
                       dsa_dtype dt, AttnChoice* ch) {
+  // valid: Hq >= 1, Dk a positive multiple of 8, 1 <= Dv <= Dk; built: Hq <= 64, Dk <= 1024
   if (!q || !kv) return DSA_ERR_INVALID_ARG;
-  if (Hq < 1 || Hq > DSA_MAX_ATTN_HEADS || Dk < 1 || Dk > DSA_MAX_ATTN_DIM || Dv < 1 || Dv > Dk)
-    return DSA_ERR_INVALID_ARG;
+  if (Hq < 1 || Dk < 8 || Dk % 8 != 0 || Dv < 1 || Dv > Dk) return DSA_ERR_INVALID_ARG;
   if (dt != DSA_F32 && dt != DSA_BF16) return DSA_ERR_INVALID_ARG;
   if (!isfinite(scale)) return DSA_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(kv, 16)) return DSA_ERR_INVALID_ARG;
+  if (Hq > DSA_MAX_ATTN_HEADS || Dk > DSA_MAX_ATTN_DIM) return DSA_ERR_UNSUPPORTED;
   *ch = choose_attn(dt == DSA_BF16, Hq, Dk, Dv);
   if (ch->kind == ATTN_NONE) return DSA_ERR_UNSUPPORTED;
   if (select_lds_bytes(*ch, Hq, Dk, DSA_MAX_K) > (size_t)lds_limit()) return DSA_ERR_UNSUPPORTED;
@@ -153,7 +155,8 @@ ChunkPlan chunk_plan(int nmax, int k, bool row, int Di) {
 
 int rows_per_score_launch(int Hi, int Di, int B) {
   const int hp = (Hi + 31) / 32 * 32;  // Hi <= 64 and Di <= 256 give at least 4 rows
-  int bg = kScoreQBytes / (hp * Di);
+  const int dp = (Di + 31) / 32 * 32;  // staged with whole 32-dim steps
+  int bg = kScoreQBytes / (hp * dp);
   bg = bg < 1 ? 1 : bg;
   bg = bg * hp > 512 ? 512 / hp : bg;  // one head weight per thread of the block
   return bg < B ? bg : B;
@@ -187,7 +190,7 @@ dsa_status run_scores(const int8_t* iq, const int8_t* iw, const int8_t* ik, cons
     a.P = (int)((((int64_t)nmax + 64 * 2048 - 1) / (64 * 2048)) * 64);
     a.G = (int)(((int64_t)nmax + a.P - 1) / a.P);
   }
-  const int MT = (Hi + 31) / 32, KT = Di / 32;
+  const int MT = (Hi + 31) / 32, KT = (Di + 31) / 32;
   if (cand && B == 1) {  // the decode hot path: one row, candidates on
     a.b0 = 0;
     a.Bg = 1;
@@ -217,7 +220,7 @@ bool cand_fits(int Hi, int Di, int B, const ChunkPlan& cp, bool fused) {
   } else if (fused) {
     if (cp.P > score_max_chunk()) return false;
     const int bg = rows_per_score_launch(Hi, Di, B);
-    need = score_lds_bytes((Hi + 31) / 32, Di / 32, bg, cp.P, true);
+    need = score_lds_bytes((Hi + 31) / 32, (Di + 31) / 32, bg, cp.P, true);
   } else {
     if (cp.P > chunk_cand_max_chunk()) return false;
     need = 8192 + (size_t)cp.P * 4;
@@ -264,7 +267,6 @@ SelArgs sel_args(const int32_t* scores, const RowLens& lens, int64_t N, int k, i
   a.sums = sums && have_cand ? reinterpret_cast<const ChunkSum*>(w + L.sums) : nullptr;
   a.idx = idx;
   a.stats = reinterpret_cast<RowStats*>(w + L.stats);
-  a.sortbuf = reinterpret_cast<uint64_t*>(w + L.sort);
   a.lens = lens;
   a.N = N;
   a.k = k;

@@ -108,7 +108,7 @@ struct AttnMfma {
     int rr[kMaxLoads], cc[kMaxLoads];  // gather slot j of this thread: row, 16-byte column
     int lo[kMaxLoads];                 // its LDS byte offset among the staged rows
   };
-  __device__ static QFrag load_q(const AttnArgs& p, int b) {
+  __device__ __forceinline__ static QFrag load_q(const AttnArgs& p, int b) {
     QFrag f;
     {
       // gather slot j of this thread is chunk i = tid + 512 j of a sub-block: row
@@ -153,7 +153,7 @@ struct AttnMfma {
     }
     return f;
   }
-  __device__ static void store_q(const QFrag& f, const AttnArgs& p, uint8_t* work) {
+  __device__ __forceinline__ static void store_q(const QFrag& f, const AttnArgs& p, uint8_t* work) {
     if (!kQInLds) return;
     const int Dk = p.Dk, rb = row_bytes(Dk), cpr = Dk >> 3;
     const int step_h = kAttnBlock / cpr, step_c = kAttnBlock - step_h * cpr;
@@ -178,7 +178,7 @@ struct AttnMfma {
     uint8_t* rows;
     float *lg, *mrun, *lrun, *alpha, *lgp;
   };
-  __device__ static Work work_of(const AttnArgs& p, uint8_t* work) {
+  __device__ __forceinline__ static Work work_of(const AttnArgs& p, uint8_t* work) {
     Work w;
     w.qs = work;
     w.rows = work + q_bytes(p.Dk);
@@ -198,7 +198,7 @@ struct AttnMfma {
     v4i v[kMaxLoads];
   };
   template <typename PosAt>
-  __device__ static Rows gather(const AttnArgs& p, const QFrag& qf, PosAt pos_at, int nr) {
+  __device__ __forceinline__ static Rows gather(const AttnArgs& p, const QFrag& qf, PosAt pos_at, int nr) {
     const uint8_t* kv = reinterpret_cast<const uint8_t*>(p.kv);
     int32_t rp[kMaxLoads];
 #pragma unroll
@@ -210,7 +210,7 @@ struct AttnMfma {
   }
   // Stores gathered rows (absent rows as zeros) and, with `with_q`, the query heads;
   // the next barrier publishes them.
-  __device__ static void put(const Rows& r, const QFrag& qf, const AttnArgs& p, int nr, bool with_q,
+  __device__ __forceinline__ static void put(const Rows& r, const QFrag& qf, const AttnArgs& p, int nr, bool with_q,
                              uint8_t* work) {
     const Work w = work_of(p, work);
     const int rb = row_bytes(p.Dk), nch = SB * (p.Dk >> 3);  // nch <= kMaxLoads * block size
@@ -220,7 +220,7 @@ struct AttnMfma {
       if ((int)threadIdx.x + kAttnBlock * j < nch)
         *(v4i*)(w.rows + qf.lo[j]) = qf.rr[j] < nr ? r.v[j] : v4i{0, 0, 0, 0};
   }
-  __device__ static void begin(const AttnArgs& p, uint8_t* work, Acc& o) {
+  __device__ __forceinline__ static void begin(const AttnArgs& p, uint8_t* work, Acc& o) {
     const Work w = work_of(p, work);
 #pragma unroll
     for (int mt = 0; mt < HQT; ++mt)
@@ -236,14 +236,13 @@ struct AttnMfma {
   // the matrix cores, online-softmax update, then P V accumulated into o. With
   // `last`, no barrier follows (nothing overwrites the staged rows afterwards, and
   // finish reads only what the softmax barrier published).
-  __device__ static void sub_block(const AttnArgs& p, int b, uint64_t live, uint8_t* work, Acc& o,
+  __device__ __forceinline__ static void sub_block(const AttnArgs& p, int b, uint64_t live, uint8_t* work, Acc& o,
                                    bool last) {
     const int lane = lane_id(), wave = wave_id();
     const int Dk = p.Dk, KS = Dk >> 5, rb = row_bytes(Dk), nt_all = p.Dv >> 4;
     const Work w = work_of(p, work);
     const __bf16* q = reinterpret_cast<const __bf16*>(p.q) + (int64_t)b * p.Hq * Dk;
     lds_barrier();
-    DSA_MARK(1, 6);
     // logits: D[head][row], head = 16*mt + 4*(l/16) + r, row = 16*nt + l%16. Wave w
     // takes row tile w % kTiles and the w / kTiles-th share of the k-steps (every
     // wave works; one wave per tile would chain all k-steps), and writes its
@@ -293,10 +292,8 @@ struct AttnMfma {
         for (int r = 0; r < 4; ++r) w.lgp[(kq * HP + 16 * mt + 4 * (lane >> 4) + r) * SB + row] = acc[mt][r];
     }
     lds_barrier();
-    DSA_MARK(1, 7);
     softmax_update_parts32(w.lgp, kParts, HP, live, p.scale, w.lg, HP, w.mrun, w.lrun, w.alpha);
     lds_barrier();
-    DSA_MARK(1, 8);
     // output: D[head][dv] += P[head][row] V[row][dv]
 #pragma unroll
     for (int mt = 0; mt < HQT; ++mt)
@@ -355,13 +352,12 @@ struct AttnMfma {
       }
     }
     if (!last) lds_barrier();  // uniform
-    DSA_MARK(1, 9);
   }
 
   // The split's partial result: (max, sum) per head and the unnormalised output in
   // accumulator order: element ((mt * tiles + nt) * 64 + lane) * 4 + r is head
   // 16*mt + 4*(lane/16) + r, value 16*nt + lane%16 (one 16-byte store per tile).
-  __device__ static void finish(const AttnArgs& p, int b, int split, uint8_t* work, const Acc& o) {
+  __device__ __forceinline__ static void finish(const AttnArgs& p, int b, int split, uint8_t* work, const Acc& o) {
     const int lane = lane_id(), wave = wave_id(), nt_all = p.Dv >> 4;
     const Work w = work_of(p, work);
     const int64_t pb = (int64_t)b * p.S + split;
@@ -381,17 +377,14 @@ struct AttnMfma {
   // positions are staged SB at a time; the query fragments (load_q) are written to
   // LDS once the first sub-block's row loads are in flight.
   template <typename PosAt>
-  __device__ static void run(const AttnArgs& p, int b, int split, PosAt pos_at, int cnt,
+  __device__ __forceinline__ static void run(const AttnArgs& p, int b, int split, PosAt pos_at, int cnt,
                              uint8_t* work, const QFrag& qf) {
     Acc o;
     begin(p, work, o);
     for (int s0 = 0; s0 < cnt; s0 += SB) {
       const int nr = cnt - s0 < SB ? cnt - s0 : SB;
-      DSA_MARK(1, 12);
       const Rows r = gather(p, qf, [&](int i) { return pos_at(s0 + i); }, nr);
-      DSA_MARK(1, 13);
       put(r, qf, p, nr, s0 == 0, work);
-      DSA_MARK(1, 14);
       sub_block(p, b, nr >= 64 ? ~0ull : (1ull << nr) - 1ull, work, o, s0 + SB >= cnt);
     }
     finish(p, b, split, work, o);
@@ -407,17 +400,17 @@ struct AttnGeneric {
   __host__ __device__ static size_t lds_bytes(int Hq, int Dk) {
     return (size_t)SB * Dk * 4 + (size_t)Hq * Dk * 4 + (size_t)Hq * SB * 4 + 3 * (size_t)Hq * 4;
   }
-  __device__ static float ld(const void* base, int64_t i) {
+  __device__ __forceinline__ static float ld(const void* base, int64_t i) {
     if constexpr (sizeof(T) == 4) return reinterpret_cast<const float*>(base)[i];
     else return bf16_to_f32(reinterpret_cast<const uint16_t*>(base)[i]);
   }
 
   struct QFrag {};
-  __device__ static QFrag load_q(const AttnArgs&, int) { return QFrag{}; }
-  __device__ static void store_q(const QFrag&, const AttnArgs&, uint8_t*) {}
+  __device__ __forceinline__ static QFrag load_q(const AttnArgs&, int) { return QFrag{}; }
+  __device__ __forceinline__ static void store_q(const QFrag&, const AttnArgs&, uint8_t*) {}
 
   template <typename PosAt>
-  __device__ static void run(const AttnArgs& p, int b, int split, PosAt pos_at, int cnt,
+  __device__ __forceinline__ static void run(const AttnArgs& p, int b, int split, PosAt pos_at, int cnt,
                              uint8_t* work, const QFrag&) {
     const int tid = threadIdx.x;
     const int Hq = p.Hq, Dk = p.Dk, Dv = p.Dv;
@@ -479,10 +472,10 @@ struct AttnGeneric {
 struct AttnNone {
   __host__ __device__ static size_t lds_bytes(int, int) { return 0; }
   struct QFrag {};
-  __device__ static QFrag load_q(const AttnArgs&, int) { return QFrag{}; }
-  __device__ static void store_q(const QFrag&, const AttnArgs&, uint8_t*) {}
+  __device__ __forceinline__ static QFrag load_q(const AttnArgs&, int) { return QFrag{}; }
+  __device__ __forceinline__ static void store_q(const QFrag&, const AttnArgs&, uint8_t*) {}
   template <typename PosAt>
-  __device__ static void run(const AttnArgs&, int, int, PosAt, int, uint8_t*, const QFrag&) {}
+  __device__ __forceinline__ static void run(const AttnArgs&, int, int, PosAt, int, uint8_t*, const QFrag&) {}
 };
 
 }  // namespace dsa

@@ -93,7 +93,6 @@ __device__ __forceinline__ void chunk_candidates(const int32_t* scores, int coun
     for (int j = 0; j < kChunkPerThread; ++j)
       if (j < per && i0 + j < count) f(u[j]);
   };
-  DSA_MARK(3, 0);
   {
     const uint32_t mine[2] = {~wave_min_u32(lo), wave_maxr_u32(hi)};
     uint32_t all[BLOCK / 64][2];
@@ -108,9 +107,7 @@ __device__ __forceinline__ void chunk_candidates(const int32_t* scores, int coun
     hi = mhi;
   }
   uint32_t above;
-  DSA_MARK(3, 1);
   const uint32_t T = block_select_range<BLOCK>(each, lo, hi, m + 1, &above, sm.radix);
-  DSA_MARK(3, 8);
   const uint32_t need_eq = (uint32_t)(m + 1) - above;  // >= 1: keys at T up to and including x
   uint32_t gt = 0, eq = 0;
   each([&](uint32_t v) {
@@ -122,7 +119,6 @@ __device__ __forceinline__ void chunk_candidates(const int32_t* scores, int coun
   const uint32_t eq_before = before >> 16;
   uint32_t slot = (before & 0xFFFF) + (eq_before < need_eq - 1 ? eq_before : need_eq - 1);
   uint32_t eqr = eq_before;
-  DSA_MARK(3, 9);
 #pragma unroll
   for (int j = 0; j < kChunkPerThread; ++j) {
     const int i = i0 + j;
@@ -137,7 +133,6 @@ __device__ __forceinline__ void chunk_candidates(const int32_t* scores, int coun
       }
     }
   }
-  DSA_MARK(3, 10);
 }
 
 // Lowest score of the bin that holds the (m+1)-th best of `count` keys (m < count),
@@ -223,7 +218,6 @@ __device__ __forceinline__ bool wave_chunk_candidates(const int32_t* scores, int
                                                       CandOut out,
                                                       uint64_t* __restrict__ x_out, uint64_t* stage) {
   const int l = lane_id();
-  DSA_MARK(3, 0);
   if (count <= m) {
     for (int i = l; i < m; i += 64) out.put(i, i < count ? make_key(scores[i], pos0 + (uint32_t)i) : 0ull);
     if (l == 0) *x_out = 0;
@@ -254,7 +248,6 @@ __device__ __forceinline__ bool wave_chunk_candidates(const int32_t* scores, int
     }
   }
   if (ns > cap) return false;
-  DSA_MARK(3, 8);
 
   const bool two = ns > 64;
   const uint64_t k0 = l < (int)ns ? stage[l] : 0ull;
@@ -275,7 +268,6 @@ __device__ __forceinline__ bool wave_chunk_candidates(const int32_t* scores, int
       if (two) r1 += (live && x > k1) ? 1u : 0u;
     }
   }
-  DSA_MARK(3, 9);
   // staged keys are distinct, so the ranks are a permutation of 0 .. ns-1
   const bool s0 = l < (int)ns && r0 < (uint32_t)m;
   const bool s1 = l + 64 < (int)ns && r1 < (uint32_t)m;
@@ -288,7 +280,6 @@ __device__ __forceinline__ bool wave_chunk_candidates(const int32_t* scores, int
   const uint32_t xlo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)xk, xl);
   const uint32_t xhi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(xk >> 32), xl);
   if (l == 0) *x_out = ((uint64_t)xhi << 32) | xlo;
-  DSA_MARK(3, 10);
   return true;
 }
 
@@ -337,12 +328,10 @@ __device__ __forceinline__ bool block_chunk_candidates(const int32_t* scores, in
       sm.tlo = t;
       sm.ok = ok ? 1u : 0u;
     }
-    DSA_MARK(3, 2);
   }
   lds_barrier();
   if (!sm.ok) return false;  // uniform
   const int32_t tlo = sm.tlo;
-  DSA_MARK(3, 1);
 
   const uint64_t lt = lanemask_lt();
   const uint32_t cap = (uint32_t)m + 64;
@@ -369,10 +358,8 @@ __device__ __forceinline__ bool block_chunk_candidates(const int32_t* scores, in
       }
     }
     if (l == 0) sm.wcount[w] = ns;
-    DSA_MARK(3, 3);
   }
   lds_barrier();
-  DSA_MARK(3, 4);
   uint32_t total = 0, off = 0;
 #pragma unroll
   for (int q = 0; q < W; ++q) {
@@ -383,9 +370,7 @@ __device__ __forceinline__ bool block_chunk_candidates(const int32_t* scores, in
   if (total > cap) return false;  // uniform
   if (active)
     for (int j = l; j < (int)ns; j += 64) sm.all[off + j] = sm.wstage[w][j];
-  DSA_MARK(3, 5);
   lds_barrier();
-  DSA_MARK(3, 8);
 
   // rank of staged key i: tpe active threads each compare it with every tpe-th key
   const int tpe = total > (uint32_t)(AT / 4) ? 2 : 4;  // AT / tpe >= cap keys
@@ -399,7 +384,6 @@ __device__ __forceinline__ bool block_chunk_candidates(const int32_t* scores, in
   if (tpe == 4) r += (uint32_t)__builtin_amdgcn_mov_dpp((int)r, dpp::kQuadXor2, 0xF, 0xF, false);
   if (active && part == 0 && i < (int)total) sm.rank[i] = r;
   lds_barrier();
-  DSA_MARK(3, 9);
 
   if (w == 0) {
     for (int q = 0; q < (int)total; q += 64) {
@@ -409,7 +393,6 @@ __device__ __forceinline__ bool block_chunk_candidates(const int32_t* scores, in
       if (rk == (uint32_t)m) *x_out = sm.all[j];
     }
   }
-  DSA_MARK(3, 10);
   return true;
 }
 

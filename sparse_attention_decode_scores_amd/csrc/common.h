@@ -74,69 +74,6 @@ __device__ __forceinline__ void lds_barrier() {
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 __device__ __forceinline__ uint64_t lanemask_lt() { return (1ull << lane_id()) - 1ull; }
 
-// Phase timestamps for performance analysis builds (-DDSA_TRACE): thread 0 of a
-// workgroup keeps the 100 MHz real-time counter per phase in LDS (a global store
-// here would hold up the wave's next wait for memory) and copies the table out at
-// the kernel's exits. In normal builds the marks compile to nothing.
-#ifdef DSA_TRACE
-constexpr int kTraceKernels = 4, kTraceBlocks = 512, kTracePhases = 16;
-extern __device__ uint64_t dsa_trace[kTraceKernels][kTraceBlocks][kTracePhases];
-__device__ __forceinline__ uint64_t* dsa_trace_lds() {
-  __shared__ uint64_t t[kTraceKernels * kTracePhases];
-  return t;
-}
-#define DSA_TRACE_BEGIN()                                                                    \
-  do {                                                                                       \
-    if (threadIdx.x == 0)                                                                    \
-      for (int i_ = 0; i_ < kTraceKernels * kTracePhases; ++i_) dsa_trace_lds()[i_] = 0;     \
-  } while (0)
-#ifdef DSA_TRACE_CLOCK
-// also the shader clock counter of kernel-0 marks, in the kernel-2 table
-#define DSA_MARK(kernel, phase)                                                              \
-  do {                                                                                       \
-    if (threadIdx.x == 0) {                                                                  \
-      dsa_trace_lds()[(kernel) * kTracePhases + (phase)] = __builtin_amdgcn_s_memrealtime(); \
-      if ((kernel) == 0) dsa_trace_lds()[2 * kTracePhases + (phase)] = __builtin_amdgcn_s_memtime(); \
-    }                                                                                        \
-  } while (0)
-#else
-#define DSA_MARK(kernel, phase)                                                              \
-  do {                                                                                       \
-    if (threadIdx.x == 0)                                                                    \
-      dsa_trace_lds()[(kernel) * kTracePhases + (phase)] = __builtin_amdgcn_s_memrealtime(); \
-  } while (0)
-#endif
-// per-wave stamp: lane 0 of wave w writes phase (phase0 + w)
-#define DSA_MARK_WAVE(kernel, phase0)                                                        \
-  do {                                                                                       \
-    if ((threadIdx.x & 63) == 0)                                                             \
-      dsa_trace_lds()[(kernel) * kTracePhases + (phase0) + (threadIdx.x >> 6)] =               \
-          __builtin_amdgcn_s_memrealtime();                                                  \
-  } while (0)
-#define DSA_TRACE_FLUSH()                                                                    \
-  do {                                                                                       \
-    const int blk_ = blockIdx.x + gridDim.x * blockIdx.y;                                    \
-    if (threadIdx.x == 0 && blk_ < kTraceBlocks)                                             \
-      for (int i_ = 0; i_ < kTraceKernels * kTracePhases; ++i_) {                            \
-        const uint64_t v_ = dsa_trace_lds()[i_];                                             \
-        if (v_) dsa_trace[i_ / kTracePhases][blk_][i_ % kTracePhases] = v_;                  \
-      }                                                                                      \
-  } while (0)
-#else
-#define DSA_TRACE_BEGIN() \
-  do {                    \
-  } while (0)
-#define DSA_MARK(kernel, phase) \
-  do {                          \
-  } while (0)
-#define DSA_MARK_WAVE(kernel, phase0) \
-  do {                                \
-  } while (0)
-#define DSA_TRACE_FLUSH() \
-  do {                    \
-  } while (0)
-#endif
-
 // ---- wave primitives on the DPP datapath (VALU-speed lane exchange; the ds_
 // shuffle path costs an LDS round trip per step).
 namespace dpp {
@@ -252,6 +189,7 @@ struct RadixSmem {
   uint32_t hist[2][kRadixBins];  // alternate passes; each pass leaves its buffer zeroed
   uint32_t part[16];
   uint32_t digit, above, inbin;
+  uint32_t tdigit[2], tabove[2], tinbin[2];  // block_narrow_first: one record per target
 };
 
 // Zeroes both histogram buffers; call once before the first block_select_range
@@ -323,7 +261,6 @@ __device__ __forceinline__ RadixBin block_narrow(Each each, uint32_t lo, uint32_
     }
     first = false;
     lds_barrier();
-    DSA_MARK(3, 2 + 2 * (shift > kRadixBits ? 0 : 1));
     uint32_t h[BPT], own = 0;
 #pragma unroll
     for (int j = 0; j < BPT; ++j) {
@@ -345,7 +282,6 @@ __device__ __forceinline__ RadixBin block_narrow(Each each, uint32_t lo, uint32_
       ab += h[j];
     }
     lds_barrier();
-    DSA_MARK(3, 3 + 2 * (shift > kRadixBits ? 0 : 1));
     const uint32_t d = sm.digit, ab2 = sm.above;
     inbin = sm.inbin;
     need -= ab2;
@@ -355,7 +291,59 @@ __device__ __forceinline__ RadixBin block_narrow(Each each, uint32_t lo, uint32_
     buf ^= 1;
   }
   const uint32_t binlo = lo + (prefix << shift);  // shift <= 21 after a pass
-  return RadixBin{binlo, binlo + ((1u << shift) - 1u), above, inbin};
+  const uint32_t top = binlo + ((1u << shift) - 1u);  // values above hi do not occur
+  return RadixBin{binlo, (top < binlo || top > hi) ? hi : top, above, inbin};
+}
+
+// The first radix pass of block_narrow for NT <= 2 ranks at once (one histogram
+// serves every rank): out[t] is the bin that holds the need[t]-th largest value
+// (1 <= need[t] <= n). Every thread gets the same results; the pass leaves its
+// histogram buffer zeroed. Three barriers (none when every value is equal).
+template <int BLOCK, int NT, class Each>
+__device__ __forceinline__ void block_narrow_first(Each each, uint32_t lo, uint32_t hi, const uint32_t (&need)[NT],
+                                                   uint32_t n, RadixSmem& sm, RadixBin (&out)[NT]) {
+  static_assert(kRadixBins % BLOCK == 0 && NT >= 1 && NT <= 2, "bins per thread, targets");
+  constexpr int BPT = kRadixBins / BLOCK;
+  const int tid = threadIdx.x;
+  const uint32_t range = hi - lo;
+  if (range == 0) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) out[t] = RadixBin{hi, hi, 0u, n};
+    return;
+  }
+  const int shift = 32 - __clz(range);
+  const int nshift = shift > kRadixBits ? shift - kRadixBits : 0;
+  uint32_t* hist = sm.hist[0];
+  each([&](uint32_t v) { atomicAdd(&hist[((v - lo) >> nshift) & (kRadixBins - 1)], 1u); });
+  lds_barrier();
+  uint32_t h[BPT], own = 0;
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) {
+    h[j] = hist[tid * BPT + j];
+    hist[tid * BPT + j] = 0;
+    own += h[j];
+  }
+  uint32_t total;
+  const uint32_t before = block_excl_scan_fresh_u32<BLOCK>(own, sm.part, &total);
+  uint32_t ab = total - before - own;
+#pragma unroll
+  for (int j = BPT - 1; j >= 0; --j) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      if (ab < need[t] && need[t] <= ab + h[j]) {
+        sm.tdigit[t] = tid * BPT + j;
+        sm.tabove[t] = ab;
+        sm.tinbin[t] = h[j];
+      }
+    ab += h[j];
+  }
+  lds_barrier();
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const uint32_t binlo = lo + (sm.tdigit[t] << nshift);
+    const uint32_t top = binlo + ((1u << nshift) - 1u);
+    out[t] = RadixBin{binlo, (top < binlo || top > hi) ? hi : top, sm.tabove[t], sm.tinbin[t]};
+  }
 }
 
 // Score-level radix selection: T, the rank-th largest value, and the number of

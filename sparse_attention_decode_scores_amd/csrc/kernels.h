@@ -126,7 +126,6 @@ struct SelArgs {
   const ChunkSum* sums;  // [B][kMaxChunks] from the one-row score pass, or nullptr
   int32_t* idx;        // [B][k]
   RowStats* stats;     // [B]
-  uint64_t* sortbuf;   // [B][2][N] scratch of the exhaustive path
   RowLens lens;
   int64_t N;
   int k;

@@ -29,16 +29,18 @@ static_assert(kScoreQBytes % (16 * kScoreBlock) == 0, "query staging slots");
 namespace {
 
 // Key fragment of the B operand: lane l holds 16 consecutive dims of key
-// (64*tile + 32*t + (l & 31)) of the chunk, starting at dim 32*kt + 16*(l >> 5).
-// Raw buffer loads against a resource that covers exactly the chunk's valid keys:
-// always issued (so the compiler's wait counts stay exact), zero past the end
-// without touching memory.
+// (64*tile + 32*t + (l & 31)) of the chunk, starting at dim 32*kt + 16*(l >> 5);
+// keys are Di bytes apart. Raw buffer loads against a resource that covers exactly
+// the chunk's valid keys: always issued (so the compiler's wait counts stay exact),
+// zero past the end without touching memory. (When Di = 32·KT - 16, the last
+// fragment's upper half reads the next key's first dims or zeros; the query's
+// matching half is zero, so those products vanish.)
 template <int KT>
-__device__ __forceinline__ void load_keys(v4i (&kf)[2][KT], __amdgpu_buffer_rsrc_t rs, int tile) {
+__device__ __forceinline__ void load_keys(v4i (&kf)[2][KT], __amdgpu_buffer_rsrc_t rs, int tile, int Di) {
   const int lane = lane_id();
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const int off = (64 * tile + 32 * t + (lane & 31)) * (32 * KT) + 16 * (lane >> 5);
+    const int off = (64 * tile + 32 * t + (lane & 31)) * Di + 16 * (lane >> 5);
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt)
       kf[t][kt] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 32 * kt, 0, 0));
@@ -64,8 +66,6 @@ __global__ __launch_bounds__(kScoreBlock) void k_score(ScoreArgs a) {
 
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   const int c = blockIdx.x;
-  DSA_TRACE_BEGIN();
-  DSA_MARK(0, 0);
   const int64_t cbeg = (int64_t)c * a.P;
   const int64_t clen64 = (int64_t)a.nmax - cbeg;
   const int clen = clen64 > a.P ? a.P : (int)(clen64 > 0 ? clen64 : 0);
@@ -89,7 +89,8 @@ __global__ __launch_bounds__(kScoreBlock) void k_score(ScoreArgs a) {
     int h = rem / (DI / 16);
     const int part = rem - h * (DI / 16);
     h = h < a.Hi ? h : a.Hi - 1;
-    qv[j] = *(const v4i*)(a.iq + ((int64_t)(a.b0 + bb) * a.Hi + h) * DI + 16 * part);
+    // 16-byte parts past Di (Di = 32·KT - 16) read a present part and are zeroed below
+    qv[j] = *(const v4i*)(a.iq + ((int64_t)(a.b0 + bb) * a.Hi + h) * a.Di + (16 * part < a.Di ? 16 * part : 0));
   }
   const int wi = tid < a.Bg * HP ? tid : a.Bg * HP - 1;
   const int wh = wi % HP < a.Hi ? wi % HP : a.Hi - 1;
@@ -97,12 +98,11 @@ __global__ __launch_bounds__(kScoreBlock) void k_score(ScoreArgs a) {
 
   // buffer resource word 3 for gfx9 raw buffers: 32-bit data format, no swizzle
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<int8_t*>(a.ik + cbeg * DI), (short)0, clen * DI, 0x00020000);
+      const_cast<int8_t*>(a.ik + cbeg * a.Di), (short)0, clen * a.Di, 0x00020000);
   v4i kb0[2][KT], kb1[2][KT], kb2[2][KT];
-  load_keys<KT>(kb0, rs, wave);
-  load_keys<KT>(kb1, rs, wave + kScoreWaves);
-  load_keys<KT>(kb2, rs, wave + 2 * kScoreWaves);
-  DSA_MARK(0, 9);
+  load_keys<KT>(kb0, rs, wave, a.Di);
+  load_keys<KT>(kb1, rs, wave + kScoreWaves, a.Di);
+  load_keys<KT>(kb2, rs, wave + 2 * kScoreWaves, a.Di);
 
   if (CAND) {
     radix_clear<kScoreBlock>(csm.radix);
@@ -112,12 +112,11 @@ __global__ __launch_bounds__(kScoreBlock) void k_score(ScoreArgs a) {
   for (int j = 0; j < kQPer; ++j) {
     const int i = tid + kScoreBlock * j;
     const int h = (i % (HP * (DI / 16))) / (DI / 16);
-    if (i < nq) *(v4i*)(qs + 16 * i) = h < a.Hi ? qv[j] : v4i{0, 0, 0, 0};
+    const int part = i % (DI / 16);
+    if (i < nq) *(v4i*)(qs + 16 * i) = h < a.Hi && 16 * part < a.Di ? qv[j] : v4i{0, 0, 0, 0};
   }
   if (tid < a.Bg * HP) wsm[tid] = tid % HP < a.Hi ? wv : (int8_t)0;
-  DSA_MARK(0, 10);
   lds_barrier();
-  DSA_MARK(0, 11);
 
   // A fragments and weights of a single row stay in registers for the whole chunk.
   v4i qreg[ONE ? MT : 1][ONE ? KT : 1];
@@ -190,10 +189,9 @@ __global__ __launch_bounds__(kScoreBlock) void k_score(ScoreArgs a) {
         a.scores[(int64_t)(a.b0 + bb) * a.N + pos] = val;
       }
     }
-    load_keys<KT>(cur, rs, tp + 3 * kScoreWaves);
+    load_keys<KT>(cur, rs, tp + 3 * kScoreWaves, a.Di);
   };
 
-  DSA_MARK(0, 1);
   // three key buffers rotate by name (a register copy would wait for its load)
   for (int tp = wave; tp < npairs; tp += 3 * kScoreWaves) {
     tile(kb0, tp);
@@ -203,16 +201,13 @@ __global__ __launch_bounds__(kScoreBlock) void k_score(ScoreArgs a) {
     tile(kb2, tp + 2 * kScoreWaves);
   }
 
-  DSA_MARK(0, 2);
   if (CAND) {
     lds_barrier();
-    DSA_MARK(0, 3);
     // the scores leave LDS first: the selection below waits for no memory
     // operation, so these stores complete underneath it. The key requests past
     // the chunk's end (buffer reads that return zeros) are drained before them,
     // so no later wait for those registers covers the stores.
     __builtin_amdgcn_s_waitcnt(0x0F70);  // gfx9 encoding: vmcnt(0), expcnt and lgkmcnt untouched
-    DSA_MARK(0, 6);
     for (int bb = 0; bb < a.Bg; ++bb) {
       const int b = a.b0 + bb;
       const int64_t n64 = (int64_t)a.lens.n[b] - cbeg;
@@ -220,7 +215,6 @@ __global__ __launch_bounds__(kScoreBlock) void k_score(ScoreArgs a) {
       int32_t* dst = a.scores + (int64_t)b * a.N + cbeg;
       for (int i = tid; i < count; i += kScoreBlock) dst[i] = sc[bb * a.P + i];
     }
-    DSA_MARK(0, 7);
     if (ONE) {
       // one row: the whole block selects the chunk's candidates
       const int b = a.b0;
@@ -242,7 +236,6 @@ __global__ __launch_bounds__(kScoreBlock) void k_score(ScoreArgs a) {
         if (lane == 0) fallback[bb] = ok ? 0 : 1;
       }
     }
-    DSA_MARK(0, 5);
     lds_barrier();
     for (int bb = 0; bb < a.Bg; ++bb) {  // rows whose threshold bin held too many keys
       if (!fallback[bb]) continue;
@@ -254,9 +247,7 @@ __global__ __launch_bounds__(kScoreBlock) void k_score(ScoreArgs a) {
                                     csm);
       lds_barrier();
     }
-    DSA_MARK(0, 4);
   }
-  DSA_TRACE_FLUSH();
 }
 
 // ------------------------------------------------------------------ one query row
@@ -281,13 +272,13 @@ struct RowCandSmem {
 namespace {
 
 // B fragments of the chunk's unit j (keys 32j·js .. 32j·js + 31 from the chunk's
-// first key): lane l holds dims 32kt + 16(l >> 5) .. +15 of the unit's key l & 31.
-// Raw buffer loads against a resource that ends with the chunk's last valid key
-// (zeros past it).
+// first key, Di bytes apart): lane l holds dims 32kt + 16(l >> 5) .. +15 of the
+// unit's key l & 31. Raw buffer loads against a resource that ends with the chunk's
+// last valid key (zeros past it); dims past Di meet a zero query half (load_keys).
 template <int KT>
-__device__ __forceinline__ void load_unit(v4i (&kf)[KT], __amdgpu_buffer_rsrc_t rs, int j, int js) {
+__device__ __forceinline__ void load_unit(v4i (&kf)[KT], __amdgpu_buffer_rsrc_t rs, int j, int js, int Di) {
   const int lane = lane_id();
-  const int off = (kUnit * j * js + (lane & 31)) * (32 * KT) + 16 * (lane >> 5);
+  const int off = (kUnit * j * js + (lane & 31)) * Di + 16 * (lane >> 5);
 #pragma unroll
   for (int kt = 0; kt < KT; ++kt)
     kf[kt] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 32 * kt, 0, 0));
@@ -298,14 +289,13 @@ __device__ __forceinline__ void load_unit(v4i (&kf)[KT], __amdgpu_buffer_rsrc_t 
 // The arguments that the first requests need come first, as separate scalars: the
 // leading arguments can be preloaded into scalar registers at wave launch, so the
 // query and key requests need not wait for a read of the argument block (a.iq,
-// a.iw, a.ik, a.lens.n[0], a.G, a.P and a.Hi, passed again).
+// a.iw, a.ik, a.lens.n[0], a.G, a.P, a.Hi and a.Di, passed again).
 template <int MT, int KT, int D>
 __global__ __launch_bounds__(kScoreBlock) void k_score_row(const int8_t* __restrict__ iq,
                                                            const int8_t* __restrict__ iw,
                                                            const int8_t* __restrict__ ik, int n, int G, int P,
-                                                           int Hi, ScoreArgs a) {
+                                                           int Hi, int Di, ScoreArgs a) {
   static_assert(D == 2 || D == 3, "units in flight per wave");
-  constexpr int DI = 32 * KT;
   extern __shared__ __align__(16) uint8_t smem[];
   using Smem = ChunkSmem<kScoreBlock>;
   Smem& csm = *reinterpret_cast<Smem*>(smem);
@@ -319,8 +309,6 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(const int8_t* __restr
   // known at entry and their reads go out together (an index read from the argument
   // block would put a second round trip before the first key request)
   const int c = blockIdx.x, b = 0;
-  DSA_TRACE_BEGIN();
-  DSA_MARK(0, 0);
   // Chunk c is the row's 32-key units c, c + G, c + 2G, ... (interleaved, so that at
   // any moment the launch streams one contiguous stretch of keys): local unit j is
   // row unit c + j·G.
@@ -334,14 +322,23 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(const int8_t* __restr
   const int span = units > 0 ? (int)((int64_t)(units - 1) * ustride) + (count - kUnit * (units - 1)) : 0;
 
   // A operand: lane l holds head 32mt + (l & 31), dims 32kt + 16(l >> 5) .. +15; lane
-  // l also holds the weight of head l (Hi <= 64). Requested before any key.
-  const int8_t* qrow = iq + (int64_t)b * Hi * DI;
+  // l also holds the weight of head l (Hi <= 64). Requested before any key, as raw
+  // buffer loads over the row's Hi·Di query bytes: dims past Di (Di = 32·KT - 16) are
+  // given an offset past the end and so read as zeros (no operation on the loaded
+  // values, which the scheduler could place, with a wait for the query, ahead of the
+  // key requests); padding heads read a present head and are zeroed after them.
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(iq + (int64_t)b * Hi * Di), (short)0, Hi * Di, 0x00020000);
   v4i qreg[MT][KT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int h = 32 * mt + (lane & 31) < Hi ? 32 * mt + (lane & 31) : Hi - 1;
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt) qreg[mt][kt] = *(const v4i*)(qrow + h * DI + 32 * kt + 16 * (lane >> 5));
+    for (int kt = 0; kt < KT; ++kt) {
+      const int d0 = 32 * kt + 16 * (lane >> 5);
+      qreg[mt][kt] =
+          __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rq, d0 < Di ? h * Di + d0 : Hi * Di, 0, 0));
+    }
   }
   const int wl = (int)iw[(int64_t)b * Hi + (lane < Hi ? lane : Hi - 1)];
 
@@ -354,11 +351,11 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(const int8_t* __restr
   lds_barrier();
 
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<int8_t*>(ik + cbeg * DI), (short)0, span * DI, 0x00020000);
+      const_cast<int8_t*>(ik + cbeg * Di), (short)0, span * Di, 0x00020000);
   v4i kb0[KT], kb1[KT], kb2[KT];
-  load_unit<KT>(kb0, rs, wave, js);
-  load_unit<KT>(kb1, rs, wave + kScoreWaves, js);
-  if constexpr (D == 3) load_unit<KT>(kb2, rs, wave + 2 * kScoreWaves, js);
+  load_unit<KT>(kb0, rs, wave, js, Di);
+  load_unit<KT>(kb1, rs, wave + kScoreWaves, js, Di);
+  if constexpr (D == 3) load_unit<KT>(kb2, rs, wave + 2 * kScoreWaves, js, Di);
 
   // weights in accumulator order: value r of tile mt at lane l is head
   // 32mt + 8(r / 4) + 4(l >> 5) + r % 4; padding heads (q = 0) get weight 0
@@ -400,7 +397,7 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(const int8_t* __restr
           acc[mt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(qreg[mt][kt], kf[kt], acc[mt], 0, 0, 0);
     }
     const int jn = __builtin_amdgcn_readfirstlane((int)nxt);
-    load_unit<KT>(kf, rs, jn, js);
+    load_unit<KT>(kf, rs, jn, js, Di);
     if (live) {
       // two independent multiply-add chains (left to itself the compiler pairs the
       // products with three-input adds, 2.5 instructions per head instead of 2)
@@ -430,7 +427,6 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(const int8_t* __restr
     j = jn;
   };
 
-  DSA_MARK(0, 1);
   // The buffers rotate by name (a register copy would wait for its load) and are
   // taken in the order their loads were issued, every iteration the same, and the
   // loop only exits at its head. Claimed units increase, so j0 < j1 (< j2)
@@ -441,10 +437,7 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(const int8_t* __restr
     unit(kb1, j1);
     if constexpr (D == 3) unit(kb2, j2);
   }
-  DSA_MARK(0, 2);
-  DSA_MARK_WAVE(0, 8);
   lds_barrier();  // every score and histogram count of the chunk is in LDS
-  DSA_MARK(0, 3);
 
   const int m = a.m;
   const CandOut out{a.cand + (int64_t)b * kCandCap, c * m};
@@ -471,14 +464,12 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(const int8_t* __restr
       // position order: best first only when at most one key is present
       if (lane == 0) a.sums[(int64_t)b * kMaxChunks + c] = ChunkSum{lo, hi, count <= 1 ? 1u : 0u, 0u};
     }
-    DSA_TRACE_FLUSH();
     return;
   }
 
   // 1. every wave finds the bin that holds the (m+1)-th best key (same result in each)
   int32_t tlo = 0;
   const bool hok = hist_threshold(hist, hgroup, count, (uint32_t)m + 1, &tlo);
-  DSA_MARK(0, 6);
   // 2. every key scoring at least that bin's floor is staged, in order of arrival
   //    (the ranks below fix the output order): four positions per thread per pass
   for (int i0 = 0; i0 < units * kUnit; i0 += 4 * kScoreBlock) {
@@ -510,7 +501,6 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(const int8_t* __restr
     }
   }
   lds_barrier();
-  DSA_MARK(0, 7);
   const uint32_t total = rsm.nstaged;
   const bool fast = hok && total <= (uint32_t)m + 64;  // uniform over the block
   if (fast) {
@@ -558,8 +548,6 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(const int8_t* __restr
     if (a.sums != nullptr && tid == 0)
       a.sums[(int64_t)b * kMaxChunks + c] = ChunkSum{0u, 0xFFFFFFFFu, 0u, 0u};
   }
-  DSA_MARK(0, 4);
-  DSA_TRACE_FLUSH();
 }
 
 size_t score_row_lds_bytes(int P) {
@@ -577,7 +565,7 @@ static hipError_t launch_score_row_t(const ScoreArgs& a, int D, int grid, hipStr
                                      (int)lds);
   if (e != hipSuccess) return e;
   return launch_timed(fn, dim3(grid), dim3(kScoreBlock), lds, s, t, a.iq, a.iw, a.ik, a.lens.n[0], a.G, a.P, a.Hi,
-                      a);
+                      a.Di, a);
 }
 
 hipError_t launch_score_row(const ScoreArgs& a, int MT, int KT, int D, int grid, hipStream_t s,

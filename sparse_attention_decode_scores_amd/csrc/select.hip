@@ -5,31 +5,29 @@
 // (2026-09-09 "rising" page, long-context paragraph): parallel scans narrow the
 // candidates, a small surviving list is ordered, and the original exhaustive
 // algorithm handles the ambiguous cases; the same positions come out in the same
-// order either way.
+// order, and the same outputs, either way.
 //  * Candidate path. The score pass left, for every chunk of positions, its m
 //    best keys and the best key it dropped (x_c). Every workgroup of this kernel
 //    loads that candidate union U (at most 8192 keys, 16 per thread in
-//    registers), narrows by radix passes over the scores (and, when one score
-//    value holds many keys, over the positions of those keys) to a key range
-//    that holds the k-th largest key K* and at most 256 keys, ranks the keys of
-//    that range among themselves, and checks that no chunk dropped a key >= K*.
-//    When that holds, the top k of the row are exactly the keys of U that are
-//    >= K*: the keys above the range, in union order, then the best of the
-//    range, in key order.
-//  * Exhaustive path ("ambiguous" case: a chunk holds more than m keys at or
-//    above K*, which happens when many positions tie at the threshold; or the
-//    flag forces it): the top-k set comes from a radix selection over every
-//    position of the row, and the ordered output from a full stable sort of the
-//    row by score (least-significant-digit radix sort, which keeps the position
-//    order of equal scores).
+//    registers) and narrows it by radix passes over the scores (and, when one
+//    score value holds many keys, over the positions of those keys). The top k of
+//    U are the top k of the row when every dropped key is below the k-th key of
+//    U: then at least k keys of U lie above the best dropped key.
+//  * Exhaustive path ("ambiguous" case: some chunk holds more than m keys at or
+//    above the k-th key, which happens when many positions tie at the threshold;
+//    rows too long for the candidate pass; or the flag forces it): a radix
+//    selection over every position of the row gives the same top-k set.
 // Two roles share the launch, so no second kernel boundary is spent:
 //  * ranking workgroups order the selected keys: each takes a slice and counts,
 //    for each of its keys, how many selected keys are larger; that count is the
 //    output slot (keys are distinct, so the slots are a permutation);
-//  * attention workgroups each take a slice of the selected positions, in the
-//    order the selection produced them (that order differs between the two paths,
-//    which changes only the rounding of the attention), and write one split of
-//    the attention.
+//  * attention workgroup s takes the selected positions whose output slot lies in
+//    [s·per, (s+1)·per) (per = ceil(k / splits)), in output order, and writes one
+//    split of the attention. The slots are found by radix narrowing to the two
+//    window ends, so this needs no ordering of the whole selection, and the
+//    grouping depends on nothing but the output order: both paths, and the
+//    stand-alone attention over the ordered indices, sum the same rows in the
+//    same groups and order, and their outputs are equal bit for bit.
 #include "attn_body.h"
 #include "chunk_select.h"
 #include "kernels.h"
@@ -42,6 +40,9 @@ constexpr int kSelBlock = kAttnBlock;  // selection, ranking and attention share
 typedef unsigned int u32x3 __attribute__((ext_vector_type(3)));  // a chunk summary without its padding
 constexpr int kSelWaves = kSelBlock / 64;
 constexpr int kUPerThread = kCandCap / kSelBlock;  // candidate keys held per thread
+constexpr int kSelPerThread = 4096 / kSelBlock;   // selected keys per thread (k <= 4096)
+// Ranking workgroups that take part on the exhaustive path (each streams the row).
+constexpr int kFallbackRankers = 16;
 
 __global__ __launch_bounds__(kSelBlock) void k_chunk_cand(CandArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
@@ -71,119 +72,32 @@ hipError_t launch_chunk_candidates(const CandArgs& a, int B, hipStream_t s) {
 
 int chunk_cand_max_chunk() { return kChunkPerThread * kSelBlock; }
 
-// ------------------------------------------------------------------ exhaustive ordered sort
-
-struct SortSmem {
-  uint32_t hist[256];
-  uint32_t base[256];
-  uint32_t wc[kSelWaves][256];
-  int skip;
-};
-
-// Stable sort of the row's (score, position) pairs by score descending, four
-// byte-wide counting passes from the least significant byte. The input is built
-// in position order, so equal scores keep ascending positions. Returns the
-// buffer that holds the result (bufA or bufB). One workgroup.
-__device__ __forceinline__ const uint64_t* block_sort_row(const int32_t* __restrict__ scores, int n,
-                                          uint64_t* bufA, uint64_t* bufB, SortSmem& ss) {
-  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
-  for (int i = tid; i < n; i += kSelBlock)
-    bufA[i] = ((uint64_t)score_bits(scores[i]) << 32) | (uint32_t)i;
-  for (int i = tid; i < kSelWaves * 256; i += kSelBlock) (&ss.wc[0][0])[i] = 0;
-  __threadfence_block();
-  __syncthreads();
-  uint64_t* src = bufA;
-  uint64_t* dst = bufB;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int sh = 32 + 8 * pass;
-    auto digit = [sh](uint64_t e) { return 255u - (uint32_t)((e >> sh) & 0xFF); };
-    if (tid < 256) ss.hist[tid] = 0;
-    __syncthreads();
-    for (int i = tid; i < n; i += kSelBlock) atomicAdd(&ss.hist[digit(src[i])], 1u);
-    __syncthreads();
-    if (tid < 64) {
-      const uint32_t h0 = ss.hist[4 * tid], h1 = ss.hist[4 * tid + 1], h2 = ss.hist[4 * tid + 2],
-                     h3 = ss.hist[4 * tid + 3];
-      const uint32_t own = h0 + h1 + h2 + h3;
-      uint32_t s = own;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t t = __shfl_up(s, o);
-        if (tid >= o) s += t;
-      }
-      const uint32_t ex = s - own;
-      ss.base[4 * tid] = ex;
-      ss.base[4 * tid + 1] = ex + h0;
-      ss.base[4 * tid + 2] = ex + h0 + h1;
-      ss.base[4 * tid + 3] = ex + h0 + h1 + h2;
-      const bool one = h0 == (uint32_t)n || h1 == (uint32_t)n || h2 == (uint32_t)n || h3 == (uint32_t)n;
-      const uint64_t any = __ballot(one);
-      if (tid == 0) ss.skip = any != 0;
-    }
-    __syncthreads();
-    if (ss.skip) {
-      __syncthreads();
-      continue;  // every element has the same digit: the order is unchanged
-    }
-    for (int t0 = 0; t0 < n; t0 += kSelBlock) {
-      const int i = t0 + tid;
-      const bool valid = i < n;
-      const uint64_t e = valid ? src[i] : 0;
-      const uint32_t d = valid ? digit(e) : 0;
-      uint64_t peers = __ballot(valid);
-#pragma unroll
-      for (int bit = 0; bit < 8; ++bit) {
-        const bool set = (d >> bit) & 1;
-        const uint64_t bb = __ballot(valid && set);
-        peers &= set ? bb : ~bb;
-      }
-      if (!valid) peers = 0;
-      const int rank = __popcll(peers & lanemask_lt());
-      const bool last = valid && (peers & ~((2ull << lane) - 1ull)) == 0;
-      if (last) ss.wc[wave][d] = rank + 1;
-      __syncthreads();
-      if (valid) {
-        uint32_t off = ss.base[d] + rank;
-        for (int w = 0; w < wave; ++w) off += ss.wc[w][d];
-        dst[off] = e;
-      }
-      __syncthreads();
-      if (tid < 256) {
-        uint32_t t = 0;
-#pragma unroll
-        for (int w = 0; w < kSelWaves; ++w) {
-          t += ss.wc[w][tid];
-          ss.wc[w][tid] = 0;
-        }
-        ss.base[tid] += t;
-      }
-      __syncthreads();
-    }
-    __threadfence_block();
-    __syncthreads();
-    uint64_t* tmp = src;
-    src = dst;
-    dst = tmp;
-  }
-  return src;
-}
-
 // ------------------------------------------------------------------ selection (+ attention)
+
+// Once the radix bin that holds a sought key has at most this many keys, they are
+// ranked among themselves instead of narrowed further.
+constexpr uint32_t kMaxBinRank = 256;
+constexpr int kBinPad = 16;       // LDS slots before the bin's keys (split_sorted's base may point there)
+constexpr int kMaxWindow = 128;   // selected positions per attention split (at most ceil(4096 / 32))
+// keys gathered around an attention window: the bins of its two ends and the keys between
+constexpr int kMaxWindowList = 2 * (int)kMaxBinRank + kMaxWindow;
 
 struct SelSmem {
   RadixSmem radix;
   uint32_t xch[kSelWaves][5];
-  uint64_t mxw[kSelWaves];  // per wave: the best key a chunk left out
+  uint64_t mxw[kSelWaves];          // per wave: the best key a chunk left out
+  uint32_t wcnt[kSelWaves][2];      // exhaustive compaction: per-wave counts above / at the threshold
+  uint32_t gtw[kSelWaves];          // attention: per-wave counts of keys above the best dropped key
   uint64_t kstar;
   uint32_t tied;
+  uint32_t winpos[kMaxWindow];      // attention: the window's positions, in output order
 };
 static_assert(kUPerThread == 16 && kSelBlock == 512, "cand_slot layout: 512 threads x 16 entries");
-
-// Once the radix bin that holds the k-th best candidate has at most this many
-// keys, they are ranked among themselves instead of narrowed further.
-constexpr uint32_t kMaxBinRank = 256;
-constexpr int kBinPad = 16;  // LDS slots before the bin's keys (split_sorted's base may point there)
 static_assert(kBinPad >= kUPerThread, "split_sorted: up <= keys per thread");
+
+// LDS the selection needs in the region that the attention working set reuses
+// afterwards: a list of bin or window keys (kBinPad before it) and the sink slots.
+constexpr size_t kRegionSelect = (size_t)(kBinPad + kMaxWindowList + kSelBlock + kUPerThread) * 8;
 
 // Exchanges (sum, min, max, max64) over the block in one round.
 struct Stats4 {
@@ -211,83 +125,102 @@ __device__ __forceinline__ Stats4 block_stats(uint32_t sum, uint32_t lo, uint32_
   return r;
 }
 
-// Writes the selected keys held E per thread (contiguous, position order) to sel:
-// those scoring above T, then the first need_eq scoring exactly T in position
-// order. Returns (in sm.kstar, valid after the call) the last key taken at T.
-template <int E, class ValidAt>
-__device__ __forceinline__ void write_selected(const uint64_t (&key)[E], ValidAt valid_at, uint32_t T,
-                                               uint32_t need_eq, uint32_t run_sel, uint32_t run_eq,
-                                               uint64_t* sel, SelSmem& sm, uint32_t* tot_sel,
-                                               uint32_t* tot_eq) {
-  uint32_t gt = 0, eq = 0;
+// Calls f(score_bits) for every score of row[0, n), 16 loads per thread in flight
+// (coalesced: load j of the block covers 512 consecutive scores).
+template <class F>
+__device__ __forceinline__ void for_each_score(const int32_t* __restrict__ row, int n, F f) {
+  constexpr int U = 16;
+  const int64_t tid = threadIdx.x;
+  for (int64_t i0 = 0; i0 < n; i0 += (int64_t)kSelBlock * U) {
+    int32_t v[U];
 #pragma unroll
-  for (int j = 0; j < E; ++j)
-    if (valid_at(j)) {
-      const uint32_t u = key_ubits(key[j]);
-      gt += u > T;
-      eq += u == T;
+    for (int j = 0; j < U; ++j) {
+      const int64_t i = i0 + tid + (int64_t)kSelBlock * j;
+      v[j] = row[i < n ? i : n - 1];
     }
-  uint32_t total;
-  const uint32_t before = block_excl_scan_u32<kSelBlock>(gt | (eq << 16), sm.radix.part, &total);
-  const uint32_t eq_before = run_eq + (before >> 16);
-  uint32_t slot = run_sel + (before & 0xFFFF) + (eq_before < need_eq ? eq_before - run_eq
-                                                                      : (need_eq > run_eq ? need_eq - run_eq : 0));
-  uint32_t eqr = eq_before;
 #pragma unroll
-  for (int j = 0; j < E; ++j) {
-    if (!valid_at(j)) continue;
-    const uint32_t u = key_ubits(key[j]);
-    if (u > T) {
-      sel[slot++] = key[j];
-    } else if (u == T) {
-      if (eqr < need_eq) {
-        sel[slot++] = key[j];
-        if (eqr == need_eq - 1) sm.kstar = key[j];
-      }
-      ++eqr;
+    for (int j = 0; j < U; ++j)
+      if (i0 + tid + (int64_t)kSelBlock * j < n) f(score_bits(v[j]));
+  }
+}
+
+// The same over positions [p0, p1) for one wave: f(score_bits, position, present)
+// is called for every lane of every 64-position row, in position order (one call
+// per row per lane, so that callers can use wave-wide ballots).
+template <class F>
+__device__ __forceinline__ void wave_rows(const int32_t* __restrict__ row, int64_t p0, int64_t p1, F f) {
+  constexpr int U = 16;
+  const int lane = lane_id();
+  for (int64_t q0 = p0; q0 < p1; q0 += 64 * U) {
+    int32_t v[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int64_t p = q0 + 64 * j + lane;
+      v[j] = row[p < p1 ? p : p1 - 1];
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int64_t p = q0 + 64 * j + lane;
+      f(score_bits(v[j]), p, p < p1);
     }
   }
-  const uint32_t teq = total >> 16;
-  const uint32_t taken = run_eq >= need_eq ? 0 : (run_eq + teq <= need_eq ? teq : need_eq - run_eq);
-  *tot_sel = (total & 0xFFFF) + taken;
-  *tot_eq = teq;
 }
 
 // Exhaustive selection: the kk best keys of the row's n positions, written to sel
-// in position order; returns the kk-th best key. Streams the scores from memory
-// (a pass for the range, one radix pass per 11 bits of it, then one ordered
-// compaction pass).
-__device__ __forceinline__ uint64_t select_row_exhaustive(const int32_t* __restrict__ row, int n, int kk,
-                                          uint64_t* sel, uint32_t* tied, SelSmem& sm) {
-  const int tid = threadIdx.x;
+// in position order; returns the kk-th best key and sets *tied to the number of
+// selected keys with its score. Streams the scores from memory: a pass for the
+// range, one radix pass per 11 bits of it, then a count and a write pass of an
+// ordered compaction in which wave w owns one contiguous eighth of the row.
+// (Out of line: the exhaustive path is rare, and inlined into the selection kernel
+// it made the candidate path's code larger and slower.)
+__device__ __noinline__ uint64_t select_row_exhaustive(const int32_t* __restrict__ row, int n, int kk,
+                                                       uint64_t* sel, uint32_t* tied, SelSmem& sm) {
   uint32_t lo = 0xFFFFFFFFu, hi = 0;
-  for (int i = tid; i < n; i += kSelBlock) {
-    const uint32_t u = score_bits(row[i]);
+  for_each_score(row, n, [&](uint32_t u) {
     lo = u < lo ? u : lo;
     hi = u > hi ? u : hi;
-  }
+  });
   const Stats4 st = block_stats(0, lo, hi, 0, sm);
-  auto each = [&](auto f) {
-    for (int i = tid; i < n; i += kSelBlock) f(score_bits(row[i]));
-  };
+  auto each = [&](auto f) { for_each_score(row, n, f); };
   uint32_t above;
   const uint32_t T = block_select_range<kSelBlock>(each, st.lo, st.hi, kk, &above, sm.radix);
   const uint32_t need_eq = (uint32_t)kk - above;
   *tied = need_eq;
-  uint32_t run_sel = 0, run_eq = 0;
-  constexpr int E = 16;
-  for (int base = 0; base < n; base += kSelBlock * E) {
-    const int i0 = base + tid * E;
-    uint64_t key[E];
-#pragma unroll
-    for (int j = 0; j < E; ++j)
-      key[j] = i0 + j < n ? make_key(row[i0 + j], (uint32_t)(i0 + j)) : 0ull;
-    uint32_t ts, te;
-    write_selected<E>(key, [&](int j) { return i0 + j < n; }, T, need_eq, run_sel, run_eq, sel, sm,
-                      &ts, &te);
-    run_sel += ts;
-    run_eq += te;
+  const int w = wave_id(), lane = lane_id();
+  const int64_t rows = ((int64_t)n + 63) / 64, rpw = (rows + kSelWaves - 1) / kSelWaves;
+  const int64_t p0 = (int64_t)w * rpw * 64 < n ? (int64_t)w * rpw * 64 : n;
+  const int64_t p1 = p0 + rpw * 64 < n ? p0 + rpw * 64 : n;
+  uint32_t gt = 0, eq = 0;
+  wave_rows(row, p0, p1, [&](uint32_t u, int64_t, bool in) {
+    gt += in && u > T ? 1u : 0u;
+    eq += in && u == T ? 1u : 0u;
+  });
+  gt = wave_sum_u32(gt);
+  eq = wave_sum_u32(eq);
+  if (lane == 0) {
+    sm.wcnt[w][0] = gt;
+    sm.wcnt[w][1] = eq;
   }
+  lds_barrier();
+  uint32_t gb = 0, eb = 0;  // above / at T before this lane's position
+  for (int x = 0; x < w; ++x) {
+    gb += sm.wcnt[x][0];
+    eb += sm.wcnt[x][1];
+  }
+  const uint64_t lt = lanemask_lt();
+  wave_rows(row, p0, p1, [&](uint32_t u, int64_t p, bool in) {
+    const bool g = in && u > T, e = in && u == T;
+    const uint64_t bg = __ballot(g), be = __ballot(e);
+    const uint32_t gbl = gb + (uint32_t)__popcll(bg & lt), ebl = eb + (uint32_t)__popcll(be & lt);
+    if (g || (e && ebl < need_eq)) {
+      const uint32_t slot = gbl + (ebl < need_eq ? ebl : need_eq);
+      const uint64_t key = ((uint64_t)u << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)p);
+      sel[slot] = key;
+      if (e && ebl == need_eq - 1) sm.kstar = key;  // the last key taken at T is the kk-th best
+    }
+    gb += (uint32_t)__popcll(bg);
+    eb += (uint32_t)__popcll(be);
+  });
   lds_barrier();
   return sm.kstar;
 }
@@ -401,8 +334,9 @@ __device__ __forceinline__ void union_range_from_sums(const u32x3 (&csum)[4], ui
 }
 
 // The same from the keys themselves (when no summaries exist), by one block
-// exchange, which also publishes the cleared radix histograms. A thread's keys run
-// best first when each is at least the next (absent keys, 0, come last).
+// exchange, which also publishes the cleared radix histograms and anything the
+// caller wrote to LDS before it. A thread's keys run best first when each is at
+// least the next (absent keys, 0, come last).
 template <int E>
 __device__ __forceinline__ void union_range_exchange(const uint64_t (&key)[E], const uint32_t (&sv)[E],
                                                      uint32_t vmask, SelSmem& sm, uint32_t* rng, bool* sorted) {
@@ -431,28 +365,196 @@ __device__ __forceinline__ void union_range_exchange(const uint64_t (&key)[E], c
   *sorted = unsorted == 0;
 }
 
-// LDS: SelSmem | selected keys [k] | region: the attention working set, or the
-// sort state of the exhaustive path (the two roles never need both); on the
-// candidate path it first holds the keys of the k-th key's radix bin.
+// A range of 64-bit keys that holds a sought key: `above` keys lie above khi and
+// `inbin` keys in [klo, khi].
+struct KeyRange {
+  uint64_t klo, khi;
+  uint32_t above, inbin;
+};
+
+// Completes the narrowing of one sought key (the need-th largest of the keys held
+// E per thread; rb from block_narrow_first) until its range holds at most
+// kMaxBinRank keys: further passes over the scores, then, when one score value T
+// holds more, over the low key words (positions) of the keys at T. Uniform: every
+// thread gets the same range.
+template <int E>
+__device__ __forceinline__ KeyRange refine_key_range(RadixBin rb, uint32_t need, const uint64_t (&key)[E],
+                                                     const uint32_t (&sv)[E], uint32_t vmask, RadixSmem& sm) {
+  if (rb.inbin > kMaxBinRank && rb.binlo < rb.binhi) {
+    const uint32_t blo = rb.binlo, bhi = rb.binhi;
+    auto each_in = [&](auto f) {
+#pragma unroll
+      for (int j = 0; j < E; ++j)
+        if (((vmask >> j) & 1u) && sv[j] >= blo && sv[j] <= bhi) f(sv[j]);
+    };
+    const RadixBin r2 = block_narrow<kSelBlock>(each_in, blo, bhi, need - rb.above, rb.inbin, kMaxBinRank, sm);
+    rb = RadixBin{r2.binlo, r2.binhi, rb.above + r2.above, r2.inbin};
+  }
+  if (rb.inbin > kMaxBinRank) {  // one score value T holds that many keys
+    const uint32_t T = rb.binlo;
+    auto each_tie = [&](auto f) {
+#pragma unroll
+      for (int j = 0; j < E; ++j)
+        if (((vmask >> j) & 1u) && sv[j] == T) f((uint32_t)key[j]);
+    };
+    const RadixBin rt = block_narrow<kSelBlock>(each_tie, 0u, 0xFFFFFFFFu, need - rb.above, rb.inbin, kMaxBinRank, sm);
+    return KeyRange{((uint64_t)T << 32) | rt.binlo, ((uint64_t)T << 32) | rt.binhi, rb.above + rt.above, rt.inbin};
+  }
+  return KeyRange{(uint64_t)rb.binlo << 32, ((uint64_t)rb.binhi << 32) | 0xFFFFFFFFull, rb.above, rb.inbin};
+}
+
+// Attention window: of the n valid keys held E per thread (score bits sv, all in
+// [lo, hi]; `sorted` when every thread's keys run best first), the positions of
+// those whose rank (0 = best) lies in [r0, r1] go to sm.winpos[rank - r0], that is
+// in output order. The two window ends are narrowed together (one shared first
+// radix pass), the keys from the lower end's range to the upper end's range are
+// collected in wl (at most kMaxWindowList) and ranked among themselves.
+// With count_mx, the call also returns the number of valid keys above the best of
+// the G dropped keys xc[0, G) (for the candidate path's coverage check). Those are
+// requested here and exchanged and counted behind the narrowing, on its barriers:
+// a load still in flight where the caller's paths join is waited for there.
+template <int E>
+__device__ __forceinline__ uint32_t window_positions(const uint64_t (&key)[E], const uint32_t (&sv)[E],
+                                                     uint32_t vmask, uint32_t n, uint32_t lo, uint32_t hi,
+                                                     bool sorted, bool count_mx, const uint64_t* __restrict__ xc,
+                                                     int G, uint32_t r0, uint32_t r1, uint64_t* wl, uint64_t* sink,
+                                                     SelSmem& sm) {
+  // one dropped key per thread (clamped address; threads past G count 0)
+  const uint64_t mx = count_mx ? xc[threadIdx.x < (unsigned)G ? threadIdx.x : G - 1] : 0ull;
+  const uint32_t need[2] = {r0 + 1, r1 + 1};
+  auto each = [&](auto f) {
+#pragma unroll
+    for (int j = 0; j < E; ++j)
+      if ((vmask >> j) & 1u) f(sv[j]);
+  };
+  RadixBin rb[2];
+  block_narrow_first<kSelBlock, 2>(each, lo, hi, need, n, sm.radix, rb);
+  const KeyRange top = refine_key_range<E>(rb[0], need[0], key, sv, vmask, sm.radix);
+  const KeyRange bot = refine_key_range<E>(rb[1], need[1], key, sv, vmask, sm.radix);
+  // every key of the window lies in [bot.klo, top.khi]; the keys above top.khi
+  // number top.above
+  const uint64_t klo = bot.klo > 0 ? bot.klo : 1, khi = top.khi;  // a present key is never 0
+  uint32_t a = 0, b = 0;  // sorted: the thread's keys in range are its keys [a, b)
+#pragma unroll
+  for (int j = 0; j < E; ++j) {
+    const bool v = (vmask >> j) & 1u;
+    a += v && key[j] > khi ? 1u : 0u;
+    b += v && key[j] >= klo ? 1u : 0u;
+  }
+  if (count_mx) {  // uniform
+    const uint64_t wmx = wave_maxr_u64(threadIdx.x < (unsigned)G ? mx : 0ull);
+    if (lane_id() == 0) sm.mxw[wave_id()] = wmx;
+  }
+  uint32_t total;
+  // the last barrier of the narrowing separates every earlier reader of the scan
+  // slots; this scan's barrier publishes the waves' dropped keys
+  const uint32_t base = block_excl_scan_fresh_u32<kSelBlock>(b - a, sm.radix.part, &total);
+  uint64_t* const mine = sink + threadIdx.x;
+  // b - a keys of each thread are in range (keys at or above klo, less those above
+  // khi): its keys [a, b) when sorted, otherwise found key by key
+  if (sorted) {  // uniform
+#pragma unroll
+    for (int j = 0; j < E; ++j)
+      *(((uint32_t)j >= a && (uint32_t)j < b) ? wl + (base + (uint32_t)j - a) : mine) = key[j];
+  } else {
+    uint32_t sl = base;
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const bool t = ((vmask >> j) & 1u) && key[j] >= klo && key[j] <= khi;
+      *(t ? wl + sl : mine) = key[j];
+      sl += t ? 1u : 0u;
+    }
+  }
+  if (count_mx) {  // uniform: keys above the largest dropped key, per wave
+    uint64_t m = 0;
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w) m = sm.mxw[w] > m ? sm.mxw[w] : m;
+    uint32_t g = 0;
+#pragma unroll
+    for (int j = 0; j < E; ++j) g += ((vmask >> j) & 1u) && key[j] > m ? 1u : 0u;
+    g = wave_sum_u32(g);
+    if (lane_id() == 0) sm.gtw[wave_id()] = g;
+  }
+  lds_barrier();
+  const uint32_t nw = total;
+  // rank of a collected key = top.above + number of collected keys above it; eight
+  // threads per key, four reads in flight each
+  const int grp = threadIdx.x >> 3, part = threadIdx.x & 7;
+  for (uint32_t b0 = 0; b0 < nw; b0 += kSelBlock / 8) {
+    const uint32_t i = b0 + (uint32_t)grp;
+    const uint64_t me = i < nw ? wl[i] : ~0ull;
+    uint32_t r = 0;
+    for (uint32_t j0 = (uint32_t)part; j0 < nw; j0 += 32) {
+      uint64_t v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t jj = j0 + 8 * u;
+        v[u] = wl[jj < nw ? jj : nw - 1];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) r += (j0 + 8 * u < nw && v[u] > me) ? 1u : 0u;
+    }
+    r += (uint32_t)__builtin_amdgcn_mov_dpp((int)r, dpp::kQuadXor1, 0xF, 0xF, false);
+    r += (uint32_t)__builtin_amdgcn_mov_dpp((int)r, dpp::kQuadXor2, 0xF, 0xF, false);
+    r += (uint32_t)__builtin_amdgcn_mov_dpp((int)r, dpp::kRowHalfMirror, 0xF, 0xF, false);
+    const uint32_t gr = top.above + r;
+    if (part == 0 && i < nw && gr >= r0 && gr <= r1) sm.winpos[gr - r0] = key_pos(me);
+  }
+  lds_barrier();
+  uint32_t gt = 0;
+  if (count_mx)
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w) gt += sm.gtw[w];
+  return gt;
+}
+
+// The attention window on the exhaustive path: the kk best keys of the row by the
+// exhaustive selection (into sel), then the window narrowing over them, 16 per thread.
+// Out of line, so that loads in flight on the candidate path are not waited for
+// where its code would otherwise join this path's.
+__device__ __noinline__ void exhaustive_window(const int32_t* __restrict__ row, int n, int kk, uint64_t* sel,
+                                               const uint64_t* xc, int G, uint32_t r0, uint32_t r1, uint64_t* wl,
+                                               uint64_t* sink, SelSmem& sm) {
+  uint32_t tied;
+  select_row_exhaustive(row, n, kk, sel, &tied, sm);
+  uint64_t key[kUPerThread];
+  uint32_t sv[kUPerThread], vmask = 0;
+#pragma unroll
+  for (int j = 0; j < kUPerThread; ++j) {
+    const int i = kUPerThread * (int)threadIdx.x + j;
+    key[j] = i < kk ? sel[i] : 0ull;
+    sv[j] = key_ubits(key[j]);
+    vmask |= i < kk ? 1u << j : 0u;
+  }
+  uint32_t rng[2];
+  bool sorted;
+  union_range_exchange<kUPerThread>(key, sv, vmask, sm, rng, &sorted);
+  window_positions<kUPerThread>(key, sv, vmask, (uint32_t)kk, rng[0], rng[1], false, false, xc, G, r0, r1, wl, sink,
+                                sm);
+}
+
+// LDS: SelSmem | selected keys [k] | region: the attention working set, which
+// reuses what the selection keeps there (a list of bin or window keys, then sink
+// slots).
 // The arguments that the first requests need come first, as separate scalars: the
 // leading arguments can be preloaded into scalar registers at wave launch, so the
-// candidate, summary and query requests need not wait for a read of the argument
-// block (a.cand, a.sums, a.G, at.q, at.Hq, at.Dk and at.S, passed again).
+// candidate, dropped-key, summary and query requests need not wait for a read of the
+// argument block (a.cand, a.xc, a.sums, a.G, at.q, at.Hq, at.Dk and at.S, passed
+// again).
 template <class Attn>
 __global__ __launch_bounds__(kSelBlock) void k_select(const uint64_t* __restrict__ cand,
+                                                      const uint64_t* __restrict__ xc,
                                                       const ChunkSum* __restrict__ sums, const void* __restrict__ q,
                                                       int G, int Hq, int Dk, int S, SelArgs a, AttnArgs at) {
   extern __shared__ __align__(16) uint8_t smem[];
   SelSmem& sm = *reinterpret_cast<SelSmem*>(smem);
   uint64_t* sel = reinterpret_cast<uint64_t*>(smem + align16(sizeof(SelSmem)));
   uint8_t* region = smem + align16(sizeof(SelSmem)) + align16((size_t)a.k * 8);
+  uint64_t* list = reinterpret_cast<uint64_t*>(region) + kBinPad;  // bin or window keys
+  uint64_t* sink = list + kMaxWindowList;
   const int tid = threadIdx.x;
   const int b = blockIdx.y;
   const bool attn_role = (int)blockIdx.x < S;
-  const int n = a.lens.n[b];
-  const int32_t* row = a.scores + (int64_t)b * a.N;
-  DSA_TRACE_BEGIN();
-  DSA_MARK(1, 0);
   // Requests first, all from preloaded arguments. The candidate union U: thread t
   // holds entries [16t, 16t + 16), eight 16-byte pieces, piece j of all threads
   // contiguous (cand_slot); its workspace region always exists, and the entries are
@@ -488,7 +590,7 @@ __global__ __launch_bounds__(kSelBlock) void k_select(const uint64_t* __restrict
   // the requests above go out before anything else (left to itself the scheduler
   // put the attention's address arithmetic first)
   __builtin_amdgcn_sched_barrier(0);
-  AttnArgs atq = at;  // the query's address and shape from the preloaded arguments
+  AttnArgs atq = at;  // the row shape from the preloaded arguments
   atq.q = q;
   atq.Hq = Hq;
   atq.Dk = Dk;
@@ -497,29 +599,73 @@ __global__ __launch_bounds__(kSelBlock) void k_select(const uint64_t* __restrict
   // for together, so every later argument read hits the scalar cache (read where
   // first used, behind the branches before them, they took several memory round
   // trips in a row).
+  // The fields that decide the path pass through the asm as opaque values, and its
+  // memory clobber keeps it behind the requests above: left to itself the compiler
+  // computed the path, and waited for these reads, ahead of the first request.
+  int n = a.lens.n[b], have_cand = a.have_cand, cand_valid = a.cand_valid.n[b], force = a.force, kq = a.k;
   {
     const int32_t* l0 = a.idx;
-    const int l1 = a.lens.n[b], l2 = a.have_cand, l3 = a.cand_valid.n[b], l4 = a.force, l5 = at.S;
-    asm volatile("" ::"s"(l0), "s"(l1), "s"(l2), "s"(l3), "s"(l4), "s"(l5));
+    asm volatile("" : "+s"(n), "+s"(have_cand), "+s"(cand_valid), "+s"(force), "+s"(kq) : "s"(l0) : "memory");
   }
+  const int32_t* row = a.scores + (int64_t)b * a.N;
 
-  int reason = a.force ? 1 : (a.have_cand ? 0 : 3);
-  uint32_t nvalid = 0, nsel = 0, tied = 0;
-  uint64_t kstar = 0;
-  uint64_t mx = 0;
+  int reason = force ? 1 : (have_cand ? 0 : 3);
+  const int kk = kq < n ? kq : n;  // positions selected on either path
+  const uint32_t nvalid = reason == 0 ? (uint32_t)cand_valid : 0u;
+  // A union with fewer valid keys than kk dropped some position (it holds every
+  // position of a chunk that keeps them all), so it cannot cover the top kk.
+  if (reason == 0 && nvalid < (uint32_t)kk) reason = 2;
   if (reason == 0) {
-    // entries past the union's end are absent (key 0); the best dropped key is only
-    // needed for the coverage check, so its load is not waited for before that
+    // entries past the union's end are absent (key 0)
     const int C = G * a.m;
 #pragma unroll
     for (int j = 0; j < kUPerThread; ++j) key[j] = kUPerThread * tid + j < C ? key[j] : 0ull;
-    mx = tid < G ? a.xc[(int64_t)b * G + tid] : 0ull;
   }
-  const bool have_sums = sums_on && reason == 0;  // uniform
   radix_clear<kSelBlock>(sm.radix);
+
+  if (attn_role) {
+    // ------------------------------------------------ attention workgroup s
+    const int per = (a.k + S - 1) / S;
+    const int r0 = (int)blockIdx.x * per;
+    const int cnt = kk - r0 < 0 ? 0 : (kk - r0 > per ? per : kk - r0);
+    // the window narrowing over the union on the candidate path; when the coverage
+    // check fails, or the path is exhaustive, over the exhaustively selected keys
+    if (cnt > 0 && reason == 0) {  // uniform
+      uint32_t sv[kUPerThread], vmask = 0;
+#pragma unroll
+      for (int j = 0; j < kUPerThread; ++j) {
+        sv[j] = key_ubits(key[j]);
+        vmask |= (uint32_t)key[j] != 0u ? 1u << j : 0u;
+      }
+      uint32_t rng[2];
+      bool sorted;
+      if (sums_on) {  // uniform
+        union_range_from_sums(csum, rng, &sorted);
+        lds_barrier();  // publishes the cleared radix histograms
+      } else {
+        union_range_exchange<kUPerThread>(key, sv, vmask, sm, rng, &sorted);
+      }
+      const uint32_t above_mx =
+          window_positions<kUPerThread>(key, sv, vmask, nvalid, rng[0], rng[1], sorted, true, xc + (int64_t)b * G,
+                                        G, (uint32_t)r0, (uint32_t)(r0 + cnt - 1), list, sink, sm);
+      // the union's top kk are the row's when at least kk of its keys lie above every
+      // dropped key (nvalid >= kk here, and a union with fewer than k valid keys then
+      // holds every position and dropped none)
+      if (above_mx < (uint32_t)kk) reason = 2;
+    }
+    if (cnt > 0 && reason != 0)  // uniform
+      exhaustive_window(row, n, kk, sel, xc + (int64_t)b * G, G, (uint32_t)r0, (uint32_t)(r0 + cnt - 1), list, sink,
+                        sm);
+    // sm.winpos is complete and published (the last barrier of the window
+    // narrowing follows its last write), and the LDS region is free again
+    Attn::run(at, b, blockIdx.x, [&](int i) { return (int64_t)sm.winpos[i]; }, cnt, region, qf);
+    return;
+  }
+
+  // -------------------------------------------------- ranking workgroup r
+  uint32_t nsel = 0, tied = 0;
+  uint64_t kstar = 0;
   if (reason == 0) {
-    // 32-bit views of the candidate keys: score bits and presence (a present key's
-    // low word, 0xFFFFFFFF - position, is never 0)
     uint32_t sv[kUPerThread], vmask = 0;
 #pragma unroll
     for (int j = 0; j < kUPerThread; ++j) {
@@ -528,24 +674,21 @@ __global__ __launch_bounds__(kSelBlock) void k_select(const uint64_t* __restrict
     }
     uint32_t rng[2];
     bool sorted;
-    if (have_sums) {
+    if (sums_on) {
       union_range_from_sums(csum, rng, &sorted);
       lds_barrier();  // publishes the cleared radix histograms
     } else {
       union_range_exchange<kUPerThread>(key, sv, vmask, sm, rng, &sorted);
     }
-    DSA_MARK(1, 11);
-    nvalid = (uint32_t)a.cand_valid.n[b];
-    DSA_MARK(1, 1);
-    const uint32_t kk = (uint32_t)a.k < nvalid ? (uint32_t)a.k : nvalid;
+    const uint32_t kku = (uint32_t)kk;  // <= nvalid here
+    const uint64_t mx = tid < G ? xc[(int64_t)b * G + tid] : 0ull;  // waited for behind the narrowing
     auto each = [&](auto f) {
 #pragma unroll
       for (int j = 0; j < kUPerThread; ++j)
         if ((vmask >> j) & 1u) f(sv[j]);
     };
     // radix passes until the bin of the kk-th best key is small
-    const RadixBin rb = block_narrow<kSelBlock>(each, rng[0], rng[1], kk, nvalid, kMaxBinRank, sm.radix);
-    DSA_MARK(1, 2);
+    const RadixBin rb = block_narrow<kSelBlock>(each, rng[0], rng[1], kku, nvalid, kMaxBinRank, sm.radix);
     const uint64_t wmx = wave_maxr_u64(mx);
     // the key range that holds the kk-th best key: the keys above it are taken
     uint64_t klo = (uint64_t)rb.binlo << 32, khi = ((uint64_t)rb.binhi << 32) | 0xFFFFFFFFull;
@@ -560,107 +703,50 @@ __global__ __launch_bounds__(kSelBlock) void k_select(const uint64_t* __restrict
           if (((vmask >> j) & 1u) && sv[j] == T) f((uint32_t)key[j]);
       };
       const RadixBin rt =
-          block_narrow<kSelBlock>(each_tie, 0u, 0xFFFFFFFFu, kk - rb.above, rb.inbin, kMaxBinRank, sm.radix);
+          block_narrow<kSelBlock>(each_tie, 0u, 0xFFFFFFFFu, kku - rb.above, rb.inbin, kMaxBinRank, sm.radix);
       klo = ((uint64_t)T << 32) | rt.binlo;
       khi = ((uint64_t)T << 32) | rt.binhi;
       above += rt.above;
       inbin = rt.inbin;
       tie_above = rt.above;
     }
-    DSA_MARK(3, 11);
     // the keys above the range are taken in union order, then the range's best in
     // key order (equal scores: ascending positions)
-    uint64_t* bin = reinterpret_cast<uint64_t*>(region) + kBinPad;
     if (sorted)  // uniform
-      split_sorted<kUPerThread>(key, klo, khi, sel, bin, bin + kMaxBinRank, sm);
+      split_sorted<kUPerThread>(key, klo, khi, sel, list, sink, sm);
     else
-      split_at_bin<kUPerThread>(key, vmask, klo, khi, sel, bin, bin + kMaxBinRank, sm);
-    DSA_MARK(3, 12);
+      split_at_bin<kUPerThread>(key, vmask, klo, khi, sel, list, sink, sm);
     if (lane_id() == 0) sm.mxw[wave_id()] = wmx;
     lds_barrier();
-    DSA_MARK(3, 13);
-    rank_bin(bin, inbin, kk - above, sel + above, sm);
-    DSA_MARK(3, 14);
+    rank_bin(list, inbin, kku - above, sel + above, sm);
     lds_barrier();
     const uint32_t tie = tie_above + sm.tied;
-    DSA_MARK(1, 3);
     kstar = sm.kstar;
-    mx = 0;
+    uint64_t mxall = 0;
 #pragma unroll
-    for (int w = 0; w < kSelWaves; ++w) mx = sm.mxw[w] > mx ? sm.mxw[w] : mx;
+    for (int w = 0; w < kSelWaves; ++w) mxall = sm.mxw[w] > mxall ? sm.mxw[w] : mxall;
     // every dropped key is below the k-th candidate: the candidates hold the top k
-    const bool ok = mx < kstar && (nvalid >= (uint32_t)a.k || mx == 0);
+    const bool ok = mxall < kstar && (nvalid >= (uint32_t)a.k || mxall == 0);
     if (ok) {
-      nsel = kk;
+      nsel = kku;
       tied = tie;
     } else {
       reason = 2;
     }
   }
-
+  // the exhaustive path streams the whole row in every workgroup that takes part,
+  // so fewer ranking workgroups take part there, each with a larger slice
+  const int R = reason == 0 ? a.R : (a.R < kFallbackRankers ? a.R : kFallbackRankers);
+  const int r = (int)blockIdx.x - S;
+  if (r >= R) return;  // uniform
   if (reason != 0) {
-    if (!attn_role) {
-      if ((int)blockIdx.x != S) {  // one ranking workgroup sorts the whole row
-        DSA_TRACE_FLUSH();
-        return;
-      }
-      uint64_t* ba = a.sortbuf + (int64_t)b * 2 * a.N;
-      const uint64_t* sorted =
-          block_sort_row(row, n, ba, ba + a.N, *reinterpret_cast<SortSmem*>(region));
-      const int kk = a.k < n ? a.k : n;
-      int32_t* out = a.idx + (int64_t)b * a.k;
-      const uint32_t ulast = (uint32_t)(sorted[kk - 1] >> 32);
-      uint32_t t = 0;
-      for (int j = tid; j < a.k; j += kSelBlock) {
-        if (j < kk) {
-          const uint64_t e = sorted[j];
-          out[j] = (int32_t)(uint32_t)e;
-          t += (uint32_t)(e >> 32) == ulast;
-        } else {
-          out[j] = -1;
-        }
-      }
-      t = block_stats(t, 0, 0, 0, sm).sum;
-      if (tid == 0) {
-        RowStats st;
-        st.path = 1;
-        st.reason = reason;
-        st.selected = kk;
-        st.kth_score = (int32_t)(ulast ^ 0x80000000u);
-        st.candidates = (int32_t)nvalid;
-        st.tied_at_kth = (int32_t)t;
-        st.bad_indices = 0;
-        st.reserved = 0;
-        a.stats[b] = st;
-      }
-      DSA_TRACE_FLUSH();
-      return;
-    }
-    // attention workgroups select the same set from every position
-    const int kk = a.k < n ? a.k : n;
     kstar = select_row_exhaustive(row, n, kk, sel, &tied, sm);
     nsel = (uint32_t)kk;
-  }
-  // sel is complete and published on both paths (the last barrier of either
-  // selection follows its last write), and the LDS region is free again
-  DSA_MARK(1, 4);
-
-  if (attn_role) {
-    const int per = ((int)nsel + S - 1) / S;
-    const int e0 = (int)blockIdx.x * per;
-    int cnt = (int)nsel - e0;
-    cnt = cnt < 0 ? 0 : (cnt > per ? per : cnt);
-    Attn::run(at, b, blockIdx.x, [&](int i) { return (int64_t)key_pos(sel[e0 + i]); }, cnt,
-              region, qf);
-    DSA_MARK(1, 10);
-    DSA_TRACE_FLUSH();
-    return;
   }
 
   // ranking: the slot of a key is the number of selected keys larger than it
   constexpr int TPE = 32;  // threads per ranked key
-  const int r = (int)blockIdx.x - S;
-  const int per = ((int)nsel + a.R - 1) / a.R;
+  const int per = ((int)nsel + R - 1) / R;
   const int e0 = r * per;
   const int e1 = e0 + per < (int)nsel ? e0 + per : (int)nsel;
   int32_t* out = a.idx + (int64_t)b * a.k;
@@ -688,13 +774,12 @@ __global__ __launch_bounds__(kSelBlock) void k_select(const uint64_t* __restrict
     cnt += (uint32_t)__shfl_xor((int)cnt, 16);
     if (e < e1 && part == 0) out[cnt] = (int32_t)key_pos(me);
   }
-  DSA_MARK(1, 5);
   if (r == 0) {
     for (int j = (int)nsel + tid; j < a.k; j += kSelBlock) out[j] = -1;
     if (tid == 0) {
       RowStats st;
-      st.path = 0;
-      st.reason = 0;
+      st.path = reason == 0 ? 0 : 1;
+      st.reason = reason;
       st.selected = (int32_t)nsel;
       st.kth_score = key_score(kstar);
       st.candidates = (int32_t)nvalid;
@@ -704,17 +789,12 @@ __global__ __launch_bounds__(kSelBlock) void k_select(const uint64_t* __restrict
       a.stats[b] = st;
     }
   }
-  DSA_TRACE_FLUSH();
 }
-
-static_assert(sizeof(SortSmem) >= (kBinPad + kMaxBinRank + kSelBlock + kUPerThread) * 8,
-              "bin keys and sink slots fit the LDS region");
 
 template <class Attn>
 static size_t select_lds_t(int Hq, int Dk, int k) {
   const size_t ra = Attn::lds_bytes(Hq, Dk);
-  return align16(sizeof(SelSmem)) + align16((size_t)k * 8) +
-         (ra > sizeof(SortSmem) ? ra : sizeof(SortSmem));
+  return align16(sizeof(SelSmem)) + align16((size_t)k * 8) + (ra > kRegionSelect ? ra : kRegionSelect);
 }
 
 template <class Attn>
@@ -724,8 +804,8 @@ static hipError_t launch_select_t(const SelArgs& a, const AttnArgs& at, int B, h
   hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
-  return launch_timed(fn, dim3(at.S + a.R, B), dim3(kSelBlock), lds, s, t, a.cand, a.sums, at.q, a.G, at.Hq, at.Dk,
-                      at.S, a, at);
+  return launch_timed(fn, dim3(at.S + a.R, B), dim3(kSelBlock), lds, s, t, a.cand, a.xc, a.sums, at.q, a.G, at.Hq,
+                      at.Dk, at.S, a, at);
 }
 
 // ------------------------------------------------------------------ attention over given indices
@@ -869,8 +949,6 @@ __global__ __launch_bounds__(kCombWideBlock) void k_combine_wide(const float2* _
   const int HP = (Hq + 15) / 16 * 16, tiles = Dv / 16;
   const int quad = blockIdx.x, tile = quad >> 2, l0 = 16 * (quad & 3);
   const int h0 = 16 * (tile / tiles) + 4 * (quad & 3);  // heads h0 .. h0 + 3
-  DSA_TRACE_BEGIN();
-  DSA_MARK(2, 0);
   // every load first: this thread's (max, sum) pairs, then its partial outputs
   const int h = t & 3, g = t >> 2;
   const int hh = h0 + h < Hq ? h0 + h : Hq - 1;
@@ -922,7 +1000,6 @@ __global__ __launch_bounds__(kCombWideBlock) void k_combine_wide(const float2* _
     if (sp < S) wt[h][sp] = ew[i] * inv;
   }
   lds_barrier();
-  DSA_MARK(2, 2);
   v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
@@ -949,7 +1026,6 @@ __global__ __launch_bounds__(kCombWideBlock) void k_combine_wide(const float2* _
     nb = wave_sum_u32(nb);
     if (t == 0) stats[b].bad_indices = (int32_t)nb;
   }
-  DSA_TRACE_FLUSH();
 }
 
 hipError_t launch_combine_wide(const AttnArgs& at, const int32_t* part_bad, RowStats* stats, float* out,
@@ -974,8 +1050,6 @@ __global__ __launch_bounds__(kCombBlock) void k_combine(AttnArgs at, const int32
   const int b = blockIdx.y, lane = threadIdx.x;
   const int S = at.S, Hq = at.Hq, Dv = at.Dv;
   const int HP = FRAG ? (Hq + 15) / 16 * 16 : Hq;
-  DSA_TRACE_BEGIN();
-  DSA_MARK(2, 0);
   // Every load is issued before any arithmetic: first the (max, sum) pairs this lane
   // turns into weights, then the partial outputs this lane combines (they do not
   // depend on the weights), so the whole pass waits for one memory round trip.
@@ -1017,7 +1091,6 @@ __global__ __launch_bounds__(kCombBlock) void k_combine(AttnArgs at, const int32
       *(v4f*)&wsh[lane][s] = v4f{e[s] * inv, e[s + 1] * inv, e[s + 2] * inv, e[s + 3] * inv};
   }
   lds_barrier();
-  DSA_MARK(2, 2);
   // the count of invalid indices (stand-alone attention) is read last, so its wait
   // does not hold up the combine
   const bool count_bad = part_bad != nullptr && blockIdx.x == 0;
@@ -1059,8 +1132,6 @@ __global__ __launch_bounds__(kCombBlock) void k_combine(AttnArgs at, const int32
     const uint32_t nb = wave_sum_u32(lane < S ? (uint32_t)part_bad[(int64_t)b * S + lane] : 0u);
     if (lane == 0) stats[b].bad_indices = (int32_t)nb;
   }
-  DSA_MARK(2, 1);
-  DSA_TRACE_FLUSH();
 }
 
 hipError_t launch_combine(const AttnArgs& at, const int32_t* part_bad, RowStats* stats, float* out,

@@ -49,7 +49,8 @@ def test_workspace_size(lib):
     assert ws(0, 100, 8) == 0 and ws(17, 100, 8) == 0 and ws(1, 0, 8) == 0
     assert ws(1, 100, 0) == 0 and ws(1, 100, 4097) == 0 and ws(1, 1 << 31, 8) == 0
     a, b = ws(1, 16384, 2048, 16, 512), ws(1, 300000, 2048, 16, 512)
-    assert 0 < a < b
+    # the workspace does not grow with the context (no full-row scratch)
+    assert 0 < a == b == ws(1, (1 << 31) - 1, 2048, 16, 512)
     assert ws(8, 131072, 2048, 16, 512) > ws(1, 131072, 2048, 16, 512)
     assert a % 256 == 0
 
@@ -67,8 +68,10 @@ def scores_call(lib, B=1, Hi=64, Di=128, N=1000, ctx=None, iq=FAKE, ik=FAKE, out
 def test_index_scores_validation(lib):
     assert scores_call(lib, B=0) == INVALID
     assert scores_call(lib, B=17, ctx=[10] * 17) == INVALID
-    assert scores_call(lib, Hi=0) == INVALID and scores_call(lib, Hi=65) == INVALID
-    assert scores_call(lib, Di=48) == INVALID and scores_call(lib, Di=288) == INVALID
+    assert scores_call(lib, Hi=0) == INVALID
+    assert scores_call(lib, Di=40) == INVALID and scores_call(lib, Di=8) == INVALID
+    # valid shapes that no built kernel covers
+    assert scores_call(lib, Hi=65) == UNSUPPORTED and scores_call(lib, Di=288) == UNSUPPORTED
     assert scores_call(lib, ctx=[0]) == INVALID and scores_call(lib, ctx=[1001]) == INVALID
     assert scores_call(lib, iq=None) == INVALID and scores_call(lib, out=None) == INVALID
     assert scores_call(lib, ik=FAKE + 8) == INVALID  # keys must be 16-byte aligned
@@ -100,14 +103,15 @@ def attn_call(lib, Hq=16, Dk=576, Dv=512, dt=1, scale=1 / 24, k=2048, N=20000, w
 
 
 def test_attention_validation(lib):
-    assert attn_call(lib, Hq=0) == INVALID and attn_call(lib, Hq=65) == INVALID
-    assert attn_call(lib, Dv=600) == INVALID and attn_call(lib, Dk=2048, Dv=512) == INVALID
-    assert attn_call(lib, dt=2) == INVALID
+    assert attn_call(lib, Hq=0) == INVALID and attn_call(lib, Dk=100, Dv=64) == INVALID
+    assert attn_call(lib, Dv=600) == INVALID and attn_call(lib, Dk=0, Dv=1) == INVALID
+    assert attn_call(lib, dt=7) == INVALID
     assert attn_call(lib, scale=float("inf")) == INVALID and attn_call(lib, scale=float("nan")) == INVALID
     assert attn_call(lib, q=FAKE + 4) == INVALID
     assert attn_call(lib, q=None) == INVALID
     # valid shapes that no built kernel covers
     assert attn_call(lib, Hq=64, Dk=1000, Dv=500) == UNSUPPORTED
+    assert attn_call(lib, Hq=65) == UNSUPPORTED and attn_call(lib, Dk=2048, Dv=512) == UNSUPPORTED
     assert attn_call(lib, ws_bytes=100) == WORKSPACE
 
 
@@ -125,6 +129,12 @@ def test_decode_step_validation(lib):
     bad = list(args)
     bad[20] = need - 1
     assert lib.dsa_decode_step(*bad) == WORKSPACE
+    # Di = 48 (a multiple of 16) passes the indexer checks: the short workspace is
+    # what the call reports (and nothing is launched on these stand-in pointers)
+    bad[8] = 48
+    assert lib.dsa_decode_step(*bad) == WORKSPACE
+    bad[7] = 65  # Hi beyond the built kernels
+    assert lib.dsa_decode_step(*bad) == UNSUPPORTED
     bad = list(args)
     bad[21] = 8  # unknown flag
     assert lib.dsa_decode_step(*bad) == INVALID

@@ -3,7 +3,11 @@
 Scores and indices must match bit for bit; attention must satisfy
 max|gpu - ref| <= 1e-2 and ||gpu - ref||_2 / ||ref||_2 <= 2e-3 (over every output of
 the case). Full workload sizes are compared element by element: the oracle
-finishes each of them in seconds."""
+finishes each of them in seconds. Beyond the oracle, the GPU paths must agree with
+each other bit for bit: the candidate path and the forced exhaustive path, the
+decode step and the stand-alone attention over its own indices, and repeated runs
+(the ds4 branch post's long-context paragraph: same positions, same order, same
+outputs)."""
 import sys
 import zlib
 
@@ -137,11 +141,15 @@ def test_ctx62k_eleven_layers(torch, dsa):
     check_attention(np.stack(outs), np.stack(refs), "ctx62k_11layers all layers")
 
 
-@pytest.mark.parametrize("name", ["ctx16k", "ctx300k_tiepool"])
+def bits_equal(a, b):
+    return np.array_equal(np.ascontiguousarray(a).view(np.uint8), np.ascontiguousarray(b).view(np.uint8))
+
+
+@pytest.mark.parametrize("name", ["ctx16k", "ctx300k", "ctx300k_tiepool", "verify8_ctx131k"])
 def test_forced_fallback_matches_fast_path(torch, dsa, name):
-    # The exhaustive path selects the same positions in the same order (bit-exact);
-    # its attention sums the same rows in another grouping, so it meets the
-    # tolerance rather than matching the fast path bit for bit.
+    # The exhaustive path selects the same positions in the same order, and attention
+    # split s takes the positions of output slots [s*per, (s+1)*per) on either path,
+    # so the outputs are equal bit for bit.
     note("forced fallback", name)
     c, (rs, ri, ro) = case(name)
     d = dev_inputs(torch, c)
@@ -152,18 +160,36 @@ def test_forced_fallback_matches_fast_path(torch, dsa, name):
     assert np.array_equal(i1, i2)
     check_attention(o2, ro, name + " exhaustive path")
     check_attention(o1, ro, name + " fast path")
+    assert bits_equal(o1, o2), name + ": fast path and exhaustive path outputs differ"
     assert all(st["path"] == 1 and st["reason"] == 1 for st in st2)
     assert all(st["path"] == 0 for st in st1)
+    for a, b in zip(st1, st2):
+        assert (a["selected"], a["kth_score"], a["tied_at_kth"]) == (b["selected"], b["kth_score"],
+                                                                     b["tied_at_kth"])
 
 
-def test_runs_are_bit_identical(torch, dsa):
-    c, _ = case("ctx16k")
+@pytest.mark.parametrize("name", ["ctx16k", "ctx300k", "verify8_ctx131k", "ctx16k_hotstride"])
+def test_decode_step_matches_attention_over_its_indices(torch, dsa, name):
+    # dsa_sparse_attn over the step's own ordered indices splits them the same way
+    # (slots [s*per, (s+1)*per) per split), so it returns the step's output bit for bit.
+    note("step vs stand-alone attention", name)
+    c, _ = case(name)
+    d = dev_inputs(torch, c)
+    _, i1, o1, _ = run_step(torch, dsa, c, d)
+    out = dsa.dsa_sparse_attn(d["q"], d["kv"], torch.from_numpy(i1).cuda(), c["Dv"], c["scale"])
+    torch.cuda.synchronize()
+    assert bits_equal(out.cpu().numpy(), o1)
+
+
+@pytest.mark.parametrize("name", ["ctx16k", "ctx300k", "verify8_ctx131k"])
+def test_runs_are_bit_identical(torch, dsa, name):
+    c, _ = case(name)
     d = dev_inputs(torch, c)
     first = run_step(torch, dsa, c, d)
-    for _ in range(3):
+    for rep in range(9):
         again = run_step(torch, dsa, c, d)
         for a, b in zip(first[:3], again[:3]):
-            assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+            assert bits_equal(a, b), "%s run %d differs" % (name, rep + 1)
 
 
 @pytest.mark.parametrize("name", ["ctx16k", "verify8_ctx131k"])
@@ -306,6 +332,11 @@ EDGE = [
     ("verify-rows", dict(B=8, N=40000, k=2048, Hi=64, Di=128, Hq=16, Dk=576, Dv=512,
                          ctx_len=[39993 + r for r in range(8)])),
     ("many-rows", dict(B=16, N=20000, k=2048, Hi=64, Di=128, Hq=16, Dk=576, Dv=512)),
+    # indexer dims that are a multiple of 16 but not of 32 (the last matrix-core step
+    # takes a zero query half)
+    ("di-48-one-row", dict(B=1, N=30000, k=1024, Hi=24, Di=48, Hq=4, Dk=64, Dv=64)),
+    ("di-80-rows", dict(B=3, N=12000, k=700, Hi=64, Di=80, Hq=16, Dk=576, Dv=512, ctx_len=[12000, 9000, 50])),
+    ("di-16", dict(B=1, N=5000, k=256, Hi=1, Di=16, Hq=1, Dk=32, Dv=32)),
 ]
 
 
@@ -316,8 +347,30 @@ def test_edge_cases(torch, dsa, label, kw):
     rs, ri, ro = oracle.decode_step(c["iq"], c["iw"], c["ik"], c["q"], c["kv"], c["ctx_len"], c["k"],
                                     c["Dv"], c["scale"])
     d = dev_inputs(torch, c)
+    outs = []
     for flags in (0, 1):
         s, i, o, stats = run_step(torch, dsa, c, d, flags)
         check_scores(s, rs, c["ctx_len"], label)
         assert np.array_equal(i, ri), "%s indices differ (flags %d)" % (label, flags)
         check_attention(o, ro, "%s flags %d" % (label, flags))
+        outs.append(o)
+    assert bits_equal(outs[0], outs[1]), label + ": fast path and exhaustive path outputs differ"
+
+
+def test_row_longer_than_candidate_pass(torch, dsa):
+    # A row of 2^21 + 1,000 positions is longer than the one-row candidate pass takes
+    # (256 chunks of at most 8,192 positions): it is scored without candidates and
+    # selected by the exhaustive path (reason 3). Small indexer and attention shapes
+    # keep the caches at about 200 MB.
+    N = (1 << 21) + 1000
+    c = inputs.random_case(2121, B=1, N=N, k=2048, Hi=4, Di=32, Hq=2, Dk=64, Dv=64, key_range=3)
+    note("long row: N=%d k=2048 Hi=4 Di=32 Hq=2 Dk=64" % N)
+    rs, ri, ro = oracle.decode_step(c["iq"], c["iw"], c["ik"], c["q"], c["kv"], c["ctx_len"], c["k"],
+                                    c["Dv"], c["scale"])
+    d = dev_inputs(torch, c)
+    s, i, o, stats = run_step(torch, dsa, c, d)
+    check_scores(s, rs, c["ctx_len"], "long row")
+    assert np.array_equal(i, ri), "long row indices differ"
+    check_attention(o, ro, "long row")
+    assert stats[0]["path"] == 1 and stats[0]["reason"] == 3
+    assert stats[0]["tied_at_kth"] == expected_ties(rs, ri, c["ctx_len"], c["k"])[0]
