@@ -182,6 +182,29 @@ dsa_status dsa_decode_step_timed(const int8_t* iq, const int8_t* iw, const int8_
                                  hipStream_t stream, hipEvent_t* kernel_events);
 
 /*
+ * dsa_decode_step for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the same
+ * step with no workspace argument. Its workspace is a static device array of
+ * DSA_NOALLOC_SCRATCH_BYTES per device, part of the library's code object and held
+ * until the process ends; its address is looked up once per device (the first call
+ * on it). Nothing is allocated or freed, here or later.
+ *  - Sizes whose dsa_workspace_size exceeds DSA_NOALLOC_SCRATCH_BYTES return
+ *    DSA_ERR_WORKSPACE (B=1, k=2048, Hq=16, Dv=512 needs about 2.2 MB; B=16 about
+ *    34 MB); other arguments are checked as for dsa_decode_step.
+ *  - Every call on a device shares that device's scratch, and the scratch keeps the
+ *    last call's contents: calls that overlap on one device (other streams, other
+ *    host threads) race and must be ordered by the caller. dsa_read_stats cannot
+ *    read these calls' statistics.
+ *  - DSA_ERR_HIP if the scratch address cannot be resolved on the current device.
+ */
+#define DSA_NOALLOC_SCRATCH_BYTES (64u << 20)
+dsa_status dsa_decode_step_noalloc(const int8_t* iq, const int8_t* iw, const int8_t* ik, const void* q,
+                                   const void* kv, const int32_t* ctx_len, int B, int Hi, int Di, int Hq,
+                                   int Dk, int Dv, int64_t N, int k, float scale, dsa_dtype dt,
+                                   int32_t* scores, int32_t* idx, float* out, unsigned flags,
+                                   hipStream_t stream);
+
+/*
  * Copies the per-row stats of the last call that used `ws` into stats[0..B).
  * Synchronises `stream` (call it outside timed regions).
  */

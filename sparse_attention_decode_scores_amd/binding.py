@@ -20,7 +20,8 @@ DSA_F32, DSA_BF16 = 0, 1
 STATUS_NAMES = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED",
                 3: "DSA_ERR_WORKSPACE", 4: "DSA_ERR_HIP"}
 EXPORTED = ("dsa_status_string", "dsa_workspace_size", "dsa_index_scores", "dsa_topk_select",
-            "dsa_sparse_attn", "dsa_decode_step", "dsa_decode_step_timed", "dsa_read_stats")
+            "dsa_sparse_attn", "dsa_decode_step", "dsa_decode_step_timed", "dsa_decode_step_noalloc",
+            "dsa_read_stats")
 
 
 class DSAError(RuntimeError):
@@ -64,6 +65,8 @@ def load_library():
         lib.dsa_decode_step.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i64, i32,
                                         f32, i32, p, p, p, p, sz, u32, p]
         lib.dsa_decode_step_timed.argtypes = lib.dsa_decode_step.argtypes + [p]
+        lib.dsa_decode_step_noalloc.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i64, i32,
+                                                f32, i32, p, p, p, u32, p]
         lib.dsa_read_stats.argtypes = [p, sz, i32, p, p]
         for name in EXPORTED[2:]:
             getattr(lib, name).restype = i32
@@ -228,6 +231,29 @@ def dsa_decode_step(iq, iw, ik, q, kv, ctx_len, k, Dv, scale, scores=None, idx=N
         evs = (ctypes.c_void_p * 6)(*[e.cuda_event for e in kernel_events])
         rc = lib.dsa_decode_step_timed(*args, ctypes.cast(evs, ctypes.c_void_p))
     _check(rc, "dsa_decode_step")
+    return scores, idx, out
+
+
+def dsa_decode_step_noalloc(iq, iw, ik, q, kv, ctx_len, k, Dv, scale, scores, idx, out, flags=0,
+                            stream=None):
+    """dsa_decode_step on the library's static per-device scratch (no workspace argument);
+    the outputs must be given. Returns (scores, idx, out)."""
+    torch = _torch()
+    lib = load_library()
+    B, Hi, Di = iq.shape
+    _, Hq, Dk = q.shape
+    N = ik.shape[0]
+    if kv.shape[0] != N:
+        raise ValueError("ik and kv must cover the same N positions")
+    lens = _host_lens(ctx_len, B)
+    dt = _attn_dtype(q, kv)
+    rc = lib.dsa_decode_step_noalloc(_dev(iq, "iq", torch.int8), _dev(iw, "iw", torch.int8),
+                                     _dev(ik, "ik", torch.int8), _dev(q, "q"), _dev(kv, "kv"),
+                                     lens.ctypes.data_as(ctypes.c_void_p), B, Hi, Di, Hq, Dk, Dv, N, k,
+                                     float(scale), dt, _dev(scores, "scores", torch.int32),
+                                     _dev(idx, "idx", torch.int32), _dev(out, "out", torch.float32), flags,
+                                     _stream(stream))
+    _check(rc, "dsa_decode_step_noalloc")
     return scores, idx, out
 
 

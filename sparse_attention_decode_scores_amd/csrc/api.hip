@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "../../include/dsa.h"
 #include "kernels.h"
@@ -163,6 +164,31 @@ int rows_per_score_launch(int Hi, int Di, int B) {
 }
 
 dsa_status hip_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
+
+// Scratch of dsa_decode_step_noalloc: one array per device, held for the life of the
+// process. Host code uses only the device address returned by hipGetSymbolAddress
+// (the array's name is a host-side stand-in there), looked up once per device with
+// that device current.
+constexpr size_t kScratchBytes = (size_t)DSA_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_lock;
+
+// The current device's scratch address, or nullptr if it cannot be resolved.
+void* device_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  std::lock_guard<std::mutex> hold(g_scratch_lock);
+  p = g_scratch[dev].load(std::memory_order_relaxed);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
 
 
 dsa_status run_scores(const int8_t* iq, const int8_t* iw, const int8_t* ik, const RowLens& lens,
@@ -423,6 +449,20 @@ dsa_status dsa_decode_step(const int8_t* iq, const int8_t* iw, const int8_t* ik,
                            unsigned flags, hipStream_t stream) {
   return dsa_decode_step_timed(iq, iw, ik, q, kv, ctx_len, B, Hi, Di, Hq, Dk, Dv, N, k, scale, dt,
                                scores, idx, out, ws, ws_bytes, flags, stream, nullptr);
+}
+
+dsa_status dsa_decode_step_noalloc(const int8_t* iq, const int8_t* iw, const int8_t* ik, const void* q,
+                                   const void* kv, const int32_t* ctx_len, int B, int Hi, int Di, int Hq,
+                                   int Dk, int Dv, int64_t N, int k, float scale, dsa_dtype dt,
+                                   int32_t* scores, int32_t* idx, float* out, unsigned flags,
+                                   hipStream_t stream) {
+  const size_t need = dsa_workspace_size(B, N, k, Hq, Dv);
+  if (need == 0) return DSA_ERR_INVALID_ARG;
+  if (need > kScratchBytes) return DSA_ERR_WORKSPACE;  // beyond the static scratch
+  void* ws = device_scratch();
+  if (ws == nullptr) return DSA_ERR_HIP;
+  return dsa_decode_step(iq, iw, ik, q, kv, ctx_len, B, Hi, Di, Hq, Dk, Dv, N, k, scale, dt, scores, idx, out,
+                         ws, kScratchBytes, flags, stream);
 }
 
 dsa_status dsa_read_stats(const void* ws, size_t ws_bytes, int B, dsa_row_stats* stats,

@@ -140,6 +140,20 @@ def test_decode_step_validation(lib):
     assert lib.dsa_decode_step(*bad) == INVALID
 
 
+def test_noalloc_rejects_sizes_beyond_its_scratch(lib):
+    # B=16, k=4096, 64 heads x 512 values needs far more than the static scratch: a clear
+    # workspace error before anything touches the device (the stand-in pointers are
+    # never read)
+    p, keep = lens(*([300000] * 16))
+    rc = lib.dsa_decode_step_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, p, 16, 64, 128, 64, 576, 512, 300000,
+                                     4096, 1 / 24, 1, FAKE, FAKE, FAKE, 0, None)
+    assert rc == WORKSPACE
+    assert binding.dsa_workspace_size(16, 300000, 4096, 64, 512) > 64 << 20
+    rc = lib.dsa_decode_step_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, p, 16, 64, 128, 64, 576, 512, 300000,
+                                     0, 1 / 24, 1, FAKE, FAKE, FAKE, 0, None)
+    assert rc == INVALID
+
+
 def test_read_stats_validation(lib):
     arr = (binding.RowStats * 2)()
     assert lib.dsa_read_stats(None, 4096, 1, ctypes.cast(arr, ctypes.c_void_p), None) == INVALID
