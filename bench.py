@@ -8,19 +8,30 @@ HBM. Default workload: 300,000 cached positions, k = 2,048, one query row.
 
 Cold cache by construction: the step cycles through --sets independent input sets
 (keys, latent cache, queries), so by the time a set comes back the other sets have
-streamed far more than the 256 MB Infinity Cache holds. The timed steps are HIP
-graph replays (one graph holds one step per set), bracketed by synchronisations.
-A second, eager pass over the same steps has the runtime stamp HIP events with the
-start and end of each stage's kernel (dsa_decode_step_timed), which times the
-indexer pass and the selection + attention pass live, kernel by kernel; its steps
-are queued in chunks behind a short sleep kernel, so they run back to back as in
-the graph rather than each starting on an idle GPU.
+streamed far more than the 256 MB Infinity Cache holds.
 
-Prints one JSON line (see the design doc for every field).
+Timings, all on the stream the library launches on:
+  - value: K steps as HIP graph replays (one graph holds one step per input set),
+    bracketed by synchronisations; mean microseconds per step.
+  - step_stats: the same steps as one-step graphs replayed back to back (queued
+    behind a sleep kernel), with HIP events between the replays: median, p10, p90.
+  - kernel durations: an eager pass of the same steps in which the runtime stamps
+    HIP events with each stage kernel's own dispatch start and end
+    (dsa_decode_step_timed), queued in chunks behind a sleep kernel so that the
+    kernels run back to back as in the graph. These feed the roofline figures.
+  - legs: the forced exhaustive path on the headline workload, the 62k-context
+    11-layer step and the 8-row verify block, each as graph replays plus the eager
+    kernel pass.
+  - cpu_baseline: the CPU oracle on the headline workload, single-threaded and with
+    its all-core OpenMP build, per stage, median of 5 after one warm-up.
+
+Prints one JSON line.
 """
 import argparse
 import json
 import os
+import platform
+import subprocess
 import sys
 import time
 
@@ -30,18 +41,35 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "DSA decode step µs & indexer+gather HBM GB/s, top-2048 at 62k/300k ctx"
-HBM_PEAK_GBPS = 8000.0
+HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E
+INT8_PEAK_TOPS = 5000.0     # MI355X dense int8 matrix-core peak (5.0 POPS)
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "decode_step_ctx300k_hbm_counters.json")
+
+# The pages' own figures, with their hardware (context, not targets).
+CONTEXT = {
+    "ds4 glm53-m3ultra branch post (rising, 2026-09-09), long-context paragraph": [
+        "Apple M3 Ultra, 80 GPU cores, Metal, GLM-5.3-Flash at 4 bits: the rewritten DSA selection "
+        "(parallel narrowing scans, then a small sort) saves about 1 ms per generated token",
+        "same machine, 300k-token context, end to end (all of the branch's changes): 21.6 -> 37.4 "
+        "tokens/s",
+        "same machine, 62k-token context, end to end (mostly decode fusion): 24 -> 38 tokens/s",
+    ],
+    "derived here": [
+        "1 ms per token over the model's 11 DSA layers is about 90 us of selection per layer per token "
+        "on the M3 Ultra, if each layer selects once per token",
+    ],
+}
 
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def device_set(torch, c, s, name):
+# ---------------------------------------------------------------- inputs and bytes
+
+def device_set(torch, c, s):
     """Inputs of rotation set s: set 0 from the shared generator, later sets drawn on the
-    GPU with the same distributions (torch generator seeded 9000 + s)."""
-    from sparse_attention_decode_scores_amd import inputs
+    GPU with the same distributions (torch generator seeded 9000 + 100 s + layer)."""
     dev = torch.device("cuda")
     if s == 0:
         d = {}
@@ -68,95 +96,172 @@ def device_set(torch, c, s, name):
     return d
 
 
-def essential_bytes(c):
-    """Algorithmic HBM bytes of one layer: every indexer key once, the scores written,
-    the k gathered latent rows, queries, weights and the output."""
-    B, N, Di, Dk, Dv, Hq, Hi, k = (c[x] for x in ("B", "N", "Di", "Dk", "Dv", "Hq", "Hi", "k"))
-    esz = 4 if c["dtype"] == "f32" else 2
-    keys = N * Di
-    scores = B * N * 4
-    gather = sum(min(k, int(n)) for n in c["ctx_len"]) * Dk * esz
-    small = B * Hi * Di + B * Hi + B * Hq * Dk * esz + B * Hq * Dv * 4 + B * k * 4
-    return keys, scores, gather, small
+def esz(c):
+    return 4 if c["dtype"] == "f32" else 2
+
+
+def rows_gathered(c):
+    return sum(min(c["k"], int(n)) for n in c["ctx_len"])
 
 
 def score_kernel_bytes(c):
-    """Algorithmic bytes of one launch of the indexer pass: keys read once, queries and
-    weights, scores written (the per-position figure is Di + 4*B bytes)."""
-    return c["N"] * c["Di"] + c["B"] * c["N"] * 4 + c["B"] * c["Hi"] * (c["Di"] + 1)
+    """Algorithmic bytes of one indexer pass: every key read once, plus the queries and
+    head weights (Di bytes per position, B*Hi*(Di+1) per launch). The int32 scores it
+    writes (4*B bytes per position) are as-built working data, reported apart."""
+    return c["N"] * c["Di"] + c["B"] * c["Hi"] * (c["Di"] + 1)
 
 
 def gather_pass_bytes(c):
-    """Algorithmic bytes of one launch of the selection + attention pass: the k selected
-    latent rows of every query row (Dk values each) and the attention queries. Candidate
-    keys and split partials are working data of this design, not counted."""
-    esz = 4 if c["dtype"] == "f32" else 2
-    rows = sum(min(c["k"], int(n)) for n in c["ctx_len"])
-    return rows * c["Dk"] * esz + c["B"] * c["Hq"] * c["Dk"] * esz
+    """Algorithmic bytes of one selection + attention pass: the k selected latent rows
+    of every query row (Dk values each) and the attention queries."""
+    return rows_gathered(c) * c["Dk"] * esz(c) + c["B"] * c["Hq"] * c["Dk"] * esz(c)
 
 
-def secondary_workload(torch, binding, name, steps, sets):
-    """Graph-replayed step time of another workload (GPU-generated inputs only; the
-    parity tests cover its correctness): one step = every layer of the workload."""
-    from sparse_attention_decode_scores_amd import inputs
-    base = dict(inputs.CONFIGS[name])
-    layers = base["layers"]
-    ctx_len = inputs.ctx_lengths(name)
-    data = []
-    for st in range(sets):
-        per = []
-        for l in range(layers):
-            c = dict(base, layer=l)
-            per.append(device_set(torch, c, 1 + st, name))
-        data.append(per)
-    B, N, k, Hq, Dv = base["B"], base["N"], base["k"], base["Hq"], base["Dv"]
-    ws = binding.new_workspace(B, N, k, Hq, Dv)
-    scores = torch.zeros((B, N), dtype=torch.int32, device="cuda")
-    idx = torch.empty((B, k), dtype=torch.int32, device="cuda")
-    out = torch.empty((B, Hq, Dv), dtype=torch.float32, device="cuda")
+def step_essential_bytes(c):
+    """Essential HBM bytes of one layer: keys once, the gathered rows, queries, head
+    weights and the attention output (scores and indices are working data)."""
+    return (c["N"] * c["Di"] + c["B"] * c["Hi"] * (c["Di"] + 1) + rows_gathered(c) * c["Dk"] * esz(c)
+            + c["B"] * c["Hq"] * c["Dk"] * esz(c) + c["B"] * c["Hq"] * c["Dv"] * 4)
 
-    def step(st):
-        for l in range(layers):
-            d = data[st][l]
-            binding.dsa_decode_step(d["iq"], d["iw"], d["ik"], d["q"], d["kv"], ctx_len, k, Dv,
-                                    base["scale"], scores=scores, idx=idx, out=out, workspace=ws)
 
-    for i in range(2 * sets):
-        step(i % sets)
-    torch.cuda.synchronize()
-    stream = torch.cuda.Stream()
-    with torch.cuda.stream(stream):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            for st in range(sets):
-                step(st)
-    torch.cuda.synchronize()
-    g.replay()
-    torch.cuda.synchronize()
-    reps = max(1, steps // sets)
-    t0 = time.perf_counter()
-    for _ in range(reps):
+def indexer_int_ops(c):
+    """Integer operations of the indexer contraction: a multiply and an add per query
+    head, dim and scored position."""
+    return 2 * c["Hi"] * c["Di"] * sum(int(n) for n in c["ctx_len"])
+
+
+# ---------------------------------------------------------------- timing helpers
+
+class Runner:
+    """One workload's rotating input sets and outputs, and its timing passes."""
+
+    def __init__(self, torch, binding, name, sets, host_set0=True):
+        from sparse_attention_decode_scores_amd import inputs
+        self.torch, self.binding, self.name = torch, binding, name
+        base = dict(inputs.CONFIGS[name])
+        self.layers = base["layers"]
+        self.hosts = []
+        if host_set0:
+            self.hosts = [inputs.make(name, l) for l in range(self.layers)]
+            self.c = self.hosts[0]
+        else:
+            self.c = dict(base, ctx_len=inputs.ctx_lengths(name), layer=0)
+        self.R = sets
+        self.data = []
+        for s in range(sets):
+            per = []
+            for l in range(self.layers):
+                c = self.hosts[l] if host_set0 else dict(self.c, layer=l)
+                per.append(device_set(torch, c, s if host_set0 else s + 1))
+            self.data.append(per)
+        c = self.c
+        self.ws = binding.new_workspace(c["B"], c["N"], c["k"], c["Hq"], c["Dv"])
+        self.scores = torch.zeros((c["B"], c["N"]), dtype=torch.int32, device="cuda")
+        self.idx = torch.empty((c["B"], c["k"]), dtype=torch.int32, device="cuda")
+        self.out = torch.empty((c["B"], c["Hq"], c["Dv"]), dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+
+    def bytes_per_set(self):
+        c = self.c
+        return self.layers * (c["N"] * c["Di"] + c["N"] * c["Dk"] * esz(c))
+
+    def step(self, s, flags=0, kernel_events=None):
+        c = self.c
+        for l in range(self.layers):
+            d = self.data[s][l]
+            ev = None if kernel_events is None else kernel_events[l]
+            self.binding.dsa_decode_step(d["iq"], d["iw"], d["ik"], d["q"], d["kv"], c["ctx_len"], c["k"],
+                                         c["Dv"], c["scale"], scores=self.scores, idx=self.idx, out=self.out,
+                                         workspace=self.ws, flags=flags, kernel_events=ev)
+
+    def capture(self, sets, flags=0):
+        torch = self.torch
+        stream = torch.cuda.Stream()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for s in sets:
+                    self.step(s, flags)
+        torch.cuda.synchronize()
         g.replay()
-    torch.cuda.synchronize()
-    us = (time.perf_counter() - t0) * 1e6 / (reps * sets)
-    keys, sc_bytes, gather, small = essential_bytes(dict(base, ctx_len=ctx_len))
-    step_bytes = layers * (keys + sc_bytes + gather + small)
-    del data
-    return {
-        "workload": "%s: %d cached positions, k=%d, %d query row(s), %d layers/step (distinct caches)"
-                    % (name, N, k, B, layers),
-        "us_per_step": round(us, 3),
-        "us_per_layer": round(us / layers, 3),
-        "step_essential_bytes": step_bytes,
-        "step_essential_GBps": round(step_bytes / (us * 1e-6) / 1e9, 1),
-        "cache": "cold: %d rotating input sets" % sets,
-        "launch": "HIP graph replay of %d step(s) per graph, %d step(s) timed" % (sets, reps * sets),
-    }
+        torch.cuda.synchronize()
+        return g
+
+    def graph_us(self, steps, flags=0):
+        """Mean us per step over `steps` graph-replayed steps (R steps per graph)."""
+        torch = self.torch
+        full = self.capture(range(self.R), flags)
+        reps = max(1, steps // self.R)
+        full.replay()  # the first replay uploads the graph: not timed
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            full.replay()
+        torch.cuda.synchronize()
+        us = (time.perf_counter() - t0) * 1e6 / (reps * self.R)
+        del full
+        return us, reps * self.R
+
+    def step_stats(self, steps, flags=0, chunk=40):
+        """Per-step times of one-step graph replays run back to back: HIP events recorded
+        between the replays on the replay stream."""
+        torch = self.torch
+        graphs = [self.capture([s], flags) for s in range(self.R)]
+        stream = torch.cuda.Stream()
+        times = []
+        with torch.cuda.stream(stream):
+            for i0 in range(0, steps, chunk):
+                n = min(chunk, steps - i0)
+                ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+                torch.cuda._sleep(20_000_000)  # lets the host queue the chunk ahead of the GPU
+                ev[0].record()
+                for i in range(n):
+                    graphs[(i0 + i) % self.R].replay()
+                    ev[i + 1].record()
+                torch.cuda.synchronize()
+                times += [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(n)]
+        del graphs
+        t = np.array(times)
+        return {"median_us": round(float(np.median(t)), 3), "p10_us": round(float(np.percentile(t, 10)), 3),
+                "p90_us": round(float(np.percentile(t, 90)), 3), "mean_us": round(float(t.mean()), 3),
+                "n": int(t.size)}
+
+    def kernel_us(self, steps, flags=0, chunk=30):
+        """Mean duration of each stage's kernels (us): score, select+attend, combine,
+        from events the runtime stamps with each dispatch's own start and end."""
+        torch = self.torch
+        evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(self.layers)]
+               for _ in range(steps)]
+        for per_step in evs:  # torch creates the HIP event on first record
+            for per_layer in per_step:
+                for e in per_layer:
+                    e.record()
+        torch.cuda.synchronize()
+        # the host takes longer to issue an eager step than the GPU takes to run it: each
+        # chunk is queued behind a sleep kernel and then runs back to back
+        for i0 in range(0, steps, chunk):
+            torch.cuda._sleep(16_000_000)
+            for i in range(i0, min(steps, i0 + chunk)):
+                self.step(i % self.R, flags, evs[i])
+        torch.cuda.synchronize()
+        st = np.array([[[e[0].elapsed_time(e[1]), e[2].elapsed_time(e[3]), e[4].elapsed_time(e[5])]
+                        for e in per_step] for per_step in evs]) * 1e3  # [steps][layers][3]
+        return [float(st[:, :, i].mean()) for i in range(3)]
+
+    def paths(self):
+        return [s["path"] for s in self.binding.dsa_read_stats(self.ws, self.c["B"])]
+
+
+def describe(c, name, layers):
+    return ("%s: %d cached positions, k=%d, %d query row(s), %d layer(s)/step; indexer %d heads x %d int8, "
+            "one shared key per position; attention %d heads over a %d-value %s latent row (%d output values)"
+            % (name, c["N"], c["k"], c["B"], layers, c["Hi"], c["Di"], c["Hq"], c["Dk"], c["dtype"], c["Dv"]))
 
 
 def measured_traffic(config):
     """HBM bytes per launch of each libdsa kernel from the committed counter summary, or
-    None for a kernel whose sources changed since the counters were taken."""
+    {} when a kernel source changed since the counters were taken."""
     from sparse_attention_decode_scores_amd.profsum import library_source_sha
     if not os.path.exists(PMC_SUMMARY):
         return {}
@@ -167,51 +272,117 @@ def measured_traffic(config):
     return {k: v.get("hbm_bytes_per_launch") for k, v in pmc.get("kernels", {}).items()}
 
 
-def cpu_baseline(name, layers, budget_s):
+# ---------------------------------------------------------------- CPU baseline
+
+def cpu_model():
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except Exception:
+        pass
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(name, reps=5):
+    """The oracle on one layer of the workload: per stage and whole step, median of
+    `reps` runs after one warm-up, single-threaded and with the OpenMP build."""
     import oracle
     from sparse_attention_decode_scores_amd import inputs
-    runs, spent, per_layer = 0, 0.0, []
-    layer = 0
-    while True:
-        c = inputs.make(name, layer % layers)
-        t = time.perf_counter()
-        oracle.decode_step(c["iq"], c["iw"], c["ik"], c["q"], c["kv"], c["ctx_len"], c["k"], c["Dv"],
-                           c["scale"])
-        dt = time.perf_counter() - t
-        per_layer.append(dt)
-        spent += dt
-        runs += 1
-        layer += 1
-        if spent >= budget_s or runs >= 50:
-            break
-    us_step = float(np.mean(per_layer)) * layers * 1e6
-    sample = ("%d oracle decode-step call(s) on layer input(s) of %s (%d positions, k=%d), "
-              "%.1f s of CPU work; step = %d layer(s) x mean per-layer time"
-              % (runs, name, c["N"], c["k"], spent, layers))
-    return {"value": us_step, "unit": "us", "cores": 1, "kind": "oracle", "sample": sample}
+    c = inputs.make(name, 0)
+    out = {}
+    for omp in (False, True):
+        stages = {"index_scores": [], "topk_select": [], "sparse_attn": []}
+        for r in range(reps + 1):
+            t0 = time.perf_counter()
+            s = oracle.index_scores(c["iq"], c["iw"], c["ik"], c["ctx_len"], omp=omp)
+            t1 = time.perf_counter()
+            i = oracle.topk_select(s, c["ctx_len"], c["k"], omp=omp)
+            t2 = time.perf_counter()
+            oracle.sparse_attn(c["q"], c["kv"], i, c["Dv"], c["scale"], omp=omp)
+            t3 = time.perf_counter()
+            if r > 0:  # run 0 warms up
+                stages["index_scores"].append(t1 - t0)
+                stages["topk_select"].append(t2 - t1)
+                stages["sparse_attn"].append(t3 - t2)
+        tot = np.sum([stages[k] for k in stages], axis=0)
+        out[omp] = {"value": round(float(np.median(tot)) * 1e6, 1),
+                    "stages_us": {k: round(float(np.median(v)) * 1e6, 1) for k, v in stages.items()},
+                    "cores": oracle.threads(omp)}
+    layers = inputs.CONFIGS[name]["layers"]
+    single, allc = out[False], out[True]
+    return {
+        "value": single["value"] * layers, "unit": "us", "cores": single["cores"], "kind": "oracle",
+        "sample": ("one layer of %s (%d positions, k=%d), each stage timed, median of %d runs after one "
+                   "warm-up; value = that step time x %d layer(s)" % (name, c["N"], c["k"], reps, layers)),
+        "stages_us": single["stages_us"],
+        "all_cores": {"value": allc["value"] * layers, "unit": "us", "cores": allc["cores"],
+                      "build": "the same oracle source with -fopenmp (positions and heads split over "
+                               "threads; the sort sequential)", "stages_us": allc["stages_us"]},
+        "cpu_model": cpu_model(), "nproc": os.cpu_count(),
+    }
 
+
+# ---------------------------------------------------------------- legs
+
+def kernel_figures(c, score_us, select_us, combine_us):
+    sb, gb = score_kernel_bytes(c), gather_pass_bytes(c)
+    return {"score_us": round(score_us, 3), "select_attend_us": round(select_us, 3),
+            "combine_us": round(combine_us, 3),
+            "indexer_GBps": round(sb / (score_us * 1e-6) / 1e9, 1),
+            "indexer_frac_of_hbm_peak": round(sb / (score_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "gather_GBps": round(gb / (select_us * 1e-6) / 1e9, 1),
+            "gather_frac_of_hbm_peak": round(gb / (select_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+
+
+def leg(torch, binding, name, steps, sets):
+    log("leg", name)
+    r = Runner(torch, binding, name, sets, host_set0=False)
+    for i in range(2 * sets):
+        r.step(i % sets)
+    torch.cuda.synchronize()
+    us, n = r.graph_us(steps)
+    k = r.kernel_us(max(8, steps // 2))
+    c = r.c
+    res = {"workload": describe(c, name, r.layers), "us_per_step": round(us, 3),
+           "us_per_layer": round(us / r.layers, 3), "steps": n,
+           "cache": "cold: %d rotating input sets of %.0f MB" % (sets, r.bytes_per_set() / 1e6),
+           "kernels_per_layer": kernel_figures(c, *k),
+           "step_essential_GBps": round(r.layers * step_essential_bytes(c) / (us * 1e-6) / 1e9, 1)}
+    if c["B"] > 1:
+        ops = indexer_int_ops(c)
+        tops = ops / (k[0] * 1e-6) / 1e12
+        res["indexer_int8_TOPS"] = round(tops, 1)
+        res["indexer_frac_of_int8_peak"] = round(tops / INT8_PEAK_TOPS, 4)
+        res["indexer_int_ops_per_launch"] = ops
+    log("leg %s: %.2f us/step" % (name, us))
+    del r
+    torch.cuda.empty_cache()
+    return res
+
+
+# ---------------------------------------------------------------- main
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=240)
     ap.add_argument("--warmup", type=int, default=24)
-    ap.add_argument("--config", default="ctx300k", choices=["ctx16k", "ctx62k_11layers", "ctx300k", "verify8_ctx131k"])
+    ap.add_argument("--config", default="ctx300k",
+                    choices=["ctx16k", "ctx62k_11layers", "ctx300k", "verify8_ctx131k"])
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = default per workload)")
-    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--legs", default="fallback,ctx62k_11layers,verify8_ctx131k",
+                    help="comma list of extra legs, or 'none'")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--secondary", default="ctx62k_11layers",
-                    help="also time this workload (reported beside the headline; 'none' to skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain copy kernel of 256 MiB (scale reference for HBM counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the design for "
-              "position-sharding over RCCL is described in DESIGN.md). Run with --gpus 1.",
-              file=sys.stderr)
+        print("bench.py measures one GPU: this build has no multi-GPU path (DESIGN.md describes how "
+              "the path would shard by position over RCCL). Run with --gpus 1.", file=sys.stderr)
         return 2
 
     import torch
@@ -220,112 +391,57 @@ def main():
     binding.load_library()
     torch.cuda.set_device(0)
     cfg = inputs.CONFIGS[args.config]
-    layers = cfg["layers"]
-    R = args.sets or (1 if layers > 1 else 12)
-    log("workload", args.config, "layers", layers, "sets", R)
-
-    # inputs: [set][layer]
-    host = [inputs.make(args.config, l) for l in range(layers)]
-    sets = []
-    for s in range(R):
-        sets.append([device_set(torch, host[l], s, args.config) for l in range(layers)])
-    c = host[0]
-    B, N, k, Hq, Dv = c["B"], c["N"], c["k"], c["Hq"], c["Dv"]
-    ws = binding.new_workspace(B, N, k, Hq, Dv)
-    scores = torch.zeros((B, N), dtype=torch.int32, device="cuda")
-    idx = torch.empty((B, k), dtype=torch.int32, device="cuda")
-    out = torch.empty((B, Hq, Dv), dtype=torch.float32, device="cuda")
-    torch.cuda.synchronize()
+    R = args.sets or (4 if cfg["layers"] > 1 else 12)
+    log("workload", args.config, "layers", cfg["layers"], "sets", R)
+    run = Runner(torch, binding, args.config, R)
+    c = run.c
     log("inputs resident: %.2f GB" % (torch.cuda.memory_allocated() / 1e9))
 
-    def step(s, kernel_events=None):
-        for l in range(layers):
-            d = sets[s][l]
-            ev = None if kernel_events is None else kernel_events[l]
-            binding.dsa_decode_step(d["iq"], d["iw"], d["ik"], d["q"], d["kv"], host[l]["ctx_len"], k,
-                                    Dv, c["scale"], scores=scores, idx=idx, out=out, workspace=ws,
-                                    kernel_events=ev)
-
     for i in range(args.warmup):
-        step(i % R)
+        run.step(i % R)
     torch.cuda.synchronize()
 
+    # ---- timed region: K graph-replayed steps
     K = args.steps
-    graphs = []
-    if not args.no_graph:
-        stream = torch.cuda.Stream()
-        torch.cuda.synchronize()
-        with torch.cuda.stream(stream):
-            full = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(full, stream=stream):
-                for s in range(R):
-                    step(s)
-            tail = None
-            if K % R:
-                tail = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(tail, stream=stream):
-                    for s in range(K % R):
-                        step(s)
-        torch.cuda.synchronize()
-        full.replay()
-        if tail is not None:
-            tail.replay()
-        torch.cuda.synchronize()
-        graphs = [full] * (K // R) + ([tail] if tail is not None else [])
-
-    # ---- timed region: K steps
+    full = run.capture(range(R))
+    tail = run.capture(range(K % R)) if K % R else None
+    graphs = [full] * (K // R) + ([tail] if tail is not None else [])
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    e0.record()
-    if graphs:
-        for g in graphs:
-            g.replay()
-    else:
-        for i in range(K):
-            step(i % R)
-    e1.record()
+    for g in graphs:
+        g.replay()
     torch.cuda.synchronize()
-    wall_s = time.perf_counter() - t0
-    gpu_ms = e0.elapsed_time(e1)
-    us_step = wall_s * 1e6 / K
-    log("timed %d steps: wall %.3f ms, events %.3f ms -> %.2f us/step" % (K, wall_s * 1e3, gpu_ms, us_step))
+    us_step = (time.perf_counter() - t0) * 1e6 / K
+    log("timed %d steps: %.2f us/step" % (K, us_step))
+    del graphs, full, tail
 
-    # ---- kernel timing pass (eager; events carry each stage kernel's own start and end)
-    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(layers)]
-           for _ in range(K)]
-    for per_step in evs:  # torch creates the HIP event on first record
-        for per_layer in per_step:
-            for e in per_layer:
-                e.record()
-    torch.cuda.synchronize()
-    # The host takes longer to issue an eager step than the GPU takes to run it, so
-    # steps issued one after another would each start on an idle GPU. Each chunk of
-    # steps is therefore queued behind a sleep kernel (longer than the host needs to
-    # issue the chunk) and then runs back to back. Every step counts, so these means
-    # are the eager pass's means in the kernel trace of the same command.
-    chunk = 30
-    for i0 in range(0, K, chunk):
-        torch.cuda._sleep(16_000_000)  # several ms at the shader clock
-        for i in range(i0, min(K, i0 + chunk)):
-            step(i % R, evs[i])
-    torch.cuda.synchronize()
-    st = np.array([[[e[0].elapsed_time(e[1]), e[2].elapsed_time(e[3]), e[4].elapsed_time(e[5])]
-                    for e in per_step] for per_step in evs]) * 1e3  # us [K][layers][3]
-    score_us = float(st[:, :, 0].mean())
-    select_us = float(st[:, :, 1].mean())
-    combine_us = float(st[:, :, 2].mean())
-    log("kernel durations (eager, HIP events): score %.2f us, select+attend %.2f us, combine %.2f us"
-        % (score_us, select_us, combine_us))
-    stats = binding.dsa_read_stats(ws, B)
+    stats = run.step_stats(K)
+    log("one-step replays: median %.2f us (p10 %.2f, p90 %.2f)" % (stats["median_us"], stats["p10_us"],
+                                                                   stats["p90_us"]))
+    score_us, select_us, combine_us = run.kernel_us(K)
+    log("kernel durations (eager, dispatch-stamped events): score %.2f us, select+attend %.2f us, "
+        "combine %.2f us" % (score_us, select_us, combine_us))
+    paths = run.paths()
 
-    # reference read rate: a vendor streaming reduction over the same key caches, in the
-    # same cold rotation (context for the roofline fraction, not part of the metric)
+    fallback = None
+    legs = [x for x in args.legs.split(",") if x and x != "none"]
+    if "fallback" in legs:
+        f_us, f_n = run.graph_us(max(R, K // 5), flags=binding.FLAG_FORCE_FALLBACK)
+        f_paths = run.paths()
+        fk = run.kernel_us(max(R, K // 10), flags=binding.FLAG_FORCE_FALLBACK)
+        fallback = {"us_per_step": round(f_us, 3), "steps": f_n, "ratio_to_candidate_path": round(f_us / us_step, 3),
+                    "paths": f_paths, "select_attend_us": round(fk[1], 3),
+                    "what": "the same workload with DSA_FLAG_FORCE_FALLBACK: the exhaustive selection "
+                            "(a radix select over every position) for every row, graph replay"}
+        log("forced fallback: %.2f us/step" % f_us)
+
+    # reference read rate: a vendor streaming reduction over the same key caches, in the same
+    # cold rotation (context for the roofline fraction, not part of the metric)
     rd = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(4 * R)]
     for i, (r0, r1) in enumerate(rd):
-        ikf = sets[i % R][0]["ik"].view(torch.float32)  # the same bytes; values are irrelevant
+        ikf = run.data[i % R][0]["ik"].view(torch.float32)  # the same bytes; values are irrelevant
         r0.record()
-        acc = torch.sum(ikf)
+        torch.sum(ikf)
         r1.record()
     torch.cuda.synchronize()
     read_us = float(np.mean([r0.elapsed_time(r1) for r0, r1 in rd[R:]])) * 1e3
@@ -338,26 +454,33 @@ def main():
             torch.neg(src, out=dst)
         torch.cuda.synchronize()
         log("copy calibration: 5 x torch.neg over 256 MiB")
+        del src, dst
+
+    layers = run.layers
+    cache = ("cold: %d rotating input sets of %.0f MB each" % (R, run.bytes_per_set() / 1e6))
+    del run
+    torch.cuda.empty_cache()
+
+    leg_out = {}
+    for name in legs:
+        if name in ("ctx62k_11layers", "verify8_ctx131k") and name != args.config:
+            leg_out[name] = leg(torch, binding, name, max(16, K // 8), 4)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline: the oracle, single-threaded and all-core, median of 5")
+        cpu = cpu_baseline(args.config)
 
     kb = score_kernel_bytes(c)
     achieved = kb / (score_us * 1e-6) / 1e9
     traffic = measured_traffic(args.config)
     gb = gather_pass_bytes(c)
     g_achieved = gb / (select_us * 1e-6) / 1e9
-    keys, sc_bytes, gather, small = essential_bytes(c)
-    step_bytes = layers * (keys + sc_bytes + gather + small)
-
-    secondary = None
-    if args.secondary != "none" and args.secondary != args.config:
-        log("secondary workload", args.secondary)
-        secondary = secondary_workload(torch, binding, args.secondary, max(8, args.steps // 8), 4)
-        log("secondary: %.2f us/step" % secondary["us_per_step"])
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        log("cpu baseline: timing the oracle for about %.0f s" % args.cpu_seconds)
-        cpu = cpu_baseline(args.config, layers, args.cpu_seconds)
-
+    sb = layers * step_essential_bytes(c)
+    budget_us = sb / (0.7 * HBM_PEAK_GBPS * 1e9) * 1e6
+    timing_note = ("duration: mean over the eager pass of dispatch-stamped HIP events on the launch stream "
+                   "(kernels run back to back as in the graph; the rocprofv3 kernel trace of the same "
+                   "command lists the graph-replayed launches beside them)")
     line = {
         "metric": METRIC,
         "value": round(us_step, 3),
@@ -371,15 +494,10 @@ def main():
         "vs_baseline": None,
         "dtype": "int8 indexer (int32 accumulate) + bf16 attention (fp32 accumulate)",
         "data": "synthetic (seeded; no model weights or caches)",
-        "config": {
-            "workload": "%s: %d cached positions, k=%d, %d query row(s), %d layer(s)/step; indexer "
-                        "%d heads x %d int8, one shared key per position; attention %d heads over a "
-                        "%d-value bf16 latent row (%d output values)"
-                        % (args.config, N, k, B, layers, c["Hi"], c["Di"], Hq, c["Dk"], Dv),
-            "cache": "cold: %d rotating input sets of %.0f MB each" % (R, layers * (keys + N * c["Dk"] * 2) / 1e6)
-                     if R > 1 else "cold: %d layers x %.0f MB streamed per step" % (layers, (keys + N * c["Dk"] * 2) / 1e6),
-            "launch": "HIP graph replay of %d step(s) per graph" % R if graphs else "eager launches",
-        },
+        "config": {"workload": describe(c, args.config, layers), "cache": cache,
+                   "launch": "HIP graph replay of %d step(s) per graph" % R},
+        "step_stats": dict(stats, how="one-step graphs replayed back to back behind a sleep kernel, HIP "
+                                      "events between the replays"),
         "roofline": {
             "bound": "hbm",
             "kernel": "indexer score pass (k_score_row: int8 MFMA, per-chunk top-m candidates)",
@@ -389,7 +507,10 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic.get("k_score"),
             "algorithmic_bytes_per_launch": kb,
+            "algorithmic_bytes": "every indexer key once (N*Di) + queries and head weights (B*Hi*(Di+1))",
+            "as_built_score_write_bytes": c["B"] * c["N"] * 4,
             "launch_us": round(score_us, 3),
+            "timing": timing_note,
         },
         "roofline_gather": {
             "bound": "hbm",
@@ -402,21 +523,31 @@ def main():
             "algorithmic_bytes_per_launch": gb,
             "launch_us": round(select_us, 3),
         },
+        "roofline_step": {
+            "bound": "hbm",
+            "essential_bytes": sb,
+            "achieved": round(sb / (us_step * 1e-6) / 1e9, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(sb / (us_step * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "us_at_70pct_of_peak": round(budget_us, 3),
+            "x_over_that": round(us_step / budget_us, 2),
+        },
+        "kernel_us_events": {"score": round(score_us, 3), "select_attend": round(select_us, 3),
+                             "combine": round(combine_us, 3)},
+        "fallback": fallback,
+        "legs": leg_out,
         "cpu_baseline": cpu,
-        "secondary": secondary,
         "read_reference": {
             "what": "torch.sum over one layer's key cache (its bytes viewed as fp32), same cold rotation, "
-                    "eager; HIP events around each launch, so dispatch latency is included (the "
-                    "kernel trace gives the kernel's own time); a streaming-read rate for this buffer",
+                    "eager, HIP events around each launch (dispatch latency included): a streaming-read "
+                    "rate for this buffer",
             "bytes": read_bytes,
             "us": round(read_us, 3),
             "GBps": round(read_bytes / (read_us * 1e-6) / 1e9, 1),
         },
-        "kernel_us_events": {"score": round(score_us, 3), "select_attend": round(select_us, 3),
-                                   "combine": round(combine_us, 3)},
-        "step_essential_bytes": step_bytes,
-        "step_essential_GBps": round(step_bytes / (us_step * 1e-6) / 1e9, 1),
-        "selection_paths": [s["path"] for s in stats],
+        "selection_paths": paths,
+        "context": CONTEXT,
     }
     print(json.dumps(line), flush=True)
     return 0

@@ -15,27 +15,30 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "dsa_oracle.cpp")
 _LIB = os.path.join(_HERE, "liboracle_dsa.so")
-_lib = None
+_LIB_OMP = os.path.join(_HERE, "liboracle_dsa_omp.so")  # the same source with -fopenmp
+_libs = {}
 
 F32, BF16 = 0, 1
 
 
 def build(force=True):
-    """Compile dsa_oracle.cpp into liboracle_dsa.so next to it (plain g++, -O2)."""
-    if not force and os.path.exists(_LIB):
-        return _LIB
-    tmp = _LIB + ".tmp%d" % os.getpid()
-    subprocess.check_call(["g++", "-O2", "-std=c++17", "-shared", "-fPIC", "-o", tmp, _SRC])
-    os.replace(tmp, _LIB)
+    """Compile dsa_oracle.cpp into liboracle_dsa.so next to it (plain g++, -O2), and the
+    same source with -fopenmp into liboracle_dsa_omp.so (the all-core CPU baseline)."""
+    for path, extra in ((_LIB, []), (_LIB_OMP, ["-fopenmp"])):
+        if not force and os.path.exists(path):
+            continue
+        tmp = path + ".tmp%d" % os.getpid()
+        subprocess.check_call(["g++", "-O2", "-std=c++17", *extra, "-shared", "-fPIC", "-o", tmp, _SRC])
+        os.replace(tmp, path)
     return _LIB
 
 
-def _load():
-    global _lib
-    if _lib is None:
-        if not os.path.exists(_LIB):
-            build()
-        lib = ctypes.CDLL(_LIB)
+def _load(omp=False):
+    path = _LIB_OMP if omp else _LIB
+    if path not in _libs:
+        if not os.path.exists(path):
+            build(force=False)
+        lib = ctypes.CDLL(path)
         p, i32, i64, dbl = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
         lib.dsa_ref_index_scores.argtypes = [p, p, p, p, i32, i32, i32, i64, p]
         lib.dsa_ref_topk_select.argtypes = [p, p, i32, i64, i32, p]
@@ -43,10 +46,15 @@ def _load():
         lib.dsa_ref_decode_step.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32, i32,
                                             i64, i32, dbl, i32, p, p, p]
         for f in (lib.dsa_ref_index_scores, lib.dsa_ref_topk_select, lib.dsa_ref_sparse_attn,
-                  lib.dsa_ref_decode_step):
+                  lib.dsa_ref_decode_step, lib.dsa_ref_threads):
             f.restype = ctypes.c_int
-        _lib = lib
-    return _lib
+        _libs[path] = lib
+    return _libs[path]
+
+
+def threads(omp=False):
+    """Threads the oracle's loops use (1, or OpenMP's count for the omp build)."""
+    return int(_load(omp).dsa_ref_threads())
 
 
 def _ptr(a):
@@ -74,7 +82,7 @@ def _kv_dtype(a):
     raise TypeError("attention inputs must be float32 or bf16 bit patterns (uint16)")
 
 
-def index_scores(iq, iw, ik, ctx_len):
+def index_scores(iq, iw, ik, ctx_len, omp=False):
     """iq [B,Hi,Di] int8, iw [B,Hi] int8, ik [N,Di] int8, ctx_len [B] int32 -> scores [B,N] int32.
 
     Entries at or past ctx_len[b] are left at 0 (the oracle never writes them).
@@ -85,22 +93,22 @@ def index_scores(iq, iw, ik, ctx_len):
     N = ik.shape[0]
     assert ik.shape[1] == Di and iw.shape == (B, Hi) and ctx_len.shape == (B,)
     scores = np.zeros((B, N), np.int32)
-    _check(_load().dsa_ref_index_scores(_ptr(iq), _ptr(iw), _ptr(ik), _ptr(ctx_len), B, Hi, Di, N,
+    _check(_load(omp).dsa_ref_index_scores(_ptr(iq), _ptr(iw), _ptr(ik), _ptr(ctx_len), B, Hi, Di, N,
                                         _ptr(scores)), "index_scores")
     return scores
 
 
-def topk_select(scores, ctx_len, k):
+def topk_select(scores, ctx_len, k, omp=False):
     """scores [B,N] int32, ctx_len [B] int32 -> idx [B,k] int32 ((score desc, pos asc), -1 pad)."""
     scores, ctx_len = _c(scores, np.int32), _c(ctx_len, np.int32)
     B, N = scores.shape
     idx = np.empty((B, k), np.int32)
-    _check(_load().dsa_ref_topk_select(_ptr(scores), _ptr(ctx_len), B, N, k, _ptr(idx)),
+    _check(_load(omp).dsa_ref_topk_select(_ptr(scores), _ptr(ctx_len), B, N, k, _ptr(idx)),
            "topk_select")
     return idx
 
 
-def sparse_attn(q, kv, idx, Dv, scale):
+def sparse_attn(q, kv, idx, Dv, scale, omp=False):
     """q [B,Hq,Dk], kv [N,Dk] (float32 or bf16 bits as uint16), idx [B,k] -> out [B,Hq,Dv] float64."""
     dt = _kv_dtype(q)
     if _kv_dtype(kv) != dt:
@@ -111,12 +119,12 @@ def sparse_attn(q, kv, idx, Dv, scale):
     k = idx.shape[1]
     assert kv.shape[1] == Dk and idx.shape[0] == B
     out = np.empty((B, Hq, Dv), np.float64)
-    _check(_load().dsa_ref_sparse_attn(_ptr(q), _ptr(kv), _ptr(idx), B, Hq, Dk, Dv, N, k,
+    _check(_load(omp).dsa_ref_sparse_attn(_ptr(q), _ptr(kv), _ptr(idx), B, Hq, Dk, Dv, N, k,
                                        float(scale), dt, _ptr(out)), "sparse_attn")
     return out
 
 
-def decode_step(iq, iw, ik, q, kv, ctx_len, k, Dv, scale):
+def decode_step(iq, iw, ik, q, kv, ctx_len, k, Dv, scale, omp=False):
     """All three stages; returns (scores [B,N] int32, idx [B,k] int32, out [B,Hq,Dv] float64)."""
     iq, iw, ik = _c(iq, np.int8), _c(iw, np.int8), _c(ik, np.int8)
     ctx_len = _c(ctx_len, np.int32)
@@ -131,7 +139,7 @@ def decode_step(iq, iw, ik, q, kv, ctx_len, k, Dv, scale):
     scores = np.zeros((B, N), np.int32)
     idx = np.empty((B, k), np.int32)
     out = np.empty((B, Hq, Dv), np.float64)
-    _check(_load().dsa_ref_decode_step(_ptr(iq), _ptr(iw), _ptr(ik), _ptr(q), _ptr(kv), _ptr(ctx_len),
+    _check(_load(omp).dsa_ref_decode_step(_ptr(iq), _ptr(iw), _ptr(ik), _ptr(q), _ptr(kv), _ptr(ctx_len),
                                        B, Hi, Di, Hq, Dk, Dv, N, k, float(scale), dt,
                                        _ptr(scores), _ptr(idx), _ptr(out)), "decode_step")
     return scores, idx, out

@@ -21,14 +21,30 @@
 //    score descending with ties to the lower position; softmax in fp64.
 //
 // Everything here is written for obviousness, not speed: int64 accumulation,
-// std::stable_sort over all valid positions, fp64 softmax with std::exp.
+// std::stable_sort over all valid positions, fp64 softmax with std::exp. Built with
+// -fopenmp (the all-core CPU baseline), the loops over positions (scores) and over
+// heads (attention) are split over threads; each iteration is independent and writes
+// only its own outputs, so the results are the same. The sort stays sequential.
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
 #include <vector>
 
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
 extern "C" {
+
+// Threads the loops above use (1 without OpenMP).
+int dsa_ref_threads() {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
 
 // Return codes of the oracle (its own, unrelated to the library's).
 enum { REF_OK = 0, REF_BAD_ARG = 1, REF_OVERFLOW = 2 };
@@ -42,6 +58,8 @@ int dsa_ref_index_scores(const int8_t* iq, const int8_t* iw, const int8_t* ik,
   if (B < 1 || Hi < 1 || Di < 1 || N < 1) return REF_BAD_ARG;
   for (int b = 0; b < B; ++b) {
     if (ctx_len[b] < 0 || ctx_len[b] > N) return REF_BAD_ARG;
+    int overflow = 0;
+#pragma omp parallel for schedule(static) reduction(| : overflow)
     for (int64_t s = 0; s < ctx_len[b]; ++s) {
       int64_t score = 0;
       for (int h = 0; h < Hi; ++h) {
@@ -51,9 +69,12 @@ int dsa_ref_index_scores(const int8_t* iq, const int8_t* iw, const int8_t* ik,
         int64_t relu = acc > 0 ? acc : 0;
         score += (int64_t)iw[(int64_t)b * Hi + h] * relu;
       }
-      if (score > INT32_MAX || score < INT32_MIN) return REF_OVERFLOW;
-      scores[(int64_t)b * N + s] = (int32_t)score;
+      if (score > INT32_MAX || score < INT32_MIN)
+        overflow = 1;
+      else
+        scores[(int64_t)b * N + s] = (int32_t)score;
     }
+    if (overflow) return REF_OVERFLOW;
   }
   return REF_OK;
 }
@@ -106,6 +127,7 @@ int dsa_ref_sparse_attn(const void* q, const void* kv, const int32_t* idx, int B
       if (r < 0 || r >= N) return REF_BAD_ARG;
       rows.push_back(r);
     }
+#pragma omp parallel for schedule(static)
     for (int h = 0; h < Hq; ++h) {
       double* o = out + ((int64_t)b * Hq + h) * Dv;
       for (int v = 0; v < Dv; ++v) o[v] = 0.0;

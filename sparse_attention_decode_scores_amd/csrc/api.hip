@@ -428,7 +428,9 @@ dsa_status dsa_decode_step_timed(const int8_t* iq, const int8_t* iw, const int8_
   }
   uint8_t* w = static_cast<uint8_t*>(ws);
   const ChunkPlan cp = chunk_plan(nmax, k, B == 1, Di);
-  const bool have = cand_fits(Hi, Di, B, cp, true) && !(flags & DSA_FLAG_FORCE_FALLBACK);
+  // (the forced exhaustive path still gets the candidate score pass: it changes the
+  // selection only, and its narrowing takes a threshold from the union)
+  const bool have = cand_fits(Hi, Di, B, cp, true);
   // the one-row score pass also leaves per-chunk summaries for the selection
   const bool sums = have && B == 1;
   st = run_scores(iq, iw, ik, lens, B, Hi, Di, N, nmax, scores, have, cp,

@@ -62,6 +62,20 @@ __device__ __forceinline__ int32_t key_score(uint64_t key) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Global-memory views for code in a called (not inlined) function, which sees
+// generic pointers: accesses through them take the flat path, which is slower and
+// also counts against the LDS wait counter.
+typedef const __attribute__((address_space(1))) int32_t* GlobalI32;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef const __attribute__((address_space(1))) i32x4* GlobalI32x4;
+__device__ __forceinline__ GlobalI32 global_view(const int32_t* p) { return (GlobalI32)p; }
+// A 64-bit value known to be the same in every lane, in scalar registers.
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
 // Workgroup barrier for LDS communication only: waits for this wave's LDS
 // operations, not for its outstanding global loads and stores (a full
 // __syncthreads() also drains those, a memory round trip when stores are in

@@ -28,6 +28,8 @@
 //    grouping depends on nothing but the output order: both paths, and the
 //    stand-alone attention over the ordered indices, sum the same rows in the
 //    same groups and order, and their outputs are equal bit for bit.
+#include <type_traits>
+
 #include "attn_body.h"
 #include "chunk_select.h"
 #include "kernels.h"
@@ -42,7 +44,7 @@ constexpr int kSelWaves = kSelBlock / 64;
 constexpr int kUPerThread = kCandCap / kSelBlock;  // candidate keys held per thread
 constexpr int kSelPerThread = 4096 / kSelBlock;   // selected keys per thread (k <= 4096)
 // Ranking workgroups that take part on the exhaustive path (each streams the row).
-constexpr int kFallbackRankers = 16;
+constexpr int kFallbackRankers = 64;
 
 __global__ __launch_bounds__(kSelBlock) void k_chunk_cand(CandArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
@@ -81,6 +83,12 @@ constexpr int kBinPad = 16;       // LDS slots before the bin's keys (split_sort
 constexpr int kMaxWindow = 128;   // selected positions per attention split (at most ceil(4096 / 32))
 // keys gathered around an attention window: the bins of its two ends and the keys between
 constexpr int kMaxWindowList = 2 * (int)kMaxBinRank + kMaxWindow;
+// Exhaustive path: positions sampled for a threshold, and the keys at or above it that
+// the LDS list may hold (kept in the region the attention working set reuses).
+constexpr int kSampleMax = 16384;  // 32 per thread
+constexpr int kCandList = 8192;
+constexpr int kWaveCand = kCandList / kSelWaves;  // one segment per wave
+static_assert((kWaveCand & (kWaveCand - 1)) == 0, "segment slots wrap by masking");
 
 struct SelSmem {
   RadixSmem radix;
@@ -88,6 +96,7 @@ struct SelSmem {
   uint64_t mxw[kSelWaves];          // per wave: the best key a chunk left out
   uint32_t wcnt[kSelWaves][2];      // exhaustive compaction: per-wave counts above / at the threshold
   uint32_t gtw[kSelWaves];          // attention: per-wave counts of keys above the best dropped key
+  uint32_t ncand;                   // exhaustive path: keys at or above the sampled threshold
   uint64_t kstar;
   uint32_t tied;
   uint32_t winpos[kMaxWindow];      // attention: the window's positions, in output order
@@ -96,8 +105,13 @@ static_assert(kUPerThread == 16 && kSelBlock == 512, "cand_slot layout: 512 thre
 static_assert(kBinPad >= kUPerThread, "split_sorted: up <= keys per thread");
 
 // LDS the selection needs in the region that the attention working set reuses
-// afterwards: a list of bin or window keys (kBinPad before it) and the sink slots.
-constexpr size_t kRegionSelect = (size_t)(kBinPad + kMaxWindowList + kSelBlock + kUPerThread) * 8;
+// afterwards: a list of bin or window keys (kBinPad before it) and the sink slots,
+// or, on the exhaustive path, first the list of keys at or above the sampled
+// threshold (kCandList keys from the region's start).
+constexpr size_t kRegionSelect =
+    (size_t)(kBinPad + kMaxWindowList + kSelBlock + kUPerThread) * 8 > (size_t)kCandList * 8
+        ? (size_t)(kBinPad + kMaxWindowList + kSelBlock + kUPerThread) * 8
+        : (size_t)kCandList * 8;
 
 // Exchanges (sum, min, max, max64) over the block in one round.
 struct Stats4 {
@@ -127,8 +141,8 @@ __device__ __forceinline__ Stats4 block_stats(uint32_t sum, uint32_t lo, uint32_
 
 // Calls f(score_bits) for every score of row[0, n), 16 loads per thread in flight
 // (coalesced: load j of the block covers 512 consecutive scores).
-template <class F>
-__device__ __forceinline__ void for_each_score(const int32_t* __restrict__ row, int n, F f) {
+template <class Row, class F>
+__device__ __forceinline__ void for_each_score(Row row, int n, F f) {
   constexpr int U = 16;
   const int64_t tid = threadIdx.x;
   for (int64_t i0 = 0; i0 < n; i0 += (int64_t)kSelBlock * U) {
@@ -147,8 +161,8 @@ __device__ __forceinline__ void for_each_score(const int32_t* __restrict__ row, 
 // The same over positions [p0, p1) for one wave: f(score_bits, position, present)
 // is called for every lane of every 64-position row, in position order (one call
 // per row per lane, so that callers can use wave-wide ballots).
-template <class F>
-__device__ __forceinline__ void wave_rows(const int32_t* __restrict__ row, int64_t p0, int64_t p1, F f) {
+template <class Row, class F>
+__device__ __forceinline__ void wave_rows(Row row, int64_t p0, int64_t p1, F f) {
   constexpr int U = 16;
   const int lane = lane_id();
   for (int64_t q0 = p0; q0 < p1; q0 += 64 * U) {
@@ -164,65 +178,6 @@ __device__ __forceinline__ void wave_rows(const int32_t* __restrict__ row, int64
       f(score_bits(v[j]), p, p < p1);
     }
   }
-}
-
-// Exhaustive selection: the kk best keys of the row's n positions, written to sel
-// in position order; returns the kk-th best key and sets *tied to the number of
-// selected keys with its score. Streams the scores from memory: a pass for the
-// range, one radix pass per 11 bits of it, then a count and a write pass of an
-// ordered compaction in which wave w owns one contiguous eighth of the row.
-// (Out of line: the exhaustive path is rare, and inlined into the selection kernel
-// it made the candidate path's code larger and slower.)
-__device__ __noinline__ uint64_t select_row_exhaustive(const int32_t* __restrict__ row, int n, int kk,
-                                                       uint64_t* sel, uint32_t* tied, SelSmem& sm) {
-  uint32_t lo = 0xFFFFFFFFu, hi = 0;
-  for_each_score(row, n, [&](uint32_t u) {
-    lo = u < lo ? u : lo;
-    hi = u > hi ? u : hi;
-  });
-  const Stats4 st = block_stats(0, lo, hi, 0, sm);
-  auto each = [&](auto f) { for_each_score(row, n, f); };
-  uint32_t above;
-  const uint32_t T = block_select_range<kSelBlock>(each, st.lo, st.hi, kk, &above, sm.radix);
-  const uint32_t need_eq = (uint32_t)kk - above;
-  *tied = need_eq;
-  const int w = wave_id(), lane = lane_id();
-  const int64_t rows = ((int64_t)n + 63) / 64, rpw = (rows + kSelWaves - 1) / kSelWaves;
-  const int64_t p0 = (int64_t)w * rpw * 64 < n ? (int64_t)w * rpw * 64 : n;
-  const int64_t p1 = p0 + rpw * 64 < n ? p0 + rpw * 64 : n;
-  uint32_t gt = 0, eq = 0;
-  wave_rows(row, p0, p1, [&](uint32_t u, int64_t, bool in) {
-    gt += in && u > T ? 1u : 0u;
-    eq += in && u == T ? 1u : 0u;
-  });
-  gt = wave_sum_u32(gt);
-  eq = wave_sum_u32(eq);
-  if (lane == 0) {
-    sm.wcnt[w][0] = gt;
-    sm.wcnt[w][1] = eq;
-  }
-  lds_barrier();
-  uint32_t gb = 0, eb = 0;  // above / at T before this lane's position
-  for (int x = 0; x < w; ++x) {
-    gb += sm.wcnt[x][0];
-    eb += sm.wcnt[x][1];
-  }
-  const uint64_t lt = lanemask_lt();
-  wave_rows(row, p0, p1, [&](uint32_t u, int64_t p, bool in) {
-    const bool g = in && u > T, e = in && u == T;
-    const uint64_t bg = __ballot(g), be = __ballot(e);
-    const uint32_t gbl = gb + (uint32_t)__popcll(bg & lt), ebl = eb + (uint32_t)__popcll(be & lt);
-    if (g || (e && ebl < need_eq)) {
-      const uint32_t slot = gbl + (ebl < need_eq ? ebl : need_eq);
-      const uint64_t key = ((uint64_t)u << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)p);
-      sel[slot] = key;
-      if (e && ebl == need_eq - 1) sm.kstar = key;  // the last key taken at T is the kk-th best
-    }
-    gb += (uint32_t)__popcll(bg);
-    eb += (uint32_t)__popcll(be);
-  });
-  lds_barrier();
-  return sm.kstar;
 }
 
 // Splits the candidates held E per thread around the key range [klo, khi]: keys
@@ -372,6 +327,420 @@ struct KeyRange {
   uint32_t above, inbin;
 };
 
+// The kk best of the nvalid valid keys held E per thread (score bits sv in [lo, hi];
+// `sorted` when every thread's keys run best first): written to sel[0, kk) (the keys
+// above the kk-th key's radix range in input order, then the range's best in key
+// order); returns the kk-th best key and the number of selected keys with its score.
+// With publish_mx, the waves' largest dropped key (mx, one per thread) goes to
+// sm.mxw behind the narrowing, published by the last barrier. Every thread gets the
+// same results.
+struct TopK {
+  uint64_t kstar;
+  uint32_t tied;
+};
+template <int E>
+__device__ __forceinline__ TopK topk_of_keys(const uint64_t (&key)[E], const uint32_t (&sv)[E], uint32_t vmask,
+                                             uint32_t nvalid, uint32_t kk, uint32_t lo, uint32_t hi, bool sorted,
+                                             uint64_t* sel, uint64_t* list, uint64_t* sink, SelSmem& sm,
+                                             bool publish_mx, uint64_t mx) {
+  auto each = [&](auto f) {
+#pragma unroll
+    for (int j = 0; j < E; ++j)
+      if ((vmask >> j) & 1u) f(sv[j]);
+  };
+  // radix passes until the bin of the kk-th best key is small
+  const RadixBin rb = block_narrow<kSelBlock>(each, lo, hi, kk, nvalid, kMaxBinRank, sm.radix);
+  const uint64_t wmx = publish_mx ? wave_maxr_u64(mx) : 0ull;
+  // the key range that holds the kk-th best key: the keys above it are taken
+  uint64_t klo = (uint64_t)rb.binlo << 32, khi = ((uint64_t)rb.binhi << 32) | 0xFFFFFFFFull;
+  uint32_t above = rb.above, inbin = rb.inbin, tie_above = 0;
+  if (rb.inbin > kMaxBinRank) {  // uniform: one score value T holds that many keys
+    // the same narrowing over the low key words of the keys at T (a larger low word
+    // is an earlier position)
+    const uint32_t T = rb.binlo;
+    auto each_tie = [&](auto f) {
+#pragma unroll
+      for (int j = 0; j < E; ++j)
+        if (((vmask >> j) & 1u) && sv[j] == T) f((uint32_t)key[j]);
+    };
+    const RadixBin rt = block_narrow<kSelBlock>(each_tie, 0u, 0xFFFFFFFFu, kk - rb.above, rb.inbin, kMaxBinRank,
+                                                sm.radix);
+    klo = ((uint64_t)T << 32) | rt.binlo;
+    khi = ((uint64_t)T << 32) | rt.binhi;
+    above += rt.above;
+    inbin = rt.inbin;
+    tie_above = rt.above;
+  }
+  // the keys above the range are taken in input order, then the range's best in key
+  // order (equal scores: ascending positions)
+  if (sorted)  // uniform
+    split_sorted<E>(key, klo, khi, sel, list, sink, sm);
+  else
+    split_at_bin<E>(key, vmask, klo, khi, sel, list, sink, sm);
+  if (publish_mx && lane_id() == 0) sm.mxw[wave_id()] = wmx;
+  lds_barrier();
+  rank_bin(list, inbin, kk - above, sel + above, sm);
+  lds_barrier();
+  return TopK{sm.kstar, tie_above + sm.tied};
+}
+
+// The selection kernel's LDS: SelSmem | selected keys [k] | region, the attention
+// working set, which reuses what the selection keeps there (a list of bin or
+// window keys, then sink slots; or first the exhaustive path's key list). Taken
+// from the dynamic LDS symbol itself, also in the called functions below: pointers
+// passed to a called function are generic, and accesses through them take the
+// flat path.
+struct SelLds {
+  SelSmem* sm;
+  uint64_t* sel;
+  uint8_t* region;
+  uint64_t* list;  // bin or window keys
+  uint64_t* sink;
+};
+__device__ __forceinline__ SelLds sel_lds(int k) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  SelLds l;
+  l.sm = reinterpret_cast<SelSmem*>(smem);
+  l.sel = reinterpret_cast<uint64_t*>(smem + align16(sizeof(SelSmem)));
+  l.region = smem + align16(sizeof(SelSmem)) + align16((size_t)k * 8);
+  l.list = reinterpret_cast<uint64_t*>(l.region) + kBinPad;
+  l.sink = l.list + kMaxWindowList;
+  return l;
+}
+
+// The exhaustive path's narrowing (the "scans that narrow before a small sort"):
+//  1. a threshold T0 at or below the kk-th best score. With the candidate union at
+//     hand (cand_row, entries [0, C), at least kk valid), a value at or below the
+//     union's kk-th best score: the union's keys are row keys, so the row's kk-th
+//     best is at least that.
+//     Otherwise the rs-th best of up to kSampleMax sampled positions, rs chosen so
+//     that about 1.25 kk + 32 of the row's positions are expected at or above it;
+//  2. one streamed pass keeps every key scoring at least T0 in an LDS list (the
+//     region's first kCandList keys, one segment per wave; no atomics);
+//  3. when at least kk keys reached the list and all fitted, the list holds the top
+//     kk (the kk-th best scores at least T0). Returns that, with the list's keys in
+//     key/sv/vmask (thread (w, lane) holds slots [16 lane, 16 lane + 16) of wave w's
+//     segment) and their count in *total. The order of the list depends on the row
+//     alone (not on timing): the ranking workgroups each build it and split the
+//     selected keys by their place in it.
+// Otherwise (a sample far from the row's distribution, more than kCandList keys
+// tied at T0, or one wave's slices holding more than its segment) the caller falls
+// back to select_row_radix.
+__device__ __forceinline__ bool exhaustive_list(GlobalI32 row, const int32_t* row_in, int n, int kk,
+                                                const uint64_t* cand_row, int C, const SelLds& l,
+                                                uint64_t (&key)[kUPerThread], uint32_t (&sv)[kUPerThread],
+                                                uint32_t& vmask, uint32_t* total_out, uint32_t (&rng)[2]) {
+  SelSmem& sm = *l.sm;
+  uint64_t* const cand = reinterpret_cast<uint64_t*>(l.region);
+  const int tid = threadIdx.x;
+  const int w = wave_id(), lane = lane_id();
+  uint32_t t0bits;
+  bool from_union = false;
+  if (cand_row != nullptr) {  // uniform
+    // the union as the selection kernel holds it: thread t's entries [16t, 16t + 16),
+    // eight 16-byte pieces, piece j of all threads contiguous
+    typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
+    typedef const __attribute__((address_space(1))) u64x2* GlobalU64x2;
+    const GlobalU64x2 src = (GlobalU64x2)cand_row + tid;
+    uint64_t u[kUPerThread];
+#pragma unroll
+    for (int j = 0; j < kUPerThread / 2; ++j) {
+      const u64x2 v = src[(kCandCap / 16) * j];
+      u[2 * j] = v.x;
+      u[2 * j + 1] = v.y;
+    }
+    uint32_t cnt = 0, lo = 0xFFFFFFFFu, hi = 0;
+#pragma unroll
+    for (int j = 0; j < kUPerThread; ++j) {
+      const bool v = kUPerThread * tid + j < C && u[j] != 0ull;  // 0: no position
+      cnt += v ? 1u : 0u;
+      lo = v && key_ubits(u[j]) < lo ? key_ubits(u[j]) : lo;
+      hi = v && key_ubits(u[j]) > hi ? key_ubits(u[j]) : hi;
+    }
+    const Stats4 st = block_stats(cnt, lo, hi, 0, sm);
+    if (st.sum >= (uint32_t)kk) {  // uniform
+      auto each_u = [&](auto f) {
+#pragma unroll
+        for (int j = 0; j < kUPerThread; ++j)
+          if (kUPerThread * tid + j < C && u[j] != 0ull) f(key_ubits(u[j]));
+      };
+      // the low end of a radix bin of at most 64 union scores that holds the kk-th
+      // (one pass, mostly, instead of narrowing to the value itself)
+      t0bits = block_narrow<kSelBlock>(each_u, st.lo, st.hi, (uint32_t)kk, st.sum, 64u, sm.radix).binlo;
+      from_union = true;
+    }
+  }
+  if (!from_union) {  // uniform
+      // 1. the sampled threshold: all positions of a short row, else 256 evenly spaced
+      // runs of 64 (one coalesced load per wave and run)
+      constexpr int SP = kSampleMax / kSelBlock;
+      const bool whole = n <= kSampleMax;
+      const int ns = whole ? n : kSampleMax;
+      const uint64_t want = (uint64_t)kk * 5 / 4 + 32;
+      const uint32_t rs0 = (uint32_t)((want * (uint64_t)ns + (uint64_t)n - 1) / (uint64_t)n);
+      const uint32_t rs = rs0 < (uint32_t)ns ? (rs0 > 0 ? rs0 : 1u) : (uint32_t)ns;
+      int32_t sx[SP];
+  #pragma unroll
+      for (int j = 0; j < SP; ++j) {
+        const int i = tid + kSelBlock * j;
+        // run w + 8 j starts at its share of the row; runs never overlap (n > 16384)
+        const int64_t p = whole ? (i < n ? i : 0) : (int64_t)(w + kSelWaves * j) * n / (kSampleMax / 64) + lane;
+        sx[j] = row[p];
+      }
+      uint32_t lo = 0xFFFFFFFFu, hi = 0;
+  #pragma unroll
+      for (int j = 0; j < SP; ++j)
+        if (!whole || tid + kSelBlock * j < n) {
+          const uint32_t u = score_bits(sx[j]);
+          lo = u < lo ? u : lo;
+          hi = u > hi ? u : hi;
+        }
+      const Stats4 st = block_stats(0, lo, hi, 0, sm);
+      auto each_s = [&](auto f) {
+  #pragma unroll
+        for (int j = 0; j < SP; ++j)
+          if (!whole || tid + kSelBlock * j < n) f(score_bits(sx[j]));
+      };
+      // T0: the low end of a radix bin of at most 16 sampled values that holds the
+      // rs-th best (every sampled value of the bin passes, a few more than rs)
+      const RadixBin tb = block_narrow<kSelBlock>(each_s, st.lo, st.hi, rs, (uint32_t)ns, 16u, sm.radix);
+      t0bits = tb.binlo;
+  }
+  const int32_t T0 = (int32_t)(t0bits ^ 0x80000000u);  // as a score
+    // 2. every key scoring at least T0 into the list. Wave w appends to its own
+    // segment, in the order of its loads, so that the list's order is the same in
+    // every workgroup that builds it (the ranking workgroups split the selected keys
+    // by their place in it). The positions before the row's first 16-byte boundary
+    // go to wave 0 first; then 16-byte loads, thread t's load j of a pass covering
+    // positions h + 4 (q0 + t + 512 j) + [0, 4).
+    const uint64_t lt = lanemask_lt();
+    uint64_t* const wseg = cand + w * kWaveCand;
+    // a kept key as stored: make_key without its sign flip (one instruction less per
+    // append; undone when the list is read)
+    auto raw_key = [](int32_t x, uint32_t pos) {
+      return ((uint64_t)(uint32_t)x << 32) | (uint64_t)(0xFFFFFFFFu - pos);
+    };
+    uint32_t wn = 0;  // keys this wave kept (uniform)
+    int32_t kmax = INT32_MIN;  // the best score this lane kept
+    const int h0 = (int)(((16u - ((uint32_t)reinterpret_cast<uintptr_t>(row_in) & 15u)) & 15u) >> 2);
+    const int h = h0 < n ? h0 : n;
+    if (w == 0 && h > 0) {  // uniform
+      int32_t x = 0;
+      if (lane < h) x = row[lane];
+      const bool keep = lane < h && x >= T0;
+      const uint64_t bal = __ballot(keep);
+      if (keep) {
+        wseg[__popcll(bal & lt)] = raw_key(x, (uint32_t)lane);
+        kmax = x;
+      }
+      wn = (uint32_t)__popcll(bal);
+    }
+    const int64_t m = (int64_t)n - h;  // positions from the boundary on
+    const int64_t nq = (m + 3) / 4;    // 16-byte vectors holding them (each holds one)
+    const GlobalI32x4 vrow = reinterpret_cast<GlobalI32x4>(row + h);
+    constexpr int U = 16;
+    constexpr int64_t step = (int64_t)kSelBlock * U;  // vectors per pass
+    // keeps the keys of vector v of pass q0 (load j of the pass)
+    auto keep_vec = [&](const i32x4& v, int64_t q0, int j, auto full) {
+      const int64_t q = q0 + tid + (int64_t)kSelBlock * j;
+      const int32_t x4[4] = {v.x, v.y, v.z, v.w};
+      // the four compares first and one branch on them all (a branch right behind
+      // each compare waits for it)
+      bool keep[4];
+      uint64_t bal[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        keep[e] = x4[e] >= T0 && (decltype(full)::value || 4 * q + e < m);
+        bal[e] = __ballot(keep[e]);
+      }
+      if ((bal[0] | bal[1] | bal[2] | bal[3]) == 0) return;  // uniform
+      const uint32_t p0 = (uint32_t)(h + 4 * q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (bal[e] != 0) {  // uniform
+          // the slot wraps within the segment: a wave that keeps more than it
+          // holds makes the list unusable, which the count below detects
+          const uint32_t at = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal[e] >> 32),
+                                                        __builtin_amdgcn_mbcnt_lo((uint32_t)bal[e], wn)) &
+                              (uint32_t)(kWaveCand - 1);
+          if (keep[e]) {
+            // raw_key as two words (no register pair to assemble)
+            uint32_t* const slot = reinterpret_cast<uint32_t*>(wseg + at);
+            slot[0] = 0xFFFFFFFFu - (p0 + (uint32_t)e);
+            slot[1] = (uint32_t)x4[e];
+            kmax = x4[e] > kmax ? x4[e] : kmax;
+          }
+          wn += (uint32_t)__popcll(bal[e]);
+        }
+      }
+    };
+    // passes whose vectors all lie inside the row: as soon as load j of a pass is
+    // used, the same slot loads its vector of the next pass, so U loads stay in
+    // flight while keys are kept (the last pass's follow-up loads repeat that pass
+    // rather than branch around the loads)
+    const int64_t nfull = (m / 4) / step;
+    if (nfull > 0) {  // uniform
+      i32x4 v[U];
+      // (issued in slot order: the waits below count on it)
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        v[j] = vrow[tid + (int64_t)kSelBlock * j];
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      for (int64_t p = 0; p < nfull; ++p) {
+        const int64_t q0 = p * step;
+        const GlobalI32x4 next = vrow + (p + 1 < nfull ? p + 1 : p) * step + tid;
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+          keep_vec(v[j], q0, j, std::true_type{});
+          v[j] = next[kSelBlock * j];
+        }
+      }
+    }
+    if (nfull * step < nq) {  // uniform: the rest, masked at the row's end
+      const int64_t q0 = nfull * step;
+      i32x4 v[U];
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        const int64_t q = q0 + tid + (int64_t)kSelBlock * j;
+        v[j] = vrow[q < nq ? q : nq - 1];  // a vector past the row's end is not read
+      }
+#pragma unroll
+      for (int j = 0; j < U; ++j) keep_vec(v[j], q0, j, std::false_type{});
+    }
+  // per wave: keys kept and the best kept score; the list's score range is then
+  // [T0, the best of those] (bounds suffice for the narrowing: no exchange of the
+  // keys' own range)
+  const uint32_t whi = wave_maxr_u32(score_bits(kmax));
+  if (lane == 0) {
+    sm.wcnt[w][0] = wn;
+    sm.wcnt[w][1] = whi;
+  }
+  lds_barrier();
+  uint32_t total = 0, fits = 1, mine = 0, hi = 0;
+#pragma unroll
+  for (int x = 0; x < kSelWaves; ++x) {
+    const uint32_t c = sm.wcnt[x][0];
+    total += c;
+    fits &= c <= (uint32_t)kWaveCand ? 1u : 0u;
+    mine = x == w ? c : mine;
+    hi = sm.wcnt[x][1] > hi ? sm.wcnt[x][1] : hi;
+  }
+  if (!fits || total < (uint32_t)kk) return false;  // uniform
+  rng[0] = t0bits;
+  rng[1] = hi;
+  vmask = 0;
+#pragma unroll
+  for (int j = 0; j < kUPerThread; ++j) {
+    const uint32_t i = (uint32_t)(kUPerThread * lane + j);
+    key[j] = i < mine ? wseg[i] ^ (1ull << 63) : 0ull;  // raw_key -> make_key
+    sv[j] = key_ubits(key[j]);
+    vmask |= i < mine ? 1u << j : 0u;
+  }
+  *total_out = total;
+  // every thread has read its keys before any writes the region again (the list
+  // and sink slots that the narrowing uses lie over the kept keys)
+  lds_barrier();
+  return true;
+}
+
+// The exhaustive path's last resort: a radix selection over every position (a pass
+// for the range, one radix pass per 11 bits of it), then a count and a write pass
+// of an ordered compaction in which wave w owns one contiguous eighth of the row.
+// Writes the kk best keys to sel in position order; returns the kk-th best key and
+// sets *tied to the number of selected keys with its score.
+__device__ __noinline__ uint64_t select_row_radix(const int32_t* __restrict__ row_in, int n, int kk, int k,
+                                                  uint32_t* tied) {
+  n = __builtin_amdgcn_readfirstlane(n);
+  kk = __builtin_amdgcn_readfirstlane(kk);
+  k = __builtin_amdgcn_readfirstlane(k);
+  const GlobalI32 row = global_view(
+      reinterpret_cast<const int32_t*>(uniform_u64(reinterpret_cast<uint64_t>(row_in))));
+  const SelLds l = sel_lds(k);
+  SelSmem& sm = *l.sm;
+  uint64_t* const sel = l.sel;
+  uint32_t lo = 0xFFFFFFFFu, hi = 0;
+  for_each_score(row, n, [&](uint32_t u) {
+    lo = u < lo ? u : lo;
+    hi = u > hi ? u : hi;
+  });
+  const Stats4 st = block_stats(0, lo, hi, 0, sm);
+  auto each = [&](auto f) { for_each_score(row, n, f); };
+  uint32_t above;
+  const uint32_t T = block_select_range<kSelBlock>(each, st.lo, st.hi, kk, &above, sm.radix);
+  const uint32_t need_eq = (uint32_t)kk - above;
+  *tied = need_eq;
+  const int w = wave_id(), lane = lane_id();
+  const int64_t rows = ((int64_t)n + 63) / 64, rpw = (rows + kSelWaves - 1) / kSelWaves;
+  const int64_t p0 = (int64_t)w * rpw * 64 < n ? (int64_t)w * rpw * 64 : n;
+  const int64_t p1 = p0 + rpw * 64 < n ? p0 + rpw * 64 : n;
+  uint32_t gt = 0, eq = 0;
+  wave_rows(row, p0, p1, [&](uint32_t u, int64_t, bool in) {
+    gt += in && u > T ? 1u : 0u;
+    eq += in && u == T ? 1u : 0u;
+  });
+  gt = wave_sum_u32(gt);
+  eq = wave_sum_u32(eq);
+  if (lane == 0) {
+    sm.wcnt[w][0] = gt;
+    sm.wcnt[w][1] = eq;
+  }
+  lds_barrier();
+  uint32_t gb = 0, eb = 0;  // above / at T before this lane's position
+  for (int x = 0; x < w; ++x) {
+    gb += sm.wcnt[x][0];
+    eb += sm.wcnt[x][1];
+  }
+  const uint64_t lt = lanemask_lt();
+  wave_rows(row, p0, p1, [&](uint32_t u, int64_t p, bool in) {
+    const bool g = in && u > T, e = in && u == T;
+    const uint64_t bg = __ballot(g), be = __ballot(e);
+    const uint32_t gbl = gb + (uint32_t)__popcll(bg & lt), ebl = eb + (uint32_t)__popcll(be & lt);
+    if (g || (e && ebl < need_eq)) {
+      const uint32_t slot = gbl + (ebl < need_eq ? ebl : need_eq);
+      const uint64_t key = ((uint64_t)u << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)p);
+      sel[slot] = key;
+      if (e && ebl == need_eq - 1) sm.kstar = key;  // the last key taken at T is the kk-th best
+    }
+    gb += (uint32_t)__popcll(bg);
+    eb += (uint32_t)__popcll(be);
+  });
+  lds_barrier();
+  return sm.kstar;
+}
+
+
+// Exhaustive selection: the kk best keys of the row's n positions, written to sel
+// (in an order that depends on the row alone); returns the kk-th best key and sets
+// *tied to the number of selected keys with its score. The narrowed list of
+// exhaustive_list, then the same exact top kk as on the candidate path; the radix
+// selection when the list does not hold the top kk.
+// Called functions get their arguments in vector registers and see generic
+// pointers: the uniform arguments are moved back to scalar registers (or the row
+// pass does its address and loop arithmetic per lane), the row's address space is
+// named, and the LDS comes from its symbol. (Out of line: the exhaustive path is
+// rare, and inlined into the selection kernel it made the candidate path's code
+// larger and slower.)
+__device__ __noinline__ uint64_t select_row_exhaustive(const int32_t* __restrict__ row_in, int n, int kk, int k,
+                                                       const uint64_t* cand_row, int C, uint32_t* tied) {
+  n = __builtin_amdgcn_readfirstlane(n);
+  kk = __builtin_amdgcn_readfirstlane(kk);
+  k = __builtin_amdgcn_readfirstlane(k);
+  C = __builtin_amdgcn_readfirstlane(C);
+  row_in = reinterpret_cast<const int32_t*>(uniform_u64(reinterpret_cast<uint64_t>(row_in)));
+  cand_row = reinterpret_cast<const uint64_t*>(uniform_u64(reinterpret_cast<uint64_t>(cand_row)));
+  const SelLds l = sel_lds(k);
+  uint64_t key[kUPerThread];
+  uint32_t sv[kUPerThread], vmask = 0, total = 0, rng[2];
+  if (kk > 0 && exhaustive_list(global_view(row_in), row_in, n, kk, cand_row, C, l, key, sv, vmask, &total, rng)) {
+    const TopK t = topk_of_keys<kUPerThread>(key, sv, vmask, total, (uint32_t)kk, rng[0], rng[1], false, l.sel,
+                                             l.list, l.sink, *l.sm, false, 0ull);
+    *tied = t.tied;
+    return t.kstar;
+  }
+  return select_row_radix(row_in, n, kk, k, tied);
+}
+
 // Completes the narrowing of one sought key (the need-th largest of the keys held
 // E per thread; rb from block_narrow_first) until its range holds at most
 // kMaxBinRank keys: further passes over the scores, then, when one score value T
@@ -508,34 +877,45 @@ __device__ __forceinline__ uint32_t window_positions(const uint64_t (&key)[E], c
   return gt;
 }
 
-// The attention window on the exhaustive path: the kk best keys of the row by the
-// exhaustive selection (into sel), then the window narrowing over them, 16 per thread.
-// Out of line, so that loads in flight on the candidate path are not waited for
-// where its code would otherwise join this path's.
-__device__ __noinline__ void exhaustive_window(const int32_t* __restrict__ row, int n, int kk, uint64_t* sel,
-                                               const uint64_t* xc, int G, uint32_t r0, uint32_t r1, uint64_t* wl,
-                                               uint64_t* sink, SelSmem& sm) {
-  uint32_t tied;
-  select_row_exhaustive(row, n, kk, sel, &tied, sm);
+// The attention window on the exhaustive path: the window narrowing over the list
+// of exhaustive_list (its ranks are the row's for the top kk), or over the kk keys
+// of the radix selection. (Out of line, so that loads in flight on the candidate
+// path are not waited for where its code would otherwise join this path's; uniform
+// arguments back in scalar registers as in select_row_exhaustive.)
+__device__ __noinline__ void exhaustive_window(const int32_t* __restrict__ row_in, int n, int kk, int k,
+                                               const uint64_t* cand_row, int C, uint32_t r0, uint32_t r1) {
+  n = __builtin_amdgcn_readfirstlane(n);
+  kk = __builtin_amdgcn_readfirstlane(kk);
+  k = __builtin_amdgcn_readfirstlane(k);
+  C = __builtin_amdgcn_readfirstlane(C);
+  r0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)r0);
+  r1 = (uint32_t)__builtin_amdgcn_readfirstlane((int)r1);
+  row_in = reinterpret_cast<const int32_t*>(uniform_u64(reinterpret_cast<uint64_t>(row_in)));
+  cand_row = reinterpret_cast<const uint64_t*>(uniform_u64(reinterpret_cast<uint64_t>(cand_row)));
+  const SelLds l = sel_lds(k);
+  SelSmem& sm = *l.sm;
   uint64_t key[kUPerThread];
-  uint32_t sv[kUPerThread], vmask = 0;
+  uint32_t sv[kUPerThread], vmask = 0, total = 0, rng[2];
+  if (!exhaustive_list(global_view(row_in), row_in, n, kk, cand_row, C, l, key, sv, vmask, &total, rng)) {
+    uint32_t tied;
+    select_row_radix(row_in, n, kk, k, &tied);
+    vmask = 0;
 #pragma unroll
-  for (int j = 0; j < kUPerThread; ++j) {
-    const int i = kUPerThread * (int)threadIdx.x + j;
-    key[j] = i < kk ? sel[i] : 0ull;
-    sv[j] = key_ubits(key[j]);
-    vmask |= i < kk ? 1u << j : 0u;
+    for (int j = 0; j < kUPerThread; ++j) {
+      const int i = kUPerThread * (int)threadIdx.x + j;
+      key[j] = i < kk ? l.sel[i] : 0ull;
+      sv[j] = key_ubits(key[j]);
+      vmask |= i < kk ? 1u << j : 0u;
+    }
+    total = (uint32_t)kk;
+    bool sorted;
+    union_range_exchange<kUPerThread>(key, sv, vmask, sm, rng, &sorted);
   }
-  uint32_t rng[2];
-  bool sorted;
-  union_range_exchange<kUPerThread>(key, sv, vmask, sm, rng, &sorted);
-  window_positions<kUPerThread>(key, sv, vmask, (uint32_t)kk, rng[0], rng[1], false, false, xc, G, r0, r1, wl, sink,
-                                sm);
+  window_positions<kUPerThread>(key, sv, vmask, total, rng[0], rng[1], false, false, nullptr, 0, r0, r1, l.list,
+                                l.sink, sm);
 }
 
-// LDS: SelSmem | selected keys [k] | region: the attention working set, which
-// reuses what the selection keeps there (a list of bin or window keys, then sink
-// slots).
+// LDS as laid out by sel_lds.
 // The arguments that the first requests need come first, as separate scalars: the
 // leading arguments can be preloaded into scalar registers at wave launch, so the
 // candidate, dropped-key, summary and query requests need not wait for a read of the
@@ -546,12 +926,12 @@ __global__ __launch_bounds__(kSelBlock) void k_select(const uint64_t* __restrict
                                                       const uint64_t* __restrict__ xc,
                                                       const ChunkSum* __restrict__ sums, const void* __restrict__ q,
                                                       int G, int Hq, int Dk, int S, SelArgs a, AttnArgs at) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  SelSmem& sm = *reinterpret_cast<SelSmem*>(smem);
-  uint64_t* sel = reinterpret_cast<uint64_t*>(smem + align16(sizeof(SelSmem)));
-  uint8_t* region = smem + align16(sizeof(SelSmem)) + align16((size_t)a.k * 8);
-  uint64_t* list = reinterpret_cast<uint64_t*>(region) + kBinPad;  // bin or window keys
-  uint64_t* sink = list + kMaxWindowList;
+  const SelLds lds = sel_lds(a.k);
+  SelSmem& sm = *lds.sm;
+  uint64_t* sel = lds.sel;
+  uint8_t* region = lds.region;
+  uint64_t* list = lds.list;  // bin or window keys
+  uint64_t* sink = lds.sink;
   const int tid = threadIdx.x;
   const int b = blockIdx.y;
   const bool attn_role = (int)blockIdx.x < S;
@@ -654,8 +1034,8 @@ __global__ __launch_bounds__(kSelBlock) void k_select(const uint64_t* __restrict
       if (above_mx < (uint32_t)kk) reason = 2;
     }
     if (cnt > 0 && reason != 0)  // uniform
-      exhaustive_window(row, n, kk, sel, xc + (int64_t)b * G, G, (uint32_t)r0, (uint32_t)(r0 + cnt - 1), list, sink,
-                        sm);
+      exhaustive_window(row, n, kk, a.k, have_cand ? cand + (int64_t)b * kCandCap : nullptr, G * a.m, (uint32_t)r0,
+                        (uint32_t)(r0 + cnt - 1));
     // sm.winpos is complete and published (the last barrier of the window
     // narrowing follows its last write), and the LDS region is free again
     Attn::run(at, b, blockIdx.x, [&](int i) { return (int64_t)sm.winpos[i]; }, cnt, region, qf);
@@ -682,46 +1062,11 @@ __global__ __launch_bounds__(kSelBlock) void k_select(const uint64_t* __restrict
     }
     const uint32_t kku = (uint32_t)kk;  // <= nvalid here
     const uint64_t mx = tid < G ? xc[(int64_t)b * G + tid] : 0ull;  // waited for behind the narrowing
-    auto each = [&](auto f) {
-#pragma unroll
-      for (int j = 0; j < kUPerThread; ++j)
-        if ((vmask >> j) & 1u) f(sv[j]);
-    };
-    // radix passes until the bin of the kk-th best key is small
-    const RadixBin rb = block_narrow<kSelBlock>(each, rng[0], rng[1], kku, nvalid, kMaxBinRank, sm.radix);
-    const uint64_t wmx = wave_maxr_u64(mx);
-    // the key range that holds the kk-th best key: the keys above it are taken
-    uint64_t klo = (uint64_t)rb.binlo << 32, khi = ((uint64_t)rb.binhi << 32) | 0xFFFFFFFFull;
-    uint32_t above = rb.above, inbin = rb.inbin, tie_above = 0;
-    if (rb.inbin > kMaxBinRank) {  // uniform: one score value T holds that many keys
-      // the same narrowing over the low key words of the keys at T (a larger low
-      // word is an earlier position)
-      const uint32_t T = rb.binlo;
-      auto each_tie = [&](auto f) {
-#pragma unroll
-        for (int j = 0; j < kUPerThread; ++j)
-          if (((vmask >> j) & 1u) && sv[j] == T) f((uint32_t)key[j]);
-      };
-      const RadixBin rt =
-          block_narrow<kSelBlock>(each_tie, 0u, 0xFFFFFFFFu, kku - rb.above, rb.inbin, kMaxBinRank, sm.radix);
-      klo = ((uint64_t)T << 32) | rt.binlo;
-      khi = ((uint64_t)T << 32) | rt.binhi;
-      above += rt.above;
-      inbin = rt.inbin;
-      tie_above = rt.above;
-    }
-    // the keys above the range are taken in union order, then the range's best in
-    // key order (equal scores: ascending positions)
-    if (sorted)  // uniform
-      split_sorted<kUPerThread>(key, klo, khi, sel, list, sink, sm);
-    else
-      split_at_bin<kUPerThread>(key, vmask, klo, khi, sel, list, sink, sm);
-    if (lane_id() == 0) sm.mxw[wave_id()] = wmx;
-    lds_barrier();
-    rank_bin(list, inbin, kku - above, sel + above, sm);
-    lds_barrier();
-    const uint32_t tie = tie_above + sm.tied;
-    kstar = sm.kstar;
+    // the keys above the kk-th key's range in union order, then the range's best in
+    // key order
+    const TopK t = topk_of_keys<kUPerThread>(key, sv, vmask, nvalid, kku, rng[0], rng[1], sorted, sel, list, sink, sm,
+                                             true, mx);
+    kstar = t.kstar;
     uint64_t mxall = 0;
 #pragma unroll
     for (int w = 0; w < kSelWaves; ++w) mxall = sm.mxw[w] > mxall ? sm.mxw[w] : mxall;
@@ -729,7 +1074,7 @@ __global__ __launch_bounds__(kSelBlock) void k_select(const uint64_t* __restrict
     const bool ok = mxall < kstar && (nvalid >= (uint32_t)a.k || mxall == 0);
     if (ok) {
       nsel = kku;
-      tied = tie;
+      tied = t.tied;
     } else {
       reason = 2;
     }
@@ -740,7 +1085,8 @@ __global__ __launch_bounds__(kSelBlock) void k_select(const uint64_t* __restrict
   const int r = (int)blockIdx.x - S;
   if (r >= R) return;  // uniform
   if (reason != 0) {
-    kstar = select_row_exhaustive(row, n, kk, sel, &tied, sm);
+    kstar = select_row_exhaustive(row, n, kk, a.k, have_cand ? cand + (int64_t)b * kCandCap : nullptr, G * a.m,
+                                  &tied);
     nsel = (uint32_t)kk;
   }
 

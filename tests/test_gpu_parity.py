@@ -269,6 +269,31 @@ def test_topk_heavy_ties_and_short_rows(torch, dsa):
             assert np.array_equal(idx.cpu().numpy(), ref), (N, k, span, flags)
 
 
+def test_topk_exhaustive_list_falls_back(torch, dsa):
+    """Rows whose narrowed list cannot hold the top k on the exhaustive path, which then
+    takes the radix selection over every position: (a) the best keys all in wave 0's
+    64-position slices (positions p with p % 512 < 64), more than its list segment
+    holds; (b) the best scores exactly at the sampled runs of 64 (run r from
+    r * n // 256), so the sampled threshold lies above the k-th best score."""
+    rng = np.random.default_rng(91)
+    N = 40000
+    s = rng.integers(-1000, 1000, size=(1, N)).astype(np.int32)
+    hot = (np.arange(N) % 512) < 64
+    s[0, hot] = rng.integers(10 ** 6, 2 * 10 ** 6, size=int(hot.sum()))
+    N2 = 300000
+    s2 = rng.integers(0, 1000, size=(1, N2)).astype(np.int32)
+    runs = (np.arange(256)[:, None] * N2 // 256 + np.arange(64)[None, :]).ravel()
+    s2[0, runs] = rng.integers(10 ** 6, 2 * 10 ** 6, size=runs.size)
+    for scores, k in ((s, 2048), (s2, 2048), (s2, 4096)):
+        ctx = np.array([scores.shape[1]], np.int32)
+        ref = oracle.topk_select(scores, ctx, k)
+        note("topk list fallback N=%d k=%d" % (scores.shape[1], k))
+        for flags in (0, 1):
+            idx = dsa.dsa_topk_select(torch.from_numpy(scores).cuda(), ctx, k, flags=flags)
+            torch.cuda.synchronize()
+            assert np.array_equal(idx.cpu().numpy(), ref), (scores.shape[1], k, flags)
+
+
 def test_sparse_attn_standalone_with_skipped_entries(torch, dsa):
     c, (rs, ri, ro) = case("ctx16k")
     d = dev_inputs(torch, c)

@@ -266,3 +266,16 @@ def test_workload_generator_is_deterministic():
     for key in ("iq", "iw", "ik", "q", "kv", "ctx_len"):
         assert (a[key] == b[key]).all()
     assert inputs.ctx_lengths("verify8_ctx131k").tolist() == [131065 + r for r in range(8)]
+
+
+def test_openmp_build_gives_identical_results():
+    # the all-core build (same source, -fopenmp) splits independent loops only
+    c = inputs.random_case(31, B=2, N=6000, k=512, Hi=16, Di=64, Hq=6, Dk=96, Dv=64, ctx_len=[6000, 3333])
+    args = (c["iq"], c["iw"], c["ik"], c["q"], c["kv"], c["ctx_len"], c["k"], c["Dv"], c["scale"])
+    a = oracle.decode_step(*args)
+    b = oracle.decode_step(*args, omp=True)
+    for x, y in zip(a, b):
+        assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
+    with pytest.raises(ValueError):  # 64 heads x 128 dims of 127s overflow int32
+        oracle.index_scores(np.full((1, 64, 128), 127, np.int8), np.full((1, 64), 127, np.int8),
+                            np.full((10, 128), 127, np.int8), np.array([10], np.int32), omp=True)
