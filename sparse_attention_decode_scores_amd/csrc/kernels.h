@@ -130,6 +130,7 @@ struct SelArgs {
   int64_t N;
   int k;
   int G, m;            // candidate layout
+  int P, ilv;          // chunk geometry of the candidate pass (row_chunk_units)
   int have_cand;       // 0: the candidate pass did not run (chunks too long)
   RowLens cand_valid;  // per row: union entries that hold a candidate (the rest are 0)
   int force;           // DSA_FLAG_FORCE_FALLBACK

@@ -88,7 +88,10 @@ constexpr int kMaxWindowList = 2 * (int)kMaxBinRank + kMaxWindow;
 constexpr int kSampleMax = 16384;  // 32 per thread
 constexpr int kCandList = 8192;
 constexpr int kWaveCand = kCandList / kSelWaves;  // one segment per wave
-static_assert((kWaveCand & (kWaveCand - 1)) == 0, "segment slots wrap by masking");
+// Keys a segment may take: an append starts at the wave's count capped here, and
+// one append adds at most 64, so every store stays inside the segment; a wave that
+// keeps more makes the list unusable, which the final count detects.
+constexpr int kWaveCap = kWaveCand - 64;
 
 struct SelSmem {
   RadixSmem radix;
@@ -96,7 +99,7 @@ struct SelSmem {
   uint64_t mxw[kSelWaves];          // per wave: the best key a chunk left out
   uint32_t wcnt[kSelWaves][2];      // exhaustive compaction: per-wave counts above / at the threshold
   uint32_t gtw[kSelWaves];          // attention: per-wave counts of keys above the best dropped key
-  uint32_t ncand;                   // exhaustive path: keys at or above the sampled threshold
+  uint64_t hotm[kMaxChunks / 64];   // exhaustive path: chunks whose best dropped key reaches T0
   uint64_t kstar;
   uint32_t tied;
   uint32_t winpos[kMaxWindow];      // attention: the window's positions, in output order
@@ -410,39 +413,75 @@ __device__ __forceinline__ SelLds sel_lds(int k) {
 
 // The exhaustive path's narrowing (the "scans that narrow before a small sort"):
 //  1. a threshold T0 at or below the kk-th best score. With the candidate union at
-//     hand (cand_row, entries [0, C), at least kk valid), a value at or below the
+//     hand (cand_row, entries [0, G m), at least kk valid), a value at or below the
 //     union's kk-th best score: the union's keys are row keys, so the row's kk-th
-//     best is at least that.
-//     Otherwise the rs-th best of up to kSampleMax sampled positions, rs chosen so
-//     that about 1.25 kk + 32 of the row's positions are expected at or above it;
-//  2. one streamed pass keeps every key scoring at least T0 in an LDS list (the
-//     region's first kCandList keys, one segment per wave; no atomics);
+//     best is at least that. Otherwise the rs-th best of up to kSampleMax sampled
+//     positions, rs chosen so that about 1.25 kk + 32 of the row's positions are
+//     expected at or above it;
+//  2. every key of the row scoring at least T0 into an LDS list (the region's first
+//     kCandList keys, one segment per wave; no atomics). With the union, a chunk
+//     whose best dropped key (xc_row) scores below T0 has no key at or above T0
+//     outside the union: the list takes the union's keys at or above T0 from those
+//     chunks and rescans only the others, at most kMaxHotChunks of them. Otherwise
+//     one streamed pass over the whole row;
 //  3. when at least kk keys reached the list and all fitted, the list holds the top
 //     kk (the kk-th best scores at least T0). Returns that, with the list's keys in
 //     key/sv/vmask (thread (w, lane) holds slots [16 lane, 16 lane + 16) of wave w's
-//     segment) and their count in *total. The order of the list depends on the row
-//     alone (not on timing): the ranking workgroups each build it and split the
-//     selected keys by their place in it.
-// Otherwise (a sample far from the row's distribution, more than kCandList keys
-// tied at T0, or one wave's slices holding more than its segment) the caller falls
-// back to select_row_radix.
+//     segment), their count in *total and their score range in rng. The order of
+//     the list depends on the row alone (not on timing): the ranking workgroups each
+//     build it and split the selected keys by their place in it.
+// Otherwise (a sample far from the row's distribution, more than the list holds at
+// or above T0, or one wave's share beyond its segment) the caller falls back to
+// select_row_radix.
+constexpr int kMaxHotChunks = 32;
+// The candidate pass's chunks (row_chunk_units): G chunks of P positions keeping m
+// candidates each; ilv: interleaved 32-position units.
+struct ChunkGeom {
+  int G, m, P, ilv;
+};
+__device__ __forceinline__ ChunkGeom uniform_geom(ChunkGeom g) {
+  return ChunkGeom{__builtin_amdgcn_readfirstlane(g.G), __builtin_amdgcn_readfirstlane(g.m),
+                   __builtin_amdgcn_readfirstlane(g.P), __builtin_amdgcn_readfirstlane(g.ilv)};
+}
 __device__ __forceinline__ bool exhaustive_list(GlobalI32 row, const int32_t* row_in, int n, int kk,
-                                                const uint64_t* cand_row, int C, const SelLds& l,
-                                                uint64_t (&key)[kUPerThread], uint32_t (&sv)[kUPerThread],
-                                                uint32_t& vmask, uint32_t* total_out, uint32_t (&rng)[2]) {
+                                                const uint64_t* cand_row, const uint64_t* xc_row, int G, int cm,
+                                                int P, int ilv, const SelLds& l, uint64_t (&key)[kUPerThread],
+                                                uint32_t (&sv)[kUPerThread], uint32_t& vmask, uint32_t* total_out,
+                                                uint32_t (&rng)[2]) {
   SelSmem& sm = *l.sm;
-  uint64_t* const cand = reinterpret_cast<uint64_t*>(l.region);
   const int tid = threadIdx.x;
   const int w = wave_id(), lane = lane_id();
-  uint32_t t0bits;
+  const uint64_t lt = lanemask_lt();
+  // wave w's list segment; a kept key as stored: make_key without its sign flip
+  // (undone when the list is read)
+  uint64_t* const wseg = reinterpret_cast<uint64_t*>(l.region) + w * kWaveCand;
+  uint32_t* const seg32 = reinterpret_cast<uint32_t*>(wseg);
+  uint32_t wn = 0;  // keys this wave kept (uniform)
+  // appends the keys of this wave's lanes for which keep holds (score x at
+  // position pos): slot = the wave's count so far (capped) + the lane's rank among
+  // the kept lanes; the key as two words
+  auto append = [&](bool keep, int32_t x, uint32_t pos) {
+    const uint64_t bal = __ballot(keep);
+    if (keep) {
+      const uint32_t r = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+      uint32_t* const slot = seg32 + 2 * ((wn < (uint32_t)kWaveCap ? wn : (uint32_t)kWaveCap) + r);
+      slot[0] = 0xFFFFFFFFu - pos;
+      slot[1] = (uint32_t)x;
+    }
+    wn += (uint32_t)__popcll(bal);
+  };
+
+  // 1. the threshold
+  uint32_t t0bits = 0;
   bool from_union = false;
+  uint64_t u[kUPerThread];  // the union as the selection kernel holds it
+  uint32_t uvalid = 0;
   if (cand_row != nullptr) {  // uniform
-    // the union as the selection kernel holds it: thread t's entries [16t, 16t + 16),
-    // eight 16-byte pieces, piece j of all threads contiguous
+    // thread t's entries [16t, 16t + 16), eight 16-byte pieces, piece j of all
+    // threads contiguous
     typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
     typedef const __attribute__((address_space(1))) u64x2* GlobalU64x2;
     const GlobalU64x2 src = (GlobalU64x2)cand_row + tid;
-    uint64_t u[kUPerThread];
 #pragma unroll
     for (int j = 0; j < kUPerThread / 2; ++j) {
       const u64x2 v = src[(kCandCap / 16) * j];
@@ -452,7 +491,8 @@ __device__ __forceinline__ bool exhaustive_list(GlobalI32 row, const int32_t* ro
     uint32_t cnt = 0, lo = 0xFFFFFFFFu, hi = 0;
 #pragma unroll
     for (int j = 0; j < kUPerThread; ++j) {
-      const bool v = kUPerThread * tid + j < C && u[j] != 0ull;  // 0: no position
+      const bool v = kUPerThread * tid + j < G * cm && u[j] != 0ull;  // 0: no position
+      uvalid |= v ? 1u << j : 0u;
       cnt += v ? 1u : 0u;
       lo = v && key_ubits(u[j]) < lo ? key_ubits(u[j]) : lo;
       hi = v && key_ubits(u[j]) > hi ? key_ubits(u[j]) : hi;
@@ -462,7 +502,7 @@ __device__ __forceinline__ bool exhaustive_list(GlobalI32 row, const int32_t* ro
       auto each_u = [&](auto f) {
 #pragma unroll
         for (int j = 0; j < kUPerThread; ++j)
-          if (kUPerThread * tid + j < C && u[j] != 0ull) f(key_ubits(u[j]));
+          if ((uvalid >> j) & 1u) f(key_ubits(u[j]));
       };
       // the low end of a radix bin of at most 64 union scores that holds the kk-th
       // (one pass, mostly, instead of narrowing to the value itself)
@@ -471,69 +511,109 @@ __device__ __forceinline__ bool exhaustive_list(GlobalI32 row, const int32_t* ro
     }
   }
   if (!from_union) {  // uniform
-      // 1. the sampled threshold: all positions of a short row, else 256 evenly spaced
-      // runs of 64 (one coalesced load per wave and run)
-      constexpr int SP = kSampleMax / kSelBlock;
-      const bool whole = n <= kSampleMax;
-      const int ns = whole ? n : kSampleMax;
-      const uint64_t want = (uint64_t)kk * 5 / 4 + 32;
-      const uint32_t rs0 = (uint32_t)((want * (uint64_t)ns + (uint64_t)n - 1) / (uint64_t)n);
-      const uint32_t rs = rs0 < (uint32_t)ns ? (rs0 > 0 ? rs0 : 1u) : (uint32_t)ns;
-      int32_t sx[SP];
-  #pragma unroll
-      for (int j = 0; j < SP; ++j) {
-        const int i = tid + kSelBlock * j;
-        // run w + 8 j starts at its share of the row; runs never overlap (n > 16384)
-        const int64_t p = whole ? (i < n ? i : 0) : (int64_t)(w + kSelWaves * j) * n / (kSampleMax / 64) + lane;
-        sx[j] = row[p];
+    // all positions of a short row, else 256 evenly spaced runs of 64 (one coalesced
+    // load per wave and run)
+    constexpr int SP = kSampleMax / kSelBlock;
+    const bool whole = n <= kSampleMax;
+    const int ns = whole ? n : kSampleMax;
+    const uint64_t want = (uint64_t)kk * 5 / 4 + 32;
+    const uint32_t rs0 = (uint32_t)((want * (uint64_t)ns + (uint64_t)n - 1) / (uint64_t)n);
+    const uint32_t rs = rs0 < (uint32_t)ns ? (rs0 > 0 ? rs0 : 1u) : (uint32_t)ns;
+    int32_t sx[SP];
+#pragma unroll
+    for (int j = 0; j < SP; ++j) {
+      const int i = tid + kSelBlock * j;
+      // run w + 8 j starts at its share of the row; runs never overlap (n > 16384)
+      const int64_t p = whole ? (i < n ? i : 0) : (int64_t)(w + kSelWaves * j) * n / (kSampleMax / 64) + lane;
+      sx[j] = row[p];
+    }
+    uint32_t lo = 0xFFFFFFFFu, hi = 0;
+#pragma unroll
+    for (int j = 0; j < SP; ++j)
+      if (!whole || tid + kSelBlock * j < n) {
+        const uint32_t v = score_bits(sx[j]);
+        lo = v < lo ? v : lo;
+        hi = v > hi ? v : hi;
       }
-      uint32_t lo = 0xFFFFFFFFu, hi = 0;
-  #pragma unroll
+    const Stats4 st = block_stats(0, lo, hi, 0, sm);
+    auto each_s = [&](auto f) {
+#pragma unroll
       for (int j = 0; j < SP; ++j)
-        if (!whole || tid + kSelBlock * j < n) {
-          const uint32_t u = score_bits(sx[j]);
-          lo = u < lo ? u : lo;
-          hi = u > hi ? u : hi;
-        }
-      const Stats4 st = block_stats(0, lo, hi, 0, sm);
-      auto each_s = [&](auto f) {
-  #pragma unroll
-        for (int j = 0; j < SP; ++j)
-          if (!whole || tid + kSelBlock * j < n) f(score_bits(sx[j]));
-      };
-      // T0: the low end of a radix bin of at most 16 sampled values that holds the
-      // rs-th best (every sampled value of the bin passes, a few more than rs)
-      const RadixBin tb = block_narrow<kSelBlock>(each_s, st.lo, st.hi, rs, (uint32_t)ns, 16u, sm.radix);
-      t0bits = tb.binlo;
+        if (!whole || tid + kSelBlock * j < n) f(score_bits(sx[j]));
+    };
+    // the low end of a radix bin of at most 16 sampled values that holds the rs-th
+    // best (every sampled value of the bin passes, a few more than rs)
+    t0bits = block_narrow<kSelBlock>(each_s, st.lo, st.hi, rs, (uint32_t)ns, 16u, sm.radix).binlo;
   }
   const int32_t T0 = (int32_t)(t0bits ^ 0x80000000u);  // as a score
-    // 2. every key scoring at least T0 into the list. Wave w appends to its own
-    // segment, in the order of its loads, so that the list's order is the same in
-    // every workgroup that builds it (the ranking workgroups split the selected keys
-    // by their place in it). The positions before the row's first 16-byte boundary
-    // go to wave 0 first; then 16-byte loads, thread t's load j of a pass covering
-    // positions h + 4 (q0 + t + 512 j) + [0, 4).
-    const uint64_t lt = lanemask_lt();
-    uint64_t* const wseg = cand + w * kWaveCand;
-    // a kept key as stored: make_key without its sign flip (one instruction less per
-    // append; undone when the list is read)
-    auto raw_key = [](int32_t x, uint32_t pos) {
-      return ((uint64_t)(uint32_t)x << 32) | (uint64_t)(0xFFFFFFFFu - pos);
-    };
-    uint32_t wn = 0;  // keys this wave kept (uniform)
-    int32_t kmax = INT32_MIN;  // the best score this lane kept
+
+  // 2. the list. With the union: the chunks whose best dropped key reaches T0
+  bool listed = false;
+  if (from_union) {  // uniform
+    typedef const __attribute__((address_space(1))) uint64_t* GlobalU64;
+    const bool hot = tid < G && ((GlobalU64)xc_row)[tid] >= ((uint64_t)t0bits << 32);
+    const uint64_t hb = __ballot(hot);
+    if (lane == 0 && w < kMaxChunks / 64) sm.hotm[w] = hb;
+    lds_barrier();
+    uint64_t hm[kMaxChunks / 64];
+    uint32_t nhot = 0;
+#pragma unroll
+    for (int x = 0; x < kMaxChunks / 64; ++x) {
+      hm[x] = sm.hotm[x];
+      nhot += (uint32_t)__popcll(hm[x]);
+    }
+    if (nhot <= (uint32_t)kMaxHotChunks) {  // uniform
+      // the union's keys at or above T0 from the other chunks (a thread's 16
+      // entries lie in one chunk: cm >= 16)
+      const int ct = kUPerThread * tid / cm;
+      const bool cold = ct >= kMaxChunks || !((hm[ct >> 6] >> (ct & 63)) & 1ull);
+#pragma unroll
+      for (int j = 0; j < kUPerThread; ++j)
+        append(((uvalid >> j) & 1u) && cold && key_ubits(u[j]) >= t0bits, key_score(u[j]), key_pos(u[j]));
+      // every key at or above T0 of the hot chunks: wave w rescans the hot chunks
+      // of rank w, w + 8, ... (each a round of up to 16 loads per lane per 1,024
+      // positions)
+      uint32_t rank = 0;
+#pragma unroll
+      for (int x = 0; x < kMaxChunks / 64; ++x) {
+        uint64_t bits = hm[x];
+        while (bits != 0ull) {  // uniform
+          const int c = 64 * x + (int)__builtin_ctzll(bits);
+          bits &= bits - 1ull;
+          if ((int)(rank++ % kSelWaves) != w) continue;
+          int cnt;
+          const int len = 32 * row_chunk_units(n, c, G, P, ilv, &cnt);  // local positions, last unit cut
+          constexpr int R = 16;
+          for (int i0 = 0; i0 < len; i0 += 64 * R) {
+            int32_t x4[R];
+            uint32_t pos[R];
+            bool ok[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+              const int i = i0 + 64 * r + lane;
+              pos[r] = (uint32_t)(ilv ? 32 * (c + G * (i >> 5)) + (i & 31) : c * P + i);
+              ok[r] = i < len && pos[r] < (uint32_t)n;
+              x4[r] = row[ok[r] ? pos[r] : 0u];
+            }
+#pragma unroll
+            for (int r = 0; r < R; ++r) append(ok[r] && x4[r] >= T0, x4[r], pos[r]);
+          }
+        }
+      }
+      listed = true;
+    }
+  }
+  if (!listed) {  // uniform
+    // one pass over the whole row: the positions before the row's first 16-byte
+    // boundary go to wave 0 first; then 16-byte loads, thread t's load j of a pass
+    // covering positions h + 4 (q0 + t + 512 j) + [0, 4) (wave w: 64-position
+    // slices)
     const int h0 = (int)(((16u - ((uint32_t)reinterpret_cast<uintptr_t>(row_in) & 15u)) & 15u) >> 2);
     const int h = h0 < n ? h0 : n;
     if (w == 0 && h > 0) {  // uniform
       int32_t x = 0;
       if (lane < h) x = row[lane];
-      const bool keep = lane < h && x >= T0;
-      const uint64_t bal = __ballot(keep);
-      if (keep) {
-        wseg[__popcll(bal & lt)] = raw_key(x, (uint32_t)lane);
-        kmax = x;
-      }
-      wn = (uint32_t)__popcll(bal);
+      append(lane < h && x >= T0, x, (uint32_t)lane);
     }
     const int64_t m = (int64_t)n - h;  // positions from the boundary on
     const int64_t nq = (m + 3) / 4;    // 16-byte vectors holding them (each holds one)
@@ -544,40 +624,22 @@ __device__ __forceinline__ bool exhaustive_list(GlobalI32 row, const int32_t* ro
     auto keep_vec = [&](const i32x4& v, int64_t q0, int j, auto full) {
       const int64_t q = q0 + tid + (int64_t)kSelBlock * j;
       const int32_t x4[4] = {v.x, v.y, v.z, v.w};
-      // the four compares first and one branch on them all (a branch right behind
-      // each compare waits for it)
+      // the four compares first and one branch on them all
       bool keep[4];
-      uint64_t bal[4];
+      uint64_t any = 0;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         keep[e] = x4[e] >= T0 && (decltype(full)::value || 4 * q + e < m);
-        bal[e] = __ballot(keep[e]);
+        any |= __ballot(keep[e]);
       }
-      if ((bal[0] | bal[1] | bal[2] | bal[3]) == 0) return;  // uniform
-      const uint32_t p0 = (uint32_t)(h + 4 * q);
+      if (any == 0ull) return;  // uniform
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (bal[e] != 0) {  // uniform
-          // the slot wraps within the segment: a wave that keeps more than it
-          // holds makes the list unusable, which the count below detects
-          const uint32_t at = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal[e] >> 32),
-                                                        __builtin_amdgcn_mbcnt_lo((uint32_t)bal[e], wn)) &
-                              (uint32_t)(kWaveCand - 1);
-          if (keep[e]) {
-            // raw_key as two words (no register pair to assemble)
-            uint32_t* const slot = reinterpret_cast<uint32_t*>(wseg + at);
-            slot[0] = 0xFFFFFFFFu - (p0 + (uint32_t)e);
-            slot[1] = (uint32_t)x4[e];
-            kmax = x4[e] > kmax ? x4[e] : kmax;
-          }
-          wn += (uint32_t)__popcll(bal[e]);
-        }
-      }
+      for (int e = 0; e < 4; ++e) append(keep[e], x4[e], (uint32_t)(h + 4 * q + e));
     };
     // passes whose vectors all lie inside the row: as soon as load j of a pass is
     // used, the same slot loads its vector of the next pass, so U loads stay in
-    // flight while keys are kept (the last pass's follow-up loads repeat that pass
-    // rather than branch around the loads)
+    // flight (the last pass's follow-up loads repeat that pass rather than branch
+    // around the loads)
     const int64_t nfull = (m / 4) / step;
     if (nfull > 0) {  // uniform
       i32x4 v[U];
@@ -608,35 +670,40 @@ __device__ __forceinline__ bool exhaustive_list(GlobalI32 row, const int32_t* ro
 #pragma unroll
       for (int j = 0; j < U; ++j) keep_vec(v[j], q0, j, std::false_type{});
     }
-  // per wave: keys kept and the best kept score; the list's score range is then
-  // [T0, the best of those] (bounds suffice for the narrowing: no exchange of the
-  // keys' own range)
-  const uint32_t whi = wave_maxr_u32(score_bits(kmax));
+  }
+
+  // 3. The wave's own keys into registers (only its lanes wrote them, and LDS work
+  // of one wave completes in order), and per wave the count and the best kept
+  // score: the list's score range is [T0, the best of those] (bounds suffice for
+  // the narrowing: no exchange of the keys' own range).
+  const uint32_t own = wn < (uint32_t)kWaveCap ? wn : (uint32_t)kWaveCap;
+  uint32_t lhi = 0;
+  vmask = 0;
+#pragma unroll
+  for (int j = 0; j < kUPerThread; ++j) {
+    const uint32_t i = (uint32_t)(kUPerThread * lane + j);
+    key[j] = i < own ? wseg[i] ^ (1ull << 63) : 0ull;  // raw -> make_key
+    sv[j] = key_ubits(key[j]);
+    vmask |= i < own ? 1u << j : 0u;
+    lhi = i < own && sv[j] > lhi ? sv[j] : lhi;
+  }
+  const uint32_t whi = wave_maxr_u32(lhi);
   if (lane == 0) {
     sm.wcnt[w][0] = wn;
     sm.wcnt[w][1] = whi;
   }
   lds_barrier();
-  uint32_t total = 0, fits = 1, mine = 0, hi = 0;
+  uint32_t total = 0, fits = 1, hi = 0;
 #pragma unroll
   for (int x = 0; x < kSelWaves; ++x) {
     const uint32_t c = sm.wcnt[x][0];
     total += c;
-    fits &= c <= (uint32_t)kWaveCand ? 1u : 0u;
-    mine = x == w ? c : mine;
+    fits &= c <= (uint32_t)kWaveCap ? 1u : 0u;
     hi = sm.wcnt[x][1] > hi ? sm.wcnt[x][1] : hi;
   }
   if (!fits || total < (uint32_t)kk) return false;  // uniform
   rng[0] = t0bits;
   rng[1] = hi;
-  vmask = 0;
-#pragma unroll
-  for (int j = 0; j < kUPerThread; ++j) {
-    const uint32_t i = (uint32_t)(kUPerThread * lane + j);
-    key[j] = i < mine ? wseg[i] ^ (1ull << 63) : 0ull;  // raw_key -> make_key
-    sv[j] = key_ubits(key[j]);
-    vmask |= i < mine ? 1u << j : 0u;
-  }
   *total_out = total;
   // every thread has read its keys before any writes the region again (the list
   // and sink slots that the narrowing uses lie over the kept keys)
@@ -722,17 +789,20 @@ __device__ __noinline__ uint64_t select_row_radix(const int32_t* __restrict__ ro
 // rare, and inlined into the selection kernel it made the candidate path's code
 // larger and slower.)
 __device__ __noinline__ uint64_t select_row_exhaustive(const int32_t* __restrict__ row_in, int n, int kk, int k,
-                                                       const uint64_t* cand_row, int C, uint32_t* tied) {
+                                                       const uint64_t* cand_row, const uint64_t* xc_row,
+                                                       ChunkGeom cg, uint32_t* tied) {
   n = __builtin_amdgcn_readfirstlane(n);
   kk = __builtin_amdgcn_readfirstlane(kk);
   k = __builtin_amdgcn_readfirstlane(k);
-  C = __builtin_amdgcn_readfirstlane(C);
+  cg = uniform_geom(cg);
   row_in = reinterpret_cast<const int32_t*>(uniform_u64(reinterpret_cast<uint64_t>(row_in)));
   cand_row = reinterpret_cast<const uint64_t*>(uniform_u64(reinterpret_cast<uint64_t>(cand_row)));
+  xc_row = reinterpret_cast<const uint64_t*>(uniform_u64(reinterpret_cast<uint64_t>(xc_row)));
   const SelLds l = sel_lds(k);
   uint64_t key[kUPerThread];
   uint32_t sv[kUPerThread], vmask = 0, total = 0, rng[2];
-  if (kk > 0 && exhaustive_list(global_view(row_in), row_in, n, kk, cand_row, C, l, key, sv, vmask, &total, rng)) {
+  if (kk > 0 && exhaustive_list(global_view(row_in), row_in, n, kk, cand_row, xc_row, cg.G, cg.m, cg.P, cg.ilv, l,
+                                key, sv, vmask, &total, rng)) {
     const TopK t = topk_of_keys<kUPerThread>(key, sv, vmask, total, (uint32_t)kk, rng[0], rng[1], false, l.sel,
                                              l.list, l.sink, *l.sm, false, 0ull);
     *tied = t.tied;
@@ -883,11 +953,13 @@ __device__ __forceinline__ uint32_t window_positions(const uint64_t (&key)[E], c
 // path are not waited for where its code would otherwise join this path's; uniform
 // arguments back in scalar registers as in select_row_exhaustive.)
 __device__ __noinline__ void exhaustive_window(const int32_t* __restrict__ row_in, int n, int kk, int k,
-                                               const uint64_t* cand_row, int C, uint32_t r0, uint32_t r1) {
+                                               const uint64_t* cand_row, const uint64_t* xc_row, ChunkGeom cg,
+                                               uint32_t r0, uint32_t r1) {
   n = __builtin_amdgcn_readfirstlane(n);
   kk = __builtin_amdgcn_readfirstlane(kk);
   k = __builtin_amdgcn_readfirstlane(k);
-  C = __builtin_amdgcn_readfirstlane(C);
+  cg = uniform_geom(cg);
+  xc_row = reinterpret_cast<const uint64_t*>(uniform_u64(reinterpret_cast<uint64_t>(xc_row)));
   r0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)r0);
   r1 = (uint32_t)__builtin_amdgcn_readfirstlane((int)r1);
   row_in = reinterpret_cast<const int32_t*>(uniform_u64(reinterpret_cast<uint64_t>(row_in)));
@@ -896,7 +968,8 @@ __device__ __noinline__ void exhaustive_window(const int32_t* __restrict__ row_i
   SelSmem& sm = *l.sm;
   uint64_t key[kUPerThread];
   uint32_t sv[kUPerThread], vmask = 0, total = 0, rng[2];
-  if (!exhaustive_list(global_view(row_in), row_in, n, kk, cand_row, C, l, key, sv, vmask, &total, rng)) {
+  if (!exhaustive_list(global_view(row_in), row_in, n, kk, cand_row, xc_row, cg.G, cg.m, cg.P, cg.ilv, l, key, sv,
+                       vmask, &total, rng)) {
     uint32_t tied;
     select_row_radix(row_in, n, kk, k, &tied);
     vmask = 0;
@@ -1034,8 +1107,8 @@ __global__ __launch_bounds__(kSelBlock) void k_select(const uint64_t* __restrict
       if (above_mx < (uint32_t)kk) reason = 2;
     }
     if (cnt > 0 && reason != 0)  // uniform
-      exhaustive_window(row, n, kk, a.k, have_cand ? cand + (int64_t)b * kCandCap : nullptr, G * a.m, (uint32_t)r0,
-                        (uint32_t)(r0 + cnt - 1));
+      exhaustive_window(row, n, kk, a.k, have_cand ? cand + (int64_t)b * kCandCap : nullptr, xc + (int64_t)b * G,
+                        ChunkGeom{G, a.m, a.P, a.ilv}, (uint32_t)r0, (uint32_t)(r0 + cnt - 1));
     // sm.winpos is complete and published (the last barrier of the window
     // narrowing follows its last write), and the LDS region is free again
     Attn::run(at, b, blockIdx.x, [&](int i) { return (int64_t)sm.winpos[i]; }, cnt, region, qf);
@@ -1085,8 +1158,8 @@ __global__ __launch_bounds__(kSelBlock) void k_select(const uint64_t* __restrict
   const int r = (int)blockIdx.x - S;
   if (r >= R) return;  // uniform
   if (reason != 0) {
-    kstar = select_row_exhaustive(row, n, kk, a.k, have_cand ? cand + (int64_t)b * kCandCap : nullptr, G * a.m,
-                                  &tied);
+    kstar = select_row_exhaustive(row, n, kk, a.k, have_cand ? cand + (int64_t)b * kCandCap : nullptr,
+                                  xc + (int64_t)b * G, ChunkGeom{G, a.m, a.P, a.ilv}, &tied);
     nsel = (uint32_t)kk;
   }
 

@@ -145,11 +145,16 @@ def bits_equal(a, b):
     return np.array_equal(np.ascontiguousarray(a).view(np.uint8), np.ascontiguousarray(b).view(np.uint8))
 
 
-@pytest.mark.parametrize("name", ["ctx16k", "ctx300k", "ctx300k_tiepool", "verify8_ctx131k"])
+@pytest.mark.parametrize("name", ["ctx16k", "ctx300k", "ctx300k_tiepool", "verify8_ctx131k", "ctx16k_zeroquery",
+                                  "ctx16k_hotstride"])
 def test_forced_fallback_matches_fast_path(torch, dsa, name):
     # The exhaustive path selects the same positions in the same order, and attention
     # split s takes the positions of output slots [s*per, (s+1)*per) on either path,
-    # so the outputs are equal bit for bit.
+    # so the outputs are equal bit for bit. The exhaustive path's list: the union's
+    # keys plus rescans of the few chunks whose best dropped key reaches the
+    # threshold (ctx16k ... verify8: few or none; hot stride: the chunk holding the
+    # tied best keys); on the zero-query row every chunk reaches it, so the row is
+    # streamed whole, the list overflows and the radix selection runs.
     note("forced fallback", name)
     c, (rs, ri, ro) = case(name)
     d = dev_inputs(torch, c)
@@ -162,7 +167,7 @@ def test_forced_fallback_matches_fast_path(torch, dsa, name):
     check_attention(o1, ro, name + " fast path")
     assert bits_equal(o1, o2), name + ": fast path and exhaustive path outputs differ"
     assert all(st["path"] == 1 and st["reason"] == 1 for st in st2)
-    assert all(st["path"] == 0 for st in st1)
+    assert all(st["path"] == (1 if name == "ctx16k_hotstride" else 0) for st in st1)
     for a, b in zip(st1, st2):
         assert (a["selected"], a["kth_score"], a["tied_at_kth"]) == (b["selected"], b["kth_score"],
                                                                      b["tied_at_kth"])
