@@ -298,9 +298,7 @@ SelArgs sel_args(const int32_t* scores, const RowLens& lens, int64_t N, int k, i
   a.k = k;
   a.G = cp.G;
   a.m = cp.m;
-  a.P = cp.P;
-  a.ilv = cp.ilv;
-  a.have_cand = have_cand ? 1 : 0;
+  a.have_cand = have_cand ? cp.P : 0;
   memset(&a.cand_valid, 0, sizeof(a.cand_valid));
   for (int b = 0; b < kMaxBatch; ++b) {  // each chunk keeps min(m, its valid positions)
     int64_t v = 0;

@@ -123,15 +123,14 @@ struct SelArgs {
   const int32_t* scores;
   const uint64_t* cand;
   const uint64_t* xc;
-  const ChunkSum* sums;  // [B][kMaxChunks] from the one-row score pass, or nullptr
+  const ChunkSum* sums;  // [B][kMaxChunks] from the one-row score pass (interleaved chunks), or nullptr
   int32_t* idx;        // [B][k]
   RowStats* stats;     // [B]
   RowLens lens;
   int64_t N;
   int k;
   int G, m;            // candidate layout
-  int P, ilv;          // chunk geometry of the candidate pass (row_chunk_units)
-  int have_cand;       // 0: the candidate pass did not run (chunks too long)
+  int have_cand;       // the candidate pass's chunk length P, or 0 when it did not run (chunks too long)
   RowLens cand_valid;  // per row: union entries that hold a candidate (the rest are 0)
   int force;           // DSA_FLAG_FORCE_FALLBACK
   int R;               // ranking workgroups per row

@@ -96,10 +96,10 @@ constexpr int kWaveCap = kWaveCand - 64;
 struct SelSmem {
   RadixSmem radix;
   uint32_t xch[kSelWaves][5];
-  uint64_t mxw[kSelWaves];          // per wave: the best key a chunk left out
+  uint64_t mxw[kSelWaves];          // per wave: the best key a chunk left out; on the exhaustive path,
+                                    // [0, 4): chunks whose best dropped key reaches T0
   uint32_t wcnt[kSelWaves][2];      // exhaustive compaction: per-wave counts above / at the threshold
   uint32_t gtw[kSelWaves];          // attention: per-wave counts of keys above the best dropped key
-  uint64_t hotm[kMaxChunks / 64];   // exhaustive path: chunks whose best dropped key reaches T0
   uint64_t kstar;
   uint32_t tied;
   uint32_t winpos[kMaxWindow];      // attention: the window's positions, in output order
@@ -435,13 +435,57 @@ __device__ __forceinline__ SelLds sel_lds(int k) {
 // select_row_radix.
 constexpr int kMaxHotChunks = 32;
 // The candidate pass's chunks (row_chunk_units): G chunks of P positions keeping m
-// candidates each; ilv: interleaved 32-position units.
+// candidates each; ilv: interleaved 32-position units. (The selection kernel gets
+// P in SelArgs::have_cand and ilv as the presence of the one-row pass's chunk
+// summaries: no argument of their own, which would move or add argument reads
+// on the candidate path.)
 struct ChunkGeom {
   int G, m, P, ilv;
 };
-__device__ __forceinline__ ChunkGeom uniform_geom(ChunkGeom g) {
-  return ChunkGeom{__builtin_amdgcn_readfirstlane(g.G), __builtin_amdgcn_readfirstlane(g.m),
-                   __builtin_amdgcn_readfirstlane(g.P), __builtin_amdgcn_readfirstlane(g.ilv)};
+
+// The selection kernel's arguments as they lie in its argument segment: its
+// parameter list in order, each at its natural alignment. The out-of-line
+// exhaustive path reads what it needs from there (scalar loads where it starts)
+// instead of taking more arguments: values passed to it would stay live through
+// the candidate path's code and push its scalar registers into spills.
+struct SelectKernArgs {
+  const uint64_t* cand;
+  const uint64_t* xc;
+  const ChunkSum* sums;
+  const void* q;
+  int G, Hq, Dk, S;
+  SelArgs a;
+  AttnArgs at;
+};
+static_assert(offsetof(SelectKernArgs, a) == 48 && offsetof(SelectKernArgs, at) == 48 + sizeof(SelArgs),
+              "the selection kernel's argument layout");
+typedef const __attribute__((address_space(4))) SelectKernArgs* KernArgPtr;
+
+// One row's inputs to the exhaustive path, from the kernel arguments.
+struct ExhRow {
+  GlobalI32 row;
+  const int32_t* row_in;
+  int n, kk, k;
+  const uint64_t* cand_row;  // the candidate union, or nullptr when the pass did not run
+  const uint64_t* xc_row;    // each chunk's best dropped key
+  ChunkGeom cg;
+};
+__device__ __forceinline__ ExhRow exh_row(const SelectKernArgs* ka_in, int b) {
+  const KernArgPtr ka = (KernArgPtr) reinterpret_cast<const SelectKernArgs*>(
+      uniform_u64(reinterpret_cast<uint64_t>(ka_in)));
+  b = __builtin_amdgcn_readfirstlane(b);
+  ExhRow r;
+  r.row_in = ka->a.scores + (int64_t)b * ka->a.N;
+  r.row = global_view(r.row_in);
+  r.n = ka->a.lens.n[b];
+  r.k = ka->a.k;
+  r.kk = r.k < r.n ? r.k : r.n;
+  const int P = ka->a.have_cand;  // the candidate pass's chunk length, or 0
+  r.cand_row = P > 0 ? ka->cand + (int64_t)b * kCandCap : nullptr;
+  r.xc_row = ka->xc + (int64_t)b * ka->G;
+  // the one-row pass (interleaved chunks) is the one that leaves chunk summaries
+  r.cg = ChunkGeom{ka->G, ka->a.m, P, ka->sums != nullptr ? 1 : 0};
+  return r;
 }
 __device__ __forceinline__ bool exhaustive_list(GlobalI32 row, const int32_t* row_in, int n, int kk,
                                                 const uint64_t* cand_row, const uint64_t* xc_row, int G, int cm,
@@ -553,13 +597,15 @@ __device__ __forceinline__ bool exhaustive_list(GlobalI32 row, const int32_t* ro
     typedef const __attribute__((address_space(1))) uint64_t* GlobalU64;
     const bool hot = tid < G && ((GlobalU64)xc_row)[tid] >= ((uint64_t)t0bits << 32);
     const uint64_t hb = __ballot(hot);
-    if (lane == 0 && w < kMaxChunks / 64) sm.hotm[w] = hb;
+    // (in sm.mxw: its last readers, on the ranking side, passed a barrier since)
+    static_assert(kMaxChunks / 64 <= kSelWaves, "hot chunk masks");
+    if (lane == 0 && w < kMaxChunks / 64) sm.mxw[w] = hb;
     lds_barrier();
     uint64_t hm[kMaxChunks / 64];
     uint32_t nhot = 0;
 #pragma unroll
     for (int x = 0; x < kMaxChunks / 64; ++x) {
-      hm[x] = sm.hotm[x];
+      hm[x] = sm.mxw[x];
       nhot += (uint32_t)__popcll(hm[x]);
     }
     if (nhot <= (uint32_t)kMaxHotChunks) {  // uniform
@@ -788,27 +834,19 @@ __device__ __noinline__ uint64_t select_row_radix(const int32_t* __restrict__ ro
 // named, and the LDS comes from its symbol. (Out of line: the exhaustive path is
 // rare, and inlined into the selection kernel it made the candidate path's code
 // larger and slower.)
-__device__ __noinline__ uint64_t select_row_exhaustive(const int32_t* __restrict__ row_in, int n, int kk, int k,
-                                                       const uint64_t* cand_row, const uint64_t* xc_row,
-                                                       ChunkGeom cg, uint32_t* tied) {
-  n = __builtin_amdgcn_readfirstlane(n);
-  kk = __builtin_amdgcn_readfirstlane(kk);
-  k = __builtin_amdgcn_readfirstlane(k);
-  cg = uniform_geom(cg);
-  row_in = reinterpret_cast<const int32_t*>(uniform_u64(reinterpret_cast<uint64_t>(row_in)));
-  cand_row = reinterpret_cast<const uint64_t*>(uniform_u64(reinterpret_cast<uint64_t>(cand_row)));
-  xc_row = reinterpret_cast<const uint64_t*>(uniform_u64(reinterpret_cast<uint64_t>(xc_row)));
-  const SelLds l = sel_lds(k);
+__device__ __noinline__ uint64_t select_row_exhaustive(const SelectKernArgs* ka, int b, uint32_t* tied) {
+  const ExhRow e = exh_row(ka, b);
+  const SelLds l = sel_lds(e.k);
   uint64_t key[kUPerThread];
   uint32_t sv[kUPerThread], vmask = 0, total = 0, rng[2];
-  if (kk > 0 && exhaustive_list(global_view(row_in), row_in, n, kk, cand_row, xc_row, cg.G, cg.m, cg.P, cg.ilv, l,
-                                key, sv, vmask, &total, rng)) {
-    const TopK t = topk_of_keys<kUPerThread>(key, sv, vmask, total, (uint32_t)kk, rng[0], rng[1], false, l.sel,
+  if (e.kk > 0 && exhaustive_list(e.row, e.row_in, e.n, e.kk, e.cand_row, e.xc_row, e.cg.G, e.cg.m, e.cg.P, e.cg.ilv,
+                                  l, key, sv, vmask, &total, rng)) {
+    const TopK t = topk_of_keys<kUPerThread>(key, sv, vmask, total, (uint32_t)e.kk, rng[0], rng[1], false, l.sel,
                                              l.list, l.sink, *l.sm, false, 0ull);
     *tied = t.tied;
     return t.kstar;
   }
-  return select_row_radix(row_in, n, kk, k, tied);
+  return select_row_radix(e.row_in, e.n, e.kk, e.k, tied);
 }
 
 // Completes the narrowing of one sought key (the need-th largest of the keys held
@@ -952,26 +990,19 @@ __device__ __forceinline__ uint32_t window_positions(const uint64_t (&key)[E], c
 // of the radix selection. (Out of line, so that loads in flight on the candidate
 // path are not waited for where its code would otherwise join this path's; uniform
 // arguments back in scalar registers as in select_row_exhaustive.)
-__device__ __noinline__ void exhaustive_window(const int32_t* __restrict__ row_in, int n, int kk, int k,
-                                               const uint64_t* cand_row, const uint64_t* xc_row, ChunkGeom cg,
-                                               uint32_t r0, uint32_t r1) {
-  n = __builtin_amdgcn_readfirstlane(n);
-  kk = __builtin_amdgcn_readfirstlane(kk);
-  k = __builtin_amdgcn_readfirstlane(k);
-  cg = uniform_geom(cg);
-  xc_row = reinterpret_cast<const uint64_t*>(uniform_u64(reinterpret_cast<uint64_t>(xc_row)));
+__device__ __noinline__ void exhaustive_window(const SelectKernArgs* ka, int b, uint32_t r0, uint32_t r1) {
+  const ExhRow e = exh_row(ka, b);
+  const int kk = e.kk;
   r0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)r0);
   r1 = (uint32_t)__builtin_amdgcn_readfirstlane((int)r1);
-  row_in = reinterpret_cast<const int32_t*>(uniform_u64(reinterpret_cast<uint64_t>(row_in)));
-  cand_row = reinterpret_cast<const uint64_t*>(uniform_u64(reinterpret_cast<uint64_t>(cand_row)));
-  const SelLds l = sel_lds(k);
+  const SelLds l = sel_lds(e.k);
   SelSmem& sm = *l.sm;
   uint64_t key[kUPerThread];
   uint32_t sv[kUPerThread], vmask = 0, total = 0, rng[2];
-  if (!exhaustive_list(global_view(row_in), row_in, n, kk, cand_row, xc_row, cg.G, cg.m, cg.P, cg.ilv, l, key, sv,
+  if (!exhaustive_list(e.row, e.row_in, e.n, kk, e.cand_row, e.xc_row, e.cg.G, e.cg.m, e.cg.P, e.cg.ilv, l, key, sv,
                        vmask, &total, rng)) {
     uint32_t tied;
-    select_row_radix(row_in, n, kk, k, &tied);
+    select_row_radix(e.row_in, e.n, kk, e.k, &tied);
     vmask = 0;
 #pragma unroll
     for (int j = 0; j < kUPerThread; ++j) {
@@ -986,6 +1017,12 @@ __device__ __noinline__ void exhaustive_window(const int32_t* __restrict__ row_i
   }
   window_positions<kUPerThread>(key, sv, vmask, total, rng[0], rng[1], false, false, nullptr, 0, r0, r1, l.list,
                                 l.sink, sm);
+}
+
+// The kernel's argument segment, as the exhaustive path reads it.
+__device__ __forceinline__ const SelectKernArgs* kernel_args() {
+  return (const SelectKernArgs*)(const __attribute__((address_space(4))) SelectKernArgs*)
+      __builtin_amdgcn_kernarg_segment_ptr();
 }
 
 // LDS as laid out by sel_lds.
@@ -1107,8 +1144,7 @@ __global__ __launch_bounds__(kSelBlock) void k_select(const uint64_t* __restrict
       if (above_mx < (uint32_t)kk) reason = 2;
     }
     if (cnt > 0 && reason != 0)  // uniform
-      exhaustive_window(row, n, kk, a.k, have_cand ? cand + (int64_t)b * kCandCap : nullptr, xc + (int64_t)b * G,
-                        ChunkGeom{G, a.m, a.P, a.ilv}, (uint32_t)r0, (uint32_t)(r0 + cnt - 1));
+      exhaustive_window(kernel_args(), b, (uint32_t)r0, (uint32_t)(r0 + cnt - 1));
     // sm.winpos is complete and published (the last barrier of the window
     // narrowing follows its last write), and the LDS region is free again
     Attn::run(at, b, blockIdx.x, [&](int i) { return (int64_t)sm.winpos[i]; }, cnt, region, qf);
@@ -1158,8 +1194,7 @@ __global__ __launch_bounds__(kSelBlock) void k_select(const uint64_t* __restrict
   const int r = (int)blockIdx.x - S;
   if (r >= R) return;  // uniform
   if (reason != 0) {
-    kstar = select_row_exhaustive(row, n, kk, a.k, have_cand ? cand + (int64_t)b * kCandCap : nullptr,
-                                  xc + (int64_t)b * G, ChunkGeom{G, a.m, a.P, a.ilv}, &tied);
+    kstar = select_row_exhaustive(kernel_args(), b, &tied);
     nsel = (uint32_t)kk;
   }
 
