@@ -13,15 +13,20 @@ streamed far more than the 256 MB Infinity Cache holds.
 Timings, all on the stream the library launches on:
   - value: K steps as HIP graph replays (one graph holds one step per input set),
     bracketed by synchronisations; mean microseconds per step.
-  - step_stats: the same steps as one-step graphs replayed back to back (queued
-    behind a sleep kernel), with HIP events between the replays: median, p10, p90.
   - kernel durations: an eager pass of the same steps in which the runtime stamps
     HIP events with each stage kernel's own dispatch start and end
     (dsa_decode_step_timed), queued in chunks behind a sleep kernel so that the
     kernels run back to back as in the graph. These feed the roofline figures.
-  - legs: the forced exhaustive path on the headline workload, the 62k-context
-    11-layer step and the 8-row verify block, each as graph replays plus the eager
-    kernel pass.
+    (Events recorded inside a graph are not restamped on replay, so per-kernel
+    times come from this pass.)
+  - step_stats: the per-step mean of each replay of the R-step graph, HIP events
+    between the replays: median, p10, p90 over replays. (eager_step_span: from the
+    eager pass, per step the span from its first kernel's start to its last
+    kernel's end, eager launch gaps included.)
+  - legs: the forced exhaustive path on the headline workload (and the stand-alone
+    exhaustive selection over every position, the path of rows without candidates),
+    the 62k-context 11-layer step and the 8-row verify block, each as graph
+    replays plus the eager kernel pass.
   - cpu_baseline: the CPU oracle on the headline workload, single-threaded and with
     its all-core OpenMP build, per stage, median of 5 after one warm-up.
 
@@ -203,33 +208,47 @@ class Runner:
         del full
         return us, reps * self.R
 
-    def step_stats(self, steps, flags=0, chunk=40):
-        """Per-step times of one-step graph replays run back to back: HIP events recorded
-        between the replays on the replay stream."""
+    def full_row_select_us(self, calls):
+        """Mean time of a forced stand-alone selection over the last step's scores (no
+        candidate pass: the exhaustive path over every position), `calls` launches queued
+        back to back behind a sleep kernel between two HIP events (gaps included)."""
+        torch, c = self.torch, self.c
+        ws = self.binding.new_workspace(c["B"], c["N"], c["k"], 1, 1)
+        idx = torch.empty((c["B"], c["k"]), dtype=torch.int32, device="cuda")
+        sel = lambda: self.binding.dsa_topk_select(self.scores, c["ctx_len"], c["k"], idx=idx, workspace=ws,
+                                                   flags=self.binding.FLAG_FORCE_FALLBACK)
+        sel()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(20_000_000)
+        e0.record()
+        for _ in range(calls):
+            sel()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / calls
+
+    def replay_stats(self, reps, flags=0):
+        """Per-step mean of each replay of an R-step graph (HIP events between the replays on
+        the replay stream): the distribution over replays of the graph-replayed step time."""
         torch = self.torch
-        graphs = [self.capture([s], flags) for s in range(self.R)]
+        full = self.capture(range(self.R), flags)
         stream = torch.cuda.Stream()
-        times = []
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
         with torch.cuda.stream(stream):
-            for i0 in range(0, steps, chunk):
-                n = min(chunk, steps - i0)
-                ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
-                torch.cuda._sleep(20_000_000)  # lets the host queue the chunk ahead of the GPU
-                ev[0].record()
-                for i in range(n):
-                    graphs[(i0 + i) % self.R].replay()
-                    ev[i + 1].record()
-                torch.cuda.synchronize()
-                times += [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(n)]
-        del graphs
-        t = np.array(times)
-        return {"median_us": round(float(np.median(t)), 3), "p10_us": round(float(np.percentile(t, 10)), 3),
-                "p90_us": round(float(np.percentile(t, 90)), 3), "mean_us": round(float(t.mean()), 3),
-                "n": int(t.size)}
+            torch.cuda._sleep(20_000_000)  # lets the host queue the replays ahead of the GPU
+            ev[0].record()
+            for i in range(reps):
+                full.replay()
+                ev[i + 1].record()
+        torch.cuda.synchronize()
+        del full
+        return summary([ev[i].elapsed_time(ev[i + 1]) * 1e3 / self.R for i in range(reps)])
 
     def kernel_us(self, steps, flags=0, chunk=30):
         """Mean duration of each stage's kernels (us): score, select+attend, combine,
-        from events the runtime stamps with each dispatch's own start and end."""
+        from events the runtime stamps with each dispatch's own start and end; and per
+        step the span from its first kernel's start to its last kernel's end."""
         torch = self.torch
         evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(self.layers)]
                for _ in range(steps)]
@@ -247,6 +266,8 @@ class Runner:
         torch.cuda.synchronize()
         st = np.array([[[e[0].elapsed_time(e[1]), e[2].elapsed_time(e[3]), e[4].elapsed_time(e[5])]
                         for e in per_step] for per_step in evs]) * 1e3  # [steps][layers][3]
+        spans = [per_step[0][0].elapsed_time(per_step[-1][5]) * 1e3 for per_step in evs]
+        self.last_spans = spans
         return [float(st[:, :, i].mean()) for i in range(3)]
 
     def paths(self):
@@ -257,6 +278,13 @@ def describe(c, name, layers):
     return ("%s: %d cached positions, k=%d, %d query row(s), %d layer(s)/step; indexer %d heads x %d int8, "
             "one shared key per position; attention %d heads over a %d-value %s latent row (%d output values)"
             % (name, c["N"], c["k"], c["B"], layers, c["Hi"], c["Di"], c["Hq"], c["Dk"], c["dtype"], c["Dv"]))
+
+
+def summary(t):
+    t = np.array(t)
+    return {"median_us": round(float(np.median(t)), 3), "p10_us": round(float(np.percentile(t, 10)), 3),
+            "p90_us": round(float(np.percentile(t, 90)), 3), "mean_us": round(float(t.mean()), 3),
+            "n": int(t.size)}
 
 
 def measured_traffic(config):
@@ -415,12 +443,14 @@ def main():
     log("timed %d steps: %.2f us/step" % (K, us_step))
     del graphs, full, tail
 
-    stats = run.step_stats(K)
-    log("one-step replays: median %.2f us (p10 %.2f, p90 %.2f)" % (stats["median_us"], stats["p10_us"],
-                                                                   stats["p90_us"]))
+    replays = run.replay_stats(max(20, K // R))
+    log("graph replays: per-step median %.2f us (p10 %.2f, p90 %.2f) over %d replays of %d steps"
+        % (replays["median_us"], replays["p10_us"], replays["p90_us"], replays["n"], R))
     score_us, select_us, combine_us = run.kernel_us(K)
+    spans = summary(run.last_spans)
     log("kernel durations (eager, dispatch-stamped events): score %.2f us, select+attend %.2f us, "
-        "combine %.2f us" % (score_us, select_us, combine_us))
+        "combine %.2f us; per-step span median %.2f us (p10 %.2f, p90 %.2f)"
+        % (score_us, select_us, combine_us, spans["median_us"], spans["p10_us"], spans["p90_us"]))
     paths = run.paths()
 
     fallback = None
@@ -429,11 +459,20 @@ def main():
         f_us, f_n = run.graph_us(max(R, K // 5), flags=binding.FLAG_FORCE_FALLBACK)
         f_paths = run.paths()
         fk = run.kernel_us(max(R, K // 10), flags=binding.FLAG_FORCE_FALLBACK)
+        full_us = run.full_row_select_us(max(R, K // 10))
         fallback = {"us_per_step": round(f_us, 3), "steps": f_n, "ratio_to_candidate_path": round(f_us / us_step, 3),
                     "paths": f_paths, "select_attend_us": round(fk[1], 3),
-                    "what": "the same workload with DSA_FLAG_FORCE_FALLBACK: the exhaustive selection "
-                            "(a radix select over every position) for every row, graph replay"}
-        log("forced fallback: %.2f us/step" % f_us)
+                    "what": "the same workload with DSA_FLAG_FORCE_FALLBACK, graph replay: the exhaustive "
+                            "path for every row (threshold from the candidate union, the union's keys plus "
+                            "rescans of the chunks whose best dropped key reaches it, exact top-k, the "
+                            "attention window from that list)",
+                    "full_row_select_us": round(full_us, 3),
+                    "full_row_what": "dsa_topk_select with DSA_FLAG_FORCE_FALLBACK on the same scores (no "
+                                     "candidate pass: sampled threshold, one streamed pass over every "
+                                     "position, exact top-k, ranking; the path of rows without "
+                                     "candidates), mean per call of back-to-back calls queued behind a "
+                                     "sleep kernel between two HIP events (launch gaps included)"}
+        log("forced fallback: %.2f us/step; full-row exhaustive selection %.2f us" % (f_us, full_us))
 
     # reference read rate: a vendor streaming reduction over the same key caches, in the same
     # cold rotation (context for the roofline fraction, not part of the metric)
@@ -496,8 +535,12 @@ def main():
         "data": "synthetic (seeded; no model weights or caches)",
         "config": {"workload": describe(c, args.config, layers), "cache": cache,
                    "launch": "HIP graph replay of %d step(s) per graph" % R},
-        "step_stats": dict(stats, how="one-step graphs replayed back to back behind a sleep kernel, HIP "
-                                      "events between the replays"),
+        "step_stats": dict(replays, how="per-step mean of each replay of the %d-step graph (HIP events "
+                                        "between replays queued behind a sleep kernel; events recorded "
+                                        "inside a graph are not restamped on replay)" % R),
+        "eager_step_span": dict(spans, how="per step of the eager kernel pass: first kernel's start to last "
+                                           "kernel's end, dispatch-stamped events (includes the eager "
+                                           "launch gaps that the graph removes)"),
         "roofline": {
             "bound": "hbm",
             "kernel": "indexer score pass (k_score_row: int8 MFMA, per-chunk top-m candidates)",
