@@ -8,6 +8,9 @@ Reads the rocpd SQLite databases that `rocprofv3 -d DIR -o NAME` writes
             then WRITE_SIZE), each scaled by what the same counter reads for a plain
             copy kernel of known size run in the same process (torch.neg over 64 Mi fp32
             values: 256 MiB read, 256 MiB written)
+  mfma      matrix-core work and busy time per dispatch of each libdsa kernel from one
+            --pmc run of SQ_INSTS_VALU_MFMA_MOPS_I8, SQ_VALU_MFMA_BUSY_CYCLES and
+            GRBM_GUI_ACTIVE
 
 The counter summary records a hash of the kernel sources it was taken from; a
 reader treats it as stale once the sources change.
@@ -193,6 +196,52 @@ def cmd_counters(args):
     print(json.dumps(out, indent=1))
 
 
+MI355X_CUS, SIMDS_PER_CU, CLOCK_GHZ, INT8_PEAK_TOPS = 256, 4, 2.4, 5000.0
+
+
+def cmd_mfma(args):
+    """Per library kernel: int8 matrix ops per dispatch (MOPS_I8 counts ops / 512), the
+    matrix-core busy cycles per SIMD (the counter sums over every SIMD), and that as a
+    fraction of the dispatch's cycles at the nominal clock; the rate those ops reach
+    over the dispatch (counters run serialises dispatches, so durations run longer
+    than in the timed bench)."""
+    con = _db(args.db)
+    rows = con.execute("SELECT kernel_name, dispatch_id, counter_name, SUM(value), MAX(end) - MIN(start) "
+                       "FROM counters_collection GROUP BY kernel_name, dispatch_id, counter_name").fetchall()
+    acc = {}
+    for name, did, counter, value, dur in rows:
+        k = short_name(name)
+        if k is None:
+            continue
+        d = acc.setdefault(name, {}).setdefault(did, {"dur_ns": dur})
+        d[counter] = float(value)
+    out = {"command": args.command, "kernel_source_sha": library_source_sha(),
+           "summary_command": "python3 -m sparse_attention_decode_scores_amd.profsum " + " ".join(
+               "'%s'" % x if " " in x else x for x in sys.argv[1:]),
+           "assumptions": {"simds": MI355X_CUS * SIMDS_PER_CU, "clock_GHz": CLOCK_GHZ,
+                           "int8_peak_TOPS": INT8_PEAK_TOPS},
+           "kernels": {}}
+    for name, per in acc.items():
+        n = len(per)
+        mean = lambda key: sum(d.get(key, 0.0) for d in per.values()) / n
+        dur_us = mean("dur_ns") / 1e3
+        ops = mean("SQ_INSTS_VALU_MFMA_MOPS_I8") * 512
+        busy_simd = mean("SQ_VALU_MFMA_BUSY_CYCLES") / (MI355X_CUS * SIMDS_PER_CU)
+        ent = {"name": name, "dispatches": n, "dispatch_us_under_counters": round(dur_us, 2),
+               "int8_ops_per_dispatch": int(ops), "mfma_busy_cycles_per_simd": round(busy_simd, 1),
+               "grbm_gui_active_per_dispatch": round(mean("GRBM_GUI_ACTIVE"), 1)}
+        if dur_us > 0:
+            ent["mfma_busy_frac_of_dispatch"] = round(busy_simd / (dur_us * 1e3 * CLOCK_GHZ), 4)
+            ent["int8_TOPS_over_dispatch"] = round(ops / (dur_us * 1e-6) / 1e12, 1)
+        if busy_simd > 0:
+            ent["int8_ops_per_busy_cycle_per_simd"] = round(ops / (busy_simd * MI355X_CUS * SIMDS_PER_CU), 1)
+        out["kernels"].setdefault(short_name(name), []).append(ent)
+    with open(args.out, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -211,8 +260,12 @@ def main(argv=None):
     c.add_argument("--command-fetch", required=True)
     c.add_argument("--command-write", required=True)
     c.add_argument("--out", required=True)
+    m = sub.add_parser("mfma")
+    m.add_argument("--db", required=True)
+    m.add_argument("--command", required=True)
+    m.add_argument("--out", required=True)
     args = ap.parse_args(argv)
-    (cmd_stats if args.cmd == "stats" else cmd_counters)(args)
+    {"stats": cmd_stats, "counters": cmd_counters, "mfma": cmd_mfma}[args.cmd](args)
 
 
 if __name__ == "__main__":
