@@ -66,7 +66,7 @@ typedef enum dsa_dtype {
 #define DSA_MAX_BATCH 16
 #define DSA_MAX_K 4096
 #define DSA_MAX_INDEX_HEADS 64   /* Hi */
-#define DSA_MAX_INDEX_DIM 256    /* Di, a multiple of 32 */
+#define DSA_MAX_INDEX_DIM 256    /* Di, a multiple of 16 (larger: DSA_ERR_UNSUPPORTED) */
 #define DSA_MAX_ATTN_HEADS 64    /* Hq */
 #define DSA_MAX_ATTN_DIM 1024    /* Dk */
 
@@ -87,10 +87,22 @@ typedef struct dsa_row_stats {
   int32_t reserved;
 } dsa_row_stats;
 
-/* Human-readable name of a status code (static storage; never NULL). */
+/*
+ * Human-readable name and meaning of a status code (static storage; never NULL;
+ * unknown codes give a string naming them unknown). Every call reports a rejected
+ * argument as a code, never as a failure of the engine: the error discipline of the
+ * glm53-tensorfold-spark README ("What's new (W19)": malformed requests get a
+ * clean client error instead of an engine error; "What's new (2026-09-30)": patch
+ * 0490's OpenAI-style errors).
+ */
 const char* dsa_status_string(dsa_status status);
 
 /*
+ * The selection's working memory is sized once, up front, and reused by every call:
+ * the pre-grown selection scratch the glm53-tensorfold-spark README adopts in
+ * "What's new (W19)" (patch 0550, one pre-grown buffer instead of growth during
+ * the run).
+ *
  * Bytes of device workspace that dsa_topk_select, dsa_sparse_attn and
  * dsa_decode_step need for these sizes (B rows, N cached positions, k selected,
  * Hq attention heads, Dv output values per head). The caller allocates it (any
@@ -110,7 +122,9 @@ size_t dsa_workspace_size(int B, int64_t N, int k, int Hq, int Dv);
  *   ctx_len host [B]           1 <= ctx_len[b] <= N
  *   scores  [B][N]      int32  out: scores[b][s] for s < ctx_len[b]; the rest of
  *                              the row is left untouched
- * Limits: 1 <= B <= 16, 1 <= Hi <= 64, Di a multiple of 32 up to 256, N < 2^31.
+ * Limits: 1 <= B <= 16, N < 2^31, Di a multiple of 16 (else DSA_ERR_INVALID_ARG);
+ * Hi <= 64 and Di <= 256 are what the kernels are built for (beyond them:
+ * DSA_ERR_UNSUPPORTED).
  */
 dsa_status dsa_index_scores(const int8_t* iq, const int8_t* iw, const int8_t* ik,
                             const int32_t* ctx_len, int B, int Hi, int Di, int64_t N,
@@ -205,8 +219,14 @@ dsa_status dsa_decode_step_noalloc(const int8_t* iq, const int8_t* iw, const int
                                    hipStream_t stream);
 
 /*
- * Copies the per-row stats of the last call that used `ws` into stats[0..B).
- * Synchronises `stream` (call it outside timed regions).
+ * Copies the per-row stats of the last call that used `ws` into stats[0..B): which
+ * selection path each row took and why (the rising post's long-context paragraph:
+ * the narrowing scans handle the common case and the original algorithm the
+ * ambiguous ones), with the threshold score and its ties. Arguments: ws as passed
+ * to that call, ws_bytes its size (at least the stats region), B <= 16 rows,
+ * stats a HOST array of B records. DSA_ERR_INVALID_ARG for a null pointer or B out
+ * of range, DSA_ERR_WORKSPACE when ws_bytes cannot hold B records, DSA_ERR_HIP if
+ * the copy fails. Synchronises `stream` (call it outside timed regions).
  */
 dsa_status dsa_read_stats(const void* ws, size_t ws_bytes, int B, dsa_row_stats* stats,
                           hipStream_t stream);

@@ -12,8 +12,8 @@ Reads the rocpd SQLite databases that `rocprofv3 -d DIR -o NAME` writes
             --pmc run of SQ_INSTS_VALU_MFMA_MOPS_I8, SQ_VALU_MFMA_BUSY_CYCLES and
             GRBM_GUI_ACTIVE
 
-The counter summary records a hash of the kernel sources it was taken from; a
-reader treats it as stale once the sources change.
+The counter summary records a hash of the kernel sources (csrc/) it was taken from;
+a reader treats it as stale once they change.
 """
 import argparse
 import glob
@@ -25,8 +25,8 @@ import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KERNEL_SOURCES = sorted(
-    [os.path.relpath(p, ROOT) for p in glob.glob(os.path.join(ROOT, "sparse_attention_decode_scores_amd", "csrc", "*"))
-     if p.endswith((".hip", ".h"))] + ["include/dsa.h"])
+    os.path.relpath(p, ROOT) for p in glob.glob(os.path.join(ROOT, "sparse_attention_decode_scores_amd", "csrc", "*"))
+    if p.endswith((".hip", ".h")))
 LIB_KERNELS = ("k_score", "k_select", "k_combine", "k_chunk_cand", "k_attend_idx")
 COPY_MATCH = "neg_kernel"
 COPY_BYTES = 64 * 1024 * 1024 * 4  # read and written by one calibration dispatch
