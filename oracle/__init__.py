@@ -18,7 +18,7 @@ _LIB = os.path.join(_HERE, "liboracle_dsa.so")
 _LIB_OMP = os.path.join(_HERE, "liboracle_dsa_omp.so")  # the same source with -fopenmp
 _libs = {}
 
-F32, BF16 = 0, 1
+F32, BF16, BF16_Q_E4M3_KV = 0, 1, 2
 
 
 def build(force=True):
@@ -45,6 +45,8 @@ def _load(omp=False):
         lib.dsa_ref_sparse_attn.argtypes = [p, p, p, i32, i32, i32, i32, i64, i32, dbl, i32, p]
         lib.dsa_ref_decode_step.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32, i32,
                                             i64, i32, dbl, i32, p, p, p]
+        lib.dsa_ref_e4m3_to_f64.argtypes = [p, i64, p]
+        lib.dsa_ref_e4m3_to_f64.restype = None
         for f in (lib.dsa_ref_index_scores, lib.dsa_ref_topk_select, lib.dsa_ref_sparse_attn,
                   lib.dsa_ref_decode_step, lib.dsa_ref_threads):
             f.restype = ctypes.c_int
@@ -74,12 +76,25 @@ def _c(a, dtype):
     return a
 
 
-def _kv_dtype(a):
-    if a.dtype == np.float32:
+def _attn_dtype(q, kv):
+    """Attention input formats: fp32 both, bf16 both (uint16 bit patterns), or bf16 queries
+    with an FP8 E4M3 latent cache (uint8 codes)."""
+    if q.dtype == np.float32 and kv.dtype == np.float32:
         return F32
-    if a.dtype == np.uint16:  # bf16 bit patterns
+    if q.dtype == np.uint16 and kv.dtype == np.uint16:
         return BF16
-    raise TypeError("attention inputs must be float32 or bf16 bit patterns (uint16)")
+    if q.dtype == np.uint16 and kv.dtype == np.uint8:
+        return BF16_Q_E4M3_KV
+    raise TypeError("attention inputs: float32 q and kv, bf16 bits (uint16) q and kv, or bf16 q with "
+                    "e4m3 codes (uint8) kv; got %s and %s" % (q.dtype, kv.dtype))
+
+
+def e4m3_to_f64(codes):
+    """FP8 E4M3 (e4m3fn) codes (uint8) -> their exact values as float64 (NaN for 0x7F/0xFF)."""
+    codes = _c(codes, np.uint8)
+    out = np.empty(codes.shape, np.float64)
+    _load().dsa_ref_e4m3_to_f64(_ptr(codes), codes.size, _ptr(out))
+    return out
 
 
 def index_scores(iq, iw, ik, ctx_len, omp=False):
@@ -109,10 +124,8 @@ def topk_select(scores, ctx_len, k, omp=False):
 
 
 def sparse_attn(q, kv, idx, Dv, scale, omp=False):
-    """q [B,Hq,Dk], kv [N,Dk] (float32 or bf16 bits as uint16), idx [B,k] -> out [B,Hq,Dv] float64."""
-    dt = _kv_dtype(q)
-    if _kv_dtype(kv) != dt:
-        raise TypeError("q and kv must share a dtype")
+    """q [B,Hq,Dk], kv [N,Dk] (see _attn_dtype for the formats), idx [B,k] -> out [B,Hq,Dv] float64."""
+    dt = _attn_dtype(q, kv)
     q, kv, idx = np.ascontiguousarray(q), np.ascontiguousarray(kv), _c(idx, np.int32)
     B, Hq, Dk = q.shape
     N = kv.shape[0]
@@ -128,9 +141,7 @@ def decode_step(iq, iw, ik, q, kv, ctx_len, k, Dv, scale, omp=False):
     """All three stages; returns (scores [B,N] int32, idx [B,k] int32, out [B,Hq,Dv] float64)."""
     iq, iw, ik = _c(iq, np.int8), _c(iw, np.int8), _c(ik, np.int8)
     ctx_len = _c(ctx_len, np.int32)
-    dt = _kv_dtype(q)
-    if _kv_dtype(kv) != dt:
-        raise TypeError("q and kv must share a dtype")
+    dt = _attn_dtype(q, kv)
     q, kv = np.ascontiguousarray(q), np.ascontiguousarray(kv)
     B, Hi, Di = iq.shape
     _, Hq, Dk = q.shape

@@ -100,25 +100,53 @@ int dsa_ref_topk_select(const int32_t* scores, const int32_t* ctx_len, int B, in
   return REF_OK;
 }
 
-static inline double load_elem(const void* p, int dtype, int64_t i) {
-  if (dtype == 0) return (double)((const float*)p)[i];
+// One FP8 E4M3 value (the OCP 8-bit "e4m3fn" format: 1 sign, 4 exponent bits with
+// bias 7, 3 mantissa bits; no infinities; exponent and mantissa all ones is NaN),
+// decoded from its definition:
+//   exponent 0:   (-1)^s * m * 2^-9              (subnormal: m/8 * 2^(1-7))
+//   otherwise:    (-1)^s * (1 + m/8) * 2^(e-7)
+// Every such value is a double exactly. The pages name FP8 KV storage
+// (glm53-tensorfold-spark README, introduction: patch list) without fixing the
+// format; e4m3fn is the plainest reading for stored activations.
+static inline double e4m3_to_double(uint8_t v) {
+  const int s = v >> 7, e = (v >> 3) & 15, m = v & 7;
+  if (e == 15 && m == 7) return NAN;
+  const double mag = e == 0 ? std::ldexp((double)m, -9) : std::ldexp(1.0 + m / 8.0, e - 7);
+  return s ? -mag : mag;
+}
+
+// The decode of n codes, for the checks that pin it.
+void dsa_ref_e4m3_to_f64(const uint8_t* codes, int64_t n, double* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = e4m3_to_double(codes[i]);
+}
+
+static inline double bf16_to_double(uint16_t b) {
   // bf16: the 16 stored bits are the high half of an fp32.
-  uint32_t u = (uint32_t)((const uint16_t*)p)[i] << 16;
+  uint32_t u = (uint32_t)b << 16;
   float f;
   std::memcpy(&f, &u, 4);
   return (double)f;
 }
 
+// Element i of a query (kv = 0) or latent-cache (kv = 1) array of the given dtype:
+// 0 = fp32 both, 1 = bf16 both, 2 = bf16 queries with an FP8 E4M3 latent cache.
+static inline double load_elem(const void* p, int dtype, int kv, int64_t i) {
+  if (dtype == 0) return (double)((const float*)p)[i];
+  if (dtype == 2 && kv) return e4m3_to_double(((const uint8_t*)p)[i]);
+  return bf16_to_double(((const uint16_t*)p)[i]);
+}
+
 // out[(b*Hq + h)*Dv + v] (fp64) = sum_i p_i * kv[idx_i, v] / sum_i p_i with
 //   l_i = scale * sum_{d<Dk} q[b,h,d] * kv[idx_i, d],  p_i = exp(l_i - max_j l_j),
 // over the entries of idx[b, 0:k] that are not -1. K is the whole row (Dk values),
-// V is its first Dv values. dtype 0 = fp32 inputs, 1 = bf16 inputs.
+// V is its first Dv values. dtype 0 = fp32 inputs, 1 = bf16 inputs, 2 = bf16
+// queries with an FP8 E4M3 latent cache (decoded exactly).
 // A row with no valid entry gets zeros.
 int dsa_ref_sparse_attn(const void* q, const void* kv, const int32_t* idx, int B, int Hq,
                         int Dk, int Dv, int64_t N, int k, double scale, int dtype,
                         double* out) {
   if (B < 1 || Hq < 1 || Dk < 1 || Dv < 1 || Dv > Dk || N < 1 || k < 1) return REF_BAD_ARG;
-  if (dtype != 0 && dtype != 1) return REF_BAD_ARG;
+  if (dtype < 0 || dtype > 2) return REF_BAD_ARG;
   for (int b = 0; b < B; ++b) {
     std::vector<int64_t> rows;
     for (int j = 0; j < k; ++j) {
@@ -138,7 +166,7 @@ int dsa_ref_sparse_attn(const void* q, const void* kv, const int32_t* idx, int B
       for (size_t i = 0; i < rows.size(); ++i) {
         double dot = 0.0;
         for (int d = 0; d < Dk; ++d)
-          dot += load_elem(q, dtype, qoff + d) * load_elem(kv, dtype, rows[i] * Dk + d);
+          dot += load_elem(q, dtype, 0, qoff + d) * load_elem(kv, dtype, 1, rows[i] * Dk + d);
         logit[i] = scale * dot;
         mx = std::max(mx, logit[i]);
       }
@@ -146,7 +174,7 @@ int dsa_ref_sparse_attn(const void* q, const void* kv, const int32_t* idx, int B
       for (size_t i = 0; i < rows.size(); ++i) {
         double p = std::exp(logit[i] - mx);
         denom += p;
-        for (int v = 0; v < Dv; ++v) o[v] += p * load_elem(kv, dtype, rows[i] * Dk + v);
+        for (int v = 0; v < Dv; ++v) o[v] += p * load_elem(kv, dtype, 1, rows[i] * Dk + v);
       }
       for (int v = 0; v < Dv; ++v) o[v] /= denom;
     }

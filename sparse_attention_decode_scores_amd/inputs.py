@@ -23,6 +23,9 @@ is synthetic with the shapes of the model's DSA layers):
   ctx300k_tiepool   ctx300k with every key row drawn from a pool of 512 rows, so that
                     many positions share a score exactly (ties at the threshold).
   ctx16k_zeroquery  ctx16k with an all-zero indexer query: every score is 0.
+  ctx16k_fp8kv,     ctx16k and ctx300k (same seeds, so the same indexer inputs and
+  ctx300k_fp8kv     the same normal draws) with the latent cache stored as FP8 E4M3
+                    codes (round to nearest even from the fp32 draw) and bf16 queries.
   ctx16k_hotstride  ctx16k with the key rows of every 256th block of 32 positions
                     (positions 0-31 and 8,192-8,223) replaced by the indexer query of
                     row 0, head 0: those 64 positions tie at one score that only about
@@ -35,8 +38,8 @@ arrays are drawn from it in the order iq, iw, ik. The normal arrays are drawn in
 blocks of 16,384 rows, block j of q from ``default_rng([seed, 1, j])`` and of kv
 from ``default_rng([seed, 2, j])`` (so they can be drawn on several threads).
 
-bf16 values are carried as uint16 bit patterns (round to nearest even from the
-fp32 draw).
+bf16 values are carried as uint16 bit patterns and FP8 E4M3 (e4m3fn) values as uint8
+codes, each rounded to nearest even from the fp32 draw.
 """
 import numpy as np
 
@@ -53,6 +56,8 @@ CONFIGS = {
     "ctx300k_tiepool": dict(_LAYER, B=1, N=300000, k=2048, key_range=2, seed=1030, key_pool=512),
     "ctx16k_zeroquery": dict(_LAYER, B=1, N=16384, k=2048, seed=1090, zero_query=True),
     "ctx16k_hotstride": dict(_LAYER, B=1, N=16384, k=2048, seed=1091, hot_stride=256),
+    "ctx16k_fp8kv": dict(_LAYER, B=1, N=16384, k=2048, seed=1001, dtype="fp8"),
+    "ctx300k_fp8kv": dict(_LAYER, B=1, N=300000, k=2048, key_range=2, seed=1003, dtype="fp8"),
 }
 
 
@@ -76,6 +81,14 @@ def f32_to_bf16_bits(x):
         t >>= np.uint32(16)
         out[s:s + step] = t
     return out.reshape(x.shape)
+
+
+def f32_to_e4m3_codes(x):
+    """Round float32 values to FP8 E4M3 (e4m3fn; nearest, ties to even) and return the
+    uint8 codes (torch's conversion)."""
+    import torch
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    return torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
 
 
 def bf16_bits_to_f32(b):
@@ -112,7 +125,9 @@ def _normal(seed, tag, shape, dtype, mul):
             list(ex.map(fill, range(nblk)))
     else:
         fill(0)
-    return x if dtype == "f32" else f32_to_bf16_bits(x)
+    if dtype == "f32":
+        return x
+    return f32_to_e4m3_codes(x) if dtype == "e4m3" else f32_to_bf16_bits(x)
 
 
 def make(name, layer=0):
@@ -138,8 +153,9 @@ def make(name, layer=0):
         ik[blocks % c["hot_stride"] == 0] = iq[0, 0]
     mul = 1.0 if c["dtype"] == "f32" else 0.5
     seed = c["seed"] + layer
-    q = _normal(seed, 1, (B, Hq, Dk), c["dtype"], mul)
-    kv = _normal(seed, 2, (N, Dk), c["dtype"], mul)
+    qd, kvd = {"f32": ("f32", "f32"), "bf16": ("bf16", "bf16"), "fp8": ("bf16", "e4m3")}[c["dtype"]]
+    q = _normal(seed, 1, (B, Hq, Dk), qd, mul)
+    kv = _normal(seed, 2, (N, Dk), kvd, mul)
     c.update(iq=iq, iw=iw, ik=np.ascontiguousarray(ik), q=q, kv=kv, ctx_len=ctx_lengths(name),
              name=name, layer=layer)
     return c
@@ -153,8 +169,9 @@ def random_case(seed, B, N, k, Hi, Di, Hq, Dk, Dv, dtype="bf16", ctx_len=None, q
     iw = rng.integers(w_range[0], w_range[1] + 1, size=(B, Hi), dtype=np.int8)
     ik = rng.integers(-key_range, key_range + 1, size=(N, Di), dtype=np.int8)
     mul = 1.0 if dtype == "f32" else 0.5
-    q = _normal(seed, 1, (B, Hq, Dk), dtype, mul)
-    kv = _normal(seed, 2, (N, Dk), dtype, mul)
+    qd, kvd = {"f32": ("f32", "f32"), "bf16": ("bf16", "bf16"), "fp8": ("bf16", "e4m3")}[dtype]
+    q = _normal(seed, 1, (B, Hq, Dk), qd, mul)
+    kv = _normal(seed, 2, (N, Dk), kvd, mul)
     if ctx_len is None:
         ctx_len = np.full(B, N, np.int32)
     return dict(B=B, N=N, k=k, Hi=Hi, Di=Di, Hq=Hq, Dk=Dk, Dv=Dv, dtype=dtype,

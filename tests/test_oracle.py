@@ -223,6 +223,61 @@ def test_attention_matches_torch_sdpa_over_whole_context(dtype):
         assert np.abs(out[b] - ref).max() < 1e-12
 
 
+# ---------------------------------------------------------------- FP8 E4M3 latent cache
+
+def test_e4m3_decode_closed_forms():
+    # from the format's definition (1 sign, 4 exponent bits, bias 7, 3 mantissa bits,
+    # no infinities, all-ones exponent and mantissa = NaN)
+    v = oracle.e4m3_to_f64(np.array([0x00, 0x80, 0x01, 0x07, 0x08, 0x38, 0x3C, 0x40, 0x7E, 0xFE, 0xB8,
+                                     0x7F, 0xFF, 0x78], np.uint8))
+    assert v[0] == 0.0 and not np.signbit(v[0]) and v[1] == 0.0 and np.signbit(v[1])
+    assert v[2] == 2.0 ** -9 and v[3] == 7 * 2.0 ** -9       # subnormals m * 2^-9
+    assert v[4] == 2.0 ** -6                                 # smallest normal
+    assert v[5] == 1.0 and v[6] == 1.5 and v[7] == 2.0
+    assert v[8] == 448.0 and v[9] == -448.0 and v[10] == -1.0
+    assert np.isnan(v[11]) and np.isnan(v[12])
+    assert v[13] == 256.0                                    # exponent 15 is finite below m = 7
+
+
+def test_e4m3_decode_matches_torch_on_every_code():
+    torch = pytest.importorskip("torch")
+    codes = np.arange(256, dtype=np.uint8)
+    mine = oracle.e4m3_to_f64(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(mine), nan) and nan.sum() == 2
+    assert np.array_equal(mine[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(mine[~nan]), np.signbit(ref[~nan]))
+
+
+def test_fp8_cache_attention_equals_fp32_attention_on_the_decoded_values():
+    # bf16 queries and e4m3 cache codes are exact in fp32, so the fp8 path must equal
+    # the fp32 path given the decoded values, bit for bit
+    c = inputs.random_case(41, B=2, N=900, k=256, Hi=2, Di=16, Hq=5, Dk=96, Dv=64, dtype="fp8")
+    assert c["q"].dtype == np.uint16 and c["kv"].dtype == np.uint8
+    rng = np.random.default_rng(42)
+    idx = rng.choice(900, size=(2, 256), replace=False).astype(np.int32)
+    idx[1, 200:] = -1
+    out = oracle.sparse_attn(c["q"], c["kv"], idx, c["Dv"], c["scale"])
+    q32 = inputs.bf16_bits_to_f32(c["q"])
+    kv32 = oracle.e4m3_to_f64(c["kv"]).astype(np.float32)
+    assert np.array_equal(kv32.astype(np.float64), oracle.e4m3_to_f64(c["kv"]))
+    assert np.array_equal(out, oracle.sparse_attn(q32, kv32, idx, c["Dv"], c["scale"]))
+
+
+def test_fp8_workload_shares_the_bf16_workload_draws():
+    # ctx16k_fp8kv: the ctx16k seed, so the same indexer inputs and queries, and the
+    # cache is the e4m3 rounding of the same normal draws (within e4m3's half step)
+    a, b = inputs.make("ctx16k"), inputs.make("ctx16k_fp8kv")
+    for key in ("iq", "iw", "ik", "q"):
+        assert np.array_equal(a[key], b[key])
+    x = inputs.bf16_bits_to_f32(a["kv"][:2048]).astype(np.float64)
+    y = oracle.e4m3_to_f64(b["kv"][:2048])
+    # e4m3 rounds the draw within half a step (2^-4 relative, 2^-10 absolute below 2^-6),
+    # bf16 within 2^-9 relative
+    assert np.all(np.abs(y - x) <= np.abs(x) * (2.0 ** -4 + 2.0 ** -8) + 2.0 ** -10)
+
+
 def test_attention_permutation_invariance_and_minus_one_skipping():
     c = inputs.make("tiny_4k")
     rng = np.random.default_rng(4)
