@@ -25,8 +25,9 @@ Timings, all on the stream the library launches on:
     kernel's end, eager launch gaps included.)
   - legs: the forced exhaustive path on the headline workload (and the stand-alone
     exhaustive selection over every position, the path of rows without candidates),
-    the 62k-context 11-layer step and the 8-row verify block, each as graph
-    replays plus the eager kernel pass.
+    the 62k-context 11-layer step, the 8-row verify block and the headline workload
+    over an FP8 E4M3 latent cache (bf16 queries; the gather reads half the bytes),
+    each as graph replays plus the eager kernel pass.
   - cpu_baseline: the CPU oracle on the headline workload, single-threaded and with
     its all-core OpenMP build, per stage, median of 5 after one warm-up.
 
@@ -82,8 +83,13 @@ def device_set(torch, c, s):
             d[key] = torch.from_numpy(np.ascontiguousarray(c[key])).to(dev)
         for key in ("q", "kv"):
             a = np.ascontiguousarray(c[key])
-            d[key] = (torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if a.dtype == np.uint16
-                      else torch.from_numpy(a)).to(dev)
+            if a.dtype == np.uint16:  # bf16 bit patterns
+                t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+            elif a.dtype == np.uint8:  # FP8 E4M3 codes
+                t = torch.from_numpy(a).view(torch.float8_e4m3fn)
+            else:
+                t = torch.from_numpy(a)
+            d[key] = t.to(dev)
         return d
     g = torch.Generator(device=dev)
     g.manual_seed(9000 + 100 * s + c.get("layer", 0))
@@ -97,11 +103,22 @@ def device_set(torch, c, s):
     mul = 1.0 if c["dtype"] == "f32" else 0.5
     for key, shape in (("q", (c["B"], c["Hq"], c["Dk"])), ("kv", (c["N"], c["Dk"]))):
         x = torch.randn(shape, dtype=torch.float32, device=dev, generator=g) * mul
-        d[key] = x if c["dtype"] == "f32" else x.to(torch.bfloat16)
+        if c["dtype"] == "f32":
+            d[key] = x
+        elif c["dtype"] == "fp8" and key == "kv":
+            d[key] = x.to(torch.float8_e4m3fn)
+        else:
+            d[key] = x.to(torch.bfloat16)
     return d
 
 
 def esz(c):
+    """Bytes per latent-cache value."""
+    return {"f32": 4, "bf16": 2, "fp8": 1}[c["dtype"]]
+
+
+def qsz(c):
+    """Bytes per attention-query value."""
     return 4 if c["dtype"] == "f32" else 2
 
 
@@ -119,14 +136,14 @@ def score_kernel_bytes(c):
 def gather_pass_bytes(c):
     """Algorithmic bytes of one selection + attention pass: the k selected latent rows
     of every query row (Dk values each) and the attention queries."""
-    return rows_gathered(c) * c["Dk"] * esz(c) + c["B"] * c["Hq"] * c["Dk"] * esz(c)
+    return rows_gathered(c) * c["Dk"] * esz(c) + c["B"] * c["Hq"] * c["Dk"] * qsz(c)
 
 
 def step_essential_bytes(c):
     """Essential HBM bytes of one layer: keys once, the gathered rows, queries, head
     weights and the attention output (scores and indices are working data)."""
     return (c["N"] * c["Di"] + c["B"] * c["Hi"] * (c["Di"] + 1) + rows_gathered(c) * c["Dk"] * esz(c)
-            + c["B"] * c["Hq"] * c["Dk"] * esz(c) + c["B"] * c["Hq"] * c["Dv"] * 4)
+            + c["B"] * c["Hq"] * c["Dk"] * qsz(c) + c["B"] * c["Hq"] * c["Dv"] * 4)
 
 
 def indexer_int_ops(c):
@@ -277,7 +294,8 @@ class Runner:
 def describe(c, name, layers):
     return ("%s: %d cached positions, k=%d, %d query row(s), %d layer(s)/step; indexer %d heads x %d int8, "
             "one shared key per position; attention %d heads over a %d-value %s latent row (%d output values)"
-            % (name, c["N"], c["k"], c["B"], layers, c["Hi"], c["Di"], c["Hq"], c["Dk"], c["dtype"], c["Dv"]))
+            % (name, c["N"], c["k"], c["B"], layers, c["Hi"], c["Di"], c["Hq"], c["Dk"],
+               "fp8 e4m3 (bf16 queries)" if c["dtype"] == "fp8" else c["dtype"], c["Dv"]))
 
 
 def summary(t):
@@ -398,9 +416,9 @@ def main():
     ap.add_argument("--steps", type=int, default=240)
     ap.add_argument("--warmup", type=int, default=24)
     ap.add_argument("--config", default="ctx300k",
-                    choices=["ctx16k", "ctx62k_11layers", "ctx300k", "verify8_ctx131k"])
+                    choices=["ctx16k", "ctx62k_11layers", "ctx300k", "verify8_ctx131k", "ctx300k_fp8kv"])
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = default per workload)")
-    ap.add_argument("--legs", default="fallback,ctx62k_11layers,verify8_ctx131k",
+    ap.add_argument("--legs", default="fallback,ctx62k_11layers,verify8_ctx131k,ctx300k_fp8kv",
                     help="comma list of extra legs, or 'none'")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -502,7 +520,7 @@ def main():
 
     leg_out = {}
     for name in legs:
-        if name in ("ctx62k_11layers", "verify8_ctx131k") and name != args.config:
+        if name in ("ctx62k_11layers", "verify8_ctx131k", "ctx300k_fp8kv") and name != args.config:
             leg_out[name] = leg(torch, binding, name, max(16, K // 8), 4)
 
     cpu = None
@@ -531,7 +549,8 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8 indexer (int32 accumulate) + bf16 attention (fp32 accumulate)",
+        "dtype": ("int8 indexer (int32 accumulate) + bf16 attention (fp32 accumulate)"
+                  + (" over an FP8 E4M3 latent cache" if c["dtype"] == "fp8" else "")),
         "data": "synthetic (seeded; no model weights or caches)",
         "config": {"workload": describe(c, args.config, layers), "cache": cache,
                    "launch": "HIP graph replay of %d step(s) per graph" % R},

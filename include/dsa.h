@@ -58,8 +58,15 @@ typedef enum dsa_status {
 } dsa_status;
 
 typedef enum dsa_dtype {
-  DSA_F32 = 0,  /* q and kv hold float32 */
-  DSA_BF16 = 1  /* q and kv hold bfloat16 */
+  DSA_F32 = 0,      /* q and kv hold float32 */
+  DSA_BF16 = 1,     /* q and kv hold bfloat16 */
+  DSA_FP8_E4M3 = 2  /* q holds bfloat16; kv holds FP8 E4M3 ("e4m3fn": 1 sign, 4 exponent bits
+                       with bias 7, 3 mantissa bits, no infinities, 0x7F/0xFF NaN), one byte
+                       per value, no scale: the FP8 KV storage of the glm53-tensorfold-spark
+                       README (introduction, patch list); a per-tensor dequantisation scale
+                       folds into `scale` for K and into the output for V. Matrix-core
+                       path only: Dk a multiple of 32 up to 1024, Dv a multiple of 16 up to
+                       512, Hq <= 64 (else DSA_ERR_UNSUPPORTED) */
 } dsa_dtype;
 
 /* Limits checked by the validators. */
@@ -150,16 +157,17 @@ dsa_status dsa_topk_select(const int32_t* scores, const int32_t* ctx_len, int B,
  * Stage 3, attention over the selected positions only (rising post, long-context
  * paragraph; MQA fold of the MLX model card; latent KV cache of the TensorFold
  * README).
- *   q    [B][Hq][Dk]  dt       query heads of each row
+ *   q    [B][Hq][Dk]  dt       query heads of each row (bfloat16 for DSA_FP8_E4M3)
  *   kv   [N][Dk]      dt       latent cache: row i = [Dv latent values | Dk-Dv rope values];
- *                              K is the whole row, V its first Dv values
+ *                              K is the whole row, V its first Dv values (one byte per
+ *                              value for DSA_FP8_E4M3, 16-byte aligned rows: Dk % 16 == 0)
  *   idx  [B][k]       int32    positions to attend; -1 entries are skipped, and so are
  *                              (with a count in the row's stats) entries outside [0, N)
  *   out  [B][Hq][Dv]  float32  out: softmax(scale * q.K) @ V over the valid entries;
  *                              a row with no valid entry gets zeros
  *   ws, ws_bytes               at least dsa_workspace_size(B, N, k, Hq, Dv) bytes
- * Limits: 1 <= Hq <= 64, Dv <= Dk <= 1024, Dk and Dv multiples of 32 (bf16) or of
- * 4 (f32, Dk <= 256).
+ * Limits: 1 <= Hq <= 64, Dv <= Dk <= 1024, Dk and Dv multiples of 32 (bf16, fp8) or
+ * of 4 (f32, Dk <= 256).
  */
 dsa_status dsa_sparse_attn(const void* q, const void* kv, const int32_t* idx, int B, int Hq,
                            int Dk, int Dv, int64_t N, int k, float scale, dsa_dtype dt,

@@ -16,7 +16,7 @@ _LIB_PATH = os.path.join(_HERE, "libdsa.so")
 _lib = None
 
 FLAG_FORCE_FALLBACK = 1
-DSA_F32, DSA_BF16 = 0, 1
+DSA_F32, DSA_BF16, DSA_FP8_E4M3 = 0, 1, 2
 STATUS_NAMES = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED",
                 3: "DSA_ERR_WORKSPACE", 4: "DSA_ERR_HIP"}
 EXPORTED = ("dsa_status_string", "dsa_workspace_size", "dsa_index_scores", "dsa_topk_select",
@@ -116,14 +116,16 @@ def _check(rc, what):
 
 
 def _attn_dtype(q, kv):
+    """float32 q and kv, bfloat16 q and kv, or bfloat16 q with a float8_e4m3fn kv."""
     torch = _torch()
-    if q.dtype != kv.dtype:
-        raise TypeError("q and kv must share a dtype")
-    if q.dtype == torch.float32:
+    if q.dtype == torch.float32 and kv.dtype == torch.float32:
         return DSA_F32
-    if q.dtype == torch.bfloat16:
+    if q.dtype == torch.bfloat16 and kv.dtype == torch.bfloat16:
         return DSA_BF16
-    raise TypeError("q and kv must be float32 or bfloat16")
+    if q.dtype == torch.bfloat16 and kv.dtype == torch.float8_e4m3fn:
+        return DSA_FP8_E4M3
+    raise TypeError("q and kv: both float32, both bfloat16, or bfloat16 q with float8_e4m3fn kv; got %s "
+                    "and %s" % (q.dtype, kv.dtype))
 
 
 def dsa_workspace_size(B, N, k, Hq=1, Dv=1):

@@ -98,11 +98,13 @@ dsa_status check_attn(const void* q, const void* kv, int Hq, int Dk, int Dv, flo
   // valid: Hq >= 1, Dk a positive multiple of 8, 1 <= Dv <= Dk; built: Hq <= 64, Dk <= 1024
   if (!q || !kv) return DSA_ERR_INVALID_ARG;
   if (Hq < 1 || Dk < 8 || Dk % 8 != 0 || Dv < 1 || Dv > Dk) return DSA_ERR_INVALID_ARG;
-  if (dt != DSA_F32 && dt != DSA_BF16) return DSA_ERR_INVALID_ARG;
+  if (dt != DSA_F32 && dt != DSA_BF16 && dt != DSA_FP8_E4M3) return DSA_ERR_INVALID_ARG;
   if (!isfinite(scale)) return DSA_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(kv, 16)) return DSA_ERR_INVALID_ARG;
   if (Hq > DSA_MAX_ATTN_HEADS || Dk > DSA_MAX_ATTN_DIM) return DSA_ERR_UNSUPPORTED;
-  *ch = choose_attn(dt == DSA_BF16, Hq, Dk, Dv);
+  static_assert((int)DSA_F32 == DT_F32 && (int)DSA_BF16 == DT_BF16 && (int)DSA_FP8_E4M3 == DT_BF16_Q_E4M3_KV,
+                "dtype codes");
+  *ch = choose_attn((int)dt, Hq, Dk, Dv);
   if (ch->kind == ATTN_NONE) return DSA_ERR_UNSUPPORTED;
   if (select_lds_bytes(*ch, Hq, Dk, DSA_MAX_K) > (size_t)lds_limit()) return DSA_ERR_UNSUPPORTED;
   return DSA_OK;
@@ -382,7 +384,7 @@ dsa_status dsa_topk_select(const int32_t* scores, const int32_t* ctx_len, int B,
   const SelArgs sa = sel_args(scores, lens, N, k, idx, w, L, cp, have, flags);
   AttnArgs at{};
   at.S = 0;
-  return hip_status(launch_select(sa, at, AttnChoice{ATTN_NONE, 0, 0, 0}, B, stream));
+  return hip_status(launch_select(sa, at, AttnChoice{ATTN_NONE, 0, 0, 0, 0}, B, stream));
 }
 
 dsa_status dsa_sparse_attn(const void* q, const void* kv, const int32_t* idx, int B, int Hq, int Dk,

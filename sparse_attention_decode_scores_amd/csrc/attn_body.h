@@ -79,9 +79,15 @@ __device__ __forceinline__ void softmax_update_parts32(const float* lgp, int par
 // 16-byte row loads per thread per sub-block, is fitted to Dk by the caller: slots
 // past the sub-block re-read a present row, so spare slots are spare address work
 // on the latency-critical gather.
-template <int HQT, int SB, int NL = 9>
+// KV8: the latent cache holds FP8 E4M3 (e4m3fn) values, one byte each, widened to
+// bf16 as the gathered rows are staged (exact: every e4m3 value is a bf16 value), so
+// the gather reads half the bytes and everything after the staging is unchanged.
+// (FP8 KV storage: glm53-tensorfold-spark README, introduction, patch list.)
+template <int HQT, int SB, int NL = 9, bool KV8 = false>
 struct AttnMfma {
   static constexpr int HP = 16 * HQT;
+  static constexpr int kKvBytes = KV8 ? 1 : 2;  // bytes per cached value in memory
+  static constexpr int kLdsPerChunk = 16 / kKvBytes * 2;  // LDS bytes one 16-byte load stages
   static constexpr int kMaxTilesPerWave = 32 / kAttnWaves;  // Dv <= 512
   static constexpr int kMaxLoads = NL;                      // 16-byte loads per thread per sub-block
   static constexpr int kLogitBatch = HQT == 1 ? 6 : (HQT == 2 ? 4 : 2);  // k-steps loaded together
@@ -112,17 +118,17 @@ struct AttnMfma {
     QFrag f;
     {
       // gather slot j of this thread is chunk i = tid + 512 j of a sub-block: row
-      // i / cpr, 16-byte column i % cpr, stepped without dividing (a divide by a
-      // runtime value costs dozens of instructions); worked out here, before the
-      // positions are known
-      const int cpr = p.Dk >> 3;
+      // i / cpr, 16-byte column i % cpr of the cached row, stepped without dividing
+      // (a divide by a runtime value costs dozens of instructions); worked out
+      // here, before the positions are known
+      const int cpr = p.Dk * kKvBytes / 16;
       const int step_r = kAttnBlock / cpr, step_c = kAttnBlock - step_r * cpr;
       int r = (int)threadIdx.x / cpr, c = (int)threadIdx.x - r * cpr;
 #pragma unroll
       for (int j = 0; j < kMaxLoads; ++j) {
         f.rr[j] = r;
         f.cc[j] = c;
-        f.lo[j] = r * row_bytes(p.Dk) + 16 * c;
+        f.lo[j] = r * row_bytes(p.Dk) + kLdsPerChunk * c;
         c += step_c;
         r += step_r;
         if (c >= cpr) {
@@ -205,7 +211,8 @@ struct AttnMfma {
     for (int j = 0; j < kMaxLoads; ++j) rp[j] = (int32_t)pos_at(qf.rr[j] < nr ? qf.rr[j] : nr - 1);
     Rows r;
 #pragma unroll
-    for (int j = 0; j < kMaxLoads; ++j) r.v[j] = *(const v4i*)(kv + ((int64_t)rp[j] * p.Dk + 8 * qf.cc[j]) * 2);
+    for (int j = 0; j < kMaxLoads; ++j)
+      r.v[j] = *(const v4i*)(kv + (int64_t)rp[j] * p.Dk * kKvBytes + 16 * qf.cc[j]);
     return r;
   }
   // Stores gathered rows (absent rows as zeros) and, with `with_q`, the query heads;
@@ -213,12 +220,35 @@ struct AttnMfma {
   __device__ __forceinline__ static void put(const Rows& r, const QFrag& qf, const AttnArgs& p, int nr, bool with_q,
                              uint8_t* work) {
     const Work w = work_of(p, work);
-    const int rb = row_bytes(p.Dk), nch = SB * (p.Dk >> 3);  // nch <= kMaxLoads * block size
+    const int nch = SB * (p.Dk * kKvBytes / 16);  // nch <= kMaxLoads * block size
     if (with_q) store_q(qf, p, work);
 #pragma unroll
     for (int j = 0; j < kMaxLoads; ++j)
-      if ((int)threadIdx.x + kAttnBlock * j < nch)
-        *(v4i*)(w.rows + qf.lo[j]) = qf.rr[j] < nr ? r.v[j] : v4i{0, 0, 0, 0};
+      if ((int)threadIdx.x + kAttnBlock * j < nch) {
+        const v4i v = qf.rr[j] < nr ? r.v[j] : v4i{0, 0, 0, 0};
+        if constexpr (KV8) {
+          // 16 e4m3 values -> 16 bf16 values (the hardware's conversion with scale 1:
+          // exact, NaN codes to NaN), in order
+          v4i lo, hi;
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)v[d], 1.0f, false);
+            const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)v[d], 1.0f, true);
+            const int ia = __builtin_bit_cast(int, a), ib = __builtin_bit_cast(int, b);
+            if (d < 2) {
+              lo[2 * d] = ia;
+              lo[2 * d + 1] = ib;
+            } else {
+              hi[2 * d - 4] = ia;
+              hi[2 * d - 3] = ib;
+            }
+          }
+          *(v4i*)(w.rows + qf.lo[j]) = lo;
+          *(v4i*)(w.rows + qf.lo[j] + 16) = hi;
+        } else {
+          *(v4i*)(w.rows + qf.lo[j]) = v;
+        }
+      }
   }
   __device__ __forceinline__ static void begin(const AttnArgs& p, uint8_t* work, Acc& o) {
     const Work w = work_of(p, work);

@@ -17,6 +17,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 // Storage slot of entry u of a row's candidate union (kCandCap entries per row).
 // The selection kernel's thread t (of 512) holds entries 16t .. 16t + 15 and reads

@@ -140,10 +140,14 @@ struct AttnChoice {
   AttnKind kind;
   int hqt;   // 16-head tiles (MFMA path)
   int sb;    // rows staged per sub-block
-  int nl;    // MFMA path: 16-byte row loads per thread per sub-block (5 or 9)
+  int nl;    // MFMA path: 16-byte row loads per thread per sub-block (bf16: 5 or 9; fp8: 3 or 5)
+  int kv8;   // MFMA path: the latent cache holds FP8 E4M3 values (queries bf16)
 };
 
-AttnChoice choose_attn(int dt_bf16, int Hq, int Dk, int Dv);
+// Attention input formats (the values of dsa_dtype).
+enum AttnDtype { DT_F32 = 0, DT_BF16 = 1, DT_BF16_Q_E4M3_KV = 2 };
+
+AttnChoice choose_attn(int dt, int Hq, int Dk, int Dv);
 // LDS bytes of one workgroup of the selection kernel (largest of the two roles).
 size_t select_lds_bytes(AttnChoice ch, int Hq, int Dk, int k);
 hipError_t launch_select(const SelArgs& a, const AttnArgs& at, AttnChoice ch, int B, hipStream_t s,

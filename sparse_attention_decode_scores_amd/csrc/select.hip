@@ -1309,20 +1309,27 @@ static hipError_t launch_attend_t(const int32_t* idx, int k, int32_t* part_bad, 
 
 // ------------------------------------------------------------------ dispatch
 
-AttnChoice choose_attn(int dt_bf16, int Hq, int Dk, int Dv) {
-  AttnChoice c{ATTN_NONE, 0, 0, 0};
-  if (dt_bf16 && Hq >= 1 && Hq <= 64 && Dk % 32 == 0 && Dk <= 1024 && Dv % 16 == 0 && Dv <= 512 &&
+AttnChoice choose_attn(int dt, int Hq, int Dk, int Dv) {
+  AttnChoice c{ATTN_NONE, 0, 0, 0, 0};
+  if (dt != DT_F32 && Hq >= 1 && Hq <= 64 && Dk % 32 == 0 && Dk <= 1024 && Dv % 16 == 0 && Dv <= 512 &&
       Dv <= Dk) {
     c.kind = ATTN_MFMA_BF16;
     c.hqt = (Hq + 15) / 16;
     c.sb = 32;  // a split's 32 rows form one sub-block
+    if (dt == DT_BF16_Q_E4M3_KV) {
+      // one gather pass of 16-byte loads over Dk-byte rows: three per thread cover
+      // Dk <= 768 (the 576-value latent row), five Dk <= 1024
+      c.kv8 = 1;
+      c.nl = c.hqt == 1 && (Dk / 16) * c.sb <= AttnMfma<1, 32, 3, true>::kMaxLoads * kAttnBlock ? 3 : 5;
+      return c;
+    }
     // one gather pass; five loads per thread cover Dk <= 640 (the 576-value latent row)
     c.nl = c.hqt == 1 && (Dk / 8) * c.sb <= AttnMfma<1, 32, 5>::kMaxLoads * kAttnBlock ? 5 : 9;
     if ((Dk / 8) * c.sb <= AttnMfma<1, 32>::kMaxLoads * kAttnBlock) return c;
-    c = AttnChoice{ATTN_NONE, 0, 0, 0};
+    c = AttnChoice{ATTN_NONE, 0, 0, 0, 0};
   }
-  if (Hq >= 1 && Hq * Dv <= 4096 && Dk <= 512 && Dv <= Dk) {
-    c.kind = dt_bf16 ? ATTN_GENERIC_BF16 : ATTN_GENERIC_F32;
+  if (dt != DT_BF16_Q_E4M3_KV && Hq >= 1 && Hq * Dv <= 4096 && Dk <= 512 && Dv <= Dk) {
+    c.kind = dt == DT_BF16 ? ATTN_GENERIC_BF16 : ATTN_GENERIC_F32;
     c.sb = AttnGeneric<float>::SB;
   }
   return c;
@@ -1334,6 +1341,17 @@ AttnChoice choose_attn(int dt_bf16, int Hq, int Dk, int Dv) {
     case ATTN_GENERIC_F32: return FN<AttnGeneric<float>>(__VA_ARGS__);                 \
     case ATTN_GENERIC_BF16: return FN<AttnGeneric<uint16_t>>(__VA_ARGS__);             \
     case ATTN_MFMA_BF16:                                                               \
+      if (ch.kv8) {                                                                    \
+        switch (ch.hqt) {                                                              \
+          case 1:                                                                      \
+            if (ch.nl == 3) return FN<AttnMfma<1, 32, 3, true>>(__VA_ARGS__);          \
+            return FN<AttnMfma<1, 32, 5, true>>(__VA_ARGS__);                          \
+          case 2: return FN<AttnMfma<2, 32, 5, true>>(__VA_ARGS__);                    \
+          case 3: return FN<AttnMfma<3, 32, 5, true>>(__VA_ARGS__);                    \
+          case 4: return FN<AttnMfma<4, 32, 5, true>>(__VA_ARGS__);                    \
+        }                                                                              \
+        break;                                                                         \
+      }                                                                                \
       switch (ch.hqt) {                                                                \
         case 1:                                                                        \
           if (ch.nl == 5) return FN<AttnMfma<1, 32, 5>>(__VA_ARGS__);                  \
@@ -1342,6 +1360,8 @@ AttnChoice choose_attn(int dt_bf16, int Hq, int Dk, int Dv) {
         case 3: return FN<AttnMfma<3, 32>>(__VA_ARGS__);                               \
         case 4: return FN<AttnMfma<4, 32>>(__VA_ARGS__);                               \
       }                                                                                \
+      break;                                                                           \
+    default: break;                                                                    \
   }                                                                                    \
   return hipErrorInvalidValue;
 

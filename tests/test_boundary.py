@@ -113,6 +113,12 @@ def test_attention_validation(lib):
     assert attn_call(lib, Hq=64, Dk=1000, Dv=500) == UNSUPPORTED
     assert attn_call(lib, Hq=65) == UNSUPPORTED and attn_call(lib, Dk=2048, Dv=512) == UNSUPPORTED
     assert attn_call(lib, ws_bytes=100) == WORKSPACE
+    # bf16 queries with an FP8 E4M3 cache (dt 2): matrix-core shapes only; a valid shape
+    # passes validation and stops at the short workspace (nothing is launched)
+    assert attn_call(lib, dt=2, ws_bytes=100) == WORKSPACE
+    assert attn_call(lib, dt=2, Hq=6, Dk=80, Dv=40) == UNSUPPORTED
+    assert attn_call(lib, dt=2, Hq=65) == UNSUPPORTED
+    assert attn_call(lib, dt=3) == INVALID
 
 
 def test_decode_step_validation(lib):

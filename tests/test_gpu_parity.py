@@ -49,8 +49,10 @@ def dev_inputs(torch, c):
         d[key] = torch.from_numpy(np.ascontiguousarray(c[key])).cuda()
     for key in ("q", "kv"):
         a = np.ascontiguousarray(c[key])
-        if a.dtype == np.uint16:
+        if a.dtype == np.uint16:  # bf16 bit patterns
             d[key] = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        elif a.dtype == np.uint8:  # FP8 E4M3 codes
+            d[key] = torch.from_numpy(a).view(torch.float8_e4m3fn).cuda()
         else:
             d[key] = torch.from_numpy(a).cuda()
     return d
@@ -101,7 +103,7 @@ def expected_ties(ref_scores, ref_idx, ctx_len, k):
 
 
 @pytest.mark.parametrize("name", ["tiny_4k", "ctx16k", "ctx300k", "verify8_ctx131k", "ctx300k_tiepool",
-                                  "ctx16k_zeroquery", "ctx16k_hotstride"])
+                                  "ctx16k_zeroquery", "ctx16k_hotstride", "ctx16k_fp8kv", "ctx300k_fp8kv"])
 def test_decode_step_matches_oracle(torch, dsa, name):
     note("decode_step", name)
     c, (rs, ri, ro) = case(name)
@@ -146,7 +148,7 @@ def bits_equal(a, b):
 
 
 @pytest.mark.parametrize("name", ["ctx16k", "ctx300k", "ctx300k_tiepool", "verify8_ctx131k", "ctx16k_zeroquery",
-                                  "ctx16k_hotstride"])
+                                  "ctx16k_hotstride", "ctx300k_fp8kv"])
 def test_forced_fallback_matches_fast_path(torch, dsa, name):
     # The exhaustive path selects the same positions in the same order, and attention
     # split s takes the positions of output slots [s*per, (s+1)*per) on either path,
@@ -173,7 +175,7 @@ def test_forced_fallback_matches_fast_path(torch, dsa, name):
                                                                      b["tied_at_kth"])
 
 
-@pytest.mark.parametrize("name", ["ctx16k", "ctx300k", "verify8_ctx131k", "ctx16k_hotstride"])
+@pytest.mark.parametrize("name", ["ctx16k", "ctx300k", "verify8_ctx131k", "ctx16k_hotstride", "ctx16k_fp8kv"])
 def test_decode_step_matches_attention_over_its_indices(torch, dsa, name):
     # dsa_sparse_attn over the step's own ordered indices splits them the same way
     # (slots [s*per, (s+1)*per) per split), so it returns the step's output bit for bit.
@@ -367,6 +369,13 @@ EDGE = [
     ("di-48-one-row", dict(B=1, N=30000, k=1024, Hi=24, Di=48, Hq=4, Dk=64, Dv=64)),
     ("di-80-rows", dict(B=3, N=12000, k=700, Hi=64, Di=80, Hq=16, Dk=576, Dv=512, ctx_len=[12000, 9000, 50])),
     ("di-16", dict(B=1, N=5000, k=256, Hi=1, Di=16, Hq=1, Dk=32, Dv=32)),
+    # FP8 E4M3 latent cache with bf16 queries: every matrix-core tiling (one to four
+    # 16-head tiles; three or five 16-byte loads per thread) and rows of 32 bytes
+    ("fp8-hq64-k4096", dict(B=1, N=50000, k=4096, Hi=64, Di=128, Hq=64, Dk=576, Dv=512, dtype="fp8")),
+    ("fp8-dk1024", dict(B=2, N=20000, k=1000, Hi=32, Di=64, Hq=16, Dk=1024, Dv=512, dtype="fp8")),
+    ("fp8-hq40-rows", dict(B=3, N=9000, k=2048, Hi=64, Di=128, Hq=40, Dk=192, Dv=128, dtype="fp8",
+                           ctx_len=[9000, 4500, 7])),
+    ("fp8-dk32", dict(B=1, N=5000, k=256, Hi=4, Di=32, Hq=1, Dk=32, Dv=32, dtype="fp8")),
 ]
 
 
