@@ -18,13 +18,20 @@ inline size_t up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
 
 // Attention splits per row: 64 selected rows per split on the vector-ALU paths;
 // 32 on the matrix-core path (more workgroups, each with half the serial work).
-int splits_for(int k, bool mfma = false) {
-  if (mfma) {
-    const int s = (k + 31) / 32;
-    return s < 1 ? 1 : (s > kMaxWideSplits ? kMaxWideSplits : s);
+// With B rows, the count is halved (each split taking twice the rows, at most
+// kMaxSplitRows) while the B rows' splits would exceed kSplitGrid workgroups: a
+// split's rows are a serial loop, and a second round of workgroups costs more
+// than a longer loop (one workgroup per compute unit fits the selection's LDS).
+int splits_for(int k, bool mfma = false, int B = 1) {
+  int s = mfma ? (k + 31) / 32 : (k + 63) / 64;
+  const int cap = mfma ? kMaxWideSplits : kMaxSplits;
+  s = s < 1 ? 1 : (s > cap ? cap : s);
+  while (s > 1 && s * B > kSplitGrid) {
+    const int h = (s + 1) / 2;
+    if ((k + h - 1) / h > kMaxSplitRows) break;
+    s = h;
   }
-  const int s = (k + 63) / 64;
-  return s < 1 ? 1 : (s > kMaxSplits ? kMaxSplits : s);
+  return s;
 }
 int rankers_for(int k) {
   int r = (k + 15) / 16;
@@ -274,9 +281,9 @@ AttnArgs attn_args(const void* q, const void* kv, int64_t N, int Hq, int Dk, int
 }
 
 // Split count and partial layout for the chosen attention path.
-void set_attn_path(AttnArgs* at, const AttnChoice& ch, int k) {
+void set_attn_path(AttnArgs* at, const AttnChoice& ch, int k, int B) {
   at->frag = ch.kind == ATTN_MFMA_BF16;
-  at->S = splits_for(k, at->frag != 0);
+  at->S = splits_for(k, at->frag != 0, B);
 }
 
 hipError_t combine(const AttnArgs& at, const int32_t* part_bad, RowStats* stats, float* out, int B,
@@ -399,7 +406,7 @@ dsa_status dsa_sparse_attn(const void* q, const void* kv, const int32_t* idx, in
   if ((st = check_ws(ws, ws_bytes, L)) != DSA_OK) return st;
   uint8_t* w = static_cast<uint8_t*>(ws);
   AttnArgs at = attn_args(q, kv, N, Hq, Dk, Dv, scale, k, w, L);
-  set_attn_path(&at, ch, k);
+  set_attn_path(&at, ch, k, B);
   int32_t* bad = reinterpret_cast<int32_t*>(w + L.bad);
   if (launch_attend_idx(idx, k, bad, at, ch, B, stream) != hipSuccess) return DSA_ERR_HIP;
   return hip_status(combine(at, bad, reinterpret_cast<RowStats*>(w + L.stats), out, B, stream));
@@ -439,9 +446,12 @@ dsa_status dsa_decode_step_timed(const int8_t* iq, const int8_t* iw, const int8_
                   reinterpret_cast<uint64_t*>(w + L.cand), reinterpret_cast<uint64_t*>(w + L.xc),
                   stream, tm[0], sums ? reinterpret_cast<ChunkSum*>(w + L.sums) : nullptr);
   if (st != DSA_OK) return st;
-  const SelArgs sa = sel_args(scores, lens, N, k, idx, w, L, cp, have, flags, sums);
+  SelArgs sa = sel_args(scores, lens, N, k, idx, w, L, cp, have, flags, sums);
+  // no ranking workgroups: the attention splits' windows are the output slots, so
+  // they write the indices and the row's record themselves
+  sa.R = 0;
   AttnArgs at = attn_args(q, kv, N, Hq, Dk, Dv, scale, k, w, L);
-  set_attn_path(&at, ch, k);
+  set_attn_path(&at, ch, k, B);
   if (launch_select(sa, at, ch, B, stream, tm[1]) != hipSuccess) return DSA_ERR_HIP;
   return hip_status(combine(at, nullptr, nullptr, out, B, stream, tm[2]));
 }

@@ -12,6 +12,11 @@ constexpr int kMaxChunks = 256;
 constexpr int kMaxSplits = 32;         // attention splits per row (vector-ALU attention)
 constexpr int kMaxWideSplits = 128;    // attention splits per row (matrix-core attention)
 constexpr int kMaxRankBlocks = 128;
+constexpr int kMaxSplitRows = 128;     // selected rows one attention split may take
+// Rows of a batch share one launch: their splits together aim at one workgroup per
+// compute unit of the chip (256 on gfx950). A constant, not the device's count, so
+// that the split of the sum, and with it every rounding, is the same on any device.
+constexpr int kSplitGrid = 256;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));

@@ -80,7 +80,7 @@ int chunk_cand_max_chunk() { return kChunkPerThread * kSelBlock; }
 // ranked among themselves instead of narrowed further.
 constexpr uint32_t kMaxBinRank = 256;
 constexpr int kBinPad = 16;       // LDS slots before the bin's keys (split_sorted's base may point there)
-constexpr int kMaxWindow = 128;   // selected positions per attention split (at most ceil(4096 / 32))
+constexpr int kMaxWindow = kMaxSplitRows;  // selected positions per attention split
 // keys gathered around an attention window: the bins of its two ends and the keys between
 constexpr int kMaxWindowList = 2 * (int)kMaxBinRank + kMaxWindow;
 // Exhaustive path: positions sampled for a threshold, and the keys at or above it that
@@ -328,6 +328,8 @@ __device__ __forceinline__ void union_range_exchange(const uint64_t (&key)[E], c
 struct KeyRange {
   uint64_t klo, khi;
   uint32_t above, inbin;
+  uint32_t gt;  // keys of a higher score than every key of the range (= above unless tie)
+  bool tie;     // the range is a run of positions within one score value
 };
 
 // The kk best of the nvalid valid keys held E per thread (score bits sv in [lo, hi];
@@ -875,9 +877,11 @@ __device__ __forceinline__ KeyRange refine_key_range(RadixBin rb, uint32_t need,
         if (((vmask >> j) & 1u) && sv[j] == T) f((uint32_t)key[j]);
     };
     const RadixBin rt = block_narrow<kSelBlock>(each_tie, 0u, 0xFFFFFFFFu, need - rb.above, rb.inbin, kMaxBinRank, sm);
-    return KeyRange{((uint64_t)T << 32) | rt.binlo, ((uint64_t)T << 32) | rt.binhi, rb.above + rt.above, rt.inbin};
+    return KeyRange{((uint64_t)T << 32) | rt.binlo, ((uint64_t)T << 32) | rt.binhi, rb.above + rt.above, rt.inbin,
+                    rb.above, true};
   }
-  return KeyRange{(uint64_t)rb.binlo << 32, ((uint64_t)rb.binhi << 32) | 0xFFFFFFFFull, rb.above, rb.inbin};
+  return KeyRange{(uint64_t)rb.binlo << 32, ((uint64_t)rb.binhi << 32) | 0xFFFFFFFFull, rb.above, rb.inbin, rb.above,
+                  false};
 }
 
 // Attention window: of the n valid keys held E per thread (score bits sv, all in
@@ -890,12 +894,16 @@ __device__ __forceinline__ KeyRange refine_key_range(RadixBin rb, uint32_t need,
 // the G dropped keys xc[0, G) (for the candidate path's coverage check). Those are
 // requested here and exchanged and counted behind the narrowing, on its barriers:
 // a load still in flight where the caller's paths join is waited for there.
+// When the window ends at rank kk - 1 (the last selected key), sm.kstar gets that
+// key K* and sm.tied the number of selected keys with its score T: K* and the keys
+// above it at T, which are collected keys (counted beside the ranks) or, when the
+// upper end's range is a run of positions at T, the keys at T above that range.
 template <int E>
 __device__ __forceinline__ uint32_t window_positions(const uint64_t (&key)[E], const uint32_t (&sv)[E],
                                                      uint32_t vmask, uint32_t n, uint32_t lo, uint32_t hi,
                                                      bool sorted, bool count_mx, const uint64_t* __restrict__ xc,
-                                                     int G, uint32_t r0, uint32_t r1, uint64_t* wl, uint64_t* sink,
-                                                     SelSmem& sm) {
+                                                     int G, uint32_t r0, uint32_t r1, uint32_t kk, uint64_t* wl,
+                                                     uint64_t* sink, SelSmem& sm) {
   // one dropped key per thread (clamped address; threads past G count 0)
   const uint64_t mx = count_mx ? xc[threadIdx.x < (unsigned)G ? threadIdx.x : G - 1] : 0ull;
   const uint32_t need[2] = {r0 + 1, r1 + 1};
@@ -957,10 +965,12 @@ __device__ __forceinline__ uint32_t window_positions(const uint64_t (&key)[E], c
   // rank of a collected key = top.above + number of collected keys above it; eight
   // threads per key, four reads in flight each
   const int grp = threadIdx.x >> 3, part = threadIdx.x & 7;
+  const bool last = r1 + 1 == kk;  // uniform
   for (uint32_t b0 = 0; b0 < nw; b0 += kSelBlock / 8) {
     const uint32_t i = b0 + (uint32_t)grp;
     const uint64_t me = i < nw ? wl[i] : ~0ull;
-    uint32_t r = 0;
+    const uint32_t mes = key_ubits(me);
+    uint32_t r = 0, eq = 0;  // collected keys above me; those of them with me's score
     for (uint32_t j0 = (uint32_t)part; j0 < nw; j0 += 32) {
       uint64_t v[4];
 #pragma unroll
@@ -969,13 +979,31 @@ __device__ __forceinline__ uint32_t window_positions(const uint64_t (&key)[E], c
         v[u] = wl[jj < nw ? jj : nw - 1];
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) r += (j0 + 8 * u < nw && v[u] > me) ? 1u : 0u;
+      for (int u = 0; u < 4; ++u) {
+        const bool above_me = j0 + 8 * u < nw && v[u] > me;
+        r += above_me ? 1u : 0u;
+        if (last) eq += above_me && key_ubits(v[u]) == mes ? 1u : 0u;
+      }
     }
     r += (uint32_t)__builtin_amdgcn_mov_dpp((int)r, dpp::kQuadXor1, 0xF, 0xF, false);
     r += (uint32_t)__builtin_amdgcn_mov_dpp((int)r, dpp::kQuadXor2, 0xF, 0xF, false);
     r += (uint32_t)__builtin_amdgcn_mov_dpp((int)r, dpp::kRowHalfMirror, 0xF, 0xF, false);
+    if (last) {
+      eq += (uint32_t)__builtin_amdgcn_mov_dpp((int)eq, dpp::kQuadXor1, 0xF, 0xF, false);
+      eq += (uint32_t)__builtin_amdgcn_mov_dpp((int)eq, dpp::kQuadXor2, 0xF, 0xF, false);
+      eq += (uint32_t)__builtin_amdgcn_mov_dpp((int)eq, dpp::kRowHalfMirror, 0xF, 0xF, false);
+    }
     const uint32_t gr = top.above + r;
-    if (part == 0 && i < nw && gr >= r0 && gr <= r1) sm.winpos[gr - r0] = key_pos(me);
+    if (part == 0 && i < nw && gr >= r0 && gr <= r1) {
+      sm.winpos[gr - r0] = key_pos(me);
+      if (gr + 1 == kk) {
+        // keys at T above the upper end's range: only when that range is a run of
+        // positions at T (a range of scores has only higher scores above it)
+        const uint32_t at_t_above = top.tie && key_ubits(top.khi) == mes ? top.above - top.gt : 0u;
+        sm.kstar = me;
+        sm.tied = 1u + eq + at_t_above;
+      }
+    }
   }
   lds_barrier();
   uint32_t gt = 0;
@@ -1015,8 +1043,8 @@ __device__ __noinline__ void exhaustive_window(const SelectKernArgs* ka, int b, 
     bool sorted;
     union_range_exchange<kUPerThread>(key, sv, vmask, sm, rng, &sorted);
   }
-  window_positions<kUPerThread>(key, sv, vmask, total, rng[0], rng[1], false, false, nullptr, 0, r0, r1, l.list,
-                                l.sink, sm);
+  window_positions<kUPerThread>(key, sv, vmask, total, rng[0], rng[1], false, false, nullptr, 0, r0, r1,
+                                (uint32_t)kk, l.list, l.sink, sm);
 }
 
 // The kernel's argument segment, as the exhaustive path reads it.
@@ -1137,7 +1165,7 @@ __global__ __launch_bounds__(kSelBlock) void k_select(const uint64_t* __restrict
       }
       const uint32_t above_mx =
           window_positions<kUPerThread>(key, sv, vmask, nvalid, rng[0], rng[1], sorted, true, xc + (int64_t)b * G,
-                                        G, (uint32_t)r0, (uint32_t)(r0 + cnt - 1), list, sink, sm);
+                                        G, (uint32_t)r0, (uint32_t)(r0 + cnt - 1), (uint32_t)kk, list, sink, sm);
       // the union's top kk are the row's when at least kk of its keys lie above every
       // dropped key (nvalid >= kk here, and a union with fewer than k valid keys then
       // holds every position and dropped none)
@@ -1147,6 +1175,23 @@ __global__ __launch_bounds__(kSelBlock) void k_select(const uint64_t* __restrict
       exhaustive_window(kernel_args(), b, (uint32_t)r0, (uint32_t)(r0 + cnt - 1));
     // sm.winpos is complete and published (the last barrier of the window
     // narrowing follows its last write), and the LDS region is free again
+    if (a.R == 0) {  // uniform: no ranking workgroups; the windows are the output
+      // slots [r0, r0 + per) of the row: the window's positions, then -1 past kk
+      int32_t* out = a.idx + (int64_t)b * a.k;
+      for (int i = tid; i < per && r0 + i < a.k; i += kSelBlock) out[r0 + i] = i < cnt ? (int32_t)sm.winpos[i] : -1;
+      if (cnt > 0 && r0 + cnt == kk && tid == 0) {  // the window of the kk-th best key
+        RowStats st;
+        st.path = reason == 0 ? 0 : 1;
+        st.reason = reason;
+        st.selected = kk;
+        st.kth_score = key_score(sm.kstar);
+        st.candidates = (int32_t)nvalid;
+        st.tied_at_kth = (int32_t)sm.tied;
+        st.bad_indices = 0;
+        st.reserved = 0;
+        a.stats[b] = st;
+      }
+    }
     Attn::run(at, b, blockIdx.x, [&](int i) { return (int64_t)sm.winpos[i]; }, cnt, region, qf);
     return;
   }

@@ -86,8 +86,12 @@ def check_scores(gpu, ref, ctx_len, what):
 
 def run_step(torch, dsa, c, d, flags=0):
     ws = dsa.new_workspace(c["B"], c["N"], c["k"], c["Hq"], c["Dv"])
+    # every index slot and row record must be written by the call: start from values
+    # no call leaves (the records are the workspace's first B x 32 bytes)
+    ws[:32 * c["B"]].fill_(0x5A)
+    idx = torch.full((c["B"], c["k"]), -7, dtype=torch.int32, device="cuda")
     scores, idx, out = dsa.dsa_decode_step(d["iq"], d["iw"], d["ik"], d["q"], d["kv"], c["ctx_len"],
-                                           c["k"], c["Dv"], c["scale"], workspace=ws, flags=flags)
+                                           c["k"], c["Dv"], c["scale"], idx=idx, workspace=ws, flags=flags)
     torch.cuda.synchronize()
     stats = dsa.dsa_read_stats(ws, c["B"])
     return scores.cpu().numpy(), idx.cpu().numpy(), out.cpu().numpy(), stats
@@ -392,6 +396,14 @@ def test_edge_cases(torch, dsa, label, kw):
         check_scores(s, rs, c["ctx_len"], label)
         assert np.array_equal(i, ri), "%s indices differ (flags %d)" % (label, flags)
         check_attention(o, ro, "%s flags %d" % (label, flags))
+        # the row record comes from the attention split that holds the kk-th best key
+        ties = expected_ties(rs, ri, c["ctx_len"], c["k"])
+        for b, st in enumerate(stats):
+            kk = min(c["k"], int(c["ctx_len"][b]))
+            assert (st["selected"], st["kth_score"], st["tied_at_kth"]) == (kk, int(rs[b, ri[b, kk - 1]]), ties[b]), \
+                "%s row %d record %s (flags %d)" % (label, b, st, flags)
+            if flags:
+                assert st["path"] == 1 and st["reason"] == 1
         outs.append(o)
     assert bits_equal(outs[0], outs[1]), label + ": fast path and exhaustive path outputs differ"
 
