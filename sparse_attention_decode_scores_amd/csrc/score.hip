@@ -53,12 +53,15 @@ template <int MT, int KT, bool CAND, bool ONE>
 __global__ __launch_bounds__(kScoreBlock) void k_score(ScoreArgs a) {
   constexpr int HP = 32 * MT;  // heads padded to whole tiles (padding has q = 0, w = 0)
   constexpr int DI = 32 * KT;
+  // LDS row stride of a staged query head: 16 bytes past its DI, so that the A
+  // fragment reads (32 heads a wave, DI bytes apart) spread over the banks
+  constexpr int DIP = DI + 16;
   extern __shared__ __align__(16) uint8_t smem[];
   using Smem = ChunkSmem<kScoreBlock>;
   Smem& csm = *reinterpret_cast<Smem*>(smem);
-  int8_t* qs = reinterpret_cast<int8_t*>(smem + align16(sizeof(Smem)));       // [Bg][HP][DI]
-  int8_t* wsm = qs + a.Bg * HP * DI;                                           // [Bg][HP]
-  int32_t* sc = reinterpret_cast<int32_t*>(wsm + a.Bg * HP);                   // [Bg][P]
+  int8_t* qs = reinterpret_cast<int8_t*>(smem + align16(sizeof(Smem)));       // [Bg][HP][DIP]
+  int32_t* wsm = reinterpret_cast<int32_t*>(qs + a.Bg * HP * DIP);             // [Bg][HP] head weights
+  int32_t* sc = wsm + a.Bg * HP;                                               // [Bg][P]
   uint32_t* hist = reinterpret_cast<uint32_t*>(sc + a.Bg * a.P);              // [Bg][kHistBins]
   using CandSmem = BlockCandSmem<kScoreBlock>;
   CandSmem& bsm = *reinterpret_cast<CandSmem*>(hist + a.Bg * kHistBins);
@@ -111,11 +114,12 @@ __global__ __launch_bounds__(kScoreBlock) void k_score(ScoreArgs a) {
 #pragma unroll
   for (int j = 0; j < kQPer; ++j) {
     const int i = tid + kScoreBlock * j;
-    const int h = (i % (HP * (DI / 16))) / (DI / 16);
+    const int hrow = i / (DI / 16);  // bb * HP + h
+    const int h = hrow % HP;
     const int part = i % (DI / 16);
-    if (i < nq) *(v4i*)(qs + 16 * i) = h < a.Hi && 16 * part < a.Di ? qv[j] : v4i{0, 0, 0, 0};
+    if (i < nq) *(v4i*)(qs + hrow * DIP + 16 * part) = h < a.Hi && 16 * part < a.Di ? qv[j] : v4i{0, 0, 0, 0};
   }
-  if (tid < a.Bg * HP) wsm[tid] = tid % HP < a.Hi ? wv : (int8_t)0;
+  if (tid < a.Bg * HP) wsm[tid] = tid % HP < a.Hi ? (int32_t)wv : 0;
   lds_barrier();
 
   // A fragments and weights of a single row stay in registers for the whole chunk.
@@ -127,12 +131,12 @@ __global__ __launch_bounds__(kScoreBlock) void k_score(ScoreArgs a) {
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt)
         qreg[ONE ? mt : 0][ONE ? kt : 0] =
-            *(const v4i*)(qs + (32 * mt + (lane & 31)) * DI + 32 * kt + 16 * (lane >> 5));
+            *(const v4i*)(qs + (32 * mt + (lane & 31)) * DIP + 32 * kt + 16 * (lane >> 5));
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int wd = *(const int*)(wsm + 32 * mt + 8 * g + 4 * (lane >> 5));
+        const v4i wd = *(const v4i*)(wsm + 32 * mt + 8 * g + 4 * (lane >> 5));
 #pragma unroll
-        for (int j = 0; j < 4; ++j) wreg[ONE ? mt : 0][ONE ? 4 * g + j : 0] = (int)(int8_t)(wd >> (8 * j));
+        for (int j = 0; j < 4; ++j) wreg[ONE ? mt : 0][ONE ? 4 * g + j : 0] = wd[j];
       }
     }
   }
@@ -140,47 +144,77 @@ __global__ __launch_bounds__(kScoreBlock) void k_score(ScoreArgs a) {
   // Scores of 64 positions (tile tp) from the key fragments `cur`, which are then
   // refilled with tile tp + 24. With candidates, scores stay in LDS until the chunk
   // is done (no global store in the loop: its completion would be waited for later).
+  // Per row the tile is two 32-key halves, and the rows form a pipeline over them:
+  // the matrix cores take a row's second half, then the next row's first half,
+  // while the vector ALU weighs the half before (otherwise the two waves of a SIMD
+  // run their products and their weighing in step, and each unit idles half the time).
+  auto load_a = [&](int bb, v4i(&qa)[MT][KT]) {  // A fragments of row bb
+    const int8_t* qb = qs + bb * HP * DIP;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        qa[mt][kt] = ONE ? qreg[ONE ? mt : 0][ONE ? kt : 0]
+                         : *(const v4i*)(qb + (32 * mt + (lane & 31)) * DIP + 32 * kt + 16 * (lane >> 5));
+  };
+  auto load_w = [&](int bb, int(&w)[MT][16]) {  // weights of the lane's accumulator heads
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        if (ONE) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) w[mt][4 * g + j] = wreg[ONE ? mt : 0][ONE ? 4 * g + j : 0];
+        } else {
+          const v4i wd = *(const v4i*)(wsm + bb * HP + 32 * mt + 8 * g + 4 * (lane >> 5));
+#pragma unroll
+          for (int j = 0; j < 4; ++j) w[mt][4 * g + j] = wd[j];
+        }
+      }
+  };
+  auto mm = [&](v16i(&acc)[MT], const v4i(&qa)[MT][KT], const v4i(&kf)[KT]) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = v16i{};
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(qa[mt][kt], kf[kt], acc[mt], 0, 0, 0);
+  };
+  // accumulator r of lane l holds head 32*mt + 8*(r/4) + 4*(l/32) + r%4 of key l%32;
+  // two independent multiply-add chains
+  auto weigh = [&](const v16i(&acc)[MT], const int(&w)[MT][16]) {
+    int c0 = 0, c1 = 0;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const int v0 = acc[mt][r], v1 = acc[mt][r + 1];
+        c0 = mad_i24(w[mt][r], v0 > 0 ? v0 : 0, c0);
+        c1 = mad_i24(w[mt][r + 1], v1 > 0 ? v1 : 0, c1);
+      }
+    return c0 + c1;
+  };
   auto tile = [&](v4i(&cur)[2][KT], int tp) {
     const int64_t p0 = cbeg + 64 * tp;
     const int nb = ONE ? 1 : a.Bg;  // a compile-time trip count keeps the wait counts exact
+    v4i qa[MT][KT];
+    int w[MT][16];
+    v16i a0[MT], a1[MT];
+    load_a(0, qa);
+    mm(a0, qa, cur[0]);
     for (int bb = 0; bb < nb; ++bb) {
-      const int8_t* qb = qs + bb * HP * DI;
-      int half[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        v16i acc[MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mt] = v16i{};
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            const v4i qf = ONE ? qreg[ONE ? mt : 0][ONE ? kt : 0]
-                               : *(const v4i*)(qb + (32 * mt + (lane & 31)) * DI + 32 * kt +
-                                               16 * (lane >> 5));
-            acc[mt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(qf, cur[t][kt], acc[mt], 0, 0, 0);
-          }
-        }
-        // accumulator r of lane l holds head 32*mt + 8*(r/4) + 4*(l/32) + r%4 of key l%32
-        int part = 0;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            int wd = 0;
-            if (!ONE) wd = *(const int*)(wsm + bb * HP + 32 * mt + 8 * g + 4 * (lane >> 5));
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int w = ONE ? wreg[ONE ? mt : 0][ONE ? 4 * g + j : 0] : (int)(int8_t)(wd >> (8 * j));
-              const int v = acc[mt][4 * g + j];
-              part += __mul24(w, v > 0 ? v : 0);
-            }
-          }
-        }
-        part += __shfl_xor(part, 32);
-        half[t] = part;
+      mm(a1, qa, cur[1]);
+      load_w(bb, w);
+      const int h0 = weigh(a0, w);
+      if (bb + 1 < nb) {  // uniform
+        load_a(bb + 1, qa);
+        mm(a0, qa, cur[0]);
       }
-      const int val = lane < 32 ? half[0] : half[1];
+      const int h1 = weigh(a1, w);
+      // lanes l and l ^ 32 hold the same key's other heads: one lane-half swap gives
+      // lane l < 32 key l of the first 32 (half 0), lane l >= 32 key l of the tile
+      const auto sw = __builtin_amdgcn_permlane32_swap(h0, h1, false, false);
+      const int val = sw[0] + sw[1];
       const int64_t pos = p0 + lane;
       if (CAND) {
         sc[bb * a.P + (int)(pos - cbeg)] = val;
@@ -583,7 +617,7 @@ hipError_t launch_score_row(const ScoreArgs& a, int MT, int KT, int D, int grid,
 int score_max_chunk() { return kChunkPerThread * kScoreBlock; }
 
 size_t score_lds_bytes(int MT, int KT, int Bg, int P, bool cand) {
-  return align16(sizeof(ChunkSmem<kScoreBlock>)) + (size_t)Bg * 32 * MT * 32 * KT + (size_t)Bg * 32 * MT +
+  return align16(sizeof(ChunkSmem<kScoreBlock>)) + (size_t)Bg * 32 * MT * (32 * KT + 16) + (size_t)Bg * 32 * MT * 4 +
          (cand ? (size_t)Bg * P * 4 + (size_t)Bg * kHistBins * 4 + sizeof(BlockCandSmem<kScoreBlock>) +
                      (size_t)Bg * 4
                : 0) +
