@@ -158,15 +158,20 @@ __device__ __forceinline__ bool threshold_floor(const uint32_t* hist, int count,
   const uint32_t incl = wave_incl_scan_u32(sum);
   if ((uint32_t)__builtin_amdgcn_readlane((int)incl, 63) != (uint32_t)count) return false;
   const uint32_t want = (uint32_t)m + 1;
-  int tb = -1;
-  uint32_t acc = incl - sum;  // keys in better bins than this lane's
-#pragma unroll
-  for (int j = 15; j >= 0; --j) {
-    tb = (tb < 0 && acc < want && want <= acc + h[j]) ? bin0 + j : tb;
-    acc += h[j];
-  }
-  const uint64_t has = __ballot(tb >= 0);  // exactly one lane
-  *tlo = bin_floor((uint32_t)__builtin_amdgcn_readlane(tb, __builtin_ctzll(has)));
+  // the lane whose 16 bins hold the want-th best key, then within them one row scan:
+  // lane j < 16 (and its copies in the other rows) takes bin bin0(L) + 15 - j
+  const uint32_t excl = incl - sum;  // keys in better bins than this lane's
+  const uint64_t hit = __ballot(excl < want && want <= incl);  // exactly one lane
+  const int L = (int)__builtin_ctzll(hit);
+  const uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)excl, L);
+  const int bj = kHistBins - 1 - 16 * L - (l & 15);
+  uint32_t c = hist[bj];
+  c += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)c, dpp::kRowShr1, 0xF, 0xF, false);
+  c += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)c, dpp::kRowShr2, 0xF, 0xF, false);
+  c += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)c, dpp::kRowShr4, 0xF, 0xF, false);
+  c += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)c, dpp::kRowShr8, 0xF, 0xF, false);
+  const uint64_t hit2 = __ballot(base + c >= want) & 0xFFFFull;  // first row
+  *tlo = bin_floor((uint32_t)(kHistBins - 1 - 16 * L - (int)__builtin_ctzll(hit2)));
   return true;
 }
 
@@ -250,12 +255,27 @@ __device__ __forceinline__ bool wave_chunk_candidates(const int32_t* scores, int
   if (ns > cap) return false;
 
   const bool two = ns > 64;
+  if (!two) {  // uniform: one key per lane; slots up to a multiple of 8 hold key 0,
+    // which is below every staged key (key 0 would be position 2^32 - 1), so no
+    // step checks the count
+    const uint32_t ns8 = (ns + 7u) & ~7u;
+    if ((uint32_t)l >= ns && (uint32_t)l < ns8) stage[l] = 0ull;
+  }
   const uint64_t k0 = l < (int)ns ? stage[l] : 0ull;
   const uint64_t k1 = l + 64 < (int)ns ? stage[l + 64] : 0ull;
   uint32_t r0 = 0, r1 = 0;
   // every lane compares its keys with all staged keys: 8 keys per step, read as
   // four 16-byte broadcasts (the staging area has kWaveStage >= cap + 8 slots)
   typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
+  if (!two) {  // uniform
+    for (int j0 = 0; j0 < (int)ns; j0 += 8) {
+      u64x2 e[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) e[t] = *reinterpret_cast<const u64x2*>(stage + j0 + 2 * t);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) r0 += ((t & 1) ? e[t >> 1].y : e[t >> 1].x) > k0 ? 1u : 0u;
+    }
+  } else
   for (int j0 = 0; j0 < (int)ns; j0 += 8) {
     u64x2 e[4];
 #pragma unroll

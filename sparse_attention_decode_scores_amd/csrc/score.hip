@@ -49,7 +49,11 @@ __device__ __forceinline__ void load_keys(v4i (&kf)[2][KT], __amdgpu_buffer_rsrc
 
 }  // namespace
 
-template <int MT, int KT, bool CAND, bool ONE>
+// NB: key tile buffers per wave (3, rotating, refilled as each is consumed; or 1
+// when a chunk has at most one 64-key tile per wave, so no request is issued for
+// tiles past the chunk: those requests returned zeros but took the address units'
+// time ahead of the query requests of the waves behind)
+template <int MT, int KT, bool CAND, bool ONE, int NB>
 __global__ __launch_bounds__(kScoreBlock) void k_score(ScoreArgs a) {
   constexpr int HP = 32 * MT;  // heads padded to whole tiles (padding has q = 0, w = 0)
   constexpr int DI = 32 * KT;
@@ -104,8 +108,10 @@ __global__ __launch_bounds__(kScoreBlock) void k_score(ScoreArgs a) {
       const_cast<int8_t*>(a.ik + cbeg * a.Di), (short)0, clen * a.Di, 0x00020000);
   v4i kb0[2][KT], kb1[2][KT], kb2[2][KT];
   load_keys<KT>(kb0, rs, wave, a.Di);
-  load_keys<KT>(kb1, rs, wave + kScoreWaves, a.Di);
-  load_keys<KT>(kb2, rs, wave + 2 * kScoreWaves, a.Di);
+  if constexpr (NB > 1) {
+    load_keys<KT>(kb1, rs, wave + kScoreWaves, a.Di);
+    load_keys<KT>(kb2, rs, wave + 2 * kScoreWaves, a.Di);
+  }
 
   if (CAND) {
     radix_clear<kScoreBlock>(csm.radix);
@@ -223,16 +229,20 @@ __global__ __launch_bounds__(kScoreBlock) void k_score(ScoreArgs a) {
         a.scores[(int64_t)(a.b0 + bb) * a.N + pos] = val;
       }
     }
-    load_keys<KT>(cur, rs, tp + 3 * kScoreWaves, a.Di);
+    if constexpr (NB > 1) load_keys<KT>(cur, rs, tp + 3 * kScoreWaves, a.Di);
   };
 
-  // three key buffers rotate by name (a register copy would wait for its load)
-  for (int tp = wave; tp < npairs; tp += 3 * kScoreWaves) {
-    tile(kb0, tp);
-    if (tp + kScoreWaves >= npairs) break;
-    tile(kb1, tp + kScoreWaves);
-    if (tp + 2 * kScoreWaves >= npairs) break;
-    tile(kb2, tp + 2 * kScoreWaves);
+  if constexpr (NB == 1) {
+    if (wave < npairs) tile(kb0, wave);
+  } else {
+    // three key buffers rotate by name (a register copy would wait for its load)
+    for (int tp = wave; tp < npairs; tp += 3 * kScoreWaves) {
+      tile(kb0, tp);
+      if (tp + kScoreWaves >= npairs) break;
+      tile(kb1, tp + kScoreWaves);
+      if (tp + 2 * kScoreWaves >= npairs) break;
+      tile(kb2, tp + 2 * kScoreWaves);
+    }
   }
 
   if (CAND) {
@@ -624,9 +634,9 @@ size_t score_lds_bytes(int MT, int KT, int Bg, int P, bool cand) {
          16;
 }
 
-template <int MT, int KT, bool CAND, bool ONE>
+template <int MT, int KT, bool CAND, bool ONE, int NB = 3>
 static hipError_t launch_score_t(const ScoreArgs& a, int grid, size_t lds, hipStream_t s, KTimer t) {
-  auto fn = k_score<MT, KT, CAND, ONE>;
+  auto fn = k_score<MT, KT, CAND, ONE, NB>;
   hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
@@ -637,6 +647,9 @@ template <int MT, int KT>
 static hipError_t launch_score_mk(const ScoreArgs& a, bool cand, int grid, size_t lds, hipStream_t s,
                                   KTimer t) {
   const bool one = a.Bg == 1;
+  // several rows with candidates: one key tile per wave when the chunk has at most
+  // kScoreWaves tiles of 64 keys
+  if (cand && !one && (a.P + 63) / 64 <= kScoreWaves) return launch_score_t<MT, KT, true, false, 1>(a, grid, lds, s, t);
   if (cand) return one ? launch_score_t<MT, KT, true, true>(a, grid, lds, s, t)
                        : launch_score_t<MT, KT, true, false>(a, grid, lds, s, t);
   return one ? launch_score_t<MT, KT, false, true>(a, grid, lds, s, t)
