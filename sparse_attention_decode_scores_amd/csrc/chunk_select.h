@@ -215,16 +215,23 @@ __device__ __forceinline__ bool hist_threshold(const uint32_t* hist, const uint3
 //  3. each staged key is ranked against the others; the m best go to the output
 //     slot of their rank (best first) and the one of rank m is x, the best key
 //     left out.
-// Returns false, having written nothing, when more than m + 64 keys are staged
+// The chunk's valid scores also go to dst[0, count) as they are read (when the
+// threshold step fails they are not read, and the caller stores them).
+// Returns false, having written no candidate, when more than m + 64 keys are staged
 // (heavy ties) or the histogram does not count `count` keys: the caller then runs
 // chunk_candidates. `stage` is this wave's LDS area of kWaveStage keys.
 __device__ __forceinline__ bool wave_chunk_candidates(const int32_t* scores, int count, uint32_t pos0,
                                                       int m, const uint32_t* hist,
                                                       CandOut out,
-                                                      uint64_t* __restrict__ x_out, uint64_t* stage) {
+                                                      uint64_t* __restrict__ x_out, uint64_t* stage,
+                                                      int32_t* __restrict__ dst) {
   const int l = lane_id();
   if (count <= m) {
-    for (int i = l; i < m; i += 64) out.put(i, i < count ? make_key(scores[i], pos0 + (uint32_t)i) : 0ull);
+    for (int i = l; i < m; i += 64) {
+      const int32_t v = scores[i < count ? i : 0];
+      if (i < count) dst[i] = v;
+      out.put(i, i < count ? make_key(v, pos0 + (uint32_t)i) : 0ull);
+    }
     if (l == 0) *x_out = 0;
     return true;
   }
@@ -245,6 +252,7 @@ __device__ __forceinline__ bool wave_chunk_candidates(const int32_t* scores, int
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const int i = r0 + 64 * t + l;
+      if (i < count) dst[i] = v[t];
       const bool in = i < count && v[t] >= tlo;
       const uint64_t b = __ballot(in);
       const uint32_t slot = ns + (uint32_t)__popcll(b & lt);

@@ -247,17 +247,17 @@ __global__ __launch_bounds__(kScoreBlock) void k_score(ScoreArgs a) {
 
   if (CAND) {
     lds_barrier();
-    // the scores leave LDS first: the selection below waits for no memory
-    // operation, so these stores complete underneath it. The key requests past
-    // the chunk's end (buffer reads that return zeros) are drained before them,
-    // so no later wait for those registers covers the stores.
+    // the scores leave LDS first (one row: here; several: in each row's epilogue, as
+    // it reads them): the selection waits for no memory operation, so these stores
+    // complete underneath it. The key requests past the chunk's end (buffer reads
+    // that return zeros) are drained before them, so no later wait for those
+    // registers covers the stores.
     __builtin_amdgcn_s_waitcnt(0x0F70);  // gfx9 encoding: vmcnt(0), expcnt and lgkmcnt untouched
-    for (int bb = 0; bb < a.Bg; ++bb) {
-      const int b = a.b0 + bb;
-      const int64_t n64 = (int64_t)a.lens.n[b] - cbeg;
+    if (ONE) {
+      const int64_t n64 = (int64_t)a.lens.n[a.b0] - cbeg;
       const int count = n64 > clen ? clen : (int)(n64 > 0 ? n64 : 0);
-      int32_t* dst = a.scores + (int64_t)b * a.N + cbeg;
-      for (int i = tid; i < count; i += kScoreBlock) dst[i] = sc[bb * a.P + i];
+      int32_t* dst = a.scores + (int64_t)a.b0 * a.N + cbeg;
+      for (int i = tid; i < count; i += kScoreBlock) dst[i] = sc[i];
     }
     if (ONE) {
       // one row: the whole block selects the chunk's candidates
@@ -276,7 +276,8 @@ __global__ __launch_bounds__(kScoreBlock) void k_score(ScoreArgs a) {
         const int count = n64 > clen ? clen : (int)(n64 > 0 ? n64 : 0);
         const bool ok = wave_chunk_candidates(sc + bb * a.P, count, (uint32_t)cbeg, a.m, hist + bb * kHistBins,
                                               CandOut{a.cand + (int64_t)b * kCandCap, c * a.m},
-                                              a.xc + (int64_t)b * a.G + c, bsm.wstage[wave]);
+                                              a.xc + (int64_t)b * a.G + c, bsm.wstage[wave],
+                                              a.scores + (int64_t)b * a.N + cbeg);
         if (lane == 0) fallback[bb] = ok ? 0 : 1;
       }
     }
@@ -286,6 +287,10 @@ __global__ __launch_bounds__(kScoreBlock) void k_score(ScoreArgs a) {
       const int b = a.b0 + bb;
       const int64_t n64 = (int64_t)a.lens.n[b] - cbeg;
       const int count = n64 > clen ? clen : (int)(n64 > 0 ? n64 : 0);
+      if (!ONE) {  // the epilogue may not have stored them
+        int32_t* dst = a.scores + (int64_t)b * a.N + cbeg;
+        for (int i = tid; i < count; i += kScoreBlock) dst[i] = sc[bb * a.P + i];
+      }
       chunk_candidates<kScoreBlock>(sc + bb * a.P, count, (uint32_t)cbeg, a.m,
                                     CandOut{a.cand + (int64_t)b * kCandCap, c * a.m}, a.xc + (int64_t)b * a.G + c,
                                     csm);
