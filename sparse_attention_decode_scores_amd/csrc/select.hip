@@ -1072,7 +1072,11 @@ __global__ __launch_bounds__(kSelBlock) void k_select(const uint64_t* __restrict
   uint64_t* sink = lds.sink;
   const int tid = threadIdx.x;
   const int b = blockIdx.y;
-  const bool attn_role = (int)blockIdx.x < S;
+  // With attention (the decode step) every workgroup is an attention split, and the
+  // splits' windows are the output; without (the stand-alone selection) every
+  // workgroup ranks a slice of the selected keys. One role per instantiation keeps
+  // each kernel's registers to its own path.
+  constexpr bool kRank = std::is_same<Attn, AttnNone>::value;
   // Requests first, all from preloaded arguments. The candidate union U: thread t
   // holds entries [16t, 16t + 16), eight 16-byte pieces, piece j of all threads
   // contiguous (cand_slot); its workspace region always exists, and the entries are
@@ -1141,7 +1145,7 @@ __global__ __launch_bounds__(kSelBlock) void k_select(const uint64_t* __restrict
   }
   radix_clear<kSelBlock>(sm.radix);
 
-  if (attn_role) {
+  if constexpr (!kRank) {
     // ------------------------------------------------ attention workgroup s
     const int per = (a.k + S - 1) / S;
     const int r0 = (int)blockIdx.x * per;
@@ -1175,8 +1179,7 @@ __global__ __launch_bounds__(kSelBlock) void k_select(const uint64_t* __restrict
       exhaustive_window(kernel_args(), b, (uint32_t)r0, (uint32_t)(r0 + cnt - 1));
     // sm.winpos is complete and published (the last barrier of the window
     // narrowing follows its last write), and the LDS region is free again
-    if (a.R == 0) {  // uniform: no ranking workgroups; the windows are the output
-      // slots [r0, r0 + per) of the row: the window's positions, then -1 past kk
+    {  // the output slots [r0, r0 + per) of the row: the window's positions, then -1 past kk
       int32_t* out = a.idx + (int64_t)b * a.k;
       for (int i = tid; i < per && r0 + i < a.k; i += kSelBlock) out[r0 + i] = i < cnt ? (int32_t)sm.winpos[i] : -1;
       if (cnt > 0 && r0 + cnt == kk && tid == 0) {  // the window of the kk-th best key
@@ -1236,7 +1239,7 @@ __global__ __launch_bounds__(kSelBlock) void k_select(const uint64_t* __restrict
   // the exhaustive path streams the whole row in every workgroup that takes part,
   // so fewer ranking workgroups take part there, each with a larger slice
   const int R = reason == 0 ? a.R : (a.R < kFallbackRankers ? a.R : kFallbackRankers);
-  const int r = (int)blockIdx.x - S;
+  const int r = (int)blockIdx.x;
   if (r >= R) return;  // uniform
   if (reason != 0) {
     kstar = select_row_exhaustive(kernel_args(), b, &tied);
@@ -1303,7 +1306,9 @@ static hipError_t launch_select_t(const SelArgs& a, const AttnArgs& at, int B, h
   hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
-  return launch_timed(fn, dim3(at.S + a.R, B), dim3(kSelBlock), lds, s, t, a.cand, a.xc, a.sums, at.q, a.G, at.Hq,
+  // attention splits (decode step) or ranking workgroups (stand-alone selection)
+  const int grid = std::is_same<Attn, AttnNone>::value ? a.R : at.S;
+  return launch_timed(fn, dim3(grid, B), dim3(kSelBlock), lds, s, t, a.cand, a.xc, a.sums, at.q, a.G, at.Hq,
                       at.Dk, at.S, a, at);
 }
 
