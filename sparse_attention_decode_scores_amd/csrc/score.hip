@@ -352,6 +352,10 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(const int8_t* __restr
   uint32_t* hist = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(sc) + align16((size_t)P * 4));
   uint32_t* hgroup = hist + kHistBins;  // [kHistGroups]: sums of 16 bins
   RowCandSmem& rsm = *reinterpret_cast<RowCandSmem*>(hgroup + kHistGroups);
+  // the query heads, rows DI + 16 bytes apart (the A-fragment reads of 32 heads then
+  // spread over the banks)
+  constexpr int DI = 32 * KT, DIP = DI + 16;
+  int8_t* qs = reinterpret_cast<int8_t*>(&rsm) + align16(sizeof(RowCandSmem));  // [32 MT][DIP]
 
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   // a batch of one: the row is row 0, a constant, so that every argument address is
@@ -370,24 +374,20 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(const int8_t* __restr
   // from the chunk's first to its last valid one
   const int span = units > 0 ? (int)((int64_t)(units - 1) * ustride) + (count - kUnit * (units - 1)) : 0;
 
-  // A operand: lane l holds head 32mt + (l & 31), dims 32kt + 16(l >> 5) .. +15; lane
-  // l also holds the weight of head l (Hi <= 64). Requested before any key, as raw
-  // buffer loads over the row's Hi·Di query bytes: dims past Di (Di = 32·KT - 16) are
-  // given an offset past the end and so read as zeros (no operation on the loaded
-  // values, which the scheduler could place, with a wait for the query, ahead of the
-  // key requests); padding heads read a present head and are zeroed after them.
+  // The query: the block requests it once, one 16-byte piece per thread (two when
+  // Hi·Di > 8 KB), before any key, and stages it in LDS, from where every wave takes
+  // its A operand (lane l: head 32mt + (l & 31), dims 32kt + 16(l >> 5) .. +15). Each
+  // wave requesting the whole query itself cost eight requests per wave, and the
+  // waves' first units started up to 2 µs apart. Lane l also holds the weight of
+  // head l (Hi <= 64).
   const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int8_t*>(iq + (int64_t)b * Hi * Di), (short)0, Hi * Di, 0x00020000);
-  v4i qreg[MT][KT];
+  const int npc = Hi * Di / 16;  // 16-byte pieces of the query (Di % 16 == 0)
+  v4i qp[2];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int h = 32 * mt + (lane & 31) < Hi ? 32 * mt + (lane & 31) : Hi - 1;
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-      const int d0 = 32 * kt + 16 * (lane >> 5);
-      qreg[mt][kt] =
-          __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rq, d0 < Di ? h * Di + d0 : Hi * Di, 0, 0));
-    }
+  for (int u = 0; u < 2; ++u) {
+    const int pc = tid + kScoreBlock * u;
+    qp[u] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rq, 16 * (pc < npc ? pc : 0), 0, 0));
   }
   const int wl = (int)iw[(int64_t)b * Hi + (lane < Hi ? lane : Hi - 1)];
 
@@ -405,6 +405,25 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(const int8_t* __restr
   load_unit<KT>(kb0, rs, wave, js, Di);
   load_unit<KT>(kb1, rs, wave + kScoreWaves, js, Di);
   if constexpr (D == 3) load_unit<KT>(kb2, rs, wave + 2 * kScoreWaves, js, Di);
+
+  // the query into LDS: head h's dims [0, Di), then zeros for dims [Di, DI) (the
+  // last key fragment's upper half there reads the next key's dims or zeros)
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int pc = tid + kScoreBlock * u;
+    if (pc < npc) {
+      const int h = (16 * pc) / Di, d = 16 * pc - h * Di;
+      *reinterpret_cast<v4i*>(qs + h * DIP + d) = qp[u];
+    }
+  }
+  if (Di < DI && tid < Hi) *reinterpret_cast<v4i*>(qs + tid * DIP + Di) = v4i{0, 0, 0, 0};
+  lds_barrier();
+  v4i qreg[MT][KT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+      qreg[mt][kt] = *reinterpret_cast<const v4i*>(qs + (32 * mt + (lane & 31)) * DIP + 32 * kt + 16 * (lane >> 5));
 
   // weights in accumulator order: value r of tile mt at lane l is head
   // 32mt + 8(r / 4) + 4(l >> 5) + r % 4; padding heads (q = 0) get weight 0
@@ -600,8 +619,9 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(const int8_t* __restr
 }
 
 size_t score_row_lds_bytes(int P) {
+  // ... + the staged query at its largest (64 heads, rows of 256 + 16 bytes)
   return align16(sizeof(ChunkSmem<kScoreBlock>)) + align16((size_t)P * 4) + (size_t)(kHistBins + kHistGroups) * 4 +
-         sizeof(RowCandSmem) + 16;
+         align16(sizeof(RowCandSmem)) + (size_t)64 * (256 + 16) + 16;
 }
 
 int score_row_max_chunk() { return kMaxUnits * kUnit; }
