@@ -356,6 +356,7 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(const int8_t* __restr
   // spread over the banks)
   constexpr int DI = 32 * KT, DIP = DI + 16;
   int8_t* qs = reinterpret_cast<int8_t*>(&rsm) + align16(sizeof(RowCandSmem));  // [32 MT][DIP]
+  int32_t* wsm = reinterpret_cast<int32_t*>(qs + 64 * (256 + 16));               // [64] head weights
 
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   // a batch of one: the row is row 0, a constant, so that every argument address is
@@ -378,8 +379,8 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(const int8_t* __restr
   // Hi·Di > 8 KB), before any key, and stages it in LDS, from where every wave takes
   // its A operand (lane l: head 32mt + (l & 31), dims 32kt + 16(l >> 5) .. +15). Each
   // wave requesting the whole query itself cost eight requests per wave, and the
-  // waves' first units started up to 2 µs apart. Lane l also holds the weight of
-  // head l (Hi <= 64).
+  // waves' first units started up to 2 µs apart. The head weights go the same way
+  // (the first wave requests them; 0 for padding heads).
   const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int8_t*>(iq + (int64_t)b * Hi * Di), (short)0, Hi * Di, 0x00020000);
   const int npc = Hi * Di / 16;  // 16-byte pieces of the query (Di % 16 == 0)
@@ -389,7 +390,8 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(const int8_t* __restr
     const int pc = tid + kScoreBlock * u;
     qp[u] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rq, 16 * (pc < npc ? pc : 0), 0, 0));
   }
-  const int wl = (int)iw[(int64_t)b * Hi + (lane < Hi ? lane : Hi - 1)];
+  int wl = 0;
+  if (wave == 0) wl = (int)iw[(int64_t)b * Hi + (lane < Hi ? lane : Hi - 1)];
 
   // the histogram is shared by the waves: cleared before any of them adds to it
   for (int i = tid; i < kHistBins + kHistGroups; i += kScoreBlock) hist[i] = 0;  // and hgroup
@@ -417,6 +419,7 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(const int8_t* __restr
     }
   }
   if (Di < DI && tid < Hi) *reinterpret_cast<v4i*>(qs + tid * DIP + Di) = v4i{0, 0, 0, 0};
+  if (wave == 0) wsm[lane] = lane < Hi ? wl : 0;
   lds_barrier();
   v4i qreg[MT][KT];
 #pragma unroll
@@ -426,15 +429,16 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(const int8_t* __restr
       qreg[mt][kt] = *reinterpret_cast<const v4i*>(qs + (32 * mt + (lane & 31)) * DIP + 32 * kt + 16 * (lane >> 5));
 
   // weights in accumulator order: value r of tile mt at lane l is head
-  // 32mt + 8(r / 4) + 4(l >> 5) + r % 4; padding heads (q = 0) get weight 0
+  // 32mt + 8(r / 4) + 4(l >> 5) + r % 4 (four consecutive heads a read); padding
+  // heads (q = 0) have weight 0
   int wreg[MT][16];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int h = 32 * mt + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      const int w = __shfl(wl, h & 63);
-      wreg[mt][r] = h < Hi ? w : 0;
+    for (int g = 0; g < 4; ++g) {
+      const v4i wd = *reinterpret_cast<const v4i*>(wsm + 32 * mt + 8 * g + 4 * (lane >> 5));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) wreg[mt][4 * g + j] = wd[j];
     }
     if (32 * mt + (lane & 31) >= Hi)
 #pragma unroll
@@ -621,7 +625,7 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(const int8_t* __restr
 size_t score_row_lds_bytes(int P) {
   // ... + the staged query at its largest (64 heads, rows of 256 + 16 bytes)
   return align16(sizeof(ChunkSmem<kScoreBlock>)) + align16((size_t)P * 4) + (size_t)(kHistBins + kHistGroups) * 4 +
-         align16(sizeof(RowCandSmem)) + (size_t)64 * (256 + 16) + 16;
+         align16(sizeof(RowCandSmem)) + (size_t)64 * (256 + 16) + 64 * 4 + 16;
 }
 
 int score_row_max_chunk() { return kMaxUnits * kUnit; }
