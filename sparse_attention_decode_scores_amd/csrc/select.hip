@@ -918,13 +918,14 @@ __device__ __forceinline__ uint32_t window_positions(const uint64_t (&key)[E], c
   const KeyRange bot = refine_key_range<E>(rb[1], need[1], key, sv, vmask, sm.radix);
   // every key of the window lies in [bot.klo, top.khi]; the keys above top.khi
   // number top.above
-  const uint64_t klo = bot.klo > 0 ? bot.klo : 1, khi = top.khi;  // a present key is never 0
+  // a present key is never 0, and an absent one is 0: below klo (>= 1) and not
+  // above khi, so the comparisons below need no presence test
+  const uint64_t klo = bot.klo > 0 ? bot.klo : 1, khi = top.khi;
   uint32_t a = 0, b = 0;  // sorted: the thread's keys in range are its keys [a, b)
 #pragma unroll
   for (int j = 0; j < E; ++j) {
-    const bool v = (vmask >> j) & 1u;
-    a += v && key[j] > khi ? 1u : 0u;
-    b += v && key[j] >= klo ? 1u : 0u;
+    a += key[j] > khi ? 1u : 0u;
+    b += key[j] >= klo ? 1u : 0u;
   }
   if (count_mx) {  // uniform
     const uint64_t wmx = wave_maxr_u64(threadIdx.x < (unsigned)G ? mx : 0ull);
@@ -945,7 +946,7 @@ __device__ __forceinline__ uint32_t window_positions(const uint64_t (&key)[E], c
     uint32_t sl = base;
 #pragma unroll
     for (int j = 0; j < E; ++j) {
-      const bool t = ((vmask >> j) & 1u) && key[j] >= klo && key[j] <= khi;
+      const bool t = key[j] >= klo && key[j] <= khi;
       *(t ? wl + sl : mine) = key[j];
       sl += t ? 1u : 0u;
     }
@@ -954,9 +955,9 @@ __device__ __forceinline__ uint32_t window_positions(const uint64_t (&key)[E], c
     uint64_t m = 0;
 #pragma unroll
     for (int w = 0; w < kSelWaves; ++w) m = sm.mxw[w] > m ? sm.mxw[w] : m;
-    uint32_t g = 0;
+    uint32_t g = 0;  // (an absent key, 0, is above no key)
 #pragma unroll
-    for (int j = 0; j < E; ++j) g += ((vmask >> j) & 1u) && key[j] > m ? 1u : 0u;
+    for (int j = 0; j < E; ++j) g += key[j] > m ? 1u : 0u;
     g = wave_sum_u32(g);
     if (lane_id() == 0) sm.gtw[wave_id()] = g;
   }
