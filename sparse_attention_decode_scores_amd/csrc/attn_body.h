@@ -405,17 +405,23 @@ struct AttnMfma {
 
   // Attention over cnt listed positions (pos_at(i), i < cnt) as split `split`: the
   // positions are staged SB at a time; the query fragments (load_q) are written to
-  // LDS once the first sub-block's row loads are in flight.
+  // LDS once the first sub-block's row loads are in flight. When a split has more
+  // than one sub-block, the next one's rows are requested before this one's
+  // products, so their latency hides behind them.
   template <typename PosAt>
   __device__ __forceinline__ static void run(const AttnArgs& p, int b, int split, PosAt pos_at, int cnt,
                              uint8_t* work, const QFrag& qf) {
     Acc o;
     begin(p, work, o);
+    Rows r;
+    if (cnt > 0) r = gather(p, qf, pos_at, cnt < SB ? cnt : SB);  // uniform
     for (int s0 = 0; s0 < cnt; s0 += SB) {
       const int nr = cnt - s0 < SB ? cnt - s0 : SB;
-      const Rows r = gather(p, qf, [&](int i) { return pos_at(s0 + i); }, nr);
       put(r, qf, p, nr, s0 == 0, work);
-      sub_block(p, b, nr >= 64 ? ~0ull : (1ull << nr) - 1ull, work, o, s0 + SB >= cnt);
+      const int s1 = s0 + SB;
+      if (s1 < cnt)  // uniform
+        r = gather(p, qf, [&](int i) { return pos_at(s1 + i); }, cnt - s1 < SB ? cnt - s1 : SB);
+      sub_block(p, b, nr >= 64 ? ~0ull : (1ull << nr) - 1ull, work, o, s1 >= cnt);
     }
     finish(p, b, split, work, o);
   }
