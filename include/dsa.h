@@ -76,6 +76,8 @@ typedef enum dsa_dtype {
 #define DSA_MAX_INDEX_DIM 256    /* Di, a multiple of 16 (larger: DSA_ERR_UNSUPPORTED) */
 #define DSA_MAX_ATTN_HEADS 64    /* Hq */
 #define DSA_MAX_ATTN_DIM 1024    /* Dk */
+#define DSA_PAGE_SIZE 256        /* positions per page of a paged cache pool */
+#define DSA_MAX_PAGES 8192       /* page-table entries of one paged call (N <= 2,097,152) */
 
 /* flags for dsa_topk_select / dsa_decode_step */
 #define DSA_FLAG_FORCE_FALLBACK 1u /* testing: take the exhaustive path for every row */
@@ -225,6 +227,46 @@ dsa_status dsa_decode_step_noalloc(const int8_t* iq, const int8_t* iw, const int
                                    int Dk, int Dv, int64_t N, int k, float scale, dsa_dtype dt,
                                    int32_t* scores, int32_t* idx, float* out, unsigned flags,
                                    hipStream_t stream);
+
+/*
+ * Paged caches: the three stages over a pool of fixed-size pages shared by many
+ * sequences, read through one sequence's page table (the glm53-tensorfold-spark
+ * README: a 1,048,576-token KV pool held in 4,096 pages, in the introduction and the
+ * "What's new (2026-09-30)" note on 1M-context fixes; 1,048,576 / 4,096 gives
+ * DSA_PAGE_SIZE = 256 positions a page). Logical position s of the sequence lives
+ * in pool row page_table[s / 256] * 256 + s % 256 of both pools, so one table serves
+ * the indexer keys and the latent rows. The results are those of the contiguous
+ * calls on the caches the table describes (ik[s] = ik_pool[that row], and the same
+ * for kv), bit for bit: scores and idx hold logical positions.
+ *   ik_pool    [pool_pages * 256][Di]  int8   indexer key pool
+ *   kv_pool    [pool_pages * 256][Dk]  dt     latent pool (layout of kv above)
+ *   page_table [ceil(N / 256)]         int32  DEVICE array: pool page of each logical
+ *                                             page of the sequence, shared by its B
+ *                                             rows (ctx_len[b] <= N as before)
+ *   pool_pages                                pages in each pool (>= 1)
+ * Entries outside [0, pool_pages) are clamped into the pool (no read leaves it; the
+ * results for those pages are unspecified). Limits, beyond those of the contiguous
+ * calls: N <= DSA_MAX_PAGES * 256, pool_pages * 256 <= INT32_MAX, and
+ * pool_pages * 256 * Di < 2^31 for calls that read ik_pool (else
+ * DSA_ERR_UNSUPPORTED); page_table NULL or misaligned, or pool_pages < 1, give
+ * DSA_ERR_INVALID_ARG. Workspace sizes are those of the contiguous calls.
+ */
+dsa_status dsa_index_scores_paged(const int8_t* iq, const int8_t* iw, const int8_t* ik_pool,
+                                  const int32_t* page_table, int64_t pool_pages, const int32_t* ctx_len,
+                                  int B, int Hi, int Di, int64_t N, int32_t* scores, hipStream_t stream);
+
+dsa_status dsa_sparse_attn_paged(const void* q, const void* kv_pool, const int32_t* page_table,
+                                 int64_t pool_pages, const int32_t* idx, int B, int Hq, int Dk, int Dv,
+                                 int64_t N, int k, float scale, dsa_dtype dt, float* out, void* ws,
+                                 size_t ws_bytes, hipStream_t stream);
+
+/* kernel_events: NULL, or 6 events as for dsa_decode_step_timed. */
+dsa_status dsa_decode_step_paged(const int8_t* iq, const int8_t* iw, const int8_t* ik_pool, const void* q,
+                                 const void* kv_pool, const int32_t* page_table, int64_t pool_pages,
+                                 const int32_t* ctx_len, int B, int Hi, int Di, int Hq, int Dk, int Dv,
+                                 int64_t N, int k, float scale, dsa_dtype dt, int32_t* scores, int32_t* idx,
+                                 float* out, void* ws, size_t ws_bytes, unsigned flags, hipStream_t stream,
+                                 hipEvent_t* kernel_events);
 
 /*
  * Copies the per-row stats of the last call that used `ws` into stats[0..B): which

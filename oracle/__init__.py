@@ -45,6 +45,8 @@ def _load(omp=False):
         lib.dsa_ref_sparse_attn.argtypes = [p, p, p, i32, i32, i32, i32, i64, i32, dbl, i32, p]
         lib.dsa_ref_decode_step.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32, i32,
                                             i64, i32, dbl, i32, p, p, p]
+        lib.dsa_ref_gather_pages.argtypes = [p, i64, p, i64, i32, i64, p]
+        lib.dsa_ref_gather_pages.restype = ctypes.c_int
         lib.dsa_ref_e4m3_to_f64.argtypes = [p, i64, p]
         lib.dsa_ref_e4m3_to_f64.restype = None
         for f in (lib.dsa_ref_index_scores, lib.dsa_ref_topk_select, lib.dsa_ref_sparse_attn,
@@ -154,3 +156,29 @@ def decode_step(iq, iw, ik, q, kv, ctx_len, k, Dv, scale, omp=False):
                                        B, Hi, Di, Hq, Dk, Dv, N, k, float(scale), dt,
                                        _ptr(scores), _ptr(idx), _ptr(out)), "decode_step")
     return scores, idx, out
+
+
+PAGE = 256  # positions per pool page (a 1,048,576-token pool held in 4,096 pages)
+
+
+def gather_pages(pool, page_table, N, page=PAGE):
+    """The contiguous cache [N, ...] that page_table describes in pool [pool_pages * page, ...]:
+    row s is pool row page_table[s // page] * page + s % page."""
+    pool = np.ascontiguousarray(pool)
+    page_table = _c(page_table, np.int32)
+    if pool.shape[0] % page != 0:
+        raise ValueError("the pool must hold whole pages")
+    if page_table.shape[0] * page < N:
+        raise ValueError("the table must cover N positions")
+    row_bytes = pool[0].nbytes
+    out = np.empty((N,) + pool.shape[1:], pool.dtype)
+    _check(_load().dsa_ref_gather_pages(_ptr(pool), row_bytes, _ptr(page_table), pool.shape[0] // page,
+                                        page, N, _ptr(out)), "gather_pages")
+    return out
+
+
+def decode_step_paged(iq, iw, ik_pool, q, kv_pool, page_table, ctx_len, k, Dv, scale, N):
+    """The step over paged pools: the contiguous step on the caches the table describes."""
+    ik = gather_pages(ik_pool, page_table, N)
+    kv = gather_pages(kv_pool, page_table, N)
+    return decode_step(iq, iw, ik, q, kv, ctx_len, k, Dv, scale)

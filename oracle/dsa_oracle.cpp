@@ -15,6 +15,12 @@
 //    so positions past it are never candidates.
 //  * Same model card, Speed section (MQA fold): at decode one shared latent row
 //    per position serves every head, as key (latent + rope) and as value (latent).
+//  * glm53-tensorfold-spark README, introduction and "What's new (2026-09-30)": the
+//    KV cache is one pool of fixed-size pages (1,048,576 tokens in 4,096 pages, so
+//    256 positions a page) shared by the sequences. A paged step reads a sequence's
+//    positions through its page table; it computes what the contiguous step
+//    computes on the cache the table describes, so the oracle gathers that cache
+//    and runs the contiguous step.
 //  * The pages leave the indexer arithmetic, the tie rule and the softmax precision
 //    open. This file takes the plainest reading: int8 query heads against one shared
 //    int8 key, ReLU, int8 per-head weight, sum over heads, an int32 result; order by
@@ -192,6 +198,20 @@ int dsa_ref_decode_step(const int8_t* iq, const int8_t* iw, const int8_t* ik, co
   rc = dsa_ref_topk_select(scores, ctx_len, B, N, k, idx);
   if (rc != REF_OK) return rc;
   return dsa_ref_sparse_attn(q, kv, idx, B, Hq, Dk, Dv, N, k, scale, dtype, out);
+}
+
+// The contiguous cache a page table describes: row s of `out` (s < N) is pool row
+// page_table[s / page] * page + s % page, row_bytes bytes each. A table entry
+// outside [0, pool_pages) is an error.
+int dsa_ref_gather_pages(const uint8_t* pool, int64_t row_bytes, const int32_t* page_table,
+                         int64_t pool_pages, int page, int64_t N, uint8_t* out) {
+  if (row_bytes < 1 || pool_pages < 1 || page < 1 || N < 1) return REF_BAD_ARG;
+  for (int64_t s = 0; s < N; ++s) {
+    const int64_t p = page_table[s / page];
+    if (p < 0 || p >= pool_pages) return REF_BAD_ARG;
+    std::memcpy(out + s * row_bytes, pool + (p * page + s % page) * row_bytes, (size_t)row_bytes);
+  }
+  return REF_OK;
 }
 
 }  // extern "C"

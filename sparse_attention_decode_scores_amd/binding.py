@@ -21,7 +21,8 @@ STATUS_NAMES = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED",
                 3: "DSA_ERR_WORKSPACE", 4: "DSA_ERR_HIP"}
 EXPORTED = ("dsa_status_string", "dsa_workspace_size", "dsa_index_scores", "dsa_topk_select",
             "dsa_sparse_attn", "dsa_decode_step", "dsa_decode_step_timed", "dsa_decode_step_noalloc",
-            "dsa_read_stats")
+            "dsa_read_stats", "dsa_index_scores_paged", "dsa_sparse_attn_paged", "dsa_decode_step_paged")
+PAGE_SIZE = 256  # positions per page of a paged pool (DSA_PAGE_SIZE)
 
 
 class DSAError(RuntimeError):
@@ -68,6 +69,11 @@ def load_library():
         lib.dsa_decode_step_noalloc.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i64, i32,
                                                 f32, i32, p, p, p, u32, p]
         lib.dsa_read_stats.argtypes = [p, sz, i32, p, p]
+        lib.dsa_index_scores_paged.argtypes = [p, p, p, p, i64, p, i32, i32, i32, i64, p, p]
+        lib.dsa_sparse_attn_paged.argtypes = [p, p, p, i64, p, i32, i32, i32, i32, i64, i32, f32, i32, p, p,
+                                              sz, p]
+        lib.dsa_decode_step_paged.argtypes = [p, p, p, p, p, p, i64, p, i32, i32, i32, i32, i32, i32, i64,
+                                              i32, f32, i32, p, p, p, p, sz, u32, p, p]
         for name in EXPORTED[2:]:
             getattr(lib, name).restype = i32
         _lib = lib
@@ -267,3 +273,97 @@ def dsa_read_stats(workspace, B, stream=None):
                             B, ctypes.cast(arr, ctypes.c_void_p), _stream(stream))
     _check(rc, "dsa_read_stats")
     return [{f: getattr(r, f) for f, _ in RowStats._fields_} for r in arr]
+
+
+def _paging(page_table, pools, N):
+    """Checks a page table (int32 on the GPU) against the pools ([pool_pages * 256, ...] each)
+    and the logical length N (default: every page of the table); returns (N, pool_pages)."""
+    torch = _torch()
+    _dev(page_table, "page_table", torch.int32)
+    rows = pools[0].shape[0]
+    if rows % PAGE_SIZE != 0 or any(p.shape[0] != rows for p in pools):
+        raise ValueError("the pools must hold the same whole number of %d-row pages" % PAGE_SIZE)
+    n_tab = page_table.numel()
+    N = n_tab * PAGE_SIZE if N is None else int(N)
+    if N < 1 or (N + PAGE_SIZE - 1) // PAGE_SIZE > n_tab:
+        raise ValueError("page_table must hold ceil(N / %d) entries" % PAGE_SIZE)
+    return N, rows // PAGE_SIZE
+
+
+def dsa_index_scores_paged(iq, iw, ik_pool, page_table, ctx_len, N=None, scores=None, stream=None):
+    """dsa_index_scores over an indexer key pool [pool_pages * 256, Di] read through
+    page_table [ceil(N / 256)] int32 (pool page of each logical page) -> scores [B,N] int32."""
+    torch = _torch()
+    lib = load_library()
+    B, Hi, Di = iq.shape
+    N, pool_pages = _paging(page_table, (ik_pool,), N)
+    lens = _host_lens(ctx_len, B)
+    if scores is None:
+        scores = torch.zeros((B, N), dtype=torch.int32, device=ik_pool.device)
+    rc = lib.dsa_index_scores_paged(_dev(iq, "iq", torch.int8), _dev(iw, "iw", torch.int8),
+                                    _dev(ik_pool, "ik_pool", torch.int8), _dev(page_table, "page_table"),
+                                    pool_pages, lens.ctypes.data_as(ctypes.c_void_p), B, Hi, Di, N,
+                                    _dev(scores, "scores", torch.int32), _stream(stream))
+    _check(rc, "dsa_index_scores_paged")
+    return scores
+
+
+def dsa_sparse_attn_paged(q, kv_pool, page_table, idx, Dv, scale, N=None, out=None, workspace=None,
+                          stream=None):
+    """dsa_sparse_attn over a latent pool [pool_pages * 256, Dk] read through page_table;
+    idx holds logical positions (< N)."""
+    torch = _torch()
+    lib = load_library()
+    B, Hq, Dk = q.shape
+    N, pool_pages = _paging(page_table, (kv_pool,), N)
+    k = idx.shape[1]
+    dt = _attn_dtype(q, kv_pool)
+    if out is None:
+        out = torch.empty((B, Hq, Dv), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = new_workspace(B, N, k, Hq, Dv, q.device)
+    rc = lib.dsa_sparse_attn_paged(_dev(q, "q"), _dev(kv_pool, "kv_pool"), _dev(page_table, "page_table"),
+                                   pool_pages, _dev(idx, "idx", torch.int32), B, Hq, Dk, Dv, N, k,
+                                   float(scale), dt, _dev(out, "out", torch.float32), _dev(workspace, "workspace"),
+                                   workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc, "dsa_sparse_attn_paged")
+    return out
+
+
+def dsa_decode_step_paged(iq, iw, ik_pool, q, kv_pool, page_table, ctx_len, k, Dv, scale, N=None,
+                          scores=None, idx=None, out=None, workspace=None, flags=0, stream=None,
+                          kernel_events=None):
+    """dsa_decode_step over paged pools (ik_pool [pool_pages * 256, Di], kv_pool
+    [pool_pages * 256, Dk]) read through one page table; returns (scores, idx, out) with
+    logical positions, as the contiguous call on the caches the table describes."""
+    torch = _torch()
+    lib = load_library()
+    B, Hi, Di = iq.shape
+    _, Hq, Dk = q.shape
+    N, pool_pages = _paging(page_table, (ik_pool, kv_pool), N)
+    lens = _host_lens(ctx_len, B)
+    dt = _attn_dtype(q, kv_pool)
+    dev = ik_pool.device
+    if scores is None:
+        scores = torch.zeros((B, N), dtype=torch.int32, device=dev)
+    if idx is None:
+        idx = torch.empty((B, k), dtype=torch.int32, device=dev)
+    if out is None:
+        out = torch.empty((B, Hq, Dv), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = new_workspace(B, N, k, Hq, Dv, dev)
+    evs = None
+    if kernel_events is not None:
+        if len(kernel_events) != 6:
+            raise ValueError("kernel_events must hold 6 events")
+        evs = ctypes.cast((ctypes.c_void_p * 6)(*[e.cuda_event for e in kernel_events]), ctypes.c_void_p)
+    rc = lib.dsa_decode_step_paged(_dev(iq, "iq", torch.int8), _dev(iw, "iw", torch.int8),
+                                   _dev(ik_pool, "ik_pool", torch.int8), _dev(q, "q"), _dev(kv_pool, "kv_pool"),
+                                   _dev(page_table, "page_table"), pool_pages,
+                                   lens.ctypes.data_as(ctypes.c_void_p), B, Hi, Di, Hq, Dk, Dv, N, k,
+                                   float(scale), dt, _dev(scores, "scores", torch.int32),
+                                   _dev(idx, "idx", torch.int32), _dev(out, "out", torch.float32),
+                                   _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                                   flags, _stream(stream), evs)
+    _check(rc, "dsa_decode_step_paged")
+    return scores, idx, out

@@ -123,6 +123,25 @@ dsa_status check_ws(void* ws, size_t ws_bytes, const Layout& L) {
   return DSA_OK;
 }
 
+// A sequence's page table into a paged pool (pages == nullptr: contiguous caches).
+struct Paging {
+  const int32_t* pages = nullptr;
+  int pool_pages = 0;
+};
+
+// Paged calls: a table of ceil(N / DSA_PAGE_SIZE) entries (N <= DSA_MAX_PAGES pages'
+// worth), a pool of at least one page whose rows an int32 counts, and (row_bytes > 0,
+// the indexer key pool) a pool the score kernels address with 32-bit offsets.
+dsa_status check_paging(const int32_t* pages, int64_t pool_pages, int64_t N, int64_t row_bytes, Paging* pg) {
+  if (pages == nullptr || !aligned(pages, 4) || pool_pages < 1) return DSA_ERR_INVALID_ARG;
+  if (pool_pages > INT32_MAX / kPageSize) return DSA_ERR_UNSUPPORTED;
+  if (N > (int64_t)DSA_MAX_PAGES * kPageSize) return DSA_ERR_UNSUPPORTED;
+  if (row_bytes > 0 && pool_pages * kPageSize * row_bytes >= ((int64_t)1 << 31)) return DSA_ERR_UNSUPPORTED;
+  pg->pages = pages;
+  pg->pool_pages = (int)pool_pages;
+  return DSA_OK;
+}
+
 // Chunking of the candidate pass for rows of at most nmax positions.
 struct ChunkPlan {
   int P, G, m;
@@ -203,8 +222,10 @@ void* device_scratch() {
 dsa_status run_scores(const int8_t* iq, const int8_t* iw, const int8_t* ik, const RowLens& lens,
                       int B, int Hi, int Di, int64_t N, int nmax, int32_t* scores, bool cand,
                       const ChunkPlan& cp, uint64_t* cbuf, uint64_t* xbuf, hipStream_t s,
-                      KTimer t = {}, ChunkSum* sums = nullptr) {
+                      KTimer t = {}, ChunkSum* sums = nullptr, Paging pg = {}) {
   ScoreArgs a;
+  a.pages = pg.pages;
+  a.pool_pages = pg.pool_pages;
   a.iq = iq;
   a.iw = iw;
   a.ik = ik;
@@ -230,7 +251,7 @@ dsa_status run_scores(const int8_t* iq, const int8_t* iw, const int8_t* ik, cons
     a.b0 = 0;
     a.Bg = 1;
     a.sums = sums;
-    return hip_status(launch_score_row(a, MT, KT, kScoreRowDepth, a.G, s, t));
+    return hip_status(launch_score_row(a, MT, KT, a.G, s, t));
   }
   const int bg = rows_per_score_launch(Hi, Di, B);
   for (int b0 = 0; b0 < B; b0 += bg) {
@@ -245,17 +266,18 @@ dsa_status run_scores(const int8_t* iq, const int8_t* iw, const int8_t* ik, cons
   return DSA_OK;
 }
 
-bool cand_fits(int Hi, int Di, int B, const ChunkPlan& cp, bool fused) {
+bool cand_fits(int Hi, int Di, int B, const ChunkPlan& cp, bool fused, bool paged = false) {
   size_t need;
   if (fused && B == 1) {
     if (cp.P > score_row_max_chunk()) return false;
     // the kernel addresses a chunk's keys, interleaved over the row, by 32-bit offsets
-    if ((int64_t)cp.G * cp.P * Di >= ((int64_t)1 << 31)) return false;
-    need = score_row_lds_bytes(cp.P);
+    // (a paged pool's size is checked against the same bound by check_paging)
+    if (!paged && (int64_t)cp.G * cp.P * Di >= ((int64_t)1 << 31)) return false;
+    need = score_row_lds_bytes(cp.P, paged);
   } else if (fused) {
     if (cp.P > score_max_chunk()) return false;
     const int bg = rows_per_score_launch(Hi, Di, B);
-    need = score_lds_bytes((Hi + 31) / 32, (Di + 31) / 32, bg, cp.P, true);
+    need = score_lds_bytes((Hi + 31) / 32, (Di + 31) / 32, bg, cp.P, true, paged);
   } else {
     if (cp.P > chunk_cand_max_chunk()) return false;
     need = 8192 + (size_t)cp.P * 4;
@@ -264,8 +286,10 @@ bool cand_fits(int Hi, int Di, int B, const ChunkPlan& cp, bool fused) {
 }
 
 AttnArgs attn_args(const void* q, const void* kv, int64_t N, int Hq, int Dk, int Dv, float scale,
-                   int k, uint8_t* w, const Layout& L) {
+                   int k, uint8_t* w, const Layout& L, Paging pg = {}) {
   AttnArgs at;
+  at.pages = pg.pages;
+  at.pool_pages = pg.pool_pages;
   at.q = q;
   at.kv = kv;
   at.N = N;
@@ -323,6 +347,89 @@ SelArgs sel_args(const int32_t* scores, const RowLens& lens, int64_t N, int k, i
   return a;
 }
 
+// The three calls on contiguous caches (pages == nullptr) or, through a page table,
+// on paged pools (ik and kv are then the pools).
+dsa_status index_scores_impl(const int8_t* iq, const int8_t* iw, const int8_t* ik, const int32_t* ctx_len, int B,
+                             int Hi, int Di, int64_t N, int32_t* scores, hipStream_t stream,
+                             const int32_t* pages, int64_t pool_pages) {
+  RowLens lens;
+  int nmax = 0;
+  dsa_status st = check_rows(ctx_len, B, N, &lens, &nmax);
+  if (st != DSA_OK) return st;
+  if ((st = check_index(iq, iw, ik, Hi, Di)) != DSA_OK) return st;
+  if (!scores || !aligned(scores, 4)) return DSA_ERR_INVALID_ARG;
+  Paging pg;
+  if (pages != nullptr && (st = check_paging(pages, pool_pages, N, Di, &pg)) != DSA_OK) return st;
+  ChunkPlan cp{64, 1, 32, 0};
+  return run_scores(iq, iw, ik, lens, B, Hi, Di, N, nmax, scores, false, cp, nullptr, nullptr,
+                    stream, {}, nullptr, pg);
+}
+
+dsa_status sparse_attn_impl(const void* q, const void* kv, const int32_t* idx, int B, int Hq, int Dk, int Dv,
+                            int64_t N, int k, float scale, dsa_dtype dt, float* out, void* ws, size_t ws_bytes,
+                            hipStream_t stream, const int32_t* pages, int64_t pool_pages) {
+  if (B < 1 || B > DSA_MAX_BATCH || N < 1 || N > INT32_MAX || k < 1 || k > DSA_MAX_K || !idx || !out)
+    return DSA_ERR_INVALID_ARG;
+  AttnChoice ch;
+  dsa_status st = check_attn(q, kv, Hq, Dk, Dv, scale, dt, &ch);
+  if (st != DSA_OK) return st;
+  Paging pg;
+  if (pages != nullptr && (st = check_paging(pages, pool_pages, N, 0, &pg)) != DSA_OK) return st;
+  const Layout L = layout(B, N, k, Hq, Dv);
+  if ((st = check_ws(ws, ws_bytes, L)) != DSA_OK) return st;
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  AttnArgs at = attn_args(q, kv, N, Hq, Dk, Dv, scale, k, w, L, pg);
+  set_attn_path(&at, ch, k, B);
+  int32_t* bad = reinterpret_cast<int32_t*>(w + L.bad);
+  if (launch_attend_idx(idx, k, bad, at, ch, B, stream) != hipSuccess) return DSA_ERR_HIP;
+  return hip_status(combine(at, bad, reinterpret_cast<RowStats*>(w + L.stats), out, B, stream));
+}
+
+dsa_status decode_step_impl(const int8_t* iq, const int8_t* iw, const int8_t* ik, const void* q, const void* kv,
+                            const int32_t* ctx_len, int B, int Hi, int Di, int Hq, int Dk, int Dv, int64_t N,
+                            int k, float scale, dsa_dtype dt, int32_t* scores, int32_t* idx, float* out, void* ws,
+                            size_t ws_bytes, unsigned flags, hipStream_t stream, hipEvent_t* kernel_events,
+                            const int32_t* pages, int64_t pool_pages) {
+  RowLens lens;
+  int nmax = 0;
+  dsa_status st = check_rows(ctx_len, B, N, &lens, &nmax);
+  if (st != DSA_OK) return st;
+  if ((st = check_index(iq, iw, ik, Hi, Di)) != DSA_OK) return st;
+  if (!scores || !idx || !out || k < 1 || k > DSA_MAX_K || (flags & ~DSA_FLAG_FORCE_FALLBACK))
+    return DSA_ERR_INVALID_ARG;
+  AttnChoice ch;
+  if ((st = check_attn(q, kv, Hq, Dk, Dv, scale, dt, &ch)) != DSA_OK) return st;
+  Paging pg;
+  if (pages != nullptr && (st = check_paging(pages, pool_pages, N, Di, &pg)) != DSA_OK) return st;
+  const Layout L = layout(B, N, k, Hq, Dv);
+  if ((st = check_ws(ws, ws_bytes, L)) != DSA_OK) return st;
+  KTimer tm[3];
+  if (kernel_events != nullptr) {
+    for (int i = 0; i < 6; ++i)
+      if (kernel_events[i] == nullptr) return DSA_ERR_INVALID_ARG;
+    for (int i = 0; i < 3; ++i) tm[i] = KTimer{kernel_events[2 * i], kernel_events[2 * i + 1]};
+  }
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  const ChunkPlan cp = chunk_plan(nmax, k, B == 1, Di);
+  // (the forced exhaustive path still gets the candidate score pass: it changes the
+  // selection only, and its narrowing takes a threshold from the union)
+  const bool have = cand_fits(Hi, Di, B, cp, true, pg.pages != nullptr);
+  // the one-row score pass also leaves per-chunk summaries for the selection
+  const bool sums = have && B == 1;
+  st = run_scores(iq, iw, ik, lens, B, Hi, Di, N, nmax, scores, have, cp,
+                  reinterpret_cast<uint64_t*>(w + L.cand), reinterpret_cast<uint64_t*>(w + L.xc),
+                  stream, tm[0], sums ? reinterpret_cast<ChunkSum*>(w + L.sums) : nullptr, pg);
+  if (st != DSA_OK) return st;
+  SelArgs sa = sel_args(scores, lens, N, k, idx, w, L, cp, have, flags, sums);
+  // no ranking workgroups: the attention splits' windows are the output slots, so
+  // they write the indices and the row's record themselves
+  sa.R = 0;
+  AttnArgs at = attn_args(q, kv, N, Hq, Dk, Dv, scale, k, w, L, pg);
+  set_attn_path(&at, ch, k, B);
+  if (launch_select(sa, at, ch, B, stream, tm[1]) != hipSuccess) return DSA_ERR_HIP;
+  return hip_status(combine(at, nullptr, nullptr, out, B, stream, tm[2]));
+}
+
 }  // namespace
 }  // namespace dsa
 
@@ -351,15 +458,14 @@ size_t dsa_workspace_size(int B, int64_t N, int k, int Hq, int Dv) {
 dsa_status dsa_index_scores(const int8_t* iq, const int8_t* iw, const int8_t* ik,
                             const int32_t* ctx_len, int B, int Hi, int Di, int64_t N,
                             int32_t* scores, hipStream_t stream) {
-  RowLens lens;
-  int nmax = 0;
-  dsa_status st = check_rows(ctx_len, B, N, &lens, &nmax);
-  if (st != DSA_OK) return st;
-  if ((st = check_index(iq, iw, ik, Hi, Di)) != DSA_OK) return st;
-  if (!scores || !aligned(scores, 4)) return DSA_ERR_INVALID_ARG;
-  ChunkPlan cp{64, 1, 32, 0};
-  return run_scores(iq, iw, ik, lens, B, Hi, Di, N, nmax, scores, false, cp, nullptr, nullptr,
-                    stream);
+  return index_scores_impl(iq, iw, ik, ctx_len, B, Hi, Di, N, scores, stream, nullptr, 0);
+}
+
+dsa_status dsa_index_scores_paged(const int8_t* iq, const int8_t* iw, const int8_t* ik_pool,
+                                  const int32_t* page_table, int64_t pool_pages, const int32_t* ctx_len,
+                                  int B, int Hi, int Di, int64_t N, int32_t* scores, hipStream_t stream) {
+  if (page_table == nullptr) return DSA_ERR_INVALID_ARG;
+  return index_scores_impl(iq, iw, ik_pool, ctx_len, B, Hi, Di, N, scores, stream, page_table, pool_pages);
 }
 
 dsa_status dsa_topk_select(const int32_t* scores, const int32_t* ctx_len, int B, int64_t N, int k,
@@ -397,19 +503,16 @@ dsa_status dsa_topk_select(const int32_t* scores, const int32_t* ctx_len, int B,
 dsa_status dsa_sparse_attn(const void* q, const void* kv, const int32_t* idx, int B, int Hq, int Dk,
                            int Dv, int64_t N, int k, float scale, dsa_dtype dt, float* out,
                            void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (B < 1 || B > DSA_MAX_BATCH || N < 1 || N > INT32_MAX || k < 1 || k > DSA_MAX_K || !idx || !out)
-    return DSA_ERR_INVALID_ARG;
-  AttnChoice ch;
-  dsa_status st = check_attn(q, kv, Hq, Dk, Dv, scale, dt, &ch);
-  if (st != DSA_OK) return st;
-  const Layout L = layout(B, N, k, Hq, Dv);
-  if ((st = check_ws(ws, ws_bytes, L)) != DSA_OK) return st;
-  uint8_t* w = static_cast<uint8_t*>(ws);
-  AttnArgs at = attn_args(q, kv, N, Hq, Dk, Dv, scale, k, w, L);
-  set_attn_path(&at, ch, k, B);
-  int32_t* bad = reinterpret_cast<int32_t*>(w + L.bad);
-  if (launch_attend_idx(idx, k, bad, at, ch, B, stream) != hipSuccess) return DSA_ERR_HIP;
-  return hip_status(combine(at, bad, reinterpret_cast<RowStats*>(w + L.stats), out, B, stream));
+  return sparse_attn_impl(q, kv, idx, B, Hq, Dk, Dv, N, k, scale, dt, out, ws, ws_bytes, stream, nullptr, 0);
+}
+
+dsa_status dsa_sparse_attn_paged(const void* q, const void* kv_pool, const int32_t* page_table,
+                                 int64_t pool_pages, const int32_t* idx, int B, int Hq, int Dk, int Dv,
+                                 int64_t N, int k, float scale, dsa_dtype dt, float* out, void* ws,
+                                 size_t ws_bytes, hipStream_t stream) {
+  if (page_table == nullptr) return DSA_ERR_INVALID_ARG;
+  return sparse_attn_impl(q, kv_pool, idx, B, Hq, Dk, Dv, N, k, scale, dt, out, ws, ws_bytes, stream, page_table,
+                          pool_pages);
 }
 
 dsa_status dsa_decode_step_timed(const int8_t* iq, const int8_t* iw, const int8_t* ik,
@@ -418,42 +521,19 @@ dsa_status dsa_decode_step_timed(const int8_t* iq, const int8_t* iw, const int8_
                                  float scale, dsa_dtype dt, int32_t* scores, int32_t* idx,
                                  float* out, void* ws, size_t ws_bytes, unsigned flags,
                                  hipStream_t stream, hipEvent_t* kernel_events) {
-  RowLens lens;
-  int nmax = 0;
-  dsa_status st = check_rows(ctx_len, B, N, &lens, &nmax);
-  if (st != DSA_OK) return st;
-  if ((st = check_index(iq, iw, ik, Hi, Di)) != DSA_OK) return st;
-  if (!scores || !idx || !out || k < 1 || k > DSA_MAX_K || (flags & ~DSA_FLAG_FORCE_FALLBACK))
-    return DSA_ERR_INVALID_ARG;
-  AttnChoice ch;
-  if ((st = check_attn(q, kv, Hq, Dk, Dv, scale, dt, &ch)) != DSA_OK) return st;
-  const Layout L = layout(B, N, k, Hq, Dv);
-  if ((st = check_ws(ws, ws_bytes, L)) != DSA_OK) return st;
-  KTimer tm[3];
-  if (kernel_events != nullptr) {
-    for (int i = 0; i < 6; ++i)
-      if (kernel_events[i] == nullptr) return DSA_ERR_INVALID_ARG;
-    for (int i = 0; i < 3; ++i) tm[i] = KTimer{kernel_events[2 * i], kernel_events[2 * i + 1]};
-  }
-  uint8_t* w = static_cast<uint8_t*>(ws);
-  const ChunkPlan cp = chunk_plan(nmax, k, B == 1, Di);
-  // (the forced exhaustive path still gets the candidate score pass: it changes the
-  // selection only, and its narrowing takes a threshold from the union)
-  const bool have = cand_fits(Hi, Di, B, cp, true);
-  // the one-row score pass also leaves per-chunk summaries for the selection
-  const bool sums = have && B == 1;
-  st = run_scores(iq, iw, ik, lens, B, Hi, Di, N, nmax, scores, have, cp,
-                  reinterpret_cast<uint64_t*>(w + L.cand), reinterpret_cast<uint64_t*>(w + L.xc),
-                  stream, tm[0], sums ? reinterpret_cast<ChunkSum*>(w + L.sums) : nullptr);
-  if (st != DSA_OK) return st;
-  SelArgs sa = sel_args(scores, lens, N, k, idx, w, L, cp, have, flags, sums);
-  // no ranking workgroups: the attention splits' windows are the output slots, so
-  // they write the indices and the row's record themselves
-  sa.R = 0;
-  AttnArgs at = attn_args(q, kv, N, Hq, Dk, Dv, scale, k, w, L);
-  set_attn_path(&at, ch, k, B);
-  if (launch_select(sa, at, ch, B, stream, tm[1]) != hipSuccess) return DSA_ERR_HIP;
-  return hip_status(combine(at, nullptr, nullptr, out, B, stream, tm[2]));
+  return decode_step_impl(iq, iw, ik, q, kv, ctx_len, B, Hi, Di, Hq, Dk, Dv, N, k, scale, dt, scores, idx, out, ws,
+                          ws_bytes, flags, stream, kernel_events, nullptr, 0);
+}
+
+dsa_status dsa_decode_step_paged(const int8_t* iq, const int8_t* iw, const int8_t* ik_pool, const void* q,
+                                 const void* kv_pool, const int32_t* page_table, int64_t pool_pages,
+                                 const int32_t* ctx_len, int B, int Hi, int Di, int Hq, int Dk, int Dv,
+                                 int64_t N, int k, float scale, dsa_dtype dt, int32_t* scores, int32_t* idx,
+                                 float* out, void* ws, size_t ws_bytes, unsigned flags, hipStream_t stream,
+                                 hipEvent_t* kernel_events) {
+  if (page_table == nullptr) return DSA_ERR_INVALID_ARG;
+  return decode_step_impl(iq, iw, ik_pool, q, kv_pool, ctx_len, B, Hi, Di, Hq, Dk, Dv, N, k, scale, dt, scores, idx,
+                          out, ws, ws_bytes, flags, stream, kernel_events, page_table, pool_pages);
 }
 
 dsa_status dsa_decode_step(const int8_t* iq, const int8_t* iw, const int8_t* ik, const void* q,

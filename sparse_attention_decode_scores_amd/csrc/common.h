@@ -17,6 +17,19 @@ constexpr int kMaxSplitRows = 128;     // selected rows one attention split may 
 // compute unit of the chip (256 on gfx950). A constant, not the device's count, so
 // that the split of the sum, and with it every rounding, is the same on any device.
 constexpr int kSplitGrid = 256;
+// Paged caches: a pool of pages of kPageSize positions each (a 1,048,576-token pool
+// held in 4,096 pages), and a sequence's page table mapping its logical page j
+// (positions 256j .. 256j + 255) to a pool page.
+constexpr int kPageSize = 256;
+constexpr int kPageShift = 8;
+
+// Pool row of logical position pos through the page table; entries outside
+// [0, pool_pages) are clamped into the pool, so a bad table never reads past it.
+__device__ __forceinline__ uint32_t page_row(const int32_t* __restrict__ pages, int pool_pages, int64_t pos) {
+  int32_t e = pages[pos >> kPageShift];
+  e = e < 0 ? 0 : (e >= pool_pages ? pool_pages - 1 : e);
+  return (uint32_t)e * (uint32_t)kPageSize + (uint32_t)(pos & (kPageSize - 1));
+}
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));

@@ -52,6 +52,10 @@ struct ScoreArgs {
   int P;           // positions per chunk (multiple of 64; of 32 for the one-row kernel)
   int G;           // chunks per row
   int m;           // candidates kept per chunk
+  // paged key cache: ik is the pool ([pool_pages * kPageSize][Di]) and pages[j] the
+  // pool page of logical page j (kernels instantiated for paging only)
+  const int32_t* pages;
+  int pool_pages;
 };
 
 // Geometry of chunk c of a row of n positions in units of 32 positions: with ilv,
@@ -81,16 +85,15 @@ constexpr int kScoreQBytes = 65536;
 hipError_t launch_score(const ScoreArgs& a, int MT, int KT, bool cand, int grid, hipStream_t s,
                         KTimer t = {});
 // One query row with candidates (the decode hot path): chunks of P = 32u positions,
-// D units of 32 keys in flight per wave (2 or 3; two measured faster: three keep
-// more requests queued without raising the key stream's rate).
-hipError_t launch_score_row(const ScoreArgs& a, int MT, int KT, int D, int grid, hipStream_t s,
-                            KTimer t = {});
+// kScoreRowDepth units of 32 keys in flight per wave (2 or 3; two measured faster:
+// three keep more requests queued without raising the key stream's rate).
+hipError_t launch_score_row(const ScoreArgs& a, int MT, int KT, int grid, hipStream_t s, KTimer t = {});
 constexpr int kScoreRowDepth = 2;
-size_t score_row_lds_bytes(int P);
+size_t score_row_lds_bytes(int P, bool paged);
 int score_row_max_chunk();
 int score_max_chunk();        // longest chunk the score kernel's candidate pass takes
 int chunk_cand_max_chunk();   // the same for the stand-alone candidate kernel
-size_t score_lds_bytes(int MT, int KT, int Bg, int P, bool cand);
+size_t score_lds_bytes(int MT, int KT, int Bg, int P, bool cand, bool paged);
 
 // Stand-alone candidate pass over scores already in memory.
 struct CandArgs {
@@ -114,6 +117,10 @@ struct AttnArgs {
   float* part_o;    // [B][S][Hp*Dv] unnormalised output of each split (layout per `frag`)
   int S;            // splits per row
   int frag;         // 1: part_o in matrix-core accumulator order with Hp = Hq rounded to 16
+  // paged latent cache, or nullptr: kv is the pool ([pool_pages * kPageSize][Dk]) and
+  // pages[j] the pool page of logical page j
+  const int32_t* pages;
+  int pool_pages;
 };
 
 enum AttnKind { ATTN_NONE = 0, ATTN_MFMA_BF16 = 1, ATTN_GENERIC_F32 = 2, ATTN_GENERIC_BF16 = 3 };

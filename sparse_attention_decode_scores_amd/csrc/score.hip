@@ -24,6 +24,7 @@ namespace dsa {
 
 constexpr int kScoreBlock = 512;
 constexpr int kScoreWaves = kScoreBlock / 64;
+constexpr int kMaxTiles = kChunkPerThread * kScoreBlock / 64;  // 64-key tiles of the longest chunk
 static_assert(kScoreQBytes % (16 * kScoreBlock) == 0, "query staging slots");
 
 namespace {
@@ -47,13 +48,29 @@ __device__ __forceinline__ void load_keys(v4i (&kf)[2][KT], __amdgpu_buffer_rsrc
   }
 }
 
+// The same for a paged pool: the tile's 64 keys are consecutive pool rows starting
+// `base` bytes into the pool (a 64-aligned tile lies inside one page); a base past
+// the pool gives zeros.
+template <int KT>
+__device__ __forceinline__ void load_keys_at(v4i (&kf)[2][KT], __amdgpu_buffer_rsrc_t rs, uint32_t base, int Di) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const uint32_t off = base + (uint32_t)((32 * t + (lane & 31)) * Di + 16 * (lane >> 5));
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+      kf[t][kt] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 32 * kt, 0, 0));
+  }
+}
+
 }  // namespace
 
 // NB: key tile buffers per wave (3, rotating, refilled as each is consumed; or 1
 // when a chunk has at most one 64-key tile per wave, so no request is issued for
 // tiles past the chunk: those requests returned zeros but took the address units'
-// time ahead of the query requests of the waves behind)
-template <int MT, int KT, bool CAND, bool ONE, int NB>
+// time ahead of the query requests of the waves behind). PG: the keys live in a
+// paged pool (a.ik) behind the page table a.pages.
+template <int MT, int KT, bool CAND, bool ONE, int NB, bool PG>
 __global__ __launch_bounds__(kScoreBlock) void k_score(ScoreArgs a) {
   constexpr int HP = 32 * MT;  // heads padded to whole tiles (padding has q = 0, w = 0)
   constexpr int DI = 32 * KT;
@@ -65,7 +82,9 @@ __global__ __launch_bounds__(kScoreBlock) void k_score(ScoreArgs a) {
   Smem& csm = *reinterpret_cast<Smem*>(smem);
   int8_t* qs = reinterpret_cast<int8_t*>(smem + align16(sizeof(Smem)));       // [Bg][HP][DIP]
   int32_t* wsm = reinterpret_cast<int32_t*>(qs + a.Bg * HP * DIP);             // [Bg][HP] head weights
-  int32_t* sc = wsm + a.Bg * HP;                                               // [Bg][P]
+  // paged: pool byte offset of each 64-key tile of the chunk
+  uint32_t* toff = reinterpret_cast<uint32_t*>(wsm + a.Bg * HP);              // [kMaxTiles] (PG)
+  int32_t* sc = wsm + a.Bg * HP + (PG ? kMaxTiles : 0);                       // [Bg][P]
   uint32_t* hist = reinterpret_cast<uint32_t*>(sc + a.Bg * a.P);              // [Bg][kHistBins]
   using CandSmem = BlockCandSmem<kScoreBlock>;
   CandSmem& bsm = *reinterpret_cast<CandSmem*>(hist + a.Bg * kHistBins);
@@ -103,14 +122,34 @@ __global__ __launch_bounds__(kScoreBlock) void k_score(ScoreArgs a) {
   const int wh = wi % HP < a.Hi ? wi % HP : a.Hi - 1;
   const int8_t wv = a.iw[(int64_t)(a.b0 + wi / HP) * a.Hi + wh];
 
-  // buffer resource word 3 for gfx9 raw buffers: 32-bit data format, no swizzle
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<int8_t*>(a.ik + cbeg * a.Di), (short)0, clen * a.Di, 0x00020000);
+  // buffer resource word 3 for gfx9 raw buffers: 32-bit data format, no swizzle.
+  // Contiguous keys: the resource covers the chunk's valid keys. Paged: it covers
+  // the pool, tile tp starts at pool byte tile_base(tp), and a tile past the chunk
+  // gets an offset past the pool (zeros). The first tiles' table entries are read
+  // per wave; the rest are staged in LDS (toff) for the refills.
+  const uint32_t pool_bytes = PG ? (uint32_t)a.pool_pages * (uint32_t)kPageSize * (uint32_t)a.Di : 0u;
+  const __amdgpu_buffer_rsrc_t rs =
+      PG ? __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(a.ik), (short)0, (int)pool_bytes, 0x00020000)
+         : __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(a.ik + cbeg * a.Di), (short)0, clen * a.Di,
+                                             0x00020000);
+  auto tile_base = [&](int tp) -> uint32_t {
+    return tp < npairs ? page_row(a.pages, a.pool_pages, cbeg + 64 * tp) * (uint32_t)a.Di : pool_bytes;
+  };
   v4i kb0[2][KT], kb1[2][KT], kb2[2][KT];
-  load_keys<KT>(kb0, rs, wave, a.Di);
-  if constexpr (NB > 1) {
-    load_keys<KT>(kb1, rs, wave + kScoreWaves, a.Di);
-    load_keys<KT>(kb2, rs, wave + 2 * kScoreWaves, a.Di);
+  uint32_t tb = 0;  // paged: thread t's tile offset, stored to LDS below
+  if constexpr (PG) {
+    load_keys_at<KT>(kb0, rs, tile_base(wave), a.Di);
+    if constexpr (NB > 1) {
+      load_keys_at<KT>(kb1, rs, tile_base(wave + kScoreWaves), a.Di);
+      load_keys_at<KT>(kb2, rs, tile_base(wave + 2 * kScoreWaves), a.Di);
+    }
+    if (tid < npairs) tb = tile_base(tid);
+  } else {
+    load_keys<KT>(kb0, rs, wave, a.Di);
+    if constexpr (NB > 1) {
+      load_keys<KT>(kb1, rs, wave + kScoreWaves, a.Di);
+      load_keys<KT>(kb2, rs, wave + 2 * kScoreWaves, a.Di);
+    }
   }
 
   if (CAND) {
@@ -126,6 +165,8 @@ __global__ __launch_bounds__(kScoreBlock) void k_score(ScoreArgs a) {
     if (i < nq) *(v4i*)(qs + hrow * DIP + 16 * part) = h < a.Hi && 16 * part < a.Di ? qv[j] : v4i{0, 0, 0, 0};
   }
   if (tid < a.Bg * HP) wsm[tid] = tid % HP < a.Hi ? (int32_t)wv : 0;
+  if constexpr (PG)
+    if (tid < npairs) toff[tid] = tb;
   lds_barrier();
 
   // A fragments and weights of a single row stay in registers for the whole chunk.
@@ -229,7 +270,14 @@ __global__ __launch_bounds__(kScoreBlock) void k_score(ScoreArgs a) {
         a.scores[(int64_t)(a.b0 + bb) * a.N + pos] = val;
       }
     }
-    if constexpr (NB > 1) load_keys<KT>(cur, rs, tp + 3 * kScoreWaves, a.Di);
+    if constexpr (NB > 1) {
+      if constexpr (PG) {
+        const int tn = tp + 3 * kScoreWaves;
+        load_keys_at<KT>(cur, rs, tn < npairs ? toff[tn] : pool_bytes, a.Di);
+      } else {
+        load_keys<KT>(cur, rs, tp + 3 * kScoreWaves, a.Di);
+      }
+    }
   };
 
   if constexpr (NB == 1) {
@@ -333,13 +381,25 @@ __device__ __forceinline__ void load_unit(v4i (&kf)[KT], __amdgpu_buffer_rsrc_t 
     kf[kt] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 32 * kt, 0, 0));
 }
 
+// The same for a paged pool: the unit's 32 keys are consecutive pool rows starting
+// `base` bytes into the pool (a 32-aligned unit lies inside one page); a base past
+// the pool gives zeros.
+template <int KT>
+__device__ __forceinline__ void load_unit_at(v4i (&kf)[KT], __amdgpu_buffer_rsrc_t rs, uint32_t base, int Di) {
+  const int lane = lane_id();
+  const uint32_t off = base + (uint32_t)((lane & 31) * Di + 16 * (lane >> 5));
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt)
+    kf[kt] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 32 * kt, 0, 0));
+}
+
 }  // namespace
 
 // The arguments that the first requests need come first, as separate scalars: the
 // leading arguments can be preloaded into scalar registers at wave launch, so the
 // query and key requests need not wait for a read of the argument block (a.iq,
 // a.iw, a.ik, a.lens.n[0], a.G, a.P, a.Hi and a.Di, passed again).
-template <int MT, int KT, int D>
+template <int MT, int KT, int D, bool PG>
 __global__ __launch_bounds__(kScoreBlock) void k_score_row(const int8_t* __restrict__ iq,
                                                            const int8_t* __restrict__ iw,
                                                            const int8_t* __restrict__ ik, int n, int G, int P,
@@ -357,6 +417,7 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(const int8_t* __restr
   constexpr int DI = 32 * KT, DIP = DI + 16;
   int8_t* qs = reinterpret_cast<int8_t*>(&rsm) + align16(sizeof(RowCandSmem));  // [32 MT][DIP]
   int32_t* wsm = reinterpret_cast<int32_t*>(qs + 64 * (256 + 16));               // [64] head weights
+  uint32_t* uoff = reinterpret_cast<uint32_t*>(wsm + 64);                        // [kMaxUnits] (PG)
 
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   // a batch of one: the row is row 0, a constant, so that every argument address is
@@ -392,6 +453,19 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(const int8_t* __restr
   }
   int wl = 0;
   if (wave == 0) wl = (int)iw[(int64_t)b * Hi + (lane < Hi ? lane : Hi - 1)];
+  // Paged keys (PG): the resource covers the pool, the chunk's unit j starts at pool
+  // byte unit_base(j) (the row's unit c + jG is slot (c + jG) % 8 of logical page
+  // (c + jG) / 8), and a unit past the chunk gets an offset past the pool (zeros).
+  // Thread t reads unit t's table entry for the LDS list the refills use; each wave
+  // reads its first units' entries itself.
+  const uint32_t pool_bytes = PG ? (uint32_t)a.pool_pages * (uint32_t)kPageSize * (uint32_t)Di : 0u;
+  auto unit_base = [&](int j) -> uint32_t {
+    return j < units ? page_row(a.pages, a.pool_pages, (int64_t)kUnit * (c + (int64_t)j * G)) * (uint32_t)Di
+                     : pool_bytes;
+  };
+  uint32_t ub = 0;
+  if constexpr (PG)
+    if (tid < units) ub = unit_base(tid);
 
   // the histogram is shared by the waves: cleared before any of them adds to it
   for (int i = tid; i < kHistBins + kHistGroups; i += kScoreBlock) hist[i] = 0;  // and hgroup
@@ -401,12 +475,19 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(const int8_t* __restr
   }
   lds_barrier();
 
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<int8_t*>(ik + cbeg * Di), (short)0, span * Di, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs =
+      PG ? __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(ik), (short)0, (int)pool_bytes, 0x00020000)
+         : __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(ik + cbeg * Di), (short)0, span * Di, 0x00020000);
   v4i kb0[KT], kb1[KT], kb2[KT];
-  load_unit<KT>(kb0, rs, wave, js, Di);
-  load_unit<KT>(kb1, rs, wave + kScoreWaves, js, Di);
-  if constexpr (D == 3) load_unit<KT>(kb2, rs, wave + 2 * kScoreWaves, js, Di);
+  if constexpr (PG) {
+    load_unit_at<KT>(kb0, rs, unit_base(wave), Di);
+    load_unit_at<KT>(kb1, rs, unit_base(wave + kScoreWaves), Di);
+    if constexpr (D == 3) load_unit_at<KT>(kb2, rs, unit_base(wave + 2 * kScoreWaves), Di);
+  } else {
+    load_unit<KT>(kb0, rs, wave, js, Di);
+    load_unit<KT>(kb1, rs, wave + kScoreWaves, js, Di);
+    if constexpr (D == 3) load_unit<KT>(kb2, rs, wave + 2 * kScoreWaves, js, Di);
+  }
 
   // the query into LDS: head h's dims [0, Di), then zeros for dims [Di, DI) (the
   // last key fragment's upper half there reads the next key's dims or zeros)
@@ -420,6 +501,8 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(const int8_t* __restr
   }
   if (Di < DI && tid < Hi) *reinterpret_cast<v4i*>(qs + tid * DIP + Di) = v4i{0, 0, 0, 0};
   if (wave == 0) wsm[lane] = lane < Hi ? wl : 0;
+  if constexpr (PG)
+    if (tid < units) uoff[tid] = ub;
   lds_barrier();
   v4i qreg[MT][KT];
 #pragma unroll
@@ -469,7 +552,10 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(const int8_t* __restr
           acc[mt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(qreg[mt][kt], kf[kt], acc[mt], 0, 0, 0);
     }
     const int jn = __builtin_amdgcn_readfirstlane((int)nxt);
-    load_unit<KT>(kf, rs, jn, js, Di);
+    if constexpr (PG)
+      load_unit_at<KT>(kf, rs, jn < units ? uoff[jn] : pool_bytes, Di);
+    else
+      load_unit<KT>(kf, rs, jn, js, Di);
     if (live) {
       // two independent multiply-add chains (left to itself the compiler pairs the
       // products with three-input adds, 2.5 instructions per head instead of 2)
@@ -622,18 +708,20 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(const int8_t* __restr
   }
 }
 
-size_t score_row_lds_bytes(int P) {
-  // ... + the staged query at its largest (64 heads, rows of 256 + 16 bytes)
+size_t score_row_lds_bytes(int P, bool paged) {
+  // ... + the staged query at its largest (64 heads, rows of 256 + 16 bytes), the
+  // weights and, paged, the units' pool offsets
   return align16(sizeof(ChunkSmem<kScoreBlock>)) + align16((size_t)P * 4) + (size_t)(kHistBins + kHistGroups) * 4 +
-         align16(sizeof(RowCandSmem)) + (size_t)64 * (256 + 16) + 64 * 4 + 16;
+         align16(sizeof(RowCandSmem)) + (size_t)64 * (256 + 16) + 64 * 4 + (paged ? (size_t)kMaxUnits * 4 : 0) + 16;
 }
 
 int score_row_max_chunk() { return kMaxUnits * kUnit; }
 
 template <int MT, int KT>
-static hipError_t launch_score_row_t(const ScoreArgs& a, int D, int grid, hipStream_t s, KTimer t) {
-  auto fn = D == 3 ? k_score_row<MT, KT, 3> : k_score_row<MT, KT, 2>;
-  const size_t lds = score_row_lds_bytes(a.P);
+static hipError_t launch_score_row_t(const ScoreArgs& a, int grid, hipStream_t s, KTimer t) {
+  const bool paged = a.pages != nullptr;
+  auto fn = paged ? k_score_row<MT, KT, kScoreRowDepth, true> : k_score_row<MT, KT, kScoreRowDepth, false>;
+  const size_t lds = score_row_lds_bytes(a.P, paged);
   hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
@@ -641,10 +729,9 @@ static hipError_t launch_score_row_t(const ScoreArgs& a, int D, int grid, hipStr
                       a.Di, a);
 }
 
-hipError_t launch_score_row(const ScoreArgs& a, int MT, int KT, int D, int grid, hipStream_t s,
-                            KTimer t) {
+hipError_t launch_score_row(const ScoreArgs& a, int MT, int KT, int grid, hipStream_t s, KTimer t) {
 #define DSA_SCORE_ROW_CASE(M, K) \
-  if (MT == M && KT == K) return launch_score_row_t<M, K>(a, D, grid, s, t);
+  if (MT == M && KT == K) return launch_score_row_t<M, K>(a, grid, s, t);
   DSA_SCORE_ROW_CASE(1, 1) DSA_SCORE_ROW_CASE(1, 2) DSA_SCORE_ROW_CASE(1, 3) DSA_SCORE_ROW_CASE(1, 4)
   DSA_SCORE_ROW_CASE(1, 5) DSA_SCORE_ROW_CASE(1, 6) DSA_SCORE_ROW_CASE(1, 7) DSA_SCORE_ROW_CASE(1, 8)
   DSA_SCORE_ROW_CASE(2, 1) DSA_SCORE_ROW_CASE(2, 2) DSA_SCORE_ROW_CASE(2, 3) DSA_SCORE_ROW_CASE(2, 4)
@@ -655,8 +742,9 @@ hipError_t launch_score_row(const ScoreArgs& a, int MT, int KT, int D, int grid,
 
 int score_max_chunk() { return kChunkPerThread * kScoreBlock; }
 
-size_t score_lds_bytes(int MT, int KT, int Bg, int P, bool cand) {
+size_t score_lds_bytes(int MT, int KT, int Bg, int P, bool cand, bool paged) {
   return align16(sizeof(ChunkSmem<kScoreBlock>)) + (size_t)Bg * 32 * MT * (32 * KT + 16) + (size_t)Bg * 32 * MT * 4 +
+         (paged ? (size_t)kMaxTiles * 4 : 0) +
          (cand ? (size_t)Bg * P * 4 + (size_t)Bg * kHistBins * 4 + sizeof(BlockCandSmem<kScoreBlock>) +
                      (size_t)Bg * 4
                : 0) +
@@ -665,7 +753,7 @@ size_t score_lds_bytes(int MT, int KT, int Bg, int P, bool cand) {
 
 template <int MT, int KT, bool CAND, bool ONE, int NB = 3>
 static hipError_t launch_score_t(const ScoreArgs& a, int grid, size_t lds, hipStream_t s, KTimer t) {
-  auto fn = k_score<MT, KT, CAND, ONE, NB>;
+  auto fn = a.pages != nullptr ? k_score<MT, KT, CAND, ONE, NB, true> : k_score<MT, KT, CAND, ONE, NB, false>;
   hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
@@ -686,7 +774,9 @@ static hipError_t launch_score_mk(const ScoreArgs& a, bool cand, int grid, size_
 }
 
 hipError_t launch_score(const ScoreArgs& a, int MT, int KT, bool cand, int grid, hipStream_t s, KTimer t) {
-  const size_t lds = score_lds_bytes(MT, KT, a.Bg, a.P, cand);
+  // paged: a chunk's tiles must fit the kernel's list of tile offsets
+  if (a.pages != nullptr && (a.P + 63) / 64 > kMaxTiles) return hipErrorInvalidValue;
+  const size_t lds = score_lds_bytes(MT, KT, a.Bg, a.P, cand, a.pages != nullptr);
 #define DSA_SCORE_CASE(M, K) \
   if (MT == M && KT == K) return launch_score_mk<M, K>(a, cand, grid, lds, s, t);
   DSA_SCORE_CASE(1, 1) DSA_SCORE_CASE(1, 2) DSA_SCORE_CASE(1, 3) DSA_SCORE_CASE(1, 4)

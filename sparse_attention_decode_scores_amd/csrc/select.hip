@@ -1182,7 +1182,14 @@ __global__ __launch_bounds__(kSelBlock) void k_select(const uint64_t* __restrict
     // narrowing follows its last write), and the LDS region is free again
     {  // the output slots [r0, r0 + per) of the row: the window's positions, then -1 past kk
       int32_t* out = a.idx + (int64_t)b * a.k;
-      for (int i = tid; i < per && r0 + i < a.k; i += kSelBlock) out[r0 + i] = i < cnt ? (int32_t)sm.winpos[i] : -1;
+      const bool paged = at.pages != nullptr;  // uniform
+      for (int i = tid; i < per && r0 + i < a.k; i += kSelBlock) {
+        const uint32_t pos = sm.winpos[i];
+        out[r0 + i] = i < cnt ? (int32_t)pos : -1;
+        // a paged latent cache: the gather below reads pool rows
+        if (paged && i < cnt) sm.winpos[i] = page_row(at.pages, at.pool_pages, pos);
+      }
+      if (paged) lds_barrier();
       if (cnt > 0 && r0 + cnt == kk && tid == 0) {  // the window of the kk-th best key
         RowStats st;
         st.path = reason == 0 ? 0 : 1;
@@ -1335,9 +1342,11 @@ __global__ __launch_bounds__(kSelBlock) void k_attend_idx(const int32_t* __restr
     const int32_t v = i < e1 ? row[i] : -1;
     const bool keep = v >= 0 && (int64_t)v < at.N;
     bad += (v != -1 && !keep);
+    // a paged latent cache: the listed positions become pool rows
+    const int32_t row_at = keep && at.pages != nullptr ? (int32_t)page_row(at.pages, at.pool_pages, v) : v;
     uint32_t total;
     const uint32_t slot = run + block_excl_scan_u32<kSelBlock>(keep ? 1u : 0u, sm.radix.part, &total);
-    if (keep) posl[slot] = v;
+    if (keep) posl[slot] = row_at;
     run += total;
   }
   bad = block_stats(bad, 0, 0, 0, sm).sum;

@@ -40,6 +40,16 @@ from ``default_rng([seed, 2, j])`` (so they can be drawn on several threads).
 
 bf16 values are carried as uint16 bit patterns and FP8 E4M3 (e4m3fn) values as uint8
 codes, each rounded to nearest even from the fp32 draw.
+
+Paged pools (``paged``): a workload's two caches placed in pools of 256-position
+pages, as the shared KV pool of the glm53-tensorfold-spark README holds them
+(1,048,576 tokens in 4,096 pages). The sequence's ceil(N / 256) logical pages go to
+distinct pool pages in a seeded random order (``default_rng([seed, 3])``
+permutation of the pool), so neighbouring pages are scattered over the pool. Every
+pool row the sequence does not own, including the tail of its last page, holds
+decoy values: indexer keys drawn uniformly from the workload's key range
+(``default_rng([seed, 4])``) and latent rows of constant 8.0 (exact in fp32, bf16
+and E4M3), large enough to dominate any softmax they were wrongly let into.
 """
 import numpy as np
 
@@ -177,3 +187,31 @@ def random_case(seed, B, N, k, Hi, Di, Hq, Dk, Dv, dtype="bf16", ctx_len=None, q
     return dict(B=B, N=N, k=k, Hi=Hi, Di=Di, Hq=Hq, Dk=Dk, Dv=Dv, dtype=dtype,
                 scale=(1.0 / np.sqrt(Dk)) if scale is None else scale, iq=iq, iw=iw, ik=ik, q=q,
                 kv=kv, ctx_len=np.asarray(ctx_len, np.int32), layers=1, name="random", layer=0)
+
+
+PAGE = 256  # positions per pool page
+
+
+def paged(c, seed=7, pool_pages=None):
+    """Pools and page table holding the caches of case ``c``: returns dict(ik_pool, kv_pool,
+    page_table, pool_pages). The pool has ``pool_pages`` pages (default: twice the
+    sequence's pages, plus three)."""
+    N = c["N"]
+    n_tab = (N + PAGE - 1) // PAGE
+    pool_pages = 2 * n_tab + 3 if pool_pages is None else int(pool_pages)
+    if pool_pages < n_tab:
+        raise ValueError("the pool must hold the sequence's pages")
+    table = np.random.default_rng([seed, 3]).permutation(pool_pages)[:n_tab].astype(np.int32)
+    rows = pool_pages * PAGE
+    kr = c.get("key_range", 16)
+    ik_pool = np.random.default_rng([seed, 4]).integers(-kr, kr + 1, size=(rows, c["Di"]), dtype=np.int8)
+    kv = c["kv"]
+    eight = np.array([8.0], np.float32)
+    decoy = {np.dtype(np.float32): eight, np.dtype(np.uint16): f32_to_bf16_bits(eight),
+             np.dtype(np.uint8): f32_to_e4m3_codes(eight)}[kv.dtype][0]
+    kv_pool = np.full((rows, kv.shape[1]), decoy, kv.dtype)
+    pos = np.arange(N, dtype=np.int64)
+    prow = table[pos // PAGE].astype(np.int64) * PAGE + pos % PAGE
+    ik_pool[prow] = c["ik"]
+    kv_pool[prow] = kv
+    return dict(ik_pool=ik_pool, kv_pool=kv_pool, page_table=table, pool_pages=pool_pages)

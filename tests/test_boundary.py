@@ -146,6 +146,54 @@ def test_decode_step_validation(lib):
     assert lib.dsa_decode_step(*bad) == INVALID
 
 
+def test_paged_validation(lib):
+    # every call below is rejected by the host checks (a short workspace where the
+    # paging arguments pass), so nothing is launched on the stand-in pointers
+    p, keep = lens(300000)
+    need = binding.dsa_workspace_size(1, 300000, 2048, 16, 512)
+    step = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2400, p, 1, 64, 128, 16, 576, 512, 300000, 2048, 1 / 24, 1,
+            FAKE, FAKE, FAKE, FAKE, need - 1, 0, None, None]
+
+    def run(**kw):
+        a = list(step)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return lib.dsa_decode_step_paged(*a)
+
+    assert run() == WORKSPACE           # paging accepted; the short workspace stops it
+    assert run(a5=None) == INVALID      # no page table
+    assert run(a5=FAKE + 2) == INVALID  # misaligned table
+    assert run(a6=0) == INVALID         # empty pool
+    assert run(a6=(1 << 31) // 256) == UNSUPPORTED  # pool rows beyond int32
+    assert run(a6=65536) == UNSUPPORTED  # 65,536 pages x 256 x 128 B of keys reach 2^31
+    assert run(a14=8192 * 256 + 1) == UNSUPPORTED  # beyond DSA_MAX_PAGES pages
+    assert run(a14=8192 * 256) == WORKSPACE          # the largest paged sequence passes
+
+    def scores(**kw):
+        a = [FAKE, FAKE, FAKE, FAKE, 2400, p, 1, 64, 128, 300000, FAKE, None]
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return lib.dsa_index_scores_paged(*a)
+
+    assert scores(a3=None) == INVALID
+    assert scores(a4=0) == INVALID
+    assert scores(a4=65536) == UNSUPPORTED
+    assert scores(a9=8192 * 256 + 1) == UNSUPPORTED
+    assert scores(a8=100) == INVALID  # Di
+
+    def attn(**kw):
+        a = [FAKE, FAKE, FAKE, 2400, FAKE, 1, 16, 576, 512, 300000, 2048, 1 / 24, 1, FAKE, FAKE, need - 1, None]
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return lib.dsa_sparse_attn_paged(*a)
+
+    assert attn() == WORKSPACE
+    assert attn(a3=65536) == WORKSPACE  # the latent pool has no 2^31-byte offset limit
+    assert attn(a2=None) == INVALID
+    assert attn(a3=-1) == INVALID
+    assert attn(a9=8192 * 256 + 1) == UNSUPPORTED
+
+
 def test_noalloc_rejects_sizes_beyond_its_scratch(lib):
     # B=16, k=4096, 64 heads x 512 values needs far more than the static scratch: a clear
     # workspace error before anything touches the device (the stand-in pointers are

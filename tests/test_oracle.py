@@ -334,3 +334,66 @@ def test_openmp_build_gives_identical_results():
     with pytest.raises(ValueError):  # 64 heads x 128 dims of 127s overflow int32
         oracle.index_scores(np.full((1, 64, 128), 127, np.int8), np.full((1, 64), 127, np.int8),
                             np.full((10, 128), 127, np.int8), np.array([10], np.int32), omp=True)
+
+
+# ---------------------------------------------------------------- paged caches
+
+def test_gather_pages_hand_example():
+    # three pool pages of 4 rows; the sequence's logical pages are pool pages 2 then 0,
+    # and it holds 7 positions: rows 8..11 of the pool, then rows 0..2
+    pool = np.arange(12, dtype=np.int32).reshape(12, 1)
+    got = oracle.gather_pages(pool, np.array([2, 0], np.int32), 7, page=4)
+    assert got[:, 0].tolist() == [8, 9, 10, 11, 0, 1, 2]
+
+
+@pytest.mark.parametrize("N", [1, 255, 256, 257, 3000])
+def test_gather_pages_reads_whole_pages_in_table_order(N):
+    # every pool row holds its own row number; the gathered cache must be the table's
+    # pages laid end to end (256 consecutive rows each), cut at N
+    pages = 17
+    pool = np.stack([np.arange(pages * 256, dtype=np.int64), -np.arange(pages * 256, dtype=np.int64)], axis=1)
+    table = np.random.default_rng(N).permutation(pages)[:(N + 255) // 256].astype(np.int32)
+    expect = np.concatenate([np.arange(256 * p, 256 * p + 256) for p in table])[:N]
+    got = oracle.gather_pages(pool, table, N)
+    assert got[:, 0].tolist() == expect.tolist()
+    assert (got[:, 1] == -got[:, 0]).all()
+
+
+def test_gather_pages_rejects_entries_outside_the_pool():
+    pool = np.zeros((512, 4), np.int8)
+    for bad in (-1, 2):
+        with pytest.raises(ValueError):
+            oracle.gather_pages(pool, np.array([0, bad], np.int32), 300)
+
+
+def test_paged_step_equals_step_on_the_described_cache():
+    # pages scattered over a pool whose other rows are decoys: the paged step is the
+    # contiguous step on the cache the table describes, and an identity table over a
+    # pool that is the cache itself changes nothing
+    c = inputs.random_case(41, B=2, N=1000, k=128, Hi=8, Di=32, Hq=4, Dk=64, Dv=32, dtype="f32",
+                           ctx_len=[1000, 617])
+    args = (c["q"], c["ctx_len"], c["k"], c["Dv"], c["scale"])
+    ref = oracle.decode_step(c["iq"], c["iw"], c["ik"], c["q"], c["kv"], *args[1:])
+    p = inputs.paged(c, seed=5)
+    got = oracle.decode_step_paged(c["iq"], c["iw"], p["ik_pool"], c["q"], p["kv_pool"], p["page_table"],
+                                   *args[1:], N=c["N"])
+    for x, y in zip(ref, got):
+        assert np.array_equal(x, y)
+    # the identity table over the (whole-page) cache itself
+    ik = np.concatenate([c["ik"], np.zeros((24, 32), np.int8)])
+    kv = np.concatenate([c["kv"], np.zeros((24, 64), np.float32)])
+    ident = oracle.decode_step_paged(c["iq"], c["iw"], ik, c["q"], kv, np.arange(4, dtype=np.int32),
+                                     *args[1:], N=c["N"])
+    for x, y in zip(ref, ident):
+        assert np.array_equal(x, y)
+
+
+def test_paged_inputs_place_every_page_once():
+    c = inputs.make("tiny_4k")
+    p = inputs.paged(c)
+    t = p["page_table"]
+    assert len(set(t.tolist())) == len(t) == 16 and p["pool_pages"] == 35
+    assert t.min() >= 0 and t.max() < p["pool_pages"]
+    # pool pages the sequence does not own hold only decoys (latent rows of 8.0)
+    free = sorted(set(range(p["pool_pages"])) - set(t.tolist()))
+    assert (p["kv_pool"].reshape(p["pool_pages"], 256, -1)[free] == 8.0).all()
