@@ -49,6 +49,7 @@ sys.path.insert(0, ROOT)
 METRIC = "DSA decode step µs & indexer+gather HBM GB/s, top-2048 at 62k/300k ctx"
 HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E
 INT8_PEAK_TOPS = 5000.0     # MI355X dense int8 matrix-core peak (5.0 POPS)
+POOL_PAGES = 4096           # paged leg: a 1,048,576-token pool of 256-position pages
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "decode_step_ctx300k_hbm_counters.json")
 
 # The pages' own figures, with their hardware (context, not targets).
@@ -157,9 +158,10 @@ def indexer_int_ops(c):
 class Runner:
     """One workload's rotating input sets and outputs, and its timing passes."""
 
-    def __init__(self, torch, binding, name, sets, host_set0=True):
+    def __init__(self, torch, binding, name, sets, host_set0=True, paged=False):
         from sparse_attention_decode_scores_amd import inputs
         self.torch, self.binding, self.name = torch, binding, name
+        self.paged = paged
         base = dict(inputs.CONFIGS[name])
         self.layers = base["layers"]
         self.hosts = []
@@ -176,11 +178,39 @@ class Runner:
                 c = self.hosts[l] if host_set0 else dict(self.c, layer=l)
                 per.append(device_set(torch, c, s if host_set0 else s + 1))
             self.data.append(per)
+        if paged:
+            self.to_pools()
         c = self.c
         self.ws = binding.new_workspace(c["B"], c["N"], c["k"], c["Hq"], c["Dv"])
         self.scores = torch.zeros((c["B"], c["N"]), dtype=torch.int32, device="cuda")
         self.idx = torch.empty((c["B"], c["k"]), dtype=torch.int32, device="cuda")
         self.out = torch.empty((c["B"], c["Hq"], c["Dv"]), dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+
+    def to_pools(self):
+        """Moves every (set, layer) cache into a pair of paged pools of its own, each the size
+        of the 1,048,576-token pool of 4,096 pages of 256 positions (at least the
+        sequence's pages): the sequence takes ceil(N / 256) of the pool's pages in a seeded
+        random order (its pages scattered over the pool, the rest left to other
+        sequences), and its page table goes into its input dict."""
+        torch, c = self.torch, self.c
+        page = self.binding.PAGE_SIZE
+        n_tab = (c["N"] + page - 1) // page
+        pool_pages = max(POOL_PAGES, n_tab)
+        g = torch.Generator(device="cuda")
+        g.manual_seed(7700)
+        pos = torch.arange(c["N"], device="cuda", dtype=torch.int64)
+        for d in (d for per in self.data for d in per):
+            table = torch.randperm(pool_pages, generator=g, device="cuda")[:n_tab].to(torch.int32).contiguous()
+            rows = table[pos // page].to(torch.int64) * page + pos % page
+            ik, kv = d.pop("ik"), d.pop("kv")
+            d["ik_pool"] = torch.zeros((pool_pages * page, c["Di"]), dtype=torch.int8, device="cuda")
+            d["kv_pool"] = torch.zeros((pool_pages * page, c["Dk"]), dtype=kv.dtype, device="cuda")
+            d["ik_pool"].index_copy_(0, rows, ik)
+            d["kv_pool"].index_copy_(0, rows, kv)
+            d["page_table"] = table
+            del ik, kv
+        self.pool_pages = pool_pages
         torch.cuda.synchronize()
 
     def bytes_per_set(self):
@@ -192,6 +222,12 @@ class Runner:
         for l in range(self.layers):
             d = self.data[s][l]
             ev = None if kernel_events is None else kernel_events[l]
+            if self.paged:
+                self.binding.dsa_decode_step_paged(d["iq"], d["iw"], d["ik_pool"], d["q"], d["kv_pool"],
+                                                   d["page_table"], c["ctx_len"], c["k"], c["Dv"], c["scale"],
+                                                   N=c["N"], scores=self.scores, idx=self.idx, out=self.out,
+                                                   workspace=self.ws, flags=flags, kernel_events=ev)
+                continue
             self.binding.dsa_decode_step(d["iq"], d["iw"], d["ik"], d["q"], d["kv"], c["ctx_len"], c["k"],
                                          c["Dv"], c["scale"], scores=self.scores, idx=self.idx, out=self.out,
                                          workspace=self.ws, flags=flags, kernel_events=ev)
@@ -382,16 +418,20 @@ def kernel_figures(c, score_us, select_us, combine_us):
             "gather_frac_of_hbm_peak": round(gb / (select_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
 
 
-def leg(torch, binding, name, steps, sets):
-    log("leg", name)
-    r = Runner(torch, binding, name, sets, host_set0=False)
+def leg(torch, binding, name, steps, sets, paged=False):
+    log("leg", name, "(paged pools)" if paged else "")
+    r = Runner(torch, binding, name, sets, host_set0=False, paged=paged)
     for i in range(2 * sets):
         r.step(i % sets)
     torch.cuda.synchronize()
     us, n = r.graph_us(steps)
     k = r.kernel_us(max(8, steps // 2))
     c = r.c
-    res = {"workload": describe(c, name, r.layers), "us_per_step": round(us, 3),
+    res = {"workload": describe(c, name, r.layers) + (
+               "; each input set's caches in pools of %d 256-position pages (the 1,048,576-token pool), "
+               "the sequence's pages in a seeded random order over the pool, read through its page "
+               "table" % r.pool_pages
+               if paged else ""), "us_per_step": round(us, 3),
            "us_per_layer": round(us / r.layers, 3), "steps": n,
            "cache": "cold: %d rotating input sets of %.0f MB" % (sets, r.bytes_per_set() / 1e6),
            "kernels_per_layer": kernel_figures(c, *k),
@@ -418,7 +458,7 @@ def main():
     ap.add_argument("--config", default="ctx300k",
                     choices=["ctx16k", "ctx62k_11layers", "ctx300k", "verify8_ctx131k", "ctx300k_fp8kv"])
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = default per workload)")
-    ap.add_argument("--legs", default="fallback,ctx62k_11layers,verify8_ctx131k,ctx300k_fp8kv",
+    ap.add_argument("--legs", default="fallback,ctx62k_11layers,verify8_ctx131k,ctx300k_fp8kv,ctx300k_paged",
                     help="comma list of extra legs, or 'none'")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -522,6 +562,8 @@ def main():
     for name in legs:
         if name in ("ctx62k_11layers", "verify8_ctx131k", "ctx300k_fp8kv") and name != args.config:
             leg_out[name] = leg(torch, binding, name, max(16, K // 8), 4)
+        elif name == "ctx300k_paged":
+            leg_out[name] = leg(torch, binding, "ctx300k", max(16, K // 8), R, paged=True)
 
     cpu = None
     if not args.no_cpu_baseline:

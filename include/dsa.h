@@ -81,6 +81,9 @@ typedef enum dsa_dtype {
 
 /* flags for dsa_topk_select / dsa_decode_step */
 #define DSA_FLAG_FORCE_FALLBACK 1u /* testing: take the exhaustive path for every row */
+#define DSA_FLAG_TABLE_IN_MEMORY 2u /* dsa_decode_step_paged, testing: the selection kernel reads
+                                       the page table from memory, as it does when the table
+                                       does not fit in its LDS */
 
 /* Per-row record of what the selection did, kept in the workspace. */
 typedef struct dsa_row_stats {

@@ -16,6 +16,7 @@ _LIB_PATH = os.path.join(_HERE, "libdsa.so")
 _lib = None
 
 FLAG_FORCE_FALLBACK = 1
+FLAG_TABLE_IN_MEMORY = 2  # dsa_decode_step_paged only (testing)
 DSA_F32, DSA_BF16, DSA_FP8_E4M3 = 0, 1, 2
 STATUS_NAMES = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED",
                 3: "DSA_ERR_WORKSPACE", 4: "DSA_ERR_HIP"}

@@ -127,6 +127,7 @@ dsa_status check_ws(void* ws, size_t ws_bytes, const Layout& L) {
 struct Paging {
   const int32_t* pages = nullptr;
   int pool_pages = 0;
+  int npages = 0;  // table entries: ceil(N / kPageSize)
 };
 
 // Paged calls: a table of ceil(N / DSA_PAGE_SIZE) entries (N <= DSA_MAX_PAGES pages'
@@ -139,6 +140,7 @@ dsa_status check_paging(const int32_t* pages, int64_t pool_pages, int64_t N, int
   if (row_bytes > 0 && pool_pages * kPageSize * row_bytes >= ((int64_t)1 << 31)) return DSA_ERR_UNSUPPORTED;
   pg->pages = pages;
   pg->pool_pages = (int)pool_pages;
+  pg->npages = (int)((N + kPageSize - 1) / kPageSize);
   return DSA_OK;
 }
 
@@ -290,6 +292,7 @@ AttnArgs attn_args(const void* q, const void* kv, int64_t N, int Hq, int Dk, int
   AttnArgs at;
   at.pages = pg.pages;
   at.pool_pages = pg.pool_pages;
+  at.lds_pages = 0;
   at.q = q;
   at.kv = kv;
   at.N = N;
@@ -395,8 +398,8 @@ dsa_status decode_step_impl(const int8_t* iq, const int8_t* iw, const int8_t* ik
   dsa_status st = check_rows(ctx_len, B, N, &lens, &nmax);
   if (st != DSA_OK) return st;
   if ((st = check_index(iq, iw, ik, Hi, Di)) != DSA_OK) return st;
-  if (!scores || !idx || !out || k < 1 || k > DSA_MAX_K || (flags & ~DSA_FLAG_FORCE_FALLBACK))
-    return DSA_ERR_INVALID_ARG;
+  const unsigned known = DSA_FLAG_FORCE_FALLBACK | (pages != nullptr ? DSA_FLAG_TABLE_IN_MEMORY : 0u);
+  if (!scores || !idx || !out || k < 1 || k > DSA_MAX_K || (flags & ~known)) return DSA_ERR_INVALID_ARG;
   AttnChoice ch;
   if ((st = check_attn(q, kv, Hq, Dk, Dv, scale, dt, &ch)) != DSA_OK) return st;
   Paging pg;
@@ -426,6 +429,10 @@ dsa_status decode_step_impl(const int8_t* iq, const int8_t* iw, const int8_t* ik
   sa.R = 0;
   AttnArgs at = attn_args(q, kv, N, Hq, Dk, Dv, scale, k, w, L, pg);
   set_attn_path(&at, ch, k, B);
+  // a paged latent cache: the selection kernel stages the table in LDS when it fits
+  if (pg.pages != nullptr && !(flags & DSA_FLAG_TABLE_IN_MEMORY) &&
+      select_lds_bytes(ch, Hq, Dk, k) + align16((size_t)pg.npages * 4) <= (size_t)lds_limit())
+    at.lds_pages = pg.npages;
   if (launch_select(sa, at, ch, B, stream, tm[1]) != hipSuccess) return DSA_ERR_HIP;
   return hip_status(combine(at, nullptr, nullptr, out, B, stream, tm[2]));
 }

@@ -37,6 +37,11 @@ struct ChunkSum {
 };
 
 struct ScoreArgs {
+  // paged key cache: ik is the pool ([pool_pages * kPageSize][Di]) and pages[j] the
+  // pool page of logical page j (kernels instantiated for paging only; first, so that
+  // the one-row kernel's early argument reads share one line)
+  const int32_t* pages;
+  int pool_pages;
   const int8_t* iq;
   const int8_t* iw;
   const int8_t* ik;
@@ -52,10 +57,6 @@ struct ScoreArgs {
   int P;           // positions per chunk (multiple of 64; of 32 for the one-row kernel)
   int G;           // chunks per row
   int m;           // candidates kept per chunk
-  // paged key cache: ik is the pool ([pool_pages * kPageSize][Di]) and pages[j] the
-  // pool page of logical page j (kernels instantiated for paging only)
-  const int32_t* pages;
-  int pool_pages;
 };
 
 // Geometry of chunk c of a row of n positions in units of 32 positions: with ilv,
@@ -121,6 +122,7 @@ struct AttnArgs {
   // pages[j] the pool page of logical page j
   const int32_t* pages;
   int pool_pages;
+  int lds_pages;  // selection kernel: table entries it stages in LDS (0: it reads the table in memory)
 };
 
 enum AttnKind { ATTN_NONE = 0, ATTN_MFMA_BF16 = 1, ATTN_GENERIC_F32 = 2, ATTN_GENERIC_BF16 = 3 };

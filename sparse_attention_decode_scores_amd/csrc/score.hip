@@ -398,13 +398,15 @@ __device__ __forceinline__ void load_unit_at(v4i (&kf)[KT], __amdgpu_buffer_rsrc
 // The arguments that the first requests need come first, as separate scalars: the
 // leading arguments can be preloaded into scalar registers at wave launch, so the
 // query and key requests need not wait for a read of the argument block (a.iq,
-// a.iw, a.ik, a.lens.n[0], a.G, a.P, a.Hi and a.Di, passed again).
+// a.iw, a.ik, a.pages, a.lens.n[0], a.G, a.P, and a.Hi | a.Di << 16, passed again).
 template <int MT, int KT, int D, bool PG>
 __global__ __launch_bounds__(kScoreBlock) void k_score_row(const int8_t* __restrict__ iq,
                                                            const int8_t* __restrict__ iw,
-                                                           const int8_t* __restrict__ ik, int n, int G, int P,
-                                                           int Hi, int Di, ScoreArgs a) {
+                                                           const int8_t* __restrict__ ik,
+                                                           const int32_t* __restrict__ pages, int n, int G, int P,
+                                                           int hidi, ScoreArgs a) {
   static_assert(D == 2 || D == 3, "units in flight per wave");
+  const int Hi = hidi & 0xFFFF, Di = hidi >> 16;
   extern __shared__ __align__(16) uint8_t smem[];
   using Smem = ChunkSmem<kScoreBlock>;
   Smem& csm = *reinterpret_cast<Smem*>(smem);
@@ -460,7 +462,7 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(const int8_t* __restr
   // reads its first units' entries itself.
   const uint32_t pool_bytes = PG ? (uint32_t)a.pool_pages * (uint32_t)kPageSize * (uint32_t)Di : 0u;
   auto unit_base = [&](int j) -> uint32_t {
-    return j < units ? page_row(a.pages, a.pool_pages, (int64_t)kUnit * (c + (int64_t)j * G)) * (uint32_t)Di
+    return j < units ? page_row(pages, a.pool_pages, (int64_t)kUnit * (c + (int64_t)j * G)) * (uint32_t)Di
                      : pool_bytes;
   };
   uint32_t ub = 0;
@@ -725,8 +727,8 @@ static hipError_t launch_score_row_t(const ScoreArgs& a, int grid, hipStream_t s
   hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
-  return launch_timed(fn, dim3(grid), dim3(kScoreBlock), lds, s, t, a.iq, a.iw, a.ik, a.lens.n[0], a.G, a.P, a.Hi,
-                      a.Di, a);
+  return launch_timed(fn, dim3(grid), dim3(kScoreBlock), lds, s, t, a.iq, a.iw, a.ik, a.pages, a.lens.n[0], a.G, a.P,
+                      a.Hi | a.Di << 16, a);
 }
 
 hipError_t launch_score_row(const ScoreArgs& a, int MT, int KT, int grid, hipStream_t s, KTimer t) {

@@ -1060,7 +1060,9 @@ __device__ __forceinline__ const SelectKernArgs* kernel_args() {
 // candidate, dropped-key, summary and query requests need not wait for a read of the
 // argument block (a.cand, a.xc, a.sums, a.G, at.q, at.Hq, at.Dk and at.S, passed
 // again).
-template <class Attn>
+// PG: the latent cache is a paged pool (at.pages); the window's positions become pool
+// rows before the gather.
+template <class Attn, bool PG>
 __global__ __launch_bounds__(kSelBlock) void k_select(const uint64_t* __restrict__ cand,
                                                       const uint64_t* __restrict__ xc,
                                                       const ChunkSum* __restrict__ sums, const void* __restrict__ q,
@@ -1130,6 +1132,37 @@ __global__ __launch_bounds__(kSelBlock) void k_select(const uint64_t* __restrict
     const int32_t* l0 = a.idx;
     asm volatile("" : "+s"(n), "+s"(have_cand), "+s"(cand_valid), "+s"(force), "+s"(kq) : "s"(l0) : "memory");
   }
+  // paged: the page table in LDS, past the largest of the selection's and the
+  // attention's regions. Its address is formed from kq, which arrives with the reads
+  // above: formed from a.k like `region`, it put a wait for the argument block ahead
+  // of the union's loads.
+  uint32_t* ptab = reinterpret_cast<uint32_t*>(
+      reinterpret_cast<uint8_t*>(lds.sm) + align16(sizeof(SelSmem)) + align16((size_t)kq * 8) +
+      align16(Attn::lds_bytes(Hq, Dk) > kRegionSelect ? Attn::lds_bytes(Hq, Dk) : kRegionSelect));
+  if constexpr (PG) {
+    // (these copies end with the staging; the translation below reads the arguments
+    // again, from the scalar cache, so nothing stays live through the selection)
+    const int32_t* pages = at.pages;
+    int pool_pages = at.pool_pages, lds_pages = at.lds_pages;
+    asm volatile("" : "+s"(pages), "+s"(pool_pages), "+s"(lds_pages)::"memory");
+    // The table into LDS, requested behind the union's loads (the wait for it ends
+    // about when those arrive, and the selection needs them first), four entries a
+    // thread per round; the window's positions are translated from there.
+    constexpr int kPer = 4;
+    for (int i0 = 0; i0 < lds_pages; i0 += kPer * kSelBlock) {  // uniform
+      int32_t e[kPer];
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int i = i0 + tid + kSelBlock * u;
+        e[u] = i < lds_pages ? pages[i] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int i = i0 + tid + kSelBlock * u;
+        if (i < lds_pages) ptab[i] = (uint32_t)(e[u] < 0 ? 0 : (e[u] >= pool_pages ? pool_pages - 1 : e[u]));
+      }
+    }
+  }
   const int32_t* row = a.scores + (int64_t)b * a.N;
 
   int reason = force ? 1 : (have_cand ? 0 : 3);
@@ -1182,14 +1215,7 @@ __global__ __launch_bounds__(kSelBlock) void k_select(const uint64_t* __restrict
     // narrowing follows its last write), and the LDS region is free again
     {  // the output slots [r0, r0 + per) of the row: the window's positions, then -1 past kk
       int32_t* out = a.idx + (int64_t)b * a.k;
-      const bool paged = at.pages != nullptr;  // uniform
-      for (int i = tid; i < per && r0 + i < a.k; i += kSelBlock) {
-        const uint32_t pos = sm.winpos[i];
-        out[r0 + i] = i < cnt ? (int32_t)pos : -1;
-        // a paged latent cache: the gather below reads pool rows
-        if (paged && i < cnt) sm.winpos[i] = page_row(at.pages, at.pool_pages, pos);
-      }
-      if (paged) lds_barrier();
+      for (int i = tid; i < per && r0 + i < a.k; i += kSelBlock) out[r0 + i] = i < cnt ? (int32_t)sm.winpos[i] : -1;
       if (cnt > 0 && r0 + cnt == kk && tid == 0) {  // the window of the kk-th best key
         RowStats st;
         st.path = reason == 0 ? 0 : 1;
@@ -1203,7 +1229,19 @@ __global__ __launch_bounds__(kSelBlock) void k_select(const uint64_t* __restrict
         a.stats[b] = st;
       }
     }
-    Attn::run(at, b, blockIdx.x, [&](int i) { return (int64_t)sm.winpos[i]; }, cnt, region, qf);
+    if constexpr (PG) {
+      // a paged latent cache: the gather reads the pool rows of the window's positions
+      // (the table in LDS, or in memory when it did not fit; one gather for both: two
+      // copies of it in the kernel measured 0.7 us slower)
+      const bool in_lds = at.lds_pages > 0;  // uniform
+      Attn::run(at, b, blockIdx.x, [&](int i) {
+        const uint32_t pos = sm.winpos[i];
+        return (int64_t)(in_lds ? ptab[pos >> kPageShift] * kPageSize + (pos & (kPageSize - 1))
+                                : page_row(at.pages, at.pool_pages, pos));
+      }, cnt, region, qf);
+    } else {
+      Attn::run(at, b, blockIdx.x, [&](int i) { return (int64_t)sm.winpos[i]; }, cnt, region, qf);
+    }
     return;
   }
 
@@ -1309,8 +1347,13 @@ static size_t select_lds_t(int Hq, int Dk, int k) {
 
 template <class Attn>
 static hipError_t launch_select_t(const SelArgs& a, const AttnArgs& at, int B, hipStream_t s, KTimer t) {
-  const size_t lds = select_lds_t<Attn>(at.Hq, at.Dk, a.k);
-  auto fn = k_select<Attn>;
+  size_t lds = select_lds_t<Attn>(at.Hq, at.Dk, a.k);
+  auto fn = k_select<Attn, false>;
+  if constexpr (!std::is_same<Attn, AttnNone>::value)
+    if (at.pages != nullptr) {
+      fn = k_select<Attn, true>;
+      lds += align16((size_t)at.lds_pages * 4);
+    }
   hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
@@ -1474,7 +1517,7 @@ constexpr int kCombWideBlock = 256;
 // at.part_o, at.S, at.Hq and at.Dv, passed again)
 __global__ __launch_bounds__(kCombWideBlock) void k_combine_wide(const float2* __restrict__ part_ml,
                                                                  const float* __restrict__ part_o, int S, int Hq,
-                                                                 int Dv, AttnArgs at, const int32_t* __restrict__ part_bad,
+                                                                 int Dv, const int32_t* __restrict__ part_bad,
                                                                  RowStats* __restrict__ stats, float* __restrict__ out) {
   __shared__ float wt[4][kMaxWideSplits];
   __shared__ float red[4][65];
@@ -1567,7 +1610,7 @@ hipError_t launch_combine_wide(const AttnArgs& at, const int32_t* part_bad, RowS
   if (!at.frag || at.S > kMaxWideSplits) return hipErrorInvalidValue;
   const int quads = (at.Hq + 15) / 16 * (at.Dv / 16) * 4;
   return launch_timed(k_combine_wide, dim3(quads, B), dim3(kCombWideBlock), 0, s, t, at.part_ml, at.part_o, at.S,
-                      at.Hq, at.Dv, at, part_bad, stats, out);
+                      at.Hq, at.Dv, part_bad, stats, out);
 }
 
 constexpr int kCombBlock = 64;

@@ -144,6 +144,8 @@ def test_decode_step_validation(lib):
     bad = list(args)
     bad[21] = 8  # unknown flag
     assert lib.dsa_decode_step(*bad) == INVALID
+    bad[21] = 2  # the table-in-memory flag is for paged calls only
+    assert lib.dsa_decode_step(*bad) == INVALID
 
 
 def test_paged_validation(lib):
@@ -168,6 +170,8 @@ def test_paged_validation(lib):
     assert run(a6=65536) == UNSUPPORTED  # 65,536 pages x 256 x 128 B of keys reach 2^31
     assert run(a14=8192 * 256 + 1) == UNSUPPORTED  # beyond DSA_MAX_PAGES pages
     assert run(a14=8192 * 256) == WORKSPACE          # the largest paged sequence passes
+    assert run(a23=2) == WORKSPACE                   # the table-in-memory testing flag
+    assert run(a23=4) == INVALID                     # an unknown flag
 
     def scores(**kw):
         a = [FAKE, FAKE, FAKE, FAKE, 2400, p, 1, 64, 128, 300000, FAKE, None]

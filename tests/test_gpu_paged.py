@@ -129,6 +129,17 @@ def test_paged_forced_fallback_matches_contiguous(torch, dsa, name):
     assert st1 == st0 and all(st["path"] == 1 and st["reason"] == 1 for st in st1)
 
 
+@pytest.mark.parametrize("name", ["ctx16k", "verify8_ctx131k"])
+def test_paged_table_read_from_memory(torch, dsa, name):
+    # the selection kernel's path for tables too large for its LDS, forced by a flag
+    note("paged table in memory", name)
+    c, (rs, ri, ro), p = case(name)
+    s1, i1, o1, st1 = run(torch, dsa, c, p, flags=dsa.FLAG_TABLE_IN_MEMORY)
+    s0, i0, o0, st0 = run(torch, dsa, c, p)
+    assert np.array_equal(i1, ri) and np.array_equal(i1, i0)
+    assert bits_equal(o1, o0) and st1 == st0
+
+
 def test_paged_timed_step_matches_untimed(torch, dsa):
     note("paged timed step")
     c, (rs, ri, ro), p = case("ctx16k")
