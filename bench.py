@@ -190,9 +190,10 @@ class Runner:
     def to_pools(self):
         """Moves every (set, layer) cache into a pair of paged pools of its own, each the size
         of the 1,048,576-token pool of 4,096 pages of 256 positions (at least the
-        sequence's pages): the sequence takes ceil(N / 256) of the pool's pages in a seeded
-        random order (its pages scattered over the pool, the rest left to other
-        sequences), and its page table goes into its input dict."""
+        sequence's pages). The rotating sets stand for the layers of one sequence, which
+        share its page table: the sequence takes ceil(N / 256) of the pool's pages in a
+        seeded random order (scattered over the pool, the rest left to other sequences),
+        and every set's caches are laid out by that one table."""
         torch, c = self.torch, self.c
         page = self.binding.PAGE_SIZE
         n_tab = (c["N"] + page - 1) // page
@@ -200,9 +201,9 @@ class Runner:
         g = torch.Generator(device="cuda")
         g.manual_seed(7700)
         pos = torch.arange(c["N"], device="cuda", dtype=torch.int64)
+        table = torch.randperm(pool_pages, generator=g, device="cuda")[:n_tab].to(torch.int32).contiguous()
+        rows = table[pos // page].to(torch.int64) * page + pos % page
         for d in (d for per in self.data for d in per):
-            table = torch.randperm(pool_pages, generator=g, device="cuda")[:n_tab].to(torch.int32).contiguous()
-            rows = table[pos // page].to(torch.int64) * page + pos % page
             ik, kv = d.pop("ik"), d.pop("kv")
             d["ik_pool"] = torch.zeros((pool_pages * page, c["Di"]), dtype=torch.int8, device="cuda")
             d["kv_pool"] = torch.zeros((pool_pages * page, c["Dk"]), dtype=kv.dtype, device="cuda")
@@ -323,6 +324,27 @@ class Runner:
         self.last_spans = spans
         return [float(st[:, :, i].mean()) for i in range(3)]
 
+    def host_issue_us(self, calls=300):
+        """Host time to issue one eager dsa_decode_step: the C entry point called through
+        ctypes with arguments marshalled once, `calls` times in a row behind a sleep kernel
+        (the GPU runs none of them meanwhile, so the wall time is the host's own: argument
+        checks, launch planning and three kernel launches)."""
+        torch, c = self.torch, self.c
+        d = self.data[0][0]
+        if self.paged:
+            return None
+        step = self.binding.prepared_decode_step(d["iq"], d["iw"], d["ik"], d["q"], d["kv"], c["ctx_len"], c["k"],
+                                                 c["Dv"], c["scale"], self.scores, self.idx, self.out, self.ws)
+        step()
+        torch.cuda.synchronize()
+        torch.cuda._sleep(50_000_000)
+        t0 = time.perf_counter()
+        for _ in range(calls):
+            step()
+        us = (time.perf_counter() - t0) * 1e6 / calls
+        torch.cuda.synchronize()
+        return us
+
     def paths(self):
         return [s["path"] for s in self.binding.dsa_read_stats(self.ws, self.c["B"])]
 
@@ -429,8 +451,8 @@ def leg(torch, binding, name, steps, sets, paged=False):
     c = r.c
     res = {"workload": describe(c, name, r.layers) + (
                "; each input set's caches in pools of %d 256-position pages (the 1,048,576-token pool), "
-               "the sequence's pages in a seeded random order over the pool, read through its page "
-               "table" % r.pool_pages
+               "laid out by one page table (the sets stand for the layers of one sequence), the "
+               "sequence's pages in a seeded random order over the pool" % r.pool_pages
                if paged else ""), "us_per_step": round(us, 3),
            "us_per_layer": round(us / r.layers, 3), "steps": n,
            "cache": "cold: %d rotating input sets of %.0f MB" % (sets, r.bytes_per_set() / 1e6),
@@ -510,6 +532,8 @@ def main():
         "combine %.2f us; per-step span median %.2f us (p10 %.2f, p90 %.2f)"
         % (score_us, select_us, combine_us, spans["median_us"], spans["p10_us"], spans["p90_us"]))
     paths = run.paths()
+    issue_us = run.host_issue_us()
+    log("host time to issue one eager step: %.2f us" % issue_us)
 
     fallback = None
     legs = [x for x in args.legs.split(",") if x and x != "none"]
@@ -650,6 +674,10 @@ def main():
             "us": round(read_us, 3),
             "GBps": round(read_bytes / (read_us * 1e-6) / 1e9, 1),
         },
+        "host_issue_us": {"us": round(issue_us, 2),
+                          "how": "dsa_decode_step called through ctypes with its arguments marshalled "
+                                 "once, 300 calls in a row while the GPU runs a sleep kernel: the host's "
+                                 "own cost per eager step (checks, planning, three launches)"},
         "selection_paths": paths,
         "context": CONTEXT,
     }

@@ -201,15 +201,8 @@ def dsa_sparse_attn(q, kv, idx, Dv, scale, out=None, workspace=None, stream=None
     return out
 
 
-def dsa_decode_step(iq, iw, ik, q, kv, ctx_len, k, Dv, scale, scores=None, idx=None, out=None,
-                    workspace=None, flags=0, stream=None, kernel_events=None):
-    """The three stages through one layer; returns (scores, idx, out).
-
-    kernel_events: optional sequence of 6 torch.cuda.Event(enable_timing=True), each
-    already recorded once (torch creates the HIP event lazily). Events 2i, 2i+1 take
-    the start and end of stage i's kernel (dsa_decode_step_timed)."""
+def _decode_step_args(iq, iw, ik, q, kv, ctx_len, k, Dv, scale, scores, idx, out, workspace, flags, stream):
     torch = _torch()
-    lib = load_library()
     B, Hi, Di = iq.shape
     _, Hq, Dk = q.shape
     N = ik.shape[0]
@@ -232,6 +225,19 @@ def dsa_decode_step(iq, iw, ik, q, kv, ctx_len, k, Dv, scale, scores=None, idx=N
             _dev(idx, "idx", torch.int32), _dev(out, "out", torch.float32),
             _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), flags,
             _stream(stream)]
+    return args, lens, scores, idx, out
+
+
+def dsa_decode_step(iq, iw, ik, q, kv, ctx_len, k, Dv, scale, scores=None, idx=None, out=None,
+                    workspace=None, flags=0, stream=None, kernel_events=None):
+    """The three stages through one layer; returns (scores, idx, out).
+
+    kernel_events: optional sequence of 6 torch.cuda.Event(enable_timing=True), each
+    already recorded once (torch creates the HIP event lazily). Events 2i, 2i+1 take
+    the start and end of stage i's kernel (dsa_decode_step_timed)."""
+    lib = load_library()
+    args, lens, scores, idx, out = _decode_step_args(iq, iw, ik, q, kv, ctx_len, k, Dv, scale, scores, idx,
+                                                     out, workspace, flags, stream)
     if kernel_events is None:
         rc = lib.dsa_decode_step(*args)
     else:
@@ -241,6 +247,24 @@ def dsa_decode_step(iq, iw, ik, q, kv, ctx_len, k, Dv, scale, scores=None, idx=N
         rc = lib.dsa_decode_step_timed(*args, ctypes.cast(evs, ctypes.c_void_p))
     _check(rc, "dsa_decode_step")
     return scores, idx, out
+
+
+def prepared_decode_step(iq, iw, ik, q, kv, ctx_len, k, Dv, scale, scores, idx, out, workspace, flags=0,
+                         stream=None):
+    """dsa_decode_step with its arguments marshalled once: returns a function of no
+    arguments that makes the C call again (and raises on a nonzero status). For
+    measuring the host's cost of issuing a step; the tensors must stay alive."""
+    lib = load_library()
+    args, lens, scores, idx, out = _decode_step_args(iq, iw, ik, q, kv, ctx_len, k, Dv, scale, scores, idx,
+                                                     out, workspace, flags, stream)
+    fn = lib.dsa_decode_step
+
+    def call():
+        rc = fn(*args)
+        if rc != 0:
+            raise DSAError(rc, "dsa_decode_step")
+    call.keep = (lens, args)
+    return call
 
 
 def dsa_decode_step_noalloc(iq, iw, ik, q, kv, ctx_len, k, Dv, scale, scores, idx, out, flags=0,

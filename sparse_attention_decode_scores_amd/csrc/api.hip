@@ -6,6 +6,7 @@
 
 #include <atomic>
 #include <mutex>
+#include <vector>
 
 #include "../../include/dsa.h"
 #include "kernels.h"
@@ -75,6 +76,38 @@ int lds_limit() {
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+struct LdsAllowed {
+  const void* fn;
+  int dev;
+  size_t lds;
+};
+std::mutex g_lds_mu;
+std::vector<LdsAllowed> g_lds_allowed;  // one entry per kernel and device launched
+
+}  // namespace
+
+hipError_t allow_lds(const void* fn, size_t lds) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  {
+    std::lock_guard<std::mutex> g(g_lds_mu);
+    for (const LdsAllowed& e : g_lds_allowed)
+      if (e.fn == fn && e.dev == dev && e.lds >= lds) return hipSuccess;
+  }
+  const hipError_t r = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (r != hipSuccess) return r;
+  std::lock_guard<std::mutex> g(g_lds_mu);
+  for (LdsAllowed& e : g_lds_allowed)
+    if (e.fn == fn && e.dev == dev) {
+      e.lds = e.lds > lds ? e.lds : lds;
+      return hipSuccess;
+    }
+  g_lds_allowed.push_back(LdsAllowed{fn, dev, lds});
+  return hipSuccess;
+}
+
+namespace {
 
 dsa_status check_rows(const int32_t* ctx_len, int B, int64_t N, RowLens* lens, int* nmax) {
   if (ctx_len == nullptr || B < 1 || B > DSA_MAX_BATCH || N < 1 || N > INT32_MAX)

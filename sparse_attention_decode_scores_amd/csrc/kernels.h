@@ -18,6 +18,11 @@ struct KTimer {
   hipEvent_t start = nullptr, stop = nullptr;
 };
 
+// A kernel's dynamic-LDS limit (hipFuncSetAttribute), raised only when a launch needs
+// more than was already allowed for that kernel on the current device, so a launch
+// of a known size makes no attribute call (thread-safe).
+hipError_t allow_lds(const void* fn, size_t lds);
+
 template <class F, class... A>
 inline hipError_t launch_timed(F fn, dim3 grid, dim3 block, size_t lds, hipStream_t s, KTimer t,
                                A... args) {

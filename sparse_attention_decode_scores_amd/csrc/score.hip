@@ -724,8 +724,7 @@ static hipError_t launch_score_row_t(const ScoreArgs& a, int grid, hipStream_t s
   const bool paged = a.pages != nullptr;
   auto fn = paged ? k_score_row<MT, KT, kScoreRowDepth, true> : k_score_row<MT, KT, kScoreRowDepth, false>;
   const size_t lds = score_row_lds_bytes(a.P, paged);
-  hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)lds);
+  hipError_t e = allow_lds((const void*)fn, lds);
   if (e != hipSuccess) return e;
   return launch_timed(fn, dim3(grid), dim3(kScoreBlock), lds, s, t, a.iq, a.iw, a.ik, a.pages, a.lens.n[0], a.G, a.P,
                       a.Hi | a.Di << 16, a);
@@ -756,8 +755,7 @@ size_t score_lds_bytes(int MT, int KT, int Bg, int P, bool cand, bool paged) {
 template <int MT, int KT, bool CAND, bool ONE, int NB = 3>
 static hipError_t launch_score_t(const ScoreArgs& a, int grid, size_t lds, hipStream_t s, KTimer t) {
   auto fn = a.pages != nullptr ? k_score<MT, KT, CAND, ONE, NB, true> : k_score<MT, KT, CAND, ONE, NB, false>;
-  hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)lds);
+  hipError_t e = allow_lds((const void*)fn, lds);
   if (e != hipSuccess) return e;
   return launch_timed(fn, dim3(grid), dim3(kScoreBlock), lds, s, t, a);
 }

@@ -65,8 +65,7 @@ __global__ __launch_bounds__(kSelBlock) void k_chunk_cand(CandArgs a) {
 
 hipError_t launch_chunk_candidates(const CandArgs& a, int B, hipStream_t s) {
   const size_t lds = align16(sizeof(ChunkSmem<kSelBlock>)) + (size_t)a.P * 4;
-  hipError_t e = hipFuncSetAttribute((const void*)k_chunk_cand,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipError_t e = allow_lds((const void*)k_chunk_cand, lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_chunk_cand, dim3(a.G, B), dim3(kSelBlock), lds, s, a);
   return hipGetLastError();
@@ -1354,8 +1353,7 @@ static hipError_t launch_select_t(const SelArgs& a, const AttnArgs& at, int B, h
       fn = k_select<Attn, true>;
       lds += align16((size_t)at.lds_pages * 4);
     }
-  hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)lds);
+  hipError_t e = allow_lds((const void*)fn, lds);
   if (e != hipSuccess) return e;
   // attention splits (decode step) or ranking workgroups (stand-alone selection)
   const int grid = std::is_same<Attn, AttnNone>::value ? a.R : at.S;
@@ -1403,8 +1401,7 @@ static hipError_t launch_attend_t(const int32_t* idx, int k, int32_t* part_bad, 
   const int per = (k + at.S - 1) / at.S;
   const size_t lds = align16(sizeof(SelSmem)) + align16((size_t)per * 4) + Attn::lds_bytes(at.Hq, at.Dk);
   auto fn = k_attend_idx<Attn>;
-  hipError_t e = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)lds);
+  hipError_t e = allow_lds((const void*)fn, lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(fn, dim3(at.S, B), dim3(kSelBlock), lds, s, idx, k, part_bad, at);
   return hipGetLastError();
