@@ -16,6 +16,10 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
          # leading scalar and pointer kernel arguments (up to eight, stopping at the
          # first structure) arrive in scalar registers at wave launch
          "-mllvm", "-amdgpu-kernarg-preload-count=8",
+         # a one-lane LDS atomic (a wave claiming the next unit of its chunk) stays a
+         # plain atomic whose result is waited for where it is used; the atomic
+         # optimizer's wave-wide form waited for it at once, ahead of the products
+         "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
          "-I", os.path.join(ROOT, "include")]
 
 
