@@ -478,9 +478,11 @@ def main():
     ap.add_argument("--steps", type=int, default=240)
     ap.add_argument("--warmup", type=int, default=24)
     ap.add_argument("--config", default="ctx300k",
-                    choices=["ctx16k", "ctx62k_11layers", "ctx300k", "verify8_ctx131k", "ctx300k_fp8kv"])
+                    choices=["ctx16k", "ctx62k_11layers", "ctx300k", "verify8_ctx131k", "verify16_ctx131k",
+                             "ctx300k_fp8kv"])
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = default per workload)")
-    ap.add_argument("--legs", default="fallback,ctx62k_11layers,verify8_ctx131k,ctx300k_fp8kv,ctx300k_paged",
+    ap.add_argument("--legs", default="fallback,ctx62k_11layers,verify8_ctx131k,verify16_ctx131k,ctx300k_fp8kv,"
+                                      "ctx300k_paged",
                     help="comma list of extra legs, or 'none'")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -584,7 +586,7 @@ def main():
 
     leg_out = {}
     for name in legs:
-        if name in ("ctx62k_11layers", "verify8_ctx131k", "ctx300k_fp8kv") and name != args.config:
+        if name in ("ctx62k_11layers", "verify8_ctx131k", "verify16_ctx131k", "ctx300k_fp8kv") and name != args.config:
             leg_out[name] = leg(torch, binding, name, max(16, K // 8), 4)
         elif name == "ctx300k_paged":
             leg_out[name] = leg(torch, binding, "ctx300k", max(16, K // 8), R, paged=True)

@@ -20,6 +20,8 @@ is synthetic with the shapes of the model's DSA layers):
                     grid {-2..2}.
   verify8_ctx131k   width-8 verify block: B=8 over a shared 131,072-position cache;
                     row r sees ctx_len = 131,065 + r.
+  verify16_ctx131k  the widest verify block: B=16 over the same cache shape, row r
+                    sees ctx_len = 131,057 + r (own seed).
   ctx300k_tiepool   ctx300k with every key row drawn from a pool of 512 rows, so that
                     many positions share a score exactly (ties at the threshold).
   ctx16k_zeroquery  ctx16k with an all-zero indexer query: every score is 0.
@@ -32,7 +34,7 @@ is synthetic with the shapes of the model's DSA layers):
                     120 other positions exceed, so all 64 are in the top 2,048.
 
 Integer ranges are inclusive. Seeds (numpy PCG64 ``default_rng(seed)``): tiny_4k
-1000, ctx16k 1001, ctx300k 1003, verify8_ctx131k 1004, ctx300k_tiepool 1030,
+1000, ctx16k 1001, ctx300k 1003, verify8_ctx131k 1004, verify16_ctx131k 1005, ctx300k_tiepool 1030,
 ctx16k_zeroquery 1090, ctx16k_hotstride 1091, and 2000 + l for layer l of ctx62k_11layers; the integer
 arrays are drawn from it in the order iq, iw, ik. The normal arrays are drawn in
 blocks of 16,384 rows, block j of q from ``default_rng([seed, 1, j])`` and of kv
@@ -63,6 +65,7 @@ CONFIGS = {
     "ctx62k_11layers": dict(_LAYER, B=1, N=62464, k=2048, layers=11, seed=2000),
     "ctx300k": dict(_LAYER, B=1, N=300000, k=2048, key_range=2, seed=1003),
     "verify8_ctx131k": dict(_LAYER, B=8, N=131072, k=2048, seed=1004, verify_offsets=True),
+    "verify16_ctx131k": dict(_LAYER, B=16, N=131072, k=2048, seed=1005, verify_offsets=True),
     "ctx300k_tiepool": dict(_LAYER, B=1, N=300000, k=2048, key_range=2, seed=1030, key_pool=512),
     "ctx16k_zeroquery": dict(_LAYER, B=1, N=16384, k=2048, seed=1090, zero_query=True),
     "ctx16k_hotstride": dict(_LAYER, B=1, N=16384, k=2048, seed=1091, hot_stride=256),
@@ -108,8 +111,8 @@ def bf16_bits_to_f32(b):
 
 def ctx_lengths(name):
     c = CONFIGS[name]
-    if c.get("verify_offsets"):
-        return np.array([c["N"] - 7 + r for r in range(c["B"])], np.int32)
+    if c.get("verify_offsets"):  # row r of a B-row block sees N - (B - 1) + r positions
+        return np.array([c["N"] - c["B"] + 1 + r for r in range(c["B"])], np.int32)
     return np.full(c["B"], c["N"], np.int32)
 
 

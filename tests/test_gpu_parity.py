@@ -106,7 +106,7 @@ def expected_ties(ref_scores, ref_idx, ctx_len, k):
     return t
 
 
-@pytest.mark.parametrize("name", ["tiny_4k", "ctx16k", "ctx300k", "verify8_ctx131k", "ctx300k_tiepool",
+@pytest.mark.parametrize("name", ["tiny_4k", "ctx16k", "ctx300k", "verify8_ctx131k", "verify16_ctx131k", "ctx300k_tiepool",
                                   "ctx16k_zeroquery", "ctx16k_hotstride", "ctx16k_fp8kv", "ctx300k_fp8kv"])
 def test_decode_step_matches_oracle(torch, dsa, name):
     note("decode_step", name)

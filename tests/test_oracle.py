@@ -321,6 +321,7 @@ def test_workload_generator_is_deterministic():
     for key in ("iq", "iw", "ik", "q", "kv", "ctx_len"):
         assert (a[key] == b[key]).all()
     assert inputs.ctx_lengths("verify8_ctx131k").tolist() == [131065 + r for r in range(8)]
+    assert inputs.ctx_lengths("verify16_ctx131k").tolist() == [131057 + r for r in range(16)]
 
 
 def test_openmp_build_gives_identical_results():
