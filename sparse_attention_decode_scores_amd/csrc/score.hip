@@ -438,6 +438,27 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(const int8_t* __restr
   // from the chunk's first to its last valid one
   const int span = units > 0 ? (int)((int64_t)(units - 1) * ustride) + (count - kUnit * (units - 1)) : 0;
 
+  // Paged keys (PG): the resource covers the pool, the chunk's unit j starts at pool
+  // byte base_of(j, e) with e its table entry (the row's unit c + jG is slot
+  // (c + jG) % 8 of logical page (c + jG) / 8), and a unit past the chunk gets an
+  // offset past the pool (zeros). Each wave requests its first units' entries before
+  // anything else (they gate its first key requests); thread t reads unit t's entry
+  // for the LDS list the refills use. Entries are read unconditionally, entry 0
+  // standing in for a unit past the chunk (read behind a branch each, the first
+  // units' entries were three round trips in a row).
+  const uint32_t pool_bytes = PG ? (uint32_t)a.pool_pages * (uint32_t)kPageSize * (uint32_t)Di : 0u;
+  auto entry_of = [&](int j) -> int { return j < units ? (c + j * G) >> 3 : 0; };
+  auto base_of = [&](int j, int32_t e) -> uint32_t {
+    e = e < 0 ? 0 : (e >= a.pool_pages ? a.pool_pages - 1 : e);
+    return j < units ? ((uint32_t)e * kPageSize + (uint32_t)(kUnit * ((c + j * G) & 7))) * (uint32_t)Di : pool_bytes;
+  };
+  int32_t e0 = 0, e1 = 0, e2 = 0;
+  if constexpr (PG) {
+    e0 = pages[entry_of(wave)];
+    e1 = pages[entry_of(wave + kScoreWaves)];
+    if constexpr (D == 3) e2 = pages[entry_of(wave + 2 * kScoreWaves)];
+  }
+
   // The query: the block requests it once, one 16-byte piece per thread (two when
   // Hi·Di > 8 KB), before any key, and stages it in LDS, from where every wave takes
   // its A operand (lane l: head 32mt + (l & 31), dims 32kt + 16(l >> 5) .. +15). Each
@@ -455,25 +476,25 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(const int8_t* __restr
   }
   int wl = 0;
   if (wave == 0) wl = (int)iw[(int64_t)b * Hi + (lane < Hi ? lane : Hi - 1)];
-  // Paged keys (PG): the resource covers the pool, the chunk's unit j starts at pool
-  // byte unit_base(j) (the row's unit c + jG is slot (c + jG) % 8 of logical page
-  // (c + jG) / 8), and a unit past the chunk gets an offset past the pool (zeros).
-  // Thread t reads unit t's table entry for the LDS list the refills use; each wave
-  // reads its first units' entries itself.
-  const uint32_t pool_bytes = PG ? (uint32_t)a.pool_pages * (uint32_t)kPageSize * (uint32_t)Di : 0u;
-  auto unit_base = [&](int j) -> uint32_t {
-    return j < units ? page_row(pages, a.pool_pages, (int64_t)kUnit * (c + (int64_t)j * G)) * (uint32_t)Di
-                     : pool_bytes;
-  };
-  uint32_t ub = 0;
-  if constexpr (PG)
-    if (tid < units) ub = unit_base(tid);
+  // (thread t's entry: requested here, unconditionally, and turned into an offset only
+  // where it is stored, behind the key requests, so no wait for it comes first)
+  int32_t ue = 0;
+  if constexpr (PG) ue = pages[entry_of(tid)];
 
   // the histogram is shared by the waves: cleared before any of them adds to it
   for (int i = tid; i < kHistBins + kHistGroups; i += kScoreBlock) hist[i] = 0;  // and hgroup
   if (tid == 0) {
     rsm.nstaged = 0;
     rsm.next = kScoreWaves * D;  // units 0 .. 8D - 1 are requested below, D per wave
+  }
+  uint32_t fb[3] = {0u, 0u, 0u};
+  if constexpr (PG) {
+    // the entries as opaque values here, where the barrier below waits anyway: left
+    // to itself the compiler moved each read behind its unit's branch
+    asm volatile("" : "+s"(e0), "+s"(e1), "+s"(e2));
+    fb[0] = base_of(wave, e0);
+    fb[1] = base_of(wave + kScoreWaves, e1);
+    if constexpr (D == 3) fb[2] = base_of(wave + 2 * kScoreWaves, e2);
   }
   lds_barrier();
 
@@ -482,9 +503,9 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(const int8_t* __restr
          : __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(ik + cbeg * Di), (short)0, span * Di, 0x00020000);
   v4i kb0[KT], kb1[KT], kb2[KT];
   if constexpr (PG) {
-    load_unit_at<KT>(kb0, rs, unit_base(wave), Di);
-    load_unit_at<KT>(kb1, rs, unit_base(wave + kScoreWaves), Di);
-    if constexpr (D == 3) load_unit_at<KT>(kb2, rs, unit_base(wave + 2 * kScoreWaves), Di);
+    load_unit_at<KT>(kb0, rs, fb[0], Di);
+    load_unit_at<KT>(kb1, rs, fb[1], Di);
+    if constexpr (D == 3) load_unit_at<KT>(kb2, rs, fb[2], Di);
   } else {
     load_unit<KT>(kb0, rs, wave, js, Di);
     load_unit<KT>(kb1, rs, wave + kScoreWaves, js, Di);
@@ -504,7 +525,7 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(const int8_t* __restr
   if (Di < DI && tid < Hi) *reinterpret_cast<v4i*>(qs + tid * DIP + Di) = v4i{0, 0, 0, 0};
   if (wave == 0) wsm[lane] = lane < Hi ? wl : 0;
   if constexpr (PG)
-    if (tid < units) uoff[tid] = ub;
+    if (tid < units) uoff[tid] = base_of(tid, ue);
   lds_barrier();
   v4i qreg[MT][KT];
 #pragma unroll
