@@ -731,6 +731,24 @@ __global__ __launch_bounds__(kScoreBlock) void k_score_row(const int8_t* __restr
   }
 }
 
+// The contiguous score kernels are instantiated, and so laid out in the code object,
+// ahead of the paged ones (as in select.hip: a kernel's place in the code object
+// changes its time, and this keeps changes to the paged kernels from moving these).
+#define DSA_ROW(M, K) (const void*)&k_score_row<M, K, kScoreRowDepth, false>,
+#define DSA_MK(M, K)                                                                                      \
+  (const void*)&k_score<M, K, true, false, 1, false>, (const void*)&k_score<M, K, true, true, 3, false>,   \
+      (const void*)&k_score<M, K, true, false, 3, false>, (const void*)&k_score<M, K, false, true, 3, false>, \
+      (const void*)&k_score<M, K, false, false, 3, false>,
+#define DSA_ALL(X) X(1, 1) X(1, 2) X(1, 3) X(1, 4) X(1, 5) X(1, 6) X(1, 7) X(1, 8) \
+  X(2, 1) X(2, 2) X(2, 3) X(2, 4) X(2, 5) X(2, 6) X(2, 7) X(2, 8)
+const void* score_order(int i) {
+  static const void* const k[] = {DSA_ALL(DSA_ROW) DSA_ALL(DSA_MK)};
+  return k[i];
+}
+#undef DSA_ROW
+#undef DSA_MK
+#undef DSA_ALL
+
 size_t score_row_lds_bytes(int P, bool paged) {
   // ... + the staged query at its largest (64 heads, rows of 256 + 16 bytes), the
   // weights and, paged, the units' pool offsets
