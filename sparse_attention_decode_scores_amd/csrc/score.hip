@@ -124,26 +124,37 @@ __global__ __launch_bounds__(kScoreBlock) void k_score(ScoreArgs a) {
 
   // buffer resource word 3 for gfx9 raw buffers: 32-bit data format, no swizzle.
   // Contiguous keys: the resource covers the chunk's valid keys. Paged: it covers
-  // the pool, tile tp starts at pool byte tile_base(tp), and a tile past the chunk
-  // gets an offset past the pool (zeros). The first tiles' table entries are read
-  // per wave; the rest are staged in LDS (toff) for the refills.
+  // the pool, tile tp starts at pool byte tile_at(tp, e) with e its table entry, and
+  // a tile past the chunk gets an offset past the pool (zeros). The first tiles'
+  // entries are read per wave; thread t reads tile t's for the LDS list (toff) the
+  // refills use. All of them are read unconditionally (entry 0 standing in for a
+  // tile past the chunk), so their requests go out together.
   const uint32_t pool_bytes = PG ? (uint32_t)a.pool_pages * (uint32_t)kPageSize * (uint32_t)a.Di : 0u;
   const __amdgpu_buffer_rsrc_t rs =
       PG ? __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(a.ik), (short)0, (int)pool_bytes, 0x00020000)
          : __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(a.ik + cbeg * a.Di), (short)0, clen * a.Di,
                                              0x00020000);
-  auto tile_base = [&](int tp) -> uint32_t {
-    return tp < npairs ? page_row(a.pages, a.pool_pages, cbeg + 64 * tp) * (uint32_t)a.Di : pool_bytes;
+  auto entry_of = [&](int tp) -> int64_t { return tp < npairs ? (cbeg + 64 * tp) >> kPageShift : 0; };
+  auto tile_at = [&](int tp, int32_t e) -> uint32_t {
+    e = e < 0 ? 0 : (e >= a.pool_pages ? a.pool_pages - 1 : e);
+    return tp < npairs ? ((uint32_t)e * kPageSize + (uint32_t)((cbeg + 64 * tp) & (kPageSize - 1))) * (uint32_t)a.Di
+                       : pool_bytes;
   };
   v4i kb0[2][KT], kb1[2][KT], kb2[2][KT];
-  uint32_t tb = 0;  // paged: thread t's tile offset, stored to LDS below
+  int32_t te = 0;  // paged: thread t's tile entry, stored to LDS (as an offset) below
   if constexpr (PG) {
-    load_keys_at<KT>(kb0, rs, tile_base(wave), a.Di);
+    int32_t e0 = a.pages[entry_of(wave)], e1 = 0, e2 = 0;
     if constexpr (NB > 1) {
-      load_keys_at<KT>(kb1, rs, tile_base(wave + kScoreWaves), a.Di);
-      load_keys_at<KT>(kb2, rs, tile_base(wave + 2 * kScoreWaves), a.Di);
+      e1 = a.pages[entry_of(wave + kScoreWaves)];
+      e2 = a.pages[entry_of(wave + 2 * kScoreWaves)];
     }
-    if (tid < npairs) tb = tile_base(tid);
+    te = a.pages[entry_of(tid)];
+    asm volatile("" : "+s"(e0), "+s"(e1), "+s"(e2));  // (read here, not behind a branch each)
+    load_keys_at<KT>(kb0, rs, tile_at(wave, e0), a.Di);
+    if constexpr (NB > 1) {
+      load_keys_at<KT>(kb1, rs, tile_at(wave + kScoreWaves, e1), a.Di);
+      load_keys_at<KT>(kb2, rs, tile_at(wave + 2 * kScoreWaves, e2), a.Di);
+    }
   } else {
     load_keys<KT>(kb0, rs, wave, a.Di);
     if constexpr (NB > 1) {
@@ -166,7 +177,7 @@ __global__ __launch_bounds__(kScoreBlock) void k_score(ScoreArgs a) {
   }
   if (tid < a.Bg * HP) wsm[tid] = tid % HP < a.Hi ? (int32_t)wv : 0;
   if constexpr (PG)
-    if (tid < npairs) toff[tid] = tb;
+    if (tid < npairs) toff[tid] = tile_at(tid, te);
   lds_barrier();
 
   // A fragments and weights of a single row stay in registers for the whole chunk.
