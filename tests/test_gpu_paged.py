@@ -99,7 +99,7 @@ def run(torch, dsa, c, p=None, flags=0, events=None):
 
 
 @pytest.mark.parametrize("name", ["tiny_4k", "ctx16k", "ctx16k_fp8kv", "ctx16k_hotstride", "verify8_ctx131k",
-                                  "ctx300k"])
+                                  "verify16_ctx131k", "ctx300k"])
 def test_paged_step_matches_oracle_and_contiguous(torch, dsa, name):
     note("paged decode_step", name)
     c, (rs, ri, ro), p = case(name)
@@ -187,12 +187,15 @@ def test_paged_table_may_repeat_and_fill_the_pool(torch, dsa):
     check_attention(o1, ro, "aliased table")
 
 
-def test_paged_index_scores_standalone(torch, dsa):
-    note("paged index_scores")
-    c = inputs.random_case(802, B=3, N=5000, k=64, Hi=64, Di=128, Hq=1, Dk=64, Dv=64, ctx_len=[5000, 300, 4097])
+@pytest.mark.parametrize("ctx", [[4999], [5000, 300, 4097]])
+def test_paged_index_scores_standalone(torch, dsa, ctx):
+    # one row (the one-row launch of the pass without candidates) and several
+    note("paged index_scores", ctx)
+    B = len(ctx)
+    c = inputs.random_case(802, B=B, N=5000, k=64, Hi=64, Di=128, Hq=1, Dk=64, Dv=64, ctx_len=ctx)
     p = inputs.paged(c, seed=13)
     ref = oracle.index_scores(c["iq"], c["iw"], c["ik"], c["ctx_len"])
-    scores = torch.full((3, 5000), -5, dtype=torch.int32, device="cuda")
+    scores = torch.full((B, 5000), -5, dtype=torch.int32, device="cuda")
     dsa.dsa_index_scores_paged(to_dev(torch, c["iq"]), to_dev(torch, c["iw"]), to_dev(torch, p["ik_pool"]),
                                to_dev(torch, p["page_table"]), c["ctx_len"], N=5000, scores=scores)
     got = scores.cpu().numpy()
@@ -201,9 +204,10 @@ def test_paged_index_scores_standalone(torch, dsa):
         assert (got[b, n:] == -5).all()
 
 
-def test_paged_sparse_attn_standalone(torch, dsa):
-    note("paged sparse_attn")
-    c, (rs, ri, ro), p = case("ctx16k")
+@pytest.mark.parametrize("name", ["ctx16k", "ctx16k_fp8kv"])
+def test_paged_sparse_attn_standalone(torch, dsa, name):
+    note("paged sparse_attn", name)
+    c, (rs, ri, ro), p = case(name)
     idx = ri.copy()
     idx[0, 5] = -1
     idx[0, 9] = c["N"] + 3  # outside [0, N): skipped and counted
