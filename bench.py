@@ -482,7 +482,7 @@ def main():
                              "ctx300k_fp8kv"])
     ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0 = default per workload)")
     ap.add_argument("--legs", default="fallback,ctx62k_11layers,verify8_ctx131k,verify16_ctx131k,ctx300k_fp8kv,"
-                                      "ctx300k_paged",
+                                      "ctx300k_paged,verify8_ctx131k_paged",
                     help="comma list of extra legs, or 'none'")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -590,6 +590,8 @@ def main():
             leg_out[name] = leg(torch, binding, name, max(16, K // 8), 4)
         elif name == "ctx300k_paged":
             leg_out[name] = leg(torch, binding, "ctx300k", max(16, K // 8), R, paged=True)
+        elif name == "verify8_ctx131k_paged":
+            leg_out[name] = leg(torch, binding, "verify8_ctx131k", max(16, K // 8), 4, paged=True)
 
     cpu = None
     if not args.no_cpu_baseline:
